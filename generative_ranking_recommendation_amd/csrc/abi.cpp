@@ -1,0 +1,439 @@
+// C ABI of the GenRank hot path: host-side argument checks, workspace layout, and the
+// composition of kernels into a block forward / backward.  Every entry point validates
+// its arguments before enqueuing anything and returns a genrank_status.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <string.h>
+
+#include "genrank.h"
+#include "internal.hpp"
+
+namespace genrank {
+
+genrank_status check_batch(const genrank_batch* b) {
+  if (!b) return GENRANK_E_ARG;
+  if (b->B < 1 || b->m < 0 || b->d < 1 || b->H < 1 || b->dh < 1 || b->max_hist < 0 ||
+      b->total_hist < 0)
+    return GENRANK_E_ARG;
+  if (b->H > GENRANK_MAX_HEADS) return GENRANK_E_SHAPE;
+  if (static_cast<int64_t>(b->H) * b->dh != b->d) return GENRANK_E_SHAPE;
+  if (b->dtype != GENRANK_F32 && b->dtype != GENRANK_BF16) return GENRANK_E_DTYPE;
+  if (b->total_hist > static_cast<int64_t>(b->max_hist) * b->B) return GENRANK_E_SHAPE;
+  const int64_t T = b->total_hist + static_cast<int64_t>(b->B) * b->m;
+  if (T >= (int64_t(1) << 31)) return GENRANK_E_SHAPE;
+  return GENRANK_OK;
+}
+
+size_t dtype_size(int dtype) { return dtype == GENRANK_BF16 ? 2 : 4; }
+
+namespace {
+
+inline hipStream_t S(genrank_stream_t s) { return reinterpret_cast<hipStream_t>(s); }
+
+inline size_t align_up(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+inline int64_t rows_of(const genrank_batch* b) {
+  return b->total_hist + static_cast<int64_t>(b->B) * b->m;
+}
+
+// Activations kept by the block forward, in this order, each 256-byte aligned.
+struct LayerFwdWs {
+  char* z;    // [T, d]   rmsnorm(x) g1          (PRENORM)
+  char* qkv;  // [T, 3d]
+  char* o;    // [T, d]   attention output
+  float* lse; // [T, H]
+  char* x1;   // [T, d]   x + attention branch   (PRENORM)
+  char* z2;   // [T, d]   rmsnorm(x1) g2         (PRENORM)
+  char* a;    // [T, f]   FFN pre-activation     (PRENORM)
+  char* hdn;  // [T, f]   silu(a)                (PRENORM)
+  size_t bytes;
+};
+
+LayerFwdWs layer_fwd_layout(const genrank_batch* b, int block, int ffn, char* base) {
+  const size_t T = static_cast<size_t>(rows_of(b));
+  const size_t es = dtype_size(b->dtype);
+  const size_t d = b->d;
+  const bool pre = block == GENRANK_BLOCK_PRENORM;
+  LayerFwdWs w{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    char* p = base ? base + off : nullptr;
+    off += align_up(bytes);
+    return p;
+  };
+  w.z = pre ? take(T * d * es) : nullptr;
+  w.qkv = take(T * 3 * d * es);
+  w.o = take(T * d * es);
+  w.lse = reinterpret_cast<float*>(take(T * b->H * sizeof(float)));
+  w.x1 = pre ? take(T * d * es) : nullptr;
+  w.z2 = pre ? take(T * d * es) : nullptr;
+  w.a = pre ? take(T * static_cast<size_t>(ffn) * es) : nullptr;
+  w.hdn = pre ? take(T * static_cast<size_t>(ffn) * es) : nullptr;
+  w.bytes = off;
+  return w;
+}
+
+struct LayerBwdWs {
+  char* dqkv;   // [T, 3d]
+  char* dout;   // [T, d]  gradient of the attention output
+  char* dz;     // [T, d]  gradient of the QKV input
+  char* dx1;    // [T, d]  (PRENORM)
+  char* dh;     // [T, f]  (PRENORM) gradient of silu(a), then of a
+  char* dz2;    // [T, d]  (PRENORM)
+  char* attn;   // attention backward scratch
+  size_t bytes;
+};
+
+LayerBwdWs layer_bwd_layout(const genrank_batch* b, int block, int ffn, char* base) {
+  const size_t T = static_cast<size_t>(rows_of(b));
+  const size_t es = dtype_size(b->dtype);
+  const size_t d = b->d;
+  const bool pre = block == GENRANK_BLOCK_PRENORM;
+  LayerBwdWs w{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    char* p = base ? base + off : nullptr;
+    off += align_up(bytes);
+    return p;
+  };
+  w.dqkv = take(T * 3 * d * es);
+  w.dout = take(T * d * es);
+  w.dz = take(T * d * es);
+  w.dx1 = pre ? take(T * d * es) : nullptr;
+  w.dh = pre ? take(T * static_cast<size_t>(ffn) * es) : nullptr;
+  w.dz2 = pre ? take(T * d * es) : nullptr;
+  w.attn = take(attn_bwd_workspace(b));
+  w.bytes = off;
+  return w;
+}
+
+genrank_status check_layer_weights(const genrank_batch* b, const genrank_layer_weights* w) {
+  if (!w || !w->wqkv || !w->wo || !w->alibi.slopes_pos || !w->alibi.slopes_time)
+    return GENRANK_E_ARG;
+  if (w->block == GENRANK_BLOCK_PRENORM) {
+    if (!w->w1 || !w->w2 || !w->g1 || !w->g2) return GENRANK_E_ARG;
+    if (w->ffn_dim < 1 || w->ffn_dim % 64 != 0) return GENRANK_E_SHAPE;
+  } else if (w->block != GENRANK_BLOCK_ATTN_ONLY) {
+    return GENRANK_E_ARG;
+  }
+  if (b->d % 64 != 0 && b->dtype == GENRANK_BF16) return GENRANK_E_SHAPE;
+  return GENRANK_OK;
+}
+
+#define GR_TRY(expr)                         \
+  do {                                       \
+    genrank_status _s = (expr);              \
+    if (_s != GENRANK_OK) return _s;         \
+  } while (0)
+
+}  // namespace
+}  // namespace genrank
+
+using namespace genrank;
+
+extern "C" {
+
+const char* genrank_status_string(int s) {
+  switch (s) {
+    case GENRANK_OK: return "GENRANK_OK";
+    case GENRANK_E_ARG: return "GENRANK_E_ARG: invalid argument";
+    case GENRANK_E_SHAPE: return "GENRANK_E_SHAPE: unsupported or inconsistent shape";
+    case GENRANK_E_DTYPE: return "GENRANK_E_DTYPE: unsupported dtype";
+    case GENRANK_E_UNSORTED: return "GENRANK_E_UNSORTED: offsets or timestamps out of order";
+    case GENRANK_E_RANGE: return "GENRANK_E_RANGE: id or time difference out of range";
+    case GENRANK_E_WORKSPACE: return "GENRANK_E_WORKSPACE: workspace missing or too small";
+    case GENRANK_E_HIP: return "GENRANK_E_HIP: HIP runtime or launch failure";
+    default: return "GENRANK: unknown status";
+  }
+}
+
+int32_t genrank_version(void) { return (GENRANK_VERSION_MAJOR << 16) | GENRANK_VERSION_MINOR; }
+
+genrank_status genrank_workspace_size(int32_t op, const genrank_batch* b,
+                                      const genrank_layer_weights* w, size_t* bytes) {
+  if (!b || !bytes) return GENRANK_E_ARG;
+  GR_TRY(check_batch(b));
+  switch (op) {
+    case GENRANK_OP_EMBED_SUM:
+    case GENRANK_OP_ATTN_FWD:
+      *bytes = 0;
+      return GENRANK_OK;
+    case GENRANK_OP_ATTN_BWD:
+      *bytes = attn_bwd_workspace(b);
+      return GENRANK_OK;
+    case GENRANK_OP_LAYER_FWD:
+    case GENRANK_OP_LAYER_BWD: {
+      if (!w) return GENRANK_E_ARG;
+      const int block = w->block;
+      const int ffn = block == GENRANK_BLOCK_PRENORM ? w->ffn_dim : 0;
+      *bytes = (op == GENRANK_OP_LAYER_FWD) ? layer_fwd_layout(b, block, ffn, nullptr).bytes
+                                            : layer_bwd_layout(b, block, ffn, nullptr).bytes;
+      return GENRANK_OK;
+    }
+    default:
+      return GENRANK_E_ARG;
+  }
+}
+
+genrank_status genrank_validate_host(const genrank_batch* b, const genrank_inputs* in,
+                                     const genrank_tables* t, int64_t* bad_row) {
+  if (bad_row) *bad_row = -1;
+  if (!b || !in || !t) return GENRANK_E_ARG;
+  GR_TRY(check_batch(b));
+  if (!in->hist_offsets || !in->req_ts) return GENRANK_E_ARG;
+  const int32_t* off = in->hist_offsets;
+  auto bad = [&](int64_t r, genrank_status s) {
+    if (bad_row) *bad_row = r;
+    return s;
+  };
+  if (off[0] != 0) return bad(0, GENRANK_E_UNSORTED);
+  int32_t mx = 0;
+  for (int u = 0; u < b->B; ++u) {
+    if (off[u + 1] < off[u]) return bad(u, GENRANK_E_UNSORTED);
+    mx = off[u + 1] - off[u] > mx ? off[u + 1] - off[u] : mx;
+  }
+  if (off[b->B] != b->total_hist || mx > b->max_hist) return bad(-1, GENRANK_E_SHAPE);
+  if (b->total_hist > 0 && (!in->hist_items || !in->hist_actions || !in->hist_ts))
+    return GENRANK_E_ARG;
+  if (b->m > 0 && !in->cand_items) return GENRANK_E_ARG;
+  for (int k = 1; k + 1 < t->n_rt; ++k)
+    if (t->rt_bounds[k] < t->rt_bounds[k - 1]) return bad(k, GENRANK_E_UNSORTED);
+  for (int u = 0; u < b->B; ++u) {
+    const int64_t a = off[u], e = off[u + 1];
+    for (int64_t r = a; r < e; ++r) {
+      if (r > a && in->hist_ts[r] < in->hist_ts[r - 1]) return bad(r, GENRANK_E_UNSORTED);
+      if (in->hist_items[r] < 0 || in->hist_items[r] >= t->n_item) return bad(r, GENRANK_E_RANGE);
+      if (in->hist_actions[r] < 0 || in->hist_actions[r] >= t->n_action)
+        return bad(r, GENRANK_E_RANGE);
+    }
+    if (e > a) {
+      if (in->req_ts[u] <= in->hist_ts[e - 1]) return bad(e - 1, GENRANK_E_UNSORTED);
+      if (in->req_ts[u] - in->hist_ts[a] >= (int64_t(1) << 24)) return bad(a, GENRANK_E_RANGE);
+    }
+    for (int k = 0; k < b->m; ++k) {
+      const int32_t it = in->cand_items[static_cast<int64_t>(u) * b->m + k];
+      if (it < 0 || it >= t->n_item) return bad(b->total_hist + static_cast<int64_t>(u) * b->m + k, GENRANK_E_RANGE);
+    }
+  }
+  return GENRANK_OK;
+}
+
+genrank_status genrank_embed_sum(const genrank_batch* b, const genrank_inputs* in,
+                                 const genrank_tables* t, void* x_out, genrank_stream_t stream) {
+  GR_TRY(check_embed_args(b, in, t));
+  if (!x_out) return GENRANK_E_ARG;
+  return launch_embed_sum(b, in, t, x_out, S(stream));
+}
+
+genrank_status genrank_debug_indices(const genrank_batch* b, const genrank_inputs* in,
+                                     const genrank_tables* t, int32_t* out,
+                                     genrank_stream_t stream) {
+  GR_TRY(check_embed_args(b, in, t));
+  if (!out) return GENRANK_E_ARG;
+  return launch_debug_indices(b, in, t, out, S(stream));
+}
+
+genrank_status genrank_embed_bwd(const genrank_batch* b, const genrank_inputs* in,
+                                 const genrank_tables* t, const void* dx, float* d_item,
+                                 float* d_action, float* d_pos, float* d_ri, float* d_rt,
+                                 genrank_stream_t stream) {
+  GR_TRY(check_embed_args(b, in, t));
+  if (!dx || !d_item || !d_action || !d_pos || !d_ri || !d_rt) return GENRANK_E_ARG;
+  return launch_embed_bwd(b, in, t, dx, d_item, d_action, d_pos, d_ri, d_rt, S(stream));
+}
+
+genrank_status genrank_attn_fwd(const genrank_batch* b, const int32_t* offsets,
+                                const int64_t* ts, const int64_t* req, genrank_alibi alibi,
+                                const void* q, const void* k, const void* v, int64_t ld_qkv,
+                                void* o, int64_t ld_o, float* lse, genrank_stream_t stream) {
+  GR_TRY(check_attn_args(b, offsets, ts, req, alibi, q, k, v, ld_qkv, o, ld_o));
+  return launch_attn_fwd(b, offsets, ts, req, alibi, q, k, v, ld_qkv, o, ld_o, lse, S(stream));
+}
+
+genrank_status genrank_attn_bwd(const genrank_batch* b, const int32_t* offsets,
+                                const int64_t* ts, const int64_t* req, genrank_alibi alibi,
+                                const void* q, const void* k, const void* v, int64_t ld_qkv,
+                                const void* o, const void* dout, int64_t ld_o, const float* lse,
+                                void* dq, void* dk, void* dv, int64_t ld_dqkv,
+                                int32_t cand_only, void* ws, size_t ws_bytes,
+                                genrank_stream_t stream) {
+  GR_TRY(check_attn_args(b, offsets, ts, req, alibi, q, k, v, ld_qkv, o, ld_o));
+  if (!dout || !lse || !dq || !dk || !dv) return GENRANK_E_ARG;
+  if (ld_dqkv < b->d) return GENRANK_E_SHAPE;
+  if (b->dh > 64) return GENRANK_E_SHAPE;
+  if (!ws || ws_bytes < attn_bwd_workspace(b)) return GENRANK_E_WORKSPACE;
+  return launch_attn_bwd(b, offsets, ts, req, alibi, q, k, v, ld_qkv, o, dout, ld_o, lse, dq, dk,
+                         dv, ld_dqkv, cand_only, ws, S(stream));
+}
+
+genrank_status genrank_layer_fwd(const genrank_batch* b, const genrank_layer_weights* w,
+                                 const int32_t* offsets, const int64_t* ts, const int64_t* req,
+                                 const void* x_in, void* y_out, int32_t flags, void* ws,
+                                 size_t ws_bytes, genrank_stream_t stream) {
+  GR_TRY(check_batch(b));
+  GR_TRY(check_layer_weights(b, w));
+  if (!x_in || !y_out || !offsets || !req || (b->total_hist > 0 && !ts)) return GENRANK_E_ARG;
+  const bool pre = w->block == GENRANK_BLOCK_PRENORM;
+  const int ffn = pre ? w->ffn_dim : 0;
+  const LayerFwdWs L = layer_fwd_layout(b, w->block, ffn, static_cast<char*>(ws));
+  if (!ws || ws_bytes < L.bytes) return GENRANK_E_WORKSPACE;
+  if (!pre && x_in == y_out) return GENRANK_E_ARG;
+  const hipStream_t s = S(stream);
+  const int dt = b->dtype;
+  const int T = static_cast<int>(rows_of(b));
+  const int d = b->d;
+  const size_t es = dtype_size(dt);
+  if (T == 0) return GENRANK_OK;
+  GR_TRY(check_attn_args(b, offsets, ts, req, w->alibi, L.qkv, L.qkv + d * es, L.qkv + 2 * d * es,
+                         3 * d, L.o, d));
+  const void* zin = x_in;
+  if (pre) {
+    GR_TRY(launch_rmsnorm(dt, x_in, w->g1, L.z, T, d, s));
+    zin = L.z;
+  }
+  GR_TRY(launch_gemm_nt(dt, zin, d, w->wqkv, d, L.qkv, 3 * d, T, 3 * d, d, GEMM_EPI_STORE,
+                        nullptr, 0, nullptr, 0, s));
+  GR_TRY(launch_attn_fwd(b, offsets, ts, req, w->alibi, L.qkv, L.qkv + d * es, L.qkv + 2 * d * es,
+                         3 * d, L.o, d, L.lse, s));
+  if (!pre) {
+    return launch_gemm_nt(dt, L.o, d, w->wo, d, y_out, d, T, d, d, GEMM_EPI_STORE, nullptr, 0,
+                          nullptr, 0, s);
+  }
+  GR_TRY(launch_gemm_nt(dt, L.o, d, w->wo, d, L.x1, d, T, d, d, GEMM_EPI_RESID, x_in, d, nullptr,
+                        0, s));
+  GR_TRY(launch_rmsnorm(dt, L.x1, w->g2, L.z2, T, d, s));
+  GR_TRY(launch_gemm_nt(dt, L.z2, d, w->w1, d, L.hdn, ffn, T, ffn, d, GEMM_EPI_SILU, nullptr, 0,
+                        (flags & GENRANK_FWD_SAVE) ? L.a : nullptr, ffn, s));
+  return launch_gemm_nt(dt, L.hdn, ffn, w->w2, ffn, y_out, d, T, d, ffn, GEMM_EPI_RESID, L.x1, d,
+                        nullptr, 0, s);
+}
+
+genrank_status genrank_layer_bwd(const genrank_batch* b, const genrank_layer_weights* w,
+                                 const int32_t* offsets, const int64_t* ts, const int64_t* req,
+                                 const void* x_in, const void* ws, const void* dy, void* dx,
+                                 genrank_layer_grads g, int32_t cand_only, void* ws_bwd,
+                                 size_t ws_bwd_bytes, genrank_stream_t stream) {
+  GR_TRY(check_batch(b));
+  GR_TRY(check_layer_weights(b, w));
+  if (!x_in || !ws || !dy || !dx || !offsets || !req || (b->total_hist > 0 && !ts))
+    return GENRANK_E_ARG;
+  const bool pre = w->block == GENRANK_BLOCK_PRENORM;
+  const int ffn = pre ? w->ffn_dim : 0;
+  if (!g.wqkv || !g.wo || (pre && (!g.w1 || !g.w2 || !g.g1 || !g.g2))) return GENRANK_E_ARG;
+  if (b->dh > 64) return GENRANK_E_SHAPE;
+  const LayerFwdWs F = layer_fwd_layout(b, w->block, ffn, static_cast<char*>(const_cast<void*>(ws)));
+  const LayerBwdWs L = layer_bwd_layout(b, w->block, ffn, static_cast<char*>(ws_bwd));
+  if (!ws_bwd || ws_bwd_bytes < L.bytes) return GENRANK_E_WORKSPACE;
+  const hipStream_t s = S(stream);
+  const int dt = b->dtype;
+  const int T = static_cast<int>(rows_of(b));
+  const int d = b->d;
+  const size_t es = dtype_size(dt);
+  const int F32 = GENRANK_F32;
+  const void* att_grad = dy;  // gradient reaching the attention branch output
+  if (pre) {
+    // FFN branch: y = x1 + W2 silu(W1 z2)
+    GR_TRY(launch_gemm_general(dt, F32, dy, 1, d, F.hdn, ffn, 1, g.w2, ffn, d, ffn, T,
+                               GEMM_EPI_STORE, false, nullptr, 0, nullptr, 0, s));
+    GR_TRY(launch_gemm_general(dt, dt, dy, d, 1, w->w2, ffn, 1, L.dh, ffn, T, ffn, d,
+                               GEMM_EPI_STORE, false, nullptr, 0, nullptr, 0, s));
+    GR_TRY(launch_silu_bwd(dt, F.a, L.dh, L.dh, static_cast<int64_t>(T) * ffn, s));
+    GR_TRY(launch_gemm_general(dt, F32, L.dh, 1, ffn, F.z2, d, 1, g.w1, d, ffn, d, T,
+                               GEMM_EPI_STORE, false, nullptr, 0, nullptr, 0, s));
+    GR_TRY(launch_gemm_general(dt, dt, L.dh, ffn, 1, w->w1, d, 1, L.dz2, d, T, d, ffn,
+                               GEMM_EPI_STORE, false, nullptr, 0, nullptr, 0, s));
+    GR_TRY(launch_fill_f32(g.g2, d, 0.f, s));
+    GR_TRY(launch_rmsnorm_bwd(dt, F.x1, w->g2, L.dz2, dy, L.dx1, g.g2, T, d, s));
+    att_grad = L.dx1;
+  }
+  // attention branch: out = Wo o
+  GR_TRY(launch_gemm_general(dt, F32, att_grad, 1, d, F.o, d, 1, g.wo, d, d, d, T,
+                             GEMM_EPI_STORE, false, nullptr, 0, nullptr, 0, s));
+  GR_TRY(launch_gemm_general(dt, dt, att_grad, d, 1, w->wo, d, 1, L.dout, d, T, d, d,
+                             GEMM_EPI_STORE, false, nullptr, 0, nullptr, 0, s));
+  GR_TRY(launch_attn_bwd(b, offsets, ts, req, w->alibi, F.qkv, F.qkv + d * es, F.qkv + 2 * d * es,
+                         3 * d, F.o, L.dout, d, F.lse, L.dqkv, L.dqkv + d * es,
+                         L.dqkv + 2 * d * es, 3 * d, cand_only, L.attn, s));
+  const void* zin = pre ? static_cast<const void*>(F.z) : x_in;
+  GR_TRY(launch_gemm_general(dt, F32, L.dqkv, 1, 3 * d, zin, d, 1, g.wqkv, d, 3 * d, d, T,
+                             GEMM_EPI_STORE, false, nullptr, 0, nullptr, 0, s));
+  if (!pre) {
+    return launch_gemm_general(dt, dt, L.dqkv, 3 * d, 1, w->wqkv, d, 1, dx, d, T, d, 3 * d,
+                               GEMM_EPI_STORE, false, nullptr, 0, nullptr, 0, s);
+  }
+  GR_TRY(launch_gemm_general(dt, dt, L.dqkv, 3 * d, 1, w->wqkv, d, 1, L.dz, d, T, d, 3 * d,
+                             GEMM_EPI_STORE, false, nullptr, 0, nullptr, 0, s));
+  GR_TRY(launch_fill_f32(g.g1, d, 0.f, s));
+  return launch_rmsnorm_bwd(dt, x_in, w->g1, L.dz, L.dx1, dx, g.g1, T, d, s);
+}
+
+genrank_status genrank_linear(int32_t dtype, const void* x, int64_t ldx, const void* w,
+                              int64_t ldw, void* y, int64_t ldy, int64_t M, int32_t N, int32_t K,
+                              int32_t epilogue, const void* residual, int64_t ldr, void* pre,
+                              int64_t ldpre, genrank_stream_t stream) {
+  if (dtype != GENRANK_F32 && dtype != GENRANK_BF16) return GENRANK_E_DTYPE;
+  if (!x || !w || !y) return GENRANK_E_ARG;
+  if (M < 0 || N < 1 || K < 1 || M >= (int64_t(1) << 31)) return GENRANK_E_SHAPE;
+  if (ldx < K || ldw < K || ldy < N) return GENRANK_E_SHAPE;
+  int epi;
+  switch (epilogue) {
+    case GENRANK_EPI_NONE: epi = GEMM_EPI_STORE; break;
+    case GENRANK_EPI_RESIDUAL:
+      if (!residual || ldr < N) return GENRANK_E_ARG;
+      epi = GEMM_EPI_RESID;
+      break;
+    case GENRANK_EPI_SILU:
+      if (pre && ldpre < N) return GENRANK_E_SHAPE;
+      epi = GEMM_EPI_SILU;
+      break;
+    default: return GENRANK_E_ARG;
+  }
+  return launch_gemm_nt(dtype, x, ldx, w, ldw, y, ldy, static_cast<int>(M), N, K, epi, residual, ldr,
+                        pre, ldpre, S(stream));
+}
+
+genrank_status genrank_head_fwd(const genrank_batch* b, const void* x, const float* g_final,
+                                const float* w_head, const float* b_head, int32_t n_tasks,
+                                float* logits, genrank_stream_t stream) {
+  GR_TRY(check_batch(b));
+  if (!x || !g_final || !w_head || !b_head || !logits) return GENRANK_E_ARG;
+  if (n_tasks < 1 || n_tasks > 8) return GENRANK_E_SHAPE;
+  return launch_head_fwd(b->dtype, x, b->total_hist, static_cast<int64_t>(b->B) * b->m, b->d,
+                         g_final, w_head, b_head, n_tasks, logits, S(stream));
+}
+
+genrank_status genrank_head_bwd(const genrank_batch* b, const void* x, const float* g_final,
+                                const float* w_head, int32_t n_tasks, const float* dlogits,
+                                void* dx, float* dg_final, float* dw_head, float* db_head,
+                                genrank_stream_t stream) {
+  GR_TRY(check_batch(b));
+  if (!x || !g_final || !w_head || !dlogits || !dx || !dg_final || !dw_head || !db_head)
+    return GENRANK_E_ARG;
+  if (n_tasks < 1 || n_tasks > 4) return GENRANK_E_SHAPE;
+  if (b->d > 1024) return GENRANK_E_SHAPE;
+  const hipStream_t s = S(stream);
+  GR_TRY(launch_fill_zero(b->dtype, dx, b->total_hist * b->d, s));
+  GR_TRY(launch_fill_f32(dg_final, b->d, 0.f, s));
+  GR_TRY(launch_fill_f32(dw_head, static_cast<int64_t>(n_tasks) * b->d, 0.f, s));
+  GR_TRY(launch_fill_f32(db_head, n_tasks, 0.f, s));
+  return launch_head_bwd(b->dtype, x, b->total_hist, static_cast<int64_t>(b->B) * b->m, b->d,
+                         g_final, w_head, n_tasks, dlogits, dx, dg_final, dw_head, db_head, s);
+}
+
+genrank_status genrank_bce_loss(int64_t n, int32_t n_tasks, const float* logits,
+                                const float* labels, float* loss, float* dlogits,
+                                genrank_stream_t stream) {
+  if (!logits || !labels || !loss || !dlogits) return GENRANK_E_ARG;
+  if (n < 1 || n_tasks < 1) return GENRANK_E_ARG;
+  return launch_bce(n, n_tasks, logits, labels, loss, dlogits, S(stream));
+}
+
+genrank_status genrank_debug_mask(const genrank_batch* b, const int32_t* offsets, int32_t user,
+                                  int32_t L_cap, uint8_t* out, genrank_stream_t stream) {
+  GR_TRY(check_batch(b));
+  if (!offsets || !out) return GENRANK_E_ARG;
+  if (user < 0 || user >= b->B || L_cap < 1) return GENRANK_E_ARG;
+  return launch_debug_mask(offsets, b->m, user, L_cap, out, S(stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,79 @@
+// Launchers shared between the kernel files and the C ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "genrank.h"
+
+namespace genrank {
+
+enum { GEMM_EPI_STORE = 0, GEMM_EPI_RESID = 1, GEMM_EPI_SILU = 2, GEMM_EPI_F32 = 3 };
+
+constexpr float RMS_EPS = 1e-6f;
+
+genrank_status check_batch(const genrank_batch* b);
+size_t dtype_size(int dtype);
+
+// embedding
+genrank_status check_embed_args(const genrank_batch* b, const genrank_inputs* in,
+                                const genrank_tables* t);
+genrank_status launch_embed_sum(const genrank_batch* b, const genrank_inputs* in,
+                                const genrank_tables* t, void* out, hipStream_t stream);
+genrank_status launch_debug_indices(const genrank_batch* b, const genrank_inputs* in,
+                                    const genrank_tables* t, int32_t* out, hipStream_t stream);
+genrank_status launch_embed_bwd(const genrank_batch* b, const genrank_inputs* in,
+                                const genrank_tables* t, const void* dx, float* g_item,
+                                float* g_action, float* g_pos, float* g_ri, float* g_rt,
+                                hipStream_t stream);
+
+// attention
+genrank_status check_attn_args(const genrank_batch* b, const int32_t* offsets, const int64_t* ts,
+                               const int64_t* req, genrank_alibi alibi, const void* q,
+                               const void* k, const void* v, int64_t ld_qkv, const void* o,
+                               int64_t ld_o);
+genrank_status launch_attn_fwd(const genrank_batch* b, const int32_t* offsets, const int64_t* ts,
+                               const int64_t* req, genrank_alibi alibi, const void* q,
+                               const void* k, const void* v, int64_t ld_qkv, void* o,
+                               int64_t ld_o, float* lse, hipStream_t stream);
+genrank_status launch_debug_mask(const int32_t* offsets, int m, int user, int L_cap, uint8_t* out,
+                                 hipStream_t stream);
+size_t attn_bwd_workspace(const genrank_batch* b);
+genrank_status launch_attn_bwd(const genrank_batch* b, const int32_t* offsets, const int64_t* ts,
+                               const int64_t* req, genrank_alibi alibi, const void* q,
+                               const void* k, const void* v, int64_t ld_qkv, const void* o,
+                               const void* dout, int64_t ld_o, const float* lse, void* dq,
+                               void* dk, void* dv, int64_t ld_dqkv, int cand_only, void* ws,
+                               hipStream_t stream);
+
+// GEMM: C = A W^T (A [M, K], W [N, K]) with an epilogue
+genrank_status launch_gemm_nt(int dtype, const void* A, int64_t lda, const void* W, int64_t ldw,
+                              void* C, int64_t ldc, int M, int N, int K, int epi, const void* R,
+                              int64_t ldr, void* Cpre, int64_t ldpre, hipStream_t stream);
+// General strided GEMM: C[m, n] (+)= sum_k A[m*sam + k*sak] B[k*sbk + n*sbn]
+genrank_status launch_gemm_general(int in_dtype, int out_dtype, const void* A, int64_t sam,
+                                   int64_t sak, const void* Bm, int64_t sbk, int64_t sbn, void* C,
+                                   int64_t ldc, int M, int N, int K, int epi, bool accumulate,
+                                   const void* R, int64_t ldr, void* Cpre, int64_t ldpre,
+                                   hipStream_t stream);
+
+// row-wise ops
+genrank_status launch_rmsnorm(int dtype, const void* x, const float* g, void* y, int64_t rows,
+                              int d, hipStream_t stream);
+genrank_status launch_rmsnorm_bwd(int dtype, const void* x, const float* g, const void* dy,
+                                  const void* add, void* dx, float* dg, int64_t rows, int d,
+                                  hipStream_t stream);
+genrank_status launch_silu_bwd(int dtype, const void* a, const void* dy, void* da, int64_t n,
+                               hipStream_t stream);
+genrank_status launch_fill_f32(float* p, int64_t n, float v, hipStream_t stream);
+genrank_status launch_fill_zero(int dtype, void* p, int64_t n, hipStream_t stream);
+genrank_status launch_head_fwd(int dtype, const void* x, int64_t row0, int64_t rows, int d,
+                               const float* g, const float* w, const float* bias, int nt,
+                               float* logits, hipStream_t stream);
+genrank_status launch_head_bwd(int dtype, const void* x, int64_t row0, int64_t rows, int d,
+                               const float* g, const float* w, int nt, const float* dlogits,
+                               void* dx, float* dg, float* dw, float* db, hipStream_t stream);
+genrank_status launch_bce(int64_t n, int nt, const float* logits, const float* labels,
+                          float* loss, float* dlogits, hipStream_t stream);
+
+}  // namespace genrank

@@ -1,0 +1,132 @@
+"""GenRank forward / training step as a chain of C-ABI calls on one HIP stream.
+
+    embed-sum (five tables, fused index derivation)
+      -> L blocks (QKV GEMM -> masked ALiBi attention -> output GEMM [-> FFN])
+      -> action head at candidate rows -> [BCE at candidates -> backward]
+
+The class owns device weights and cached workspaces; every step runs in libgenrank's
+kernels.  Workspaces are allocated once per batch shape, outside any timed region.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import binding as B
+from .device import DTYPE_CODE, TORCH_DTYPE, DeviceHead, DeviceLayer, DeviceTables
+
+
+class GenRank:
+    def __init__(self, tables: DeviceTables, layers: list, H: int, head: DeviceHead = None,
+                 device="cuda"):
+        self.tables = tables
+        self.layers = layers
+        self.head = head
+        self.H = H
+        self.d = tables.d
+        self.dtype = tables.dtype
+        self.code = DTYPE_CODE[self.dtype]
+        self.device = device
+        self._ws = {}
+
+    @classmethod
+    def from_host(cls, cfg, tables, weights, slopes_pos, slopes_time, device="cuda"):
+        block = B.BLOCK_PRENORM if cfg.block == "prenorm" else B.BLOCK_ATTN_ONLY
+        dt = DeviceTables(tables, device)
+        layers = [DeviceLayer(lw, slopes_pos, slopes_time, block, device) for lw in weights.layers]
+        head = DeviceHead(weights, device) if cfg.block == "prenorm" else None
+        return cls(dt, layers, cfg.H, head, device)
+
+    # ---------------------------------------------------------------- helpers
+    def batch(self, inp) -> B.Batch:
+        return B.make_batch(inp.B, inp.m, self.d, self.H, inp.max_hist, inp.total_hist, self.code)
+
+    def _buf(self, key, nbytes):
+        t = self._ws.get(key)
+        if t is None or t.numel() < nbytes:
+            t = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=self.device)
+            self._ws[key] = t
+        return t
+
+    def act(self, rows, cols=None):
+        return torch.empty((rows, cols or self.d), dtype=TORCH_DTYPE[self.dtype], device=self.device)
+
+    # ---------------------------------------------------------------- forward
+    def embed(self, inp, x_out, stream=None):
+        B.genrank_embed_sum(self.batch(inp), inp.struct, self.tables.struct, x_out, stream)
+
+    def layer(self, i, inp, x_in, y_out, save=False, stream=None):
+        lay = self.layers[i]
+        bt = self.batch(inp)
+        nbytes = B.genrank_workspace_size(B.OP_LAYER_FWD, bt, lay.struct)
+        ws = self._buf(("fwd", i), nbytes)
+        B.genrank_layer_fwd(bt, lay.struct, inp.hist_offsets, inp.hist_ts, inp.req_ts, x_in, y_out,
+                            B.FWD_SAVE if save else 0, ws, nbytes, stream)
+        return ws
+
+    def forward(self, inp, save=False, stream=None, bufs=None):
+        """Returns (x_final, logits or None).  ``bufs`` may pass preallocated
+        {"x": [T, d], "y": [T, d], "logits": [B*m, n_tasks]} tensors."""
+        T = inp.rows
+        bufs = bufs or {}
+        x = bufs.get("x") if bufs.get("x") is not None else self.act(T)
+        self.embed(inp, x, stream)
+        xs = [x]
+        for i in range(len(self.layers)):
+            if self.layers[i].block == B.BLOCK_ATTN_ONLY:
+                y = bufs.get("y") if bufs.get("y") is not None else self.act(T)
+            else:
+                y = x if not save else self.act(T)
+            self.layer(i, inp, x, y, save, stream)
+            x = y
+            xs.append(x)
+        self._xs = xs
+        logits = None
+        if self.head is not None:
+            logits = bufs.get("logits")
+            if logits is None:
+                logits = torch.empty((inp.B * inp.m, self.head.n_tasks), dtype=torch.float32,
+                                     device=self.device)
+            B.genrank_head_fwd(self.batch(inp), x, self.head.g_final, self.head.w_head,
+                               self.head.b_head, self.head.n_tasks, logits, stream)
+        return x, logits
+
+    # ---------------------------------------------------------------- training
+    def train_step(self, inp, labels, stream=None):
+        """Forward with saved activations, BCE at candidates, full backward.  Returns
+        (loss tensor [1], logits, grads dict of f32 tensors)."""
+        x_final, logits = self.forward(inp, save=True, stream=stream)
+        bt = self.batch(inp)
+        dev, d = self.device, self.d
+        n = inp.B * inp.m
+        nt = self.head.n_tasks
+        loss = torch.empty(1, dtype=torch.float32, device=dev)
+        dlogits = torch.empty((n, nt), dtype=torch.float32, device=dev)
+        B.genrank_bce_loss(n, nt, logits, labels, loss, dlogits, stream)
+        f32 = lambda *s: torch.empty(s, dtype=torch.float32, device=dev)
+        grads = {"g_final": f32(d), "w_head": f32(nt, d), "b_head": f32(nt)}
+        dx = self.act(inp.rows)
+        B.genrank_head_bwd(bt, x_final, self.head.g_final, self.head.w_head, nt, dlogits, dx,
+                           grads["g_final"], grads["w_head"], grads["b_head"], stream)
+        grads["layers"] = [None] * len(self.layers)
+        for i in range(len(self.layers) - 1, -1, -1):
+            lay = self.layers[i]
+            lg = {"wqkv": f32(3 * d, d), "wo": f32(d, d)}
+            if lay.block == B.BLOCK_PRENORM:
+                lg.update(w1=f32(lay.ffn_dim, d), w2=f32(d, lay.ffn_dim), g1=f32(d), g2=f32(d))
+            gstruct = B.make_layer_grads(lg["wqkv"], lg["wo"], lg.get("w1"), lg.get("w2"),
+                                         lg.get("g1"), lg.get("g2"))
+            nb = B.genrank_workspace_size(B.OP_LAYER_BWD, bt, lay.struct)
+            wsb = self._buf(("bwd",), nb)
+            nf = B.genrank_workspace_size(B.OP_LAYER_FWD, bt, lay.struct)
+            B.genrank_layer_bwd(bt, lay.struct, inp.hist_offsets, inp.hist_ts, inp.req_ts,
+                                self._xs[i], self._ws[("fwd", i)], dx, dx, gstruct,
+                                1 if i == len(self.layers) - 1 else 0, wsb, nb, stream)
+            del nf
+            grads["layers"][i] = lg
+        t = self.tables
+        tg = {k: torch.zeros(getattr(t, k).shape, dtype=torch.float32, device=dev)
+              for k in ("item", "action", "pos", "ri", "rt")}
+        B.genrank_embed_bwd(bt, inp.struct, t.struct, dx, tg["item"], tg["action"], tg["pos"],
+                            tg["ri"], tg["rt"], stream)
+        grads["tables"] = tg
+        return loss, logits, grads

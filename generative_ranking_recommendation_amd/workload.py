@@ -1,0 +1,49 @@
+"""Algorithmic work of the GenRank hot path, for measurement (no GPU needed).
+
+Attention: user u with N history actions and m candidates has N(N+1)/2 causal history
+pairs plus m(N+1) candidate pairs (all history + itself); each pair costs 2*d flops for
+QK^T and 2*d for PV over all heads (4*d per pair).  Candidate x candidate pairs other than
+the diagonal are not work: the mask removes them.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def attention_pairs(lengths, m: int) -> int:
+    n = np.asarray(lengths, dtype=np.int64)
+    return int((n * (n + 1) // 2).sum() + m * (n + 1).sum())
+
+
+def attention_fwd_flops(lengths, m: int, d: int) -> int:
+    return 4 * d * attention_pairs(lengths, m)
+
+
+def attention_hbm_floor_bytes(rows: int, d: int, elem: int = 2, lse: bool = True, H: int = 1) -> int:
+    """Read Q, K, V once and write O once (+ the f32 log-sum-exp)."""
+    return rows * d * elem * 4 + (rows * H * 4 if lse else 0)
+
+
+def gemm_flops(M: int, N: int, K: int) -> int:
+    return 2 * M * N * K
+
+
+def gather_compulsory_bytes(rows: int, d: int, elem: int, unique_items: int, small_rows: int,
+                            index_bytes: int) -> int:
+    """Embedding gather-sum: one write of every output row, each distinct item row read once,
+    the small tables read once, and the per-row index inputs."""
+    return rows * d * elem + unique_items * d * elem + small_rows * d * elem + index_bytes
+
+
+def gather_logical_bytes(rows: int, d: int, elem: int, index_bytes: int) -> int:
+    """Five table rows read and one row written per token."""
+    return rows * d * elem * 6 + index_bytes
+
+
+def interleaved_tokens(n_c: int, m: int = 0) -> int:
+    """HSTU-style interleaving: one token per item and one per action, then candidates."""
+    return 2 * n_c + m
+
+
+def action_oriented_tokens(n_c: int, m: int = 0) -> int:
+    return n_c + m

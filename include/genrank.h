@@ -1,0 +1,323 @@
+/*
+ * genrank.h -- C ABI of the MI355X (gfx950) GenRank ranking hot path.
+ *
+ * GenRank ("Towards Large-scale Generative Ranking") scores a request's candidates
+ * against a user's chronological action history.  One token per history action is the
+ * sum of five embeddings (item, action, position, request index, pre-request time gap);
+ * each candidate token uses the mask-action embedding and shares one position with the
+ * other candidates of its request.  Tokens feed causal attention with ALiBi position and
+ * time biases and a candidate mask: history tokens attend causally, each candidate sees
+ * the whole history and itself, never another candidate.
+ *
+ * Page titles cited below:
+ *   [GR-zh]   "一、 GenRank [2025]" (huaxiaozhuan.com)
+ *   [GR-note] "生成式排序 —— 小红书 GenRank 精读笔记" (wln20.github.io)
+ *   [FR-en]   "The Overall Generative Ranking Paradigm" (fun-rec mdbook, chapter 7.2)
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Row layout.  B users; user u has N_u = hist_offsets[u+1] - hist_offsets[u] history
+ *    actions and m candidates.  Rows [0, T_h) are history rows, user after user
+ *    (T_h = hist_offsets[B]); row T_h + u*m + k is candidate k of user u.  T = T_h + B*m.
+ *  - Pointers.  Unless a parameter says "host", every array pointer is DEVICE memory
+ *    owned by the caller.  The library allocates nothing and keeps no pointer after a
+ *    call returns.  Scratch memory comes from a caller-supplied workspace whose size
+ *    genrank_workspace_size() reports.
+ *  - Streams.  Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *    is asynchronous; nothing synchronises except genrank_validate_host (host only).
+ *  - Errors.  Host-side argument checks run before anything is enqueued; on error the
+ *    call returns a negative genrank_status, enqueues nothing and leaves outputs
+ *    untouched.  A failed kernel launch returns GENRANK_E_HIP.  Data-dependent
+ *    preconditions (sorted timestamps, ids in range) are NOT checked on the hot path:
+ *    genrank_validate_host checks host copies of the inputs.
+ *  - Dtypes.  Activations and tables are f32 or bf16 (genrank_dtype); accumulation is
+ *    always f32; softmax statistics (LSE) are f32; timestamps are int64 seconds.
+ *  - Matrices are row-major.  A weight W of shape [out, in] is applied as y = x W^T.
+ *  - Reentrancy.  Stateless; calls on different streams may overlap.
+ */
+#ifndef GENRANK_H
+#define GENRANK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__) || defined(__clang__)
+#define GENRANK_API __attribute__((visibility("default")))
+#else
+#define GENRANK_API
+#endif
+
+#define GENRANK_VERSION_MAJOR 0
+#define GENRANK_VERSION_MINOR 1
+#define GENRANK_MAX_HEADS 16
+
+typedef void* genrank_stream_t; /* hipStream_t */
+
+typedef enum {
+  GENRANK_OK = 0,
+  GENRANK_E_ARG = -1,       /* null pointer or invalid scalar argument */
+  GENRANK_E_SHAPE = -2,     /* inconsistent sizes (H*dh != d, unsupported d/dh, ...) */
+  GENRANK_E_DTYPE = -3,     /* unsupported dtype for this entry point */
+  GENRANK_E_UNSORTED = -4,  /* offsets or timestamps out of order (validate only) */
+  GENRANK_E_RANGE = -5,     /* an id or time difference out of range (validate only) */
+  GENRANK_E_WORKSPACE = -6, /* workspace missing or smaller than required */
+  GENRANK_E_HIP = -7        /* a HIP runtime call or kernel launch failed */
+} genrank_status;
+
+typedef enum { GENRANK_F32 = 0, GENRANK_BF16 = 1 } genrank_dtype;
+
+typedef enum { GENRANK_BLOCK_ATTN_ONLY = 0, GENRANK_BLOCK_PRENORM = 1 } genrank_block;
+
+typedef enum {
+  GENRANK_OP_EMBED_SUM = 0,
+  GENRANK_OP_ATTN_FWD = 1,
+  GENRANK_OP_ATTN_BWD = 2,
+  GENRANK_OP_LAYER_FWD = 3,
+  GENRANK_OP_LAYER_BWD = 4
+} genrank_op;
+
+/* Batch geometry.  total_hist and max_hist are host copies of hist_offsets[B] and
+ * max_u N_u so that no device-to-host copy is needed; they must match the device data. */
+typedef struct {
+  int32_t B;          /* users, >= 1 */
+  int32_t m;          /* candidates per user, >= 0 */
+  int32_t d;          /* model dim */
+  int32_t H;          /* heads, 1..GENRANK_MAX_HEADS */
+  int32_t dh;         /* head dim; H*dh == d */
+  int32_t max_hist;   /* max_u N_u */
+  int64_t total_hist; /* T_h = sum_u N_u */
+  int32_t dtype;      /* genrank_dtype of activations and embedding tables */
+  int32_t reserved;
+} genrank_batch;
+
+/* Per-user chronological histories and the candidates of one request
+ * ([GR-zh] section 1.4.1: items x_i with actions a_i at timestamps t_i). */
+typedef struct {
+  const int32_t* hist_offsets; /* [B+1], hist_offsets[0] = 0, non-decreasing */
+  const int32_t* hist_items;   /* [T_h] item ids in [0, n_item) */
+  const int32_t* hist_actions; /* [T_h] action ids in [0, n_action) */
+  const int64_t* hist_ts;      /* [T_h] seconds, non-decreasing within a user */
+  const int32_t* cand_items;   /* [B*m] candidate item ids */
+  const int64_t* req_ts;       /* [B] request time of the candidates, > the user's last ts */
+} genrank_inputs;
+
+/* The five embedding tables ([GR-zh] section 1.4.2, five-term input representation),
+ * each row-major [rows, d] in batch.dtype. */
+typedef struct {
+  const void* item;   /* psi     [n_item, d] */
+  const void* action; /* phi     [n_action + 1, d]; row n_action is the mask-action row M */
+  const void* pos;    /* Omega_pe [n_pos, d]; slot = min(position, n_pos - 1) */
+  const void* ri;     /* Omega_ri [n_ri, d]; slot = min(request index - 1, n_ri - 1) */
+  const void* rt;     /* Omega_rt [n_rt, d]; slot = time-gap bucket */
+  const int64_t* rt_bounds; /* [n_rt - 1] non-decreasing integer bucket edges (seconds):
+                               bucket = #{k : rt_bounds[k] <= gap}; 0 = no earlier request */
+  int64_t n_item;
+  int32_t n_action;
+  int32_t n_pos;
+  int32_t n_ri;
+  int32_t n_rt;
+} genrank_tables;
+
+/* ALiBi slopes, HOST arrays of H floats: the score of query i and key j in head h gets
+ * -slopes_pos[h]*|p_i - p_j| - slopes_time[h]*|tau_i - tau_j|, p the position id (all
+ * candidates of a request share p = N_u) and tau the timestamp in seconds relative to
+ * the user's first history timestamp ([GR-zh] section 1.4.2, ALiBi score; [FR-en]
+ * section 7.2.2, position-and-time bias). */
+typedef struct {
+  const float* slopes_pos;  /* host [H] */
+  const float* slopes_time; /* host [H] */
+} genrank_alibi;
+
+/* Weights of one block.  GENRANK_BLOCK_ATTN_ONLY: y = Wo . attn(Wqkv . x).
+ * GENRANK_BLOCK_PRENORM: x1 = x + Wo . attn(Wqkv . rmsnorm(x)*g1);
+ *                         y = x1 + W2 . silu(W1 . rmsnorm(x1)*g2).
+ * Matrices are in batch.dtype; gains are f32. */
+typedef struct {
+  const void* wqkv;  /* [3d, d]: rows [0,d) -> Q, [d,2d) -> K, [2d,3d) -> V; head h at h*dh */
+  const void* wo;    /* [d, d] */
+  const void* w1;    /* [ffn_dim, d] (PRENORM) */
+  const void* w2;    /* [d, ffn_dim] (PRENORM) */
+  const float* g1;   /* [d] (PRENORM) */
+  const float* g2;   /* [d] (PRENORM) */
+  int32_t ffn_dim;   /* PRENORM: hidden size of the FFN, multiple of 64 */
+  int32_t block;     /* genrank_block */
+  genrank_alibi alibi;
+} genrank_layer_weights;
+
+/* Gradients of one block, f32, same shapes as the weights.  Overwritten (not added). */
+typedef struct {
+  float* wqkv;
+  float* wo;
+  float* w1;
+  float* w2;
+  float* g1;
+  float* g2;
+} genrank_layer_grads;
+
+/* ------------------------------------------------------------------ informational */
+
+/* Human-readable name of a status code (static storage). */
+GENRANK_API const char* genrank_status_string(int status);
+/* (major << 16) | minor */
+GENRANK_API int32_t genrank_version(void);
+
+/* Bytes of workspace `op` needs for this batch (and, for the layer ops, this block:
+ * `w` may be NULL for the other ops).  Writes *bytes; returns E_ARG on null pointers. */
+GENRANK_API genrank_status genrank_workspace_size(int32_t op, const genrank_batch* batch,
+                                      const genrank_layer_weights* w, size_t* bytes);
+
+/* Checks HOST copies of the inputs against the preconditions the kernels assume:
+ * hist_offsets[0] == 0 and non-decreasing (E_UNSORTED), timestamps non-decreasing per
+ * user and req_ts[u] > the user's last timestamp (E_UNSORTED), ids in range and
+ * req_ts[u] - first timestamp < 2^24 s so that relative times are exact in f32
+ * (E_RANGE), rt_bounds non-decreasing (E_UNSORTED).  All pointers are HOST memory here.
+ * Writes the first offending row (or -1) to *bad_row when bad_row is not NULL. */
+GENRANK_API genrank_status genrank_validate_host(const genrank_batch* batch, const genrank_inputs* in,
+                                     const genrank_tables* tables, int64_t* bad_row);
+
+/* ------------------------------------------------------------------ hot path */
+
+/* Fused index derivation + five-table gather-sum ([GR-zh] section 1.4.2, the input
+ * representation e = psi(x) + phi(a) + E_pe + E_ri + E_rt; section 1.4.1 for the
+ * mask-action row of candidates).  Per row, in one kernel:
+ *   action slot a_i (history) or n_action (candidates);
+ *   position p = i - hist_offsets[u] (history) or N_u (candidates), slot min(p, n_pos-1);
+ *   request index = number of distinct timestamps in the user's prefix (a candidate's
+ *   prefix is the whole history plus its request), slot min(ri-1, n_ri-1);
+ *   gap = t - (largest earlier distinct timestamp), bucket #{k: rt_bounds[k] <= gap},
+ *   0 when there is no earlier request.
+ * The five rows are summed in f32 and stored once in batch.dtype.
+ * x_out: [T, d] in batch.dtype.  d must be a multiple of 8 (bf16) / 4 (f32). */
+GENRANK_API genrank_status genrank_embed_sum(const genrank_batch* batch, const genrank_inputs* in,
+                                 const genrank_tables* tables, void* x_out,
+                                 genrank_stream_t stream);
+
+/* Masked ALiBi flash attention forward ([GR-zh] section 1.4.2, ALiBi score with the
+ * 1/sqrt(head dim) scale; [FR-en] sections 7.2.1-7.2.2, causal history mask, candidate
+ * mask, position and time bias).  For each user and head:
+ *   score_ij = q_i.k_j/sqrt(dh) - sp_h|p_i-p_j| - st_h|tau_i-tau_j| on allowed pairs,
+ *   allowed = (i history and j <= i) or (i candidate and (j history or j == i)),
+ *   o_i = softmax_j(score_ij) v_j, lse_i = log sum_j exp(score_ij)  (natural log).
+ * Positions, times and the mask are derived in-kernel from hist_offsets, hist_ts and
+ * req_ts; the bias is computed in registers and no T x T array is formed.
+ * q, k, v: [T, ld_qkv] rows, head h at columns [h*dh, (h+1)*dh) of each (they may be
+ * three views into one [T, 3d] buffer).  o: [T, ld_o], head h at h*dh.
+ * lse: [T, H] f32 or NULL.  bf16 requires dh == 64; f32 requires dh <= 64. */
+GENRANK_API genrank_status genrank_attn_fwd(const genrank_batch* batch, const int32_t* hist_offsets,
+                                const int64_t* hist_ts, const int64_t* req_ts,
+                                genrank_alibi alibi, const void* q, const void* k,
+                                const void* v, int64_t ld_qkv, void* o, int64_t ld_o,
+                                float* lse, genrank_stream_t stream);
+
+/* Backward of genrank_attn_fwd (ALiBi is parameter-free, so it has no gradient,
+ * [GR-zh] section 1.4.2).  Inputs are the forward's q, k, v, o, its lse (required) and
+ * dout = dL/do ([T, ld_o]).  Writes dq, dk, dv ([T, ld_dqkv], head h at h*dh; they may
+ * be views into one [T, 3d] buffer) in batch.dtype.  When cand_only_dout != 0 the
+ * caller asserts that dout is zero on every history row (loss at candidate positions
+ * only, [GR-zh] section 1.3.1, at the last block) and the history query rows are
+ * skipped.  ws: workspace of genrank_workspace_size(GENRANK_OP_ATTN_BWD) bytes. */
+GENRANK_API genrank_status genrank_attn_bwd(const genrank_batch* batch, const int32_t* hist_offsets,
+                                const int64_t* hist_ts, const int64_t* req_ts,
+                                genrank_alibi alibi, const void* q, const void* k,
+                                const void* v, int64_t ld_qkv, const void* o,
+                                const void* dout, int64_t ld_o, const float* lse, void* dq,
+                                void* dk, void* dv, int64_t ld_dqkv, int32_t cand_only_dout,
+                                void* ws, size_t ws_bytes, genrank_stream_t stream);
+
+/* One block forward (see genrank_layer_weights for the two block forms): the dense
+ * projections (QKV, output, FFN) as bf16 MFMA GEMMs with fused residual / SiLU
+ * epilogues, RMSNorm, and genrank_attn_fwd between them.
+ * x_in, y_out: [T, d] in batch.dtype; y_out may equal x_in (inference only: the backward
+ * needs the block input).  ws: genrank_workspace_size(GENRANK_OP_LAYER_FWD) bytes.
+ * flags: GENRANK_FWD_SAVE makes the workspace keep every activation genrank_layer_bwd
+ * needs (keep it untouched until then); without it the FFN pre-activation is not stored. */
+#define GENRANK_FWD_SAVE 1
+GENRANK_API genrank_status genrank_layer_fwd(const genrank_batch* batch, const genrank_layer_weights* w,
+                                 const int32_t* hist_offsets, const int64_t* hist_ts,
+                                 const int64_t* req_ts, const void* x_in, void* y_out,
+                                 int32_t flags, void* ws, size_t ws_bytes,
+                                 genrank_stream_t stream);
+
+/* Backward of one block.  x_in is the block's forward input, ws the workspace the
+ * forward filled; dy: [T, d] gradient of the block output; dx: [T, d] (may equal dy).
+ * ws_bwd: genrank_workspace_size(GENRANK_OP_LAYER_BWD) bytes.  Gradients are f32. */
+GENRANK_API genrank_status genrank_layer_bwd(const genrank_batch* batch, const genrank_layer_weights* w,
+                                 const int32_t* hist_offsets, const int64_t* hist_ts,
+                                 const int64_t* req_ts, const void* x_in, const void* ws,
+                                 const void* dy, void* dx, genrank_layer_grads grads,
+                                 int32_t cand_only_dout, void* ws_bwd, size_t ws_bwd_bytes,
+                                 genrank_stream_t stream);
+
+/* Dense projection of the block (the QKV, output and FFN layers of
+ * genrank_layer_weights): y[M, N] = x[M, K] . w[N, K]^T, f32 accumulation, then
+ *   GENRANK_EPI_NONE:     y = acc
+ *   GENRANK_EPI_RESIDUAL: y = acc + residual   (residual [M, ldr], may equal y)
+ *   GENRANK_EPI_SILU:     y = silu(acc), and pre = acc when pre is not NULL.
+ * bf16 runs on MFMA when N % 128 == 0, K % 64 == 0 and the leading dimensions are
+ * multiples of 8; other shapes and f32 use a plain tiled kernel. */
+#define GENRANK_EPI_NONE 0
+#define GENRANK_EPI_RESIDUAL 1
+#define GENRANK_EPI_SILU 2
+GENRANK_API genrank_status genrank_linear(int32_t dtype, const void* x, int64_t ldx, const void* w,
+                                          int64_t ldw, void* y, int64_t ldy, int64_t M, int32_t N,
+                                          int32_t K, int32_t epilogue, const void* residual,
+                                          int64_t ldr, void* pre, int64_t ldpre,
+                                          genrank_stream_t stream);
+
+/* Per-candidate action logits ([GR-zh] section 1.2: predictions for a set of predefined
+ * tasks): logits[c, t] = (rmsnorm(x[T_h + c]) * g_final) . w_head[t] + b_head[t].
+ * x: [T, d] in batch.dtype; g_final [d], w_head [n_tasks, d], b_head [n_tasks] f32;
+ * logits: [B*m, n_tasks] f32.  n_tasks in 1..8. */
+GENRANK_API genrank_status genrank_head_fwd(const genrank_batch* batch, const void* x, const float* g_final,
+                                const float* w_head, const float* b_head, int32_t n_tasks,
+                                float* logits, genrank_stream_t stream);
+
+/* Backward of genrank_head_fwd.  dx: [T, d] in batch.dtype; history rows are set to
+ * zero (the loss is taken at candidate positions only, [GR-zh] section 1.3.1).
+ * dg_final [d], dw_head [n_tasks, d], db_head [n_tasks]: f32, overwritten. */
+GENRANK_API genrank_status genrank_head_bwd(const genrank_batch* batch, const void* x, const float* g_final,
+                                const float* w_head, int32_t n_tasks, const float* dlogits,
+                                void* dx, float* dg_final, float* dw_head, float* db_head,
+                                genrank_stream_t stream);
+
+/* Mean sigmoid binary cross-entropy over n rows x n_tasks logits and its gradient:
+ * loss[0] = mean(softplus(z) - y z); dlogits = (sigmoid(z) - y) / (n * n_tasks).
+ * logits, labels, dlogits: [n, n_tasks] f32; loss: [1] f32 (device). */
+GENRANK_API genrank_status genrank_bce_loss(int64_t n, int32_t n_tasks, const float* logits,
+                                const float* labels, float* loss, float* dlogits,
+                                genrank_stream_t stream);
+
+/* Adjoint of genrank_embed_sum: each table's f32 gradient receives dx[row] at the row's
+ * slot.  d_* are [rows, d] f32 and are ACCUMULATED into (zero them first).
+ * dx: [T, d] in batch.dtype.  Uses f32 atomics, so the summation order is not fixed. */
+GENRANK_API genrank_status genrank_embed_bwd(const genrank_batch* batch, const genrank_inputs* in,
+                                 const genrank_tables* tables, const void* dx, float* d_item,
+                                 float* d_action, float* d_pos, float* d_ri, float* d_rt,
+                                 genrank_stream_t stream);
+
+/* ------------------------------------------------------------------ debug exports */
+
+/* The per-row indices genrank_embed_sum derives, written as int32 out[6][T]:
+ * out[0] action slot, out[1] position id (unclamped), out[2] position slot,
+ * out[3] request index (unclamped), out[4] request-index slot, out[5] time-gap bucket. */
+GENRANK_API genrank_status genrank_debug_indices(const genrank_batch* batch, const genrank_inputs* in,
+                                     const genrank_tables* tables, int32_t* out,
+                                     genrank_stream_t stream);
+
+/* The attention mask of user `user` as the attention kernels evaluate it, on sequence
+ * slots (0..N_u-1 history, N_u..N_u+m-1 candidates): out[i*L_cap + j] = 1 if i and j are
+ * below L = N_u + m and slot i may attend slot j, else 0.  out: [L_cap * L_cap] uint8;
+ * L_cap >= 1 (pass max_hist + m to see every user whole). */
+GENRANK_API genrank_status genrank_debug_mask(const genrank_batch* batch, const int32_t* hist_offsets,
+                                  int32_t user, int32_t L_cap, uint8_t* out,
+                                  genrank_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GENRANK_H */
