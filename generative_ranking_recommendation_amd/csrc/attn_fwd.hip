@@ -102,7 +102,6 @@ __global__ void __launch_bounds__(256) attn_fwd_bf16_kernel(AttnArgs a) {
   const int wave = tid >> 6;
   const int l16 = lane & 15, g4 = lane >> 4;
   const float sp2 = a.sp2[h], st2 = a.st2[h];
-  const int64_t t0 = (N > 0) ? a.ts[off] : a.req[u];
   // bias reference point: the candidates' shared (p, tau), or the tile's first query
   const int p_ref = is_cand ? N : q0;
   const int64_t ts_ref = is_cand ? a.req[u] : a.ts[off + q0];
@@ -112,12 +111,13 @@ __global__ void __launch_bounds__(256) attn_fwd_bf16_kernel(AttnArgs a) {
   const bool q_valid = qi_local < nq;
   const int64_t qrow = qrow0 + qi_local;
   const int q_slot = is_cand ? (N + q0 + qi_local) : (q0 + qi_local);  // sequence slot
+  // lanes past the tile's last query read that query's row (never stored)
+  const int64_t qrow_ld = qrow0 + min(qi_local, nq - 1);
   bf16x8_t qf[2];
   {
-    uint4 z = make_uint4(0, 0, 0, 0);
-    const bf16_t* qp = a.q + qrow * a.ld_qkv + h * DH + g4 * 8;
-    qf[0] = as_bf16x8(q_valid ? *reinterpret_cast<const uint4*>(qp) : z);
-    qf[1] = as_bf16x8(q_valid ? *reinterpret_cast<const uint4*>(qp + 32) : z);
+    const bf16_t* qp = a.q + qrow_ld * a.ld_qkv + h * DH + g4 * 8;
+    qf[0] = as_bf16x8(*reinterpret_cast<const uint4*>(qp));
+    qf[1] = as_bf16x8(*reinterpret_cast<const uint4*>(qp + 32));
   }
 
   f32x4_t accO[4];
@@ -125,8 +125,8 @@ __global__ void __launch_bounds__(256) attn_fwd_bf16_kernel(AttnArgs a) {
   if (is_cand) {
     // seed with the candidate's own key: bias 0 (same position and time as p_ref)
     float dot = 0.f;
-    if (q_valid) {
-      const bf16_t* kp = a.k + qrow * a.ld_qkv + h * DH + g4 * 8;
+    {
+      const bf16_t* kp = a.k + qrow_ld * a.ld_qkv + h * DH + g4 * 8;
       float kf[8], qv[8];
       uint4 kk = *reinterpret_cast<const uint4*>(kp);
       unpack8(kk, kf);
@@ -145,13 +145,9 @@ __global__ void __launch_bounds__(256) attn_fwd_bf16_kernel(AttnArgs a) {
     lsum = (g4 == 0) ? 1.f : 0.f;
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
-      if (q_valid) {
-        const uint2 vv = *reinterpret_cast<const uint2*>(a.v + qrow * a.ld_qkv + h * DH + nb * 16 + g4 * 4);
-        accO[nb] = f32x4_t{__uint_as_float(vv.x << 16), __uint_as_float(vv.x & 0xFFFF0000u),
-                           __uint_as_float(vv.y << 16), __uint_as_float(vv.y & 0xFFFF0000u)};
-      } else {
-        accO[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      }
+      const uint2 vv = *reinterpret_cast<const uint2*>(a.v + qrow_ld * a.ld_qkv + h * DH + nb * 16 + g4 * 4);
+      accO[nb] = f32x4_t{__uint_as_float(vv.x << 16), __uint_as_float(vv.x & 0xFFFF0000u),
+                         __uint_as_float(vv.y << 16), __uint_as_float(vv.y & 0xFFFF0000u)};
     }
   } else {
     m2 = -1e30f;
@@ -160,48 +156,52 @@ __global__ void __launch_bounds__(256) attn_fwd_bf16_kernel(AttnArgs a) {
     for (int nb = 0; nb < 4; ++nb) accO[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 
-  // ---- K/V tile staging: 2 chunks of 16 B per operand per thread + one key's bias
-  uint4 rk[2], rv[2];
-  float rw = 0.f;
+  // ---- K/V tile staging: 2 chunks of 16 B per operand per thread + one key's timestamp.
+  // Keys past the history end read the last history row (finite values; the mask gives
+  // them probability 0).  The timestamp is only consumed in stash(), after the tile's
+  // math, so the prefetch stays in flight.
+  // Named registers (an indexed array here would be placed in scratch memory).
+  uint4 rk0, rk1, rv0, rv1;
+  int64_t rts = 0;
+  int fetched_base = 0;
+  const int skey = tid >> 3;           // chunk 0: key skey, chunk 1: key skey + 32
+  const int sd0 = (tid & 7) * 8;
+  const bf16_t* kbase = a.k + h * DH + sd0;
+  const bf16_t* vbase = a.v + h * DH + sd0;
   auto fetch = [&](int kt) {
     const int base = kt * AK;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = tid + i * 256;
-      const int key = c >> 3;
-      const int d0 = (c & 7) * 8;
-      const bool ok = base + key < N;
-      const int64_t row = off + base + key;
-      rk[i] = ok ? *reinterpret_cast<const uint4*>(a.k + row * a.ld_qkv + h * DH + d0) : make_uint4(0, 0, 0, 0);
-      rv[i] = ok ? *reinterpret_cast<const uint4*>(a.v + row * a.ld_qkv + h * DH + d0) : make_uint4(0, 0, 0, 0);
-    }
-    if (tid < AK) {
-      const int j = base + tid;
-      rw = 0.f;
-      if (j < N) {
-        const float dp = static_cast<float>(j - p_ref);
-        const float dt = static_cast<float>(a.ts[off + j] - ts_ref);
-        rw = sp2 * dp + st2 * dt;
-      }
-    }
+    fetched_base = base;
+    const int64_t r0 = off + min(base + skey, N - 1);
+    const int64_t r1 = off + min(base + skey + 32, N - 1);
+    rk0 = *reinterpret_cast<const uint4*>(kbase + r0 * a.ld_qkv);
+    rk1 = *reinterpret_cast<const uint4*>(kbase + r1 * a.ld_qkv);
+    rv0 = *reinterpret_cast<const uint4*>(vbase + r0 * a.ld_qkv);
+    rv1 = *reinterpret_cast<const uint4*>(vbase + r1 * a.ld_qkv);
+    if (tid < AK) rts = a.ts[off + min(base + tid, N - 1)];
+  };
+  auto put_vt = [&](int buf, int key, const uint4 vv) {
+    const int slot = vt_slot(key);
+    bf16_t* col = &sVt[buf][sd0 * VLD + slot];
+    col[0 * VLD] = static_cast<bf16_t>(vv.x & 0xFFFFu);
+    col[1 * VLD] = static_cast<bf16_t>(vv.x >> 16);
+    col[2 * VLD] = static_cast<bf16_t>(vv.y & 0xFFFFu);
+    col[3 * VLD] = static_cast<bf16_t>(vv.y >> 16);
+    col[4 * VLD] = static_cast<bf16_t>(vv.z & 0xFFFFu);
+    col[5 * VLD] = static_cast<bf16_t>(vv.z >> 16);
+    col[6 * VLD] = static_cast<bf16_t>(vv.w & 0xFFFFu);
+    col[7 * VLD] = static_cast<bf16_t>(vv.w >> 16);
   };
   auto stash = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = tid + i * 256;
-      const int key = c >> 3;
-      const int d0 = (c & 7) * 8;
-      *reinterpret_cast<uint4*>(&sK[buf][key * KLD + d0]) = rk[i];
-      const int slot = vt_slot(key);
-      const uint4 vv = rv[i];
-      const uint32_t w4[4] = {vv.x, vv.y, vv.z, vv.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        sVt[buf][(d0 + 2 * e) * VLD + slot] = static_cast<bf16_t>(w4[e] & 0xFFFFu);
-        sVt[buf][(d0 + 2 * e + 1) * VLD + slot] = static_cast<bf16_t>(w4[e] >> 16);
-      }
+    *reinterpret_cast<uint4*>(&sK[buf][skey * KLD + sd0]) = rk0;
+    *reinterpret_cast<uint4*>(&sK[buf][(skey + 32) * KLD + sd0]) = rk1;
+    put_vt(buf, skey, rv0);
+    put_vt(buf, skey + 32, rv1);
+    if (tid < AK) {
+      // w_j = sp (p_j - p_ref) + st (tau_j - tau_ref); the time difference is < 2^24 s
+      const float dp = static_cast<float>(fetched_base + tid - p_ref);
+      const float dt = static_cast<float>(static_cast<int32_t>(rts - ts_ref));
+      sW[buf][tid] = sp2 * dp + st2 * dt;
     }
-    if (tid < AK) sW[buf][tid] = rw;
   };
 
   if (n_tiles > 0) {
@@ -313,11 +313,10 @@ __global__ void __launch_bounds__(256) attn_fwd_bf16_kernel(AttnArgs a) {
     float w_i = 0.f;
     if (!is_cand) {
       w_i = sp2 * static_cast<float>(q_slot - p_ref) +
-            st2 * static_cast<float>(a.ts[off + q_slot] - ts_ref);
+            st2 * static_cast<float>(static_cast<int32_t>(a.ts[off + q_slot] - ts_ref));
     }
     a.lse[qrow * a.H + h] = LN2 * (m2 + log2f(ltot) - w_i);
   }
-  (void)t0;
 }
 
 // ------------------------------------------------------------------ f32 kernel

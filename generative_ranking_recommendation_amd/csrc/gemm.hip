@@ -59,30 +59,42 @@ __global__ void __launch_bounds__(GTHREADS) gemm_nt_bf16_kernel(GemmArgs g) {
   const int wm = wave & 1, wn = wave >> 1;
   const int l16 = lane & 15, g4 = lane >> 4;
 
-  // global -> register staging: 4 chunks of 16 B per operand per thread
-  uint4 ra[4], rw[4];
-  auto fetch = [&](int k0) {
+  // global -> register staging: 4 chunks of 16 B per operand per thread (named
+  // registers: an indexed array here ends up in scratch memory)
+  uint4 ra0, ra1, ra2, ra3, rw0, rw1, rw2, rw3;
+  const int srow = tid >> 3;          // + 32 * i for chunk i
+  const int skc = (tid & 7) * 8;
+  const bf16_t* a_row[4];
+  const bf16_t* w_row[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + i * GTHREADS;
-      const int row = c >> 3;
-      const int kc = (c & 7) * 8;
-      const int gm = m0 + row;
-      ra[i] = (gm < g.M) ? *reinterpret_cast<const uint4*>(g.A + gm * g.lda + k0 + kc)
-                         : make_uint4(0, 0, 0, 0);
-      rw[i] = *reinterpret_cast<const uint4*>(g.W + static_cast<int64_t>(n0 + row) * g.ldw + k0 + kc);
-    }
-  };
-  auto stash = [&]() {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + i * GTHREADS;
-      const int row = c >> 3;
-      const int kc = (c & 7) * 8;
-      *reinterpret_cast<uint4*>(sA + row * GLD + kc) = ra[i];
-      *reinterpret_cast<uint4*>(sW + row * GLD + kc) = rw[i];
-    }
-  };
+  for (int i = 0; i < 4; ++i) {
+    // rows past M are clamped to M-1: their results are never stored
+    const int gm = min(m0 + srow + 32 * i, g.M - 1);
+    a_row[i] = g.A + static_cast<int64_t>(gm) * g.lda + skc;
+    w_row[i] = g.W + static_cast<int64_t>(n0 + srow + 32 * i) * g.ldw + skc;
+  }
+#define GR_FETCH(k0)                                                     \
+  do {                                                                   \
+    ra0 = *reinterpret_cast<const uint4*>(a_row[0] + (k0));              \
+    ra1 = *reinterpret_cast<const uint4*>(a_row[1] + (k0));              \
+    ra2 = *reinterpret_cast<const uint4*>(a_row[2] + (k0));              \
+    ra3 = *reinterpret_cast<const uint4*>(a_row[3] + (k0));              \
+    rw0 = *reinterpret_cast<const uint4*>(w_row[0] + (k0));              \
+    rw1 = *reinterpret_cast<const uint4*>(w_row[1] + (k0));              \
+    rw2 = *reinterpret_cast<const uint4*>(w_row[2] + (k0));              \
+    rw3 = *reinterpret_cast<const uint4*>(w_row[3] + (k0));              \
+  } while (0)
+#define GR_STASH()                                                        \
+  do {                                                                    \
+    *reinterpret_cast<uint4*>(sA + (srow + 0) * GLD + skc) = ra0;         \
+    *reinterpret_cast<uint4*>(sA + (srow + 32) * GLD + skc) = ra1;        \
+    *reinterpret_cast<uint4*>(sA + (srow + 64) * GLD + skc) = ra2;        \
+    *reinterpret_cast<uint4*>(sA + (srow + 96) * GLD + skc) = ra3;        \
+    *reinterpret_cast<uint4*>(sW + (srow + 0) * GLD + skc) = rw0;         \
+    *reinterpret_cast<uint4*>(sW + (srow + 32) * GLD + skc) = rw1;        \
+    *reinterpret_cast<uint4*>(sW + (srow + 64) * GLD + skc) = rw2;        \
+    *reinterpret_cast<uint4*>(sW + (srow + 96) * GLD + skc) = rw3;        \
+  } while (0)
 
   f32x4_t acc[4][4];
 #pragma unroll
@@ -91,12 +103,12 @@ __global__ void __launch_bounds__(GTHREADS) gemm_nt_bf16_kernel(GemmArgs g) {
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   const int nk = g.K / GBK;
-  fetch(0);
+  GR_FETCH(0);
   for (int kt = 0; kt < nk; ++kt) {
     __syncthreads();
-    stash();
+    GR_STASH();
     __syncthreads();
-    if (kt + 1 < nk) fetch((kt + 1) * GBK);
+    if (kt + 1 < nk) GR_FETCH((kt + 1) * GBK);
 #pragma unroll
     for (int ks = 0; ks < GBK / 32; ++ks) {
       bf16x8_t fw[4], fa[4];
@@ -115,6 +127,9 @@ __global__ void __launch_bounds__(GTHREADS) gemm_nt_bf16_kernel(GemmArgs g) {
           acc[nb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fw[nb], fa[mb], acc[nb][mb], 0, 0, 0);
     }
   }
+
+#undef GR_FETCH
+#undef GR_STASH
 
   // epilogue: lane holds C[m][n .. n+3] for each (nb, mb)
 #pragma unroll

@@ -126,7 +126,7 @@ def _compare_train(cfg, batch, tables, weights, tol, relative_to="bf16"):
 
     if relative_to == "bf16":
         unit_close([float(gl.item())], [wl], "loss")
-        unit_close(glog, wlog, "logits")
+        unit_close(to_numpy(glog), wlog, "logits")
     else:
         assert abs(float(gl.item()) - wl) <= 1e-5
         close(glog, wlog, "logits")
