@@ -33,6 +33,8 @@ FLAGS = [
     "-Wno-unused-result",
     # keep hipcc from emitting packed-f32 VALU forms (v_pk_{add,mul,fma}_f32)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs: no copies to and from AGPRs around each MFMA
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     f"-I{INCLUDE}",
     f"-I{CSRC}",
 ]

@@ -38,6 +38,8 @@ constexpr int AK = 64;          // keys per tile
 constexpr int DH = 64;          // head dim of the bf16 kernel
 constexpr int KLD = DH + 8;     // sK row pitch (bf16)
 constexpr int VLD = AK + 8;     // sVt row pitch (bf16)
+constexpr int WCHUNK = 512;     // keys whose bias terms sit in LDS at a time
+constexpr int BUF_DWORD3 = 0x00020000;  // raw buffer descriptor word 3 (gfx9 family)
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 
@@ -69,7 +71,7 @@ __device__ __forceinline__ int vt_slot(int j) {
 __global__ void __launch_bounds__(256) attn_fwd_bf16_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) bf16_t sK[2][AK * KLD];
   __shared__ __attribute__((aligned(16))) bf16_t sVt[2][DH * VLD];
-  __shared__ __attribute__((aligned(16))) float sW[2][AK];
+  __shared__ __attribute__((aligned(16))) float sW[WCHUNK];
 
   const int u = blockIdx.x / a.H;
   const int h = blockIdx.x - u * a.H;
@@ -99,12 +101,28 @@ __global__ void __launch_bounds__(256) attn_fwd_bf16_kernel(AttnArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
   const int l16 = lane & 15, g4 = lane >> 4;
   const float sp2 = a.sp2[h], st2 = a.st2[h];
   // bias reference point: the candidates' shared (p, tau), or the tile's first query
   const int p_ref = is_cand ? N : q0;
   const int64_t ts_ref = is_cand ? a.req[u] : a.ts[off + q0];
+
+  // ---- per-key bias terms w_j = sp (p_j - p_ref) + st (tau_j - tau_ref) for keys
+  // [wbase, wbase + WCHUNK); keys past the history end get 0 (they are masked).  The time
+  // difference is below 2^24 s, so it converts exactly through int32.
+  auto load_w = [&](int wbase) {
+    for (int j = tid; j < WCHUNK; j += 256) {
+      const int key = wbase + j;
+      float w = 0.f;
+      if (key < N) {
+        w = sp2 * static_cast<float>(key - p_ref) +
+            st2 * static_cast<float>(static_cast<int32_t>(a.ts[off + key] - ts_ref));
+      }
+      sW[j] = w;
+    }
+  };
+  if (n_tiles > 0) load_w(0);
 
   // ---- this lane's query (column of S^T / O^T)
   const int qi_local = wave * 16 + l16;       // 0..63 within the tile
@@ -156,64 +174,71 @@ __global__ void __launch_bounds__(256) attn_fwd_bf16_kernel(AttnArgs a) {
     for (int nb = 0; nb < 4; ++nb) accO[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 
-  // ---- K/V tile staging: 2 chunks of 16 B per operand per thread + one key's timestamp.
-  // Keys past the history end read the last history row (finite values; the mask gives
-  // them probability 0).  The timestamp is only consumed in stash(), after the tile's
-  // math, so the prefetch stays in flight.
-  // Named registers (an indexed array here would be placed in scratch memory).
-  uint4 rk0, rk1, rv0, rv1;
-  int64_t rts = 0;
-  int fetched_base = 0;
-  const int skey = tid >> 3;           // chunk 0: key skey, chunk 1: key skey + 32
-  const int sd0 = (tid & 7) * 8;
-  const bf16_t* kbase = a.k + h * DH + sd0;
-  const bf16_t* vbase = a.v + h * DH + sd0;
+  // ---- K/V tile staging.  Thread (pair p, chunk c) moves rows 2p and 2p+1, columns
+  // 8c..8c+7, of both K and V: K rows go to sK as 16-byte writes; V goes to sVt
+  // transposed, each 32-bit write holding the two keys' values of one column (adjacent
+  // in the permuted key order).  Loads are buffer loads over the user's history rows:
+  // the descriptor sits in scalar registers, the lane offset is loop-invariant and the
+  // tile offset is scalar, and rows past the history end read as zero (the mask gives
+  // those keys probability 0).
+  const int pr = tid & 31;
+  const int ch = tid >> 5;
+  const int kA = 2 * pr, kB = 2 * pr + 1;
+  const int d0 = ch * 8;
+  const uint32_t row_bytes = static_cast<uint32_t>(a.ld_qkv) * 2u;
+  const uint32_t hist_bytes = static_cast<uint32_t>(N) * row_bytes;
+  const __amdgpu_buffer_rsrc_t rsK = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16_t*>(a.k + off * a.ld_qkv), static_cast<short>(0), hist_bytes, BUF_DWORD3);
+  const __amdgpu_buffer_rsrc_t rsV = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16_t*>(a.v + off * a.ld_qkv), static_cast<short>(0), hist_bytes, BUF_DWORD3);
+  const uint32_t voA = static_cast<uint32_t>(kA) * row_bytes + (h * DH + d0) * 2u;
+  const uint32_t voB = voA + row_bytes;
+  uint4 rka, rkb, rva, rvb;
   auto fetch = [&](int kt) {
-    const int base = kt * AK;
-    fetched_base = base;
-    const int64_t r0 = off + min(base + skey, N - 1);
-    const int64_t r1 = off + min(base + skey + 32, N - 1);
-    rk0 = *reinterpret_cast<const uint4*>(kbase + r0 * a.ld_qkv);
-    rk1 = *reinterpret_cast<const uint4*>(kbase + r1 * a.ld_qkv);
-    rv0 = *reinterpret_cast<const uint4*>(vbase + r0 * a.ld_qkv);
-    rv1 = *reinterpret_cast<const uint4*>(vbase + r1 * a.ld_qkv);
-    if (tid < AK) rts = a.ts[off + min(base + tid, N - 1)];
+    const uint32_t so = static_cast<uint32_t>(kt * AK) * row_bytes;
+    rka = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsK, voA, so, 0));
+    rkb = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsK, voB, so, 0));
+    rva = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsV, voA, so, 0));
+    rvb = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsV, voB, so, 0));
   };
-  auto put_vt = [&](int buf, int key, const uint4 vv) {
-    const int slot = vt_slot(key);
-    bf16_t* col = &sVt[buf][sd0 * VLD + slot];
-    col[0 * VLD] = static_cast<bf16_t>(vv.x & 0xFFFFu);
-    col[1 * VLD] = static_cast<bf16_t>(vv.x >> 16);
-    col[2 * VLD] = static_cast<bf16_t>(vv.y & 0xFFFFu);
-    col[3 * VLD] = static_cast<bf16_t>(vv.y >> 16);
-    col[4 * VLD] = static_cast<bf16_t>(vv.z & 0xFFFFu);
-    col[5 * VLD] = static_cast<bf16_t>(vv.z >> 16);
-    col[6 * VLD] = static_cast<bf16_t>(vv.w & 0xFFFFu);
-    col[7 * VLD] = static_cast<bf16_t>(vv.w >> 16);
-  };
+  const int slotA = vt_slot(kA);  // slot(kB) == slotA + 1
   auto stash = [&](int buf) {
-    *reinterpret_cast<uint4*>(&sK[buf][skey * KLD + sd0]) = rk0;
-    *reinterpret_cast<uint4*>(&sK[buf][(skey + 32) * KLD + sd0]) = rk1;
-    put_vt(buf, skey, rv0);
-    put_vt(buf, skey + 32, rv1);
-    if (tid < AK) {
-      // w_j = sp (p_j - p_ref) + st (tau_j - tau_ref); the time difference is < 2^24 s
-      const float dp = static_cast<float>(fetched_base + tid - p_ref);
-      const float dt = static_cast<float>(static_cast<int32_t>(rts - ts_ref));
-      sW[buf][tid] = sp2 * dp + st2 * dt;
-    }
+    *reinterpret_cast<uint4*>(&sK[buf][kA * KLD + d0]) = rka;
+    *reinterpret_cast<uint4*>(&sK[buf][kB * KLD + d0]) = rkb;
+    uint32_t* col = reinterpret_cast<uint32_t*>(&sVt[buf][d0 * VLD + slotA]);
+    constexpr int P = VLD / 2;  // row pitch in 32-bit words
+    col[0 * P] = __builtin_amdgcn_perm(rvb.x, rva.x, 0x05040100u);
+    col[1 * P] = __builtin_amdgcn_perm(rvb.x, rva.x, 0x07060302u);
+    col[2 * P] = __builtin_amdgcn_perm(rvb.y, rva.y, 0x05040100u);
+    col[3 * P] = __builtin_amdgcn_perm(rvb.y, rva.y, 0x07060302u);
+    col[4 * P] = __builtin_amdgcn_perm(rvb.z, rva.z, 0x05040100u);
+    col[5 * P] = __builtin_amdgcn_perm(rvb.z, rva.z, 0x07060302u);
+    col[6 * P] = __builtin_amdgcn_perm(rvb.w, rva.w, 0x05040100u);
+    col[7 * P] = __builtin_amdgcn_perm(rvb.w, rva.w, 0x07060302u);
   };
 
   if (n_tiles > 0) {
     fetch(0);
     stash(0);
   }
+  // The query fragments come straight from a global load.  Without this the compiler's
+  // wait-count analysis cannot prove at the loop head that the load has landed and makes
+  // every iteration wait for that iteration's K/V prefetch before its first MFMA.  An
+  // empty asm that reads and redefines the registers makes it wait here, once.
+  asm volatile("" : "+v"(qf[0]), "+v"(qf[1]));
   __syncthreads();
 
+  int wbase = 0;
   for (int kt = 0; kt < n_tiles; ++kt) {
     const int buf = kt & 1;
-    if (kt + 1 < n_tiles) fetch(kt + 1);
     const int base = kt * AK;
+    if (base >= wbase + WCHUNK) {  // histories longer than WCHUNK keys: next bias chunk
+      __syncthreads();
+      wbase += WCHUNK;
+      load_w(wbase);
+      __syncthreads();
+    }
+    if (kt + 1 < n_tiles) fetch(kt + 1);
     const bool diag = !is_cand && kt == n_tiles - 1;   // causal diagonal tile
     const bool ragged = base + AK > N;                  // keys past the history end
     const int kb_end = diag ? (wave + 1) : 4;           // key blocks this wave needs
@@ -236,7 +261,7 @@ __global__ void __launch_bounds__(256) attn_fwd_bf16_kernel(AttnArgs a) {
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-      const float4 w = *reinterpret_cast<const float4*>(&sW[buf][kb * 16 + g4 * 4]);
+      const float4 w = *reinterpret_cast<const float4*>(&sW[base - wbase + kb * 16 + g4 * 4]);
       const float wv[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
