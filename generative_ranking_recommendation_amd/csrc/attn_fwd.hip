@@ -11,7 +11,7 @@
 // only added back into the saved log-sum-exp.  The bias therefore costs one FMA per score
 // and no T x T array exists anywhere.
 //
-// bf16 kernel (dh = 64).  One workgroup = 4 waves = 64 query rows of one (user, head):
+// bf16 kernel (dh = 64).  One workgroup = 4 waves x 16 query rows of one (user, head):
 // either a 64-row history tile (keys: history tiles up to and including the diagonal) or
 // a 64-row candidate tile (keys: every history tile, plus each candidate's own key, which
 // seeds the online softmax so the m x m candidate block is never formed).
@@ -26,6 +26,8 @@
 // x dimension is a multiple of 8), so their K/V reuse hits one L2.
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -33,7 +35,9 @@ namespace genrank {
 
 namespace {
 
-constexpr int AQ = 64;          // queries per workgroup
+constexpr int QW = 16;          // queries per wave (16-column MFMA blocks)
+constexpr int QB = QW / 16;     // column blocks per wave
+constexpr int AQ = 4 * QW;      // queries per workgroup (4 waves)
 constexpr int AK = 64;          // keys per tile
 constexpr int DH = 64;          // head dim of the bf16 kernel
 constexpr int KLD = DH + 8;     // sK row pitch (bf16)
@@ -68,7 +72,25 @@ __device__ __forceinline__ int vt_slot(int j) {
   return ks * 32 + (rr >> 2) * 8 + hi * 4 + (rr & 3);
 }
 
-__global__ void __launch_bounds__(256) attn_fwd_bf16_kernel(AttnArgs a) {
+// max / sum with lane l ^ 16 and lane l ^ 32 via the gfx950 lane-swap instructions
+__device__ __forceinline__ float xor16_max(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor16_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) attn_fwd_bf16_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) bf16_t sK[2][AK * KLD];
   __shared__ __attribute__((aligned(16))) bf16_t sVt[2][DH * VLD];
   __shared__ __attribute__((aligned(16))) float sW[WCHUNK];
@@ -96,7 +118,7 @@ __global__ void __launch_bounds__(256) attn_fwd_bf16_kernel(AttnArgs a) {
     if (q0 >= N) return;
     nq = min(AQ, N - q0);
     qrow0 = off + q0;
-    n_tiles = t + 1;
+    n_tiles = (q0 + nq + AK - 1) / AK;  // keys up to the tile's last query
   }
 
   const int tid = threadIdx.x;
@@ -122,69 +144,83 @@ __global__ void __launch_bounds__(256) attn_fwd_bf16_kernel(AttnArgs a) {
       sW[j] = w;
     }
   };
-  if (n_tiles > 0) load_w(0);
+  // key tiles run newest first; the first one lies in this bias chunk
+  const int kt_first = n_tiles - 1;
+  int wbase = n_tiles > 0 ? (kt_first * AK / WCHUNK) * WCHUNK : 0;
+  if (n_tiles > 0) load_w(wbase);
 
-  // ---- this lane's query (column of S^T / O^T)
-  const int qi_local = wave * 16 + l16;       // 0..63 within the tile
-  const bool q_valid = qi_local < nq;
-  const int64_t qrow = qrow0 + qi_local;
-  const int q_slot = is_cand ? (N + q0 + qi_local) : (q0 + qi_local);  // sequence slot
-  // lanes past the tile's last query read that query's row (never stored)
-  const int64_t qrow_ld = qrow0 + min(qi_local, nq - 1);
-  bf16x8_t qf[2];
-  {
-    const bf16_t* qp = a.q + qrow_ld * a.ld_qkv + h * DH + g4 * 8;
-    qf[0] = as_bf16x8(*reinterpret_cast<const uint4*>(qp));
-    qf[1] = as_bf16x8(*reinterpret_cast<const uint4*>(qp + 32));
+  // ---- this lane's two queries: column blocks c = 0, 1 of the wave's 32 rows
+  int q_local[QB], q_slot[QB], k_lim[QB], kmax_blk[QB];
+  bool q_valid[QB];
+  int64_t qrow[QB], qrow_ld[QB];
+  bf16x8_t qf[QB][2];
+#pragma unroll
+  for (int c = 0; c < QB; ++c) {
+    q_local[c] = wave * QW + c * 16 + l16;
+    q_valid[c] = q_local[c] < nq;
+    qrow[c] = qrow0 + q_local[c];
+    q_slot[c] = is_cand ? (N + q0 + q_local[c]) : (q0 + q_local[c]);
+    // lanes past the tile's last query read that query's row (never stored)
+    qrow_ld[c] = qrow0 + min(q_local[c], nq - 1);
+    // keys with a slot above k_lim are masked: history queries see keys up to
+    // themselves, candidates every history key (their own key is the seed below)
+    k_lim[c] = is_cand ? (N - 1) : min(q_slot[c], N - 1);
+    // largest key any query of this 16-column block may see (uniform per wave)
+    kmax_blk[c] = is_cand ? (N - 1) : min(q0 + wave * QW + c * 16 + 15, N - 1);
+    const bf16_t* qp = a.q + qrow_ld[c] * a.ld_qkv + h * DH + g4 * 8;
+    qf[c][0] = as_bf16x8(*reinterpret_cast<const uint4*>(qp));
+    qf[c][1] = as_bf16x8(*reinterpret_cast<const uint4*>(qp + 32));
   }
 
-  f32x4_t accO[4];
-  float m2, lsum;
-  if (is_cand) {
-    // seed with the candidate's own key: bias 0 (same position and time as p_ref)
-    float dot = 0.f;
-    {
-      const bf16_t* kp = a.k + qrow_ld * a.ld_qkv + h * DH + g4 * 8;
+  f32x4_t accO[QB][4];
+  float m2[QB], lsum[QB];
+#pragma unroll
+  for (int c = 0; c < QB; ++c) {
+    if (is_cand) {
+      // seed with the candidate's own key: bias 0 (same position and time as p_ref)
+      float dot = 0.f;
+      const bf16_t* kp = a.k + qrow_ld[c] * a.ld_qkv + h * DH + g4 * 8;
       float kf[8], qv[8];
       uint4 kk = *reinterpret_cast<const uint4*>(kp);
       unpack8(kk, kf);
-      unpack8(__builtin_bit_cast(uint4, qf[0]), qv);
+      unpack8(__builtin_bit_cast(uint4, qf[c][0]), qv);
 #pragma unroll
       for (int e = 0; e < 8; ++e) dot += qv[e] * kf[e];
       kk = *reinterpret_cast<const uint4*>(kp + 32);
       unpack8(kk, kf);
-      unpack8(__builtin_bit_cast(uint4, qf[1]), qv);
+      unpack8(__builtin_bit_cast(uint4, qf[c][1]), qv);
 #pragma unroll
       for (int e = 0; e < 8; ++e) dot += qv[e] * kf[e];
-    }
-    dot += __shfl_xor(dot, 16);
-    dot += __shfl_xor(dot, 32);
-    m2 = dot * a.scale2;
-    lsum = (g4 == 0) ? 1.f : 0.f;
+      dot = xor32_sum(xor16_sum(dot));
+      m2[c] = dot * a.scale2;
+      lsum[c] = (g4 == 0) ? 1.f : 0.f;
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      const uint2 vv = *reinterpret_cast<const uint2*>(a.v + qrow_ld * a.ld_qkv + h * DH + nb * 16 + g4 * 4);
-      accO[nb] = f32x4_t{__uint_as_float(vv.x << 16), __uint_as_float(vv.x & 0xFFFF0000u),
-                         __uint_as_float(vv.y << 16), __uint_as_float(vv.y & 0xFFFF0000u)};
-    }
-  } else {
-    m2 = -1e30f;
-    lsum = 0.f;
+      for (int nb = 0; nb < 4; ++nb) {
+        const uint2 vv = *reinterpret_cast<const uint2*>(a.v + qrow_ld[c] * a.ld_qkv + h * DH + nb * 16 + g4 * 4);
+        accO[c][nb] = f32x4_t{__uint_as_float(vv.x << 16), __uint_as_float(vv.x & 0xFFFF0000u),
+                              __uint_as_float(vv.y << 16), __uint_as_float(vv.y & 0xFFFF0000u)};
+      }
+    } else {
+      m2[c] = -1e30f;
+      lsum[c] = 0.f;
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) accO[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int nb = 0; nb < 4; ++nb) accO[c][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
   }
 
-  // ---- K/V tile staging.  Thread (pair p, chunk c) moves rows 2p and 2p+1, columns
-  // 8c..8c+7, of both K and V: K rows go to sK as 16-byte writes; V goes to sVt
-  // transposed, each 32-bit write holding the two keys' values of one column (adjacent
-  // in the permuted key order).  Loads are buffer loads over the user's history rows:
-  // the descriptor sits in scalar registers, the lane offset is loop-invariant and the
-  // tile offset is scalar, and rows past the history end read as zero (the mask gives
-  // those keys probability 0).
+  // ---- K/V tile staging.  K: thread moves rows krow and krow+32, columns kcol..kcol+7
+  // (8 lanes per 128-byte row: conflict-free 16-byte LDS writes).  V: thread moves the
+  // key pair 2pr, 2pr+1, columns 8ch..8ch+7, into sVt transposed; each 32-bit write
+  // holds the two keys' values of one column (adjacent in the permuted key order).
+  // Loads are buffer loads over the user's history rows: descriptor in scalar
+  // registers, loop-invariant lane offsets, scalar tile offset; rows past the history
+  // end read as zero (the mask gives those keys probability 0).
   const int pr = tid & 31;
   const int ch = tid >> 5;
-  const int kA = 2 * pr, kB = 2 * pr + 1;
+  const int kA = 2 * pr;
   const int d0 = ch * 8;
+  const int krow = tid >> 3;
+  const int kcol = (tid & 7) * 8;
   const uint32_t row_bytes = static_cast<uint32_t>(a.ld_qkv) * 2u;
   const uint32_t hist_bytes = static_cast<uint32_t>(N) * row_bytes;
   const __amdgpu_buffer_rsrc_t rsK = __builtin_amdgcn_make_buffer_rsrc(
@@ -193,18 +229,20 @@ __global__ void __launch_bounds__(256) attn_fwd_bf16_kernel(AttnArgs a) {
       const_cast<bf16_t*>(a.v + off * a.ld_qkv), static_cast<short>(0), hist_bytes, BUF_DWORD3);
   const uint32_t voA = static_cast<uint32_t>(kA) * row_bytes + (h * DH + d0) * 2u;
   const uint32_t voB = voA + row_bytes;
+  const uint32_t voK0 = static_cast<uint32_t>(krow) * row_bytes + (h * DH + kcol) * 2u;
+  const uint32_t voK1 = voK0 + 32u * row_bytes;
   uint4 rka, rkb, rva, rvb;
   auto fetch = [&](int kt) {
     const uint32_t so = static_cast<uint32_t>(kt * AK) * row_bytes;
-    rka = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsK, voA, so, 0));
-    rkb = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsK, voB, so, 0));
+    rka = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsK, voK0, so, 0));
+    rkb = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsK, voK1, so, 0));
     rva = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsV, voA, so, 0));
     rvb = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsV, voB, so, 0));
   };
-  const int slotA = vt_slot(kA);  // slot(kB) == slotA + 1
+  const int slotA = vt_slot(kA);  // the pair's second key sits at slotA + 1
   auto stash = [&](int buf) {
-    *reinterpret_cast<uint4*>(&sK[buf][kA * KLD + d0]) = rka;
-    *reinterpret_cast<uint4*>(&sK[buf][kB * KLD + d0]) = rkb;
+    *reinterpret_cast<uint4*>(&sK[buf][krow * KLD + kcol]) = rka;
+    *reinterpret_cast<uint4*>(&sK[buf][(krow + 32) * KLD + kcol]) = rkb;
     uint32_t* col = reinterpret_cast<uint32_t*>(&sVt[buf][d0 * VLD + slotA]);
     constexpr int P = VLD / 2;  // row pitch in 32-bit words
     col[0 * P] = __builtin_amdgcn_perm(rvb.x, rva.x, 0x05040100u);
@@ -218,129 +256,183 @@ __global__ void __launch_bounds__(256) attn_fwd_bf16_kernel(AttnArgs a) {
   };
 
   if (n_tiles > 0) {
-    fetch(0);
+    fetch(kt_first);
     stash(0);
   }
   // The query fragments come straight from a global load.  Without this the compiler's
   // wait-count analysis cannot prove at the loop head that the load has landed and makes
   // every iteration wait for that iteration's K/V prefetch before its first MFMA.  An
   // empty asm that reads and redefines the registers makes it wait here, once.
-  asm volatile("" : "+v"(qf[0]), "+v"(qf[1]));
+#pragma unroll
+  for (int c = 0; c < QB; ++c) asm volatile("" : "+v"(qf[c][0]), "+v"(qf[c][1]));
   __syncthreads();
 
-  int wbase = 0;
-  for (int kt = 0; kt < n_tiles; ++kt) {
-    const int buf = kt & 1;
+  // One key tile, newest first: the recency bias puts each row's maximum in the first
+  // tiles, so the rescaling of O is rarely needed later.  Tiles that reach past some
+  // query's limit (the causal diagonal, the ragged end of the history) take the masked
+  // instantiation; the steady-state loop carries no mask code.
+  auto tile = [&](auto masked_tag, int it) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    const int kt = kt_first - it;
+    const int buf = it & 1;
     const int base = kt * AK;
-    if (base >= wbase + WCHUNK) {  // histories longer than WCHUNK keys: next bias chunk
+    if (base < wbase) {  // histories longer than WCHUNK keys: previous bias chunk
       __syncthreads();
-      wbase += WCHUNK;
+      wbase -= WCHUNK;
       load_w(wbase);
       __syncthreads();
     }
-    if (kt + 1 < n_tiles) fetch(kt + 1);
-    const bool diag = !is_cand && kt == n_tiles - 1;   // causal diagonal tile
-    const bool ragged = base + AK > N;                  // keys past the history end
-    const int kb_end = diag ? (wave + 1) : 4;           // key blocks this wave needs
+    if (kt > 0) fetch(kt - 1);
 
-    // S^T = K Q^T
-    f32x4_t s[4];
+    // S^T = K Q^T for both column blocks (each K fragment feeds two MFMAs).  In masked
+    // tiles a key block entirely above a column block's last query is skipped.
+    f32x4_t s[QB][4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-      s[kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      if (kb < kb_end) {
+      bool need[QB], any = false;
+#pragma unroll
+      for (int c = 0; c < QB; ++c) {
+        need[c] = !MASKED || base + kb * 16 <= kmax_blk[c];
+        any = any || need[c];
+        s[c][kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
+      if (any) {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
           const bf16x8_t kf = as_bf16x8(*reinterpret_cast<const uint4*>(
               &sK[buf][(kb * 16 + l16) * KLD + ks * 32 + g4 * 8]));
-          s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], s[kb], 0, 0, 0);
+#pragma unroll
+          for (int c = 0; c < QB; ++c)
+            if (need[c]) s[c][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[c][ks], s[c][kb], 0, 0, 0);
         }
       }
     }
-    // scale + separable bias, mask, tile max
-    float mx = -INFINITY;
+    // scale + separable bias (log2 units), mask, row max
+    float mx[QB];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       const float4 w = *reinterpret_cast<const float4*>(&sW[base - wbase + kb * 16 + g4 * 4]);
-      const float wv[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float v = s[kb][i] * a.scale2 + wv[i];
-        if (kb >= kb_end) {
-          v = -INFINITY;
-        } else if (diag || ragged) {
-          const int k_slot = base + kb * 16 + g4 * 4 + i;
-          if (!(k_slot < N && attn_allowed(q_slot, k_slot, N))) v = -INFINITY;
+      for (int c = 0; c < QB; ++c) {
+        s[c][kb][0] = s[c][kb][0] * a.scale2 + w.x;
+        s[c][kb][1] = s[c][kb][1] * a.scale2 + w.y;
+        s[c][kb][2] = s[c][kb][2] * a.scale2 + w.z;
+        s[c][kb][3] = s[c][kb][3] * a.scale2 + w.w;
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < QB; ++c) {
+      if constexpr (MASKED) {
+        const int lim = k_lim[c] - base - g4 * 4;  // local key kb*16 + i must be <= lim
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (kb * 16 + i > lim) s[c][kb][i] = -INFINITY;
+      }
+      float m = fmaxf(fmaxf(fmaxf(s[c][0][0], s[c][0][1]), s[c][0][2]), fmaxf(fmaxf(s[c][0][3], s[c][1][0]), s[c][1][1]));
+      m = fmaxf(fmaxf(m, s[c][1][2]), fmaxf(fmaxf(s[c][1][3], s[c][2][0]), s[c][2][1]));
+      m = fmaxf(fmaxf(m, s[c][2][2]), fmaxf(fmaxf(s[c][2][3], s[c][3][0]), s[c][3][1]));
+      m = fmaxf(fmaxf(m, s[c][3][2]), s[c][3][3]);
+      mx[c] = xor32_max(xor16_max(m));
+    }
+    // Lazy rescaling: probabilities are taken against m2 as long as no score exceeds
+    // it by more than 2^8 (p <= 256 is exact enough in f32 and bf16); only then is the
+    // reference raised and O, l rescaled.  The decision is uniform across the wave.
+    bool grow = false;
+#pragma unroll
+    for (int c = 0; c < QB; ++c) grow = grow || mx[c] > m2[c] + 8.f;
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+#pragma unroll
+      for (int c = 0; c < QB; ++c) {
+        const float m_new = fmaxf(m2[c], mx[c]);
+        const float alpha = __builtin_amdgcn_exp2f(m2[c] - m_new);
+        m2[c] = m_new;
+        lsum[c] *= alpha;
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) accO[c][nb][i] *= alpha;
+      }
+    }
+    bf16x8_t pf[QB][2];
+#pragma unroll
+    for (int c = 0; c < QB; ++c) {
+      float psum = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p = __builtin_amdgcn_exp2f(s[c][kb][i] - m2[c]);
+          s[c][kb][i] = p;
+          psum += p;
         }
-        s[kb][i] = v;
-        mx = fmaxf(mx, v);
-      }
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m2, mx);
-    const float alpha = __builtin_amdgcn_exp2f(m2 - m_new);
-    m2 = m_new;
-    float psum = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p = __builtin_amdgcn_exp2f(s[kb][i] - m_new);
-        s[kb][i] = p;
-        psum += p;
-      }
-    lsum = lsum * alpha + psum;
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) accO[nb][i] *= alpha;
-
-    // P^T as the column operand: keys {4g..4g+3} of blocks 2ks and 2ks+1
-    bf16x8_t pf[2];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      uint4 pk;
-      pk.x = pack_bf16x2(s[2 * ks][0], s[2 * ks][1]);
-      pk.y = pack_bf16x2(s[2 * ks][2], s[2 * ks][3]);
-      pk.z = pack_bf16x2(s[2 * ks + 1][0], s[2 * ks + 1][1]);
-      pk.w = pack_bf16x2(s[2 * ks + 1][2], s[2 * ks + 1][3]);
-      pf[ks] = as_bf16x8(pk);
-    }
-    // O^T += V^T P^T
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
+      lsum[c] += psum;
+      // P^T as the column operand: keys {4g..4g+3} of blocks 2ks and 2ks+1
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        if (ks * 2 >= kb_end) continue;
+        uint4 pk;
+        pk.x = pack_bf16x2(s[c][2 * ks][0], s[c][2 * ks][1]);
+        pk.y = pack_bf16x2(s[c][2 * ks][2], s[c][2 * ks][3]);
+        pk.z = pack_bf16x2(s[c][2 * ks + 1][0], s[c][2 * ks + 1][1]);
+        pk.w = pack_bf16x2(s[c][2 * ks + 1][2], s[c][2 * ks + 1][3]);
+        pf[c][ks] = as_bf16x8(pk);
+      }
+    }
+    // O^T += V^T P^T (each V fragment feeds both column blocks)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      bool need[QB], any = false;
+#pragma unroll
+      for (int c = 0; c < QB; ++c) {
+        need[c] = !MASKED || base + ks * 32 <= kmax_blk[c];
+        any = any || need[c];
+      }
+      if (!any) continue;
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
         const bf16x8_t vf = as_bf16x8(*reinterpret_cast<const uint4*>(
             &sVt[buf][(nb * 16 + l16) * VLD + ks * 32 + g4 * 8]));
-        accO[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[ks], accO[nb], 0, 0, 0);
+#pragma unroll
+        for (int c = 0; c < QB; ++c)
+          if (need[c]) accO[c][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[c][ks], accO[c][nb], 0, 0, 0);
       }
+    }
 
-    if (kt + 1 < n_tiles) stash(buf ^ 1);
+    if (kt > 0) stash(buf ^ 1);
     __syncthreads();
+  };
+
+  // a tile needs the mask when its last key lies past some query's limit
+  const int klim_min = is_cand ? (N - 1) : q0;
+  for (int it = 0; it < n_tiles; ++it) {
+    if ((kt_first - it) * AK + AK - 1 > klim_min)
+      tile(std::true_type{}, it);
+    else
+      tile(std::false_type{}, it);
   }
 
   // ---- epilogue
-  float ltot = lsum + __shfl_xor(lsum, 16);
-  ltot += __shfl_xor(ltot, 32);
-  if (!q_valid) return;
-  const float inv = 1.f / ltot;
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
-    uint2 o;
-    o.x = pack_bf16x2(accO[nb][0] * inv, accO[nb][1] * inv);
-    o.y = pack_bf16x2(accO[nb][2] * inv, accO[nb][3] * inv);
-    *reinterpret_cast<uint2*>(a.o + qrow * a.ld_o + h * DH + nb * 16 + g4 * 4) = o;
-  }
-  if (a.lse && g4 == 0) {
-    float w_i = 0.f;
-    if (!is_cand) {
-      w_i = sp2 * static_cast<float>(q_slot - p_ref) +
-            st2 * static_cast<float>(static_cast<int32_t>(a.ts[off + q_slot] - ts_ref));
+  for (int c = 0; c < QB; ++c) {
+    const float ltot = xor32_sum(xor16_sum(lsum[c]));
+    if (!q_valid[c]) continue;
+    const float inv = 1.f / ltot;
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      uint2 o;
+      o.x = pack_bf16x2(accO[c][nb][0] * inv, accO[c][nb][1] * inv);
+      o.y = pack_bf16x2(accO[c][nb][2] * inv, accO[c][nb][3] * inv);
+      *reinterpret_cast<uint2*>(a.o + qrow[c] * a.ld_o + h * DH + nb * 16 + g4 * 4) = o;
     }
-    a.lse[qrow * a.H + h] = LN2 * (m2 + log2f(ltot) - w_i);
+    if (a.lse && g4 == 0) {
+      float w_i = 0.f;
+      if (!is_cand) {
+        w_i = sp2 * static_cast<float>(q_slot[c] - p_ref) +
+              st2 * static_cast<float>(static_cast<int32_t>(a.ts[off + q_slot[c]] - ts_ref));
+      }
+      a.lse[qrow[c] * a.H + h] = LN2 * (m2[c] + log2f(ltot) - w_i);
+    }
   }
 }
 

@@ -18,15 +18,17 @@ __device__ __forceinline__ float bf16_to_f32(bf16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 
-// Round to nearest even (inputs are finite).
-__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return static_cast<bf16_t>(u >> 16);
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2_t;
+
+// Two floats to packed bf16 with one v_cvt_pk_bf16_f32 (round to nearest even).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const f32x2_t f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
 }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  return static_cast<bf16_t>(pack_bf16x2(f, 0.f) & 0xFFFFu);
 }
 
 // Unpack 8 bf16 held in a uint4 to floats.

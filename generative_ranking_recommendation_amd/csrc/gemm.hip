@@ -19,10 +19,9 @@ namespace genrank {
 
 namespace {
 
-constexpr int GBM = 128, GBN = 128, GBK = 64;
-constexpr int GPAD = 8;              // bf16 elements of padding per LDS row
-constexpr int GLD = GBK + GPAD;      // LDS row pitch (elements)
+constexpr int GBM = 128, GBN = 128, GBK = 32;
 constexpr int GTHREADS = 256;
+constexpr int BUF_DWORD3 = 0x00020000;  // raw buffer descriptor word 3 (gfx9 family)
 
 struct GemmArgs {
   const bf16_t* A; int64_t lda;
@@ -35,10 +34,22 @@ struct GemmArgs {
 
 __device__ __forceinline__ float silu_f(float x) { return x / (1.0f + __expf(-x)); }
 
+// LDS operand tile: [128 rows][32 bf16] = 64 B per row, four 16-byte chunks.  Chunk c of
+// row r is stored at chunk c ^ ((r >> 1) & 3): the 16-byte reads of 16 consecutive rows at
+// one chunk (an MFMA operand fragment) and the 16-byte writes of the staging pattern both
+// hit distinct banks.
+__device__ __forceinline__ int swz(int r, int c) { return r * GBK + ((c ^ ((r >> 1) & 3)) << 3); }
+
+constexpr int CP = GBN + 8;                           // staged C row pitch (bf16)
+constexpr int SMEM_OPS = 2 * 2 * GBM * GBK;           // [stage][A|W] operand tiles
+constexpr int SMEM = SMEM_OPS > GBM * CP ? SMEM_OPS : GBM * CP;
+
 template <int EPI>
 __global__ void __launch_bounds__(GTHREADS) gemm_nt_bf16_kernel(GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) bf16_t sA[GBM * GLD];
-  __shared__ __attribute__((aligned(16))) bf16_t sW[GBN * GLD];
+  __shared__ __attribute__((aligned(16))) bf16_t smem[SMEM];  // operands, then the C tile
+  // stage st: A tile at smem + st * 2 * GBM * GBK, W tile right after it
+  auto sA = [&](int st) { return smem + st * (2 * GBM * GBK); };
+  auto sW = [&](int st) { return smem + st * (2 * GBM * GBK) + GBM * GBK; };
 
   // XCD-aware renumbering: hardware hands workgroup w to XCD w % 8; give the tiles of
   // one M row-block consecutive logical ids on the same XCD.
@@ -55,46 +66,38 @@ __global__ void __launch_bounds__(GTHREADS) gemm_nt_bf16_kernel(GemmArgs g) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave & 1, wn = wave >> 1;
   const int l16 = lane & 15, g4 = lane >> 4;
 
-  // global -> register staging: 4 chunks of 16 B per operand per thread (named
-  // registers: an indexed array here ends up in scratch memory)
-  uint4 ra0, ra1, ra2, ra3, rw0, rw1, rw2, rw3;
-  const int srow = tid >> 3;          // + 32 * i for chunk i
-  const int skc = (tid & 7) * 8;
-  const bf16_t* a_row[4];
-  const bf16_t* w_row[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    // rows past M are clamped to M-1: their results are never stored
-    const int gm = min(m0 + srow + 32 * i, g.M - 1);
-    a_row[i] = g.A + static_cast<int64_t>(gm) * g.lda + skc;
-    w_row[i] = g.W + static_cast<int64_t>(n0 + srow + 32 * i) * g.ldw + skc;
-  }
-#define GR_FETCH(k0)                                                     \
-  do {                                                                   \
-    ra0 = *reinterpret_cast<const uint4*>(a_row[0] + (k0));              \
-    ra1 = *reinterpret_cast<const uint4*>(a_row[1] + (k0));              \
-    ra2 = *reinterpret_cast<const uint4*>(a_row[2] + (k0));              \
-    ra3 = *reinterpret_cast<const uint4*>(a_row[3] + (k0));              \
-    rw0 = *reinterpret_cast<const uint4*>(w_row[0] + (k0));              \
-    rw1 = *reinterpret_cast<const uint4*>(w_row[1] + (k0));              \
-    rw2 = *reinterpret_cast<const uint4*>(w_row[2] + (k0));              \
-    rw3 = *reinterpret_cast<const uint4*>(w_row[3] + (k0));              \
-  } while (0)
-#define GR_STASH()                                                        \
-  do {                                                                    \
-    *reinterpret_cast<uint4*>(sA + (srow + 0) * GLD + skc) = ra0;         \
-    *reinterpret_cast<uint4*>(sA + (srow + 32) * GLD + skc) = ra1;        \
-    *reinterpret_cast<uint4*>(sA + (srow + 64) * GLD + skc) = ra2;        \
-    *reinterpret_cast<uint4*>(sA + (srow + 96) * GLD + skc) = ra3;        \
-    *reinterpret_cast<uint4*>(sW + (srow + 0) * GLD + skc) = rw0;         \
-    *reinterpret_cast<uint4*>(sW + (srow + 32) * GLD + skc) = rw1;        \
-    *reinterpret_cast<uint4*>(sW + (srow + 64) * GLD + skc) = rw2;        \
-    *reinterpret_cast<uint4*>(sW + (srow + 96) * GLD + skc) = rw3;        \
-  } while (0)
+  // Buffer descriptors over this tile's rows: rows past M read as zero.
+  const uint64_t a_rows = static_cast<uint64_t>(g.M - m0);
+  const uint32_t a_bytes = static_cast<uint32_t>(min<uint64_t>(a_rows * g.lda * 2u, 0xFFFFFFF0ull));
+  const __amdgpu_buffer_rsrc_t rsA = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16_t*>(g.A + static_cast<int64_t>(m0) * g.lda), static_cast<short>(0), a_bytes, BUF_DWORD3);
+  const __amdgpu_buffer_rsrc_t rsW = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16_t*>(g.W + static_cast<int64_t>(n0) * g.ldw), static_cast<short>(0),
+      static_cast<uint32_t>(GBN * g.ldw * 2), BUF_DWORD3);
+  // staging: thread moves rows srow and srow + 64, chunk sc (16 B) of A and of W
+  const int srow = tid >> 2, sc = tid & 3;
+  const uint32_t voA0 = static_cast<uint32_t>(srow * g.lda + sc * 8) * 2u;
+  const uint32_t voA1 = voA0 + static_cast<uint32_t>(64 * g.lda * 2);
+  const uint32_t voW0 = static_cast<uint32_t>(srow * g.ldw + sc * 8) * 2u;
+  const uint32_t voW1 = voW0 + static_cast<uint32_t>(64 * g.ldw * 2);
+  uint4 ra0, ra1, rw0, rw1;
+  auto fetch = [&](int k0) {
+    const uint32_t so = static_cast<uint32_t>(k0) * 2u;
+    ra0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsA, voA0, so, 0));
+    ra1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsA, voA1, so, 0));
+    rw0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsW, voW0, so, 0));
+    rw1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsW, voW1, so, 0));
+  };
+  auto stash = [&](int st) {
+    *reinterpret_cast<uint4*>(sA(st) + swz(srow, sc)) = ra0;
+    *reinterpret_cast<uint4*>(sA(st) + swz(srow + 64, sc)) = ra1;
+    *reinterpret_cast<uint4*>(sW(st) + swz(srow, sc)) = rw0;
+    *reinterpret_cast<uint4*>(sW(st) + swz(srow + 64, sc)) = rw1;
+  };
 
   f32x4_t acc[4][4];
 #pragma unroll
@@ -103,68 +106,89 @@ __global__ void __launch_bounds__(GTHREADS) gemm_nt_bf16_kernel(GemmArgs g) {
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   const int nk = g.K / GBK;
-  GR_FETCH(0);
+  fetch(0);
+  stash(0);
+  __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
-    __syncthreads();
-    GR_STASH();
-    __syncthreads();
-    if (kt + 1 < nk) GR_FETCH((kt + 1) * GBK);
+    const int st = kt & 1;
+    if (kt + 1 < nk) fetch((kt + 1) * GBK);
+    bf16x8_t fw[4], fa[4];
 #pragma unroll
-    for (int ks = 0; ks < GBK / 32; ++ks) {
-      bf16x8_t fw[4], fa[4];
+    for (int nb = 0; nb < 4; ++nb)
+      fw[nb] = as_bf16x8(*reinterpret_cast<const uint4*>(sW(st) + swz(wn * 64 + nb * 16 + l16, g4)));
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
-        fw[nb] = as_bf16x8(*reinterpret_cast<const uint4*>(
-            sW + (wn * 64 + nb * 16 + l16) * GLD + ks * 32 + g4 * 8));
+    for (int mb = 0; mb < 4; ++mb)
+      fa[mb] = as_bf16x8(*reinterpret_cast<const uint4*>(sA(st) + swz(wm * 64 + mb * 16 + l16, g4)));
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb)
-        fa[mb] = as_bf16x8(*reinterpret_cast<const uint4*>(
-            sA + (wm * 64 + mb * 16 + l16) * GLD + ks * 32 + g4 * 8));
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-          acc[nb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fw[nb], fa[mb], acc[nb][mb], 0, 0, 0);
-    }
+        acc[nb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fw[nb], fa[mb], acc[nb][mb], 0, 0, 0);
+    if (kt + 1 < nk) stash(st ^ 1);
+    __syncthreads();
   }
 
-#undef GR_FETCH
-#undef GR_STASH
-
-  // epilogue: lane holds C[m][n .. n+3] for each (nb, mb)
+  // ---- epilogue: lane holds C[m][n .. n+3] for each (nb, mb).  Stage the 128 x 128 tile
+  // (after the epilogue math, in the output dtype) through LDS so that every global store
+  // is a 16-byte piece of a row.
+  if constexpr (EPI == GEMM_EPI_F32) {
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      const int m = m0 + wm * 64 + mb * 16 + l16;
+      if (m >= g.M) continue;
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        const int n = n0 + wn * 64 + nb * 16 + g4 * 4;
+        float* c = static_cast<float*>(g.C) + static_cast<int64_t>(m) * g.ldc + n;
+        *reinterpret_cast<float4*>(c) = make_float4(acc[nb][mb][0], acc[nb][mb][1], acc[nb][mb][2], acc[nb][mb][3]);
+      }
+    }
+    return;
+  }
+  bf16_t* sC = smem;  // the operand tiles are dead after the loop's final barrier
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) {
-    const int m = m0 + wm * 64 + mb * 16 + l16;
-    if (m >= g.M) continue;
+    const int ml = wm * 64 + mb * 16 + l16;
+    const int m = m0 + ml;
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
-      const int n = n0 + wn * 64 + nb * 16 + g4 * 4;
+      const int nl = wn * 64 + nb * 16 + g4 * 4;
+      const int n = n0 + nl;
       float v[4] = {acc[nb][mb][0], acc[nb][mb][1], acc[nb][mb][2], acc[nb][mb][3]};
-      if constexpr (EPI == GEMM_EPI_F32) {
-        float* c = static_cast<float*>(g.C) + static_cast<int64_t>(m) * g.ldc + n;
-        *reinterpret_cast<float4*>(c) = make_float4(v[0], v[1], v[2], v[3]);
-      } else {
-        if constexpr (EPI == GEMM_EPI_RESID) {
+      if constexpr (EPI == GEMM_EPI_RESID) {
+        if (m < g.M) {
           const uint2 r = *reinterpret_cast<const uint2*>(g.R + static_cast<int64_t>(m) * g.ldr + n);
           v[0] += __uint_as_float(r.x << 16); v[1] += __uint_as_float(r.x & 0xFFFF0000u);
           v[2] += __uint_as_float(r.y << 16); v[3] += __uint_as_float(r.y & 0xFFFF0000u);
         }
-        if constexpr (EPI == GEMM_EPI_SILU) {
-          if (g.Cpre) {
-            uint2 p;
-            p.x = pack_bf16x2(v[0], v[1]);
-            p.y = pack_bf16x2(v[2], v[3]);
-            *reinterpret_cast<uint2*>(g.Cpre + static_cast<int64_t>(m) * g.ldpre + n) = p;
-          }
-#pragma unroll
-          for (int i = 0; i < 4; ++i) v[i] = silu_f(v[i]);
-        }
-        uint2 o;
-        o.x = pack_bf16x2(v[0], v[1]);
-        o.y = pack_bf16x2(v[2], v[3]);
-        *reinterpret_cast<uint2*>(static_cast<bf16_t*>(g.C) + static_cast<int64_t>(m) * g.ldc + n) = o;
       }
+      if constexpr (EPI == GEMM_EPI_SILU) {
+        if (g.Cpre && m < g.M) {
+          uint2 p;
+          p.x = pack_bf16x2(v[0], v[1]);
+          p.y = pack_bf16x2(v[2], v[3]);
+          *reinterpret_cast<uint2*>(g.Cpre + static_cast<int64_t>(m) * g.ldpre + n) = p;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = silu_f(v[i]);
+      }
+      uint2 o;
+      o.x = pack_bf16x2(v[0], v[1]);
+      o.y = pack_bf16x2(v[2], v[3]);
+      *reinterpret_cast<uint2*>(sC + ml * CP + nl) = o;
     }
+  }
+  __syncthreads();
+  // 128 rows x 256 B: 16 threads per row, 16 rows per pass
+  bf16_t* C = static_cast<bf16_t*>(g.C);
+#pragma unroll
+  for (int pass = 0; pass < GBM / 16; ++pass) {
+    const int ml = pass * 16 + (tid >> 4);
+    const int m = m0 + ml;
+    if (m >= g.M) continue;
+    const int nl = (tid & 15) * 8;
+    *reinterpret_cast<uint4*>(C + static_cast<int64_t>(m) * g.ldc + n0 + nl) =
+        *reinterpret_cast<const uint4*>(sC + ml * CP + nl);
   }
 }
 
@@ -213,7 +237,8 @@ genrank_status launch_gemm_nt(int dtype, const void* A, int64_t lda, const void*
                               int64_t ldr, void* Cpre, int64_t ldpre, hipStream_t stream) {
   if (M <= 0) return GENRANK_OK;
   if (dtype == GENRANK_BF16 && N % GBN == 0 && K % GBK == 0 && lda % 8 == 0 && ldw % 8 == 0 &&
-      ldc % 4 == 0 && (epi != GEMM_EPI_RESID || ldr % 4 == 0) && (!Cpre || ldpre % 4 == 0)) {
+      ldc % 8 == 0 && (epi != GEMM_EPI_RESID || ldr % 4 == 0) && (!Cpre || ldpre % 4 == 0) &&
+      static_cast<int64_t>(GBN) * ldw * 2 < (int64_t(1) << 32)) {
     GemmArgs g{static_cast<const bf16_t*>(A), lda, static_cast<const bf16_t*>(W), ldw, C, ldc,
                static_cast<const bf16_t*>(R), ldr, static_cast<bf16_t*>(Cpre), ldpre, M, N, K};
     const int grid = (N / GBN) * ((M + GBM - 1) / GBM);
