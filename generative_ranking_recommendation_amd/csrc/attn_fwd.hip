@@ -22,8 +22,8 @@
 //         V is stored transposed in LDS with its keys permuted to match that register
 //         order, so each lane's row-operand fragment is one 16-byte LDS read.
 // K/V tiles are double-buffered in LDS and the next tile is fetched into registers while
-// the current one is multiplied.  Workgroups of one (user, head) share an XCD (the grid's
-// x dimension is a multiple of 8), so their K/V reuse hits one L2.
+// the current one is multiplied.  Workgroups of one (user, head) run next to each other on
+// one XCD, so their K/V reuse hits that XCD's L2.
 #include <math.h>
 
 #include <type_traits>
@@ -35,9 +35,12 @@ namespace genrank {
 
 namespace {
 
+constexpr int GROUP = 16;       // (user, head) pairs per XCD scheduling group
 constexpr int QW = 16;          // queries per wave (16-column MFMA blocks)
 constexpr int QB = QW / 16;     // column blocks per wave
-constexpr int AQ = 4 * QW;      // queries per workgroup (4 waves)
+constexpr int NW = 8;           // waves per workgroup
+constexpr int NT = 64 * NW;     // threads per workgroup
+constexpr int AQ = NW * QW;     // queries per workgroup
 constexpr int AK = 64;          // keys per tile
 constexpr int DH = 64;          // head dim of the bf16 kernel
 constexpr int KLD = DH + 8;     // sK row pitch (bf16)
@@ -90,14 +93,27 @@ __device__ __forceinline__ float xor32_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) attn_fwd_bf16_kernel(AttnArgs a) {
+__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8))) attn_fwd_bf16_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) bf16_t sK[2][AK * KLD];
   __shared__ __attribute__((aligned(16))) bf16_t sVt[2][DH * VLD];
   __shared__ __attribute__((aligned(16))) float sW[WCHUNK];
 
-  const int u = blockIdx.x / a.H;
-  const int h = blockIdx.x - u * a.H;
-  const int y = blockIdx.y;
+  // Flat grid over (user, head, tile).  Workgroup w runs on XCD w % 8 as that XCD's
+  // (w / 8)-th workgroup.  Each XCD owns the (user, head) pairs bh = x mod 8 and walks them
+  // in groups of GROUP pairs; inside a group it runs tile 0 of every pair, then tile 1, ...
+  // (candidate tiles first, then history tiles largest first).  A pair's tiles thus run
+  // at about the same time on one XCD and re-read its K/V from that L2, while the
+  // largest-first order inside each group keeps the XCDs' finishing times close.
+  const int TY = a.cand_tiles + a.hist_tiles;
+  const int x8 = blockIdx.x & 7;
+  const int kx = blockIdx.x >> 3;
+  const int grp = kx / (TY * GROUP);
+  const int rem = kx - grp * (TY * GROUP);
+  const int y = rem / GROUP;
+  const int bh = (grp * GROUP + (rem - y * GROUP)) * 8 + x8;
+  if (bh >= a.B * a.H) return;
+  const int u = bh / a.H;
+  const int h = bh - u * a.H;
   const int64_t off = a.offsets[u];
   const int N = a.offsets[u + 1] - a.offsets[u];
 
@@ -134,7 +150,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))
   // [wbase, wbase + WCHUNK); keys past the history end get 0 (they are masked).  The time
   // difference is below 2^24 s, so it converts exactly through int32.
   auto load_w = [&](int wbase) {
-    for (int j = tid; j < WCHUNK; j += 256) {
+    for (int j = tid; j < WCHUNK; j += NT) {
       const int key = wbase + j;
       float w = 0.f;
       if (key < N) {
@@ -208,57 +224,63 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))
     }
   }
 
-  // ---- K/V tile staging.  K: thread moves rows krow and krow+32, columns kcol..kcol+7
-  // (8 lanes per 128-byte row: conflict-free 16-byte LDS writes).  V: thread moves the
-  // key pair 2pr, 2pr+1, columns 8ch..8ch+7, into sVt transposed; each 32-bit write
-  // holds the two keys' values of one column (adjacent in the permuted key order).
-  // Loads are buffer loads over the user's history rows: descriptor in scalar
-  // registers, loop-invariant lane offsets, scalar tile offset; rows past the history
-  // end read as zero (the mask gives those keys probability 0).
-  const int pr = tid & 31;
-  const int ch = tid >> 5;
+  // ---- K/V tile staging: waves 0-3 move K, waves 4-7 move V, two 16-byte loads per lane
+  // per tile.  K: rows krow and krow+32, columns kcol..kcol+7 (8 lanes per 128-byte row:
+  // conflict-free 16-byte LDS writes).  V: the key pair 2pr, 2pr+1, columns 8ch..8ch+7,
+  // into sVt transposed; each 32-bit write holds the two keys' values of one column
+  // (adjacent in the permuted key order).  Loads are buffer loads over the user's history
+  // rows: descriptor in scalar registers, loop-invariant lane offsets, scalar tile offset;
+  // rows past the history end read as zero (the mask gives those keys probability 0).
+  // Two tiles are in flight: the loads for tile kt-2 are issued while tile kt is
+  // multiplied, and tile kt-1 (issued one step earlier) is written to LDS after it.
+  const bool stage_k = wave < NW / 2;
+  const int st = tid & (NT / 2 - 1);
+  const int pr = st & 31;
+  const int ch = st >> 5;
   const int kA = 2 * pr;
-  const int d0 = ch * 8;
-  const int krow = tid >> 3;
-  const int kcol = (tid & 7) * 8;
+  const int krow = st >> 3;
+  const int kcol = (st & 7) * 8;
   const uint32_t row_bytes = static_cast<uint32_t>(a.ld_qkv) * 2u;
   const uint32_t hist_bytes = static_cast<uint32_t>(N) * row_bytes;
-  const __amdgpu_buffer_rsrc_t rsK = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<bf16_t*>(a.k + off * a.ld_qkv), static_cast<short>(0), hist_bytes, BUF_DWORD3);
-  const __amdgpu_buffer_rsrc_t rsV = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<bf16_t*>(a.v + off * a.ld_qkv), static_cast<short>(0), hist_bytes, BUF_DWORD3);
-  const uint32_t voA = static_cast<uint32_t>(kA) * row_bytes + (h * DH + d0) * 2u;
-  const uint32_t voB = voA + row_bytes;
-  const uint32_t voK0 = static_cast<uint32_t>(krow) * row_bytes + (h * DH + kcol) * 2u;
-  const uint32_t voK1 = voK0 + 32u * row_bytes;
-  uint4 rka, rkb, rva, rvb;
-  auto fetch = [&](int kt) {
-    const uint32_t so = static_cast<uint32_t>(kt * AK) * row_bytes;
-    rka = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsK, voK0, so, 0));
-    rkb = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsK, voK1, so, 0));
-    rva = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsV, voA, so, 0));
-    rvb = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsV, voB, so, 0));
+  const __amdgpu_buffer_rsrc_t rsKV = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16_t*>((stage_k ? a.k : a.v) + off * a.ld_qkv), static_cast<short>(0), hist_bytes,
+      BUF_DWORD3);
+  const uint32_t vo0 = stage_k ? static_cast<uint32_t>(krow) * row_bytes + (h * DH + kcol) * 2u
+                               : static_cast<uint32_t>(kA) * row_bytes + (h * DH + ch * 8) * 2u;
+  const uint32_t vo1 = vo0 + (stage_k ? 32u : 1u) * row_bytes;
+  struct Stage { uint4 r0, r1; };
+  Stage S0, S1;
+  // A tile index below 0 gets an offset at the descriptor's record count: the hardware
+  // returns zeros without touching memory, and such a stage is never written to LDS.
+  // Issuing every fetch keeps the count of loads in flight the same on all paths, so the
+  // wait before a stash covers only that stage's own two loads.
+  auto fetch = [&](int kt, Stage& S) {
+    const uint32_t so = kt >= 0 ? static_cast<uint32_t>(kt * AK) * row_bytes : hist_bytes;
+    S.r0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsKV, vo0, so, 0));
+    S.r1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsKV, vo1, so, 0));
   };
   const int slotA = vt_slot(kA);  // the pair's second key sits at slotA + 1
-  auto stash = [&](int buf) {
-    *reinterpret_cast<uint4*>(&sK[buf][krow * KLD + kcol]) = rka;
-    *reinterpret_cast<uint4*>(&sK[buf][(krow + 32) * KLD + kcol]) = rkb;
-    uint32_t* col = reinterpret_cast<uint32_t*>(&sVt[buf][d0 * VLD + slotA]);
-    constexpr int P = VLD / 2;  // row pitch in 32-bit words
-    col[0 * P] = __builtin_amdgcn_perm(rvb.x, rva.x, 0x05040100u);
-    col[1 * P] = __builtin_amdgcn_perm(rvb.x, rva.x, 0x07060302u);
-    col[2 * P] = __builtin_amdgcn_perm(rvb.y, rva.y, 0x05040100u);
-    col[3 * P] = __builtin_amdgcn_perm(rvb.y, rva.y, 0x07060302u);
-    col[4 * P] = __builtin_amdgcn_perm(rvb.z, rva.z, 0x05040100u);
-    col[5 * P] = __builtin_amdgcn_perm(rvb.z, rva.z, 0x07060302u);
-    col[6 * P] = __builtin_amdgcn_perm(rvb.w, rva.w, 0x05040100u);
-    col[7 * P] = __builtin_amdgcn_perm(rvb.w, rva.w, 0x07060302u);
+  auto stash = [&](int buf, const Stage& S) {
+    if (stage_k) {
+      *reinterpret_cast<uint4*>(&sK[buf][krow * KLD + kcol]) = S.r0;
+      *reinterpret_cast<uint4*>(&sK[buf][(krow + 32) * KLD + kcol]) = S.r1;
+    } else {
+      uint32_t* col = reinterpret_cast<uint32_t*>(&sVt[buf][ch * 8 * VLD + slotA]);
+      constexpr int P = VLD / 2;  // row pitch in 32-bit words
+      col[0 * P] = __builtin_amdgcn_perm(S.r1.x, S.r0.x, 0x05040100u);
+      col[1 * P] = __builtin_amdgcn_perm(S.r1.x, S.r0.x, 0x07060302u);
+      col[2 * P] = __builtin_amdgcn_perm(S.r1.y, S.r0.y, 0x05040100u);
+      col[3 * P] = __builtin_amdgcn_perm(S.r1.y, S.r0.y, 0x07060302u);
+      col[4 * P] = __builtin_amdgcn_perm(S.r1.z, S.r0.z, 0x05040100u);
+      col[5 * P] = __builtin_amdgcn_perm(S.r1.z, S.r0.z, 0x07060302u);
+      col[6 * P] = __builtin_amdgcn_perm(S.r1.w, S.r0.w, 0x05040100u);
+      col[7 * P] = __builtin_amdgcn_perm(S.r1.w, S.r0.w, 0x07060302u);
+    }
   };
 
-  if (n_tiles > 0) {
-    fetch(kt_first);
-    stash(0);
-  }
+  fetch(kt_first, S0);
+  fetch(kt_first - 1, S1);
+  stash(0, S0);
   // The query fragments come straight from a global load.  Without this the compiler's
   // wait-count analysis cannot prove at the loop head that the load has landed and makes
   // every iteration wait for that iteration's K/V prefetch before its first MFMA.  An
@@ -266,12 +288,22 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))
 #pragma unroll
   for (int c = 0; c < QB; ++c) asm volatile("" : "+v"(qf[c][0]), "+v"(qf[c][1]));
   __syncthreads();
+  // a history query's own bias term w_i (its key lies in the first tile's bias chunk);
+  // the row term of the bias, added back into the log-sum-exp at the end
+  float w_i[QB];
+#pragma unroll
+  for (int c = 0; c < QB; ++c) w_i[c] = (!is_cand && q_valid[c]) ? sW[q_slot[c] - wbase] : 0.f;
 
   // One key tile, newest first: the recency bias puts each row's maximum in the first
   // tiles, so the rescaling of O is rarely needed later.  Tiles that reach past some
   // query's limit (the causal diagonal, the ragged end of the history) take the masked
   // instantiation; the steady-state loop carries no mask code.
-  auto tile = [&](auto masked_tag, int it) {
+  // Waves whose 16 queries all lie past the tile's end only stage and synchronise.  They
+  // run their own copy of the loop (same barriers in the same order), so no accumulator
+  // of the working waves crosses a branch inside the loop.
+  const bool wave_on = wave * QW < nq;
+  auto tile = [&](auto active_tag, auto masked_tag, int it, Stage& ld, const Stage& nxt) {
+    constexpr bool ACTIVE = decltype(active_tag)::value;
     constexpr bool MASKED = decltype(masked_tag)::value;
     const int kt = kt_first - it;
     const int buf = it & 1;
@@ -282,7 +314,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))
       load_w(wbase);
       __syncthreads();
     }
-    if (kt > 0) fetch(kt - 1);
+    fetch(kt - 2, ld);
+    if constexpr (ACTIVE) {
 
     // S^T = K Q^T for both column blocks (each K fragment feeds two MFMAs).  In masked
     // tiles a key block entirely above a column block's last query is skipped.
@@ -311,7 +344,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))
     float mx[QB];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-      const float4 w = *reinterpret_cast<const float4*>(&sW[base - wbase + kb * 16 + g4 * 4]);
+      const float4 w = reinterpret_cast<const float4*>(sW)[((base - wbase) >> 2) + kb * 4 + g4];
 #pragma unroll
       for (int c = 0; c < QB; ++c) {
         s[c][kb][0] = s[c][kb][0] * a.scale2 + w.x;
@@ -336,24 +369,15 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))
       m = fmaxf(fmaxf(m, s[c][3][2]), s[c][3][3]);
       mx[c] = xor32_max(xor16_max(m));
     }
-    // Lazy rescaling: probabilities are taken against m2 as long as no score exceeds
-    // it by more than 2^8 (p <= 256 is exact enough in f32 and bf16); only then is the
-    // reference raised and O, l rescaled.  The decision is uniform across the wave.
-    bool grow = false;
+    // online softmax: raise the running maximum and rescale O and l by 2^(m_old - m_new)
 #pragma unroll
-    for (int c = 0; c < QB; ++c) grow = grow || mx[c] > m2[c] + 8.f;
-    if (__builtin_amdgcn_ballot_w64(grow)) {
+    for (int c = 0; c < QB; ++c) {
+      const float m_new = fmaxf(m2[c], mx[c]);
+      const float alpha = __builtin_amdgcn_exp2f(m2[c] - m_new);
+      m2[c] = m_new;
+      lsum[c] *= alpha;
 #pragma unroll
-      for (int c = 0; c < QB; ++c) {
-        const float m_new = fmaxf(m2[c], mx[c]);
-        const float alpha = __builtin_amdgcn_exp2f(m2[c] - m_new);
-        m2[c] = m_new;
-        lsum[c] *= alpha;
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) accO[c][nb][i] *= alpha;
-      }
+      for (int nb = 0; nb < 4; ++nb) accO[c][nb] = accO[c][nb] * alpha;
     }
     bf16x8_t pf[QB][2];
 #pragma unroll
@@ -399,18 +423,31 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))
       }
     }
 
-    if (kt > 0) stash(buf ^ 1);
+    }  // ACTIVE
+
+    if (kt > 0) stash(buf ^ 1, nxt);
     __syncthreads();
   };
 
   // a tile needs the mask when its last key lies past some query's limit
   const int klim_min = is_cand ? (N - 1) : q0;
-  for (int it = 0; it < n_tiles; ++it) {
-    if ((kt_first - it) * AK + AK - 1 > klim_min)
-      tile(std::true_type{}, it);
-    else
-      tile(std::false_type{}, it);
-  }
+  auto loop = [&](auto active_tag) {
+    auto step = [&](int it, Stage& ld, const Stage& nxt) {
+      if ((kt_first - it) * AK + AK - 1 > klim_min)
+        tile(active_tag, std::true_type{}, it, ld, nxt);
+      else
+        tile(active_tag, std::false_type{}, it, ld, nxt);
+    };
+    // unrolled by two so that the two staging register sets keep fixed names
+    for (int it = 0; it < n_tiles; it += 2) {
+      step(it, S0, S1);
+      if (it + 1 < n_tiles) step(it + 1, S1, S0);
+    }
+  };
+  if (wave_on)
+    loop(std::true_type{});
+  else
+    loop(std::false_type{});
 
   // ---- epilogue
 #pragma unroll
@@ -425,14 +462,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))
       o.y = pack_bf16x2(accO[c][nb][2] * inv, accO[c][nb][3] * inv);
       *reinterpret_cast<uint2*>(a.o + qrow[c] * a.ld_o + h * DH + nb * 16 + g4 * 4) = o;
     }
-    if (a.lse && g4 == 0) {
-      float w_i = 0.f;
-      if (!is_cand) {
-        w_i = sp2 * static_cast<float>(q_slot[c] - p_ref) +
-              st2 * static_cast<float>(static_cast<int32_t>(a.ts[off + q_slot[c]] - ts_ref));
-      }
-      a.lse[qrow[c] * a.H + h] = LN2 * (m2[c] + log2f(ltot) - w_i);
-    }
+    if (a.lse && g4 == 0) a.lse[qrow[c] * a.H + h] = LN2 * (m2[c] + log2f(ltot) - w_i[c]);
   }
 }
 
@@ -531,6 +561,8 @@ genrank_status check_attn_args(const genrank_batch* b, const int32_t* offsets, c
   if (b->dtype == GENRANK_BF16) {
     if (b->dh != DH) return GENRANK_E_SHAPE;
     if (ld_qkv % 8 || ld_o % 4) return GENRANK_E_SHAPE;
+    // the kernel addresses one user's K/V rows with 32-bit buffer offsets
+    if ((static_cast<int64_t>(b->max_hist) + AK) * ld_qkv * 2 >= (int64_t{1} << 31)) return GENRANK_E_SHAPE;
     if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) |
          reinterpret_cast<uintptr_t>(v)) % 16 || reinterpret_cast<uintptr_t>(o) % 8)
       return GENRANK_E_ARG;
@@ -566,8 +598,10 @@ genrank_status launch_attn_fwd(const genrank_batch* b, const int32_t* offsets, c
     a.cand_tiles = (b->m + AQ - 1) / AQ;
     a.T_h = b->total_hist;
     if (a.hist_tiles + a.cand_tiles == 0) return GENRANK_OK;
-    dim3 grid(b->B * b->H, a.hist_tiles + a.cand_tiles);
-    hipLaunchKernelGGL(attn_fwd_bf16_kernel, grid, dim3(256), 0, stream, a);
+    const int64_t pairs = (static_cast<int64_t>(b->B) * b->H + 8 * GROUP - 1) / (8 * GROUP) * (8 * GROUP);
+    const int64_t G = pairs * (a.hist_tiles + a.cand_tiles);
+    if (G > INT32_MAX) return GENRANK_E_SHAPE;
+    hipLaunchKernelGGL(attn_fwd_bf16_kernel, dim3(static_cast<unsigned>(G)), dim3(NT), 0, stream, a);
   } else {
     AttnF32Args a{};
     a.offsets = offsets; a.ts = ts; a.req = req;

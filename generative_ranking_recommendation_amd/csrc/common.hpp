@@ -69,6 +69,17 @@ __device__ __forceinline__ int find_user(const int32_t* __restrict__ offsets, in
   return lo;
 }
 
+// The chip hands workgroup w of a launch to XCD w % 8, and each XCD runs its share in order
+// of w / 8.  This maps w to a logical id so that every XCD owns one contiguous range of
+// logical ids (the first G % 8 XCDs one id more), walked in order: work items with
+// neighbouring logical ids then run on the same XCD at about the same time and share its L2.
+// A bijection on [0, G) for every G.
+__device__ __forceinline__ int xcd_local_id(int w, int G) {
+  const int q = G >> 3, r = G & 7;
+  const int x = w & 7, k = w >> 3;
+  return x * q + (x < r ? x : r) + k;
+}
+
 // The attention mask on one user's sequence slots: 0..N-1 history, N.. candidates.
 // History queries see history keys at or before them; a candidate sees all history and
 // itself.  Every attention kernel's masked tiles and genrank_debug_mask use this.

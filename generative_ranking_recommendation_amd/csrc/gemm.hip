@@ -56,9 +56,7 @@ __global__ void __launch_bounds__(GTHREADS) gemm_nt_bf16_kernel(GemmArgs g) {
   const int nN = g.N / GBN;
   const int nM = (g.M + GBM - 1) / GBM;
   const int G = nN * nM;
-  const int w = blockIdx.x;
-  int L = w;
-  if (G % 8 == 0) L = (w % 8) * (G / 8) + (w / 8);
+  const int L = xcd_local_id(blockIdx.x, G);
   const int mblk = L / nN;
   const int nblk = L - mblk * nN;
   const int m0 = mblk * GBM;

@@ -57,6 +57,7 @@ __all__ = [
     "hstu_sequence",
     "hstu_rab",
     "hstu_attn_fwd_user",
+    "round_bf16",
 ]
 
 RMS_EPS = 1e-6
@@ -357,30 +358,51 @@ def _split_heads(t, H):
     return t.reshape(t.shape[0], H, -1)
 
 
-def layer_fwd(x, lw, block, H, geom):
+def round_bf16(x):
+    """Storage rounding to bfloat16: the value is rounded to float32, then to the nearest
+    bfloat16 (float32's sign and 8-bit exponent, the top 7 of its 23 fraction bits), ties
+    to the even fraction; returned as float64.  Not part of the method: it models a
+    tensor held in bf16 between two operations (see ``store`` below)."""
+    b = np.asarray(np.asarray(x, np.float64).astype(np.float32)).view(np.uint32).astype(np.uint64)
+    kept = (b + 0x7FFF + ((b >> 16) & 1)) >> 16
+    return (kept << 16).astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def _identity(t):
+    return t
+
+
+def layer_fwd(x, lw, block, H, geom, store=None):
     """One block.  ``lw``: dict with wqkv [3d, d], wo [d, d], and for the pre-norm block
     w1 [f d, d], w2 [d, f d], g1, g2.  ``geom``: dict with hist_offsets, m, pos, tau,
-    slopes_pos, slopes_time.  Returns (y, cache)."""
+    slopes_pos, slopes_time.  Returns (y, cache).
+
+    ``store`` (default: none) is applied to every intermediate tensor that an
+    implementation holds in memory between two operations: the normalised input, Q/K/V,
+    the attention output, the residual sum, the FFN hidden activation and the output.
+    With ``store=round_bf16`` this is the same computation with those tensors kept in
+    bf16, which measures the error that bf16 storage alone brings."""
+    S = store or _identity
     x = np.asarray(x, np.float64)
     d = x.shape[1]
     wqkv = np.asarray(lw["wqkv"], np.float64)
     wo = np.asarray(lw["wo"], np.float64)
     cache = {"x": x}
-    z = rmsnorm(x, lw["g1"]) if block == "prenorm" else x
-    qkv = z @ wqkv.T
+    z = S(rmsnorm(x, lw["g1"])) if block == "prenorm" else x
+    qkv = S(z @ wqkv.T)
     q, k, v = (_split_heads(qkv[:, i * d:(i + 1) * d], H) for i in range(3))
     o, _ = attn_fwd(q, k, v, geom["hist_offsets"], geom["m"], geom["pos"], geom["tau"],
                     geom["slopes_pos"], geom["slopes_time"])
-    o2 = o.reshape(o.shape[0], d)
+    o2 = S(o.reshape(o.shape[0], d))
     attn_out = o2 @ wo.T
     cache.update(z=z, q=q, k=k, v=v, o=o2)
     if block == "attn_only":
-        return attn_out, cache
-    x1 = x + attn_out
-    z2 = rmsnorm(x1, lw["g2"])
+        return S(attn_out), cache
+    x1 = S(x + attn_out)
+    z2 = S(rmsnorm(x1, lw["g2"]))
     a = z2 @ np.asarray(lw["w1"], np.float64).T
-    hdn = silu(a)
-    y = x1 + hdn @ np.asarray(lw["w2"], np.float64).T
+    hdn = S(silu(a))
+    y = S(x1 + hdn @ np.asarray(lw["w2"], np.float64).T)
     cache.update(x1=x1, z2=z2, a=a, hdn=hdn)
     return y, cache
 
@@ -453,13 +475,14 @@ def bce_loss_bwd(logits, labels):
     return (1.0 / (1.0 + np.exp(-z)) - y) / z.size
 
 
-def model_fwd(x0, layers, block, H, geom, head=None):
+def model_fwd(x0, layers, block, H, geom, head=None, store=None):
     """Embedded rows -> stacked blocks -> (optional) head at candidate rows.
-    Returns (x_final, logits or None, caches)."""
-    x = np.asarray(x0, np.float64)
+    Returns (x_final, logits or None, caches).  ``store``: as in ``layer_fwd``, also
+    applied to the embedded rows."""
+    x = (store or _identity)(np.asarray(x0, np.float64))
     caches = []
     for lw in layers:
-        x, c = layer_fwd(x, lw, block, H, geom)
+        x, c = layer_fwd(x, lw, block, H, geom, store)
         caches.append(c)
     logits = None
     if head is not None:

@@ -17,12 +17,12 @@ from gpu_common import (DEV, DeviceInputs, GenRank, bf16_close, custom_batch, gp
 pytestmark = pytest.mark.gpu
 
 
-def _oracle_forward(cfg, batch, tables, weights):
+def _oracle_forward(cfg, batch, tables, weights, store=None):
     idx = oracle_indices(cfg, batch, tables)
     x = oracle.embed_sum(oracle_tables(tables), batch.hist_items, batch.cand_items, idx)
     geom = oracle_geom(cfg, batch, idx)
     head = oracle_head(weights) if cfg.block == "prenorm" else None
-    y, logits, _ = oracle.model_fwd(x, oracle_layers(weights), cfg.block, cfg.H, geom, head)
+    y, logits, _ = oracle.model_fwd(x, oracle_layers(weights), cfg.block, cfg.H, geom, head, store=store)
     return y, logits
 
 
@@ -72,7 +72,14 @@ def test_layer_bf16_infer_subset():
 
 def test_stack_bf16_small_batch():
     """stack4_bf16 shapes (4 pre-norm layers, d = 512, 8 heads, FFN 4x, head of 4 logits)
-    on 3 users with jagged lengths."""
+    on 3 users with jagged lengths.
+
+    Four bf16 blocks put the logits' error at the 2e-2 bar by storage alone: the oracle
+    with every intermediate tensor rounded to bf16 (and exact arithmetic otherwise) is
+    off by 0.0057 rms and 0.0176 at most over these 480 logits, and which elements round
+    which way decides the maximum.  So the kernels are held to (a) an rms error within
+    1.25x of that storage-only error, and (b) a maximum within max(2e-2, 1.5x the
+    storage-only maximum)."""
     say("layer: bf16 stack4 small batch")
     cfg = synth.make_config("stack4_bf16", m=40)
     batch = custom_batch(cfg, [480, 123, 7], seed=4)
@@ -80,8 +87,14 @@ def test_stack_bf16_small_batch():
     weights = synth.make_weights(cfg)
     gy, gl = _gpu_forward(cfg, batch, tables, weights)
     wy, wl = _oracle_forward(cfg, batch, tables, weights)
+    _, sl = _oracle_forward(cfg, batch, tables, weights, store=oracle.round_bf16)
     assert np.std(wl) > 0.3  # the logits are unit-scale
-    unit_close(gl, wl, "logits")
+    rms = lambda e: float(np.sqrt(np.mean(np.square(e))))
+    e_gpu, e_store = gl - wl, sl - wl
+    say(f"  logits: gpu rms {rms(e_gpu):.4f} max {np.abs(e_gpu).max():.4f}; "
+        f"bf16 storage alone rms {rms(e_store):.4f} max {np.abs(e_store).max():.4f}")
+    assert rms(e_gpu) <= 1.25 * rms(e_store), (rms(e_gpu), rms(e_store))
+    unit_close(gl, wl, "logits", tol=max(2e-2, 1.5 * float(np.abs(e_store).max())))
     bf16_close(gy, wy, "final hidden state")
 
 
