@@ -163,13 +163,22 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
   // key tiles run newest first; the first one lies in this bias chunk
   const int kt_first = n_tiles - 1;
   int wbase = n_tiles > 0 ? (kt_first * AK / WCHUNK) * WCHUNK : 0;
-  if (n_tiles > 0) load_w(wbase);
 
-  // ---- this lane's two queries: column blocks c = 0, 1 of the wave's 32 rows
+  // ---- Prologue.  Every load below depends only on the user's offsets; they are all
+  // issued before the first wait, so the workgroup pays about one memory round trip
+  // before its first tile instead of one per kind of data.
+  static_assert(WCHUNK == NT, "one bias key per thread in the first chunk");
+  const int wkey = wbase + tid;
+  const bool wkey_in = wkey < N;
+  const int64_t ts_key = wkey_in ? a.ts[off + wkey] : ts_ref;
+
+  // this lane's queries: column block c of the wave's QW rows
   int q_local[QB], q_slot[QB], k_lim[QB], kmax_blk[QB];
   bool q_valid[QB];
   int64_t qrow[QB], qrow_ld[QB];
   bf16x8_t qf[QB][2];
+  uint4 kself[QB][2];
+  uint2 vself[QB][4];
 #pragma unroll
   for (int c = 0; c < QB; ++c) {
     q_local[c] = wave * QW + c * 16 + l16;
@@ -183,44 +192,15 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
     k_lim[c] = is_cand ? (N - 1) : min(q_slot[c], N - 1);
     // largest key any query of this 16-column block may see (uniform per wave)
     kmax_blk[c] = is_cand ? (N - 1) : min(q0 + wave * QW + c * 16 + 15, N - 1);
-    const bf16_t* qp = a.q + qrow_ld[c] * a.ld_qkv + h * DH + g4 * 8;
-    qf[c][0] = as_bf16x8(*reinterpret_cast<const uint4*>(qp));
-    qf[c][1] = as_bf16x8(*reinterpret_cast<const uint4*>(qp + 32));
-  }
-
-  f32x4_t accO[QB][4];
-  float m2[QB], lsum[QB];
+    const int64_t rowoff = qrow_ld[c] * a.ld_qkv + h * DH;
+    qf[c][0] = as_bf16x8(*reinterpret_cast<const uint4*>(a.q + rowoff + g4 * 8));
+    qf[c][1] = as_bf16x8(*reinterpret_cast<const uint4*>(a.q + rowoff + g4 * 8 + 32));
+    if (is_cand) {  // the candidate's own key and value (the softmax seed below)
+      kself[c][0] = *reinterpret_cast<const uint4*>(a.k + rowoff + g4 * 8);
+      kself[c][1] = *reinterpret_cast<const uint4*>(a.k + rowoff + g4 * 8 + 32);
 #pragma unroll
-  for (int c = 0; c < QB; ++c) {
-    if (is_cand) {
-      // seed with the candidate's own key: bias 0 (same position and time as p_ref)
-      float dot = 0.f;
-      const bf16_t* kp = a.k + qrow_ld[c] * a.ld_qkv + h * DH + g4 * 8;
-      float kf[8], qv[8];
-      uint4 kk = *reinterpret_cast<const uint4*>(kp);
-      unpack8(kk, kf);
-      unpack8(__builtin_bit_cast(uint4, qf[c][0]), qv);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) dot += qv[e] * kf[e];
-      kk = *reinterpret_cast<const uint4*>(kp + 32);
-      unpack8(kk, kf);
-      unpack8(__builtin_bit_cast(uint4, qf[c][1]), qv);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) dot += qv[e] * kf[e];
-      dot = xor32_sum(xor16_sum(dot));
-      m2[c] = dot * a.scale2;
-      lsum[c] = (g4 == 0) ? 1.f : 0.f;
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        const uint2 vv = *reinterpret_cast<const uint2*>(a.v + qrow_ld[c] * a.ld_qkv + h * DH + nb * 16 + g4 * 4);
-        accO[c][nb] = f32x4_t{__uint_as_float(vv.x << 16), __uint_as_float(vv.x & 0xFFFF0000u),
-                              __uint_as_float(vv.y << 16), __uint_as_float(vv.y & 0xFFFF0000u)};
-      }
-    } else {
-      m2[c] = -1e30f;
-      lsum[c] = 0.f;
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) accO[c][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int nb = 0; nb < 4; ++nb)
+        vself[c][nb] = *reinterpret_cast<const uint2*>(a.v + rowoff + nb * 16 + g4 * 4);
     }
   }
 
@@ -277,9 +257,47 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
       col[7 * P] = __builtin_amdgcn_perm(S.r1.w, S.r0.w, 0x07060302u);
     }
   };
-
   fetch(kt_first, S0);
   fetch(kt_first - 1, S1);
+
+  // ---- bias terms of the first chunk (the loads above stay in flight)
+  sW[tid] = wkey_in ? sp2 * static_cast<float>(wkey - p_ref) +
+                          st2 * static_cast<float>(static_cast<int32_t>(ts_key - ts_ref))
+                    : 0.f;
+
+  // ---- softmax state; a candidate starts from its own key: bias 0 (it shares p_ref and
+  // tau_ref), so its score is the plain scaled dot product
+  f32x4_t accO[QB][4];
+  float m2[QB], lsum[QB];
+#pragma unroll
+  for (int c = 0; c < QB; ++c) {
+    if (is_cand) {
+      float dot = 0.f;
+      float kf[8], qv[8];
+#pragma unroll
+      for (int hlf = 0; hlf < 2; ++hlf) {
+        unpack8(kself[c][hlf], kf);
+        unpack8(__builtin_bit_cast(uint4, qf[c][hlf]), qv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dot += qv[e] * kf[e];
+      }
+      dot = xor32_sum(xor16_sum(dot));
+      m2[c] = dot * a.scale2;
+      lsum[c] = (g4 == 0) ? 1.f : 0.f;
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        const uint2 vv = vself[c][nb];
+        accO[c][nb] = f32x4_t{__uint_as_float(vv.x << 16), __uint_as_float(vv.x & 0xFFFF0000u),
+                              __uint_as_float(vv.y << 16), __uint_as_float(vv.y & 0xFFFF0000u)};
+      }
+    } else {
+      m2[c] = -1e30f;
+      lsum[c] = 0.f;
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) accO[c][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+
   stash(0, S0);
   // The query fragments come straight from a global load.  Without this the compiler's
   // wait-count analysis cannot prove at the loop head that the load has landed and makes

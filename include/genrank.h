@@ -257,8 +257,9 @@ GENRANK_API genrank_status genrank_layer_bwd(const genrank_batch* batch, const g
  *   GENRANK_EPI_NONE:     y = acc
  *   GENRANK_EPI_RESIDUAL: y = acc + residual   (residual [M, ldr], may equal y)
  *   GENRANK_EPI_SILU:     y = silu(acc), and pre = acc when pre is not NULL.
- * bf16 runs on MFMA when N % 128 == 0, K % 64 == 0 and the leading dimensions are
- * multiples of 8; other shapes and f32 use a plain tiled kernel. */
+ * bf16 runs on MFMA when N % 128 == 0, K % 32 == 0 and the leading dimensions are
+ * multiples of 8 (K % 128 == 0 takes the kernel that streams operands straight into LDS);
+ * other shapes and f32 use a plain tiled kernel.  Rows of y past M are not written. */
 #define GENRANK_EPI_NONE 0
 #define GENRANK_EPI_RESIDUAL 1
 #define GENRANK_EPI_SILU 2

@@ -95,6 +95,8 @@ def test_attn_f32_shapes(lengths, m):
     ([50, 300, 480], 128),
     ([10, 200], 65),
     ([37, 64], 0),
+    ([512, 511, 1, 17], 33),
+    ([700, 3, 513, 64], 21),      # histories beyond one bias chunk (512 keys)
 ])
 def test_attn_bf16_shapes(lengths, m):
     say(f"attn: bf16 lengths={lengths} m={m}")
