@@ -39,6 +39,7 @@ struct EmbedArgs {
   int B, m, d, hist_chunks, cand_chunks;
   int n_action, n_pos, n_ri, n_bounds;
   int64_t T_h;
+  uint32_t bytes_item, bytes_action, bytes_pos, bytes_ri, bytes_rt;  // table sizes (< 4 GB)
   void* out;            // gather: [T, d]; debug: int32 [6, T]
   const void* dx;       // backward: [T, d]
   float* g_item; float* g_action; float* g_pos; float* g_ri; float* g_rt;
@@ -63,22 +64,6 @@ __device__ __forceinline__ void store_vec(float* p, const float* f) {
   *reinterpret_cast<float4*>(p) = make_float4(f[0], f[1], f[2], f[3]);
 }
 
-// Count k in [lo, hi) with ts[k] != ts[k-1] (block-wide; every thread gets the result).
-__device__ int block_count_changes(const int64_t* __restrict__ ts, int64_t lo, int64_t hi,
-                                   int* red) {
-  int c = 0;
-  for (int64_t k = lo + threadIdx.x; k < hi; k += EMB_THREADS) c += (ts[k] != ts[k - 1]);
-  for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off);
-  const int wave = threadIdx.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[wave] = c;
-  __syncthreads();
-  int total = 0;
-#pragma unroll
-  for (int w = 0; w < EMB_THREADS / 64; ++w) total += red[w];
-  return total;
-}
-
 // #{k : bounds[k] <= gap} over non-decreasing bounds (upper bound).
 __device__ __forceinline__ int bucket_of(const int64_t* bounds, int n, int64_t gap) {
   int lo = 0, hi = n;
@@ -93,62 +78,98 @@ struct RowIdx {
   int item, act, pos, pe, ri, ri_slot, rt;
 };
 
+// Block-wide sum (int) and max (int64) of per-thread values; every thread gets both.
+__device__ __forceinline__ void block_sum_max(int& c, int64_t& mx, int* red_c, int64_t* red_m) {
+  for (int off = 32; off > 0; off >>= 1) {
+    c += __shfl_xor(c, off);
+    const int64_t o = __shfl_xor(mx, off);
+    mx = o > mx ? o : mx;
+  }
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    red_c[wave] = c;
+    red_m[wave] = mx;
+  }
+  __syncthreads();
+  c = 0;
+  mx = INT64_MIN;
+#pragma unroll
+  for (int w = 0; w < EMB_THREADS / 64; ++w) {
+    c += red_c[w];
+    mx = red_m[w] > mx ? red_m[w] : mx;
+  }
+}
+
 // Derives the indices of the workgroup's rows into shared memory.  Returns the number of
-// valid rows and the global row of the first one (via *row0).
-__device__ int derive_chunk(const EmbedArgs& a, RowIdx* sidx, int64_t* sbounds, int* red,
-                            int64_t* row0_out) {
+// valid rows and the global row of the first one (via *row0).  Every load that depends
+// only on the user's offsets is issued before the first wait, so a chunk costs about two
+// memory round trips before its gathers:
+//   * request index: 1 + number of timestamp changes up to the row (timestamps are
+//     non-decreasing, so distinct values are runs); changes before the chunk come from a
+//     block reduction over the user's prefix, changes inside it from a 64-lane ballot;
+//   * gap to the previous request: the row's time minus the time just before its run.
+//     Inside the chunk that is a neighbouring lane's value; for a run that began before
+//     the chunk it is the largest prefix timestamp below ts[r0], reduced alongside.
+__device__ int derive_chunk(const EmbedArgs& a, RowIdx* sidx, int64_t* sbounds, int* red_c,
+                            int64_t* red_m, int64_t* row0_out) {
   const int u = blockIdx.y;
   const int chunk = blockIdx.x;
   const int64_t off = a.offsets[u];
   const int N = a.offsets[u + 1] - a.offsets[u];
-  const int lane = threadIdx.x & 63;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
   const bool is_hist = chunk < a.hist_chunks;
-
-  for (int k = threadIdx.x; k < a.n_bounds; k += EMB_THREADS) sbounds[k] = a.rt_bounds[k];
 
   if (is_hist) {
     const int s0 = chunk * EMB_ROWS;  // first sequence slot of the chunk
     if (s0 >= N) return 0;            // uniform across the block
     const int rows = min(EMB_ROWS, N - s0);
     const int64_t r0 = off + s0;
-    // changes at k in [off+1, r0): each one starts a new request before the chunk
-    const int before = block_count_changes(a.hist_ts, off + 1, r0, red);
-    if (threadIdx.x < 64) {
-      const int i = lane;
-      const bool valid = i < rows;
-      const int64_t r = r0 + i;
-      const int64_t t = valid ? a.hist_ts[r] : 0;
-      const bool change = valid && r > off && t != a.hist_ts[r - 1];
+    // the chunk's own rows (wave 0), the bucket bounds and the prefix, all in flight
+    const bool valid = tid < rows;
+    const int64_t r = r0 + lane;
+    int64_t t = 0;
+    int item = 0, act = 0;
+    if (tid < 64 && valid) {
+      t = a.hist_ts[r];
+      item = a.hist_items[r];
+      act = a.hist_actions[r];
+    }
+    for (int k = tid; k < a.n_bounds; k += EMB_THREADS) sbounds[k] = a.rt_bounds[k];
+    const int64_t t_r0 = a.hist_ts[r0];
+    const int64_t t_rm1 = r0 > off ? a.hist_ts[r0 - 1] : t_r0;
+    int c = 0;
+    int64_t mx = INT64_MIN;
+    for (int64_t k = off + tid; k < r0; k += EMB_THREADS) {
+      const int64_t v = a.hist_ts[k];
+      if (k > off) c += (v != a.hist_ts[k - 1]);
+      if (v < t_r0 && v > mx) mx = v;
+    }
+    block_sum_max(c, mx, red_c, red_m);  // also orders the sbounds writes
+    const int before = c;                // changes at k in [off + 1, r0)
+    const int64_t prev_head = mx;        // time before the run holding r0 (INT64_MIN: none)
+    if (tid < 64) {
+      const int64_t tl = __shfl_up(t, 1);  // lane i - 1's time
+      const bool change = valid && (lane == 0 ? t != t_rm1 : t != tl);
       const uint64_t mask = __ballot(change);
-      // start of the run that holds r0: lower bound of ts[r0] in ts[off .. r0]
-      int64_t run0;
-      {
-        const int64_t key = a.hist_ts[r0];
-        int64_t lo = off, hi = r0;
-        while (lo < hi) {
-          int64_t mid = (lo + hi) >> 1;
-          if (a.hist_ts[mid] < key) lo = mid + 1; else hi = mid;
-        }
-        run0 = lo;
-      }
+      const uint64_t upto = (lane == 63) ? ~0ull : ((2ull << lane) - 1ull);
+      const uint64_t cm = mask & upto;
+      // the run of row r starts at lane j = highest change at or below r, or before the
+      // chunk (j = -1); a change at lane 0 means ts[r0 - 1] < ts[r0], which is then the
+      // largest prefix time below ts[r0], i.e. prev_head
+      const int j = cm ? 63 - __clzll(static_cast<long long>(cm)) : -1;
+      const int64_t tj = __shfl(t, j > 0 ? j - 1 : 0);
+      const int64_t prev = j > 0 ? tj : prev_head;
       if (valid) {
-        const uint64_t upto = (i == 63) ? ~0ull : ((2ull << i) - 1ull);
-        const uint64_t c = mask & upto;
-        const int64_t run_start = c ? (r0 + 63 - __clzll(static_cast<long long>(c))) : run0;
-        int rt = 0;
-        if (run_start > off) {
-          const int64_t gap = t - a.hist_ts[run_start - 1];
-          rt = bucket_of(sbounds, a.n_bounds, gap);
-        }
         RowIdx ix;
-        ix.item = a.hist_items[r];
-        ix.act = a.hist_actions[r];
-        ix.pos = s0 + i;
+        ix.item = item;
+        ix.act = act;
+        ix.pos = s0 + lane;
         ix.pe = min(ix.pos, a.n_pos - 1);
-        ix.ri = 1 + before + __popcll(c);
+        ix.ri = 1 + before + __popcll(cm);
         ix.ri_slot = min(ix.ri - 1, a.n_ri - 1);
-        ix.rt = rt;
-        sidx[i] = ix;
+        ix.rt = prev != INT64_MIN ? bucket_of(sbounds, a.n_bounds, t - prev) : 0;
+        sidx[lane] = ix;
       }
     }
     __syncthreads();
@@ -159,21 +180,27 @@ __device__ int derive_chunk(const EmbedArgs& a, RowIdx* sidx, int64_t* sbounds, 
   const int c0 = (chunk - a.hist_chunks) * EMB_ROWS;
   if (c0 >= a.m) return 0;
   const int rows = min(EMB_ROWS, a.m - c0);
-  const int changes = block_count_changes(a.hist_ts, off + 1, off + N, red);
-  const int distinct_hist = (N > 0) ? 1 + changes : 0;
-  int rt = 0;
-  if (N > 0) rt = bucket_of(sbounds, a.n_bounds, a.req_ts[u] - a.hist_ts[off + N - 1]);
   const int64_t r0 = a.T_h + static_cast<int64_t>(u) * a.m + c0;
-  if (threadIdx.x < rows) {
+  int item = 0;
+  if (tid < rows) item = a.cand_items[static_cast<int64_t>(u) * a.m + c0 + tid];
+  for (int k = tid; k < a.n_bounds; k += EMB_THREADS) sbounds[k] = a.rt_bounds[k];
+  const int64_t req = a.req_ts[u];
+  const int64_t t_last = N > 0 ? a.hist_ts[off + N - 1] : 0;
+  int c = 0;
+  int64_t mx = INT64_MIN;
+  for (int64_t k = off + 1 + tid; k < off + N; k += EMB_THREADS) c += (a.hist_ts[k] != a.hist_ts[k - 1]);
+  block_sum_max(c, mx, red_c, red_m);
+  const int distinct_hist = (N > 0) ? 1 + c : 0;
+  if (tid < rows) {
     RowIdx ix;
-    ix.item = a.cand_items[static_cast<int64_t>(u) * a.m + c0 + threadIdx.x];
+    ix.item = item;
     ix.act = a.n_action;
     ix.pos = N;
     ix.pe = min(N, a.n_pos - 1);
     ix.ri = distinct_hist + 1;
     ix.ri_slot = min(ix.ri - 1, a.n_ri - 1);
-    ix.rt = rt;
-    sidx[threadIdx.x] = ix;
+    ix.rt = N > 0 ? bucket_of(sbounds, a.n_bounds, req - t_last) : 0;
+    sidx[tid] = ix;
   }
   __syncthreads();
   *row0_out = r0;
@@ -184,9 +211,10 @@ template <typename T>
 __global__ void __launch_bounds__(EMB_THREADS) embed_sum_kernel(EmbedArgs a) {
   __shared__ RowIdx sidx[EMB_ROWS];
   __shared__ int64_t sbounds[MAX_BOUNDS];
-  __shared__ int red[EMB_THREADS / 64];
+  __shared__ int red_c[EMB_THREADS / 64];
+  __shared__ int64_t red_m[EMB_THREADS / 64];
   int64_t row0;
-  const int rows = derive_chunk(a, sidx, sbounds, red, &row0);
+  const int rows = derive_chunk(a, sidx, sbounds, red_c, red_m, &row0);
   if (rows == 0) return;
   constexpr int V = Vec<T>::N;
   const int cpr = a.d / V;  // 16-byte chunks per row
@@ -236,12 +264,91 @@ __global__ void __launch_bounds__(EMB_THREADS) embed_sum_kernel(EmbedArgs a) {
   }
 }
 
+// Gather phase with a fixed 16-byte column per thread: thread t handles column chunk
+// t % cpr of rows t / cpr, t / cpr + rpp, ... (rpp = threads / cpr), four rows in flight
+// (twenty 16-byte loads).  Table reads and output writes are buffer accesses with 32-bit
+// byte offsets (every table is below 4 GB); rows past the chunk write nothing.
+constexpr int BUF_DWORD3 = 0x00020000;  // raw buffer descriptor word 3 (gfx9 family)
+
+template <typename T>
+__device__ __forceinline__ void add_vec(const uint4& v, float* acc) {
+  if constexpr (sizeof(T) == 2) {
+    acc[0] += __uint_as_float(v.x << 16); acc[1] += __uint_as_float(v.x & 0xFFFF0000u);
+    acc[2] += __uint_as_float(v.y << 16); acc[3] += __uint_as_float(v.y & 0xFFFF0000u);
+    acc[4] += __uint_as_float(v.z << 16); acc[5] += __uint_as_float(v.z & 0xFFFF0000u);
+    acc[6] += __uint_as_float(v.w << 16); acc[7] += __uint_as_float(v.w & 0xFFFF0000u);
+  } else {
+    acc[0] += __uint_as_float(v.x); acc[1] += __uint_as_float(v.y);
+    acc[2] += __uint_as_float(v.z); acc[3] += __uint_as_float(v.w);
+  }
+}
+
+template <typename T>
+__global__ void __launch_bounds__(EMB_THREADS) embed_sum_rows_kernel(EmbedArgs a) {
+  __shared__ RowIdx sidx[EMB_ROWS];
+  __shared__ int64_t sbounds[MAX_BOUNDS];
+  __shared__ int red_c[EMB_THREADS / 64];
+  __shared__ int64_t red_m[EMB_THREADS / 64];
+  int64_t row0;
+  const int rows = derive_chunk(a, sidx, sbounds, red_c, red_m, &row0);
+  if (rows == 0) return;
+  constexpr int V = Vec<T>::N;
+  constexpr int UR = 4;
+  const int cpr = a.d / V;
+  const int rpp = EMB_THREADS / cpr;
+  const int rp = threadIdx.x / cpr;
+  const uint32_t colb = static_cast<uint32_t>((threadIdx.x - rp * cpr) * V * sizeof(T));
+  const uint32_t rowb = static_cast<uint32_t>(a.d * sizeof(T));
+  auto rsrc = [](const void* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), static_cast<short>(0), bytes, BUF_DWORD3);
+  };
+  const __amdgpu_buffer_rsrc_t rs_item = rsrc(a.t_item, a.bytes_item);
+  const __amdgpu_buffer_rsrc_t rs_act = rsrc(a.t_action, a.bytes_action);
+  const __amdgpu_buffer_rsrc_t rs_pos = rsrc(a.t_pos, a.bytes_pos);
+  const __amdgpu_buffer_rsrc_t rs_ri = rsrc(a.t_ri, a.bytes_ri);
+  const __amdgpu_buffer_rsrc_t rs_rt = rsrc(a.t_rt, a.bytes_rt);
+  const uint32_t out_bytes = static_cast<uint32_t>(rows) * rowb;
+  const __amdgpu_buffer_rsrc_t rs_out = rsrc(static_cast<T*>(a.out) + row0 * a.d, out_bytes);
+  for (int r = rp; r < rows; r += rpp * UR) {
+    uint4 v[UR][5];
+#pragma unroll
+    for (int u = 0; u < UR; ++u) {
+      const RowIdx ix = sidx[min(r + u * rpp, rows - 1)];
+      v[u][0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_item, ix.item * rowb + colb, 0, 0));
+      v[u][1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_act, ix.act * rowb + colb, 0, 0));
+      v[u][2] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_pos, ix.pe * rowb + colb, 0, 0));
+      v[u][3] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_ri, ix.ri_slot * rowb + colb, 0, 0));
+      v[u][4] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_rt, ix.rt * rowb + colb, 0, 0));
+    }
+#pragma unroll
+    for (int u = 0; u < UR; ++u) {
+      float acc[V];
+#pragma unroll
+      for (int e = 0; e < V; ++e) acc[e] = 0.f;
+#pragma unroll
+      for (int t = 0; t < 5; ++t) add_vec<T>(v[u][t], acc);
+      const int rr = r + u * rpp;
+      const uint32_t ob = rr < rows ? static_cast<uint32_t>(rr) * rowb + colb : out_bytes;
+      uint4 o;
+      if constexpr (sizeof(T) == 2) {
+        o = pack8(acc);
+      } else {
+        o = make_uint4(__float_as_uint(acc[0]), __float_as_uint(acc[1]), __float_as_uint(acc[2]),
+                       __float_as_uint(acc[3]));
+      }
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, o),
+                                             rs_out, ob, 0, 0);
+    }
+  }
+}
+
 __global__ void __launch_bounds__(EMB_THREADS) debug_indices_kernel(EmbedArgs a, int64_t T) {
   __shared__ RowIdx sidx[EMB_ROWS];
   __shared__ int64_t sbounds[MAX_BOUNDS];
-  __shared__ int red[EMB_THREADS / 64];
+  __shared__ int red_c[EMB_THREADS / 64];
+  __shared__ int64_t red_m[EMB_THREADS / 64];
   int64_t row0;
-  const int rows = derive_chunk(a, sidx, sbounds, red, &row0);
+  const int rows = derive_chunk(a, sidx, sbounds, red_c, red_m, &row0);
   if (static_cast<int>(threadIdx.x) < rows) {
     int32_t* out = static_cast<int32_t*>(a.out);
     const RowIdx ix = sidx[threadIdx.x];
@@ -260,9 +367,10 @@ template <typename T>
 __global__ void __launch_bounds__(EMB_THREADS) embed_bwd_kernel(EmbedArgs a) {
   __shared__ RowIdx sidx[EMB_ROWS];
   __shared__ int64_t sbounds[MAX_BOUNDS];
-  __shared__ int red[EMB_THREADS / 64];
+  __shared__ int red_c[EMB_THREADS / 64];
+  __shared__ int64_t red_m[EMB_THREADS / 64];
   int64_t row0;
-  const int rows = derive_chunk(a, sidx, sbounds, red, &row0);
+  const int rows = derive_chunk(a, sidx, sbounds, red_c, red_m, &row0);
   if (rows == 0) return;
   constexpr int V = Vec<T>::N;
   const int cpr = a.d / V;
@@ -310,6 +418,14 @@ EmbedArgs make_args(const genrank_batch* b, const genrank_inputs* in, const genr
   a.n_ri = t->n_ri;
   a.n_bounds = t->n_rt - 1;
   a.T_h = b->total_hist;
+  const int64_t es = b->dtype == GENRANK_BF16 ? 2 : 4;
+  const int64_t rb = static_cast<int64_t>(b->d) * es;
+  auto clamp32 = [](int64_t v) { return static_cast<uint32_t>(v < 0xFFFFFFFFll ? v : 0xFFFFFFFFll); };
+  a.bytes_item = clamp32(t->n_item * rb);
+  a.bytes_action = clamp32((static_cast<int64_t>(t->n_action) + 1) * rb);
+  a.bytes_pos = clamp32(static_cast<int64_t>(t->n_pos) * rb);
+  a.bytes_ri = clamp32(static_cast<int64_t>(t->n_ri) * rb);
+  a.bytes_rt = clamp32(static_cast<int64_t>(t->n_rt) * rb);
   return a;
 }
 
@@ -342,7 +458,18 @@ genrank_status launch_embed_sum(const genrank_batch* b, const genrank_inputs* in
                                 const genrank_tables* t, void* out, hipStream_t stream) {
   EmbedArgs a = make_args(b, in, t);
   a.out = out;
-  if (b->dtype == GENRANK_BF16)
+  const int es = b->dtype == GENRANK_BF16 ? 2 : 4;
+  const int cpr = b->d * es / 16;
+  // the row kernel needs whole 16-byte columns that divide the workgroup, and every table
+  // and the chunk's output addressable with 32-bit offsets
+  const int64_t rb = static_cast<int64_t>(b->d) * es;
+  const bool rows_ok = b->d * es % 16 == 0 && cpr <= EMB_THREADS && EMB_THREADS % cpr == 0 &&
+                       t->n_item * rb < 0xFFFFFFFFll && EMB_ROWS * rb < 0xFFFFFFFFll;
+  if (rows_ok && b->dtype == GENRANK_BF16)
+    hipLaunchKernelGGL(embed_sum_rows_kernel<bf16_t>, grid_of(a), dim3(EMB_THREADS), 0, stream, a);
+  else if (rows_ok)
+    hipLaunchKernelGGL(embed_sum_rows_kernel<float>, grid_of(a), dim3(EMB_THREADS), 0, stream, a);
+  else if (b->dtype == GENRANK_BF16)
     hipLaunchKernelGGL(embed_sum_kernel<bf16_t>, grid_of(a), dim3(EMB_THREADS), 0, stream, a);
   else
     hipLaunchKernelGGL(embed_sum_kernel<float>, grid_of(a), dim3(EMB_THREADS), 0, stream, a);
