@@ -220,9 +220,17 @@ def main():
     idx_bytes = inp.total_hist * (4 + 4 + 8) + inp.B * m * 4 + (inp.B + 1) * 4 + inp.B * 8
     gather_bytes = W.gather_compulsory_bytes(T, d, es, uniq, small_rows, idx_bytes)
     work = {"embed_sum": ("hbm", gather_bytes, "GB/s")}
+    attn_flops = None
     if decomposed:
+        # attention: algorithmic flops over allowed pairs, and the floor bytes (Q, K, V read
+        # once, O and the log-sum-exp written once); the bound is whichever needs longer at peak
         attn_flops = W.attention_fwd_flops(lengths, m, d)
-        work["attn_fwd"] = ("mfma", attn_flops, "TFLOP/s")
+        attn_bytes = T * 3 * d * es + T * d * es + T * H * 4
+        peak_f = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
+        if attn_bytes / (PEAK_HBM_GBS * 1e9) >= attn_flops / (peak_f * 1e12):
+            work["attn_fwd"] = ("hbm", attn_bytes, "GB/s")
+        else:
+            work["attn_fwd"] = ("mfma", attn_flops, "TFLOP/s")
         work["qkv_gemm"] = ("hbm", (T * d + 3 * d * d + T * 3 * d) * es, "GB/s")
         work["out_gemm"] = ("hbm", (T * d + d * d + T * d) * es, "GB/s")
     traffic = load_traffic(cfg.name)
@@ -273,8 +281,12 @@ def main():
         "cpu_baseline": cpu,
         "kernels": kernels,
     }
-    if "attn_fwd" in kernels:
-        out["attn_mfma_util_pct"] = round(100 * kernels["attn_fwd"]["frac"], 2)
+    if attn_flops is not None:
+        peak_f = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
+        tf = attn_flops / (per["attn_fwd"] * 1e-3) / 1e12
+        kernels["attn_fwd"]["tflops"] = round(tf, 2)
+        kernels["attn_fwd"]["flops"] = int(attn_flops)
+        out["attn_mfma_util_pct"] = round(100 * tf / peak_f, 2)
     out["gather_gbps"] = kernels["embed_sum"]["achieved"]
     print(json.dumps(out), flush=True)
 
