@@ -94,6 +94,12 @@ _SIGS = {
                                     c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
     "genrank_debug_indices": (c_int32, [POINTER(Batch), POINTER(Inputs), POINTER(Tables), c_void_p, c_void_p]),
     "genrank_debug_mask": (c_int32, [POINTER(Batch), c_void_p, c_int32, c_int32, c_void_p, c_void_p]),
+    "genrank_hstu_rab_layout": (c_int32, [POINTER(Batch), c_void_p, c_void_p, c_void_p]),
+    "genrank_hstu_rab": (c_int32, [POINTER(Batch), c_void_p, c_void_p, c_void_p, c_void_p, c_int32,
+                                   c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_void_p]),
+    "genrank_hstu_attn_fwd": (c_int32, [POINTER(Batch), c_void_p, c_void_p, c_void_p, c_void_p,
+                                        c_void_p, c_void_p, c_int64, c_void_p, c_int64, c_void_p,
+                                        c_void_p]),
 }
 EXPORTS = tuple(_SIGS)
 
@@ -210,6 +216,25 @@ def genrank_attn_fwd(batch, hist_offsets, hist_ts, req_ts, slopes: HostSlopes, q
     _check("genrank_attn_fwd", lib().genrank_attn_fwd(
         ctypes.byref(batch), _p(hist_offsets), _p(hist_ts), _p(req_ts), slopes.struct, _p(q), _p(k),
         _p(v), ld_qkv, _p(o), ld_o, _p(lse), _stream(stream)))
+
+
+def genrank_hstu_rab_layout(batch, hist_offsets, rab_offsets, stream=None):
+    _check("genrank_hstu_rab_layout", lib().genrank_hstu_rab_layout(
+        ctypes.byref(batch), _p(hist_offsets), _p(rab_offsets), _stream(stream)))
+
+
+def genrank_hstu_rab(batch, hist_offsets, hist_ts, req_ts, pos_table, n_pos, time_table, time_bounds,
+                     n_time, rab_offsets, rab, stream=None):
+    _check("genrank_hstu_rab", lib().genrank_hstu_rab(
+        ctypes.byref(batch), _p(hist_offsets), _p(hist_ts), _p(req_ts), _p(pos_table), n_pos,
+        _p(time_table), _p(time_bounds), n_time, _p(rab_offsets), _p(rab), _stream(stream)))
+
+
+def genrank_hstu_attn_fwd(batch, hist_offsets, rab, rab_offsets, q, k, v, ld_qkv, o, ld_o, lse=None,
+                          stream=None):
+    _check("genrank_hstu_attn_fwd", lib().genrank_hstu_attn_fwd(
+        ctypes.byref(batch), _p(hist_offsets), _p(rab), _p(rab_offsets), _p(q), _p(k), _p(v), ld_qkv,
+        _p(o), ld_o, _p(lse), _stream(stream)))
 
 
 def genrank_attn_bwd(batch, hist_offsets, hist_ts, req_ts, slopes: HostSlopes, q, k, v, ld_qkv, o,

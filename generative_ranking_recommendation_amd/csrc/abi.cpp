@@ -250,6 +250,34 @@ genrank_status genrank_attn_fwd(const genrank_batch* b, const int32_t* offsets,
   return launch_attn_fwd(b, offsets, ts, req, alibi, q, k, v, ld_qkv, o, ld_o, lse, S(stream));
 }
 
+genrank_status genrank_hstu_rab_layout(const genrank_batch* b, const int32_t* offsets,
+                                       int64_t* rab_offsets, genrank_stream_t stream) {
+  GR_TRY(check_batch(b));
+  if (!offsets || !rab_offsets) return GENRANK_E_ARG;
+  return launch_hstu_rab_layout(b, offsets, rab_offsets, S(stream));
+}
+
+genrank_status genrank_hstu_rab(const genrank_batch* b, const int32_t* offsets, const int64_t* ts,
+                                const int64_t* req, const float* pos_table, int32_t n_pos,
+                                const float* time_table, const int64_t* time_bounds, int32_t n_time,
+                                const int64_t* rab_offsets, void* rab, genrank_stream_t stream) {
+  GR_TRY(check_batch(b));
+  if (!offsets || !req || !pos_table || !time_table || !rab_offsets || !rab) return GENRANK_E_ARG;
+  if (b->total_hist > 0 && !ts) return GENRANK_E_ARG;
+  if (n_pos < 1 || n_time < 1 || (n_time > 1 && !time_bounds)) return GENRANK_E_ARG;
+  return launch_hstu_rab(b, offsets, ts, req, pos_table, n_pos, time_table, time_bounds, n_time,
+                         rab_offsets, rab, S(stream));
+}
+
+genrank_status genrank_hstu_attn_fwd(const genrank_batch* b, const int32_t* offsets, const void* rab,
+                                     const int64_t* rab_offsets, const void* q, const void* k,
+                                     const void* v, int64_t ld_qkv, void* o, int64_t ld_o, float* lse,
+                                     genrank_stream_t stream) {
+  GR_TRY(check_batch(b));
+  if (!offsets || !rab || !rab_offsets || !q || !k || !v || !o) return GENRANK_E_ARG;
+  return launch_hstu_attn_fwd(b, offsets, rab, rab_offsets, q, k, v, ld_qkv, o, ld_o, lse, S(stream));
+}
+
 genrank_status genrank_attn_bwd(const genrank_batch* b, const int32_t* offsets,
                                 const int64_t* ts, const int64_t* req, genrank_alibi alibi,
                                 const void* q, const void* k, const void* v, int64_t ld_qkv,

@@ -66,6 +66,8 @@ struct AttnArgs {
   float scale2;                  // log2(e) / sqrt(dh)
   int B, m, H, hist_tiles, cand_tiles;
   int64_t T_h;
+  const bf16_t* rab;       // learned-bias variant: per-user [L, P] bf16 matrices
+  const int64_t* rab_off;  // element offset of user u's matrix, [B + 1]
 };
 
 // slot of key j (0..63 in a tile) in the permuted key axis of sVt
@@ -93,6 +95,12 @@ __device__ __forceinline__ float xor32_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// RAB = false: ALiBi bias computed from positions and times (the action-oriented path).
+// RAB = true: the HSTU-style comparison, where each user's history is the interleaved
+// item/action sequence (2 N slots, rows 2 off .. 2 off + 2N) and the bias is a learned
+// matrix read from memory (user u's [L, P] bf16 block, L = 2N + m, row pitch P = L rounded
+// up to 8); everything else is the same kernel.
+template <bool RAB>
 __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8))) attn_fwd_bf16_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) bf16_t sK[2][AK * KLD];
   __shared__ __attribute__((aligned(16))) bf16_t sVt[2][DH * VLD];
@@ -114,8 +122,9 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
   if (bh >= a.B * a.H) return;
   const int u = bh / a.H;
   const int h = bh - u * a.H;
-  const int64_t off = a.offsets[u];
-  const int N = a.offsets[u + 1] - a.offsets[u];
+  constexpr int HS = RAB ? 2 : 1;  // history slots per history action
+  const int64_t off = HS * static_cast<int64_t>(a.offsets[u]);
+  const int N = HS * (a.offsets[u + 1] - a.offsets[u]);
 
   bool is_cand;
   int q0, nq, n_tiles;
@@ -144,7 +153,7 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
   const float sp2 = a.sp2[h], st2 = a.st2[h];
   // bias reference point: the candidates' shared (p, tau), or the tile's first query
   const int p_ref = is_cand ? N : q0;
-  const int64_t ts_ref = is_cand ? a.req[u] : a.ts[off + q0];
+  const int64_t ts_ref = RAB ? 0 : (is_cand ? a.req[u] : a.ts[off + q0]);
 
   // ---- per-key bias terms w_j = sp (p_j - p_ref) + st (tau_j - tau_ref) for keys
   // [wbase, wbase + WCHUNK); keys past the history end get 0 (they are masked).  The time
@@ -170,7 +179,7 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
   static_assert(WCHUNK == NT, "one bias key per thread in the first chunk");
   const int wkey = wbase + tid;
   const bool wkey_in = wkey < N;
-  const int64_t ts_key = wkey_in ? a.ts[off + wkey] : ts_ref;
+  const int64_t ts_key = (!RAB && wkey_in) ? a.ts[off + wkey] : ts_ref;
 
   // this lane's queries: column block c of the wave's QW rows
   int q_local[QB], q_slot[QB], k_lim[QB], kmax_blk[QB];
@@ -260,10 +269,42 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
   fetch(kt_first, S0);
   fetch(kt_first - 1, S1);
 
+  // ---- learned bias (RAB): the lane's 16 bias values of a key tile are four 8-byte
+  // pieces of its query's row, loaded one tile ahead.  A buffer descriptor over the user's
+  // matrix: rows past it and tile indices below 0 read zeros without a memory access.
+  struct RabRegs { uint2 v[4]; };
+  RabRegs R0, R1;
+  static_assert(!RAB || QB == 1, "one query per lane");
+  const uint32_t rab_P = RAB ? static_cast<uint32_t>((N + a.m + 7) & ~7) : 0u;
+  const uint32_t rab_bytes = RAB ? static_cast<uint32_t>(N + a.m) * rab_P * 2u : 0u;
+  const uint32_t rab_row = static_cast<uint32_t>(q_slot[0]) * rab_P * 2u + g4 * 8u;
+  const __amdgpu_buffer_rsrc_t rsR = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16_t*>(RAB ? a.rab + a.rab_off[u] : a.q), static_cast<short>(0), rab_bytes, BUF_DWORD3);
+  float rab_self[QB];
+  if constexpr (RAB) {
+    const uint32_t P = rab_P;
+#pragma unroll
+    for (int c = 0; c < QB; ++c) {
+      const uint16_t b = __builtin_amdgcn_raw_buffer_load_b16(
+          rsR, static_cast<uint32_t>(q_slot[c]) * static_cast<uint32_t>(P + 1) * 2u, 0, 0);
+      rab_self[c] = __uint_as_float(static_cast<uint32_t>(b) << 16);
+    }
+  }
+  auto rab_load = [&](int kt, RabRegs& R) {
+    if constexpr (RAB) {
+      const uint32_t so = kt >= 0 ? static_cast<uint32_t>(kt * AK) * 2u : rab_bytes;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+        R.v[kb] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rsR, rab_row + kb * 32u, so, 0));
+    }
+  };
+  rab_load(kt_first, R0);
+
   // ---- bias terms of the first chunk (the loads above stay in flight)
-  sW[tid] = wkey_in ? sp2 * static_cast<float>(wkey - p_ref) +
-                          st2 * static_cast<float>(static_cast<int32_t>(ts_key - ts_ref))
-                    : 0.f;
+  if constexpr (!RAB)
+    sW[tid] = wkey_in ? sp2 * static_cast<float>(wkey - p_ref) +
+                            st2 * static_cast<float>(static_cast<int32_t>(ts_key - ts_ref))
+                      : 0.f;
 
   // ---- softmax state; a candidate starts from its own key: bias 0 (it shares p_ref and
   // tau_ref), so its score is the plain scaled dot product
@@ -283,6 +324,7 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
       }
       dot = xor32_sum(xor16_sum(dot));
       m2[c] = dot * a.scale2;
+      if constexpr (RAB) m2[c] += rab_self[c] * LOG2E;  // the learned bias of (i, i)
       lsum[c] = (g4 == 0) ? 1.f : 0.f;
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) {
@@ -310,7 +352,7 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
   // the row term of the bias, added back into the log-sum-exp at the end
   float w_i[QB];
 #pragma unroll
-  for (int c = 0; c < QB; ++c) w_i[c] = (!is_cand && q_valid[c]) ? sW[q_slot[c] - wbase] : 0.f;
+  for (int c = 0; c < QB; ++c) w_i[c] = (!RAB && !is_cand && q_valid[c]) ? sW[q_slot[c] - wbase] : 0.f;
 
   // One key tile, newest first: the recency bias puts each row's maximum in the first
   // tiles, so the rescaling of O is rarely needed later.  Tiles that reach past some
@@ -320,19 +362,23 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
   // run their own copy of the loop (same barriers in the same order), so no accumulator
   // of the working waves crosses a branch inside the loop.
   const bool wave_on = wave * QW < nq;
-  auto tile = [&](auto active_tag, auto masked_tag, int it, Stage& ld, const Stage& nxt) {
+  auto tile = [&](auto active_tag, auto masked_tag, int it, Stage& ld, const Stage& nxt,
+                  const RabRegs& rc, RabRegs& rn) {
     constexpr bool ACTIVE = decltype(active_tag)::value;
     constexpr bool MASKED = decltype(masked_tag)::value;
     const int kt = kt_first - it;
     const int buf = it & 1;
     const int base = kt * AK;
-    if (base < wbase) {  // histories longer than WCHUNK keys: previous bias chunk
-      __syncthreads();
-      wbase -= WCHUNK;
-      load_w(wbase);
-      __syncthreads();
+    if constexpr (!RAB) {
+      if (base < wbase) {  // histories longer than WCHUNK keys: previous bias chunk
+        __syncthreads();
+        wbase -= WCHUNK;
+        load_w(wbase);
+        __syncthreads();
+      }
     }
     fetch(kt - 2, ld);
+    rab_load(kt - 1, rn);
     if constexpr (ACTIVE) {
 
     // S^T = K Q^T for both column blocks (each K fragment feeds two MFMAs).  In masked
@@ -362,7 +408,14 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
     float mx[QB];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-      const float4 w = reinterpret_cast<const float4*>(sW)[((base - wbase) >> 2) + kb * 4 + g4];
+      float4 w;
+      if constexpr (RAB) {  // the learned bias, natural-log units -> log2 units
+        const uint2 r = rc.v[kb];
+        w = make_float4(__uint_as_float(r.x << 16) * LOG2E, __uint_as_float(r.x & 0xFFFF0000u) * LOG2E,
+                        __uint_as_float(r.y << 16) * LOG2E, __uint_as_float(r.y & 0xFFFF0000u) * LOG2E);
+      } else {
+        w = reinterpret_cast<const float4*>(sW)[((base - wbase) >> 2) + kb * 4 + g4];
+      }
 #pragma unroll
       for (int c = 0; c < QB; ++c) {
         s[c][kb][0] = s[c][kb][0] * a.scale2 + w.x;
@@ -450,16 +503,16 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
   // a tile needs the mask when its last key lies past some query's limit
   const int klim_min = is_cand ? (N - 1) : q0;
   auto loop = [&](auto active_tag) {
-    auto step = [&](int it, Stage& ld, const Stage& nxt) {
+    auto step = [&](int it, Stage& ld, const Stage& nxt, const RabRegs& rc, RabRegs& rn) {
       if ((kt_first - it) * AK + AK - 1 > klim_min)
-        tile(active_tag, std::true_type{}, it, ld, nxt);
+        tile(active_tag, std::true_type{}, it, ld, nxt, rc, rn);
       else
-        tile(active_tag, std::false_type{}, it, ld, nxt);
+        tile(active_tag, std::false_type{}, it, ld, nxt, rc, rn);
     };
     // unrolled by two so that the two staging register sets keep fixed names
     for (int it = 0; it < n_tiles; it += 2) {
-      step(it, S0, S1);
-      if (it + 1 < n_tiles) step(it + 1, S1, S0);
+      step(it, S0, S1, R0, R1);
+      if (it + 1 < n_tiles) step(it + 1, S1, S0, R1, R0);
     }
   };
   if (wave_on)
@@ -590,6 +643,42 @@ genrank_status check_attn_args(const genrank_batch* b, const int32_t* offsets, c
   return GENRANK_OK;
 }
 
+genrank_status launch_hstu_attn_fwd(const genrank_batch* b, const int32_t* offsets, const void* rab,
+                                    const int64_t* rab_off, const void* q, const void* k,
+                                    const void* v, int64_t ld_qkv, void* o, int64_t ld_o, float* lse,
+                                    hipStream_t stream) {
+  if (b->dtype != GENRANK_BF16) return GENRANK_E_DTYPE;
+  if (b->dh != DH || ld_qkv < b->d || ld_o < b->d || ld_qkv % 8 || ld_o % 4) return GENRANK_E_SHAPE;
+  if ((2 * static_cast<int64_t>(b->max_hist) + AK) * ld_qkv * 2 >= (int64_t{1} << 31)) return GENRANK_E_SHAPE;
+  const int64_t Lmax = 2 * static_cast<int64_t>(b->max_hist) + b->m;
+  if (Lmax * ((Lmax + 7) & ~int64_t{7}) * 2 >= (int64_t{1} << 32)) return GENRANK_E_SHAPE;
+  const int64_t T = 2 * b->total_hist + static_cast<int64_t>(b->B) * b->m;
+  if (T == 0) return GENRANK_OK;
+  AttnArgs a{};
+  a.offsets = offsets;
+  a.q = static_cast<const bf16_t*>(q);
+  a.k = static_cast<const bf16_t*>(k);
+  a.v = static_cast<const bf16_t*>(v);
+  a.ld_qkv = ld_qkv;
+  a.o = static_cast<bf16_t*>(o);
+  a.ld_o = ld_o;
+  a.lse = lse;
+  a.scale2 = LOG2E / sqrtf(static_cast<float>(b->dh));
+  a.B = b->B; a.m = b->m; a.H = b->H;
+  a.hist_tiles = static_cast<int>((2 * static_cast<int64_t>(b->max_hist) + AQ - 1) / AQ);
+  a.cand_tiles = (b->m + AQ - 1) / AQ;
+  a.T_h = 2 * b->total_hist;
+  a.rab = static_cast<const bf16_t*>(rab);
+  a.rab_off = rab_off;
+  if (a.hist_tiles + a.cand_tiles == 0) return GENRANK_OK;
+  const int64_t pairs = (static_cast<int64_t>(b->B) * b->H + 8 * GROUP - 1) / (8 * GROUP) * (8 * GROUP);
+  const int64_t G = pairs * (a.hist_tiles + a.cand_tiles);
+  if (G > INT32_MAX) return GENRANK_E_SHAPE;
+  hipLaunchKernelGGL(attn_fwd_bf16_kernel<true>, dim3(static_cast<unsigned>(G)), dim3(NT), 0, stream, a);
+  GR_CHECK_LAUNCH();
+  return GENRANK_OK;
+}
+
 genrank_status launch_attn_fwd(const genrank_batch* b, const int32_t* offsets, const int64_t* ts,
                                const int64_t* req, genrank_alibi alibi, const void* q,
                                const void* k, const void* v, int64_t ld_qkv, void* o,
@@ -619,7 +708,7 @@ genrank_status launch_attn_fwd(const genrank_batch* b, const int32_t* offsets, c
     const int64_t pairs = (static_cast<int64_t>(b->B) * b->H + 8 * GROUP - 1) / (8 * GROUP) * (8 * GROUP);
     const int64_t G = pairs * (a.hist_tiles + a.cand_tiles);
     if (G > INT32_MAX) return GENRANK_E_SHAPE;
-    hipLaunchKernelGGL(attn_fwd_bf16_kernel, dim3(static_cast<unsigned>(G)), dim3(NT), 0, stream, a);
+    hipLaunchKernelGGL(attn_fwd_bf16_kernel<false>, dim3(static_cast<unsigned>(G)), dim3(NT), 0, stream, a);
   } else {
     AttnF32Args a{};
     a.offsets = offsets; a.ts = ts; a.req = req;

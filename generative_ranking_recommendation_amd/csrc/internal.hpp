@@ -46,6 +46,18 @@ genrank_status launch_attn_bwd(const genrank_batch* b, const int32_t* offsets, c
                                void* dk, void* dv, int64_t ld_dqkv, int cand_only, void* ws,
                                hipStream_t stream);
 
+// HSTU-style comparison (interleaved sequence, learned bias in memory)
+genrank_status launch_hstu_rab_layout(const genrank_batch* b, const int32_t* offsets, int64_t* rab_off,
+                                      hipStream_t stream);
+genrank_status launch_hstu_rab(const genrank_batch* b, const int32_t* offsets, const int64_t* ts,
+                               const int64_t* req, const float* pos_table, int n_pos,
+                               const float* time_table, const int64_t* bounds, int n_time,
+                               const int64_t* rab_off, void* rab, hipStream_t stream);
+genrank_status launch_hstu_attn_fwd(const genrank_batch* b, const int32_t* offsets, const void* rab,
+                                    const int64_t* rab_off, const void* q, const void* k,
+                                    const void* v, int64_t ld_qkv, void* o, int64_t ld_o, float* lse,
+                                    hipStream_t stream);
+
 // GEMM: C = A W^T (A [M, K], W [N, K]) with an epilogue
 genrank_status launch_gemm_nt(int dtype, const void* A, int64_t lda, const void* W, int64_t ldw,
                               void* C, int64_t ldc, int M, int N, int K, int epi, const void* R,

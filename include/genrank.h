@@ -317,6 +317,41 @@ GENRANK_API genrank_status genrank_debug_mask(const genrank_batch* batch, const 
                                   int32_t user, int32_t L_cap, uint8_t* out,
                                   genrank_stream_t stream);
 
+/* ---- HSTU-style comparison path ("一、 GenRank [2025]" section 1.4.1: the interleaved
+ * item/action organisation the action-oriented sequence replaces; "The Overall Generative
+ * Ranking Paradigm" section 7.2.2: a learned relative bias).  Measured against the ALiBi path;
+ * not part of the ranking forward.
+ * User u's sequence: slots 0 .. 2N_u-1 alternate the item and the action token of history
+ * action i (both at time hist_ts[i], position = slot), then the m candidates (position 2N_u,
+ * time req_ts[u]); L_u = 2N_u + m.  Its bias matrix is [L_u, P_u] bf16 (row pitch
+ * P_u = L_u rounded up to a multiple of 8) at element offset rab_offsets[u]:
+ *   rab[i][j] = pos_table[min(|p_i - p_j|, n_pos - 1)] + time_table[#{k : time_bounds[k] <= |t_i - t_j|}]
+ * summed in f32, rounded to bf16 (round to nearest even); pad columns are 0.
+ * q/k/v/o rows: [0, 2 T_h) the interleaved history, user after user (user u at rows
+ * 2 hist_offsets[u] ..), then candidate c of user u at row 2 T_h + u m + c. */
+
+/* rab_offsets (device int64 [B + 1]): exclusive prefix sums of L_u * P_u; rab_offsets[B] is
+ * the element count of the whole bias buffer. */
+GENRANK_API genrank_status genrank_hstu_rab_layout(const genrank_batch* batch, const int32_t* hist_offsets,
+                                       int64_t* rab_offsets, genrank_stream_t stream);
+/* Materialises every user's bias matrix into rab (device, rab_offsets[B] bf16 elements).
+ * pos_table: f32 [n_pos] (n_pos >= 1); time_table: f32 [n_time]; time_bounds: int64
+ * [n_time - 1], non-decreasing.  E_SHAPE if 2 * max_hist + m > 2048, n_pos > 1024 or
+ * n_time - 1 > 1024. */
+GENRANK_API genrank_status genrank_hstu_rab(const genrank_batch* batch, const int32_t* hist_offsets,
+                                const int64_t* hist_ts, const int64_t* req_ts,
+                                const float* pos_table, int32_t n_pos, const float* time_table,
+                                const int64_t* time_bounds, int32_t n_time,
+                                const int64_t* rab_offsets, void* rab, genrank_stream_t stream);
+/* Attention over the interleaved sequences: softmax(q k^T / sqrt(dh) + rab) over the mask
+ * of genrank_attn_fwd with 2N_u history slots (history causal, candidates see every history
+ * slot and themselves), o = P v, lse (f32 [rows, H], natural log, or NULL).  bf16 only,
+ * dh = 64, same strides and errors as genrank_attn_fwd. */
+GENRANK_API genrank_status genrank_hstu_attn_fwd(const genrank_batch* batch, const int32_t* hist_offsets,
+                                     const void* rab, const int64_t* rab_offsets, const void* q,
+                                     const void* k, const void* v, int64_t ld_qkv, void* o,
+                                     int64_t ld_o, float* lse, genrank_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -57,6 +57,7 @@ __all__ = [
     "hstu_sequence",
     "hstu_rab",
     "hstu_attn_fwd_user",
+    "hstu_times",
     "round_bf16",
 ]
 
@@ -543,17 +544,32 @@ def hstu_rab(pos, t, pos_table, time_table, time_bounds):
 
 
 def hstu_attn_fwd_user(q, k, v, rab, N, m):
-    """Softmax attention over the interleaved sequence with bias ``rab`` [L, L]; history
-    slots causal, candidates see all 2N history slots and themselves.  q/k/v [L, H, dh]."""
+    """Softmax attention over the interleaved sequence with bias ``rab`` [L, L] (one matrix
+    shared by the heads); history slots causal, candidates see all 2N history slots and
+    themselves.  q/k/v [L, H, dh].  Returns (O [L, H, dh], lse [L, H])."""
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
     L, H, dh = q.shape
     allowed = attention_mask(2 * N, m)
     o = np.zeros_like(q)
+    lse = np.zeros((L, H))
     for h in range(H):
         s = q[:, h] @ k[:, h].T / math.sqrt(dh) + np.asarray(rab, np.float64)
         s = np.where(allowed, s, -np.inf)
-        e = np.where(allowed, np.exp(s - s.max(axis=1, keepdims=True)), 0.0)
-        o[:, h] = (e / e.sum(axis=1, keepdims=True)) @ v[:, h]
-    return o
+        mx = s.max(axis=1, keepdims=True)
+        e = np.where(allowed, np.exp(s - mx), 0.0)
+        z = e.sum(axis=1, keepdims=True)
+        o[:, h] = (e / z) @ v[:, h]
+        lse[:, h] = mx[:, 0] + np.log(z[:, 0])
+    return o, lse
+
+
+def hstu_times(hist_ts, req_t, N, m):
+    """Times of the interleaved slots: both tokens of history action i carry t_i, the
+    candidates the request time (reading: an action happens at its item's time)."""
+    t = np.empty(2 * N + m, np.int64)
+    t[0:2 * N:2] = hist_ts[:N]
+    t[1:2 * N:2] = hist_ts[:N]
+    t[2 * N:] = req_t
+    return t
