@@ -289,6 +289,12 @@ genrank_status genrank_attn_bwd(const genrank_batch* b, const int32_t* offsets,
   if (!dout || !lse || !dq || !dk || !dv) return GENRANK_E_ARG;
   if (ld_dqkv < b->d) return GENRANK_E_SHAPE;
   if (b->dh > 64) return GENRANK_E_SHAPE;
+  if (b->dtype == GENRANK_BF16) {  // 16-byte fragments of dout, 8-byte ones of dq, dk, dv
+    if (ld_o % 8 || ld_dqkv % 4) return GENRANK_E_SHAPE;
+    if (reinterpret_cast<uintptr_t>(dout) % 16 ||
+        (reinterpret_cast<uintptr_t>(dq) | reinterpret_cast<uintptr_t>(dk) | reinterpret_cast<uintptr_t>(dv)) % 8)
+      return GENRANK_E_ARG;
+  }
   if (!ws || ws_bytes < attn_bwd_workspace(b)) return GENRANK_E_WORKSPACE;
   return launch_attn_bwd(b, offsets, ts, req, alibi, q, k, v, ld_qkv, o, dout, ld_o, lse, dq, dk,
                          dv, ld_dqkv, cand_only, ws, S(stream));

@@ -157,6 +157,480 @@ __global__ void __launch_bounds__(64) dkv_kernel(BwdArgs a) {
   }
 }
 
+// ------------------------------------------------------------------ MFMA kernels (bf16, dh = 64)
+// The same products as above, on 64 x 64 tiles with v_mfma_f32_16x16x32_bf16 and the
+// forward's conventions: scores in log2 units, the bias as w_j - w_i against a reference
+// point of the query tile (its first query, or the candidates' shared (N, request time)), so
+//   P_ij = exp2(q_i.k_j scale2 + w_j - c_i),  c_i = w_i + lse_i log2(e).
+// dQ kernel: one 256-thread workgroup per 64-query tile (4 waves x 16 queries, one query per
+//   lane as in the forward): per key tile S^T = K Q^T and dP^T = V dO^T (K, V rows in LDS,
+//   Q, dO fragments in registers), dS^T = P^T (dP^T - D), dQ^T += K^T dS^T (K^T in LDS with
+//   its keys permuted to match the registers).  Candidate tiles also take the candidate's
+//   own key, which gives the candidate rows their whole dK and dV.
+// dK/dV kernel: one workgroup per 64-key history tile (4 waves x 16 keys, one key per lane):
+//   per query tile that sees the keys (every later history tile unless the loss sits at
+//   the candidates only, then every candidate tile) S = Q K^T and dP = dO V^T (Q, dO rows in
+//   LDS, K, V fragments in registers), dV^T += dO^T P and dK^T += Q^T dS (Q^T, dO^T in LDS
+//   with the queries permuted to match).
+constexpr int TB = 64;      // rows per tile (queries or keys)
+constexpr int DHB = 64;     // head dim
+constexpr int PLD = 72;     // LDS row pitch (bf16)
+constexpr int BWCH = 512;   // keys whose bias terms sit in LDS at a time
+constexpr int BUF_DWORD3_B = 0x00020000;
+constexpr float LOG2E_B = 1.4426950408889634f;
+
+struct BwdMArgs {
+  const int32_t* offsets;
+  const int64_t* ts;
+  const int64_t* req;
+  const bf16_t* q; const bf16_t* k; const bf16_t* v; int64_t ld_qkv;
+  const bf16_t* dout; int64_t ld_o;
+  const float* lse;
+  const float* delta;
+  bf16_t* dq; bf16_t* dk; bf16_t* dv; int64_t ld_d;
+  float sp2[GENRANK_MAX_HEADS];
+  float st2[GENRANK_MAX_HEADS];
+  float scale2, scale;
+  int B, m, H, hist_tiles, cand_tiles, cand_only;
+  int64_t T_h;
+};
+
+// slot of row j (0..63 of a tile) in the permuted axis: the 8 values a lane packs from two
+// 16-row MFMA result blocks land in 8 consecutive slots
+__device__ __forceinline__ int perm_slot(int j) {
+  const int ks = j >> 5, r = j & 31, hi = r >> 4, rr = r & 15;
+  return ks * 32 + (rr >> 2) * 8 + hi * 4 + (rr & 3);
+}
+__device__ __forceinline__ float bxor16_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float bxor32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float dot16(const uint4& a0, const uint4& a1, const uint4& b0, const uint4& b1) {
+  float fa[8], fb[8], s = 0.f;
+  unpack8(a0, fa); unpack8(b0, fb);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) s += fa[e] * fb[e];
+  unpack8(a1, fa); unpack8(b1, fb);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) s += fa[e] * fb[e];
+  return s;
+}
+// row-pair staging: a thread moves rows 2pr, 2pr+1, columns 8ch..8ch+7 of a 64 x 64 tile
+// into a row-major copy and a transposed copy with permuted rows
+__device__ __forceinline__ void stash_pair(bf16_t* rows, bf16_t* tr, int pr, int ch, const uint4& ra,
+                                           const uint4& rb) {
+  *reinterpret_cast<uint4*>(rows + (2 * pr) * PLD + ch * 8) = ra;
+  *reinterpret_cast<uint4*>(rows + (2 * pr + 1) * PLD + ch * 8) = rb;
+  uint32_t* col = reinterpret_cast<uint32_t*>(tr + ch * 8 * PLD + perm_slot(2 * pr));
+  constexpr int P = PLD / 2;
+  col[0 * P] = __builtin_amdgcn_perm(rb.x, ra.x, 0x05040100u);
+  col[1 * P] = __builtin_amdgcn_perm(rb.x, ra.x, 0x07060302u);
+  col[2 * P] = __builtin_amdgcn_perm(rb.y, ra.y, 0x05040100u);
+  col[3 * P] = __builtin_amdgcn_perm(rb.y, ra.y, 0x07060302u);
+  col[4 * P] = __builtin_amdgcn_perm(rb.z, ra.z, 0x05040100u);
+  col[5 * P] = __builtin_amdgcn_perm(rb.z, ra.z, 0x07060302u);
+  col[6 * P] = __builtin_amdgcn_perm(rb.w, ra.w, 0x05040100u);
+  col[7 * P] = __builtin_amdgcn_perm(rb.w, ra.w, 0x07060302u);
+}
+// pack the 8 values a lane holds for two 16-row result blocks into an MFMA operand
+__device__ __forceinline__ bf16x8_t pack_blocks(const f32x4_t& lo, const f32x4_t& hi) {
+  uint4 p;
+  p.x = pack_bf16x2(lo[0], lo[1]);
+  p.y = pack_bf16x2(lo[2], lo[3]);
+  p.z = pack_bf16x2(hi[0], hi[1]);
+  p.w = pack_bf16x2(hi[2], hi[3]);
+  return as_bf16x8(p);
+}
+
+__global__ void __launch_bounds__(256) attn_bwd_dq_kernel(BwdMArgs a) {
+  __shared__ __attribute__((aligned(16))) bf16_t sK[2][TB * PLD];
+  __shared__ __attribute__((aligned(16))) bf16_t sKt[2][DHB * PLD];
+  __shared__ __attribute__((aligned(16))) bf16_t sV[2][TB * PLD];
+  __shared__ __attribute__((aligned(16))) float sW[BWCH];
+
+  const int u = blockIdx.x / a.H;
+  const int h = blockIdx.x - u * a.H;
+  const int y = blockIdx.y;
+  const int64_t off = a.offsets[u];
+  const int N = a.offsets[u + 1] - a.offsets[u];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, g4 = lane >> 4;
+
+  bool is_cand;
+  int q0, nq, n_tiles;
+  int64_t qrow0;
+  if (y < a.cand_tiles) {
+    is_cand = true;
+    q0 = y * TB;
+    if (q0 >= a.m) return;
+    nq = min(TB, a.m - q0);
+    qrow0 = a.T_h + static_cast<int64_t>(u) * a.m + q0;
+    n_tiles = (N + TB - 1) / TB;
+  } else {
+    is_cand = false;
+    q0 = (y - a.cand_tiles) * TB;
+    if (q0 >= N) return;
+    nq = min(TB, N - q0);
+    qrow0 = off + q0;
+    n_tiles = (q0 + nq + TB - 1) / TB;
+    if (a.cand_only) {  // the history rows carry no gradient: dQ = 0
+      for (int e = tid; e < nq * (DHB / 4); e += 256) {
+        const int r = e / (DHB / 4), c = (e - r * (DHB / 4)) * 4;
+        *reinterpret_cast<uint2*>(a.dq + (qrow0 + r) * a.ld_d + h * DHB + c) = make_uint2(0u, 0u);
+      }
+      return;
+    }
+  }
+
+  const float sp2 = a.sp2[h], st2 = a.st2[h];
+  const int p_ref = is_cand ? N : q0;
+  const int64_t ts_ref = is_cand ? a.req[u] : a.ts[off + q0];
+  auto load_w = [&](int wbase) {
+    for (int j = tid; j < BWCH; j += 256) {
+      const int key = wbase + j;
+      sW[j] = key < N ? sp2 * static_cast<float>(key - p_ref) +
+                            st2 * static_cast<float>(static_cast<int32_t>(a.ts[off + key] - ts_ref))
+                      : 0.f;
+    }
+  };
+  const int kt_first = n_tiles - 1;
+  int wbase = n_tiles > 0 ? (kt_first * TB / BWCH) * BWCH : 0;
+
+  // this lane's query
+  const int q_local = wave * 16 + l16;
+  const bool q_valid = q_local < nq;
+  const int64_t qrow = qrow0 + min(q_local, nq - 1);
+  const int q_slot = is_cand ? N + q0 + q_local : q0 + q_local;
+  const int k_lim = is_cand ? N - 1 : min(q_slot, N - 1);
+  const int64_t ro = qrow * a.ld_qkv + h * DHB;
+  const int64_t rdo = qrow * a.ld_o + h * DHB;
+  const uint4 qa = *reinterpret_cast<const uint4*>(a.q + ro + g4 * 8);
+  const uint4 qb = *reinterpret_cast<const uint4*>(a.q + ro + g4 * 8 + 32);
+  const uint4 da = *reinterpret_cast<const uint4*>(a.dout + rdo + g4 * 8);
+  const uint4 db = *reinterpret_cast<const uint4*>(a.dout + rdo + g4 * 8 + 32);
+  bf16x8_t qf[2] = {as_bf16x8(qa), as_bf16x8(qb)};
+  bf16x8_t dof[2] = {as_bf16x8(da), as_bf16x8(db)};
+  const float lse2 = a.lse[qrow * a.H + h] * LOG2E_B;
+  const float Di = a.delta[qrow * a.H + h];
+  float w_i = 0.f;
+  if (!is_cand)
+    w_i = sp2 * static_cast<float>(q_slot - p_ref) +
+          st2 * static_cast<float>(static_cast<int32_t>(a.ts[off + min(q_slot, N - 1)] - ts_ref));
+  const float c_i = w_i + lse2;
+
+  f32x4_t accQ[4];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) accQ[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // a candidate's own key: P_ii, dS_ii from dot products over the lane group's 16 dims, then
+  // dQ_i += dS_ii k_i, dK_i = dS_ii q_i scale, dV_i = P_ii dO_i (the candidate key's only terms)
+  if (is_cand) {
+    const uint4 ka = *reinterpret_cast<const uint4*>(a.k + ro + g4 * 8);
+    const uint4 kb = *reinterpret_cast<const uint4*>(a.k + ro + g4 * 8 + 32);
+    const uint4 va = *reinterpret_cast<const uint4*>(a.v + ro + g4 * 8);
+    const uint4 vb = *reinterpret_cast<const uint4*>(a.v + ro + g4 * 8 + 32);
+    const float sqk = bxor32_sum(bxor16_sum(dot16(qa, qb, ka, kb)));
+    const float sdv = bxor32_sum(bxor16_sum(dot16(da, db, va, vb)));
+    const float p = __builtin_amdgcn_exp2f(sqk * a.scale2 - c_i);
+    const float ds = p * (sdv - Di);
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const int dcol = nb * 16 + g4 * 4;
+      const uint2 kk = *reinterpret_cast<const uint2*>(a.k + ro + dcol);
+      const uint2 qq = *reinterpret_cast<const uint2*>(a.q + ro + dcol);
+      const uint2 dd = *reinterpret_cast<const uint2*>(a.dout + rdo + dcol);
+      const float kf[4] = {__uint_as_float(kk.x << 16), __uint_as_float(kk.x & 0xFFFF0000u),
+                           __uint_as_float(kk.y << 16), __uint_as_float(kk.y & 0xFFFF0000u)};
+      const float qv[4] = {__uint_as_float(qq.x << 16), __uint_as_float(qq.x & 0xFFFF0000u),
+                           __uint_as_float(qq.y << 16), __uint_as_float(qq.y & 0xFFFF0000u)};
+      const float dv[4] = {__uint_as_float(dd.x << 16), __uint_as_float(dd.x & 0xFFFF0000u),
+                           __uint_as_float(dd.y << 16), __uint_as_float(dd.y & 0xFFFF0000u)};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) accQ[nb][i] += ds * kf[i];
+      if (q_valid) {
+        const int64_t dro = qrow * a.ld_d + h * DHB + dcol;
+        uint2 o;
+        o.x = pack_bf16x2(ds * qv[0] * a.scale, ds * qv[1] * a.scale);
+        o.y = pack_bf16x2(ds * qv[2] * a.scale, ds * qv[3] * a.scale);
+        *reinterpret_cast<uint2*>(a.dk + dro) = o;
+        o.x = pack_bf16x2(p * dv[0], p * dv[1]);
+        o.y = pack_bf16x2(p * dv[2], p * dv[3]);
+        *reinterpret_cast<uint2*>(a.dv + dro) = o;
+      }
+    }
+  }
+
+  // K/V staging (rows 2pr, 2pr+1, columns 8ch..8ch+7), one tile ahead, buffer loads over the
+  // user's history rows (rows past it read as zero)
+  const int pr = tid & 31, ch = tid >> 5;
+  const uint32_t row_bytes = static_cast<uint32_t>(a.ld_qkv) * 2u;
+  const uint32_t hist_bytes = static_cast<uint32_t>(N) * row_bytes;
+  const __amdgpu_buffer_rsrc_t rsK = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16_t*>(a.k + off * a.ld_qkv), static_cast<short>(0), hist_bytes, BUF_DWORD3_B);
+  const __amdgpu_buffer_rsrc_t rsV = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16_t*>(a.v + off * a.ld_qkv), static_cast<short>(0), hist_bytes, BUF_DWORD3_B);
+  const uint32_t voA = static_cast<uint32_t>(2 * pr) * row_bytes + (h * DHB + ch * 8) * 2u;
+  const uint32_t voB = voA + row_bytes;
+  uint4 rka, rkb, rva, rvb;
+  auto fetch = [&](int kt) {
+    const uint32_t so = static_cast<uint32_t>(kt * TB) * row_bytes;
+    rka = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsK, voA, so, 0));
+    rkb = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsK, voB, so, 0));
+    rva = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsV, voA, so, 0));
+    rvb = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsV, voB, so, 0));
+  };
+  auto stash = [&](int buf) {
+    stash_pair(sK[buf], sKt[buf], pr, ch, rka, rkb);
+    *reinterpret_cast<uint4*>(&sV[buf][(2 * pr) * PLD + ch * 8]) = rva;
+    *reinterpret_cast<uint4*>(&sV[buf][(2 * pr + 1) * PLD + ch * 8]) = rvb;
+  };
+  if (n_tiles > 0) {
+    load_w(wbase);
+    fetch(kt_first);
+    stash(0);
+  }
+  asm volatile("" : "+v"(qf[0]), "+v"(qf[1]), "+v"(dof[0]), "+v"(dof[1]));
+  __syncthreads();
+
+  const int klim_min = is_cand ? N - 1 : q0;
+  for (int it = 0; it < n_tiles; ++it) {
+    const int kt = kt_first - it;
+    const int buf = it & 1;
+    const int base = kt * TB;
+    if (base < wbase) {
+      __syncthreads();
+      wbase -= BWCH;
+      load_w(wbase);
+      __syncthreads();
+    }
+    if (kt > 0) fetch(kt - 1);
+    const bool masked = base + TB - 1 > klim_min;
+    f32x4_t s[4], dp[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      s[kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      dp[kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8_t kf = as_bf16x8(*reinterpret_cast<const uint4*>(&sK[buf][(kb * 16 + l16) * PLD + ks * 32 + g4 * 8]));
+        const bf16x8_t vf = as_bf16x8(*reinterpret_cast<const uint4*>(&sV[buf][(kb * 16 + l16) * PLD + ks * 32 + g4 * 8]));
+        s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], s[kb], 0, 0, 0);
+        dp[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, dof[ks], dp[kb], 0, 0, 0);
+      }
+    }
+    // P^T and dS^T for keys base + kb*16 + 4*g4 + i of this lane's query
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const float4 w = reinterpret_cast<const float4*>(sW)[((base - wbase) >> 2) + kb * 4 + g4];
+      const float wv[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float p = __builtin_amdgcn_exp2f(s[kb][i] * a.scale2 + wv[i] - c_i);
+        if (masked && base + kb * 16 + g4 * 4 + i > k_lim) p = 0.f;
+        s[kb][i] = p * (dp[kb][i] - Di);
+      }
+    }
+    // dQ^T += K^T dS^T
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const bf16x8_t dsf = pack_blocks(s[2 * ks], s[2 * ks + 1]);
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        const bf16x8_t ktf = as_bf16x8(*reinterpret_cast<const uint4*>(&sKt[buf][(nb * 16 + l16) * PLD + ks * 32 + g4 * 8]));
+        accQ[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ktf, dsf, accQ[nb], 0, 0, 0);
+      }
+    }
+    if (kt > 0) stash(buf ^ 1);
+    __syncthreads();
+  }
+
+  if (q_valid) {
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      uint2 o;
+      o.x = pack_bf16x2(accQ[nb][0] * a.scale, accQ[nb][1] * a.scale);
+      o.y = pack_bf16x2(accQ[nb][2] * a.scale, accQ[nb][3] * a.scale);
+      *reinterpret_cast<uint2*>(a.dq + qrow * a.ld_d + h * DHB + nb * 16 + g4 * 4) = o;
+    }
+  }
+}
+
+__global__ void __launch_bounds__(256) attn_bwd_dkv_kernel(BwdMArgs a) {
+  __shared__ __attribute__((aligned(16))) bf16_t sQ[2][TB * PLD];
+  __shared__ __attribute__((aligned(16))) bf16_t sQt[2][DHB * PLD];
+  __shared__ __attribute__((aligned(16))) bf16_t sO[2][TB * PLD];
+  __shared__ __attribute__((aligned(16))) bf16_t sOt[2][DHB * PLD];
+  __shared__ __attribute__((aligned(16))) float sC[2][TB];
+  __shared__ __attribute__((aligned(16))) float sD[2][TB];
+
+  const int u = blockIdx.x / a.H;
+  const int h = blockIdx.x - u * a.H;
+  const int kt = blockIdx.y;
+  const int64_t off = a.offsets[u];
+  const int N = a.offsets[u + 1] - a.offsets[u];
+  const int k0 = kt * TB;
+  if (k0 >= N) return;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, g4 = lane >> 4;
+  const float sp2 = a.sp2[h], st2 = a.st2[h];
+
+  // this lane's key
+  const int j = k0 + wave * 16 + l16;
+  const bool key_valid = j < N;
+  const int64_t krow = off + min(j, N - 1);
+  const int64_t rk = krow * a.ld_qkv + h * DHB;
+  bf16x8_t kf[2], vf[2];
+  kf[0] = as_bf16x8(*reinterpret_cast<const uint4*>(a.k + rk + g4 * 8));
+  kf[1] = as_bf16x8(*reinterpret_cast<const uint4*>(a.k + rk + g4 * 8 + 32));
+  vf[0] = as_bf16x8(*reinterpret_cast<const uint4*>(a.v + rk + g4 * 8));
+  vf[1] = as_bf16x8(*reinterpret_cast<const uint4*>(a.v + rk + g4 * 8 + 32));
+  const int64_t ts_j = a.ts[krow];
+
+  // query tiles that see these keys: history tiles kt .. (unless only candidates carry a
+  // gradient), then every candidate tile
+  const int n_ht = (N + TB - 1) / TB;
+  const int n_ct = (a.m + TB - 1) / TB;
+  const int h_first = a.cand_only ? n_ht : kt;
+  const int n_qt = (n_ht - h_first) + n_ct;
+  struct QT { bool cand; int q0, nq; int64_t row0; };
+  auto qtile = [&](int qi) {
+    QT t;
+    const int ht = h_first + qi;
+    t.cand = ht >= n_ht;
+    if (t.cand) {
+      t.q0 = (ht - n_ht) * TB;
+      t.nq = min(TB, a.m - t.q0);
+      t.row0 = a.T_h + static_cast<int64_t>(u) * a.m + t.q0;
+    } else {
+      t.q0 = ht * TB;
+      t.nq = min(TB, N - t.q0);
+      t.row0 = off + t.q0;
+    }
+    return t;
+  };
+
+  // staging of a query tile: Q and dO rows 2pr, 2pr+1 (clamped to the tile), columns
+  // 8ch..8ch+7; threads 0..63 also compute c_i and D_i of query tid
+  const int pr = tid & 31, ch = tid >> 5;
+  uint4 rqa, rqb, roa, rob;
+  float rc = 0.f, rd = 0.f;
+  auto fetch = [&](const QT& t) {
+    const int64_t ra = t.row0 + min(2 * pr, t.nq - 1), rb = t.row0 + min(2 * pr + 1, t.nq - 1);
+    rqa = *reinterpret_cast<const uint4*>(a.q + ra * a.ld_qkv + h * DHB + ch * 8);
+    rqb = *reinterpret_cast<const uint4*>(a.q + rb * a.ld_qkv + h * DHB + ch * 8);
+    roa = *reinterpret_cast<const uint4*>(a.dout + ra * a.ld_o + h * DHB + ch * 8);
+    rob = *reinterpret_cast<const uint4*>(a.dout + rb * a.ld_o + h * DHB + ch * 8);
+    if (tid < TB) {
+      const int ql = min(tid, t.nq - 1);
+      const int64_t r = t.row0 + ql;
+      float w_i = 0.f;
+      if (!t.cand)
+        w_i = sp2 * static_cast<float>(ql) +
+              st2 * static_cast<float>(static_cast<int32_t>(a.ts[off + t.q0 + ql] - a.ts[off + t.q0]));
+      rc = w_i + a.lse[r * a.H + h] * LOG2E_B;
+      rd = a.delta[r * a.H + h];
+    }
+  };
+  auto stash = [&](int buf) {
+    stash_pair(sQ[buf], sQt[buf], pr, ch, rqa, rqb);
+    stash_pair(sO[buf], sOt[buf], pr, ch, roa, rob);
+    if (tid < TB) {
+      sC[buf][tid] = rc;
+      sD[buf][tid] = rd;
+    }
+  };
+
+  f32x4_t accK[4], accV[4];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    accK[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    accV[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  if (n_qt > 0) {
+    fetch(qtile(0));
+    stash(0);
+  }
+  asm volatile("" : "+v"(kf[0]), "+v"(kf[1]), "+v"(vf[0]), "+v"(vf[1]));
+  __syncthreads();
+
+  for (int qi = 0; qi < n_qt; ++qi) {
+    const int buf = qi & 1;
+    const QT t = qtile(qi);
+    if (qi + 1 < n_qt) fetch(qtile(qi + 1));
+    // this tile's bias reference: its first query, or the candidates' (N, request time)
+    const int p_ref = t.cand ? N : t.q0;
+    const int64_t ts_ref = t.cand ? a.req[u] : a.ts[off + t.q0];
+    const float w_j = sp2 * static_cast<float>(j - p_ref) + st2 * static_cast<float>(static_cast<int32_t>(ts_j - ts_ref));
+    f32x4_t s[4], dp[4];
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb) {
+      s[qb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      dp[qb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8_t qf = as_bf16x8(*reinterpret_cast<const uint4*>(&sQ[buf][(qb * 16 + l16) * PLD + ks * 32 + g4 * 8]));
+        const bf16x8_t of = as_bf16x8(*reinterpret_cast<const uint4*>(&sO[buf][(qb * 16 + l16) * PLD + ks * 32 + g4 * 8]));
+        s[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf, kf[ks], s[qb], 0, 0, 0);
+        dp[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(of, vf[ks], dp[qb], 0, 0, 0);
+      }
+    }
+    // P and dS for queries qb*16 + 4*g4 + i of the tile and this lane's key
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb) {
+      const float4 c4 = reinterpret_cast<const float4*>(sC[buf])[qb * 4 + g4];
+      const float4 d4 = reinterpret_cast<const float4*>(sD[buf])[qb * 4 + g4];
+      const float cv[4] = {c4.x, c4.y, c4.z, c4.w};
+      const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int ql = qb * 16 + g4 * 4 + i;
+        const int slot = t.cand ? N + t.q0 + ql : t.q0 + ql;
+        const bool ok = key_valid && ql < t.nq && (t.cand || j <= slot);
+        const float p = ok ? __builtin_amdgcn_exp2f(s[qb][i] * a.scale2 + w_j - cv[i]) : 0.f;
+        s[qb][i] = p;
+        dp[qb][i] = p * (dp[qb][i] - dv[i]);
+      }
+    }
+    // dV^T += dO^T P,  dK^T += Q^T dS
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const bf16x8_t pf = pack_blocks(s[2 * ks], s[2 * ks + 1]);
+      const bf16x8_t dsf = pack_blocks(dp[2 * ks], dp[2 * ks + 1]);
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        const bf16x8_t otf = as_bf16x8(*reinterpret_cast<const uint4*>(&sOt[buf][(nb * 16 + l16) * PLD + ks * 32 + g4 * 8]));
+        const bf16x8_t qtf = as_bf16x8(*reinterpret_cast<const uint4*>(&sQt[buf][(nb * 16 + l16) * PLD + ks * 32 + g4 * 8]));
+        accV[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(otf, pf, accV[nb], 0, 0, 0);
+        accK[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qtf, dsf, accK[nb], 0, 0, 0);
+      }
+    }
+    if (qi + 1 < n_qt) stash(buf ^ 1);
+    __syncthreads();
+  }
+
+  if (key_valid) {
+    const int64_t dro = krow * a.ld_d + h * DHB;
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      uint2 o;
+      o.x = pack_bf16x2(accK[nb][0] * a.scale, accK[nb][1] * a.scale);
+      o.y = pack_bf16x2(accK[nb][2] * a.scale, accK[nb][3] * a.scale);
+      *reinterpret_cast<uint2*>(a.dk + dro + nb * 16 + g4 * 4) = o;
+      o.x = pack_bf16x2(accV[nb][0], accV[nb][1]);
+      o.y = pack_bf16x2(accV[nb][2], accV[nb][3]);
+      *reinterpret_cast<uint2*>(a.dv + dro + nb * 16 + g4 * 4) = o;
+    }
+  }
+}
+
 }  // namespace
 
 size_t attn_bwd_workspace(const genrank_batch* b) {
@@ -186,10 +660,30 @@ genrank_status launch_attn_bwd(const genrank_batch* b, const int32_t* offsets, c
   a.B = b->B; a.m = b->m; a.H = b->H; a.dh = b->dh; a.cand_only = cand_only;
   a.T_h = b->total_hist;
   dim3 grid(static_cast<unsigned>(T), b->H);
-  if (b->dtype == GENRANK_BF16) {
+  if (b->dtype == GENRANK_BF16) {  // dh == 64 and the alignments are checked by the caller
     hipLaunchKernelGGL(delta_kernel<bf16_t>, grid, dim3(64), 0, stream, a);
-    hipLaunchKernelGGL(dq_kernel<bf16_t>, grid, dim3(64), 0, stream, a);
-    hipLaunchKernelGGL(dkv_kernel<bf16_t>, grid, dim3(64), 0, stream, a);
+    BwdMArgs m{};
+    m.offsets = offsets; m.ts = ts; m.req = req;
+    m.q = static_cast<const bf16_t*>(q); m.k = static_cast<const bf16_t*>(k); m.v = static_cast<const bf16_t*>(v);
+    m.ld_qkv = ld_qkv;
+    m.dout = static_cast<const bf16_t*>(dout); m.ld_o = ld_o;
+    m.lse = lse; m.delta = a.delta;
+    m.dq = static_cast<bf16_t*>(dq); m.dk = static_cast<bf16_t*>(dk); m.dv = static_cast<bf16_t*>(dv);
+    m.ld_d = ld_dqkv;
+    for (int h = 0; h < b->H; ++h) {
+      m.sp2[h] = alibi.slopes_pos[h] * LOG2E_B;
+      m.st2[h] = alibi.slopes_time[h] * LOG2E_B;
+    }
+    m.scale = 1.f / sqrtf(static_cast<float>(b->dh));
+    m.scale2 = m.scale * LOG2E_B;
+    m.B = b->B; m.m = b->m; m.H = b->H; m.cand_only = cand_only;
+    m.hist_tiles = (b->max_hist + TB - 1) / TB;
+    m.cand_tiles = (b->m + TB - 1) / TB;
+    m.T_h = b->total_hist;
+    if (m.hist_tiles + m.cand_tiles > 0)
+      hipLaunchKernelGGL(attn_bwd_dq_kernel, dim3(b->B * b->H, m.cand_tiles + m.hist_tiles), dim3(256), 0, stream, m);
+    if (m.hist_tiles > 0)
+      hipLaunchKernelGGL(attn_bwd_dkv_kernel, dim3(b->B * b->H, m.hist_tiles), dim3(256), 0, stream, m);
   } else {
     hipLaunchKernelGGL(delta_kernel<float>, grid, dim3(64), 0, stream, a);
     hipLaunchKernelGGL(dq_kernel<float>, grid, dim3(64), 0, stream, a);

@@ -219,7 +219,11 @@ GENRANK_API genrank_status genrank_attn_fwd(const genrank_batch* batch, const in
  * be views into one [T, 3d] buffer) in batch.dtype.  When cand_only_dout != 0 the
  * caller asserts that dout is zero on every history row (loss at candidate positions
  * only, [GR-zh] section 1.3.1, at the last block) and the history query rows are
- * skipped.  ws: workspace of genrank_workspace_size(GENRANK_OP_ATTN_BWD) bytes. */
+ * skipped (their dq rows are written as zero).  bf16 (dh == 64): tiled MFMA kernels
+ * that take P and dS as bf16 operands with f32 accumulation; ld_o must be a multiple of 8
+ * and ld_dqkv of 4 (else GENRANK_E_SHAPE), dout 16-byte and dq, dk, dv 8-byte aligned
+ * (else GENRANK_E_ARG).  f32: per-row kernels, f32 throughout.
+ * ws: workspace of genrank_workspace_size(GENRANK_OP_ATTN_BWD) bytes. */
 GENRANK_API genrank_status genrank_attn_bwd(const genrank_batch* batch, const int32_t* hist_offsets,
                                 const int64_t* hist_ts, const int64_t* req_ts,
                                 genrank_alibi alibi, const void* q, const void* k,

@@ -101,6 +101,13 @@ def test_entry_points_reject_bad_arguments(lib):
     # attention backward: workspace too small
     assert lib.genrank_attn_bwd(ctypes.byref(bt), FAKE, FAKE, FAKE, sl.struct, FAKE, FAKE, FAKE, 768,
                                 FAKE, FAKE, 256, FAKE, FAKE, FAKE, FAKE, 768, 0, FAKE, 16, None) == -6
+    # bf16 backward: dout rows in whole 16-byte vectors, gradient rows in 8-byte ones
+    assert lib.genrank_attn_bwd(ctypes.byref(bt), FAKE, FAKE, FAKE, sl.struct, FAKE, FAKE, FAKE, 768,
+                                FAKE, FAKE, 260, FAKE, FAKE, FAKE, FAKE, 768, 0, FAKE, 1 << 40, None) == -2
+    assert lib.genrank_attn_bwd(ctypes.byref(bt), FAKE, FAKE, FAKE, sl.struct, FAKE, FAKE, FAKE, 768,
+                                FAKE, FAKE, 256, FAKE, FAKE, FAKE, FAKE, 770, 0, FAKE, 1 << 40, None) == -2
+    assert lib.genrank_attn_bwd(ctypes.byref(bt), FAKE, FAKE, FAKE, sl.struct, FAKE, FAKE, FAKE, 768,
+                                FAKE, FAKE, 256, FAKE, FAKE + 2, FAKE, FAKE, 768, 0, FAKE, 1 << 40, None) == -1
     # layer: workspace too small, missing FFN weights, bad ffn size
     w = B.make_layer_weights(FAKE, FAKE, sl, B.BLOCK_ATTN_ONLY)
     assert lib.genrank_layer_fwd(ctypes.byref(bt), ctypes.byref(w), FAKE, FAKE, FAKE, FAKE, FAKE + 64,

@@ -2,9 +2,12 @@
 candidate positions, head, blocks, embedding tables) against the oracle's fp64 gradients.
 
 Bars: f32 1e-5 of each gradient's max magnitude (absolute errors of ~1e-7 in f32 on values
-of order 1e-2..1).  bf16: the attention backward is driven with unit-scale N(0, 1) inputs and
-held to 2e-2 absolute; training-step gradients (not unit-scale) by ``bf16_close``; the
-unit-scale logits and the loss to 2e-2 absolute."""
+of order 1e-2..1).  bf16: the attention backward is driven with N(0, 1) q, k, v, dO, but its
+gradients are not unit-scale: dV_j sums P_ij dO_i over every query that sees key j, so |dV|
+reaches ~6.6 on 480-key histories and ~11.5 on 700-key ones, where one bf16 half-ulp is
+0.016 to 0.03; the tiled kernels also take P and dS as bf16 MFMA operands.  So dQ, dK, dV
+are held to ``bf16_close`` (2e-2 of the tensor's max magnitude, 1e-2 norm-wise), as are the
+training-step gradients; the unit-scale logits and the loss to 2e-2 absolute."""
 import numpy as np
 import pytest
 import torch
@@ -81,7 +84,20 @@ def test_attn_bwd_bf16(cand_only):
     got, want = _attn_case(cfg, batch, 41, cand_only)
     d = cfg.d
     for i, name in enumerate(("dq", "dk", "dv")):
-        unit_close(got[:, i * d:(i + 1) * d], want[:, i * d:(i + 1) * d], name)
+        bf16_close(got[:, i * d:(i + 1) * d], want[:, i * d:(i + 1) * d], name)
+
+
+@pytest.mark.parametrize("cand_only", [0, 1])
+def test_attn_bwd_bf16_long(cand_only):
+    """Histories past 512 keys (the bias terms are staged in 512-key chunks), an empty and a
+    one-action history, and 70 candidates (a full and a ragged 64-row tile)."""
+    say(f"bwd: attention bf16 long cand_only={cand_only}")
+    cfg = synth.make_config("train2_bf16", m=70)
+    batch = custom_batch(cfg, [700, 0, 1, 129, 576], seed=9)
+    got, want = _attn_case(cfg, batch, 43, cand_only)
+    d = cfg.d
+    for i, name in enumerate(("dq", "dk", "dv")):
+        bf16_close(got[:, i * d:(i + 1) * d], want[:, i * d:(i + 1) * d], name)
 
 
 def _oracle_train(cfg, batch, tables, weights, labels):
