@@ -85,6 +85,10 @@ _SIGS = {
     "genrank_linear": (c_int32, [c_int32, c_void_p, c_int64, c_void_p, c_int64, c_void_p, c_int64,
                                  c_int64, c_int32, c_int32, c_int32, c_void_p, c_int64, c_void_p,
                                  c_int64, c_void_p]),
+    "genrank_linear_bwd_workspace": (c_int32, [c_int32, c_int64, c_int32, c_int32, POINTER(c_size_t)]),
+    "genrank_linear_bwd": (c_int32, [c_int32, c_void_p, c_int64, c_void_p, c_int64, c_void_p, c_int64,
+                                     c_void_p, c_int64, c_void_p, c_int64, c_int64, c_int32, c_int32,
+                                     c_void_p, c_size_t, c_void_p]),
     "genrank_head_fwd": (c_int32, [POINTER(Batch), c_void_p, c_void_p, c_void_p, c_void_p, c_int32,
                                    c_void_p, c_void_p]),
     "genrank_head_bwd": (c_int32, [POINTER(Batch), c_void_p, c_void_p, c_void_p, c_int32, c_void_p,
@@ -265,6 +269,19 @@ def genrank_linear(dtype, x, ldx, w, ldw, y, ldy, M, N, K, epilogue=EPI_NONE, re
     _check("genrank_linear", lib().genrank_linear(
         dtype, _p(x), ldx, _p(w), ldw, _p(y), ldy, M, N, K, epilogue, _p(residual), ldr, _p(pre),
         ldpre, _stream(stream)))
+
+
+def genrank_linear_bwd_workspace(dtype, M, N, K):
+    n = c_size_t(0)
+    _check("genrank_linear_bwd_workspace", lib().genrank_linear_bwd_workspace(dtype, M, N, K, ctypes.byref(n)))
+    return n.value
+
+
+def genrank_linear_bwd(dtype, x, ldx, w, ldw, dy, ldy, dx, lddx, dw, lddw, M, N, K, ws, ws_bytes,
+                       stream=None):
+    _check("genrank_linear_bwd", lib().genrank_linear_bwd(
+        dtype, _p(x), ldx, _p(w), ldw, _p(dy), ldy, _p(dx), lddx, _p(dw), lddw, M, N, K, _p(ws),
+        ws_bytes, _stream(stream)))
 
 
 def genrank_head_fwd(batch, x, g_final, w_head, b_head, n_tasks, logits, stream=None):

@@ -2,6 +2,7 @@
 // composition of kernels into a block forward / backward.  Every entry point validates
 // its arguments before enqueuing anything and returns a genrank_status.
 #include <hip/hip_runtime.h>
+#include <algorithm>
 #include <math.h>
 #include <string.h>
 
@@ -81,6 +82,9 @@ struct LayerBwdWs {
   char* dh;     // [T, f]  (PRENORM) gradient of silu(a), then of a
   char* dz2;    // [T, d]  (PRENORM)
   char* attn;   // attention backward scratch
+  char* wt;     // one transposed weight (bf16 data gradients)
+  char* tn;     // split partial tiles of the weight gradients
+  size_t tn_bytes;
   size_t bytes;
 };
 
@@ -103,6 +107,16 @@ LayerBwdWs layer_bwd_layout(const genrank_batch* b, int block, int ffn, char* ba
   w.dh = pre ? take(T * static_cast<size_t>(ffn) * es) : nullptr;
   w.dz2 = pre ? take(T * d * es) : nullptr;
   w.attn = take(attn_bwd_workspace(b));
+  const int64_t Ti = static_cast<int64_t>(T);
+  const int di = static_cast<int>(d);
+  size_t wt = 3 * d * d, tn = std::max(gemm_tn_workspace(3 * di, di, Ti), gemm_tn_workspace(di, di, Ti));
+  if (pre) {
+    wt = std::max(wt, d * static_cast<size_t>(ffn));
+    tn = std::max({tn, gemm_tn_workspace(di, ffn, Ti), gemm_tn_workspace(ffn, di, Ti)});
+  }
+  w.wt = take(wt * es);
+  w.tn = take(tn);
+  w.tn_bytes = tn;
   w.bytes = off;
   return w;
 }
@@ -365,38 +379,28 @@ genrank_status genrank_layer_bwd(const genrank_batch* b, const genrank_layer_wei
   const size_t es = dtype_size(dt);
   const int F32 = GENRANK_F32;
   const void* att_grad = dy;  // gradient reaching the attention branch output
+  const int64_t Tl = T;
   if (pre) {
     // FFN branch: y = x1 + W2 silu(W1 z2)
-    GR_TRY(launch_gemm_general(dt, F32, dy, 1, d, F.hdn, ffn, 1, g.w2, ffn, d, ffn, T,
-                               GEMM_EPI_STORE, false, nullptr, 0, nullptr, 0, s));
-    GR_TRY(launch_gemm_general(dt, dt, dy, d, 1, w->w2, ffn, 1, L.dh, ffn, T, ffn, d,
-                               GEMM_EPI_STORE, false, nullptr, 0, nullptr, 0, s));
+    GR_TRY(launch_gemm_tn(dt, dy, d, F.hdn, ffn, g.w2, ffn, d, ffn, Tl, L.tn, L.tn_bytes, s));
+    GR_TRY(launch_gemm_nn(dt, dy, d, w->w2, ffn, L.dh, ffn, T, ffn, d, L.wt, s));
     GR_TRY(launch_silu_bwd(dt, F.a, L.dh, L.dh, static_cast<int64_t>(T) * ffn, s));
-    GR_TRY(launch_gemm_general(dt, F32, L.dh, 1, ffn, F.z2, d, 1, g.w1, d, ffn, d, T,
-                               GEMM_EPI_STORE, false, nullptr, 0, nullptr, 0, s));
-    GR_TRY(launch_gemm_general(dt, dt, L.dh, ffn, 1, w->w1, d, 1, L.dz2, d, T, d, ffn,
-                               GEMM_EPI_STORE, false, nullptr, 0, nullptr, 0, s));
+    GR_TRY(launch_gemm_tn(dt, L.dh, ffn, F.z2, d, g.w1, d, ffn, d, Tl, L.tn, L.tn_bytes, s));
+    GR_TRY(launch_gemm_nn(dt, L.dh, ffn, w->w1, d, L.dz2, d, T, d, ffn, L.wt, s));
     GR_TRY(launch_fill_f32(g.g2, d, 0.f, s));
     GR_TRY(launch_rmsnorm_bwd(dt, F.x1, w->g2, L.dz2, dy, L.dx1, g.g2, T, d, s));
     att_grad = L.dx1;
   }
   // attention branch: out = Wo o
-  GR_TRY(launch_gemm_general(dt, F32, att_grad, 1, d, F.o, d, 1, g.wo, d, d, d, T,
-                             GEMM_EPI_STORE, false, nullptr, 0, nullptr, 0, s));
-  GR_TRY(launch_gemm_general(dt, dt, att_grad, d, 1, w->wo, d, 1, L.dout, d, T, d, d,
-                             GEMM_EPI_STORE, false, nullptr, 0, nullptr, 0, s));
+  GR_TRY(launch_gemm_tn(dt, att_grad, d, F.o, d, g.wo, d, d, d, Tl, L.tn, L.tn_bytes, s));
+  GR_TRY(launch_gemm_nn(dt, att_grad, d, w->wo, d, L.dout, d, T, d, d, L.wt, s));
   GR_TRY(launch_attn_bwd(b, offsets, ts, req, w->alibi, F.qkv, F.qkv + d * es, F.qkv + 2 * d * es,
                          3 * d, F.o, L.dout, d, F.lse, L.dqkv, L.dqkv + d * es,
                          L.dqkv + 2 * d * es, 3 * d, cand_only, L.attn, s));
   const void* zin = pre ? static_cast<const void*>(F.z) : x_in;
-  GR_TRY(launch_gemm_general(dt, F32, L.dqkv, 1, 3 * d, zin, d, 1, g.wqkv, d, 3 * d, d, T,
-                             GEMM_EPI_STORE, false, nullptr, 0, nullptr, 0, s));
-  if (!pre) {
-    return launch_gemm_general(dt, dt, L.dqkv, 3 * d, 1, w->wqkv, d, 1, dx, d, T, d, 3 * d,
-                               GEMM_EPI_STORE, false, nullptr, 0, nullptr, 0, s);
-  }
-  GR_TRY(launch_gemm_general(dt, dt, L.dqkv, 3 * d, 1, w->wqkv, d, 1, L.dz, d, T, d, 3 * d,
-                             GEMM_EPI_STORE, false, nullptr, 0, nullptr, 0, s));
+  GR_TRY(launch_gemm_tn(dt, L.dqkv, 3 * d, zin, d, g.wqkv, d, 3 * d, d, Tl, L.tn, L.tn_bytes, s));
+  if (!pre) return launch_gemm_nn(dt, L.dqkv, 3 * d, w->wqkv, d, dx, d, T, d, 3 * d, L.wt, s);
+  GR_TRY(launch_gemm_nn(dt, L.dqkv, 3 * d, w->wqkv, d, L.dz, d, T, d, 3 * d, L.wt, s));
   GR_TRY(launch_fill_f32(g.g1, d, 0.f, s));
   return launch_rmsnorm_bwd(dt, x_in, w->g1, L.dz, L.dx1, dx, g.g1, T, d, s);
 }
@@ -424,6 +428,42 @@ genrank_status genrank_linear(int32_t dtype, const void* x, int64_t ldx, const v
   }
   return launch_gemm_nt(dtype, x, ldx, w, ldw, y, ldy, static_cast<int>(M), N, K, epi, residual, ldr,
                         pre, ldpre, S(stream));
+}
+
+namespace genrank {
+namespace {
+size_t linear_bwd_bytes(int32_t dtype, int64_t M, int32_t N, int32_t K) {
+  if (dtype != GENRANK_BF16) return 0;
+  return align_up(static_cast<size_t>(N) * K * 2) + gemm_tn_workspace(N, K, M);
+}
+}  // namespace
+}  // namespace genrank
+
+genrank_status genrank_linear_bwd_workspace(int32_t dtype, int64_t M, int32_t N, int32_t K, size_t* bytes) {
+  if (!bytes) return GENRANK_E_ARG;
+  if (dtype != GENRANK_F32 && dtype != GENRANK_BF16) return GENRANK_E_DTYPE;
+  if (M < 0 || N < 1 || K < 1 || M >= (int64_t(1) << 31)) return GENRANK_E_SHAPE;
+  *bytes = linear_bwd_bytes(dtype, M, N, K);
+  return GENRANK_OK;
+}
+
+genrank_status genrank_linear_bwd(int32_t dtype, const void* x, int64_t ldx, const void* w, int64_t ldw,
+                                  const void* dy, int64_t ldy, void* dx, int64_t lddx, float* dw,
+                                  int64_t lddw, int64_t M, int32_t N, int32_t K, void* ws,
+                                  size_t ws_bytes, genrank_stream_t stream) {
+  if (dtype != GENRANK_F32 && dtype != GENRANK_BF16) return GENRANK_E_DTYPE;
+  if (!dy || (dx && !w) || (dw && !x)) return GENRANK_E_ARG;
+  if (M < 0 || N < 1 || K < 1 || M >= (int64_t(1) << 31)) return GENRANK_E_SHAPE;
+  if (ldy < N || (dx && (ldw < K || lddx < K)) || (dw && (ldx < K || lddw < K))) return GENRANK_E_SHAPE;
+  const size_t need = linear_bwd_bytes(dtype, M, N, K);
+  if (need > 0 && (!ws || ws_bytes < need || reinterpret_cast<uintptr_t>(ws) % 16)) return GENRANK_E_WORKSPACE;
+  const hipStream_t s = S(stream);
+  char* wt = static_cast<char*>(ws);
+  char* tn = need > 0 ? wt + align_up(static_cast<size_t>(N) * K * 2) : nullptr;
+  const size_t tn_bytes = need > 0 ? need - align_up(static_cast<size_t>(N) * K * 2) : 0;
+  if (dx) GR_TRY(launch_gemm_nn(dtype, dy, ldy, w, ldw, dx, lddx, static_cast<int>(M), K, N, wt, s));
+  if (dw) GR_TRY(launch_gemm_tn(dtype, dy, ldy, x, ldx, dw, lddw, N, K, M, tn, tn_bytes, s));
+  return GENRANK_OK;
 }
 
 genrank_status genrank_head_fwd(const genrank_batch* b, const void* x, const float* g_final,

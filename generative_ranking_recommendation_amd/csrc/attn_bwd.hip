@@ -367,7 +367,8 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(BwdMArgs a) {
   }
 
   // K/V staging (rows 2pr, 2pr+1, columns 8ch..8ch+7), one tile ahead, buffer loads over the
-  // user's history rows (rows past it read as zero)
+  // user's history rows (rows past it read as zero; the whole offset sits in the vector
+  // operand, which the range check covers)
   const int pr = tid & 31, ch = tid >> 5;
   const uint32_t row_bytes = static_cast<uint32_t>(a.ld_qkv) * 2u;
   const uint32_t hist_bytes = static_cast<uint32_t>(N) * row_bytes;
@@ -380,10 +381,10 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(BwdMArgs a) {
   uint4 rka, rkb, rva, rvb;
   auto fetch = [&](int kt) {
     const uint32_t so = static_cast<uint32_t>(kt * TB) * row_bytes;
-    rka = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsK, voA, so, 0));
-    rkb = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsK, voB, so, 0));
-    rva = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsV, voA, so, 0));
-    rvb = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsV, voB, so, 0));
+    rka = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsK, voA + so, 0, 0));
+    rkb = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsK, voB + so, 0, 0));
+    rva = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsV, voA + so, 0, 0));
+    rvb = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsV, voB + so, 0, 0));
   };
   auto stash = [&](int buf) {
     stash_pair(sK[buf], sKt[buf], pr, ch, rka, rkb);

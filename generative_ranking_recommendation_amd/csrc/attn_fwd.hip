@@ -240,13 +240,14 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
   struct Stage { uint4 r0, r1; };
   Stage S0, S1;
   // A tile index below 0 gets an offset at the descriptor's record count: the hardware
-  // returns zeros without touching memory, and such a stage is never written to LDS.
+  // returns zeros without touching memory, and such a stage is never written to LDS.  The
+  // whole offset goes in the vector operand, which the range check covers.
   // Issuing every fetch keeps the count of loads in flight the same on all paths, so the
   // wait before a stash covers only that stage's own two loads.
   auto fetch = [&](int kt, Stage& S) {
     const uint32_t so = kt >= 0 ? static_cast<uint32_t>(kt * AK) * row_bytes : hist_bytes;
-    S.r0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsKV, vo0, so, 0));
-    S.r1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsKV, vo1, so, 0));
+    S.r0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsKV, vo0 + so, 0, 0));
+    S.r1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsKV, vo1 + so, 0, 0));
   };
   const int slotA = vt_slot(kA);  // the pair's second key sits at slotA + 1
   auto stash = [&](int buf, const Stage& S) {
@@ -295,7 +296,7 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
       const uint32_t so = kt >= 0 ? static_cast<uint32_t>(kt * AK) * 2u : rab_bytes;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
-        R.v[kb] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rsR, rab_row + kb * 32u, so, 0));
+        R.v[kb] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rsR, rab_row + kb * 32u + so, 0, 0));
     }
   };
   rab_load(kt_first, R0);

@@ -12,6 +12,8 @@
 //
 // A second, simple kernel handles f32 data and the transposed products of the backward
 // pass (general strides, LDS-tiled FMA).
+#include <algorithm>
+
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -351,6 +353,183 @@ __global__ void __launch_bounds__(ST * ST) gemm_general_kernel(
   C[ci] = from_f32<TO>(v);
 }
 
+// ------------------------------------------------------------------ weight-gradient GEMM
+// C[m, n] = sum_t A[t, m] B[t, n] over T rows: the weight gradient dW = dY^T X of a
+// projection Y = X W^T.  Both operands are row-major with the reduction running down their
+// rows, so the MFMA fragments (8 consecutive t per lane) come from tiles transposed on the
+// way into LDS: a thread loads 4 rows x 8 columns of each operand (four 16-byte loads),
+// packs each column's 4 values into 8 bytes and writes them to the tile [column][t].
+// Tile 128 x 128 x 64 rows of T, 2 x 2 waves of 64 x 64 as in the NT kernel.  The T rows
+// are split over S workgroups per output tile: each writes an f32 partial tile and a second
+// kernel sums the S partials in a fixed order (deterministic), so the grid fills the chip
+// even for a 256 x 256 gradient.
+constexpr int TBT = 64;          // rows of T per step
+constexpr int TP = TBT + 8;      // transposed tile pitch (bf16)
+constexpr int TTILE = 128 * TP;  // elements of one transposed operand tile
+
+struct TnArgs {
+  const bf16_t* A; int64_t lda;
+  const bf16_t* B; int64_t ldb;
+  float* C; int64_t ldc;   // the output (S == 1) or the partial tiles (pitch N)
+  int64_t split_stride;    // elements between the partial results of two splits
+  int M, N, T, chunk;      // chunk: rows of T per split, a multiple of TBT
+};
+
+__device__ __forceinline__ uint32_t word_of(const uint4& v, int j) {
+  return j == 0 ? v.x : (j == 1 ? v.y : (j == 2 ? v.z : v.w));
+}
+
+__global__ void __launch_bounds__(GTHREADS) gemm_tn_bf16_kernel(TnArgs g) {
+  __shared__ __attribute__((aligned(16))) bf16_t sA[2][TTILE];
+  __shared__ __attribute__((aligned(16))) bf16_t sB[2][TTILE];
+  const int nN = (g.N + 127) / 128;
+  const int mblk = static_cast<int>(blockIdx.x) / nN;
+  const int m0 = mblk * 128, n0 = (static_cast<int>(blockIdx.x) - mblk * nN) * 128;
+  const int t_begin = static_cast<int>(blockIdx.y) * g.chunk;
+  const int rows = min(g.chunk, g.T - t_begin);  // >= 1: the host sizes the grid to T
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 1, wn = wave >> 1;
+  const int l16 = lane & 15, g4 = lane >> 4;
+
+  // staging: rows 4 rq .. 4 rq + 3 of the step, columns 8 ch .. 8 ch + 7 of the tile; the
+  // descriptors cover this split's rows (later rows read as zero: the whole offset sits in
+  // the vector operand, which the range check covers); columns past M (N) re-read valid
+  // ones, whose results are never stored
+  const int rq = tid & 15, ch = tid >> 4;
+  const __amdgpu_buffer_rsrc_t rsA = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16_t*>(g.A + static_cast<int64_t>(t_begin) * g.lda), static_cast<short>(0),
+      static_cast<uint32_t>(rows * g.lda * 2), BUF_DWORD3);
+  const __amdgpu_buffer_rsrc_t rsB = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16_t*>(g.B + static_cast<int64_t>(t_begin) * g.ldb), static_cast<short>(0),
+      static_cast<uint32_t>(rows * g.ldb * 2), BUF_DWORD3);
+  const uint32_t voA = static_cast<uint32_t>(4 * rq * g.lda + min(m0 + 8 * ch, g.M - 8)) * 2u;
+  const uint32_t voB = static_cast<uint32_t>(4 * rq * g.ldb + min(n0 + 8 * ch, g.N - 8)) * 2u;
+  const uint32_t rowA = static_cast<uint32_t>(g.lda) * 2u, rowB = static_cast<uint32_t>(g.ldb) * 2u;
+  uint4 ra[4], rb[4];
+  auto fetch = [&](int t0) {
+    const uint32_t soA = static_cast<uint32_t>(t0) * rowA, soB = static_cast<uint32_t>(t0) * rowB;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      ra[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsA, voA + r * rowA + soA, 0, 0));
+      rb[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsB, voB + r * rowB + soB, 0, 0));
+    }
+  };
+  // column 2j (2j + 1) of the 8: the low (high) halves of word j of the four rows
+  auto put = [&](bf16_t* dst, const uint4 (&v)[4]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t w0 = word_of(v[0], j), w1 = word_of(v[1], j), w2 = word_of(v[2], j), w3 = word_of(v[3], j);
+      *reinterpret_cast<uint2*>(dst + (8 * ch + 2 * j) * TP + 4 * rq) =
+          make_uint2(__builtin_amdgcn_perm(w1, w0, 0x05040100u), __builtin_amdgcn_perm(w3, w2, 0x05040100u));
+      *reinterpret_cast<uint2*>(dst + (8 * ch + 2 * j + 1) * TP + 4 * rq) =
+          make_uint2(__builtin_amdgcn_perm(w1, w0, 0x07060302u), __builtin_amdgcn_perm(w3, w2, 0x07060302u));
+    }
+  };
+
+  f32x4_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int nsteps = (rows + TBT - 1) / TBT;
+  fetch(0);
+  put(sA[0], ra);
+  put(sB[0], rb);
+  __syncthreads();
+  for (int it = 0; it < nsteps; ++it) {
+    const int buf = it & 1;
+    if (it + 1 < nsteps) fetch((it + 1) * TBT);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8_t fb[4], fa[4];
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+        fb[nb] = as_bf16x8(*reinterpret_cast<const uint4*>(&sB[buf][(wn * 64 + nb * 16 + l16) * TP + ks * 32 + g4 * 8]));
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+        fa[mb] = as_bf16x8(*reinterpret_cast<const uint4*>(&sA[buf][(wm * 64 + mb * 16 + l16) * TP + ks * 32 + g4 * 8]));
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+          acc[nb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[nb], fa[mb], acc[nb][mb], 0, 0, 0);
+    }
+    if (it + 1 < nsteps) {
+      put(sA[buf ^ 1], ra);
+      put(sB[buf ^ 1], rb);
+    }
+    __syncthreads();
+  }
+
+  // lane holds C[m][n .. n + 3] for each (nb, mb)
+  float* C = g.C + static_cast<int64_t>(blockIdx.y) * g.split_stride;
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+    const int m = m0 + wm * 64 + mb * 16 + l16;
+    if (m >= g.M) continue;
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const int n = n0 + wn * 64 + nb * 16 + g4 * 4;
+      if (n < g.N)
+        *reinterpret_cast<float4*>(C + static_cast<int64_t>(m) * g.ldc + n) =
+            make_float4(acc[nb][mb][0], acc[nb][mb][1], acc[nb][mb][2], acc[nb][mb][3]);
+    }
+  }
+}
+
+// C[m, n] = sum over s of P[s][m, n] (partials of pitch N), s in increasing order
+__global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* P, int64_t split_stride, int S,
+                                                            float* C, int64_t ldc, int M, int N) {
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int n4 = N / 4;
+  if (e >= static_cast<int64_t>(M) * n4) return;
+  const int m = static_cast<int>(e / n4), n = static_cast<int>(e - static_cast<int64_t>(m) * n4) * 4;
+  const float* p = P + static_cast<int64_t>(m) * N + n;
+  float4 a = *reinterpret_cast<const float4*>(p);
+  for (int s = 1; s < S; ++s) {
+    const float4 b = *reinterpret_cast<const float4*>(p + s * split_stride);
+    a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+  }
+  *reinterpret_cast<float4*>(C + static_cast<int64_t>(m) * ldc + n) = a;
+}
+
+// dst[c, r] = src[r, c] for an R x C bf16 matrix, 32 x 32 tiles through LDS
+__global__ void __launch_bounds__(256) transpose_bf16_kernel(const bf16_t* src, int64_t lds, bf16_t* dst,
+                                                             int64_t ldd, int R, int C) {
+  __shared__ bf16_t t[32][33];
+  const int c0 = blockIdx.x * 32, r0 = blockIdx.y * 32;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+#pragma unroll
+  for (int i = 0; i < 32; i += 8) {
+    const int r = r0 + ty + i, c = c0 + tx;
+    if (r < R && c < C) t[ty + i][tx] = src[static_cast<int64_t>(r) * lds + c];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 32; i += 8) {
+    const int c = c0 + ty + i, r = r0 + tx;
+    if (r < R && c < C) dst[static_cast<int64_t>(c) * ldd + r] = t[tx][ty + i];
+  }
+}
+
+struct TnPlan {
+  int S, chunk;
+};
+// enough splits for ~512 workgroups, at least 256 rows each
+TnPlan tn_plan(int M, int N, int64_t T) {
+  const int tiles = ((M + 127) / 128) * ((N + 127) / 128);
+  int64_t S = (512 + tiles - 1) / tiles;
+  S = std::min<int64_t>(S, std::max<int64_t>(1, (T + 255) / 256));
+  int64_t chunk = (T + S - 1) / S;
+  chunk = (chunk + TBT - 1) / TBT * TBT;
+  S = (T + chunk - 1) / chunk;
+  return {static_cast<int>(S), static_cast<int>(chunk)};
+}
+
 }  // namespace
 
 genrank_status launch_gemm_nt(int dtype, const void* A, int64_t lda, const void* W, int64_t ldw,
@@ -434,6 +613,60 @@ genrank_status launch_gemm_general(int in_dtype, int out_dtype, const void* A, i
 #undef GR_GEN
   GR_CHECK_LAUNCH();
   return GENRANK_OK;
+}
+
+}  // namespace genrank
+
+namespace genrank {
+
+size_t gemm_tn_workspace(int M, int N, int64_t T) {
+  if (T <= 0) return 0;
+  const TnPlan p = tn_plan(M, N, T);
+  return p.S > 1 ? static_cast<size_t>(p.S) * M * N * sizeof(float) : 0;
+}
+
+genrank_status launch_gemm_tn(int dtype, const void* A, int64_t lda, const void* Bm, int64_t ldb, float* C,
+                              int64_t ldc, int M, int N, int64_t T, void* ws, size_t ws_bytes,
+                              hipStream_t stream) {
+  if (M <= 0 || N <= 0) return GENRANK_OK;
+  auto al = [](const void* p, uintptr_t n) { return reinterpret_cast<uintptr_t>(p) % n == 0; };
+  const TnPlan p = T > 0 ? tn_plan(M, N, T) : TnPlan{0, 0};
+  if (dtype == GENRANK_BF16 && T > 0 && M % 8 == 0 && N % 8 == 0 && lda % 8 == 0 && ldb % 8 == 0 &&
+      ldc % 4 == 0 && al(A, 16) && al(Bm, 16) && al(C, 16) &&
+      static_cast<int64_t>(p.chunk) * std::max(lda, ldb) * 2 < (int64_t(1) << 31)) {
+    const size_t need = gemm_tn_workspace(M, N, T);
+    if (need > 0 && (!ws || ws_bytes < need || !al(ws, 16))) return GENRANK_E_WORKSPACE;
+    TnArgs g{static_cast<const bf16_t*>(A), lda, static_cast<const bf16_t*>(Bm), ldb,
+             p.S > 1 ? static_cast<float*>(ws) : C, p.S > 1 ? N : ldc,
+             p.S > 1 ? static_cast<int64_t>(M) * N : 0, M, N, static_cast<int>(T), p.chunk};
+    const dim3 grid(((M + 127) / 128) * ((N + 127) / 128), p.S);
+    hipLaunchKernelGGL(gemm_tn_bf16_kernel, grid, dim3(GTHREADS), 0, stream, g);
+    if (p.S > 1) {
+      const int64_t n = static_cast<int64_t>(M) * (N / 4);
+      hipLaunchKernelGGL(splitk_reduce_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, stream,
+                         static_cast<const float*>(ws), static_cast<int64_t>(M) * N, p.S, C, ldc, M, N);
+    }
+    GR_CHECK_LAUNCH();
+    return GENRANK_OK;
+  }
+  // C[m, n] = sum_t A[t * lda + m] B[t * ldb + n]
+  return launch_gemm_general(dtype, GENRANK_F32, A, 1, lda, Bm, ldb, 1, C, ldc, M, N, static_cast<int>(T),
+                             GEMM_EPI_STORE, false, nullptr, 0, nullptr, 0, stream);
+}
+
+genrank_status launch_gemm_nn(int dtype, const void* A, int64_t lda, const void* W, int64_t ldw, void* C,
+                              int64_t ldc, int M, int N, int K, void* wt, hipStream_t stream) {
+  if (M <= 0 || N <= 0) return GENRANK_OK;
+  if (dtype == GENRANK_BF16 && wt && K > 0) {
+    // W [K, N] -> W^T [N, K] (pitch K), then C = A (W^T)^T on the NT kernels
+    const dim3 grid((N + 31) / 32, (K + 31) / 32);
+    hipLaunchKernelGGL(transpose_bf16_kernel, grid, dim3(256), 0, stream, static_cast<const bf16_t*>(W), ldw,
+                       static_cast<bf16_t*>(wt), static_cast<int64_t>(K), K, N);
+    GR_CHECK_LAUNCH();
+    return launch_gemm_nt(dtype, A, lda, wt, K, C, ldc, M, N, K, GEMM_EPI_STORE, nullptr, 0, nullptr, 0, stream);
+  }
+  return launch_gemm_general(dtype, dtype, A, lda, 1, W, ldw, 1, C, ldc, M, N, K, GEMM_EPI_STORE, false, nullptr,
+                             0, nullptr, 0, stream);
 }
 
 }  // namespace genrank

@@ -69,6 +69,17 @@ genrank_status launch_gemm_general(int in_dtype, int out_dtype, const void* A, i
                                    const void* R, int64_t ldr, void* Cpre, int64_t ldpre,
                                    hipStream_t stream);
 
+// Weight gradient: C[m, n] = sum_t A[t, m] B[t, n] (f32 out), split over T with f32 partial
+// tiles in ws (gemm_tn_workspace bytes) when the bf16 MFMA kernel takes it
+size_t gemm_tn_workspace(int M, int N, int64_t T);
+genrank_status launch_gemm_tn(int dtype, const void* A, int64_t lda, const void* Bm, int64_t ldb, float* C,
+                              int64_t ldc, int M, int N, int64_t T, void* ws, size_t ws_bytes,
+                              hipStream_t stream);
+// Data gradient: C[M, N] = A[M, K] W[K, N]; bf16 transposes W into wt ([N, K], N * K elements)
+// and runs the NT kernels
+genrank_status launch_gemm_nn(int dtype, const void* A, int64_t lda, const void* W, int64_t ldw, void* C,
+                              int64_t ldc, int M, int N, int K, void* wt, hipStream_t stream);
+
 // row-wise ops
 genrank_status launch_rmsnorm(int dtype, const void* x, const float* g, void* y, int64_t rows,
                               int d, hipStream_t stream);

@@ -273,6 +273,26 @@ GENRANK_API genrank_status genrank_linear(int32_t dtype, const void* x, int64_t 
                                           int64_t ldr, void* pre, int64_t ldpre,
                                           genrank_stream_t stream);
 
+/* Backward of genrank_linear without an epilogue (y = x w^T; a residual or SiLU epilogue
+ * is differentiated by the caller first):
+ *   dx[M, K] = dy[M, N] . w[N, K]   in dtype ([M, lddx]),
+ *   dw[N, K] = dy^T . x             f32 ([N, lddw]), overwritten.
+ * Either dx or dw may be NULL to skip it.  bf16: dx transposes w into the workspace and
+ * runs on the genrank_linear kernels; dw runs on an MFMA kernel that transposes tiles of
+ * dy and x on their way into LDS and splits the M rows over several workgroups per output
+ * tile (f32 partial tiles in the workspace, summed in a fixed order, so the result does
+ * not depend on scheduling).  Its MFMA path needs N and K multiples of 8, ldx and ldy
+ * multiples of 8 and lddw of 4 with 16-byte aligned x, dy, dw; other layouts and f32 take a
+ * plain tiled kernel.  ws: genrank_linear_bwd_workspace() bytes, 16-byte aligned
+ * (GENRANK_E_WORKSPACE if short). */
+GENRANK_API genrank_status genrank_linear_bwd_workspace(int32_t dtype, int64_t M, int32_t N, int32_t K,
+                                                        size_t* bytes);
+GENRANK_API genrank_status genrank_linear_bwd(int32_t dtype, const void* x, int64_t ldx, const void* w,
+                                              int64_t ldw, const void* dy, int64_t ldy, void* dx,
+                                              int64_t lddx, float* dw, int64_t lddw, int64_t M,
+                                              int32_t N, int32_t K, void* ws, size_t ws_bytes,
+                                              genrank_stream_t stream);
+
 /* Per-candidate action logits ([GR-zh] section 1.2: predictions for a set of predefined
  * tasks): logits[c, t] = (rmsnorm(x[T_h + c]) * g_final) . w_head[t] + b_head[t].
  * x: [T, d] in batch.dtype; g_final [d], w_head [n_tasks, d], b_head [n_tasks] f32;

@@ -75,3 +75,60 @@ def test_linear_bf16_silu_with_pre(M, N, K):
     s = z / (1.0 + np.exp(-z))
     # silu is 1.1-Lipschitz; its f32 evaluation adds a few ulps
     assert np.all(np.abs(to_numpy(y) - s) <= 1.1 * bound + 2.0 ** -8 * np.abs(s) + 1e-6)
+
+
+# ---------------------------------------------------------------- backward of a projection
+# dx = dy w (bf16 out): the bound above with the roles of the operands swapped.  dw = dy^T x
+# (f32 out, summed over M rows): M * 2^-23 * sum_t |dy_tn x_tk| + 1e-6, the f32 summation
+# bound with a factor 2 of slack; no final rounding.
+@pytest.mark.parametrize("M,N,K", [
+    (1, 256, 256), (5000, 768, 256), (3001, 1024, 256), (777, 192, 320), (64, 256, 1024),
+    (40, 8, 8),
+])
+def test_linear_bwd_bf16(M, N, K):
+    say(f"linear bwd: bf16 M={M} N={N} K={K}")
+    x = synth.inputs.normal_array((M, K), std=1.0, seed=M + 7, dtype="bf16")
+    w = synth.inputs.normal_array((N, K), std=K ** -0.5, seed=N + 8, dtype="bf16")
+    dy = synth.inputs.normal_array((M, N), std=1.0, seed=K + 9, dtype="bf16")
+    x64, w64, dy64 = (t.f32().astype(np.float64) for t in (x, w, dy))
+    xd, wd, dyd = (stored_to_device(t, DEV) for t in (x, w, dy))
+    lddx, lddw = K + 8, K + 4  # strided outputs: the pad columns stay untouched
+    dx = torch.full((M, lddx), 7.0, dtype=torch.bfloat16, device=DEV)
+    dw = torch.full((N, lddw), 7.0, dtype=torch.float32, device=DEV)
+    nws = B.genrank_linear_bwd_workspace(B.BF16, M, N, K)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=DEV)
+    B.genrank_linear_bwd(B.BF16, xd, K, wd, K, dyd, N, dx, lddx, dw, lddw, M, N, K, ws, nws)
+    torch.cuda.synchronize()
+    gx, gw = to_numpy(dx), to_numpy(dw)
+    want_x = dy64 @ w64
+    bound_x = 2.0 ** -8 * np.abs(want_x) + N * 2.0 ** -23 * (np.abs(dy64) @ np.abs(w64)) + 1e-6
+    assert np.all(np.abs(gx[:, :K] - want_x) <= bound_x), float(np.abs(gx[:, :K] - want_x).max())
+    want_w = dy64.T @ x64
+    bound_w = M * 2.0 ** -23 * (np.abs(dy64).T @ np.abs(x64)) + 1e-6
+    assert np.all(np.abs(gw[:, :K] - want_w) <= bound_w), float(np.abs(gw[:, :K] - want_w).max())
+    assert np.all(gx[:, K:] == 7.0) and np.all(gw[:, K:] == 7.0)
+
+
+def test_linear_bwd_one_output_and_f32():
+    """dw only, then dx only (the other pointer NULL), and the f32 path."""
+    say("linear bwd: single outputs, f32")
+    M, N, K = 300, 256, 128
+    for dt, name in ((B.BF16, "bf16"), (B.F32, "f32")):
+        x = synth.inputs.normal_array((M, K), std=1.0, seed=1, dtype=name)
+        w = synth.inputs.normal_array((N, K), std=K ** -0.5, seed=2, dtype=name)
+        dy = synth.inputs.normal_array((M, N), std=1.0, seed=3, dtype=name)
+        x64, w64, dy64 = (t.f32().astype(np.float64) for t in (x, w, dy))
+        xd, wd, dyd = (stored_to_device(t, DEV) for t in (x, w, dy))
+        nws = B.genrank_linear_bwd_workspace(dt, M, N, K)
+        ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=DEV)
+        dw = torch.zeros((N, K), dtype=torch.float32, device=DEV)
+        B.genrank_linear_bwd(dt, xd, K, None, K, dyd, N, None, K, dw, K, M, N, K, ws, nws)
+        dx = torch.zeros((M, K), dtype=xd.dtype, device=DEV)
+        B.genrank_linear_bwd(dt, None, K, wd, K, dyd, N, dx, K, None, K, M, N, K, ws, nws)
+        torch.cuda.synchronize()
+        want_x, want_w = dy64 @ w64, dy64.T @ x64
+        rx = 2.0 ** -8 * np.abs(want_x) if name == "bf16" else 0.0  # bf16 output rounding
+        bound_x = rx + N * 2.0 ** -23 * (np.abs(dy64) @ np.abs(w64)) + 1e-6
+        bound_w = M * 2.0 ** -23 * (np.abs(dy64).T @ np.abs(x64)) + 1e-6
+        assert np.all(np.abs(to_numpy(dx) - want_x) <= bound_x), name
+        assert np.all(np.abs(to_numpy(dw) - want_w) <= bound_w), name
