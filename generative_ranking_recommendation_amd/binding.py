@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgenrank.
 
 F32, BF16 = 0, 1
 BLOCK_ATTN_ONLY, BLOCK_PRENORM = 0, 1
-OP_EMBED_SUM, OP_ATTN_FWD, OP_ATTN_BWD, OP_LAYER_FWD, OP_LAYER_BWD = range(5)
+OP_EMBED_SUM, OP_ATTN_FWD, OP_ATTN_BWD, OP_LAYER_FWD, OP_LAYER_BWD, OP_EMBED_BWD = range(6)
 FWD_SAVE = 1
 EPI_NONE, EPI_RESIDUAL, EPI_SILU = 0, 1, 2
 STATUS = {0: "OK", -1: "E_ARG", -2: "E_SHAPE", -3: "E_DTYPE", -4: "E_UNSORTED",
@@ -95,7 +95,8 @@ _SIGS = {
                                    c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
     "genrank_bce_loss": (c_int32, [c_int64, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
     "genrank_embed_bwd": (c_int32, [POINTER(Batch), POINTER(Inputs), POINTER(Tables), c_void_p,
-                                    c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
+                                    c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                    c_void_p, c_void_p, c_size_t, c_void_p]),
     "genrank_debug_indices": (c_int32, [POINTER(Batch), POINTER(Inputs), POINTER(Tables), c_void_p, c_void_p]),
     "genrank_debug_mask": (c_int32, [POINTER(Batch), c_void_p, c_int32, c_int32, c_void_p, c_void_p]),
     "genrank_hstu_rab_layout": (c_int32, [POINTER(Batch), c_void_p, c_void_p, c_void_p]),
@@ -302,10 +303,12 @@ def genrank_bce_loss(n, n_tasks, logits, labels, loss, dlogits, stream=None):
         n, n_tasks, _p(logits), _p(labels), _p(loss), _p(dlogits), _stream(stream)))
 
 
-def genrank_embed_bwd(batch, inputs, tables, dx, d_item, d_action, d_pos, d_ri, d_rt, stream=None):
+def genrank_embed_bwd(batch, inputs, tables, dx, item_ids, item_rows, n_items, d_action, d_pos, d_ri,
+                      d_rt, ws, ws_bytes, stream=None):
     _check("genrank_embed_bwd", lib().genrank_embed_bwd(
-        ctypes.byref(batch), ctypes.byref(inputs), ctypes.byref(tables), _p(dx), _p(d_item),
-        _p(d_action), _p(d_pos), _p(d_ri), _p(d_rt), _stream(stream)))
+        ctypes.byref(batch), ctypes.byref(inputs), ctypes.byref(tables), _p(dx), _p(item_ids),
+        _p(item_rows), _p(n_items), _p(d_action), _p(d_pos), _p(d_ri), _p(d_rt), _p(ws), ws_bytes,
+        _stream(stream)))
 
 
 def genrank_debug_indices(batch, inputs, tables, out, stream=None):

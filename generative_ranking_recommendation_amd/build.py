@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgenrank.so")
-SOURCES = ["abi.cpp", "embed.hip", "attn_fwd.hip", "attn_bwd.hip", "gemm.hip", "rowops.hip", "hstu.hip"]
+SOURCES = ["abi.cpp", "embed.hip", "attn_fwd.hip", "attn_bwd.hip", "gemm.hip", "rowops.hip", "hstu.hip", "radix.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")

@@ -175,6 +175,9 @@ genrank_status genrank_workspace_size(int32_t op, const genrank_batch* b,
     case GENRANK_OP_ATTN_BWD:
       *bytes = attn_bwd_workspace(b);
       return GENRANK_OK;
+    case GENRANK_OP_EMBED_BWD:
+      *bytes = embed_bwd_workspace(b);
+      return GENRANK_OK;
     case GENRANK_OP_LAYER_FWD:
     case GENRANK_OP_LAYER_BWD: {
       if (!w) return GENRANK_E_ARG;
@@ -248,12 +251,17 @@ genrank_status genrank_debug_indices(const genrank_batch* b, const genrank_input
 }
 
 genrank_status genrank_embed_bwd(const genrank_batch* b, const genrank_inputs* in,
-                                 const genrank_tables* t, const void* dx, float* d_item,
-                                 float* d_action, float* d_pos, float* d_ri, float* d_rt,
+                                 const genrank_tables* t, const void* dx, int32_t* item_ids,
+                                 float* item_rows, int32_t* n_items, float* d_action, float* d_pos,
+                                 float* d_ri, float* d_rt, void* ws, size_t ws_bytes,
                                  genrank_stream_t stream) {
   GR_TRY(check_embed_args(b, in, t));
-  if (!dx || !d_item || !d_action || !d_pos || !d_ri || !d_rt) return GENRANK_E_ARG;
-  return launch_embed_bwd(b, in, t, dx, d_item, d_action, d_pos, d_ri, d_rt, S(stream));
+  if (!dx || !item_ids || !item_rows || !n_items || !d_action || !d_pos || !d_ri || !d_rt)
+    return GENRANK_E_ARG;
+  if (5 * static_cast<int64_t>(rows_of(b)) >= (int64_t(1) << 31)) return GENRANK_E_SHAPE;
+  if (!ws || ws_bytes < embed_bwd_workspace(b)) return GENRANK_E_WORKSPACE;
+  return launch_embed_bwd(b, in, t, dx, item_ids, item_rows, n_items, d_action, d_pos, d_ri, d_rt, ws,
+                          S(stream));
 }
 
 genrank_status genrank_attn_fwd(const genrank_batch* b, const int32_t* offsets,

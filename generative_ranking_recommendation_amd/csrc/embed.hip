@@ -12,6 +12,8 @@
 // The previous distinct timestamp of a row is the one just before its run.  The five
 // rows are then gathered with 16-byte loads (d/8 lanes per bf16 row), summed in f32 and
 // written once.  The small tables stay L2-resident across the grid.
+#include <algorithm>
+
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -362,35 +364,242 @@ __global__ void __launch_bounds__(EMB_THREADS) debug_indices_kernel(EmbedArgs a,
   }
 }
 
-// Adjoint: scatter-add dx rows into the five f32 table gradients.
-template <typename T>
-__global__ void __launch_bounds__(EMB_THREADS) embed_bwd_kernel(EmbedArgs a) {
+// ---------------------------------------------------------------- backward (adjoint)
+// Row r of table t's gradient is the sum of dx over the batch rows whose slot in table t is
+// r.  The rows are grouped by slot rather than scattered with atomics:
+//   1. keys: every batch row writes its five slots, table t into slice t of T (key, row)
+//      pairs;
+//   2. the five slices are radix-sorted by key, stably, so a group keeps its rows in
+//      ascending order;
+//   3. the sorted pairs are cut into chunks of SEG; a run of equal keys that lies inside a
+//      chunk is summed there column by column in row order and written out; a run that
+//      crosses chunk borders leaves one partial sum per chunk, and the chunk holding its
+//      first row adds those up in chunk order.
+// The summation order is fixed (deterministic results) and there are no atomics.  The item
+// gradient comes out sparse (one row per distinct item, ascending ids); the four small
+// tables dense, every row written.
+constexpr int SEG = 64;  // sorted pairs per chunk (one wave classifies a chunk)
+
+__global__ void __launch_bounds__(EMB_THREADS) embed_keys_kernel(EmbedArgs a, uint32_t* keys, uint32_t* vals,
+                                                                 int64_t T) {
   __shared__ RowIdx sidx[EMB_ROWS];
   __shared__ int64_t sbounds[MAX_BOUNDS];
   __shared__ int red_c[EMB_THREADS / 64];
   __shared__ int64_t red_m[EMB_THREADS / 64];
   int64_t row0;
   const int rows = derive_chunk(a, sidx, sbounds, red_c, red_m, &row0);
-  if (rows == 0) return;
-  constexpr int V = Vec<T>::N;
-  const int cpr = a.d / V;
-  const int total = rows * cpr;
-  const T* dx = static_cast<const T*>(a.dx);
-  const int64_t d = a.d;
-  for (int idx = threadIdx.x; idx < total; idx += EMB_THREADS) {
-    const int r = idx / cpr;
-    const int col = (idx - r * cpr) * V;
-    const RowIdx ix = sidx[r];
-    float g[V];
-    load_vec(dx + (row0 + r) * d + col, g);
+  if (static_cast<int>(threadIdx.x) >= rows) return;
+  const RowIdx ix = sidx[threadIdx.x];
+  const int64_t r = row0 + threadIdx.x;
+  const uint32_t k[5] = {static_cast<uint32_t>(ix.item), static_cast<uint32_t>(ix.act),
+                         static_cast<uint32_t>(ix.pe), static_cast<uint32_t>(ix.ri_slot),
+                         static_cast<uint32_t>(ix.rt)};
 #pragma unroll
-    for (int e = 0; e < V; ++e) {
-      atomicAdd(a.g_item + ix.item * d + col + e, g[e]);
-      atomicAdd(a.g_action + ix.act * d + col + e, g[e]);
-      atomicAdd(a.g_pos + ix.pe * d + col + e, g[e]);
-      atomicAdd(a.g_ri + ix.ri_slot * d + col + e, g[e]);
-      atomicAdd(a.g_rt + ix.rt * d + col + e, g[e]);
+  for (int t = 0; t < 5; ++t) {
+    keys[t * T + r] = k[t];
+    vals[t * T + r] = static_cast<uint32_t>(r);
+  }
+}
+
+struct SegArgs {
+  const uint32_t* keys;   // sorted, 5 slices of T
+  const uint32_t* vals;   // batch row of each sorted pair
+  int64_t T, total;       // total = 5 T
+  int nch;                // chunks of SEG pairs
+  uint32_t* cnt;          // [nch] run heads per chunk, then their exclusive scan
+  uint32_t* cnt_item;     // [nch] run heads in the item slice
+  int32_t* n_items;       // [1] distinct items
+  const void* dx;
+  int d;
+  int32_t* item_ids;      // [T] sparse item gradient: ids
+  float* item_rows;       // [T, d] and rows
+  float* dense[4];        // action, pos, ri, rt gradients
+  int64_t dense_elems[4];
+  float* carry_in;        // [nch, d] partial sum of a run that began in an earlier chunk
+  float* carry_out;       // [nch, d] partial sum of a run that begins here and goes on
+  int32_t* meta;          // [nch, 4]: flags, table, key, sparse slot of the carry_out run
+};
+constexpr int META_CONT_IN = 1;   // the chunk's first pair continues a run
+constexpr int META_NO_HEAD = 2;   // no run starts in the chunk
+constexpr int META_CARRY_OUT = 4; // the chunk's last run starts here and goes on
+
+__device__ __forceinline__ bool seg_head(const SegArgs& g, int64_t p) {
+  return p % g.T == 0 || g.keys[p] != g.keys[p - 1];
+}
+
+// One wave per chunk: count run heads (all, and in the item slice); the first waves also
+// clear the dense gradients.
+__global__ void __launch_bounds__(256) seg_count_kernel(SegArgs g) {
+  const int64_t gt = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t nthreads = static_cast<int64_t>(gridDim.x) * 256;
+  for (int t = 0; t < 4; ++t)
+    for (int64_t e = gt; e < g.dense_elems[t]; e += nthreads) g.dense[t][e] = 0.f;
+  const int c = static_cast<int>(gt >> 6);
+  const int lane = threadIdx.x & 63;
+  if (c >= g.nch) return;
+  const int64_t p = static_cast<int64_t>(c) * SEG + lane;
+  const bool head = p < g.total && seg_head(g, p);
+  const uint64_t m = __ballot(head);
+  const uint64_t mi = __ballot(head && p < g.T);
+  if (lane == 0) {
+    g.cnt[c] = static_cast<uint32_t>(__popcll(m));
+    g.cnt_item[c] = static_cast<uint32_t>(__popcll(mi));
+  }
+}
+
+// One workgroup: exclusive scan of the head counts; the number of distinct items.
+__global__ void __launch_bounds__(1024) seg_scan_kernel(SegArgs g) {
+  __shared__ uint32_t sw[16];
+  __shared__ uint32_t si[16];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t carry = 0, items = 0;
+  for (int base = 0; base < g.nch; base += 1024) {
+    const int c = base + static_cast<int>(threadIdx.x);
+    const uint32_t x = c < g.nch ? g.cnt[c] : 0u;
+    uint32_t xi = c < g.nch ? g.cnt_item[c] : 0u;
+    uint32_t inc = x;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t y = __shfl_up(inc, o);
+      if (lane >= o) inc += y;
+      xi += __shfl_xor(xi, o);
     }
+    if (lane == 63) sw[wave] = inc;
+    if (lane == 0) si[wave] = xi;
+    __syncthreads();
+    uint32_t pre = carry, tot = 0;
+    for (int w = 0; w < 16; ++w) {
+      pre += w < wave ? sw[w] : 0u;
+      tot += sw[w];
+      items += (threadIdx.x == 0) ? si[w] : 0u;
+    }
+    if (c < g.nch) g.cnt[c] = pre + inc - x;
+    carry += tot;
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) *g.n_items = static_cast<int32_t>(items);
+}
+
+template <typename T>
+__device__ __forceinline__ float ld_elem(const T* p);
+template <>
+__device__ __forceinline__ float ld_elem<bf16_t>(const bf16_t* p) {
+  return __uint_as_float(static_cast<uint32_t>(*reinterpret_cast<const uint16_t*>(p)) << 16);
+}
+template <>
+__device__ __forceinline__ float ld_elem<float>(const float* p) { return *p; }
+
+// destination of a finished run: the sparse item row, or the dense small-table row (null
+// for a slot past the table, which only ids out of range can produce)
+__device__ __forceinline__ float* seg_dest(const SegArgs& g, int table, uint32_t key, uint32_t slot) {
+  if (table == 0) return g.item_rows + static_cast<int64_t>(slot) * g.d;
+  const int64_t off = static_cast<int64_t>(key) * g.d;
+  return off < g.dense_elems[table - 1] ? g.dense[table - 1] + off : nullptr;
+}
+
+// One workgroup per chunk; thread j owns columns j, j + 256, ...  and walks the chunk's
+// pairs in order, loading eight rows ahead.
+template <typename T>
+__global__ void __launch_bounds__(256) seg_sum_kernel(SegArgs g) {
+  __shared__ uint32_t sk[SEG], sv[SEG], sslot[SEG];
+  __shared__ int shead[SEG + 1];
+  __shared__ int stab[SEG];
+  __shared__ int sinfo[2];
+  const int c = blockIdx.x;
+  const int64_t p0 = static_cast<int64_t>(c) * SEG;
+  const int cnt = static_cast<int>(min<int64_t>(SEG, g.total - p0));
+  const int tid = threadIdx.x;
+  if (tid < 64) {
+    const int64_t p = p0 + tid;
+    const bool valid = tid < cnt;
+    const bool head = valid && seg_head(g, p);
+    const uint64_t m = __ballot(head);
+    if (valid) {
+      const uint32_t key = g.keys[p];
+      const uint32_t slot = g.cnt[c] + static_cast<uint32_t>(__popcll(m & ((1ull << tid) - 1ull)));
+      sk[tid] = key;
+      sv[tid] = g.vals[p];
+      sslot[tid] = slot;
+      shead[tid] = head ? 1 : 0;
+      stab[tid] = static_cast<int>(p / g.T);
+      if (head && p < g.T) g.item_ids[slot] = static_cast<int32_t>(key);
+    }
+    if (tid == 0) {
+      const int64_t pn = p0 + SEG;
+      const bool next_cont = pn < g.total && !seg_head(g, pn);
+      shead[cnt] = next_cont ? 0 : 1;  // a run ending at the chunk's end goes on iff 0
+      sinfo[0] = next_cont ? 1 : 0;
+      sinfo[1] = (m & 1ull) ? 0 : 1;   // the first pair continues a run
+    }
+  }
+  __syncthreads();
+  const bool next_cont = sinfo[0] != 0;
+  const bool cont_in = sinfo[1] != 0;
+  // the last run: its first pair (or -1 for the continued run) and whether it goes on
+  int last_head = -1;
+  for (int i = cnt - 1; i >= 0; --i)
+    if (shead[i]) { last_head = i; break; }
+  if (tid == 0) {
+    int32_t* mt = g.meta + 4 * c;
+    int flags = (cont_in ? META_CONT_IN : 0) | (last_head < 0 ? META_NO_HEAD : 0);
+    if (next_cont && last_head >= 0) {
+      flags |= META_CARRY_OUT;
+      mt[1] = stab[last_head];
+      mt[2] = static_cast<int32_t>(sk[last_head]);
+      mt[3] = static_cast<int32_t>(sslot[last_head]);
+    }
+    mt[0] = flags;
+  }
+  const T* dx = static_cast<const T*>(g.dx);
+  const int64_t d = g.d;
+  for (int col = tid; col < g.d; col += 256) {
+    float acc = 0.f;
+    int run = shead[0] ? 0 : -1;
+    for (int i0 = 0; i0 < cnt; i0 += 8) {
+      float v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = i0 + j < cnt ? ld_elem<T>(dx + static_cast<int64_t>(sv[i0 + j]) * d + col) : 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int i = i0 + j;
+        if (i >= cnt) break;
+        acc += v[j];
+        if (i + 1 == cnt || shead[i + 1]) {  // the run ends at pair i (in this chunk)
+          float* dst;
+          if (run < 0)
+            dst = g.carry_in + static_cast<int64_t>(c) * d;
+          else if (i + 1 == cnt && next_cont)
+            dst = g.carry_out + static_cast<int64_t>(c) * d;
+          else
+            dst = seg_dest(g, stab[run], sk[run], sslot[run]);
+          if (dst) dst[col] = acc;
+          acc = 0.f;
+          run = i + 1;
+        }
+      }
+    }
+  }
+}
+
+// One workgroup per chunk whose last run goes on: its partial plus the continuing chunks'
+// partials, in chunk order.
+__global__ void __launch_bounds__(256) seg_fix_kernel(SegArgs g) {
+  const int c = blockIdx.x;
+  const int32_t* mt = g.meta + 4 * c;
+  if (!(mt[0] & META_CARRY_OUT)) return;
+  const int table = mt[1];
+  const uint32_t key = static_cast<uint32_t>(mt[2]), slot = static_cast<uint32_t>(mt[3]);
+  float* dst = seg_dest(g, table, key, slot);
+  if (!dst) return;
+  const int64_t d = g.d;
+  for (int col = threadIdx.x; col < g.d; col += 256) {
+    float acc = g.carry_out[c * d + col];
+    for (int j = c + 1; j < g.nch; ++j) {
+      acc += g.carry_in[j * d + col];
+      const bool passes = (g.meta[4 * j] & META_NO_HEAD) != 0;
+      if (!passes || j + 1 >= g.nch || !(g.meta[4 * (j + 1)] & META_CONT_IN)) break;
+    }
+    dst[col] = acc;
   }
 }
 
@@ -487,21 +696,91 @@ genrank_status launch_debug_indices(const genrank_batch* b, const genrank_inputs
   return GENRANK_OK;
 }
 
-genrank_status launch_embed_bwd(const genrank_batch* b, const genrank_inputs* in,
-                                const genrank_tables* t, const void* dx, float* g_item,
-                                float* g_action, float* g_pos, float* g_ri, float* g_rt,
+struct EmbedBwdWs {
+  uint32_t *keys, *vals, *tkeys, *tvals, *hist, *cnt, *cnt_item;
+  float *carry_in, *carry_out;
+  int32_t* meta;
+  size_t bytes;
+};
+
+EmbedBwdWs embed_bwd_layout(const genrank_batch* b, char* base) {
+  const int64_t T = b->total_hist + static_cast<int64_t>(b->B) * b->m;
+  const int64_t total = 5 * T;
+  const int64_t nch = (total + SEG - 1) / SEG;
+  EmbedBwdWs w{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    char* p = base ? base + off : nullptr;
+    off += (bytes + 255) & ~static_cast<size_t>(255);
+    return p;
+  };
+  w.keys = reinterpret_cast<uint32_t*>(take(total * 4));
+  w.vals = reinterpret_cast<uint32_t*>(take(total * 4));
+  w.tkeys = reinterpret_cast<uint32_t*>(take(total * 4));
+  w.tvals = reinterpret_cast<uint32_t*>(take(total * 4));
+  w.hist = reinterpret_cast<uint32_t*>(take(radix_sort_workspace(T, 5)));
+  w.cnt = reinterpret_cast<uint32_t*>(take(nch * 4));
+  w.cnt_item = reinterpret_cast<uint32_t*>(take(nch * 4));
+  w.carry_in = reinterpret_cast<float*>(take(nch * b->d * 4));
+  w.carry_out = reinterpret_cast<float*>(take(nch * b->d * 4));
+  w.meta = reinterpret_cast<int32_t*>(take(nch * 16));
+  w.bytes = off;
+  return w;
+}
+
+size_t embed_bwd_workspace(const genrank_batch* b) { return embed_bwd_layout(b, nullptr).bytes; }
+
+genrank_status launch_embed_bwd(const genrank_batch* b, const genrank_inputs* in, const genrank_tables* t,
+                                const void* dx, int32_t* item_ids, float* item_rows, int32_t* n_items,
+                                float* g_action, float* g_pos, float* g_ri, float* g_rt, void* ws,
                                 hipStream_t stream) {
-  EmbedArgs a = make_args(b, in, t);
-  a.dx = dx;
-  a.g_item = g_item;
-  a.g_action = g_action;
-  a.g_pos = g_pos;
-  a.g_ri = g_ri;
-  a.g_rt = g_rt;
-  if (b->dtype == GENRANK_BF16)
-    hipLaunchKernelGGL(embed_bwd_kernel<bf16_t>, grid_of(a), dim3(EMB_THREADS), 0, stream, a);
-  else
-    hipLaunchKernelGGL(embed_bwd_kernel<float>, grid_of(a), dim3(EMB_THREADS), 0, stream, a);
+  const int64_t T = b->total_hist + static_cast<int64_t>(b->B) * b->m;
+  EmbedBwdWs w = embed_bwd_layout(b, static_cast<char*>(ws));
+  SegArgs g{};
+  g.T = T;
+  g.total = 5 * T;
+  g.nch = static_cast<int>((g.total + SEG - 1) / SEG);
+  g.n_items = n_items;
+  g.dx = dx;
+  g.d = b->d;
+  g.item_ids = item_ids;
+  g.item_rows = item_rows;
+  g.dense[0] = g_action; g.dense[1] = g_pos; g.dense[2] = g_ri; g.dense[3] = g_rt;
+  g.dense_elems[0] = (static_cast<int64_t>(t->n_action) + 1) * b->d;
+  g.dense_elems[1] = static_cast<int64_t>(t->n_pos) * b->d;
+  g.dense_elems[2] = static_cast<int64_t>(t->n_ri) * b->d;
+  g.dense_elems[3] = static_cast<int64_t>(t->n_rt) * b->d;
+  g.cnt = w.cnt;
+  g.cnt_item = w.cnt_item;
+  g.carry_in = w.carry_in;
+  g.carry_out = w.carry_out;
+  g.meta = w.meta;
+  if (T > 0) {
+    EmbedArgs a = make_args(b, in, t);
+    hipLaunchKernelGGL(embed_keys_kernel, grid_of(a), dim3(EMB_THREADS), 0, stream, a, w.keys, w.vals, T);
+    // key bits: the largest slot of any table
+    const int64_t top = std::max<int64_t>({t->n_item - 1, t->n_action, t->n_pos - 1, t->n_ri - 1, t->n_rt - 1, 1});
+    int bits = 0;
+    while (bits < 32 && (top >> bits) != 0) ++bits;
+    int in_tmp = 0;
+    const genrank_status st = launch_radix_sort(w.keys, w.vals, w.tkeys, w.tvals, T, 5, bits, w.hist, &in_tmp, stream);
+    if (st != GENRANK_OK) return st;
+    g.keys = in_tmp ? w.tkeys : w.keys;
+    g.vals = in_tmp ? w.tvals : w.vals;
+  }
+  // the count kernel also clears the dense gradients: enough threads for both jobs
+  int64_t need = std::max<int64_t>(static_cast<int64_t>(g.nch) * 64, 1);
+  need = std::max<int64_t>(need, std::min<int64_t>(g.dense_elems[1], int64_t(1) << 20));
+  const unsigned cgrid = static_cast<unsigned>((need + 255) / 256);
+  hipLaunchKernelGGL(seg_count_kernel, dim3(cgrid), dim3(256), 0, stream, g);
+  hipLaunchKernelGGL(seg_scan_kernel, dim3(1), dim3(1024), 0, stream, g);
+  if (T > 0) {
+    if (b->dtype == GENRANK_BF16)
+      hipLaunchKernelGGL(seg_sum_kernel<bf16_t>, dim3(g.nch), dim3(256), 0, stream, g);
+    else
+      hipLaunchKernelGGL(seg_sum_kernel<float>, dim3(g.nch), dim3(256), 0, stream, g);
+    hipLaunchKernelGGL(seg_fix_kernel, dim3(g.nch), dim3(256), 0, stream, g);
+  }
   GR_CHECK_LAUNCH();
   return GENRANK_OK;
 }

@@ -22,10 +22,17 @@ genrank_status launch_embed_sum(const genrank_batch* b, const genrank_inputs* in
                                 const genrank_tables* t, void* out, hipStream_t stream);
 genrank_status launch_debug_indices(const genrank_batch* b, const genrank_inputs* in,
                                     const genrank_tables* t, int32_t* out, hipStream_t stream);
-genrank_status launch_embed_bwd(const genrank_batch* b, const genrank_inputs* in,
-                                const genrank_tables* t, const void* dx, float* g_item,
-                                float* g_action, float* g_pos, float* g_ri, float* g_rt,
+size_t embed_bwd_workspace(const genrank_batch* b);
+genrank_status launch_embed_bwd(const genrank_batch* b, const genrank_inputs* in, const genrank_tables* t,
+                                const void* dx, int32_t* item_ids, float* item_rows, int32_t* n_items,
+                                float* g_action, float* g_pos, float* g_ri, float* g_rt, void* ws,
                                 hipStream_t stream);
+// Stable radix sort of `slices` arrays of n (key, value) pairs by the low `bits` key bits;
+// *result_in_tmp tells whether the result ended in (tmp_keys, tmp_vals).
+size_t radix_sort_workspace(int64_t n, int slices);
+genrank_status launch_radix_sort(uint32_t* keys, uint32_t* vals, uint32_t* tmp_keys, uint32_t* tmp_vals,
+                                 int64_t n, int slices, int bits, uint32_t* hist, int* result_in_tmp,
+                                 hipStream_t stream);
 
 // attention
 genrank_status check_attn_args(const genrank_batch* b, const int32_t* offsets, const int64_t* ts,

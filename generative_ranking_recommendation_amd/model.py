@@ -123,10 +123,18 @@ class GenRank:
                                 1 if i == len(self.layers) - 1 else 0, wsb, nb, stream)
             del nf
             grads["layers"][i] = lg
+        # table gradients: the item table's sparse (distinct ids ascending, their rows, the
+        # count on the device), the small tables' dense
         t = self.tables
-        tg = {k: torch.zeros(getattr(t, k).shape, dtype=torch.float32, device=dev)
-              for k in ("item", "action", "pos", "ri", "rt")}
-        B.genrank_embed_bwd(bt, inp.struct, t.struct, dx, tg["item"], tg["action"], tg["pos"],
-                            tg["ri"], tg["rt"], stream)
+        T = inp.rows
+        tg = {k: torch.empty(getattr(t, k).shape, dtype=torch.float32, device=dev)
+              for k in ("action", "pos", "ri", "rt")}
+        tg["item_ids"] = torch.empty(T, dtype=torch.int32, device=dev)
+        tg["item_rows"] = torch.empty((T, d), dtype=torch.float32, device=dev)
+        tg["n_items"] = torch.empty(1, dtype=torch.int32, device=dev)
+        nwe = B.genrank_workspace_size(B.OP_EMBED_BWD, bt)
+        wse = self._buf(("embed_bwd",), nwe)
+        B.genrank_embed_bwd(bt, inp.struct, t.struct, dx, tg["item_ids"], tg["item_rows"], tg["n_items"],
+                            tg["action"], tg["pos"], tg["ri"], tg["rt"], wse, nwe, stream)
         grads["tables"] = tg
         return loss, logits, grads

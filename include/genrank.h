@@ -77,7 +77,8 @@ typedef enum {
   GENRANK_OP_ATTN_FWD = 1,
   GENRANK_OP_ATTN_BWD = 2,
   GENRANK_OP_LAYER_FWD = 3,
-  GENRANK_OP_LAYER_BWD = 4
+  GENRANK_OP_LAYER_BWD = 4,
+  GENRANK_OP_EMBED_BWD = 5
 } genrank_op;
 
 /* Batch geometry.  total_hist and max_hist are host copies of hist_offsets[B] and
@@ -316,13 +317,22 @@ GENRANK_API genrank_status genrank_bce_loss(int64_t n, int32_t n_tasks, const fl
                                 const float* labels, float* loss, float* dlogits,
                                 genrank_stream_t stream);
 
-/* Adjoint of genrank_embed_sum: each table's f32 gradient receives dx[row] at the row's
- * slot.  d_* are [rows, d] f32 and are ACCUMULATED into (zero them first).
- * dx: [T, d] in batch.dtype.  Uses f32 atomics, so the summation order is not fixed. */
+/* Adjoint of genrank_embed_sum: row r of a table's gradient is the sum of dx over the
+ * batch rows whose slot in that table is r.  dx: [T, d] in batch.dtype.  Outputs, f32,
+ * overwritten:
+ *   item gradient, sparse: *n_items (device int32) distinct item ids in ascending order
+ *     in item_ids[0 .. n_items) ([T] capacity), their gradient rows in item_rows
+ *     ([T, d] capacity; rows past n_items untouched);
+ *   d_action [n_action + 1, d], d_pos [n_pos, d], d_ri [n_ri, d], d_rt [n_rt, d]: dense,
+ *     zero where no row maps.
+ * The rows are grouped by slot with a radix sort and each group is summed in ascending row
+ * order (no atomics): the result does not depend on scheduling.  5 T must be below 2^31.
+ * ws: genrank_workspace_size(GENRANK_OP_EMBED_BWD) bytes. */
 GENRANK_API genrank_status genrank_embed_bwd(const genrank_batch* batch, const genrank_inputs* in,
-                                 const genrank_tables* tables, const void* dx, float* d_item,
-                                 float* d_action, float* d_pos, float* d_ri, float* d_rt,
-                                 genrank_stream_t stream);
+                                             const genrank_tables* tables, const void* dx,
+                                             int32_t* item_ids, float* item_rows, int32_t* n_items,
+                                             float* d_action, float* d_pos, float* d_ri, float* d_rt,
+                                             void* ws, size_t ws_bytes, genrank_stream_t stream);
 
 /* ------------------------------------------------------------------ debug exports */
 

@@ -153,7 +153,10 @@ def _compare_train(cfg, batch, tables, weights, tol, relative_to="bf16"):
             close(grads["layers"][li][k], v, f"layer{li}.{k}")
     for k in ("action", "pos", "ri", "rt"):
         close(grads["tables"][k], wtg[k], k)
-    close(to_numpy(grads["tables"]["item"])[used], wtg["item"][used], "item")
+    tg = grads["tables"]
+    n = int(tg["n_items"].item())
+    assert np.array_equal(tg["item_ids"][:n].cpu().numpy(), used), "item ids"
+    close(to_numpy(tg["item_rows"][:n]), wtg["item"][used], "item")
 
 
 def test_train_step_f32_tiny():

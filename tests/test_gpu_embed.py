@@ -1,6 +1,8 @@
 """GPU parity of the fused index derivation + embedding gather-sum against the oracle:
 indices bit-exact, sums within the dtype's tolerance (f32: 1e-5 absolute; bf16: 2e-2 of the
-RMS, i.e. the output rounding)."""
+RMS, i.e. the output rounding).  The embedding backward: distinct item ids bit-exact; each
+gradient element, an f32 sum of k stored dx values, within k * 2^-23 * sum|dx| (the
+summation bound with a factor 2 of slack) of the float64 sum; bit-identical on a rerun."""
 import numpy as np
 import pytest
 import torch
@@ -11,6 +13,7 @@ from common import oracle_indices, oracle_tables
 from gpu_common import (DEV, DeviceInputs, DeviceTables, batch_struct, custom_batch, rel_err, say,
                         tables_for, to_numpy)
 from generative_ranking_recommendation_amd import binding as B
+from generative_ranking_recommendation_amd.device import stored_to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -110,3 +113,67 @@ def test_embed_sum_full_size_sampled():
     want = oracle.embed_sum(oracle_tables(tables), batch.hist_items, batch.cand_items, idx, rows=rows)
     assert np.all(np.abs(got[rows] - want) <= np.abs(want) * 2.0 ** -8 + 1e-6)
     assert np.isfinite(got).all()
+
+
+def _embed_bwd_case(cfg, batch, tables, seed):
+    T = batch.total_rows
+    dxs = synth.inputs.normal_array((T, cfg.d), std=1.0, seed=seed, dtype=cfg.dtype)
+    dx64 = dxs.f32().astype(np.float64)
+    idx = oracle_indices(cfg, batch, tables)
+    shapes = {k: getattr(tables, k).shape for k in ("action", "pos", "ri", "rt")}
+    used = np.unique(np.concatenate([batch.hist_items, batch.cand_items]))
+    shapes["item"] = (int(used.max()) + 1 if used.size else 1, cfg.d)
+    items = dict(hist_items=batch.hist_items, cand_items=batch.cand_items, idx=idx)
+    want = oracle.embed_bwd(dx64, shapes, **items)
+    mag = oracle.embed_bwd(np.abs(dx64), shapes, **items)      # sum |dx| per element
+    cnt = oracle.embed_bwd(np.ones_like(dx64), shapes, **items)  # rows per element
+    inp = DeviceInputs(batch, DEV)
+    tab = DeviceTables(tables, DEV)
+    bt = batch_struct(cfg, inp)
+    dx = stored_to_device(dxs, DEV)
+    nws = B.genrank_workspace_size(B.OP_EMBED_BWD, bt)
+    ws = torch.empty(nws, dtype=torch.uint8, device=DEV)
+    runs = []
+    for _ in range(2):
+        out = {k: torch.full(s, float("nan"), dtype=torch.float32, device=DEV) for k, s in shapes.items()
+               if k != "item"}
+        ids = torch.full((max(T, 1),), -1, dtype=torch.int32, device=DEV)
+        rows = torch.full((max(T, 1), cfg.d), float("nan"), dtype=torch.float32, device=DEV)
+        n = torch.full((1,), -1, dtype=torch.int32, device=DEV)
+        B.genrank_embed_bwd(bt, inp.struct, tab.struct, dx, ids, rows, n, out["action"], out["pos"],
+                            out["ri"], out["rt"], ws, nws)
+        torch.cuda.synchronize()
+        k = int(n.item())
+        got = {key: v.cpu().numpy().astype(np.float64) for key, v in out.items()}
+        got["ids"] = ids[:k].cpu().numpy()
+        got["item"] = rows[:k].cpu().numpy().astype(np.float64)
+        runs.append(got)
+    got = runs[0]
+    assert np.array_equal(got["ids"], used), "item ids"
+    for key in ("item", "action", "pos", "ri", "rt"):
+        sel = used if key == "item" else slice(None)
+        w, m, c = want[key][sel], mag[key][sel], cnt[key][sel]
+        assert np.all(np.abs(got[key] - w) <= c * 2.0 ** -23 * m + 1e-6), key
+        assert np.array_equal(runs[0][key], runs[1][key]), ("not deterministic", key)
+
+
+def test_embed_bwd_f32_tiny():
+    say("embed bwd: tiny_fp32")
+    cfg = synth.make_config("tiny_fp32")
+    _embed_bwd_case(cfg, synth.make_batch(cfg), synth.make_tables(cfg), seed=21)
+
+
+def test_embed_bwd_bf16_edges():
+    """Zipf items (hot ids span several 64-pair chunks), empty and one-action users, 40
+    candidates per user."""
+    say("embed bwd: bf16 edge lengths")
+    cfg = synth.make_config("train2_bf16", m=40)
+    batch = custom_batch(cfg, [300, 0, 1, 480, 64, 65, 250], seed=12)
+    _embed_bwd_case(cfg, batch, synth.make_tables(cfg), seed=22)
+
+
+def test_embed_bwd_bf16_train_batch():
+    """The full training batch (128 users, 32 candidates)."""
+    say("embed bwd: bf16 train batch")
+    cfg = synth.make_config("train2_bf16")
+    _embed_bwd_case(cfg, synth.make_batch(cfg), synth.make_tables(cfg), seed=23)
