@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgenrank.
 
 F32, BF16 = 0, 1
 BLOCK_ATTN_ONLY, BLOCK_PRENORM = 0, 1
-OP_EMBED_SUM, OP_ATTN_FWD, OP_ATTN_BWD, OP_LAYER_FWD, OP_LAYER_BWD, OP_EMBED_BWD = range(6)
+OP_EMBED_SUM, OP_ATTN_FWD, OP_ATTN_BWD, OP_LAYER_FWD, OP_LAYER_BWD, OP_EMBED_BWD, OP_HEAD_BWD = range(7)
 FWD_SAVE = 1
 EPI_NONE, EPI_RESIDUAL, EPI_SILU = 0, 1, 2
 STATUS = {0: "OK", -1: "E_ARG", -2: "E_SHAPE", -3: "E_DTYPE", -4: "E_UNSORTED",
@@ -92,7 +92,8 @@ _SIGS = {
     "genrank_head_fwd": (c_int32, [POINTER(Batch), c_void_p, c_void_p, c_void_p, c_void_p, c_int32,
                                    c_void_p, c_void_p]),
     "genrank_head_bwd": (c_int32, [POINTER(Batch), c_void_p, c_void_p, c_void_p, c_int32, c_void_p,
-                                   c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
+                                   c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
+                                   c_void_p]),
     "genrank_bce_loss": (c_int32, [c_int64, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
     "genrank_embed_bwd": (c_int32, [POINTER(Batch), POINTER(Inputs), POINTER(Tables), c_void_p,
                                     c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
@@ -292,10 +293,10 @@ def genrank_head_fwd(batch, x, g_final, w_head, b_head, n_tasks, logits, stream=
 
 
 def genrank_head_bwd(batch, x, g_final, w_head, n_tasks, dlogits, dx, dg_final, dw_head, db_head,
-                     stream=None):
+                     ws, ws_bytes, stream=None):
     _check("genrank_head_bwd", lib().genrank_head_bwd(
         ctypes.byref(batch), _p(x), _p(g_final), _p(w_head), n_tasks, _p(dlogits), _p(dx),
-        _p(dg_final), _p(dw_head), _p(db_head), _stream(stream)))
+        _p(dg_final), _p(dw_head), _p(db_head), _p(ws), ws_bytes, _stream(stream)))
 
 
 def genrank_bce_loss(n, n_tasks, logits, labels, loss, dlogits, stream=None):

@@ -82,6 +82,7 @@ struct LayerBwdWs {
   char* dh;     // [T, f]  (PRENORM) gradient of silu(a), then of a
   char* dz2;    // [T, d]  (PRENORM)
   char* attn;   // attention backward scratch
+  char* rms;    // RMSNorm backward partial rows
   char* wt;     // one transposed weight (bf16 data gradients)
   char* tn;     // split partial tiles of the weight gradients
   size_t tn_bytes;
@@ -114,6 +115,7 @@ LayerBwdWs layer_bwd_layout(const genrank_batch* b, int block, int ffn, char* ba
     wt = std::max(wt, d * static_cast<size_t>(ffn));
     tn = std::max({tn, gemm_tn_workspace(di, ffn, Ti), gemm_tn_workspace(ffn, di, Ti)});
   }
+  w.rms = take(rmsnorm_bwd_workspace(di));
   w.wt = take(wt * es);
   w.tn = take(tn);
   w.tn_bytes = tn;
@@ -177,6 +179,9 @@ genrank_status genrank_workspace_size(int32_t op, const genrank_batch* b,
       return GENRANK_OK;
     case GENRANK_OP_EMBED_BWD:
       *bytes = embed_bwd_workspace(b);
+      return GENRANK_OK;
+    case GENRANK_OP_HEAD_BWD:
+      *bytes = head_bwd_workspace(b->d, 4);
       return GENRANK_OK;
     case GENRANK_OP_LAYER_FWD:
     case GENRANK_OP_LAYER_BWD: {
@@ -391,12 +396,11 @@ genrank_status genrank_layer_bwd(const genrank_batch* b, const genrank_layer_wei
   if (pre) {
     // FFN branch: y = x1 + W2 silu(W1 z2)
     GR_TRY(launch_gemm_tn(dt, dy, d, F.hdn, ffn, g.w2, ffn, d, ffn, Tl, L.tn, L.tn_bytes, s));
-    GR_TRY(launch_gemm_nn(dt, dy, d, w->w2, ffn, L.dh, ffn, T, ffn, d, L.wt, s));
-    GR_TRY(launch_silu_bwd(dt, F.a, L.dh, L.dh, static_cast<int64_t>(T) * ffn, s));
+    // d a = (dy W2) * silu'(a), the SiLU backward fused into the product's epilogue
+    GR_TRY(launch_gemm_nn(dt, dy, d, w->w2, ffn, L.dh, ffn, T, ffn, d, L.wt, s, GEMM_EPI_DSILU, F.a, ffn));
     GR_TRY(launch_gemm_tn(dt, L.dh, ffn, F.z2, d, g.w1, d, ffn, d, Tl, L.tn, L.tn_bytes, s));
     GR_TRY(launch_gemm_nn(dt, L.dh, ffn, w->w1, d, L.dz2, d, T, d, ffn, L.wt, s));
-    GR_TRY(launch_fill_f32(g.g2, d, 0.f, s));
-    GR_TRY(launch_rmsnorm_bwd(dt, F.x1, w->g2, L.dz2, dy, L.dx1, g.g2, T, d, s));
+    GR_TRY(launch_rmsnorm_bwd(dt, F.x1, w->g2, L.dz2, dy, L.dx1, g.g2, T, d, L.rms, s));
     att_grad = L.dx1;
   }
   // attention branch: out = Wo o
@@ -409,8 +413,7 @@ genrank_status genrank_layer_bwd(const genrank_batch* b, const genrank_layer_wei
   GR_TRY(launch_gemm_tn(dt, L.dqkv, 3 * d, zin, d, g.wqkv, d, 3 * d, d, Tl, L.tn, L.tn_bytes, s));
   if (!pre) return launch_gemm_nn(dt, L.dqkv, 3 * d, w->wqkv, d, dx, d, T, d, 3 * d, L.wt, s);
   GR_TRY(launch_gemm_nn(dt, L.dqkv, 3 * d, w->wqkv, d, L.dz, d, T, d, 3 * d, L.wt, s));
-  GR_TRY(launch_fill_f32(g.g1, d, 0.f, s));
-  return launch_rmsnorm_bwd(dt, x_in, w->g1, L.dz, L.dx1, dx, g.g1, T, d, s);
+  return launch_rmsnorm_bwd(dt, x_in, w->g1, L.dz, L.dx1, dx, g.g1, T, d, L.rms, s);
 }
 
 genrank_status genrank_linear(int32_t dtype, const void* x, int64_t ldx, const void* w,
@@ -486,20 +489,18 @@ genrank_status genrank_head_fwd(const genrank_batch* b, const void* x, const flo
 
 genrank_status genrank_head_bwd(const genrank_batch* b, const void* x, const float* g_final,
                                 const float* w_head, int32_t n_tasks, const float* dlogits,
-                                void* dx, float* dg_final, float* dw_head, float* db_head,
-                                genrank_stream_t stream) {
+                                void* dx, float* dg_final, float* dw_head, float* db_head, void* ws,
+                                size_t ws_bytes, genrank_stream_t stream) {
   GR_TRY(check_batch(b));
   if (!x || !g_final || !w_head || !dlogits || !dx || !dg_final || !dw_head || !db_head)
     return GENRANK_E_ARG;
   if (n_tasks < 1 || n_tasks > 4) return GENRANK_E_SHAPE;
-  if (b->d > 1024) return GENRANK_E_SHAPE;
+  if (b->d > 1024 || b->d % 4) return GENRANK_E_SHAPE;
+  if (!ws || ws_bytes < head_bwd_workspace(b->d, n_tasks)) return GENRANK_E_WORKSPACE;
   const hipStream_t s = S(stream);
   GR_TRY(launch_fill_zero(b->dtype, dx, b->total_hist * b->d, s));
-  GR_TRY(launch_fill_f32(dg_final, b->d, 0.f, s));
-  GR_TRY(launch_fill_f32(dw_head, static_cast<int64_t>(n_tasks) * b->d, 0.f, s));
-  GR_TRY(launch_fill_f32(db_head, n_tasks, 0.f, s));
   return launch_head_bwd(b->dtype, x, b->total_hist, static_cast<int64_t>(b->B) * b->m, b->d,
-                         g_final, w_head, n_tasks, dlogits, dx, dg_final, dw_head, db_head, s);
+                         g_final, w_head, n_tasks, dlogits, dx, dg_final, dw_head, db_head, ws, s);
 }
 
 genrank_status genrank_bce_loss(int64_t n, int32_t n_tasks, const float* logits,

@@ -35,6 +35,11 @@ struct GemmArgs {
 };
 
 __device__ __forceinline__ float silu_f(float x) { return x / (1.0f + __expf(-x)); }
+// d silu(a) / da = s (1 + a (1 - s)), s = sigmoid(a)
+__device__ __forceinline__ float dsilu_f(float a) {
+  const float sg = 1.0f / (1.0f + __expf(-a));
+  return sg * (1.0f + a * (1.0f - sg));
+}
 
 // LDS operand tile: [128 rows][32 bf16] = 64 B per row, four 16-byte chunks.  Chunk c of
 // row r is stored at chunk c ^ ((r >> 1) & 3): the 16-byte reads of 16 consecutive rows at
@@ -83,6 +88,13 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, const f32x4_t (&acc)
           const uint2 r = *reinterpret_cast<const uint2*>(g.R + static_cast<int64_t>(m) * g.ldr + n);
           v[0] += __uint_as_float(r.x << 16); v[1] += __uint_as_float(r.x & 0xFFFF0000u);
           v[2] += __uint_as_float(r.y << 16); v[3] += __uint_as_float(r.y & 0xFFFF0000u);
+        }
+      }
+      if constexpr (EPI == GEMM_EPI_DSILU) {
+        if (m < g.M) {
+          const uint2 r = *reinterpret_cast<const uint2*>(g.R + static_cast<int64_t>(m) * g.ldr + n);
+          v[0] *= dsilu_f(__uint_as_float(r.x << 16)); v[1] *= dsilu_f(__uint_as_float(r.x & 0xFFFF0000u));
+          v[2] *= dsilu_f(__uint_as_float(r.y << 16)); v[3] *= dsilu_f(__uint_as_float(r.y & 0xFFFF0000u));
         }
       }
       if constexpr (EPI == GEMM_EPI_SILU) {
@@ -346,6 +358,7 @@ __global__ void __launch_bounds__(ST * ST) gemm_general_kernel(
   float v = acc;
   if constexpr (ACCUM) v += to_f32(C[ci]);
   if constexpr (EPI == GEMM_EPI_RESID) v += to_f32(R[static_cast<int64_t>(m) * ldr + n]);
+  if constexpr (EPI == GEMM_EPI_DSILU) v *= dsilu_f(to_f32(R[static_cast<int64_t>(m) * ldr + n]));
   if constexpr (EPI == GEMM_EPI_SILU) {
     if (Cpre) Cpre[static_cast<int64_t>(m) * ldpre + n] = from_f32<TO>(v);
     v = silu_f(v);
@@ -537,7 +550,7 @@ genrank_status launch_gemm_nt(int dtype, const void* A, int64_t lda, const void*
                               int64_t ldr, void* Cpre, int64_t ldpre, hipStream_t stream) {
   if (M <= 0) return GENRANK_OK;
   if (dtype == GENRANK_BF16 && N % GBN == 0 && K % GBK == 0 && lda % 8 == 0 && ldw % 8 == 0 &&
-      ldc % 8 == 0 && (epi != GEMM_EPI_RESID || ldr % 4 == 0) && (!Cpre || ldpre % 4 == 0) &&
+      ldc % 8 == 0 && ((epi != GEMM_EPI_RESID && epi != GEMM_EPI_DSILU) || ldr % 4 == 0) && (!Cpre || ldpre % 4 == 0) &&
       static_cast<int64_t>(GBN) * ldw * 2 < (int64_t(1) << 32)) {
     GemmArgs g{static_cast<const bf16_t*>(A), lda, static_cast<const bf16_t*>(W), ldw, C, ldc,
                static_cast<const bf16_t*>(R), ldr, static_cast<bf16_t*>(Cpre), ldpre, M, N, K};
@@ -552,6 +565,9 @@ genrank_status launch_gemm_nt(int dtype, const void* A, int64_t lda, const void*
           break;
         case GEMM_EPI_SILU:
           hipLaunchKernelGGL(gemm_nt_bf16_dma_kernel<GEMM_EPI_SILU>, dim3(grid), dim3(GTHREADS), 0, stream, g);
+          break;
+        case GEMM_EPI_DSILU:
+          hipLaunchKernelGGL(gemm_nt_bf16_dma_kernel<GEMM_EPI_DSILU>, dim3(grid), dim3(GTHREADS), 0, stream, g);
           break;
         default:
           return GENRANK_E_ARG;
@@ -568,6 +584,9 @@ genrank_status launch_gemm_nt(int dtype, const void* A, int64_t lda, const void*
         break;
       case GEMM_EPI_SILU:
         hipLaunchKernelGGL(gemm_nt_bf16_kernel<GEMM_EPI_SILU>, dim3(grid), dim3(GTHREADS), 0, stream, g);
+        break;
+      case GEMM_EPI_DSILU:
+        hipLaunchKernelGGL(gemm_nt_bf16_kernel<GEMM_EPI_DSILU>, dim3(grid), dim3(GTHREADS), 0, stream, g);
         break;
       default:
         return GENRANK_E_ARG;
@@ -598,6 +617,7 @@ genrank_status launch_gemm_general(int in_dtype, int out_dtype, const void* A, i
     case GEMM_EPI_STORE: GR_GEN(TI, TO, GEMM_EPI_STORE, ACC); break; \
     case GEMM_EPI_RESID: GR_GEN(TI, TO, GEMM_EPI_RESID, ACC); break; \
     case GEMM_EPI_SILU: GR_GEN(TI, TO, GEMM_EPI_SILU, ACC); break;   \
+    case GEMM_EPI_DSILU: GR_GEN(TI, TO, GEMM_EPI_DSILU, ACC); break; \
     default: return GENRANK_E_ARG;                      \
   }
   if (in_dtype == GENRANK_F32 && out_dtype == GENRANK_F32) {
@@ -655,7 +675,8 @@ genrank_status launch_gemm_tn(int dtype, const void* A, int64_t lda, const void*
 }
 
 genrank_status launch_gemm_nn(int dtype, const void* A, int64_t lda, const void* W, int64_t ldw, void* C,
-                              int64_t ldc, int M, int N, int K, void* wt, hipStream_t stream) {
+                              int64_t ldc, int M, int N, int K, void* wt, hipStream_t stream, int epi,
+                              const void* R, int64_t ldr) {
   if (M <= 0 || N <= 0) return GENRANK_OK;
   if (dtype == GENRANK_BF16 && wt && K > 0) {
     // W [K, N] -> W^T [N, K] (pitch K), then C = A (W^T)^T on the NT kernels
@@ -663,10 +684,10 @@ genrank_status launch_gemm_nn(int dtype, const void* A, int64_t lda, const void*
     hipLaunchKernelGGL(transpose_bf16_kernel, grid, dim3(256), 0, stream, static_cast<const bf16_t*>(W), ldw,
                        static_cast<bf16_t*>(wt), static_cast<int64_t>(K), K, N);
     GR_CHECK_LAUNCH();
-    return launch_gemm_nt(dtype, A, lda, wt, K, C, ldc, M, N, K, GEMM_EPI_STORE, nullptr, 0, nullptr, 0, stream);
+    return launch_gemm_nt(dtype, A, lda, wt, K, C, ldc, M, N, K, epi, R, ldr, nullptr, 0, stream);
   }
-  return launch_gemm_general(dtype, dtype, A, lda, 1, W, ldw, 1, C, ldc, M, N, K, GEMM_EPI_STORE, false, nullptr,
-                             0, nullptr, 0, stream);
+  return launch_gemm_general(dtype, dtype, A, lda, 1, W, ldw, 1, C, ldc, M, N, K, epi, false, R, ldr, nullptr, 0,
+                             stream);
 }
 
 }  // namespace genrank

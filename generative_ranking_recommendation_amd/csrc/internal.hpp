@@ -8,7 +8,9 @@
 
 namespace genrank {
 
-enum { GEMM_EPI_STORE = 0, GEMM_EPI_RESID = 1, GEMM_EPI_SILU = 2, GEMM_EPI_F32 = 3 };
+// epilogues: STORE C = acc; RESID C = acc + R; SILU C = silu(acc) (Cpre = acc);
+// F32 C = acc in f32; DSILU C = acc * silu'(R) (R the pre-activation: the SiLU backward)
+enum { GEMM_EPI_STORE = 0, GEMM_EPI_RESID = 1, GEMM_EPI_SILU = 2, GEMM_EPI_F32 = 3, GEMM_EPI_DSILU = 4 };
 
 constexpr float RMS_EPS = 1e-6f;
 
@@ -85,24 +87,25 @@ genrank_status launch_gemm_tn(int dtype, const void* A, int64_t lda, const void*
 // Data gradient: C[M, N] = A[M, K] W[K, N]; bf16 transposes W into wt ([N, K], N * K elements)
 // and runs the NT kernels
 genrank_status launch_gemm_nn(int dtype, const void* A, int64_t lda, const void* W, int64_t ldw, void* C,
-                              int64_t ldc, int M, int N, int K, void* wt, hipStream_t stream);
+                              int64_t ldc, int M, int N, int K, void* wt, hipStream_t stream,
+                              int epi = GEMM_EPI_STORE, const void* R = nullptr, int64_t ldr = 0);
 
 // row-wise ops
 genrank_status launch_rmsnorm(int dtype, const void* x, const float* g, void* y, int64_t rows,
                               int d, hipStream_t stream);
+size_t rmsnorm_bwd_workspace(int d);  // per-block partial rows of dg
 genrank_status launch_rmsnorm_bwd(int dtype, const void* x, const float* g, const void* dy,
-                                  const void* add, void* dx, float* dg, int64_t rows, int d,
+                                  const void* add, void* dx, float* dg, int64_t rows, int d, void* ws,
                                   hipStream_t stream);
-genrank_status launch_silu_bwd(int dtype, const void* a, const void* dy, void* da, int64_t n,
-                               hipStream_t stream);
 genrank_status launch_fill_f32(float* p, int64_t n, float v, hipStream_t stream);
 genrank_status launch_fill_zero(int dtype, void* p, int64_t n, hipStream_t stream);
 genrank_status launch_head_fwd(int dtype, const void* x, int64_t row0, int64_t rows, int d,
                                const float* g, const float* w, const float* bias, int nt,
                                float* logits, hipStream_t stream);
+size_t head_bwd_workspace(int d, int nt);  // per-block partial rows of dg, dw, db
 genrank_status launch_head_bwd(int dtype, const void* x, int64_t row0, int64_t rows, int d,
                                const float* g, const float* w, int nt, const float* dlogits,
-                               void* dx, float* dg, float* dw, float* db, hipStream_t stream);
+                               void* dx, float* dg, float* dw, float* db, void* ws, hipStream_t stream);
 genrank_status launch_bce(int64_t n, int nt, const float* logits, const float* labels,
                           float* loss, float* dlogits, hipStream_t stream);
 

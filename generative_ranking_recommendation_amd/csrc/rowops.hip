@@ -1,6 +1,8 @@
-// Row-wise pieces of the GenRank block and head: RMSNorm (+ backward), SiLU backward,
+// Row-wise pieces of the GenRank block and head: RMSNorm (+ backward),
 // the per-candidate action head (+ backward), sigmoid BCE at candidate rows, fills.
 // One wave per row; rows are read with 16-byte vector loads where the width allows.
+#include <algorithm>
+
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -33,61 +35,145 @@ __global__ void __launch_bounds__(RW) rmsnorm_kernel(const T* __restrict__ x, co
   for (int c = lane; c < d; c += 64) yr[c] = from_f32<T>(to_f32(xr[c]) * inv * g[c]);
 }
 
-// dx = r g dy - r^3 x sum(g dy x) / d  (+ add);  dg += sum_rows dy x r.
-// Each wave walks rows with a grid stride and keeps its dg partial in registers (lane c
-// owns columns c, c+64, ...), so dg takes one atomic per column per wave.
-constexpr int MAXC = 16;  // d <= 1024
-
-template <typename T>
-__global__ void __launch_bounds__(RW) rmsnorm_bwd_kernel(const T* __restrict__ x, const float* __restrict__ g,
-                                                         const T* __restrict__ dy, const T* add,
-                                                         T* dx, float* __restrict__ dg,
-                                                         int64_t rows, int d) {
-  const int lane = threadIdx.x & 63;
-  const int64_t nw = static_cast<int64_t>(gridDim.x) * (RW / 64);
-  float part[MAXC];
-#pragma unroll
-  for (int i = 0; i < MAXC; ++i) part[i] = 0.f;
-  for (int64_t r = static_cast<int64_t>(blockIdx.x) * (RW / 64) + (threadIdx.x >> 6); r < rows; r += nw) {
-    const T* xr = x + r * d;
-    const T* dyr = dy + r * d;
-    float ss = 0.f, dot = 0.f;
-    for (int c = lane; c < d; c += 64) {
-      const float v = to_f32(xr[c]);
-      ss += v * v;
-      dot += g[c] * to_f32(dyr[c]) * v;
-    }
-    ss = wave_sum(ss);
-    dot = wave_sum(dot);
-    const float rr = rsqrtf(ss / d + RMS_EPS);
-    const float c3 = rr * rr * rr * dot / d;
-#pragma unroll
-    for (int i = 0; i < MAXC; ++i) {
-      const int c = lane + 64 * i;
-      if (c >= d) break;
-      const float v = to_f32(xr[c]);
-      const float gy = to_f32(dyr[c]);
-      float o = rr * g[c] * gy - c3 * v;
-      if (add) o += to_f32(add[r * d + c]);
-      dx[r * d + c] = from_f32<T>(o);
-      part[i] += gy * v * rr;
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < MAXC; ++i) {
-    const int c = lane + 64 * i;
-    if (c >= d) break;
-    atomicAdd(dg + c, part[i]);
-  }
+// 4 consecutive elements as f32 (8-byte bf16 / 16-byte f32 accesses)
+__device__ __forceinline__ void ld4(const bf16_t* p, float* f) {
+  const uint2 v = *reinterpret_cast<const uint2*>(p);
+  f[0] = __uint_as_float(v.x << 16); f[1] = __uint_as_float(v.x & 0xFFFF0000u);
+  f[2] = __uint_as_float(v.y << 16); f[3] = __uint_as_float(v.y & 0xFFFF0000u);
+}
+__device__ __forceinline__ void ld4(const float* p, float* f) {
+  const float4 v = *reinterpret_cast<const float4*>(p);
+  f[0] = v.x; f[1] = v.y; f[2] = v.z; f[3] = v.w;
+}
+__device__ __forceinline__ void st4(bf16_t* p, const float* f) {
+  *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]));
+}
+__device__ __forceinline__ void st4(float* p, const float* f) {
+  *reinterpret_cast<float4*>(p) = make_float4(f[0], f[1], f[2], f[3]);
 }
 
+// Parameter gradients (sums over rows) are formed without atomics: each wave keeps its
+// partial in registers, the block adds its waves' partials in order through LDS and
+// writes one partial row, and column_sum_kernel adds the blocks' rows in order.
+constexpr int MAXQ = 4;           // 4-column groups per lane: d <= 64 * 4 * MAXQ = 1024
+constexpr int PART_BLOCKS = 512;  // rmsnorm backward blocks (partial rows)
+
+// dx = r g dy - r^3 x sum(g dy x) / d  (+ add);  dg = sum over rows of dy x r.
+// Lane l owns columns 4 l + 256 q; a wave takes two rows per step.
 template <typename T>
-__global__ void silu_bwd_kernel(const T* __restrict__ a, const T* __restrict__ dy, T* __restrict__ da, int64_t n) {
-  for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < n;
-       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    const float av = to_f32(a[i]);
-    const float sg = 1.f / (1.f + __expf(-av));
-    da[i] = from_f32<T>(to_f32(dy[i]) * sg * (1.f + av * (1.f - sg)));
+__global__ void __launch_bounds__(RW) rmsnorm_bwd_kernel(const T* __restrict__ x, const float* __restrict__ g,
+                                                         const T* dy, const T* add, T* dx,
+                                                         float* __restrict__ part, int64_t rows, int d) {
+  __shared__ float sp[RW / 64][64 * 4 * MAXQ];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t nw = static_cast<int64_t>(gridDim.x) * (RW / 64);
+  float pg[MAXQ][4];
+#pragma unroll
+  for (int q = 0; q < MAXQ; ++q)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) pg[q][e] = 0.f;
+  for (int64_t r0 = static_cast<int64_t>(blockIdx.x) * (RW / 64) + wave; r0 < rows; r0 += 2 * nw) {
+    float xv[2][MAXQ][4], gv[2][MAXQ][4], ss[2] = {0.f, 0.f}, dot[2] = {0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int64_t r = r0 + k * nw;
+#pragma unroll
+      for (int q = 0; q < MAXQ; ++q) {
+        const int c = 4 * lane + 256 * q;
+        if (r < rows && c < d) {
+          ld4(x + r * d + c, xv[k][q]);
+          ld4(dy + r * d + c, gv[k][q]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) xv[k][q][e] = gv[k][q][e] = 0.f;
+        }
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+#pragma unroll
+      for (int q = 0; q < MAXQ; ++q) {
+        const int c = 4 * lane + 256 * q;
+        if (c >= d) break;
+        const float4 g4 = *reinterpret_cast<const float4*>(g + c);
+        const float gg[4] = {g4.x, g4.y, g4.z, g4.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          ss[k] += xv[k][q][e] * xv[k][q][e];
+          dot[k] += gg[e] * gv[k][q][e] * xv[k][q][e];
+        }
+      }
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int64_t r = r0 + k * nw;
+      const float s2 = wave_sum(ss[k]), dt = wave_sum(dot[k]);
+      if (r >= rows) continue;
+      const float rr = rsqrtf(s2 / d + RMS_EPS);
+      const float c3 = rr * rr * rr * dt / d;
+#pragma unroll
+      for (int q = 0; q < MAXQ; ++q) {
+        const int c = 4 * lane + 256 * q;
+        if (c >= d) break;
+        const float4 g4 = *reinterpret_cast<const float4*>(g + c);
+        const float gg[4] = {g4.x, g4.y, g4.z, g4.w};
+        float o[4], ad[4] = {0.f, 0.f, 0.f, 0.f};
+        if (add) ld4(add + r * d + c, ad);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          o[e] = rr * gg[e] * gv[k][q][e] - c3 * xv[k][q][e] + ad[e];
+          pg[q][e] += gv[k][q][e] * xv[k][q][e] * rr;
+        }
+        st4(dx + r * d + c, o);
+      }
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < MAXQ; ++q) {
+    const int c = 4 * lane + 256 * q;
+    if (c < d)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sp[wave][c + e] = pg[q][e];
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < d; c += RW)
+    part[static_cast<int64_t>(blockIdx.x) * d + c] = ((sp[0][c] + sp[1][c]) + sp[2][c]) + sp[3][c];
+}
+
+// Column c's sum over b < nparts of part[b * width + c], b ascending, goes to out0[c] for
+// c < n0, out1[c - n0] for c < n0 + n1, out2[c - n0 - n1] beyond.  Block: 16 columns x 16
+// groups of partial rows; the groups' sums are added in order.
+__global__ void __launch_bounds__(256) column_sum_kernel(const float* __restrict__ part, int nparts, int width,
+                                                         float* __restrict__ out0, int n0,
+                                                         float* __restrict__ out1, int n1,
+                                                         float* __restrict__ out2) {
+  __shared__ float sg[16][17];
+  const int cl = threadIdx.x & 15, grp = threadIdx.x >> 4;
+  const int c = blockIdx.x * 16 + cl;
+  float acc = 0.f;
+  if (c < width) {
+    const int per = (nparts + 15) / 16;
+    const int b0 = grp * per, b1 = min(nparts, b0 + per);
+    int b = b0;
+    for (; b + 4 <= b1; b += 4) {
+      const float v0 = part[static_cast<int64_t>(b) * width + c];
+      const float v1 = part[static_cast<int64_t>(b + 1) * width + c];
+      const float v2 = part[static_cast<int64_t>(b + 2) * width + c];
+      const float v3 = part[static_cast<int64_t>(b + 3) * width + c];
+      acc = (((acc + v0) + v1) + v2) + v3;
+    }
+    for (; b < b1; ++b) acc += part[static_cast<int64_t>(b) * width + c];
+  }
+  sg[grp][cl] = acc;
+  __syncthreads();
+  if (grp == 0 && c < width) {
+    float t = 0.f;
+    for (int k = 0; k < 16; ++k) t += sg[k][cl];
+    if (c < n0)
+      out0[c] = t;
+    else if (c < n0 + n1)
+      out1[c - n0] = t;
+    else
+      out2[c - n0 - n1] = t;
   }
 }
 
@@ -135,80 +221,103 @@ __global__ void __launch_bounds__(RW) head_fwd_kernel(const T* __restrict__ x, i
 }
 
 // z = rmsnorm(x) g; dz = dlogits . w; dx by the RMSNorm backward with dz as the output
-// gradient; dw[t] += dlogits[t] z; db[t] += dlogits[t]; dg += dz x r.  Parameter
-// gradients are summed per wave in registers, then added with one atomic per element.
+// gradient; dw[t] = sum dlogits[t] z; db[t] = sum dlogits[t]; dg = sum dz x r.  One wave per
+// row (grid stride), lane l owning columns 4 l + 256 q; the block's waves add their
+// parameter partials in order through LDS into one partial row
+// [dg (d) | dw (nt d) | db (nt)], summed over blocks by column_sum_kernel.
+constexpr int HEAD_BLOCKS = 64;
+
 template <typename T>
 __global__ void __launch_bounds__(RW) head_bwd_kernel(const T* __restrict__ x, int64_t row0, int64_t rows,
                                                       int d, const float* __restrict__ g,
                                                       const float* __restrict__ w, int nt,
                                                       const float* __restrict__ dl, T* __restrict__ dx,
-                                                      float* __restrict__ dg, float* __restrict__ dw,
-                                                      float* __restrict__ db) {
-  const int lane = threadIdx.x & 63;
+                                                      float* __restrict__ part) {
+  __shared__ float sp[64 * 4 * MAXQ * 5 + 4];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t nw = static_cast<int64_t>(gridDim.x) * (RW / 64);
-  float pg[MAXC], pw[4][MAXC], pb[4];
+  const int width = d * (1 + nt) + nt;
+  float pg[MAXQ][4], pw[4][MAXQ][4], pb[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int i = 0; i < MAXC; ++i) {
-    pg[i] = 0.f;
+  for (int q = 0; q < MAXQ; ++q)
 #pragma unroll
-    for (int t = 0; t < 4; ++t) pw[t][i] = 0.f;
-  }
+    for (int e = 0; e < 4; ++e) {
+      pg[q][e] = 0.f;
 #pragma unroll
-  for (int t = 0; t < 4; ++t) pb[t] = 0.f;
-  for (int64_t r = static_cast<int64_t>(blockIdx.x) * (RW / 64) + (threadIdx.x >> 6); r < rows; r += nw) {
+      for (int t = 0; t < 4; ++t) pw[t][q][e] = 0.f;
+    }
+  for (int64_t r = static_cast<int64_t>(blockIdx.x) * (RW / 64) + wave; r < rows; r += nw) {
     const T* xr = x + (row0 + r) * d;
     float dlr[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) dlr[t] = (t < nt) ? dl[r * nt + t] : 0.f;
-    float ss = 0.f, dot = 0.f;
+    float xv[MAXQ][4], dz[MAXQ][4], ss = 0.f, dot = 0.f;
 #pragma unroll
-    for (int i = 0; i < MAXC; ++i) {
-      const int c = lane + 64 * i;
-      if (c >= d) break;
-      const float v = to_f32(xr[c]);
-      ss += v * v;
-      float dz = 0.f;
+    for (int q = 0; q < MAXQ; ++q) {
+      const int c = 4 * lane + 256 * q;
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
-        if (t < nt) dz += dlr[t] * w[t * d + c];
-      dot += g[c] * dz * v;
+      for (int e = 0; e < 4; ++e) xv[q][e] = dz[q][e] = 0.f;
+      if (c >= d) continue;
+      ld4(xr + c, xv[q]);
+      const float4 g4 = *reinterpret_cast<const float4*>(g + c);
+      const float gg[4] = {g4.x, g4.y, g4.z, g4.w};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        if (t >= nt) break;
+        const float4 w4 = *reinterpret_cast<const float4*>(w + t * d + c);
+        dz[q][0] += dlr[t] * w4.x; dz[q][1] += dlr[t] * w4.y;
+        dz[q][2] += dlr[t] * w4.z; dz[q][3] += dlr[t] * w4.w;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        ss += xv[q][e] * xv[q][e];
+        dot += gg[e] * dz[q][e] * xv[q][e];
+      }
     }
     ss = wave_sum(ss);
     dot = wave_sum(dot);
     const float rr = rsqrtf(ss / d + RMS_EPS);
     const float c3 = rr * rr * rr * dot / d;
 #pragma unroll
-    for (int i = 0; i < MAXC; ++i) {
-      const int c = lane + 64 * i;
+    for (int q = 0; q < MAXQ; ++q) {
+      const int c = 4 * lane + 256 * q;
       if (c >= d) break;
-      const float v = to_f32(xr[c]);
-      float dz = 0.f;
+      const float4 g4 = *reinterpret_cast<const float4*>(g + c);
+      const float gg[4] = {g4.x, g4.y, g4.z, g4.w};
+      float o[4];
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
-        if (t < nt) dz += dlr[t] * w[t * d + c];
-      dx[(row0 + r) * d + c] = from_f32<T>(rr * g[c] * dz - c3 * v);
-      pg[i] += dz * v * rr;
-      const float z = v * rr * g[c];
+      for (int e = 0; e < 4; ++e) {
+        o[e] = rr * gg[e] * dz[q][e] - c3 * xv[q][e];
+        pg[q][e] += dz[q][e] * xv[q][e] * rr;
+        const float z = xv[q][e] * rr * gg[e];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) pw[t][i] += dlr[t] * z;
+        for (int t = 0; t < 4; ++t) pw[t][q][e] += dlr[t] * z;
+      }
+      st4(dx + (row0 + r) * d + c, o);
     }
 #pragma unroll
     for (int t = 0; t < 4; ++t) pb[t] += dlr[t];
   }
+  // waves in order: wave 0 writes, waves 1..3 add
+  for (int wv = 0; wv < RW / 64; ++wv) {
+    if (wave == wv) {
 #pragma unroll
-  for (int i = 0; i < MAXC; ++i) {
-    const int c = lane + 64 * i;
-    if (c >= d) break;
-    atomicAdd(dg + c, pg[i]);
+      for (int q = 0; q < MAXQ; ++q) {
+        const int c = 4 * lane + 256 * q;
+        if (c >= d) break;
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
-      if (t < nt) atomicAdd(dw + t * d + c, pw[t][i]);
+        for (int e = 0; e < 4; ++e) {
+          sp[c + e] = wv ? sp[c + e] + pg[q][e] : pg[q][e];
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+            if (t < nt) sp[d * (1 + t) + c + e] = wv ? sp[d * (1 + t) + c + e] + pw[t][q][e] : pw[t][q][e];
+        }
+      }
+      if (lane < nt) sp[d * (1 + nt) + lane] = wv ? sp[d * (1 + nt) + lane] + pb[lane] : pb[lane];
+    }
+    __syncthreads();
   }
-  if (lane == 0) {
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-      if (t < nt) atomicAdd(db + t, pb[t]);
-  }
+  for (int c = threadIdx.x; c < width; c += RW) part[static_cast<int64_t>(blockIdx.x) * width + c] = sp[c];
 }
 
 // one block: mean BCE over n*nt logits (deterministic order) and its gradient
@@ -255,35 +364,25 @@ genrank_status launch_rmsnorm(int dtype, const void* x, const float* g, void* y,
   return GENRANK_OK;
 }
 
+size_t rmsnorm_bwd_workspace(int d) { return static_cast<size_t>(PART_BLOCKS) * d * sizeof(float); }
+
 genrank_status launch_rmsnorm_bwd(int dtype, const void* x, const float* g, const void* dy,
-                                  const void* add, void* dx, float* dg, int64_t rows, int d,
+                                  const void* add, void* dx, float* dg, int64_t rows, int d, void* ws,
                                   hipStream_t stream) {
-  if (rows <= 0) return GENRANK_OK;
-  if (d > 64 * MAXC) return GENRANK_E_SHAPE;
-  const unsigned grid = static_cast<unsigned>(rows < 4096 ? (rows + 3) / 4 : 1024);
+  if (d > 256 * MAXQ || d % 4) return GENRANK_E_SHAPE;
+  float* part = static_cast<float*>(ws);
+  if (rows <= 0) return launch_fill_f32(dg, d, 0.f, stream);
+  const unsigned grid = static_cast<unsigned>(std::min<int64_t>(PART_BLOCKS, (rows + 7) / 8));
   if (dtype == GENRANK_BF16)
     hipLaunchKernelGGL(rmsnorm_bwd_kernel<bf16_t>, dim3(grid), dim3(RW), 0, stream,
                        static_cast<const bf16_t*>(x), g, static_cast<const bf16_t*>(dy),
-                       static_cast<const bf16_t*>(add), static_cast<bf16_t*>(dx), dg, rows, d);
+                       static_cast<const bf16_t*>(add), static_cast<bf16_t*>(dx), part, rows, d);
   else
     hipLaunchKernelGGL(rmsnorm_bwd_kernel<float>, dim3(grid), dim3(RW), 0, stream,
                        static_cast<const float*>(x), g, static_cast<const float*>(dy),
-                       static_cast<const float*>(add), static_cast<float*>(dx), dg, rows, d);
-  GR_CHECK_LAUNCH();
-  return GENRANK_OK;
-}
-
-genrank_status launch_silu_bwd(int dtype, const void* a, const void* dy, void* da, int64_t n,
-                               hipStream_t stream) {
-  if (n <= 0) return GENRANK_OK;
-  if (dtype == GENRANK_BF16)
-    hipLaunchKernelGGL(silu_bwd_kernel<bf16_t>, dim3(blocks_for(n, 256)), dim3(256), 0, stream,
-                       static_cast<const bf16_t*>(a), static_cast<const bf16_t*>(dy),
-                       static_cast<bf16_t*>(da), n);
-  else
-    hipLaunchKernelGGL(silu_bwd_kernel<float>, dim3(blocks_for(n, 256)), dim3(256), 0, stream,
-                       static_cast<const float*>(a), static_cast<const float*>(dy),
-                       static_cast<float*>(da), n);
+                       static_cast<const float*>(add), static_cast<float*>(dx), part, rows, d);
+  hipLaunchKernelGGL(column_sum_kernel, dim3((d + 15) / 16), dim3(256), 0, stream, part,
+                     static_cast<int>(grid), d, dg, d, nullptr, 0, nullptr);
   GR_CHECK_LAUNCH();
   return GENRANK_OK;
 }
@@ -319,23 +418,36 @@ genrank_status launch_head_fwd(int dtype, const void* x, int64_t row0, int64_t r
   return GENRANK_OK;
 }
 
+size_t head_bwd_workspace(int d, int nt) {
+  return static_cast<size_t>(HEAD_BLOCKS) * (static_cast<size_t>(d) * (1 + nt) + nt) * sizeof(float);
+}
+
 genrank_status launch_head_bwd(int dtype, const void* x, int64_t row0, int64_t rows, int d,
                                const float* g, const float* w, int nt, const float* dlogits,
-                               void* dx, float* dg, float* dw, float* db, hipStream_t stream) {
-  if (rows <= 0) return GENRANK_OK;
-  if (d > 64 * MAXC || nt > 4) return GENRANK_E_SHAPE;
-  const unsigned grid = static_cast<unsigned>(rows < 4096 ? (rows + 3) / 4 : 1024);
+                               void* dx, float* dg, float* dw, float* db, void* ws, hipStream_t stream) {
+  if (d > 256 * MAXQ || d % 4 || nt > 4) return GENRANK_E_SHAPE;
+  if (rows <= 0) {
+    genrank_status st = launch_fill_f32(dg, d, 0.f, stream);
+    if (st == GENRANK_OK) st = launch_fill_f32(dw, static_cast<int64_t>(nt) * d, 0.f, stream);
+    return st == GENRANK_OK ? launch_fill_f32(db, nt, 0.f, stream) : st;
+  }
+  float* part = static_cast<float*>(ws);
+  const int width = d * (1 + nt) + nt;
+  const unsigned grid = static_cast<unsigned>(std::min<int64_t>(HEAD_BLOCKS, (rows + 3) / 4));
   if (dtype == GENRANK_BF16)
     hipLaunchKernelGGL(head_bwd_kernel<bf16_t>, dim3(grid), dim3(RW), 0, stream,
                        static_cast<const bf16_t*>(x), row0, rows, d, g, w, nt, dlogits,
-                       static_cast<bf16_t*>(dx), dg, dw, db);
+                       static_cast<bf16_t*>(dx), part);
   else
     hipLaunchKernelGGL(head_bwd_kernel<float>, dim3(grid), dim3(RW), 0, stream,
                        static_cast<const float*>(x), row0, rows, d, g, w, nt, dlogits,
-                       static_cast<float*>(dx), dg, dw, db);
+                       static_cast<float*>(dx), part);
+  hipLaunchKernelGGL(column_sum_kernel, dim3((width + 15) / 16), dim3(256), 0, stream, part,
+                     static_cast<int>(grid), width, dg, d, dw, nt * d, db);
   GR_CHECK_LAUNCH();
   return GENRANK_OK;
 }
+
 
 genrank_status launch_bce(int64_t n, int nt, const float* logits, const float* labels,
                           float* loss, float* dlogits, hipStream_t stream) {

@@ -105,8 +105,10 @@ class GenRank:
         f32 = lambda *s: torch.empty(s, dtype=torch.float32, device=dev)
         grads = {"g_final": f32(d), "w_head": f32(nt, d), "b_head": f32(nt)}
         dx = self.act(inp.rows)
+        nwh = B.genrank_workspace_size(B.OP_HEAD_BWD, bt)
         B.genrank_head_bwd(bt, x_final, self.head.g_final, self.head.w_head, nt, dlogits, dx,
-                           grads["g_final"], grads["w_head"], grads["b_head"], stream)
+                           grads["g_final"], grads["w_head"], grads["b_head"],
+                           self._buf(("head_bwd",), nwh), nwh, stream)
         grads["layers"] = [None] * len(self.layers)
         for i in range(len(self.layers) - 1, -1, -1):
             lay = self.layers[i]

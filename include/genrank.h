@@ -78,7 +78,8 @@ typedef enum {
   GENRANK_OP_ATTN_BWD = 2,
   GENRANK_OP_LAYER_FWD = 3,
   GENRANK_OP_LAYER_BWD = 4,
-  GENRANK_OP_EMBED_BWD = 5
+  GENRANK_OP_EMBED_BWD = 5,
+  GENRANK_OP_HEAD_BWD = 6
 } genrank_op;
 
 /* Batch geometry.  total_hist and max_hist are host copies of hist_offsets[B] and
@@ -304,11 +305,14 @@ GENRANK_API genrank_status genrank_head_fwd(const genrank_batch* batch, const vo
 
 /* Backward of genrank_head_fwd.  dx: [T, d] in batch.dtype; history rows are set to
  * zero (the loss is taken at candidate positions only, [GR-zh] section 1.3.1).
- * dg_final [d], dw_head [n_tasks, d], db_head [n_tasks]: f32, overwritten. */
+ * dg_final [d], dw_head [n_tasks, d], db_head [n_tasks]: f32, overwritten; they are sums over
+ * the candidate rows formed in a fixed order (per-block partials in ws, then summed), so
+ * the result does not depend on scheduling.  ws: genrank_workspace_size(GENRANK_OP_HEAD_BWD)
+ * bytes (sized for n_tasks <= 4). */
 GENRANK_API genrank_status genrank_head_bwd(const genrank_batch* batch, const void* x, const float* g_final,
                                 const float* w_head, int32_t n_tasks, const float* dlogits,
                                 void* dx, float* dg_final, float* dw_head, float* db_head,
-                                genrank_stream_t stream);
+                                void* ws, size_t ws_bytes, genrank_stream_t stream);
 
 /* Mean sigmoid binary cross-entropy over n rows x n_tasks logits and its gradient:
  * loss[0] = mean(softplus(z) - y z); dlogits = (sigmoid(z) - y) / (n * n_tasks).
