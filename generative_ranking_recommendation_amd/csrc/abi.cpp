@@ -390,7 +390,6 @@ genrank_status genrank_layer_bwd(const genrank_batch* b, const genrank_layer_wei
   const int T = static_cast<int>(rows_of(b));
   const int d = b->d;
   const size_t es = dtype_size(dt);
-  const int F32 = GENRANK_F32;
   const void* att_grad = dy;  // gradient reaching the attention branch output
   const int64_t Tl = T;
   if (pre) {

@@ -87,6 +87,26 @@ __device__ __forceinline__ bool attn_allowed(int i, int j, int N) {
   return (i < N) ? (j <= i) : (j < N || j == i);
 }
 
+// ---- direct global -> LDS loads and explicit waits (operand rings)
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
+// vmcnt(n) with every other counter left alone (gfx9 encoding: vmcnt in bits 3:0 and
+// 15:14, expcnt 6:4, lgkmcnt 11:8).  On gfx9 vector loads and stores share this counter
+// and retire in issue order.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+// all waves past this point see every LDS write made before it; the empty asm keeps the
+// compiler from moving memory accesses across
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 }  // namespace genrank
 
 #define GR_CHECK_LAUNCH()                                   \

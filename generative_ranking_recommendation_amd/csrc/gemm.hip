@@ -226,23 +226,6 @@ __global__ void __launch_bounds__(GTHREADS) gemm_nt_bf16_kernel(GemmArgs g) {
 constexpr int DSTAGE_ELEMS = 64 * CP;  // bf16 per stage buffer: A and W tiles, or half of C
 static_assert(2 * GBM * GBK <= DSTAGE_ELEMS, "stage buffer holds an A and a W tile");
 
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) void glb_void_t;
-
-// vmcnt(n) with every other counter left alone (gfx9 encoding: vmcnt in bits 3:0 and
-// 15:14, expcnt 6:4, lgkmcnt 11:8)
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 16, "");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
-}
-// all waves past this point see every LDS write made before it; the empty asm keeps the
-// compiler from moving memory accesses across
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
 
 template <int EPI>
 __global__ void __launch_bounds__(GTHREADS) gemm_nt_bf16_dma_kernel(GemmArgs g) {
