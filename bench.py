@@ -7,6 +7,8 @@ A step is one pass of the hot path over one batch already resident in HBM:
     embed-sum (fused index derivation + five-table gather)
     -> QKV projection -> masked ALiBi attention -> output projection      (single-layer form)
 or, for pre-norm workloads, embed-sum -> L x genrank_layer_fwd -> action head.
+With --workload train2_bf16 a step is one training step (forward, BCE at the candidates,
+backward, table gradients) and the roofline is the attention backward's.
 With --workload hstu_interleaved it instead measures the HSTU-style comparison on the same
 users: the interleaved item/action sequence (2N + m slots) with a learned relative bias
 materialised in memory, against the action-oriented attention with in-register ALiBi.
@@ -203,6 +205,147 @@ def bench_hstu(args):
     print(json.dumps(out), flush=True)
 
 
+def cpu_baseline_train(cfg, batch, tables, weights, labels, budget_s):
+    """The fp64 CPU oracle's training step (forward, BCE at candidates, backward, table
+    gradients) on the first users of the same batch, for about budget_s seconds."""
+    import numpy as np
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import oracle
+    from common import oracle_geom, oracle_head, oracle_indices, oracle_layers, oracle_tables
+    layers, head, tabs = oracle_layers(weights), oracle_head(weights), oracle_tables(tables)
+    t0 = time.perf_counter()
+    users = 0
+    while users < batch.B and (users < 1 or time.perf_counter() - t0 < budget_s):
+        sub = batch.subset([users])
+        c1 = cfg.replace(B=1)
+        idx = oracle_indices(c1, sub, tables)
+        x = oracle.embed_sum(tabs, sub.hist_items, sub.cand_items, idx)
+        geom = oracle_geom(c1, sub, idx)
+        xf, logits, caches = oracle.model_fwd(x, layers, cfg.block, cfg.H, geom, head)
+        lab = labels[users * cfg.m:(users + 1) * cfg.m]
+        oracle.bce_loss(logits, lab)
+        dx0, _, _ = oracle.model_bwd(oracle.bce_loss_bwd(logits, lab), xf, layers, cfg.block, cfg.H, geom,
+                                     caches, head)
+        shapes = {k: getattr(tables, k).shape for k in ("action", "pos", "ri", "rt")}
+        used = np.concatenate([sub.hist_items, sub.cand_items])
+        shapes["item"] = (int(used.max()) + 1, cfg.d)
+        oracle.embed_bwd(dx0, shapes, sub.hist_items, sub.cand_items, idx)
+        users += 1
+    dt = time.perf_counter() - t0
+    return {"value": users * cfg.m / dt, "unit": "candidates/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {users} users of {cfg.name} (same seeded batch), full training step in fp64 "
+                      f"numpy: forward, BCE at candidates, backward, table gradients; {dt:.1f} s",
+            "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def bench_train(args, cfg):
+    """One training step (forward with saved activations, BCE at candidate positions, full
+    backward with table gradients) per step; candidates trained per second.  The roofline is
+    reported for the attention backward, timed alone on the same batch geometry with
+    q, k, v, dO ~ N(0, 1) (two MFMA kernels plus the D pass)."""
+    import numpy as np
+    import torch
+
+    import synth
+    from generative_ranking_recommendation_amd import binding as B
+    from generative_ranking_recommendation_amd import workload as W
+    from generative_ranking_recommendation_amd.device import DeviceInputs, to_device
+    from generative_ranking_recommendation_amd.model import GenRank
+    from generative_ranking_recommendation_amd.slopes import alibi_slopes
+
+    log(f"workload {cfg.name}: generating inputs")
+    batch, tables, weights = synth.make_batch(cfg), synth.make_tables(cfg), synth.make_weights(cfg)
+    labels = synth.make_labels(cfg)
+    sp, st = alibi_slopes(cfg.H, cfg.time_ratio)
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    model = GenRank.from_host(cfg, tables, weights, sp, st, dev)
+    inp = DeviceInputs(batch, dev)
+    lab = to_device(labels, dev, np.float32)
+    T, d, H, m = inp.rows, cfg.d, cfg.H, cfg.m
+    for _ in range(args.warmup):
+        model.train_step(inp, lab)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        model.train_step(inp, lab)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    log(f"{ms:.4f} ms/step")
+
+    # attention backward alone
+    bt = model.batch(inp)
+    g = torch.Generator(device=dev)
+    g.manual_seed(11)
+    qkv = torch.randn((T, 3 * d), generator=g, device=dev).to(torch.bfloat16)
+    dout = torch.randn((T, d), generator=g, device=dev).to(torch.bfloat16)
+    o = torch.empty((T, d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+    dqkv = torch.empty((T, 3 * d), dtype=torch.bfloat16, device=dev)
+    nws = B.genrank_workspace_size(B.OP_ATTN_BWD, bt)
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev)
+    sl = B.HostSlopes(sp, st)
+    stream = torch.cuda.current_stream()
+    p, q = qkv.data_ptr(), dqkv.data_ptr()
+    B.genrank_attn_fwd(bt, inp.hist_offsets, inp.hist_ts, inp.req_ts, sl, p, p + 2 * d, p + 4 * d, 3 * d,
+                       o, d, lse, stream)
+
+    def bwd():
+        B.genrank_attn_bwd(bt, inp.hist_offsets, inp.hist_ts, inp.req_ts, sl, p, p + 2 * d, p + 4 * d, 3 * d,
+                           o, dout, d, lse, q, q + 2 * d, q + 4 * d, 3 * d, 0, ws, nws, stream)
+    for _ in range(args.warmup):
+        bwd()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for k in range(args.steps):
+        bwd()
+        ev[k + 1].record(stream)
+    torch.cuda.synchronize()
+    t_us = float(np.mean([ev[k].elapsed_time(ev[k + 1]) for k in range(args.steps)])) * 1e3
+    lengths = inp.lengths
+    flops = W.attention_bwd_flops(lengths, m, d)
+    flops_rc = W.attention_bwd_flops(lengths, m, d, recompute=True)
+    nbytes = W.attention_bwd_hbm_floor_bytes(T, d, H)
+    if nbytes / (PEAK_HBM_GBS * 1e9) >= flops / (PEAK_BF16_TFLOPS * 1e12):
+        bound, achieved, peak, unit = "hbm", nbytes / (t_us * 1e-6) / 1e9, PEAK_HBM_GBS, "GB/s"
+    else:
+        bound, achieved, peak, unit = "mfma", flops / (t_us * 1e-6) / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
+    tf = flops / (t_us * 1e-6) / 1e12
+    log(f"attention backward {t_us:.1f} us, {tf:.1f} TFLOP/s (recompute excluded)")
+    roofline = {"kernel": "attn_bwd", "bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+                "frac": round(achieved / peak, 4), "traffic": None}
+    cpu = None
+    if args.cpu_seconds > 0:
+        log("CPU oracle baseline ...")
+        cpu = cpu_baseline_train(cfg, batch, tables, weights, labels, args.cpu_seconds)
+        log(f"CPU oracle: {cpu['value']:.1f} candidates/s on {cpu['cores']} threads")
+    out = {
+        "metric": "candidates trained/sec (GenRank fwd + bwd, bf16)",
+        "value": round(inp.B * m / (ms * 1e-3), 1),
+        "unit": "candidates/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype,
+        "data": "synthetic (seeded; Zipf(1.1) item ids, jagged histories, Bernoulli(0.1) labels)",
+        "config": {"workload": cfg.name, "users": inp.B, "candidates_per_user": m,
+                   "history": f"U[{cfg.hist_min},{cfg.hist_max}]", "rows": T, "d": d, "heads": H,
+                   "layers": cfg.layers, "block": cfg.block},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernels": {"attn_bwd": {"time_us": round(t_us, 2), "bound": bound, "achieved": round(achieved, 2),
+                                 "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),
+                                 "flops": int(flops), "flops_with_recompute": int(flops_rc),
+                                 "floor_bytes": int(nbytes), "tflops": round(tf, 2),
+                                 "mfma_util_pct": round(100 * tf / PEAK_BF16_TFLOPS, 2)}},
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.workload == "hstu_interleaved":
@@ -226,6 +369,9 @@ def main():
     from generative_ranking_recommendation_amd.slopes import alibi_slopes
 
     cfg = synth.make_config(args.workload)
+    if cfg.train:
+        bench_train(args, cfg)
+        return
     log(f"workload {cfg.name}: generating inputs")
     batch = synth.make_batch(cfg)
     tables = synth.make_tables(cfg)

@@ -318,7 +318,7 @@ genrank_status genrank_attn_bwd(const genrank_batch* b, const int32_t* offsets,
   if (b->dh > 64) return GENRANK_E_SHAPE;
   if (b->dtype == GENRANK_BF16) {  // 16-byte fragments of dout, 8-byte ones of dq, dk, dv
     if (ld_o % 8 || ld_dqkv % 4) return GENRANK_E_SHAPE;
-    if (reinterpret_cast<uintptr_t>(dout) % 16 ||
+    if (reinterpret_cast<uintptr_t>(dout) % 16 || reinterpret_cast<uintptr_t>(o) % 16 ||
         (reinterpret_cast<uintptr_t>(dq) | reinterpret_cast<uintptr_t>(dk) | reinterpret_cast<uintptr_t>(dv)) % 8)
       return GENRANK_E_ARG;
   }

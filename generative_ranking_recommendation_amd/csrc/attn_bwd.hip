@@ -86,6 +86,28 @@ __global__ void __launch_bounds__(64) delta_kernel(BwdArgs a) {
   if (lane == 0) a.delta[row * a.H + h] = v;
 }
 
+// bf16, dh = 64: D for 32 (row, head) pairs per 256-thread block, 8 lanes per pair, each
+// lane one 16-byte piece of O and of dO
+__global__ void __launch_bounds__(256) delta_bf16_kernel(BwdArgs a, int64_t pairs) {
+  const int64_t p = static_cast<int64_t>(blockIdx.x) * 32 + (threadIdx.x >> 3);
+  const int l8 = threadIdx.x & 7;
+  float v = 0.f;
+  if (p < pairs) {
+    const int64_t row = p / a.H;
+    const int h = static_cast<int>(p - row * a.H);
+    const int64_t off = row * a.ld_o + h * 64 + l8 * 8;
+    float fo[8], fd[8];
+    unpack8(*reinterpret_cast<const uint4*>(static_cast<const bf16_t*>(a.o) + off), fo);
+    unpack8(*reinterpret_cast<const uint4*>(static_cast<const bf16_t*>(a.dout) + off), fd);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v += fo[e] * fd[e];
+  }
+  v += __shfl_xor(v, 1);
+  v += __shfl_xor(v, 2);
+  v += __shfl_xor(v, 4);
+  if (p < pairs && l8 == 0) a.delta[p] = v;
+}
+
 template <typename T>
 __global__ void __launch_bounds__(64) dq_kernel(BwdArgs a) {
   const int64_t row = blockIdx.x;
@@ -662,7 +684,9 @@ genrank_status launch_attn_bwd(const genrank_batch* b, const int32_t* offsets, c
   a.T_h = b->total_hist;
   dim3 grid(static_cast<unsigned>(T), b->H);
   if (b->dtype == GENRANK_BF16) {  // dh == 64 and the alignments are checked by the caller
-    hipLaunchKernelGGL(delta_kernel<bf16_t>, grid, dim3(64), 0, stream, a);
+    const int64_t pairs = T * b->H;
+    hipLaunchKernelGGL(delta_bf16_kernel, dim3(static_cast<unsigned>((pairs + 31) / 32)), dim3(256), 0, stream, a,
+                       pairs);
     BwdMArgs m{};
     m.offsets = offsets; m.ts = ts; m.req = req;
     m.q = static_cast<const bf16_t*>(q); m.k = static_cast<const bf16_t*>(k); m.v = static_cast<const bf16_t*>(v);

@@ -582,8 +582,10 @@ __global__ void __launch_bounds__(256) seg_sum_kernel(SegArgs g) {
 }
 
 // One workgroup per chunk whose last run goes on: its partial plus the continuing chunks'
-// partials, in chunk order.
+// partials, in chunk order.  The run's last chunk is found first (the threads test 256
+// chunks at a time), then each column adds the partials with several loads in flight.
 __global__ void __launch_bounds__(256) seg_fix_kernel(SegArgs g) {
+  __shared__ int s_end;
   const int c = blockIdx.x;
   const int32_t* mt = g.meta + 4 * c;
   if (!(mt[0] & META_CARRY_OUT)) return;
@@ -591,14 +593,30 @@ __global__ void __launch_bounds__(256) seg_fix_kernel(SegArgs g) {
   const uint32_t key = static_cast<uint32_t>(mt[2]), slot = static_cast<uint32_t>(mt[3]);
   float* dst = seg_dest(g, table, key, slot);
   if (!dst) return;
+  // chunk j (> c) holds the run's last piece unless no run starts in it and chunk j + 1
+  // continues it
+  if (threadIdx.x == 0) s_end = g.nch - 1;
+  __syncthreads();
+  for (int base = c + 1; base < g.nch; base += 256) {
+    const int j = base + static_cast<int>(threadIdx.x);
+    const bool ends = j < g.nch && !((g.meta[4 * j] & META_NO_HEAD) && j + 1 < g.nch &&
+                                     (g.meta[4 * (j + 1)] & META_CONT_IN));
+    if (ends) atomicMin(&s_end, j);
+    __syncthreads();
+    if (s_end < base + 256) break;  // uniform: read after the barrier
+    __syncthreads();
+  }
+  const int j1 = s_end;
   const int64_t d = g.d;
   for (int col = threadIdx.x; col < g.d; col += 256) {
     float acc = g.carry_out[c * d + col];
-    for (int j = c + 1; j < g.nch; ++j) {
-      acc += g.carry_in[j * d + col];
-      const bool passes = (g.meta[4 * j] & META_NO_HEAD) != 0;
-      if (!passes || j + 1 >= g.nch || !(g.meta[4 * (j + 1)] & META_CONT_IN)) break;
+    int j = c + 1;
+    for (; j + 4 <= j1 + 1; j += 4) {
+      const float v0 = g.carry_in[j * d + col], v1 = g.carry_in[(j + 1) * d + col];
+      const float v2 = g.carry_in[(j + 2) * d + col], v3 = g.carry_in[(j + 3) * d + col];
+      acc = (((acc + v0) + v1) + v2) + v3;
     }
+    for (; j <= j1; ++j) acc += g.carry_in[j * d + col];
     dst[col] = acc;
   }
 }

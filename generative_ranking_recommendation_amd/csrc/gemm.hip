@@ -486,7 +486,17 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* P, int6
   const int m = static_cast<int>(e / n4), n = static_cast<int>(e - static_cast<int64_t>(m) * n4) * 4;
   const float* p = P + static_cast<int64_t>(m) * N + n;
   float4 a = *reinterpret_cast<const float4*>(p);
-  for (int s = 1; s < S; ++s) {
+  int s = 1;
+  for (; s + 4 <= S; s += 4) {  // four loads in flight, added in split order
+    float4 b[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) b[i] = *reinterpret_cast<const float4*>(p + (s + i) * split_stride);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      a.x += b[i].x; a.y += b[i].y; a.z += b[i].z; a.w += b[i].w;
+    }
+  }
+  for (; s < S; ++s) {
     const float4 b = *reinterpret_cast<const float4*>(p + s * split_stride);
     a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
   }

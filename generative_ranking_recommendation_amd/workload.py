@@ -47,3 +47,17 @@ def interleaved_tokens(n_c: int, m: int = 0) -> int:
 
 def action_oriented_tokens(n_c: int, m: int = 0) -> int:
     return n_c + m
+
+
+def attention_bwd_flops(lengths, m: int, d: int, recompute: bool = False) -> int:
+    """Backward over the allowed pairs: dV = P^T dO, dP = dO V^T, dQ = dS K, dK = dS^T Q
+    (2 d flops each per pair, twice the forward); with ``recompute`` also S = Q K^T again
+    (2.5 times the forward)."""
+    per_pair = 8 * d + (2 * d if recompute else 0)
+    return per_pair * attention_pairs(lengths, m)
+
+
+def attention_bwd_hbm_floor_bytes(rows: int, d: int, H: int, elem: int = 2) -> int:
+    """Read Q, K, V, O, dO and the log-sum-exp once, write dQ, dK, dV once, and write and
+    read the per-row D = rowsum(dO * O) once."""
+    return rows * d * elem * 8 + rows * H * 4 * 3

@@ -223,7 +223,7 @@ GENRANK_API genrank_status genrank_attn_fwd(const genrank_batch* batch, const in
  * only, [GR-zh] section 1.3.1, at the last block) and the history query rows are
  * skipped (their dq rows are written as zero).  bf16 (dh == 64): tiled MFMA kernels
  * that take P and dS as bf16 operands with f32 accumulation; ld_o must be a multiple of 8
- * and ld_dqkv of 4 (else GENRANK_E_SHAPE), dout 16-byte and dq, dk, dv 8-byte aligned
+ * and ld_dqkv of 4 (else GENRANK_E_SHAPE), o and dout 16-byte and dq, dk, dv 8-byte aligned
  * (else GENRANK_E_ARG).  f32: per-row kernels, f32 throughout.
  * ws: workspace of genrank_workspace_size(GENRANK_OP_ATTN_BWD) bytes. */
 GENRANK_API genrank_status genrank_attn_bwd(const genrank_batch* batch, const int32_t* hist_offsets,

@@ -54,3 +54,14 @@ def test_attention_pairs_match_the_mask():
 def test_gather_byte_counts():
     assert W.gather_logical_bytes(10, 256, 2, 0) == 10 * 256 * 2 * 6
     assert W.gather_compulsory_bytes(10, 256, 2, 3, 4, 100) == (10 + 3 + 4) * 256 * 2 + 100
+
+
+def test_attention_bwd_work_model():
+    """The backward's four products per allowed pair are twice the forward's two; with the
+    recomputed scores 2.5 times; the floor reads Q, K, V, O, dO once and writes dQ, dK, dV."""
+    from generative_ranking_recommendation_amd import workload as W
+    lengths, m, d = [3, 0, 7], 4, 64
+    fwd = W.attention_fwd_flops(lengths, m, d)
+    assert W.attention_bwd_flops(lengths, m, d) == 2 * fwd
+    assert W.attention_bwd_flops(lengths, m, d, recompute=True) * 2 == 5 * fwd
+    assert W.attention_bwd_hbm_floor_bytes(10, 64, 2) == 10 * 64 * 2 * 8 + 10 * 2 * 4 * 3
