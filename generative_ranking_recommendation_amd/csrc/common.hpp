@@ -99,10 +99,20 @@ __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "");
   __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
-// all waves past this point see every LDS write made before it; the empty asm keeps the
-// compiler from moving memory accesses across
+// Barrier for LDS filled by direct loads: each wave first waits (vmcnt) for its own loads,
+// then all waves meet; the empty asm keeps the compiler from moving memory accesses across.
+// It does not wait for the wave's own ds_write instructions: use lds_sync for those.
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+// lgkmcnt(0) with vmcnt and expcnt left alone: the wave's LDS reads and writes are done
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+// Barrier for ordinary LDS writes and reads (without the vmcnt wait __syncthreads implies)
+__device__ __forceinline__ void lds_sync() {
+  asm volatile("" ::: "memory");
+  wait_lgkm0();
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }

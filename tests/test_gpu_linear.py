@@ -30,6 +30,7 @@ def _bound(a64, w64, want, K):
 @pytest.mark.parametrize("M,N,K", [
     (1, 128, 128), (127, 256, 256), (129, 768, 256), (1000, 256, 512), (4099, 128, 2048),
     (300, 512, 96), (64, 128, 32),     # K not a multiple of 128: the register-staged kernel
+    (30011, 768, 256), (66000, 256, 512),  # many tiles, ragged M
 ])
 def test_linear_bf16_store(M, N, K):
     say(f"linear: bf16 M={M} N={N} K={K}")
