@@ -7,6 +7,7 @@ A step is one pass of the hot path over one batch already resident in HBM:
     embed-sum (fused index derivation + five-table gather)
     -> QKV projection -> masked ALiBi attention -> output projection      (single-layer form)
 or, for pre-norm workloads, embed-sum -> L x genrank_layer_fwd -> action head.
+With --kv-cache a step scores the candidates against cached history keys and values.
 With --workload train2_bf16 a step is one training step (forward, BCE at the candidates,
 backward, table gradients) and the roofline is the attention backward's.
 With --workload hstu_interleaved it instead measures the HSTU-style comparison on the same
@@ -48,6 +49,8 @@ def parse():
     p.add_argument("--workload", default="infer_1layer_bf16")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="CPU-oracle baseline budget (0 disables the leg)")
+    p.add_argument("--kv-cache", action="store_true",
+                   help="serving: score the candidates against the users' cached history keys/values")
     p.add_argument("--calibrate-copy-mb", type=int, default=0,
                    help="also run one plain device copy of this many MiB (counter calibration)")
     return p.parse_args()
@@ -346,6 +349,113 @@ def bench_train(args, cfg):
     print(json.dumps(out), flush=True)
 
 
+def bench_serve(args, cfg):
+    """Serving with cached history: the users' history keys and values are computed once
+    (prefill, timed and reported on its own); a step scores the request's candidates only:
+    embed the candidate rows -> QKV of those rows -> candidate attention against the cached
+    history K/V (plus each candidate's own key) -> output projection."""
+    import numpy as np
+    import torch
+
+    import synth
+    from generative_ranking_recommendation_amd import binding as B
+    from generative_ranking_recommendation_amd import workload as W
+    from generative_ranking_recommendation_amd.device import DeviceInputs
+    from generative_ranking_recommendation_amd.model import GenRank
+    from generative_ranking_recommendation_amd.slopes import alibi_slopes
+
+    if not (cfg.block == "attn_only" and cfg.layers == 1 and cfg.dtype == "bf16"):
+        print("--kv-cache measures the single-layer bf16 form", file=sys.stderr)
+        sys.exit(2)
+    log(f"workload {cfg.name} (cached history): generating inputs")
+    batch, tables, weights = synth.make_batch(cfg), synth.make_tables(cfg), synth.make_weights(cfg)
+    sp, st = alibi_slopes(cfg.H, cfg.time_ratio)
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    model = GenRank.from_host(cfg, tables, weights, sp, st, dev)
+    inp = DeviceInputs(batch, dev)
+    T_h, d, H, m = inp.total_hist, cfg.d, cfg.H, cfg.m
+    Tc = inp.B * m
+    bt = model.batch(inp)
+    lay = model.layers[0]
+    stream = torch.cuda.current_stream()
+    # prefill: the history keys and values
+    for _ in range(2):
+        caches = model.prefill(inp)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(5):
+        caches = model.prefill(inp)
+    torch.cuda.synchronize()
+    prefill_ms = (time.perf_counter() - t0) * 1e3 / 5
+    kv = caches[0]
+    xc = torch.empty((Tc, d), dtype=torch.bfloat16, device=dev)
+    qkv = torch.empty((Tc, 3 * d), dtype=torch.bfloat16, device=dev)
+    o = torch.empty((Tc, d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((Tc, H), dtype=torch.float32, device=dev)
+    y = torch.empty((Tc, d), dtype=torch.bfloat16, device=dev)
+    qp, kp = qkv.data_ptr(), kv.data_ptr()
+    names = ["embed_cand", "qkv_gemm", "attn_cached", "out_gemm"]
+
+    def step(ev):
+        ev[0].record(stream)
+        B.genrank_embed_sum_cand(bt, inp.struct, model.tables.struct, xc, stream)
+        ev[1].record(stream)
+        B.genrank_linear(B.BF16, xc, d, lay.wqkv, d, qkv, 3 * d, Tc, 3 * d, d, stream=stream)
+        ev[2].record(stream)
+        B.genrank_attn_fwd_cached(bt, inp.hist_offsets, inp.hist_ts, inp.req_ts, lay.slopes, qp, qp + 2 * d,
+                                  qp + 4 * d, 3 * d, kp, kp + 2 * d, 2 * d, o, d, lse, stream)
+        ev[3].record(stream)
+        B.genrank_linear(B.BF16, o, d, lay.wo, d, y, d, Tc, d, d, stream=stream)
+        ev[4].record(stream)
+    mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+    for _ in range(args.warmup):
+        step(mk())
+    torch.cuda.synchronize()
+    # the scored rows must equal the candidate rows of the full forward
+    y_full, _ = model.forward(inp)
+    torch.cuda.synchronize()
+    if not torch.equal(y_full[T_h:], y):
+        log("WARNING: cached scoring differs from the full forward")
+    events = [mk() for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(events[k])
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    per = {n: float(np.mean([events[k][i].elapsed_time(events[k][i + 1]) for k in range(args.steps)]))
+           for i, n in enumerate(names)}
+    log(f"{ms:.4f} ms/step; kernels (ms): " + ", ".join(f"{k}={v:.4f}" for k, v in per.items()))
+    lengths = inp.lengths
+    cand_pairs = int(m * (np.asarray(lengths, np.int64) + 1).sum())
+    flops = 4 * d * cand_pairs
+    nbytes = T_h * 2 * d * 2 + Tc * 3 * d * 2 + Tc * d * 2 + Tc * H * 4
+    t_us = per["attn_cached"] * 1e3
+    achieved = nbytes / (t_us * 1e-6) / 1e9
+    roofline = {"kernel": "attn_cached", "bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None}
+    kernels = {n: {"time_us": round(v * 1e3, 2)} for n, v in per.items()}
+    kernels["attn_cached"].update({"bound": "hbm", "achieved": round(achieved, 2), "floor_bytes": int(nbytes),
+                                   "flops": int(flops),
+                                   "tflops": round(flops / (t_us * 1e-6) / 1e12, 2)})
+    out = {
+        "metric": "candidates scored/sec with cached history K/V (GenRank fwd, bf16)",
+        "value": round(Tc / (ms * 1e-3), 1),
+        "unit": "candidates/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype,
+        "data": "synthetic (seeded; Zipf(1.1) item ids, jagged histories, runs of 1-4 actions per request)",
+        "config": {"workload": cfg.name, "mode": "cached history", "users": inp.B, "candidates_per_user": m,
+                   "history": f"U[{cfg.hist_min},{cfg.hist_max}]", "history_rows": T_h, "d": d, "heads": H},
+        "prefill_ms": round(prefill_ms, 4),
+        "roofline": roofline,
+        "cpu_baseline": None,
+        "kernels": kernels,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.workload == "hstu_interleaved":
@@ -371,6 +481,9 @@ def main():
     cfg = synth.make_config(args.workload)
     if cfg.train:
         bench_train(args, cfg)
+        return
+    if args.kv_cache:
+        bench_serve(args, cfg)
         return
     log(f"workload {cfg.name}: generating inputs")
     batch = synth.make_batch(cfg)

@@ -18,7 +18,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgenrank.
 
 F32, BF16 = 0, 1
 BLOCK_ATTN_ONLY, BLOCK_PRENORM = 0, 1
-OP_EMBED_SUM, OP_ATTN_FWD, OP_ATTN_BWD, OP_LAYER_FWD, OP_LAYER_BWD, OP_EMBED_BWD, OP_HEAD_BWD = range(7)
+(OP_EMBED_SUM, OP_ATTN_FWD, OP_ATTN_BWD, OP_LAYER_FWD, OP_LAYER_BWD, OP_EMBED_BWD, OP_HEAD_BWD, OP_LAYER_KV,
+ OP_LAYER_FWD_CACHED) = range(9)
 FWD_SAVE = 1
 EPI_NONE, EPI_RESIDUAL, EPI_SILU = 0, 1, 2
 STATUS = {0: "OK", -1: "E_ARG", -2: "E_SHAPE", -3: "E_DTYPE", -4: "E_UNSORTED",
@@ -89,6 +90,14 @@ _SIGS = {
     "genrank_linear_bwd": (c_int32, [c_int32, c_void_p, c_int64, c_void_p, c_int64, c_void_p, c_int64,
                                      c_void_p, c_int64, c_void_p, c_int64, c_int64, c_int32, c_int32,
                                      c_void_p, c_size_t, c_void_p]),
+    "genrank_embed_sum_cand": (c_int32, [POINTER(Batch), POINTER(Inputs), POINTER(Tables), c_void_p, c_void_p]),
+    "genrank_attn_fwd_cached": (c_int32, [POINTER(Batch), c_void_p, c_void_p, c_void_p, Alibi, c_void_p, c_void_p,
+                                          c_void_p, c_int64, c_void_p, c_void_p, c_int64, c_void_p, c_int64,
+                                          c_void_p, c_void_p]),
+    "genrank_layer_kv": (c_int32, [POINTER(Batch), POINTER(LayerWeights), c_void_p, c_void_p, c_int64, c_void_p,
+                                   c_size_t, c_void_p]),
+    "genrank_layer_fwd_cached": (c_int32, [POINTER(Batch), POINTER(LayerWeights), c_void_p, c_void_p, c_void_p,
+                                           c_void_p, c_int64, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
     "genrank_head_fwd": (c_int32, [POINTER(Batch), c_void_p, c_void_p, c_void_p, c_void_p, c_int32,
                                    c_void_p, c_void_p]),
     "genrank_head_bwd": (c_int32, [POINTER(Batch), c_void_p, c_void_p, c_void_p, c_int32, c_void_p,
@@ -284,6 +293,32 @@ def genrank_linear_bwd(dtype, x, ldx, w, ldw, dy, ldy, dx, lddx, dw, lddw, M, N,
     _check("genrank_linear_bwd", lib().genrank_linear_bwd(
         dtype, _p(x), ldx, _p(w), ldw, _p(dy), ldy, _p(dx), lddx, _p(dw), lddw, M, N, K, _p(ws),
         ws_bytes, _stream(stream)))
+
+
+def genrank_embed_sum_cand(batch, inputs, tables, x_cand, stream=None):
+    _check("genrank_embed_sum_cand", lib().genrank_embed_sum_cand(
+        ctypes.byref(batch), ctypes.byref(inputs), ctypes.byref(tables), _p(x_cand), _stream(stream)))
+
+
+def genrank_attn_fwd_cached(batch, hist_offsets, hist_ts, req_ts, slopes, q, k, v, ld_qkv, k_hist, v_hist,
+                            ld_hist, o, ld_o, lse=None, stream=None):
+    al = slopes.struct if isinstance(slopes, HostSlopes) else slopes
+    _check("genrank_attn_fwd_cached", lib().genrank_attn_fwd_cached(
+        ctypes.byref(batch), _p(hist_offsets), _p(hist_ts), _p(req_ts), al, _p(q), _p(k), _p(v), ld_qkv,
+        _p(k_hist), _p(v_hist), ld_hist, _p(o), ld_o, _p(lse), _stream(stream)))
+
+
+def genrank_layer_kv(batch, weights: LayerWeights, x_hist, kv, ld_kv, ws, ws_bytes, stream=None):
+    _check("genrank_layer_kv", lib().genrank_layer_kv(
+        ctypes.byref(batch), ctypes.byref(weights), _p(x_hist), _p(kv), ld_kv, _p(ws), ws_bytes,
+        _stream(stream)))
+
+
+def genrank_layer_fwd_cached(batch, weights: LayerWeights, hist_offsets, hist_ts, req_ts, kv_hist, ld_kv, x_cand,
+                             y_cand, ws, ws_bytes, stream=None):
+    _check("genrank_layer_fwd_cached", lib().genrank_layer_fwd_cached(
+        ctypes.byref(batch), ctypes.byref(weights), _p(hist_offsets), _p(hist_ts), _p(req_ts), _p(kv_hist), ld_kv,
+        _p(x_cand), _p(y_cand), _p(ws), ws_bytes, _stream(stream)))
 
 
 def genrank_head_fwd(batch, x, g_final, w_head, b_head, n_tasks, logits, stream=None):

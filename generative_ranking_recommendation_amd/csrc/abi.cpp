@@ -165,6 +165,38 @@ const char* genrank_status_string(int s) {
 
 int32_t genrank_version(void) { return (GENRANK_VERSION_MAJOR << 16) | GENRANK_VERSION_MINOR; }
 
+// ---------------------------------------------------------------- serving with cached history
+namespace genrank {
+namespace {
+// the candidate rows of a batch as a batch of their own (no history rows)
+genrank_batch cand_rows_batch(const genrank_batch* b) {
+  genrank_batch c = *b;
+  c.total_hist = 0;
+  c.max_hist = 0;
+  return c;
+}
+genrank_status check_cached_attn(const genrank_batch* b, const void* q, const void* k, const void* v,
+                                 int64_t ld_c, const void* kh, const void* vh, int64_t ld_h, const void* o,
+                                 int64_t ld_o) {
+  if (b->dtype != GENRANK_BF16) return GENRANK_E_DTYPE;
+  if (b->dh != 64) return GENRANK_E_SHAPE;
+  if (ld_c < b->d || ld_h < b->d || ld_o < b->d || ld_c % 8 || ld_h % 8 || ld_o % 4) return GENRANK_E_SHAPE;
+  if ((static_cast<int64_t>(b->max_hist) + 64) * ld_h * 2 >= (int64_t{1} << 31)) return GENRANK_E_SHAPE;
+  auto al = [](const void* p, uintptr_t n) { return reinterpret_cast<uintptr_t>(p) % n == 0; };
+  if (!al(q, 16) || !al(k, 16) || !al(v, 16) || !al(kh, 16) || !al(vh, 16) || !al(o, 8)) return GENRANK_E_ARG;
+  return GENRANK_OK;
+}
+size_t layer_kv_bytes(const genrank_batch* b, const genrank_layer_weights* w) {
+  return w->block == GENRANK_BLOCK_PRENORM ? align_up(static_cast<size_t>(b->total_hist) * b->d * dtype_size(b->dtype))
+                                           : 0;
+}
+size_t layer_fwd_cached_bytes(const genrank_batch* b, const genrank_layer_weights* w) {
+  const genrank_batch c = cand_rows_batch(b);
+  return layer_fwd_layout(&c, w->block, w->block == GENRANK_BLOCK_PRENORM ? w->ffn_dim : 0, nullptr).bytes;
+}
+}  // namespace
+}  // namespace genrank
+
 genrank_status genrank_workspace_size(int32_t op, const genrank_batch* b,
                                       const genrank_layer_weights* w, size_t* bytes) {
   if (!b || !bytes) return GENRANK_E_ARG;
@@ -182,6 +214,11 @@ genrank_status genrank_workspace_size(int32_t op, const genrank_batch* b,
       return GENRANK_OK;
     case GENRANK_OP_HEAD_BWD:
       *bytes = head_bwd_workspace(b->d, 4);
+      return GENRANK_OK;
+    case GENRANK_OP_LAYER_KV:
+    case GENRANK_OP_LAYER_FWD_CACHED:
+      if (!w) return GENRANK_E_ARG;
+      *bytes = op == GENRANK_OP_LAYER_KV ? layer_kv_bytes(b, w) : layer_fwd_cached_bytes(b, w);
       return GENRANK_OK;
     case GENRANK_OP_LAYER_FWD:
     case GENRANK_OP_LAYER_BWD: {
@@ -367,6 +404,88 @@ genrank_status genrank_layer_fwd(const genrank_batch* b, const genrank_layer_wei
                         (flags & GENRANK_FWD_SAVE) ? L.a : nullptr, ffn, s));
   return launch_gemm_nt(dt, L.hdn, ffn, w->w2, ffn, y_out, d, T, d, ffn, GEMM_EPI_RESID, L.x1, d,
                         nullptr, 0, s);
+}
+
+genrank_status genrank_embed_sum_cand(const genrank_batch* b, const genrank_inputs* in, const genrank_tables* t,
+                                      void* x_cand, genrank_stream_t stream) {
+  GR_TRY(check_embed_args(b, in, t));
+  if (!x_cand) return GENRANK_E_ARG;
+  return launch_embed_sum_cand(b, in, t, x_cand, S(stream));
+}
+
+genrank_status genrank_attn_fwd_cached(const genrank_batch* b, const int32_t* offsets, const int64_t* ts,
+                                       const int64_t* req, genrank_alibi alibi, const void* q, const void* k,
+                                       const void* v, int64_t ld_qkv, const void* k_hist, const void* v_hist,
+                                       int64_t ld_hist, void* o, int64_t ld_o, float* lse, genrank_stream_t stream) {
+  if (!b) return GENRANK_E_ARG;
+  GR_TRY(check_batch(b));
+  if (!offsets || !req || !alibi.slopes_pos || !alibi.slopes_time) return GENRANK_E_ARG;
+  if ((b->total_hist > 0 && (!ts || !k_hist || !v_hist)) || !q || !k || !v || !o) return GENRANK_E_ARG;
+  GR_TRY(check_cached_attn(b, q, k, v, ld_qkv, k_hist, v_hist, ld_hist, o, ld_o));
+  return launch_attn_fwd_cached(b, offsets, ts, req, alibi, q, k, v, ld_qkv, k_hist, v_hist, ld_hist, o, ld_o,
+                                lse, S(stream));
+}
+
+genrank_status genrank_layer_kv(const genrank_batch* b, const genrank_layer_weights* w, const void* x_hist,
+                                void* kv, int64_t ld_kv, void* ws, size_t ws_bytes, genrank_stream_t stream) {
+  GR_TRY(check_batch(b));
+  GR_TRY(check_layer_weights(b, w));
+  if (!x_hist || !kv) return GENRANK_E_ARG;
+  if (ld_kv < 2 * b->d) return GENRANK_E_SHAPE;
+  if (ws_bytes < layer_kv_bytes(b, w) || (layer_kv_bytes(b, w) > 0 && !ws)) return GENRANK_E_WORKSPACE;
+  const int64_t Th = b->total_hist;
+  if (Th == 0) return GENRANK_OK;
+  const hipStream_t s = S(stream);
+  const int dt = b->dtype;
+  const int d = b->d;
+  const void* z = x_hist;
+  if (w->block == GENRANK_BLOCK_PRENORM) {
+    GR_TRY(launch_rmsnorm(dt, x_hist, w->g1, ws, Th, d, s));
+    z = ws;
+  }
+  // rows [d, 3d) of wqkv: the key and value projections
+  const char* wkv = static_cast<const char*>(w->wqkv) + static_cast<size_t>(d) * d * dtype_size(dt);
+  return launch_gemm_nt(dt, z, d, wkv, d, kv, ld_kv, static_cast<int>(Th), 2 * d, d, GEMM_EPI_STORE, nullptr, 0,
+                        nullptr, 0, s);
+}
+
+genrank_status genrank_layer_fwd_cached(const genrank_batch* b, const genrank_layer_weights* w,
+                                        const int32_t* offsets, const int64_t* ts, const int64_t* req,
+                                        const void* kv_hist, int64_t ld_kv, const void* x_cand, void* y_cand,
+                                        void* ws, size_t ws_bytes, genrank_stream_t stream) {
+  GR_TRY(check_batch(b));
+  GR_TRY(check_layer_weights(b, w));
+  if (!x_cand || !y_cand || !offsets || !req || (b->total_hist > 0 && (!ts || !kv_hist))) return GENRANK_E_ARG;
+  const bool pre = w->block == GENRANK_BLOCK_PRENORM;
+  if (!pre && x_cand == y_cand) return GENRANK_E_ARG;
+  const genrank_batch c = cand_rows_batch(b);
+  const int ffn = pre ? w->ffn_dim : 0;
+  const LayerFwdWs L = layer_fwd_layout(&c, w->block, ffn, static_cast<char*>(ws));
+  if (!ws || ws_bytes < L.bytes) return GENRANK_E_WORKSPACE;
+  const int dt = b->dtype;
+  const int d = b->d;
+  const size_t es = dtype_size(dt);
+  const int Tc = static_cast<int>(static_cast<int64_t>(b->B) * b->m);
+  const char* kh = static_cast<const char*>(kv_hist);
+  GR_TRY(check_cached_attn(b, L.qkv, L.qkv + d * es, L.qkv + 2 * d * es, 3 * d, kh ? kh : L.qkv,
+                           kh ? kh + d * es : L.qkv, ld_kv, L.o, d));
+  if (Tc == 0) return GENRANK_OK;
+  const hipStream_t s = S(stream);
+  const void* zin = x_cand;
+  if (pre) {
+    GR_TRY(launch_rmsnorm(dt, x_cand, w->g1, L.z, Tc, d, s));
+    zin = L.z;
+  }
+  GR_TRY(launch_gemm_nt(dt, zin, d, w->wqkv, d, L.qkv, 3 * d, Tc, 3 * d, d, GEMM_EPI_STORE, nullptr, 0, nullptr,
+                        0, s));
+  GR_TRY(launch_attn_fwd_cached(b, offsets, ts, req, w->alibi, L.qkv, L.qkv + d * es, L.qkv + 2 * d * es, 3 * d,
+                                kh ? kh : L.qkv, kh ? kh + d * es : L.qkv, ld_kv, L.o, d, L.lse, s));
+  if (!pre)
+    return launch_gemm_nt(dt, L.o, d, w->wo, d, y_cand, d, Tc, d, d, GEMM_EPI_STORE, nullptr, 0, nullptr, 0, s);
+  GR_TRY(launch_gemm_nt(dt, L.o, d, w->wo, d, L.x1, d, Tc, d, d, GEMM_EPI_RESID, x_cand, d, nullptr, 0, s));
+  GR_TRY(launch_rmsnorm(dt, L.x1, w->g2, L.z2, Tc, d, s));
+  GR_TRY(launch_gemm_nt(dt, L.z2, d, w->w1, d, L.hdn, ffn, Tc, ffn, d, GEMM_EPI_SILU, nullptr, 0, nullptr, ffn, s));
+  return launch_gemm_nt(dt, L.hdn, ffn, w->w2, ffn, y_cand, d, Tc, d, ffn, GEMM_EPI_RESID, L.x1, d, nullptr, 0, s);
 }
 
 genrank_status genrank_layer_bwd(const genrank_batch* b, const genrank_layer_weights* w,

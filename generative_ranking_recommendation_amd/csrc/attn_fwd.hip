@@ -68,6 +68,12 @@ struct AttnArgs {
   int64_t T_h;
   const bf16_t* rab;       // learned-bias variant: per-user [L, P] bf16 matrices
   const int64_t* rab_off;  // element offset of user u's matrix, [B + 1]
+  // history keys and values: rows [off_u, off_u + N_u) of kh / vh (row stride ld_h); the
+  // q / k / v rows above in the batch layout, or a cache of earlier requests' history
+  const bf16_t* kh;
+  const bf16_t* vh;
+  int64_t ld_h;
+  int64_t crow0;           // row of candidate (u, 0) in q / k / v / o / lse: T_h, or 0
 };
 
 // slot of key j (0..63 in a tile) in the permuted key axis of sVt
@@ -134,7 +140,7 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
     q0 = y * AQ;
     if (q0 >= a.m) return;
     nq = min(AQ, a.m - q0);
-    qrow0 = a.T_h + static_cast<int64_t>(u) * a.m + q0;
+    qrow0 = a.crow0 + static_cast<int64_t>(u) * a.m + q0;
     n_tiles = (N + AK - 1) / AK;
   } else {
     is_cand = false;
@@ -229,10 +235,10 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
   const int kA = 2 * pr;
   const int krow = st >> 3;
   const int kcol = (st & 7) * 8;
-  const uint32_t row_bytes = static_cast<uint32_t>(a.ld_qkv) * 2u;
+  const uint32_t row_bytes = static_cast<uint32_t>(a.ld_h) * 2u;
   const uint32_t hist_bytes = static_cast<uint32_t>(N) * row_bytes;
   const __amdgpu_buffer_rsrc_t rsKV = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<bf16_t*>((stage_k ? a.k : a.v) + off * a.ld_qkv), static_cast<short>(0), hist_bytes,
+      const_cast<bf16_t*>((stage_k ? a.kh : a.vh) + off * a.ld_h), static_cast<short>(0), hist_bytes,
       BUF_DWORD3);
   const uint32_t vo0 = stage_k ? static_cast<uint32_t>(krow) * row_bytes + (h * DH + kcol) * 2u
                                : static_cast<uint32_t>(kA) * row_bytes + (h * DH + ch * 8) * 2u;
@@ -669,6 +675,7 @@ genrank_status launch_hstu_attn_fwd(const genrank_batch* b, const int32_t* offse
   a.hist_tiles = static_cast<int>((2 * static_cast<int64_t>(b->max_hist) + AQ - 1) / AQ);
   a.cand_tiles = (b->m + AQ - 1) / AQ;
   a.T_h = 2 * b->total_hist;
+  a.kh = a.k; a.vh = a.v; a.ld_h = ld_qkv; a.crow0 = a.T_h;
   a.rab = static_cast<const bf16_t*>(rab);
   a.rab_off = rab_off;
   if (a.hist_tiles + a.cand_tiles == 0) return GENRANK_OK;
@@ -705,6 +712,7 @@ genrank_status launch_attn_fwd(const genrank_batch* b, const int32_t* offsets, c
     a.hist_tiles = (b->max_hist + AQ - 1) / AQ;
     a.cand_tiles = (b->m + AQ - 1) / AQ;
     a.T_h = b->total_hist;
+    a.kh = a.k; a.vh = a.v; a.ld_h = ld_qkv; a.crow0 = a.T_h;
     if (a.hist_tiles + a.cand_tiles == 0) return GENRANK_OK;
     const int64_t pairs = (static_cast<int64_t>(b->B) * b->H + 8 * GROUP - 1) / (8 * GROUP) * (8 * GROUP);
     const int64_t G = pairs * (a.hist_tiles + a.cand_tiles);
@@ -730,6 +738,39 @@ genrank_status launch_attn_fwd(const genrank_batch* b, const int32_t* offsets, c
     hipLaunchKernelGGL(attn_fwd_f32_kernel, dim3(static_cast<unsigned>(T), b->H), dim3(64), 0,
                        stream, a);
   }
+  GR_CHECK_LAUNCH();
+  return GENRANK_OK;
+}
+
+genrank_status launch_attn_fwd_cached(const genrank_batch* b, const int32_t* offsets, const int64_t* ts,
+                                      const int64_t* req, genrank_alibi alibi, const void* q, const void* k,
+                                      const void* v, int64_t ld_c, const void* kh, const void* vh, int64_t ld_h,
+                                      void* o, int64_t ld_o, float* lse, hipStream_t stream) {
+  if (b->m == 0) return GENRANK_OK;
+  AttnArgs a{};
+  a.offsets = offsets; a.ts = ts; a.req = req;
+  a.q = static_cast<const bf16_t*>(q);
+  a.k = static_cast<const bf16_t*>(k);
+  a.v = static_cast<const bf16_t*>(v);
+  a.ld_qkv = ld_c;
+  a.o = static_cast<bf16_t*>(o);
+  a.ld_o = ld_o;
+  a.lse = lse;
+  for (int h = 0; h < b->H; ++h) {
+    a.sp2[h] = alibi.slopes_pos[h] * LOG2E;
+    a.st2[h] = alibi.slopes_time[h] * LOG2E;
+  }
+  a.scale2 = LOG2E / sqrtf(static_cast<float>(b->dh));
+  a.B = b->B; a.m = b->m; a.H = b->H;
+  a.hist_tiles = 0;  // candidate tiles only: history queries were answered earlier
+  a.cand_tiles = (b->m + AQ - 1) / AQ;
+  a.T_h = b->total_hist;
+  a.kh = static_cast<const bf16_t*>(kh); a.vh = static_cast<const bf16_t*>(vh); a.ld_h = ld_h;
+  a.crow0 = 0;
+  const int64_t pairs = (static_cast<int64_t>(b->B) * b->H + 8 * GROUP - 1) / (8 * GROUP) * (8 * GROUP);
+  const int64_t G = pairs * a.cand_tiles;
+  if (G > INT32_MAX) return GENRANK_E_SHAPE;
+  hipLaunchKernelGGL(attn_fwd_bf16_kernel<false>, dim3(static_cast<unsigned>(G)), dim3(NT), 0, stream, a);
   GR_CHECK_LAUNCH();
   return GENRANK_OK;
 }

@@ -704,6 +704,31 @@ genrank_status launch_embed_sum(const genrank_batch* b, const genrank_inputs* in
   return GENRANK_OK;
 }
 
+genrank_status launch_embed_sum_cand(const genrank_batch* b, const genrank_inputs* in, const genrank_tables* t,
+                                     void* out, hipStream_t stream) {
+  // candidate chunks only (no history chunk in the grid), rows written from 0
+  EmbedArgs a = make_args(b, in, t);
+  a.hist_chunks = 0;
+  a.T_h = 0;
+  a.out = out;
+  if (a.cand_chunks == 0) return GENRANK_OK;
+  const int es = b->dtype == GENRANK_BF16 ? 2 : 4;
+  const int cpr = b->d * es / 16;
+  const int64_t rb = static_cast<int64_t>(b->d) * es;
+  const bool rows_ok = b->d * es % 16 == 0 && cpr <= EMB_THREADS && EMB_THREADS % cpr == 0 &&
+                       t->n_item * rb < 0xFFFFFFFFll && EMB_ROWS * rb < 0xFFFFFFFFll;
+  if (rows_ok && b->dtype == GENRANK_BF16)
+    hipLaunchKernelGGL(embed_sum_rows_kernel<bf16_t>, grid_of(a), dim3(EMB_THREADS), 0, stream, a);
+  else if (rows_ok)
+    hipLaunchKernelGGL(embed_sum_rows_kernel<float>, grid_of(a), dim3(EMB_THREADS), 0, stream, a);
+  else if (b->dtype == GENRANK_BF16)
+    hipLaunchKernelGGL(embed_sum_kernel<bf16_t>, grid_of(a), dim3(EMB_THREADS), 0, stream, a);
+  else
+    hipLaunchKernelGGL(embed_sum_kernel<float>, grid_of(a), dim3(EMB_THREADS), 0, stream, a);
+  GR_CHECK_LAUNCH();
+  return GENRANK_OK;
+}
+
 genrank_status launch_debug_indices(const genrank_batch* b, const genrank_inputs* in,
                                     const genrank_tables* t, int32_t* out, hipStream_t stream) {
   EmbedArgs a = make_args(b, in, t);

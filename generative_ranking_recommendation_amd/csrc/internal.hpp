@@ -24,6 +24,15 @@ genrank_status launch_embed_sum(const genrank_batch* b, const genrank_inputs* in
                                 const genrank_tables* t, void* out, hipStream_t stream);
 genrank_status launch_debug_indices(const genrank_batch* b, const genrank_inputs* in,
                                     const genrank_tables* t, int32_t* out, hipStream_t stream);
+// candidate rows only: [B*m, d] written from row 0
+genrank_status launch_embed_sum_cand(const genrank_batch* b, const genrank_inputs* in, const genrank_tables* t,
+                                     void* out, hipStream_t stream);
+// candidate queries ([B*m] rows of q / k / v / o / lse) against history keys and values
+// held elsewhere (rows [off_u, off_u + N_u) of kh / vh); bf16, dh = 64
+genrank_status launch_attn_fwd_cached(const genrank_batch* b, const int32_t* offsets, const int64_t* ts,
+                                      const int64_t* req, genrank_alibi alibi, const void* q, const void* k,
+                                      const void* v, int64_t ld_c, const void* kh, const void* vh, int64_t ld_h,
+                                      void* o, int64_t ld_o, float* lse, hipStream_t stream);
 size_t embed_bwd_workspace(const genrank_batch* b);
 genrank_status launch_embed_bwd(const genrank_batch* b, const genrank_inputs* in, const genrank_tables* t,
                                 const void* dx, int32_t* item_ids, float* item_rows, int32_t* n_items,

@@ -90,6 +90,53 @@ class GenRank:
                                self.head.b_head, self.head.n_tasks, logits, stream)
         return x, logits
 
+    # ---------------------------------------------------------------- serving with cached history
+    def prefill(self, inp, stream=None):
+        """Per-block history keys and values of the batch's users, each [T_h, 2d] (keys in
+        columns [0, d), values in [d, 2d)).  History rows never depend on candidates, so this
+        is a forward over the history rows alone; the top block stops at its key/value
+        projection (its history outputs are never read)."""
+        T_h = inp.total_hist
+        d = self.d
+        bh = B.make_batch(inp.B, 0, d, self.H, inp.max_hist, T_h, self.code)
+        x = self.act(T_h)
+        B.genrank_embed_sum(bh, inp.struct, self.tables.struct, x, stream)
+        caches = []
+        for i, lay in enumerate(self.layers):
+            kv = self.act(T_h, 2 * d)
+            nb = B.genrank_workspace_size(B.OP_LAYER_KV, bh, lay.struct)
+            B.genrank_layer_kv(bh, lay.struct, x, kv, 2 * d, self._buf(("kv", i), nb), nb, stream)
+            caches.append(kv)
+            if i + 1 < len(self.layers):
+                y = self.act(T_h)
+                nf = B.genrank_workspace_size(B.OP_LAYER_FWD, bh, lay.struct)
+                B.genrank_layer_fwd(bh, lay.struct, inp.hist_offsets, inp.hist_ts, inp.req_ts, x, y, 0,
+                                    self._buf(("prefill", i), nf), nf, stream)
+                x = y
+        return caches
+
+    def score(self, inp, caches, stream=None):
+        """The candidate rows of ``forward`` from cached history keys and values: returns
+        (x [B*m, d] after the last block, logits [B*m, n_tasks] or None)."""
+        bt = self.batch(inp)
+        Tc = inp.B * inp.m
+        d = self.d
+        x = self.act(Tc)
+        B.genrank_embed_sum_cand(bt, inp.struct, self.tables.struct, x, stream)
+        for i, lay in enumerate(self.layers):
+            y = self.act(Tc) if lay.block == B.BLOCK_ATTN_ONLY else x
+            nb = B.genrank_workspace_size(B.OP_LAYER_FWD_CACHED, bt, lay.struct)
+            B.genrank_layer_fwd_cached(bt, lay.struct, inp.hist_offsets, inp.hist_ts, inp.req_ts, caches[i],
+                                       2 * d, x, y, self._buf(("cached", i), nb), nb, stream)
+            x = y
+        logits = None
+        if self.head is not None:
+            bc = B.make_batch(inp.B, inp.m, d, self.H, 0, 0, self.code)  # candidate rows only
+            logits = torch.empty((Tc, self.head.n_tasks), dtype=torch.float32, device=self.device)
+            B.genrank_head_fwd(bc, x, self.head.g_final, self.head.w_head, self.head.b_head, self.head.n_tasks,
+                               logits, stream)
+        return x, logits
+
     # ---------------------------------------------------------------- training
     def train_step(self, inp, labels, stream=None):
         """Forward with saved activations, BCE at candidates, full backward.  Returns

@@ -79,7 +79,9 @@ typedef enum {
   GENRANK_OP_LAYER_FWD = 3,
   GENRANK_OP_LAYER_BWD = 4,
   GENRANK_OP_EMBED_BWD = 5,
-  GENRANK_OP_HEAD_BWD = 6
+  GENRANK_OP_HEAD_BWD = 6,
+  GENRANK_OP_LAYER_KV = 7,
+  GENRANK_OP_LAYER_FWD_CACHED = 8
 } genrank_op;
 
 /* Batch geometry.  total_hist and max_hist are host copies of hist_offsets[B] and
@@ -337,6 +339,49 @@ GENRANK_API genrank_status genrank_embed_bwd(const genrank_batch* batch, const g
                                              int32_t* item_ids, float* item_rows, int32_t* n_items,
                                              float* d_action, float* d_pos, float* d_ri, float* d_rt,
                                              void* ws, size_t ws_bytes, genrank_stream_t stream);
+
+/* ------------------------------------------------------------------ serving with cached history
+ *
+ * History rows never depend on candidates (history queries only see earlier history keys,
+ * [GR-zh] 1.4.2 mask; [FR-en] 7.2.1), so a user's per-block history keys and values can be
+ * computed once and reused for every later request: a request then runs its m candidate
+ * rows only, each candidate attending to the cached history and to itself.  The results
+ * equal the candidate rows of the full forward (bit for bit on this library's kernels).
+ * Layout of a cache for one block: kv [T_h, ld_kv] with the keys in columns [0, d) and the
+ * values in [d, 2d), head h at h * dh in each; rows in the batch's history order.
+ * bf16 with dh == 64 for the attention. */
+
+/* genrank_embed_sum for the candidate rows only: x_cand [B*m, d], row u*m + k. */
+GENRANK_API genrank_status genrank_embed_sum_cand(const genrank_batch* batch, const genrank_inputs* in,
+                                                  const genrank_tables* tables, void* x_cand,
+                                                  genrank_stream_t stream);
+
+/* The attention of genrank_attn_fwd for the candidate rows only: q, k, v, o: [B*m] rows
+ * (row stride ld_qkv, ld_o; lse [B*m, H] or NULL); the history keys and values come from
+ * k_hist, v_hist ([T_h] rows, stride ld_hist).  ld_qkv, ld_hist multiples of 8, ld_o of 4;
+ * q, k, v, k_hist, v_hist 16-byte and o 8-byte aligned (else GENRANK_E_SHAPE / E_ARG). */
+GENRANK_API genrank_status genrank_attn_fwd_cached(const genrank_batch* batch, const int32_t* hist_offsets,
+                                                   const int64_t* hist_ts, const int64_t* req_ts,
+                                                   genrank_alibi alibi, const void* q, const void* k,
+                                                   const void* v, int64_t ld_qkv, const void* k_hist,
+                                                   const void* v_hist, int64_t ld_hist, void* o, int64_t ld_o,
+                                                   float* lse, genrank_stream_t stream);
+
+/* A block's history keys and values: kv [T_h, ld_kv] (see above) from the block's input on
+ * the history rows, x_hist [T_h, d] (the top block needs nothing else of the history: its
+ * history outputs are never read).  ws: genrank_workspace_size(GENRANK_OP_LAYER_KV). */
+GENRANK_API genrank_status genrank_layer_kv(const genrank_batch* batch, const genrank_layer_weights* w,
+                                            const void* x_hist, void* kv, int64_t ld_kv, void* ws,
+                                            size_t ws_bytes, genrank_stream_t stream);
+
+/* genrank_layer_fwd on the candidate rows only: x_cand, y_cand [B*m, d] (equal only for
+ * GENRANK_BLOCK_PRENORM), history keys and values from kv_hist ([T_h, ld_kv]).
+ * ws: genrank_workspace_size(GENRANK_OP_LAYER_FWD_CACHED). */
+GENRANK_API genrank_status genrank_layer_fwd_cached(const genrank_batch* batch, const genrank_layer_weights* w,
+                                                    const int32_t* hist_offsets, const int64_t* hist_ts,
+                                                    const int64_t* req_ts, const void* kv_hist, int64_t ld_kv,
+                                                    const void* x_cand, void* y_cand, void* ws, size_t ws_bytes,
+                                                    genrank_stream_t stream);
 
 /* ------------------------------------------------------------------ debug exports */
 

@@ -108,6 +108,15 @@ def test_entry_points_reject_bad_arguments(lib):
                                 FAKE, FAKE, 256, FAKE, FAKE, FAKE, FAKE, 770, 0, FAKE, 1 << 40, None) == -2
     assert lib.genrank_attn_bwd(ctypes.byref(bt), FAKE, FAKE, FAKE, sl.struct, FAKE, FAKE, FAKE, 768,
                                 FAKE, FAKE, 256, FAKE, FAKE + 2, FAKE, FAKE, 768, 0, FAKE, 1 << 40, None) == -1
+    # cached-history attention: bf16 only; history stride must hold 2 x 16-byte aligned rows
+    b32f = _batch(dtype=B.F32)
+    assert lib.genrank_attn_fwd_cached(ctypes.byref(b32f), FAKE, FAKE, FAKE, sl.struct, FAKE, FAKE, FAKE, 768,
+                                       FAKE, FAKE, 512, FAKE, 256, None, None) == -3
+    assert lib.genrank_attn_fwd_cached(ctypes.byref(bt), FAKE, FAKE, FAKE, sl.struct, FAKE, FAKE, FAKE, 768,
+                                       FAKE, FAKE, 100, FAKE, 256, None, None) == -2
+    # layer key/value projection: the kv stride must hold keys and values
+    wk = B.make_layer_weights(FAKE, FAKE, sl, B.BLOCK_ATTN_ONLY)
+    assert lib.genrank_layer_kv(ctypes.byref(bt), ctypes.byref(wk), FAKE, FAKE, 300, FAKE, 1 << 30, None) == -2
     # layer: workspace too small, missing FFN weights, bad ffn size
     w = B.make_layer_weights(FAKE, FAKE, sl, B.BLOCK_ATTN_ONLY)
     assert lib.genrank_layer_fwd(ctypes.byref(bt), ctypes.byref(w), FAKE, FAKE, FAKE, FAKE, FAKE + 64,
