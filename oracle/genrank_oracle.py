@@ -37,6 +37,7 @@ __all__ = [
     "token_indices",
     "embed_sum",
     "attention_mask",
+    "time_bucket",
     "attn_fwd_user",
     "attn_fwd",
     "attn_bwd_user",
@@ -204,51 +205,67 @@ def embed_bwd(dx, table_shapes, hist_items, cand_items, idx):
 # ----------------------------------------------------------------------------------------
 
 
-def attention_mask(N: int, m: int) -> np.ndarray:
+def attention_mask(N: int, m: int, history: str = "causal") -> np.ndarray:
     """allowed[i, j] for one user's sequence of N history actions then m candidates.
 
     History queries see history keys at or before them (causal mask); a candidate sees
     every history key and itself, never another candidate ([FR-en] section 7.2.1, the
     candidate mask; [GR-note], the worked example of one history item and two
     candidates; reading: the candidate's own key is visible, as when it is appended
-    alone)."""
+    alone).  ``history="full"``: the variant in which every history query sees every
+    history key ([GR-zh] section 1.3.1, the fully visible mask over the historical
+    positions, as in T5); candidates are unchanged."""
     L = N + m
     allowed = np.zeros((L, L), dtype=bool)
     for i in range(L):
         if i < N:
-            allowed[i, : i + 1] = True
+            allowed[i, : (N if history == "full" else i + 1)] = True
         else:
             allowed[i, :N] = True
             allowed[i, i] = True
     return allowed
 
 
-def _alibi_bias(pos, tau, sp, st):
+def time_bucket(gap, bounds):
+    """#{k : bounds[k] <= gap} for non-negative integer gaps (the request-gap bucketing of
+    the time embedding, [GR-zh] section 1.4.2), element-wise."""
+    b = np.asarray(bounds, np.int64)
+    g = np.asarray(gap, np.int64)
+    return (b[None, :] <= g.reshape(-1)[:, None]).sum(axis=1).reshape(g.shape)
+
+
+def _alibi_bias(pos, tau, sp, st, time_bounds=None):
     """-s_h |p_i - p_j| - s'_h |tau_i - tau_j| for one head ([GR-zh] section 1.4.2, the
     ALiBi score with position ids; time term as in [FR-en] section 7.2.2 with raw
-    seconds instead of a bucket)."""
+    seconds).  With ``time_bounds`` the time term is -s'_h bucket(|tau_i - tau_j|): the
+    page's -m_t bucket(t_i - t_j), reading: its bucket is the request-gap bucketing, on the
+    absolute difference (for causal pairs t_i >= t_j, so the same as the page's)."""
     pos = np.asarray(pos, np.float64)
     tau = np.asarray(tau, np.float64)
-    return -sp * np.abs(pos[:, None] - pos[None, :]) - st * np.abs(tau[:, None] - tau[None, :])
+    dt = np.abs(tau[:, None] - tau[None, :])
+    if time_bounds is not None:
+        dt = time_bucket(np.rint(dt).astype(np.int64), time_bounds).astype(np.float64)
+    return -sp * np.abs(pos[:, None] - pos[None, :]) - st * dt
 
 
-def attn_fwd_user(q, k, v, pos, tau, slopes_pos, slopes_time, N, m):
+def attn_fwd_user(q, k, v, pos, tau, slopes_pos, slopes_time, N, m, history="causal", time_bounds=None):
     """One user's attention.  q, k, v: [L, H, dh] with L = N + m.
 
     score_ij = q_i . k_j / sqrt(dh) - s_h |p_i - p_j| - s'_h |tau_i - tau_j| on allowed
     pairs ([GR-zh] section 1.4.2, ALiBi score, d = head dimension); softmax over allowed
     keys; O = P V.  Returns (O [L, H, dh], lse [L, H]) with lse = log sum_j exp(score_ij).
+    ``history`` and ``time_bounds``: the variants of ``attention_mask`` and ``_alibi_bias``.
     """
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
     L, H, dh = q.shape
-    allowed = attention_mask(N, m)
+    allowed = attention_mask(N, m, history)
     o = np.zeros_like(q)
     lse = np.zeros((L, H))
     for h in range(H):
         s = q[:, h, :] @ k[:, h, :].T / math.sqrt(dh)
-        s = s + _alibi_bias(pos, tau, slopes_pos[h], slopes_time[h])
+        s = s + _alibi_bias(pos, tau, slopes_pos[h], slopes_time[h], time_bounds)
         s = np.where(allowed, s, -np.inf)
         mx = s.max(axis=1, keepdims=True)
         e = np.where(allowed, np.exp(s - mx), 0.0)
@@ -259,7 +276,8 @@ def attn_fwd_user(q, k, v, pos, tau, slopes_pos, slopes_time, N, m):
     return o, lse
 
 
-def attn_fwd(q, k, v, hist_offsets, m, pos, tau, slopes_pos, slopes_time, users=None):
+def attn_fwd(q, k, v, hist_offsets, m, pos, tau, slopes_pos, slopes_time, users=None, history="causal",
+             time_bounds=None):
     """Batch attention over jagged users; q/k/v [T, H, dh] in the shared row layout."""
     q = np.asarray(q, np.float64)
     B = len(hist_offsets) - 1
@@ -269,13 +287,13 @@ def attn_fwd(q, k, v, hist_offsets, m, pos, tau, slopes_pos, slopes_time, users=
         rows = user_rows(hist_offsets, m, u)
         N = int(hist_offsets[u + 1] - hist_offsets[u])
         ou, lu = attn_fwd_user(q[rows], np.asarray(k)[rows], np.asarray(v)[rows], pos[rows],
-                               tau[rows], slopes_pos, slopes_time, N, m)
+                               tau[rows], slopes_pos, slopes_time, N, m, history, time_bounds)
         o[rows] = ou
         lse[rows] = lu
     return o, lse
 
 
-def attn_bwd_user(q, k, v, do, pos, tau, slopes_pos, slopes_time, N, m):
+def attn_bwd_user(q, k, v, do, pos, tau, slopes_pos, slopes_time, N, m, history="causal", time_bounds=None):
     """Gradients of one user's attention (the biases are constants: ALiBi has no
     parameters and needs no gradient, [GR-zh] section 1.4.2).
 
@@ -286,11 +304,11 @@ def attn_bwd_user(q, k, v, do, pos, tau, slopes_pos, slopes_time, N, m):
     v = np.asarray(v, np.float64)
     do = np.asarray(do, np.float64)
     L, H, dh = q.shape
-    allowed = attention_mask(N, m)
+    allowed = attention_mask(N, m, history)
     dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
     for h in range(H):
         s = q[:, h, :] @ k[:, h, :].T / math.sqrt(dh)
-        s = s + _alibi_bias(pos, tau, slopes_pos[h], slopes_time[h])
+        s = s + _alibi_bias(pos, tau, slopes_pos[h], slopes_time[h], time_bounds)
         s = np.where(allowed, s, -np.inf)
         e = np.where(allowed, np.exp(s - s.max(axis=1, keepdims=True)), 0.0)
         p = e / e.sum(axis=1, keepdims=True)
@@ -302,7 +320,8 @@ def attn_bwd_user(q, k, v, do, pos, tau, slopes_pos, slopes_time, N, m):
     return dq, dk, dv
 
 
-def attn_bwd(q, k, v, do, hist_offsets, m, pos, tau, slopes_pos, slopes_time, users=None):
+def attn_bwd(q, k, v, do, hist_offsets, m, pos, tau, slopes_pos, slopes_time, users=None, history="causal",
+             time_bounds=None):
     q = np.asarray(q, np.float64)
     B = len(hist_offsets) - 1
     dq, dk, dv = np.zeros_like(q), np.zeros_like(q), np.zeros_like(q)
@@ -311,7 +330,7 @@ def attn_bwd(q, k, v, do, hist_offsets, m, pos, tau, slopes_pos, slopes_time, us
         N = int(hist_offsets[u + 1] - hist_offsets[u])
         a, b, c = attn_bwd_user(q[rows], np.asarray(k)[rows], np.asarray(v)[rows],
                                 np.asarray(do)[rows], pos[rows], tau[rows], slopes_pos,
-                                slopes_time, N, m)
+                                slopes_time, N, m, history, time_bounds)
         dq[rows], dk[rows], dv[rows] = a, b, c
     return dq, dk, dv
 
@@ -393,7 +412,8 @@ def layer_fwd(x, lw, block, H, geom, store=None):
     qkv = S(z @ wqkv.T)
     q, k, v = (_split_heads(qkv[:, i * d:(i + 1) * d], H) for i in range(3))
     o, _ = attn_fwd(q, k, v, geom["hist_offsets"], geom["m"], geom["pos"], geom["tau"],
-                    geom["slopes_pos"], geom["slopes_time"])
+                    geom["slopes_pos"], geom["slopes_time"], history=geom.get("history", "causal"),
+                    time_bounds=geom.get("time_bounds"))
     o2 = S(o.reshape(o.shape[0], d))
     attn_out = o2 @ wo.T
     cache.update(z=z, q=q, k=k, v=v, o=o2)
@@ -434,7 +454,8 @@ def layer_bwd(dy, lw, block, H, geom, cache):
     do = (d_attn_out @ wo).reshape(-1, H, d // H)
     dq, dk, dv = attn_bwd(cache["q"], cache["k"], cache["v"], do, geom["hist_offsets"],
                           geom["m"], geom["pos"], geom["tau"], geom["slopes_pos"],
-                          geom["slopes_time"])
+                          geom["slopes_time"], history=geom.get("history", "causal"),
+                          time_bounds=geom.get("time_bounds"))
     dqkv = np.concatenate([t.reshape(-1, d) for t in (dq, dk, dv)], axis=1)
     grads["wqkv"] = dqkv.T @ cache["z"]
     dz = dqkv @ wqkv
