@@ -50,7 +50,12 @@ class Tables(Structure):
 
 
 class Alibi(Structure):
-    _fields_ = [("slopes_pos", c_void_p), ("slopes_time", c_void_p)]
+    _fields_ = [("slopes_pos", c_void_p), ("slopes_time", c_void_p), ("flags", c_int32),
+                ("n_time_bounds", c_int32), ("time_bounds", c_void_p)]
+
+
+ATTN_FULL_HISTORY = 1
+ATTN_TIME_BUCKET = 2
 
 
 class LayerWeights(Structure):
@@ -183,10 +188,13 @@ def make_tables(item, action, pos, ri, rt, rt_bounds, n_item, n_action, n_pos, n
 class HostSlopes:
     """Keeps the float32 host arrays alive for as long as the Alibi struct is used."""
 
-    def __init__(self, slopes_pos, slopes_time):
+    def __init__(self, slopes_pos, slopes_time, flags=0, time_bounds=None):
+        """time_bounds: a device tensor of int64 edges (GENRANK_ATTN_TIME_BUCKET)."""
         self.sp = np.ascontiguousarray(slopes_pos, dtype=np.float32)
         self.st = np.ascontiguousarray(slopes_time, dtype=np.float32)
-        self.struct = Alibi(self.sp.ctypes.data, self.st.ctypes.data)
+        self.time_bounds = time_bounds
+        n = 0 if time_bounds is None else int(time_bounds.numel())
+        self.struct = Alibi(self.sp.ctypes.data, self.st.ctypes.data, int(flags), n, _p(time_bounds))
 
 
 def make_layer_weights(wqkv, wo, slopes: HostSlopes, block, w1=None, w2=None, g1=None, g2=None,

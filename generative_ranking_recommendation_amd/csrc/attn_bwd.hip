@@ -34,6 +34,9 @@ struct BwdArgs {
   float scale;
   int B, m, H, dh, cand_only;
   int64_t T_h;
+  int flags;              // GENRANK_ATTN_* variants
+  const int64_t* tb;      // bucket edges (time-bucket variant)
+  int n_tb;
 };
 
 __device__ __forceinline__ float wsum(float v) {
@@ -70,7 +73,10 @@ __device__ __forceinline__ float slot_bias(const BwdArgs& a, const Slots& s, int
   const int pi = (i < s.N) ? i : s.N, pj = (j < s.N) ? j : s.N;
   const int64_t ti = ((i < s.N) ? a.ts[s.off + i] : a.req[s.u]) - s.t0;
   const int64_t tj = ((j < s.N) ? a.ts[s.off + j] : a.req[s.u]) - s.t0;
-  return -a.sp[h] * fabsf(static_cast<float>(pi - pj)) - a.st[h] * fabsf(static_cast<float>(ti - tj));
+  const int64_t gap = ti > tj ? ti - tj : tj - ti;
+  const float dt = (a.flags & GENRANK_ATTN_TIME_BUCKET) ? static_cast<float>(bucket_search_global(a.tb, a.n_tb, gap))
+                                                        : static_cast<float>(gap);
+  return -a.sp[h] * fabsf(static_cast<float>(pi - pj)) - a.st[h] * dt;
 }
 
 template <typename T>
@@ -130,8 +136,9 @@ __global__ void __launch_bounds__(64) dq_kernel(BwdArgs a) {
   const float lse = a.lse[row * a.H + h];
   const float Di = a.delta[row * a.H + h];
   float acc = 0.f;
+  const bool full = (a.flags & GENRANK_ATTN_FULL_HISTORY) != 0;
   for (int j = 0; j < L; ++j) {
-    if (!attn_allowed(s.i, j, s.N)) continue;
+    if (!attn_allowed(s.i, j, s.N, full)) continue;
     const int64_t kr = slot_row(a, s, j);
     const float kd = act ? to_f32(k[kr * a.ld_qkv + h * a.dh + lane]) : 0.f;
     const float vd = act ? to_f32(v[kr * a.ld_qkv + h * a.dh + lane]) : 0.f;
@@ -159,9 +166,10 @@ __global__ void __launch_bounds__(64) dkv_kernel(BwdArgs a) {
   const float kd = act ? to_f32(k[row * a.ld_qkv + h * a.dh + lane]) : 0.f;
   const float vd = act ? to_f32(v[row * a.ld_qkv + h * a.dh + lane]) : 0.f;
   float ak = 0.f, av = 0.f;
-  const int i_begin = (a.cand_only && j < s.N) ? s.N : j;
+  const bool full = (a.flags & GENRANK_ATTN_FULL_HISTORY) != 0;
+  const int i_begin = (a.cand_only && j < s.N) ? s.N : (full && j < s.N ? 0 : j);
   for (int i = i_begin; i < L; ++i) {
-    if (!attn_allowed(i, j, s.N)) continue;
+    if (!attn_allowed(i, j, s.N, full)) continue;
     if (a.cand_only && i < s.N) continue;
     const int64_t qr = slot_row(a, s, i);
     const float qd = act ? to_f32(q[qr * a.ld_qkv + h * a.dh + lane]) : 0.f;
@@ -215,7 +223,10 @@ struct BwdMArgs {
   float scale2, scale;
   int B, m, H, hist_tiles, cand_tiles, cand_only;
   int64_t T_h;
+  const int64_t* tb;  // bucket edges (time-bucket variant), their count, pow2 >= count + 1
+  int n_tb, tb_p2;
 };
+constexpr int BVAR_FULL = 1, BVAR_TBUCKET = 2;  // the ALiBi variants, as template bits
 
 // slot of row j (0..63 of a tile) in the permuted axis: the 8 values a lane packs from two
 // 16-row MFMA result blocks land in 8 consecutive slots
@@ -268,11 +279,15 @@ __device__ __forceinline__ bf16x8_t pack_blocks(const f32x4_t& lo, const f32x4_t
   return as_bf16x8(p);
 }
 
+template <int VAR>
 __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(BwdMArgs a) {
+  constexpr bool FULL = (VAR & BVAR_FULL) != 0, TBK = (VAR & BVAR_TBUCKET) != 0;
   __shared__ __attribute__((aligned(16))) bf16_t sK[2][TB * PLD];
   __shared__ __attribute__((aligned(16))) bf16_t sKt[2][DHB * PLD];
   __shared__ __attribute__((aligned(16))) bf16_t sV[2][TB * PLD];
   __shared__ __attribute__((aligned(16))) float sW[BWCH];
+  __shared__ __attribute__((aligned(16))) int32_t sT[TBK ? BWCH : 4];
+  __shared__ int32_t sTB[TBK ? ATTN_MAX_TIME_BOUNDS : 1];
 
   const int u = blockIdx.x / a.H;
   const int h = blockIdx.x - u * a.H;
@@ -300,7 +315,7 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(BwdMArgs a) {
     if (q0 >= N) return;
     nq = min(TB, N - q0);
     qrow0 = off + q0;
-    n_tiles = (q0 + nq + TB - 1) / TB;
+    n_tiles = FULL ? (N + TB - 1) / TB : (q0 + nq + TB - 1) / TB;
     if (a.cand_only) {  // the history rows carry no gradient: dQ = 0
       for (int e = tid; e < nq * (DHB / 4); e += 256) {
         const int r = e / (DHB / 4), c = (e - r * (DHB / 4)) * 4;
@@ -313,14 +328,22 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(BwdMArgs a) {
   const float sp2 = a.sp2[h], st2 = a.st2[h];
   const int p_ref = is_cand ? N : q0;
   const int64_t ts_ref = is_cand ? a.req[u] : a.ts[off + q0];
+  // with the bucketed time term, w holds the position term and sT the key time
   auto load_w = [&](int wbase) {
     for (int j = tid; j < BWCH; j += 256) {
       const int key = wbase + j;
-      sW[j] = key < N ? sp2 * static_cast<float>(key - p_ref) +
-                            st2 * static_cast<float>(static_cast<int32_t>(a.ts[off + key] - ts_ref))
+      const int32_t tk = key < N ? static_cast<int32_t>(a.ts[off + key] - ts_ref) : 0;
+      sW[j] = key < N ? (TBK ? sp2 * static_cast<float>(key - p_ref)
+                             : sp2 * static_cast<float>(key - p_ref) + st2 * static_cast<float>(tk))
                       : 0.f;
+      if constexpr (TBK) sT[j] = tk;
     }
   };
+  if constexpr (TBK)
+    for (int k = tid; k < a.tb_p2; k += 256) {
+      const int64_t b = k < a.n_tb ? a.tb[k] : INT64_MAX;
+      sTB[k] = b > INT32_MAX ? INT32_MAX : (b < INT32_MIN ? INT32_MIN : static_cast<int32_t>(b));
+    }
   const int kt_first = n_tiles - 1;
   int wbase = n_tiles > 0 ? (kt_first * TB / BWCH) * BWCH : 0;
 
@@ -329,7 +352,7 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(BwdMArgs a) {
   const bool q_valid = q_local < nq;
   const int64_t qrow = qrow0 + min(q_local, nq - 1);
   const int q_slot = is_cand ? N + q0 + q_local : q0 + q_local;
-  const int k_lim = is_cand ? N - 1 : min(q_slot, N - 1);
+  const int k_lim = (is_cand || FULL) ? N - 1 : min(q_slot, N - 1);
   const int64_t ro = qrow * a.ld_qkv + h * DHB;
   const int64_t rdo = qrow * a.ld_o + h * DHB;
   const uint4 qa = *reinterpret_cast<const uint4*>(a.q + ro + g4 * 8);
@@ -341,9 +364,12 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(BwdMArgs a) {
   const float lse2 = a.lse[qrow * a.H + h] * LOG2E_B;
   const float Di = a.delta[qrow * a.H + h];
   float w_i = 0.f;
-  if (!is_cand)
-    w_i = sp2 * static_cast<float>(q_slot - p_ref) +
-          st2 * static_cast<float>(static_cast<int32_t>(a.ts[off + min(q_slot, N - 1)] - ts_ref));
+  int32_t tq = 0;  // the query's time relative to ts_ref
+  if (!is_cand) {
+    tq = static_cast<int32_t>(a.ts[off + min(q_slot, N - 1)] - ts_ref);
+    w_i = TBK ? sp2 * static_cast<float>(q_slot - p_ref)
+              : sp2 * static_cast<float>(q_slot - p_ref) + st2 * static_cast<float>(tq);
+  }
   const float c_i = w_i + lse2;
 
   f32x4_t accQ[4];
@@ -359,7 +385,9 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(BwdMArgs a) {
     const uint4 vb = *reinterpret_cast<const uint4*>(a.v + ro + g4 * 8 + 32);
     const float sqk = bxor32_sum(bxor16_sum(dot16(qa, qb, ka, kb)));
     const float sdv = bxor32_sum(bxor16_sum(dot16(da, db, va, vb)));
-    const float p = __builtin_amdgcn_exp2f(sqk * a.scale2 - c_i);
+    float self_bias = 0.f;  // the bucketed time term of the gap 0
+    if constexpr (TBK) self_bias = -st2 * static_cast<float>(bucket_search_global(a.tb, a.n_tb, 0));
+    const float p = __builtin_amdgcn_exp2f(sqk * a.scale2 + self_bias - c_i);
     const float ds = p * (sdv - Di);
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
@@ -421,7 +449,7 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(BwdMArgs a) {
   asm volatile("" : "+v"(qf[0]), "+v"(qf[1]), "+v"(dof[0]), "+v"(dof[1]));
   __syncthreads();
 
-  const int klim_min = is_cand ? N - 1 : q0;
+  const int klim_min = (is_cand || FULL) ? N - 1 : q0;
   for (int it = 0; it < n_tiles; ++it) {
     const int kt = kt_first - it;
     const int buf = it & 1;
@@ -452,9 +480,22 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(BwdMArgs a) {
     for (int kb = 0; kb < 4; ++kb) {
       const float4 w = reinterpret_cast<const float4*>(sW)[((base - wbase) >> 2) + kb * 4 + g4];
       const float wv[4] = {w.x, w.y, w.z, w.w};
+      int32_t tkv[4] = {0, 0, 0, 0};
+      if constexpr (TBK) {
+        const int4 t4 = reinterpret_cast<const int4*>(sT)[((base - wbase) >> 2) + kb * 4 + g4];
+        tkv[0] = t4.x; tkv[1] = t4.y; tkv[2] = t4.z; tkv[3] = t4.w;
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        float p = __builtin_amdgcn_exp2f(s[kb][i] * a.scale2 + wv[i] - c_i);
+        float arg;
+        if constexpr (!FULL && !TBK) {
+          arg = s[kb][i] * a.scale2 + wv[i] - c_i;
+        } else {
+          // fully visible: -|w_j - w_i|; bucketed time: - s' bucket(|t_i - t_j|)
+          arg = s[kb][i] * a.scale2 + (FULL ? -fabsf(wv[i] - w_i) : wv[i] - w_i) - lse2;
+          if constexpr (TBK) arg -= st2 * static_cast<float>(bucket_search(sTB, a.tb_p2, abs(tq - tkv[i])));
+        }
+        float p = __builtin_amdgcn_exp2f(arg);
         if (masked && base + kb * 16 + g4 * 4 + i > k_lim) p = 0.f;
         s[kb][i] = p * (dp[kb][i] - Di);
       }
@@ -484,13 +525,20 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(BwdMArgs a) {
   }
 }
 
+template <int VAR>
 __global__ void __launch_bounds__(256) attn_bwd_dkv_kernel(BwdMArgs a) {
+  constexpr bool FULL = (VAR & BVAR_FULL) != 0, TBK = (VAR & BVAR_TBUCKET) != 0;
   __shared__ __attribute__((aligned(16))) bf16_t sQ[2][TB * PLD];
   __shared__ __attribute__((aligned(16))) bf16_t sQt[2][DHB * PLD];
   __shared__ __attribute__((aligned(16))) bf16_t sO[2][TB * PLD];
   __shared__ __attribute__((aligned(16))) bf16_t sOt[2][DHB * PLD];
   __shared__ __attribute__((aligned(16))) float sC[2][TB];
   __shared__ __attribute__((aligned(16))) float sD[2][TB];
+  // variants: sC holds w_i alone and sL the query's lse (fully visible history), sTq the
+  // query's time relative to the tile's reference (bucketed time), sTB the bucket edges
+  __shared__ __attribute__((aligned(16))) float sL[FULL ? 2 : 1][FULL ? TB : 4];
+  __shared__ __attribute__((aligned(16))) int32_t sTq[TBK ? 2 : 1][TBK ? TB : 4];
+  __shared__ int32_t sTB[TBK ? ATTN_MAX_TIME_BOUNDS : 1];
 
   const int u = blockIdx.x / a.H;
   const int h = blockIdx.x - u * a.H;
@@ -521,7 +569,7 @@ __global__ void __launch_bounds__(256) attn_bwd_dkv_kernel(BwdMArgs a) {
   // gradient), then every candidate tile
   const int n_ht = (N + TB - 1) / TB;
   const int n_ct = (a.m + TB - 1) / TB;
-  const int h_first = a.cand_only ? n_ht : kt;
+  const int h_first = a.cand_only ? n_ht : (FULL ? 0 : kt);
   const int n_qt = (n_ht - h_first) + n_ct;
   struct QT { bool cand; int q0, nq; int64_t row0; };
   auto qtile = [&](int qi) {
@@ -544,7 +592,8 @@ __global__ void __launch_bounds__(256) attn_bwd_dkv_kernel(BwdMArgs a) {
   // 8ch..8ch+7; threads 0..63 also compute c_i and D_i of query tid
   const int pr = tid & 31, ch = tid >> 5;
   uint4 rqa, rqb, roa, rob;
-  float rc = 0.f, rd = 0.f;
+  float rc = 0.f, rd = 0.f, rl = 0.f;
+  int32_t rt = 0;
   auto fetch = [&](const QT& t) {
     const int64_t ra = t.row0 + min(2 * pr, t.nq - 1), rb = t.row0 + min(2 * pr + 1, t.nq - 1);
     rqa = *reinterpret_cast<const uint4*>(a.q + ra * a.ld_qkv + h * DHB + ch * 8);
@@ -555,10 +604,15 @@ __global__ void __launch_bounds__(256) attn_bwd_dkv_kernel(BwdMArgs a) {
       const int ql = min(tid, t.nq - 1);
       const int64_t r = t.row0 + ql;
       float w_i = 0.f;
-      if (!t.cand)
-        w_i = sp2 * static_cast<float>(ql) +
-              st2 * static_cast<float>(static_cast<int32_t>(a.ts[off + t.q0 + ql] - a.ts[off + t.q0]));
-      rc = w_i + a.lse[r * a.H + h] * LOG2E_B;
+      int32_t tq = 0;
+      if (!t.cand) {
+        tq = static_cast<int32_t>(a.ts[off + t.q0 + ql] - a.ts[off + t.q0]);
+        w_i = TBK ? sp2 * static_cast<float>(ql) : sp2 * static_cast<float>(ql) + st2 * static_cast<float>(tq);
+      }
+      const float lse2 = a.lse[r * a.H + h] * LOG2E_B;
+      rc = FULL ? w_i : w_i + lse2;
+      rl = lse2;
+      rt = tq;
       rd = a.delta[r * a.H + h];
     }
   };
@@ -568,8 +622,15 @@ __global__ void __launch_bounds__(256) attn_bwd_dkv_kernel(BwdMArgs a) {
     if (tid < TB) {
       sC[buf][tid] = rc;
       sD[buf][tid] = rd;
+      if constexpr (FULL) sL[buf][tid] = rl;
+      if constexpr (TBK) sTq[buf][tid] = rt;
     }
   };
+  if constexpr (TBK)
+    for (int k = tid; k < a.tb_p2; k += 256) {
+      const int64_t b = k < a.n_tb ? a.tb[k] : INT64_MAX;
+      sTB[k] = b > INT32_MAX ? INT32_MAX : (b < INT32_MIN ? INT32_MIN : static_cast<int32_t>(b));
+    }
 
   f32x4_t accK[4], accV[4];
 #pragma unroll
@@ -591,7 +652,9 @@ __global__ void __launch_bounds__(256) attn_bwd_dkv_kernel(BwdMArgs a) {
     // this tile's bias reference: its first query, or the candidates' (N, request time)
     const int p_ref = t.cand ? N : t.q0;
     const int64_t ts_ref = t.cand ? a.req[u] : a.ts[off + t.q0];
-    const float w_j = sp2 * static_cast<float>(j - p_ref) + st2 * static_cast<float>(static_cast<int32_t>(ts_j - ts_ref));
+    const int32_t tk = static_cast<int32_t>(ts_j - ts_ref);
+    const float w_j = TBK ? sp2 * static_cast<float>(j - p_ref)
+                          : sp2 * static_cast<float>(j - p_ref) + st2 * static_cast<float>(tk);
     f32x4_t s[4], dp[4];
 #pragma unroll
     for (int qb = 0; qb < 4; ++qb) {
@@ -612,12 +675,30 @@ __global__ void __launch_bounds__(256) attn_bwd_dkv_kernel(BwdMArgs a) {
       const float4 d4 = reinterpret_cast<const float4*>(sD[buf])[qb * 4 + g4];
       const float cv[4] = {c4.x, c4.y, c4.z, c4.w};
       const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
+      float lv[4] = {0.f, 0.f, 0.f, 0.f};
+      int32_t tv[4] = {0, 0, 0, 0};
+      if constexpr (FULL) {
+        const float4 l4 = reinterpret_cast<const float4*>(sL[buf])[qb * 4 + g4];
+        lv[0] = l4.x; lv[1] = l4.y; lv[2] = l4.z; lv[3] = l4.w;
+      }
+      if constexpr (TBK) {
+        const int4 t4 = reinterpret_cast<const int4*>(sTq[buf])[qb * 4 + g4];
+        tv[0] = t4.x; tv[1] = t4.y; tv[2] = t4.z; tv[3] = t4.w;
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int ql = qb * 16 + g4 * 4 + i;
         const int slot = t.cand ? N + t.q0 + ql : t.q0 + ql;
-        const bool ok = key_valid && ql < t.nq && (t.cand || j <= slot);
-        const float p = ok ? __builtin_amdgcn_exp2f(s[qb][i] * a.scale2 + w_j - cv[i]) : 0.f;
+        const bool ok = key_valid && ql < t.nq && (t.cand || FULL || j <= slot);
+        float arg;
+        if constexpr (!FULL && !TBK) {
+          arg = s[qb][i] * a.scale2 + w_j - cv[i];
+        } else {
+          // fully visible: -|w_j - w_i|; bucketed time: - s' bucket(|t_i - t_j|)
+          arg = FULL ? s[qb][i] * a.scale2 - fabsf(w_j - cv[i]) - lv[i] : s[qb][i] * a.scale2 + w_j - cv[i];
+          if constexpr (TBK) arg -= st2 * static_cast<float>(bucket_search(sTB, a.tb_p2, abs(tv[i] - tk)));
+        }
+        const float p = ok ? __builtin_amdgcn_exp2f(arg) : 0.f;
         s[qb][i] = p;
         dp[qb][i] = p * (dp[qb][i] - dv[i]);
       }
@@ -682,6 +763,9 @@ genrank_status launch_attn_bwd(const genrank_batch* b, const int32_t* offsets, c
   a.scale = 1.f / sqrtf(static_cast<float>(b->dh));
   a.B = b->B; a.m = b->m; a.H = b->H; a.dh = b->dh; a.cand_only = cand_only;
   a.T_h = b->total_hist;
+  a.flags = alibi.flags;
+  a.tb = alibi.time_bounds;
+  a.n_tb = alibi.n_time_bounds;
   dim3 grid(static_cast<unsigned>(T), b->H);
   if (b->dtype == GENRANK_BF16) {  // dh == 64 and the alignments are checked by the caller
     const int64_t pairs = T * b->H;
@@ -705,10 +789,26 @@ genrank_status launch_attn_bwd(const genrank_batch* b, const int32_t* offsets, c
     m.hist_tiles = (b->max_hist + TB - 1) / TB;
     m.cand_tiles = (b->m + TB - 1) / TB;
     m.T_h = b->total_hist;
-    if (m.hist_tiles + m.cand_tiles > 0)
-      hipLaunchKernelGGL(attn_bwd_dq_kernel, dim3(b->B * b->H, m.cand_tiles + m.hist_tiles), dim3(256), 0, stream, m);
-    if (m.hist_tiles > 0)
-      hipLaunchKernelGGL(attn_bwd_dkv_kernel, dim3(b->B * b->H, m.hist_tiles), dim3(256), 0, stream, m);
+    if (alibi.flags & GENRANK_ATTN_TIME_BUCKET) {
+      m.tb = alibi.time_bounds;
+      m.n_tb = alibi.n_time_bounds;
+      m.tb_p2 = bucket_p2(m.n_tb);
+    }
+    const dim3 gq(b->B * b->H, m.cand_tiles + m.hist_tiles), gk(b->B * b->H, m.hist_tiles);
+    const int var = ((alibi.flags & GENRANK_ATTN_FULL_HISTORY) ? BVAR_FULL : 0) |
+                    ((alibi.flags & GENRANK_ATTN_TIME_BUCKET) ? BVAR_TBUCKET : 0);
+    auto launch = [&](auto dq_kernel, auto dkv_kernel) {
+      if (m.hist_tiles + m.cand_tiles > 0) hipLaunchKernelGGL(dq_kernel, gq, dim3(256), 0, stream, m);
+      if (m.hist_tiles > 0) hipLaunchKernelGGL(dkv_kernel, gk, dim3(256), 0, stream, m);
+    };
+    switch (var) {
+      case 0: launch(attn_bwd_dq_kernel<0>, attn_bwd_dkv_kernel<0>); break;
+      case BVAR_FULL: launch(attn_bwd_dq_kernel<BVAR_FULL>, attn_bwd_dkv_kernel<BVAR_FULL>); break;
+      case BVAR_TBUCKET: launch(attn_bwd_dq_kernel<BVAR_TBUCKET>, attn_bwd_dkv_kernel<BVAR_TBUCKET>); break;
+      default:
+        launch(attn_bwd_dq_kernel<BVAR_FULL | BVAR_TBUCKET>, attn_bwd_dkv_kernel<BVAR_FULL | BVAR_TBUCKET>);
+        break;
+    }
   } else {
     hipLaunchKernelGGL(delta_kernel<float>, grid, dim3(64), 0, stream, a);
     hipLaunchKernelGGL(dq_kernel<float>, grid, dim3(64), 0, stream, a);

@@ -74,7 +74,13 @@ struct AttnArgs {
   const bf16_t* vh;
   int64_t ld_h;
   int64_t crow0;           // row of candidate (u, 0) in q / k / v / o / lse: T_h, or 0
+  // bucketed time term: edges (int64, device), their count, and the power of two >= count + 1
+  const int64_t* tb;
+  int n_tb, tb_p2;
 };
+
+// variant bits of the bf16 kernel: the fully visible history mask, the bucketed time term
+constexpr int VAR_FULL = 1, VAR_TBUCKET = 2;
 
 // slot of key j (0..63 in a tile) in the permuted key axis of sVt
 __device__ __forceinline__ int vt_slot(int j) {
@@ -106,11 +112,17 @@ __device__ __forceinline__ float xor32_sum(float x) {
 // item/action sequence (2 N slots, rows 2 off .. 2 off + 2N) and the bias is a learned
 // matrix read from memory (user u's [L, P] bf16 block, L = 2N + m, row pitch P = L rounded
 // up to 8); everything else is the same kernel.
-template <bool RAB>
+template <bool RAB, int VAR = 0>
 __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8))) attn_fwd_bf16_kernel(AttnArgs a) {
+  constexpr bool FULL = (VAR & VAR_FULL) != 0;
+  constexpr bool TBK = (VAR & VAR_TBUCKET) != 0;
+  static_assert(!RAB || VAR == 0, "the learned bias takes no ALiBi variant");
   __shared__ __attribute__((aligned(16))) bf16_t sK[2][AK * KLD];
   __shared__ __attribute__((aligned(16))) bf16_t sVt[2][DH * VLD];
   __shared__ __attribute__((aligned(16))) float sW[WCHUNK];
+  // bucketed time term: the chunk's key times relative to tau_ref, and the bucket edges
+  __shared__ __attribute__((aligned(16))) int32_t sT[TBK ? WCHUNK : 4];
+  __shared__ int32_t sTB[TBK ? ATTN_MAX_TIME_BOUNDS : 1];
 
   // Flat grid over (user, head, tile).  Workgroup w runs on XCD w % 8 as that XCD's
   // (w / 8)-th workgroup.  Each XCD owns the (user, head) pairs bh = x mod 8 and walks them
@@ -149,7 +161,8 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
     if (q0 >= N) return;
     nq = min(AQ, N - q0);
     qrow0 = off + q0;
-    n_tiles = (q0 + nq + AK - 1) / AK;  // keys up to the tile's last query
+    // keys up to the tile's last query, or every history key
+    n_tiles = FULL ? (N + AK - 1) / AK : (q0 + nq + AK - 1) / AK;
   }
 
   const int tid = threadIdx.x;
@@ -164,15 +177,19 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
   // ---- per-key bias terms w_j = sp (p_j - p_ref) + st (tau_j - tau_ref) for keys
   // [wbase, wbase + WCHUNK); keys past the history end get 0 (they are masked).  The time
   // difference is below 2^24 s, so it converts exactly through int32.
+  // With the bucketed time term w_j holds the position term only and sT the key's time.
   auto load_w = [&](int wbase) {
     for (int j = tid; j < WCHUNK; j += NT) {
       const int key = wbase + j;
       float w = 0.f;
+      int32_t tk = 0;
       if (key < N) {
-        w = sp2 * static_cast<float>(key - p_ref) +
-            st2 * static_cast<float>(static_cast<int32_t>(a.ts[off + key] - ts_ref));
+        tk = static_cast<int32_t>(a.ts[off + key] - ts_ref);
+        w = TBK ? sp2 * static_cast<float>(key - p_ref)
+                : sp2 * static_cast<float>(key - p_ref) + st2 * static_cast<float>(tk);
       }
       sW[j] = w;
+      if constexpr (TBK) sT[j] = tk;
     }
   };
   // key tiles run newest first; the first one lies in this bias chunk
@@ -203,10 +220,11 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
     // lanes past the tile's last query read that query's row (never stored)
     qrow_ld[c] = qrow0 + min(q_local[c], nq - 1);
     // keys with a slot above k_lim are masked: history queries see keys up to
-    // themselves, candidates every history key (their own key is the seed below)
-    k_lim[c] = is_cand ? (N - 1) : min(q_slot[c], N - 1);
+    // themselves (all history keys with the fully visible mask), candidates every
+    // history key (their own key is the seed below)
+    k_lim[c] = (is_cand || FULL) ? (N - 1) : min(q_slot[c], N - 1);
     // largest key any query of this 16-column block may see (uniform per wave)
-    kmax_blk[c] = is_cand ? (N - 1) : min(q0 + wave * QW + c * 16 + 15, N - 1);
+    kmax_blk[c] = (is_cand || FULL) ? (N - 1) : min(q0 + wave * QW + c * 16 + 15, N - 1);
     const int64_t rowoff = qrow_ld[c] * a.ld_qkv + h * DH;
     qf[c][0] = as_bf16x8(*reinterpret_cast<const uint4*>(a.q + rowoff + g4 * 8));
     qf[c][1] = as_bf16x8(*reinterpret_cast<const uint4*>(a.q + rowoff + g4 * 8 + 32));
@@ -308,10 +326,19 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
   rab_load(kt_first, R0);
 
   // ---- bias terms of the first chunk (the loads above stay in flight)
-  if constexpr (!RAB)
-    sW[tid] = wkey_in ? sp2 * static_cast<float>(wkey - p_ref) +
-                            st2 * static_cast<float>(static_cast<int32_t>(ts_key - ts_ref))
+  if constexpr (!RAB) {
+    const int32_t tk = static_cast<int32_t>(ts_key - ts_ref);
+    sW[tid] = wkey_in ? (TBK ? sp2 * static_cast<float>(wkey - p_ref)
+                             : sp2 * static_cast<float>(wkey - p_ref) + st2 * static_cast<float>(tk))
                       : 0.f;
+    if constexpr (TBK) sT[tid] = wkey_in ? tk : 0;
+  }
+  // bucket edges in LDS, padded to a power of two with the largest int32
+  if constexpr (TBK)
+    for (int k = tid; k < a.tb_p2; k += NT) {
+      const int64_t b = k < a.n_tb ? a.tb[k] : INT64_MAX;
+      sTB[k] = b > INT32_MAX ? INT32_MAX : (b < INT32_MIN ? INT32_MIN : static_cast<int32_t>(b));
+    }
 
   // ---- softmax state; a candidate starts from its own key: bias 0 (it shares p_ref and
   // tau_ref), so its score is the plain scaled dot product
@@ -332,6 +359,9 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
       dot = xor32_sum(xor16_sum(dot));
       m2[c] = dot * a.scale2;
       if constexpr (RAB) m2[c] += rab_self[c] * LOG2E;  // the learned bias of (i, i)
+      // the bucketed time term of the candidate's own key (gap 0), read from global
+      // memory: the LDS copy of the edges is not complete yet
+      if constexpr (TBK) m2[c] -= st2 * static_cast<float>(bucket_search_global(a.tb, a.n_tb, 0));
       lsum[c] = (g4 == 0) ? 1.f : 0.f;
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) {
@@ -357,9 +387,26 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
   __syncthreads();
   // a history query's own bias term w_i (its key lies in the first tile's bias chunk);
   // the row term of the bias, added back into the log-sum-exp at the end
+  // (With the fully visible mask the query's slot may lie in an earlier chunk: its term is
+  // computed from the definition.)  With the bucketed time term: the query's time tq.
   float w_i[QB];
+  int32_t tq[QB];
 #pragma unroll
-  for (int c = 0; c < QB; ++c) w_i[c] = (!RAB && !is_cand && q_valid[c]) ? sW[q_slot[c] - wbase] : 0.f;
+  for (int c = 0; c < QB; ++c) {
+    tq[c] = 0;
+    if constexpr (FULL || TBK) {
+      const int sl = min(q_slot[c], N - 1);
+      if (!is_cand && N > 0) tq[c] = static_cast<int32_t>(a.ts[off + sl] - ts_ref);
+    }
+    if constexpr (FULL) {
+      w_i[c] = (!is_cand && q_valid[c]) ? (TBK ? sp2 * static_cast<float>(q_slot[c] - p_ref)
+                                               : sp2 * static_cast<float>(q_slot[c] - p_ref) +
+                                                     st2 * static_cast<float>(tq[c]))
+                                        : 0.f;
+    } else {
+      w_i[c] = (!RAB && !is_cand && q_valid[c]) ? sW[q_slot[c] - wbase] : 0.f;
+    }
+  }
 
   // One key tile, newest first: the recency bias puts each row's maximum in the first
   // tiles, so the rescaling of O is rarely needed later.  Tiles that reach past some
@@ -423,12 +470,30 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
       } else {
         w = reinterpret_cast<const float4*>(sW)[((base - wbase) >> 2) + kb * 4 + g4];
       }
+      if constexpr (!FULL && !TBK) {
 #pragma unroll
-      for (int c = 0; c < QB; ++c) {
-        s[c][kb][0] = s[c][kb][0] * a.scale2 + w.x;
-        s[c][kb][1] = s[c][kb][1] * a.scale2 + w.y;
-        s[c][kb][2] = s[c][kb][2] * a.scale2 + w.z;
-        s[c][kb][3] = s[c][kb][3] * a.scale2 + w.w;
+        for (int c = 0; c < QB; ++c) {
+          s[c][kb][0] = s[c][kb][0] * a.scale2 + w.x;
+          s[c][kb][1] = s[c][kb][1] * a.scale2 + w.y;
+          s[c][kb][2] = s[c][kb][2] * a.scale2 + w.z;
+          s[c][kb][3] = s[c][kb][3] * a.scale2 + w.w;
+        }
+      } else {
+        // fully visible: -|w_j - w_i| (positions and times are sorted, so both terms of
+        // a pair have the same sign); bucketed time: - s' bucket(|t_i - t_j|)
+        const float wv[4] = {w.x, w.y, w.z, w.w};
+        int4 t4 = make_int4(0, 0, 0, 0);
+        if constexpr (TBK) t4 = reinterpret_cast<const int4*>(sT)[((base - wbase) >> 2) + kb * 4 + g4];
+        const int32_t tkv[4] = {t4.x, t4.y, t4.z, t4.w};
+#pragma unroll
+        for (int c = 0; c < QB; ++c)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float x = s[c][kb][i] * a.scale2 + (FULL ? -fabsf(wv[i] - w_i[c]) : wv[i]);
+            if constexpr (TBK)
+              x -= st2 * static_cast<float>(bucket_search(sTB, a.tb_p2, abs(tq[c] - tkv[i])));
+            s[c][kb][i] = x;
+          }
       }
     }
 #pragma unroll
@@ -508,7 +573,7 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
   };
 
   // a tile needs the mask when its last key lies past some query's limit
-  const int klim_min = is_cand ? (N - 1) : q0;
+  const int klim_min = (is_cand || FULL) ? (N - 1) : q0;
   auto loop = [&](auto active_tag) {
     auto step = [&](int it, Stage& ld, const Stage& nxt, const RabRegs& rc, RabRegs& rn) {
       if ((kt_first - it) * AK + AK - 1 > klim_min)
@@ -540,7 +605,7 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
       o.y = pack_bf16x2(accO[c][nb][2] * inv, accO[c][nb][3] * inv);
       *reinterpret_cast<uint2*>(a.o + qrow[c] * a.ld_o + h * DH + nb * 16 + g4 * 4) = o;
     }
-    if (a.lse && g4 == 0) a.lse[qrow[c] * a.H + h] = LN2 * (m2[c] + log2f(ltot) - w_i[c]);
+    if (a.lse && g4 == 0) a.lse[qrow[c] * a.H + h] = LN2 * (m2[c] + log2f(ltot) - (FULL ? 0.f : w_i[c]));
   }
 }
 
@@ -563,6 +628,9 @@ struct AttnF32Args {
   float scale;
   int B, m, H, dh;
   int64_t T_h;
+  int flags;
+  const int64_t* tb;
+  int n_tb;
 };
 
 __global__ void __launch_bounds__(64) attn_fwd_f32_kernel(AttnF32Args a) {
@@ -594,13 +662,16 @@ __global__ void __launch_bounds__(64) attn_fwd_f32_kernel(AttnF32Args a) {
   const int pi = slot_pos(i);
   const int64_t ti = slot_tau(i);
   float mx = -INFINITY, l = 0.f, acc = 0.f;
+  const bool full = (a.flags & GENRANK_ATTN_FULL_HISTORY) != 0;
+  const bool tbk = (a.flags & GENRANK_ATTN_TIME_BUCKET) != 0;
   for (int j = 0; j < L; ++j) {
-    if (!attn_allowed(i, j, N)) continue;
+    if (!attn_allowed(i, j, N, full)) continue;
     const int64_t kr = slot_row(j);
     float dot = act ? qd * a.k[kr * a.ld_qkv + h * a.dh + lane] : 0.f;
     for (int off2 = 32; off2 > 0; off2 >>= 1) dot += __shfl_xor(dot, off2);
-    const float s = dot * a.scale - a.sp[h] * fabsf(static_cast<float>(pi - slot_pos(j))) -
-                    a.st[h] * fabsf(static_cast<float>(ti - slot_tau(j)));
+    const int64_t gap = ti > slot_tau(j) ? ti - slot_tau(j) : slot_tau(j) - ti;
+    const float dt = tbk ? static_cast<float>(bucket_search_global(a.tb, a.n_tb, gap)) : static_cast<float>(gap);
+    const float s = dot * a.scale - a.sp[h] * fabsf(static_cast<float>(pi - slot_pos(j))) - a.st[h] * dt;
     const float m_new = fmaxf(mx, s);
     const float c = expf(mx - m_new);
     const float p = expf(s - m_new);
@@ -633,6 +704,10 @@ genrank_status check_attn_args(const genrank_batch* b, const int32_t* offsets, c
   genrank_status s = check_batch(b);
   if (s != GENRANK_OK) return s;
   if (!offsets || !req || !alibi.slopes_pos || !alibi.slopes_time) return GENRANK_E_ARG;
+  {
+    const genrank_status vs = check_alibi_variant(alibi);
+    if (vs != GENRANK_OK) return vs;
+  }
   if (b->total_hist > 0 && !ts) return GENRANK_E_ARG;
   if (!q || !k || !v || !o) return GENRANK_E_ARG;
   if (ld_qkv < b->d || ld_o < b->d) return GENRANK_E_SHAPE;
@@ -687,6 +762,23 @@ genrank_status launch_hstu_attn_fwd(const genrank_batch* b, const int32_t* offse
   return GENRANK_OK;
 }
 
+// the instantiation for the ALiBi variant flags, and the bucket edges' fields
+void set_variant(AttnArgs& a, const genrank_alibi& alibi) {
+  a.tb = alibi.time_bounds;
+  a.n_tb = (alibi.flags & GENRANK_ATTN_TIME_BUCKET) ? alibi.n_time_bounds : 0;
+  a.tb_p2 = bucket_p2(a.n_tb);
+}
+void launch_bf16_variant(int flags, dim3 grid, hipStream_t stream, const AttnArgs& a) {
+  const int var = ((flags & GENRANK_ATTN_FULL_HISTORY) ? VAR_FULL : 0) |
+                  ((flags & GENRANK_ATTN_TIME_BUCKET) ? VAR_TBUCKET : 0);
+  switch (var) {
+    case 0: hipLaunchKernelGGL((attn_fwd_bf16_kernel<false, 0>), grid, dim3(NT), 0, stream, a); break;
+    case 1: hipLaunchKernelGGL((attn_fwd_bf16_kernel<false, 1>), grid, dim3(NT), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((attn_fwd_bf16_kernel<false, 2>), grid, dim3(NT), 0, stream, a); break;
+    default: hipLaunchKernelGGL((attn_fwd_bf16_kernel<false, 3>), grid, dim3(NT), 0, stream, a); break;
+  }
+}
+
 genrank_status launch_attn_fwd(const genrank_batch* b, const int32_t* offsets, const int64_t* ts,
                                const int64_t* req, genrank_alibi alibi, const void* q,
                                const void* k, const void* v, int64_t ld_qkv, void* o,
@@ -717,7 +809,8 @@ genrank_status launch_attn_fwd(const genrank_batch* b, const int32_t* offsets, c
     const int64_t pairs = (static_cast<int64_t>(b->B) * b->H + 8 * GROUP - 1) / (8 * GROUP) * (8 * GROUP);
     const int64_t G = pairs * (a.hist_tiles + a.cand_tiles);
     if (G > INT32_MAX) return GENRANK_E_SHAPE;
-    hipLaunchKernelGGL(attn_fwd_bf16_kernel<false>, dim3(static_cast<unsigned>(G)), dim3(NT), 0, stream, a);
+    set_variant(a, alibi);
+    launch_bf16_variant(alibi.flags, dim3(static_cast<unsigned>(G)), stream, a);
   } else {
     AttnF32Args a{};
     a.offsets = offsets; a.ts = ts; a.req = req;
@@ -735,6 +828,9 @@ genrank_status launch_attn_fwd(const genrank_batch* b, const int32_t* offsets, c
     a.scale = 1.f / sqrtf(static_cast<float>(b->dh));
     a.B = b->B; a.m = b->m; a.H = b->H; a.dh = b->dh;
     a.T_h = b->total_hist;
+    a.flags = alibi.flags;
+    a.tb = alibi.time_bounds;
+    a.n_tb = (alibi.flags & GENRANK_ATTN_TIME_BUCKET) ? alibi.n_time_bounds : 0;
     hipLaunchKernelGGL(attn_fwd_f32_kernel, dim3(static_cast<unsigned>(T), b->H), dim3(64), 0,
                        stream, a);
   }
@@ -770,7 +866,9 @@ genrank_status launch_attn_fwd_cached(const genrank_batch* b, const int32_t* off
   const int64_t pairs = (static_cast<int64_t>(b->B) * b->H + 8 * GROUP - 1) / (8 * GROUP) * (8 * GROUP);
   const int64_t G = pairs * a.cand_tiles;
   if (G > INT32_MAX) return GENRANK_E_SHAPE;
-  hipLaunchKernelGGL(attn_fwd_bf16_kernel<false>, dim3(static_cast<unsigned>(G)), dim3(NT), 0, stream, a);
+  set_variant(a, alibi);
+  // no history query is answered here: only the time variant matters
+  launch_bf16_variant(alibi.flags & GENRANK_ATTN_TIME_BUCKET, dim3(static_cast<unsigned>(G)), stream, a);
   GR_CHECK_LAUNCH();
   return GENRANK_OK;
 }

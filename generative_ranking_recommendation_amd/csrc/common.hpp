@@ -81,11 +81,38 @@ __device__ __forceinline__ int xcd_local_id(int w, int G) {
 }
 
 // The attention mask on one user's sequence slots: 0..N-1 history, N.. candidates.
-// History queries see history keys at or before them; a candidate sees all history and
-// itself.  Every attention kernel's masked tiles and genrank_debug_mask use this.
-__device__ __forceinline__ bool attn_allowed(int i, int j, int N) {
-  return (i < N) ? (j <= i) : (j < N || j == i);
+// History queries see history keys at or before them (every history key with the fully
+// visible history variant); a candidate sees all history and itself.  Every attention
+// kernel's masked tiles and genrank_debug_mask use this.
+__device__ __forceinline__ bool attn_allowed(int i, int j, int N, bool full_history = false) {
+  return (i < N) ? (full_history ? j < N : j <= i) : (j < N || j == i);
 }
+
+// #{k : b[k] <= g} for b sorted ascending in p2 entries (a power of two >= the edge count,
+// at least 1), the entries past the real edges being INT32_MAX (g < INT32_MAX): a branchless
+// binary search over the first p2 - 1 entries, then one compare with the entry it stops at
+// (index <= p2 - 1), so that p2 entries count
+__device__ __forceinline__ int bucket_search(const int32_t* b, int p2, int32_t g) {
+  int pos = 0;
+  for (int step = p2 >> 1; step > 0; step >>= 1) pos += (b[pos + step - 1] <= g) ? step : 0;
+  return pos + (b[pos] <= g ? 1 : 0);
+}
+// the power of two that bucket_search takes for n edges (n <= ATTN_MAX_TIME_BOUNDS)
+inline int bucket_p2(int n) {
+  int p2 = 1;
+  while (p2 < n) p2 <<= 1;
+  return p2;
+}
+// the same count over int64 edges in global memory (n edges, upper bound search)
+__device__ __forceinline__ int bucket_search_global(const int64_t* b, int n, int64_t g) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (b[mid] <= g) lo = mid + 1; else hi = mid;
+  }
+  return lo;
+}
+constexpr int ATTN_MAX_TIME_BOUNDS = 1024;
 
 // ---- direct global -> LDS loads and explicit waits (operand rings)
 typedef __attribute__((address_space(3))) void lds_void_t;

@@ -76,6 +76,16 @@ genrank_status launch_hstu_attn_fwd(const genrank_batch* b, const int32_t* offse
                                     const void* v, int64_t ld_qkv, void* o, int64_t ld_o, float* lse,
                                     hipStream_t stream);
 
+// the ALiBi variant flags: known bits only; bucket edges present and at most 1024
+inline genrank_status check_alibi_variant(const genrank_alibi& a) {
+  if (a.flags & ~(GENRANK_ATTN_FULL_HISTORY | GENRANK_ATTN_TIME_BUCKET)) return GENRANK_E_ARG;
+  if (a.flags & GENRANK_ATTN_TIME_BUCKET) {
+    if (a.n_time_bounds < 0 || a.n_time_bounds > 1024) return GENRANK_E_SHAPE;
+    if (a.n_time_bounds > 0 && !a.time_bounds) return GENRANK_E_ARG;
+  }
+  return GENRANK_OK;
+}
+
 // GEMM: C = A W^T (A [M, K], W [N, K]) with an epilogue
 genrank_status launch_gemm_nt(int dtype, const void* A, int64_t lda, const void* W, int64_t ldw,
                               void* C, int64_t ldc, int M, int N, int K, int epi, const void* R,

@@ -72,11 +72,16 @@ class DeviceTables:
 class DeviceLayer:
     """One block's weights on the device plus its ALiBi slopes (host)."""
 
-    def __init__(self, lw, slopes_pos, slopes_time, block, device="cuda"):
+    def __init__(self, lw, slopes_pos, slopes_time, block, device="cuda", attn_flags=0, time_bounds=None):
+        """attn_flags: ATTN_FULL_HISTORY and/or ATTN_TIME_BUCKET; time_bounds: the ascending
+        integer bucket edges (seconds) of the bucketed time term."""
         self.block = block
         self.wqkv = stored_to_device(lw.wqkv, device)
         self.wo = stored_to_device(lw.wo, device)
-        self.slopes = B.HostSlopes(slopes_pos, slopes_time)
+        self.time_bounds = None
+        if time_bounds is not None:
+            self.time_bounds = torch.as_tensor(np.ascontiguousarray(time_bounds, np.int64)).to(device)
+        self.slopes = B.HostSlopes(slopes_pos, slopes_time, attn_flags, self.time_bounds)
         if block == B.BLOCK_PRENORM:
             self.w1 = stored_to_device(lw.w1, device)
             self.w2 = stored_to_device(lw.w2, device)

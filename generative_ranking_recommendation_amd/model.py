@@ -29,10 +29,12 @@ class GenRank:
         self._ws = {}
 
     @classmethod
-    def from_host(cls, cfg, tables, weights, slopes_pos, slopes_time, device="cuda"):
+    def from_host(cls, cfg, tables, weights, slopes_pos, slopes_time, device="cuda", attn_flags=0,
+                  time_bounds=None):
         block = B.BLOCK_PRENORM if cfg.block == "prenorm" else B.BLOCK_ATTN_ONLY
         dt = DeviceTables(tables, device)
-        layers = [DeviceLayer(lw, slopes_pos, slopes_time, block, device) for lw in weights.layers]
+        layers = [DeviceLayer(lw, slopes_pos, slopes_time, block, device, attn_flags, time_bounds)
+                  for lw in weights.layers]
         head = DeviceHead(weights, device) if cfg.block == "prenorm" else None
         return cls(dt, layers, cfg.H, head, device)
 

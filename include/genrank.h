@@ -130,10 +130,22 @@ typedef struct {
  * -slopes_pos[h]*|p_i - p_j| - slopes_time[h]*|tau_i - tau_j|, p the position id (all
  * candidates of a request share p = N_u) and tau the timestamp in seconds relative to
  * the user's first history timestamp ([GR-zh] section 1.4.2, ALiBi score; [FR-en]
- * section 7.2.2, position-and-time bias). */
+ * section 7.2.2, position-and-time bias).
+ * flags (0 = the default above and the causal history mask):
+ *   GENRANK_ATTN_FULL_HISTORY: history queries see every history key (the fully visible
+ *     mask over the historical positions, [GR-zh] section 1.3.1); candidates unchanged.
+ *   GENRANK_ATTN_TIME_BUCKET: the time term is -slopes_time[h]*bucket(|tau_i - tau_j|),
+ *     bucket(g) = #{k : time_bounds[k] <= g} ([GR-zh] section 1.4.2, -m_t bucket(t_i - t_j);
+ *     the request-gap bucketing of the time embedding).  time_bounds: DEVICE int64
+ *     [n_time_bounds], non-decreasing, n_time_bounds <= 1024. */
+#define GENRANK_ATTN_FULL_HISTORY 1
+#define GENRANK_ATTN_TIME_BUCKET 2
 typedef struct {
-  const float* slopes_pos;  /* host [H] */
-  const float* slopes_time; /* host [H] */
+  const float* slopes_pos;    /* host [H] */
+  const float* slopes_time;   /* host [H] */
+  int32_t flags;              /* GENRANK_ATTN_* */
+  int32_t n_time_bounds;      /* GENRANK_ATTN_TIME_BUCKET only */
+  const int64_t* time_bounds; /* device, GENRANK_ATTN_TIME_BUCKET only */
 } genrank_alibi;
 
 /* Weights of one block.  GENRANK_BLOCK_ATTN_ONLY: y = Wo . attn(Wqkv . x).

@@ -310,6 +310,8 @@ class Tables:
 
 def _normal_stored(rng, shape, std, dtype, chunk_rows=65536) -> Stored:
     rows = shape[0]
+    if dtype not in ("f32", "bf16"):
+        raise ValueError(f"storage dtype must be 'f32' or 'bf16', not {dtype!r}")
     if dtype == "f32":
         return Stored(rng.standard_normal(shape, dtype=np.float32) * np.float32(std), "f32")
     bits = np.empty(shape, np.uint16)

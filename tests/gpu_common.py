@@ -58,7 +58,7 @@ def rel_err(got, want):
 
 def bf16_close(got, want, name=""):
     """bf16 bar for tensors that are not unit-scale by construction (activations of
-    N(0, 0.02)-initialised blocks, weight gradients): the benchmark spec's 2e-2 after rescaling
+    N(0, 0.02)-initialised blocks, weight gradients): the 2e-2 unit-scale bar after rescaling
     the tensor to unit max-magnitude, plus a norm-wise 1e-2 that a systematic error (a
     dropped term, a wrong sign, a wrong row) cannot meet."""
     got = np.asarray(got, np.float64)

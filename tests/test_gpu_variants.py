@@ -1,0 +1,297 @@
+"""GPU parity of the attention variants against the oracle: the fully visible history mask
+(every history query sees every history key, [GR-zh] section 1.3.1) and the bucketed time
+bias (-s'_h times the bucket of |t_i - t_j|, [GR-zh] section 1.4.2), alone and together;
+forward and backward, f32 and bf16; a training step of a two-layer model; and serving from
+cached history keys and values under each variant.
+
+Bars as for the default attention: f32 1e-5 of the tensor's max magnitude; bf16 outputs
+2e-2 absolute on unit-scale q, k, v (the log-sum-exp too); bf16 gradients and block
+outputs ``bf16_close``.  The bucketed cases use strong time slopes (0.02 .. 0.3 per
+bucket), so a wrong bucket moves a score by far more than the bar."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from common import oracle_indices, oracle_layers, oracle_head, oracle_tables
+from gpu_common import (DEV, DeviceInputs, GenRank, batch_struct, bf16_close, custom_batch, gpu_slopes,
+                        random_qkv, say, to_numpy, unit_close)
+from generative_ranking_recommendation_amd import binding as B
+from generative_ranking_recommendation_amd.device import stored_to_device, to_device
+
+pytestmark = pytest.mark.gpu
+
+STRONG = dict(slopes_pos=(0.5, 0.25, 0.125, 0.0625), slopes_time=(0.3, 0.1, 0.05, 0.02))
+
+
+def _edges(kind, cfg):
+    if kind is None:
+        return None
+    if kind == "rt":
+        return synth.rt_boundaries(cfg.n_rt)
+    if kind == "none":
+        return np.zeros(0, np.int64)
+    if kind == "max":  # 1024 ascending edges, spread over the gaps the batches hold
+        rng = np.random.default_rng(3)
+        return np.cumsum(rng.integers(1, 9000, 1024)).astype(np.int64)
+    raise ValueError(kind)
+
+
+# (name, flags, oracle history, edge kind, strong slopes)
+VARIANTS = [
+    ("full", B.ATTN_FULL_HISTORY, "full", None, False),
+    ("bucket", B.ATTN_TIME_BUCKET, "causal", "rt", True),
+    ("both", B.ATTN_FULL_HISTORY | B.ATTN_TIME_BUCKET, "full", "rt", True),
+]
+
+
+def _cfg(name, var, **kw):
+    if not var[4]:
+        return synth.make_config(name, **kw)
+    H = synth.make_config(name).H
+    return synth.make_config(name, **kw, **{k: v[:H] for k, v in STRONG.items()})
+
+
+def _slopes(cfg, flags, tb):
+    sp, st = gpu_slopes(cfg)
+    tbt = torch.as_tensor(tb).to(DEV) if tb is not None else None
+    return B.HostSlopes(sp, st, flags, tbt)
+
+
+def _oracle_attn(cfg, batch, qkv64, history, tb, users=None):
+    idx = oracle.token_indices(batch.hist_offsets, batch.hist_actions, batch.hist_ts, batch.req_ts,
+                               batch.m, cfg.n_action, cfg.n_pos, cfg.n_ri, synth.rt_boundaries(cfg.n_rt),
+                               users=users)
+    sp, st = gpu_slopes(cfg)
+    sp, st = np.asarray(sp, np.float64), np.asarray(st, np.float64)
+    d, H = cfg.d, cfg.H
+    q, k, v = (qkv64[:, i * d:(i + 1) * d].reshape(-1, H, d // H) for i in range(3))
+    o, lse = oracle.attn_fwd(q, k, v, batch.hist_offsets, batch.m, idx["pos"], idx["tau"], sp, st,
+                             users=users, history=history, time_bounds=tb)
+    return o.reshape(-1, d), lse, idx
+
+
+def _gpu_fwd(cfg, batch, qkv_st, flags, tb):
+    inp = DeviceInputs(batch, DEV)
+    T, d = inp.rows, cfg.d
+    qkv = stored_to_device(qkv_st, DEV)
+    o = torch.full((T, d), float("nan"), dtype=qkv.dtype, device=DEV)
+    lse = torch.full((T, cfg.H), float("nan"), dtype=torch.float32, device=DEV)
+    sl = _slopes(cfg, flags, tb)
+    es = qkv.element_size()
+    p = qkv.data_ptr()
+    B.genrank_attn_fwd(batch_struct(cfg, inp), inp.hist_offsets, inp.hist_ts, inp.req_ts, sl, p, p + d * es,
+                       p + 2 * d * es, 3 * d, o, d, lse)
+    torch.cuda.synchronize()
+    return to_numpy(o), lse.cpu().numpy().astype(np.float64), (inp, qkv, o, lse, sl)
+
+
+@pytest.mark.parametrize("var", VARIANTS, ids=[v[0] for v in VARIANTS])
+def test_variant_fwd_f32(var):
+    say(f"variants: fwd f32 {var[0]}")
+    cfg = _cfg("tiny_fp32", var, m=5)
+    batch = custom_batch(cfg, [16, 0, 40, 3, 1], seed=6)
+    tb = _edges(var[3], cfg)
+    st, q64 = random_qkv(batch.total_rows, cfg.d, cfg.dtype, seed=21)
+    got, glse, _ = _gpu_fwd(cfg, batch, st, var[1], tb)
+    want, wlse, _ = _oracle_attn(cfg, batch, q64, var[2], tb)
+    assert np.abs(got - want).max() <= 1e-5 * max(1.0, np.abs(want).max())
+    assert np.abs(glse - wlse).max() <= 1e-5 * max(1.0, np.abs(wlse).max())
+
+
+@pytest.mark.parametrize("var", VARIANTS, ids=[v[0] for v in VARIANTS])
+@pytest.mark.parametrize("lengths,m", [
+    ([0, 1, 2, 63, 64, 65, 127, 128, 129, 480], 5),
+    ([700, 3, 513, 64], 21),      # histories beyond one bias chunk (512 keys)
+    ([37, 64], 0),
+])
+def test_variant_fwd_bf16(var, lengths, m):
+    say(f"variants: fwd bf16 {var[0]} lengths={lengths} m={m}")
+    cfg = _cfg("infer_1layer_bf16", var, m=m)
+    batch = custom_batch(cfg, lengths, seed=5)
+    tb = _edges(var[3], cfg)
+    st, q64 = random_qkv(batch.total_rows, cfg.d, cfg.dtype, seed=7)
+    got, glse, _ = _gpu_fwd(cfg, batch, st, var[1], tb)
+    want, wlse, _ = _oracle_attn(cfg, batch, q64, var[2], tb)
+    assert np.isfinite(got).all()
+    assert np.abs(got - want).max() <= 2e-2
+    assert np.abs(glse - wlse).max() <= 2e-2
+
+
+@pytest.mark.parametrize("kind", ["none", "max"])
+def test_bucket_edge_counts_bf16(kind):
+    """No edges (every gap in bucket 0: the time term vanishes) and the largest edge count."""
+    say(f"variants: fwd bf16 bucket edges={kind}")
+    var = VARIANTS[1]
+    cfg = _cfg("infer_1layer_bf16", var, m=9)
+    batch = custom_batch(cfg, [300, 0, 65, 480], seed=15)
+    tb = _edges(kind, cfg)
+    st, q64 = random_qkv(batch.total_rows, cfg.d, cfg.dtype, seed=17)
+    got, glse, _ = _gpu_fwd(cfg, batch, st, var[1], tb)
+    want, wlse, _ = _oracle_attn(cfg, batch, q64, var[2], tb)
+    assert np.abs(got - want).max() <= 2e-2
+    assert np.abs(glse - wlse).max() <= 2e-2
+
+
+def test_full_history_sampled_full_size():
+    """The fully visible mask on the full 256-user inference batch; 4 users checked."""
+    say("variants: fwd bf16 full history, full infer batch, sampled users")
+    var = VARIANTS[0]
+    cfg = _cfg("infer_1layer_bf16", var)
+    batch = synth.make_batch(cfg)
+    st, q64 = random_qkv(batch.total_rows, cfg.d, cfg.dtype, seed=12)
+    got, glse, _ = _gpu_fwd(cfg, batch, st, var[1], None)
+    users = [0, 77, 200, 255]
+    want, wlse, idx = _oracle_attn(cfg, batch, q64, var[2], None, users=users)
+    rows = np.nonzero(idx["act"] >= 0)[0]
+    assert np.abs(got[rows] - want[rows]).max() <= 2e-2
+    assert np.abs(glse[rows] - wlse[rows]).max() <= 2e-2
+    assert np.isfinite(got).all()
+
+
+def _bwd_case(cfg, batch, var, seed, cand_only):
+    d, H = cfg.d, cfg.H
+    T = batch.total_rows
+    tb = _edges(var[3], cfg)
+    st, q64 = random_qkv(T, d, cfg.dtype, seed=seed)
+    dst = synth.inputs.normal_array((T, d), std=1.0, seed=seed + 1, dtype=cfg.dtype)
+    do64 = dst.f32().astype(np.float64)
+    if cand_only:
+        do64[:batch.total_hist] = 0.0
+        if cfg.dtype == "bf16":
+            dst.bits[:batch.total_hist] = 0
+        else:
+            dst._f32[:batch.total_hist] = 0.0
+    idx = oracle.token_indices(batch.hist_offsets, batch.hist_actions, batch.hist_ts, batch.req_ts,
+                               batch.m, cfg.n_action, cfg.n_pos, cfg.n_ri, synth.rt_boundaries(cfg.n_rt))
+    sp, stt = (np.asarray(a, np.float64) for a in gpu_slopes(cfg))
+    q, k, v = (q64[:, i * d:(i + 1) * d].reshape(-1, H, d // H) for i in range(3))
+    dq, dk, dv = oracle.attn_bwd(q, k, v, do64.reshape(-1, H, d // H), batch.hist_offsets, batch.m,
+                                 idx["pos"], idx["tau"], sp, stt, history=var[2], time_bounds=tb)
+    want = np.concatenate([t.reshape(T, d) for t in (dq, dk, dv)], 1)
+    _, _, (inp, qkv, o, lse, sl) = _gpu_fwd(cfg, batch, st, var[1], tb)
+    bt = batch_struct(cfg, inp)
+    dout = stored_to_device(dst, DEV)
+    es = qkv.element_size()
+    dqkv = torch.full((T, 3 * d), float("nan"), dtype=qkv.dtype, device=DEV)
+    nws = B.genrank_workspace_size(B.OP_ATTN_BWD, bt)
+    ws = torch.empty(nws, dtype=torch.uint8, device=DEV)
+    p, g = qkv.data_ptr(), dqkv.data_ptr()
+    B.genrank_attn_bwd(bt, inp.hist_offsets, inp.hist_ts, inp.req_ts, sl, p, p + d * es, p + 2 * d * es,
+                       3 * d, o, dout, d, lse, g, g + d * es, g + 2 * d * es, 3 * d, cand_only, ws, nws)
+    torch.cuda.synchronize()
+    return to_numpy(dqkv), want
+
+
+@pytest.mark.parametrize("var", VARIANTS, ids=[v[0] for v in VARIANTS])
+@pytest.mark.parametrize("cand_only", [0, 1])
+def test_variant_bwd_f32(var, cand_only):
+    say(f"variants: bwd f32 {var[0]} cand_only={cand_only}")
+    cfg = _cfg("tiny_fp32", var, m=5)
+    batch = custom_batch(cfg, [16, 0, 40, 3], seed=6)
+    got, want = _bwd_case(cfg, batch, var, 31, cand_only)
+    assert np.abs(got - want).max() <= 1e-5 * max(1.0, np.abs(want).max())
+
+
+@pytest.mark.parametrize("var", VARIANTS, ids=[v[0] for v in VARIANTS])
+@pytest.mark.parametrize("cand_only", [0, 1])
+def test_variant_bwd_bf16(var, cand_only):
+    """Histories past 512 keys, an empty and a one-action history, a ragged 64-row tile and
+    70 candidates."""
+    say(f"variants: bwd bf16 {var[0]} cand_only={cand_only}")
+    cfg = _cfg("train2_bf16", var, m=70)
+    batch = custom_batch(cfg, [700, 0, 1, 129, 300], seed=9)
+    got, want = _bwd_case(cfg, batch, var, 43, cand_only)
+    d = cfg.d
+    for i, name in enumerate(("dq", "dk", "dv")):
+        bf16_close(got[:, i * d:(i + 1) * d], want[:, i * d:(i + 1) * d], name)
+
+
+def _geom(cfg, batch, idx, history, tb):
+    sp, st = (np.asarray(a, np.float64) for a in gpu_slopes(cfg))
+    return {"hist_offsets": batch.hist_offsets, "m": batch.m, "pos": idx["pos"], "tau": idx["tau"],
+            "slopes_pos": sp, "slopes_time": st, "history": history, "time_bounds": tb}
+
+
+@pytest.mark.parametrize("var", VARIANTS, ids=[v[0] for v in VARIANTS])
+def test_variant_train_step_f32(var):
+    """Two pre-norm blocks, BCE at the candidates, every gradient against the oracle's."""
+    say(f"variants: train step f32 {var[0]}")
+    cfg = _cfg("tiny_fp32", var, block="prenorm", layers=2)
+    batch = custom_batch(cfg, [16, 9, 0], seed=1)
+    tables, weights = synth.make_tables(cfg), synth.make_weights(cfg)
+    tb = _edges(var[3], cfg)
+    labels = synth.make_labels(cfg, B=batch.B)
+    idx = oracle_indices(cfg, batch, tables)
+    x0 = oracle.embed_sum(oracle_tables(tables), batch.hist_items, batch.cand_items, idx)
+    geom = _geom(cfg, batch, idx, var[2], tb)
+    layers, head = oracle_layers(weights), oracle_head(weights)
+    xf, logits, caches = oracle.model_fwd(x0, layers, cfg.block, cfg.H, geom, head)
+    wl = oracle.bce_loss(logits, labels)
+    _, lg, hg = oracle.model_bwd(oracle.bce_loss_bwd(logits, labels), xf, layers, cfg.block, cfg.H, geom,
+                                 caches, head)
+    sp, st = gpu_slopes(cfg)
+    model = GenRank.from_host(cfg, tables, weights, sp, st, DEV, attn_flags=var[1], time_bounds=tb)
+    inp = DeviceInputs(batch, DEV)
+    gl, glog, grads = model.train_step(inp, to_device(labels, DEV, np.float32))
+    torch.cuda.synchronize()
+    assert abs(float(gl.item()) - wl) <= 1e-5
+    assert np.abs(to_numpy(glog) - logits).max() <= 1e-5 * max(1.0, np.abs(logits).max())
+    for li in range(cfg.layers):
+        for k, v in lg[li].items():
+            got = to_numpy(grads["layers"][li][k])
+            assert np.abs(got - v).max() <= 1e-5 * max(np.abs(v).max(), 1e-3), f"layer{li}.{k}"
+    for k in ("w_head", "b_head", "g_final"):
+        got = to_numpy(grads[k])
+        assert np.abs(got - hg[k]).max() <= 1e-5 * max(np.abs(hg[k]).max(), 1e-3), k
+
+
+@pytest.mark.parametrize("var", VARIANTS, ids=[v[0] for v in VARIANTS])
+def test_variant_train_step_bf16(var):
+    """train2_bf16 shapes (2 blocks, d = 256, 4 heads, m = 32) on 4 users."""
+    say(f"variants: train step bf16 {var[0]}")
+    cfg = _cfg("train2_bf16", var)
+    batch = synth.make_batch(cfg, B=4)
+    tables, weights = synth.make_tables(cfg), synth.make_weights(cfg)
+    tb = _edges(var[3], cfg)
+    labels = synth.make_labels(cfg, B=batch.B)
+    idx = oracle_indices(cfg, batch, tables)
+    x0 = oracle.embed_sum(oracle_tables(tables), batch.hist_items, batch.cand_items, idx)
+    geom = _geom(cfg, batch, idx, var[2], tb)
+    layers, head = oracle_layers(weights), oracle_head(weights)
+    xf, logits, caches = oracle.model_fwd(x0, layers, cfg.block, cfg.H, geom, head)
+    wl = oracle.bce_loss(logits, labels)
+    _, lg, hg = oracle.model_bwd(oracle.bce_loss_bwd(logits, labels), xf, layers, cfg.block, cfg.H, geom,
+                                 caches, head)
+    sp, st = gpu_slopes(cfg)
+    model = GenRank.from_host(cfg, tables, weights, sp, st, DEV, attn_flags=var[1], time_bounds=tb)
+    inp = DeviceInputs(batch, DEV)
+    gl, glog, grads = model.train_step(inp, to_device(labels, DEV, np.float32))
+    torch.cuda.synchronize()
+    unit_close([float(gl.item())], [wl], "loss")
+    unit_close(to_numpy(glog), logits, "logits")
+    for li in range(cfg.layers):
+        for k, v in lg[li].items():
+            bf16_close(to_numpy(grads["layers"][li][k]), v, f"layer{li}.{k}")
+    for k in ("w_head", "b_head", "g_final"):
+        bf16_close(to_numpy(grads[k]), hg[k], k)
+
+
+@pytest.mark.parametrize("var", VARIANTS, ids=[v[0] for v in VARIANTS])
+def test_variant_score_equals_forward(var):
+    """Serving from cached history keys and values reproduces the full forward's candidate
+    rows bit for bit under each variant (history rows still never see candidates)."""
+    say(f"variants: score vs forward {var[0]}")
+    cfg = _cfg("train2_bf16", var, m=40)
+    batch = custom_batch(cfg, [64, 300, 700, 5, 0], seed=9)
+    sp, st = gpu_slopes(cfg)
+    model = GenRank.from_host(cfg, synth.make_tables(cfg), synth.make_weights(cfg), sp, st, DEV,
+                              attn_flags=var[1], time_bounds=_edges(var[3], cfg))
+    inp = DeviceInputs(batch, DEV)
+    x_full, logits_full = model.forward(inp)
+    x_c, logits_c = model.score(inp, model.prefill(inp))
+    torch.cuda.synchronize()
+    Th = inp.total_hist
+    assert torch.equal(x_c, x_full[Th:]), "candidate rows differ"
+    assert torch.equal(logits_c, logits_full), "logits differ"
