@@ -37,6 +37,18 @@ KERNEL_SOURCES = {"embed_sum": "embed.hip", "attn_fwd": "attn_fwd.hip", "qkv_gem
                   "out_gemm": "gemm.hip"}
 
 
+# --attn-variant -> genrank_alibi.flags (1 = fully visible history, 2 = bucketed time term)
+VARIANT_FLAGS = {"causal": 0, "full": 1, "bucket": 2, "both": 3}
+
+
+def variant_args(args, cfg):
+    """(flags, bucket edges or None) of the requested ALiBi variant; the edges are the
+    request-gap bucket edges of the workload's time table."""
+    import synth
+    flags = VARIANT_FLAGS[args.attn_variant]
+    return flags, (synth.rt_boundaries(cfg.n_rt) if flags & 2 else None)
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -51,6 +63,9 @@ def parse():
                    help="CPU-oracle baseline budget (0 disables the leg)")
     p.add_argument("--kv-cache", action="store_true",
                    help="serving: score the candidates against the users' cached history keys/values")
+    p.add_argument("--attn-variant", default="causal", choices=sorted(VARIANT_FLAGS),
+                   help="ALiBi variant: causal history (default), fully visible history, bucketed "
+                        "time bias, or both")
     p.add_argument("--calibrate-copy-mb", type=int, default=0,
                    help="also run one plain device copy of this many MiB (counter calibration)")
     return p.parse_args()
@@ -78,8 +93,9 @@ def load_traffic(workload):
     return out
 
 
-def cpu_baseline(cfg, batch, tables, weights, budget_s):
-    """The fp64 CPU oracle on the first users of the same batch, for about budget_s seconds."""
+def cpu_baseline(cfg, batch, tables, weights, budget_s, variant=(0, None)):
+    """The fp64 CPU oracle on the first users of the same batch, for about budget_s seconds
+    (``variant``: the ALiBi variant's flags and bucket edges)."""
     import numpy as np
     try:
         from threadpoolctl import threadpool_info
@@ -99,7 +115,9 @@ def cpu_baseline(cfg, batch, tables, weights, budget_s):
         c1 = cfg.replace(B=1)
         idx = oracle_indices(c1, sub, tables)
         x = oracle.embed_sum(tabs, sub.hist_items, sub.cand_items, idx)
-        oracle.model_fwd(x, layers, cfg.block, cfg.H, oracle_geom(c1, sub, idx), head)
+        geom = oracle_geom(c1, sub, idx)
+        geom.update(history="full" if variant[0] & 1 else "causal", time_bounds=variant[1])
+        oracle.model_fwd(x, layers, cfg.block, cfg.H, geom, head)
         users += 1
     dt = time.perf_counter() - t0
     return {"value": users * cfg.m / dt, "unit": "candidates/s", "cores": int(threads),
@@ -208,7 +226,7 @@ def bench_hstu(args):
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline_train(cfg, batch, tables, weights, labels, budget_s):
+def cpu_baseline_train(cfg, batch, tables, weights, labels, budget_s, variant=(0, None)):
     """The fp64 CPU oracle's training step (forward, BCE at candidates, backward, table
     gradients) on the first users of the same batch, for about budget_s seconds."""
     import numpy as np
@@ -229,6 +247,7 @@ def cpu_baseline_train(cfg, batch, tables, weights, labels, budget_s):
         idx = oracle_indices(c1, sub, tables)
         x = oracle.embed_sum(tabs, sub.hist_items, sub.cand_items, idx)
         geom = oracle_geom(c1, sub, idx)
+        geom.update(history="full" if variant[0] & 1 else "causal", time_bounds=variant[1])
         xf, logits, caches = oracle.model_fwd(x, layers, cfg.block, cfg.H, geom, head)
         lab = labels[users * cfg.m:(users + 1) * cfg.m]
         oracle.bce_loss(logits, lab)
@@ -267,7 +286,8 @@ def bench_train(args, cfg):
     sp, st = alibi_slopes(cfg.H, cfg.time_ratio)
     dev = "cuda"
     torch.cuda.set_device(0)
-    model = GenRank.from_host(cfg, tables, weights, sp, st, dev)
+    vflags, vedges = variant_args(args, cfg)
+    model = GenRank.from_host(cfg, tables, weights, sp, st, dev, attn_flags=vflags, time_bounds=vedges)
     inp = DeviceInputs(batch, dev)
     lab = to_device(labels, dev, np.float32)
     T, d, H, m = inp.rows, cfg.d, cfg.H, cfg.m
@@ -292,7 +312,7 @@ def bench_train(args, cfg):
     dqkv = torch.empty((T, 3 * d), dtype=torch.bfloat16, device=dev)
     nws = B.genrank_workspace_size(B.OP_ATTN_BWD, bt)
     ws = torch.empty(nws, dtype=torch.uint8, device=dev)
-    sl = B.HostSlopes(sp, st)
+    sl = model.layers[0].slopes
     stream = torch.cuda.current_stream()
     p, q = qkv.data_ptr(), dqkv.data_ptr()
     B.genrank_attn_fwd(bt, inp.hist_offsets, inp.hist_ts, inp.req_ts, sl, p, p + 2 * d, p + 4 * d, 3 * d,
@@ -312,8 +332,8 @@ def bench_train(args, cfg):
     torch.cuda.synchronize()
     t_us = float(np.mean([ev[k].elapsed_time(ev[k + 1]) for k in range(args.steps)])) * 1e3
     lengths = inp.lengths
-    flops = W.attention_bwd_flops(lengths, m, d)
-    flops_rc = W.attention_bwd_flops(lengths, m, d, recompute=True)
+    flops = W.attention_bwd_flops(lengths, m, d, full_history=bool(vflags & 1))
+    flops_rc = W.attention_bwd_flops(lengths, m, d, recompute=True, full_history=bool(vflags & 1))
     nbytes = W.attention_bwd_hbm_floor_bytes(T, d, H)
     if nbytes / (PEAK_HBM_GBS * 1e9) >= flops / (PEAK_BF16_TFLOPS * 1e12):
         bound, achieved, peak, unit = "hbm", nbytes / (t_us * 1e-6) / 1e9, PEAK_HBM_GBS, "GB/s"
@@ -326,7 +346,7 @@ def bench_train(args, cfg):
     cpu = None
     if args.cpu_seconds > 0:
         log("CPU oracle baseline ...")
-        cpu = cpu_baseline_train(cfg, batch, tables, weights, labels, args.cpu_seconds)
+        cpu = cpu_baseline_train(cfg, batch, tables, weights, labels, args.cpu_seconds, (vflags, vedges))
         log(f"CPU oracle: {cpu['value']:.1f} candidates/s on {cpu['cores']} threads")
     out = {
         "metric": "candidates trained/sec (GenRank fwd + bwd, bf16)",
@@ -337,7 +357,7 @@ def bench_train(args, cfg):
         "data": "synthetic (seeded; Zipf(1.1) item ids, jagged histories, Bernoulli(0.1) labels)",
         "config": {"workload": cfg.name, "users": inp.B, "candidates_per_user": m,
                    "history": f"U[{cfg.hist_min},{cfg.hist_max}]", "rows": T, "d": d, "heads": H,
-                   "layers": cfg.layers, "block": cfg.block},
+                   "layers": cfg.layers, "block": cfg.block, "attn_variant": args.attn_variant},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernels": {"attn_bwd": {"time_us": round(t_us, 2), "bound": bound, "achieved": round(achieved, 2),
@@ -372,7 +392,8 @@ def bench_serve(args, cfg):
     sp, st = alibi_slopes(cfg.H, cfg.time_ratio)
     dev = "cuda"
     torch.cuda.set_device(0)
-    model = GenRank.from_host(cfg, tables, weights, sp, st, dev)
+    vflags, vedges = variant_args(args, cfg)
+    model = GenRank.from_host(cfg, tables, weights, sp, st, dev, attn_flags=vflags, time_bounds=vedges)
     inp = DeviceInputs(batch, dev)
     T_h, d, H, m = inp.total_hist, cfg.d, cfg.H, cfg.m
     Tc = inp.B * m
@@ -439,6 +460,11 @@ def bench_serve(args, cfg):
     kernels["attn_cached"].update({"bound": "hbm", "achieved": round(achieved, 2), "floor_bytes": int(nbytes),
                                    "flops": int(flops),
                                    "tflops": round(flops / (t_us * 1e-6) / 1e12, 2)})
+    cpu = None
+    if args.cpu_seconds > 0:
+        log("CPU oracle baseline (the oracle's full forward: it keeps no cache) ...")
+        cpu = cpu_baseline(cfg, batch, tables, weights, args.cpu_seconds, (vflags, vedges))
+        log(f"CPU oracle: {cpu['value']:.1f} candidates/s on {cpu['cores']} threads")
     out = {
         "metric": "candidates scored/sec with cached history K/V (GenRank fwd, bf16)",
         "value": round(Tc / (ms * 1e-3), 1),
@@ -447,10 +473,11 @@ def bench_serve(args, cfg):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype,
         "data": "synthetic (seeded; Zipf(1.1) item ids, jagged histories, runs of 1-4 actions per request)",
         "config": {"workload": cfg.name, "mode": "cached history", "users": inp.B, "candidates_per_user": m,
-                   "history": f"U[{cfg.hist_min},{cfg.hist_max}]", "history_rows": T_h, "d": d, "heads": H},
+                   "history": f"U[{cfg.hist_min},{cfg.hist_max}]", "history_rows": T_h, "d": d, "heads": H,
+                   "attn_variant": args.attn_variant},
         "prefill_ms": round(prefill_ms, 4),
         "roofline": roofline,
-        "cpu_baseline": None,
+        "cpu_baseline": cpu,
         "kernels": kernels,
     }
     print(json.dumps(out), flush=True)
@@ -496,7 +523,8 @@ def main():
 
     dev = "cuda"
     torch.cuda.set_device(0)
-    model = GenRank.from_host(cfg, tables, weights, sp, st, dev)
+    vflags, vedges = variant_args(args, cfg)
+    model = GenRank.from_host(cfg, tables, weights, sp, st, dev, attn_flags=vflags, time_bounds=vedges)
     inp = DeviceInputs(batch, dev)
     T, d, H, m = inp.rows, cfg.d, cfg.H, cfg.m
     bt = model.batch(inp)
@@ -587,7 +615,7 @@ def main():
     if decomposed:
         # attention: algorithmic flops over allowed pairs, and the floor bytes (Q, K, V read
         # once, O and the log-sum-exp written once); the bound is whichever needs longer at peak
-        attn_flops = W.attention_fwd_flops(lengths, m, d)
+        attn_flops = W.attention_fwd_flops(lengths, m, d, full_history=bool(vflags & 1))
         attn_bytes = T * 3 * d * es + T * d * es + T * H * 4
         peak_f = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
         if attn_bytes / (PEAK_HBM_GBS * 1e9) >= attn_flops / (peak_f * 1e12):
@@ -620,7 +648,7 @@ def main():
     cpu = None
     if args.cpu_seconds > 0:
         log("CPU oracle baseline ...")
-        cpu = cpu_baseline(cfg, batch, tables, weights, args.cpu_seconds)
+        cpu = cpu_baseline(cfg, batch, tables, weights, args.cpu_seconds, (vflags, vedges))
         log(f"CPU oracle: {cpu['value']:.1f} candidates/s on {cpu['cores']} threads")
 
     cands = inp.B * m
@@ -639,7 +667,7 @@ def main():
         "data": "synthetic (seeded; Zipf(1.1) item ids, jagged histories, runs of 1-4 actions per request)",
         "config": {"workload": cfg.name, "users": inp.B, "candidates_per_user": m,
                    "history": f"U[{cfg.hist_min},{cfg.hist_max}]", "rows": T, "d": d, "heads": H,
-                   "layers": cfg.layers, "block": cfg.block},
+                   "layers": cfg.layers, "block": cfg.block, "attn_variant": args.attn_variant},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernels": kernels,

@@ -133,7 +133,7 @@ genrank_status check_layer_weights(const genrank_batch* b, const genrank_layer_w
     return GENRANK_E_ARG;
   }
   if (b->d % 64 != 0 && b->dtype == GENRANK_BF16) return GENRANK_E_SHAPE;
-  return check_alibi_variant(w->alibi);
+  return check_alibi_variant(w->alibi, b->H);
 }
 
 #define GR_TRY(expr)                         \
@@ -421,7 +421,7 @@ genrank_status genrank_attn_fwd_cached(const genrank_batch* b, const int32_t* of
   GR_TRY(check_batch(b));
   if (!offsets || !req || !alibi.slopes_pos || !alibi.slopes_time) return GENRANK_E_ARG;
   if ((b->total_hist > 0 && (!ts || !k_hist || !v_hist)) || !q || !k || !v || !o) return GENRANK_E_ARG;
-  GR_TRY(check_alibi_variant(alibi));
+  GR_TRY(check_alibi_variant(alibi, b->H));
   GR_TRY(check_cached_attn(b, q, k, v, ld_qkv, k_hist, v_hist, ld_hist, o, ld_o));
   return launch_attn_fwd_cached(b, offsets, ts, req, alibi, q, k, v, ld_qkv, k_hist, v_hist, ld_hist, o, ld_o,
                                 lse, S(stream));

@@ -288,6 +288,7 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(BwdMArgs a) {
   __shared__ __attribute__((aligned(16))) float sW[BWCH];
   __shared__ __attribute__((aligned(16))) int32_t sT[TBK ? BWCH : 4];
   __shared__ int32_t sTB[TBK ? ATTN_MAX_TIME_BOUNDS : 1];
+  __shared__ uint32_t sLUT[TBK ? BK_CELLS : 1];  // bucket table over the gap
 
   const int u = blockIdx.x / a.H;
   const int h = blockIdx.x - u * a.H;
@@ -448,6 +449,10 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(BwdMArgs a) {
   }
   asm volatile("" : "+v"(qf[0]), "+v"(qf[1]), "+v"(dof[0]), "+v"(dof[1]));
   __syncthreads();
+  if constexpr (TBK) {
+    bucket_table_build(sLUT, sTB, a.tb_p2, tid, 256);
+    __syncthreads();
+  }
 
   const int klim_min = (is_cand || FULL) ? N - 1 : q0;
   for (int it = 0; it < n_tiles; ++it) {
@@ -493,7 +498,7 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(BwdMArgs a) {
         } else {
           // fully visible: -|w_j - w_i|; bucketed time: - s' bucket(|t_i - t_j|)
           arg = s[kb][i] * a.scale2 + (FULL ? -fabsf(wv[i] - w_i) : wv[i] - w_i) - lse2;
-          if constexpr (TBK) arg -= st2 * static_cast<float>(bucket_search(sTB, a.tb_p2, abs(tq - tkv[i])));
+          if constexpr (TBK) arg -= st2 * static_cast<float>(bucket_lookup(sLUT, sTB, a.tb_p2, abs(tq - tkv[i])));
         }
         float p = __builtin_amdgcn_exp2f(arg);
         if (masked && base + kb * 16 + g4 * 4 + i > k_lim) p = 0.f;
@@ -534,11 +539,15 @@ __global__ void __launch_bounds__(256) attn_bwd_dkv_kernel(BwdMArgs a) {
   __shared__ __attribute__((aligned(16))) bf16_t sOt[2][DHB * PLD];
   __shared__ __attribute__((aligned(16))) float sC[2][TB];
   __shared__ __attribute__((aligned(16))) float sD[2][TB];
-  // variants: sC holds w_i alone and sL the query's lse (fully visible history), sTq the
-  // query's time relative to the tile's reference (bucketed time), sTB the bucket edges
-  __shared__ __attribute__((aligned(16))) float sL[FULL ? 2 : 1][FULL ? TB : 4];
+  // variants: with the fully visible history sC holds w_i alone and sL the query's lse (with
+  // the bucketed time term as well, w_i is the position term, formed in registers, and sC
+  // holds the lse); sTq the query's time relative to the tile's reference (bucketed time);
+  // sTB the bucket edges
+  constexpr bool SPLIT_L = FULL && !TBK;
+  __shared__ __attribute__((aligned(16))) float sL[SPLIT_L ? 2 : 1][SPLIT_L ? TB : 4];
   __shared__ __attribute__((aligned(16))) int32_t sTq[TBK ? 2 : 1][TBK ? TB : 4];
   __shared__ int32_t sTB[TBK ? ATTN_MAX_TIME_BOUNDS : 1];
+  __shared__ uint32_t sLUT[TBK ? BK_CELLS : 1];  // bucket table over the gap
 
   const int u = blockIdx.x / a.H;
   const int h = blockIdx.x - u * a.H;
@@ -610,7 +619,7 @@ __global__ void __launch_bounds__(256) attn_bwd_dkv_kernel(BwdMArgs a) {
         w_i = TBK ? sp2 * static_cast<float>(ql) : sp2 * static_cast<float>(ql) + st2 * static_cast<float>(tq);
       }
       const float lse2 = a.lse[r * a.H + h] * LOG2E_B;
-      rc = FULL ? w_i : w_i + lse2;
+      rc = FULL ? (TBK ? lse2 : w_i) : w_i + lse2;
       rl = lse2;
       rt = tq;
       rd = a.delta[r * a.H + h];
@@ -622,7 +631,7 @@ __global__ void __launch_bounds__(256) attn_bwd_dkv_kernel(BwdMArgs a) {
     if (tid < TB) {
       sC[buf][tid] = rc;
       sD[buf][tid] = rd;
-      if constexpr (FULL) sL[buf][tid] = rl;
+      if constexpr (SPLIT_L) sL[buf][tid] = rl;
       if constexpr (TBK) sTq[buf][tid] = rt;
     }
   };
@@ -644,6 +653,10 @@ __global__ void __launch_bounds__(256) attn_bwd_dkv_kernel(BwdMArgs a) {
   }
   asm volatile("" : "+v"(kf[0]), "+v"(kf[1]), "+v"(vf[0]), "+v"(vf[1]));
   __syncthreads();
+  if constexpr (TBK) {
+    bucket_table_build(sLUT, sTB, a.tb_p2, tid, 256);
+    __syncthreads();
+  }
 
   for (int qi = 0; qi < n_qt; ++qi) {
     const int buf = qi & 1;
@@ -677,7 +690,7 @@ __global__ void __launch_bounds__(256) attn_bwd_dkv_kernel(BwdMArgs a) {
       const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
       float lv[4] = {0.f, 0.f, 0.f, 0.f};
       int32_t tv[4] = {0, 0, 0, 0};
-      if constexpr (FULL) {
+      if constexpr (SPLIT_L) {
         const float4 l4 = reinterpret_cast<const float4*>(sL[buf])[qb * 4 + g4];
         lv[0] = l4.x; lv[1] = l4.y; lv[2] = l4.z; lv[3] = l4.w;
       }
@@ -695,8 +708,15 @@ __global__ void __launch_bounds__(256) attn_bwd_dkv_kernel(BwdMArgs a) {
           arg = s[qb][i] * a.scale2 + w_j - cv[i];
         } else {
           // fully visible: -|w_j - w_i|; bucketed time: - s' bucket(|t_i - t_j|)
-          arg = FULL ? s[qb][i] * a.scale2 - fabsf(w_j - cv[i]) - lv[i] : s[qb][i] * a.scale2 + w_j - cv[i];
-          if constexpr (TBK) arg -= st2 * static_cast<float>(bucket_search(sTB, a.tb_p2, abs(tv[i] - tk)));
+          if constexpr (SPLIT_L) {
+            arg = s[qb][i] * a.scale2 - fabsf(w_j - cv[i]) - lv[i];
+          } else if constexpr (FULL) {  // and TBK: w_i = s (p_i - p_ref) = s ql on history tiles
+            const float w_i = t.cand ? 0.f : sp2 * static_cast<float>(ql);
+            arg = s[qb][i] * a.scale2 - fabsf(w_j - w_i) - cv[i];
+          } else {
+            arg = s[qb][i] * a.scale2 + w_j - cv[i];
+          }
+          if constexpr (TBK) arg -= st2 * static_cast<float>(bucket_lookup(sLUT, sTB, a.tb_p2, abs(tv[i] - tk)));
         }
         const float p = ok ? __builtin_amdgcn_exp2f(arg) : 0.f;
         s[qb][i] = p;

@@ -123,6 +123,7 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
   // bucketed time term: the chunk's key times relative to tau_ref, and the bucket edges
   __shared__ __attribute__((aligned(16))) int32_t sT[TBK ? WCHUNK : 4];
   __shared__ int32_t sTB[TBK ? ATTN_MAX_TIME_BOUNDS : 1];
+  __shared__ uint32_t sLUT[TBK ? BK_CELLS : 1];  // bucket table over the gap
 
   // Flat grid over (user, head, tile).  Workgroup w runs on XCD w % 8 as that XCD's
   // (w / 8)-th workgroup.  Each XCD owns the (user, head) pairs bh = x mod 8 and walks them
@@ -385,6 +386,10 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
 #pragma unroll
   for (int c = 0; c < QB; ++c) asm volatile("" : "+v"(qf[c][0]), "+v"(qf[c][1]));
   __syncthreads();
+  if constexpr (TBK) {
+    bucket_table_build(sLUT, sTB, a.tb_p2, threadIdx.x, NT);
+    __syncthreads();
+  }
   // a history query's own bias term w_i (its key lies in the first tile's bias chunk);
   // the row term of the bias, added back into the log-sum-exp at the end
   // (With the fully visible mask the query's slot may lie in an earlier chunk: its term is
@@ -491,7 +496,7 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
           for (int i = 0; i < 4; ++i) {
             float x = s[c][kb][i] * a.scale2 + (FULL ? -fabsf(wv[i] - w_i[c]) : wv[i]);
             if constexpr (TBK)
-              x -= st2 * static_cast<float>(bucket_search(sTB, a.tb_p2, abs(tq[c] - tkv[i])));
+              x -= st2 * static_cast<float>(bucket_lookup(sLUT, sTB, a.tb_p2, abs(tq[c] - tkv[i])));
             s[c][kb][i] = x;
           }
       }
@@ -705,7 +710,7 @@ genrank_status check_attn_args(const genrank_batch* b, const int32_t* offsets, c
   if (s != GENRANK_OK) return s;
   if (!offsets || !req || !alibi.slopes_pos || !alibi.slopes_time) return GENRANK_E_ARG;
   {
-    const genrank_status vs = check_alibi_variant(alibi);
+    const genrank_status vs = check_alibi_variant(alibi, b->H);
     if (vs != GENRANK_OK) return vs;
   }
   if (b->total_hist > 0 && !ts) return GENRANK_E_ARG;

@@ -97,6 +97,45 @@ __device__ __forceinline__ int bucket_search(const int32_t* b, int p2, int32_t g
   for (int step = p2 >> 1; step > 0; step >>= 1) pos += (b[pos + step - 1] <= g) ? step : 0;
   return pos + (b[pos] <= g ? 1 : 0);
 }
+// Bucket table over gaps g in [0, 2^24): one cell per integer below 2^BK_M, then 2^BK_M
+// cells per octave [2^e, 2^(e+1)) (the top BK_M bits after the leading one; cell width
+// 2^(e - BK_M)).  A cell is one 32-bit word: bits 0-10 lo = #{k : b_k < start}, bit 11 set
+// when the cell holds two or more edges, bits 12-30 the offset from the cell's start of
+// the one edge inside it (2^19 - 1 if none), so that bucket(g) = lo + (g - start >= offset).
+// Dense cells and gaps of 2^24 s or more fall back to bucket_search: exact for any edges.
+constexpr int BK_M = 5;
+constexpr int BK_CELLS = (25 - BK_M) << BK_M;  // 640
+constexpr uint32_t BK_DENSE = 1u << 11, BK_NONE = (1u << 19) - 1;
+// fill the table from the padded edges b (p2 entries, visible to every thread; at most 1024
+// edges); thread t of nt; the caller synchronises before the first lookup
+__device__ __forceinline__ void bucket_table_build(uint32_t* lut, const int32_t* b, int p2, int t, int nt) {
+  for (int c = t; c < BK_CELLS; c += nt) {
+    int32_t start, width;
+    if (c < (1 << BK_M)) {
+      start = c;
+      width = 1;
+    } else {
+      const int q = c >> BK_M, r = c & ((1 << BK_M) - 1);
+      start = ((1 << BK_M) + r) << (q - 1);
+      width = 1 << (q - 1);
+    }
+    const int lo = bucket_search(b, p2, start - 1);          // #{k : b_k < start}
+    const int hi = bucket_search(b, p2, start + width - 1);  // #{k : b_k < end}, end <= 2^24
+    const uint32_t off = hi == lo ? BK_NONE : static_cast<uint32_t>(b[lo] - start);  // < 2^18
+    lut[c] = static_cast<uint32_t>(lo) | (hi > lo + 1 ? BK_DENSE : 0u) | (off << 12);
+  }
+}
+__device__ __forceinline__ int bucket_lookup(const uint32_t* lut, const int32_t* b, int p2, int32_t g) {
+  const uint32_t fb = __float_as_uint(static_cast<float>(g));  // exact below 2^24
+  const bool big = g >= (1 << 24);
+  const int sh = max(static_cast<int>(fb >> 23) - (127 + BK_M), 0);  // log2 of the cell width
+  const int c = g < (1 << BK_M) ? g : static_cast<int>(fb >> (23 - BK_M)) - ((126 + BK_M) << BK_M);
+  const uint32_t e = lut[big ? 0 : c];
+  const uint32_t low = static_cast<uint32_t>(g) & ((1u << sh) - 1u);  // g - start
+  int bk = static_cast<int>(e & 0x7FFu) + (low >= (e >> 12) ? 1 : 0);
+  if (big || (e & BK_DENSE)) bk = bucket_search(b, p2, g);
+  return bk;
+}
 // the power of two that bucket_search takes for n edges (n <= ATTN_MAX_TIME_BOUNDS)
 inline int bucket_p2(int n) {
   int p2 = 1;

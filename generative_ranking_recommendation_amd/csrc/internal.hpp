@@ -76,9 +76,14 @@ genrank_status launch_hstu_attn_fwd(const genrank_batch* b, const int32_t* offse
                                     const void* v, int64_t ld_qkv, void* o, int64_t ld_o, float* lse,
                                     hipStream_t stream);
 
-// the ALiBi variant flags: known bits only; bucket edges present and at most 1024
-inline genrank_status check_alibi_variant(const genrank_alibi& a) {
+// the ALiBi variant flags: known bits only; bucket edges present and at most 1024; under the
+// fully visible mask the kernels form the bias as -|w_j - w_i| (w = s p + s' tau), which is
+// the per-term form only when the H slopes are non-negative (positions and times are sorted)
+inline genrank_status check_alibi_variant(const genrank_alibi& a, int H) {
   if (a.flags & ~(GENRANK_ATTN_FULL_HISTORY | GENRANK_ATTN_TIME_BUCKET)) return GENRANK_E_ARG;
+  if (a.flags & GENRANK_ATTN_FULL_HISTORY)
+    for (int h = 0; h < H; ++h)
+      if (!(a.slopes_pos[h] >= 0.f) || !(a.slopes_time[h] >= 0.f)) return GENRANK_E_ARG;
   if (a.flags & GENRANK_ATTN_TIME_BUCKET) {
     if (a.n_time_bounds < 0 || a.n_time_bounds > 1024) return GENRANK_E_SHAPE;
     if (a.n_time_bounds > 0 && !a.time_bounds) return GENRANK_E_ARG;

@@ -10,13 +10,16 @@ from __future__ import annotations
 import numpy as np
 
 
-def attention_pairs(lengths, m: int) -> int:
+def attention_pairs(lengths, m: int, full_history: bool = False) -> int:
+    """Allowed (query, key) pairs: a causal (or, with ``full_history``, fully visible)
+    history, and m candidates that each see the history and themselves."""
     n = np.asarray(lengths, dtype=np.int64)
-    return int((n * (n + 1) // 2).sum() + m * (n + 1).sum())
+    hist = (n * n).sum() if full_history else (n * (n + 1) // 2).sum()
+    return int(hist + m * (n + 1).sum())
 
 
-def attention_fwd_flops(lengths, m: int, d: int) -> int:
-    return 4 * d * attention_pairs(lengths, m)
+def attention_fwd_flops(lengths, m: int, d: int, full_history: bool = False) -> int:
+    return 4 * d * attention_pairs(lengths, m, full_history)
 
 
 def attention_hbm_floor_bytes(rows: int, d: int, elem: int = 2, lse: bool = True, H: int = 1) -> int:
@@ -49,12 +52,12 @@ def action_oriented_tokens(n_c: int, m: int = 0) -> int:
     return n_c + m
 
 
-def attention_bwd_flops(lengths, m: int, d: int, recompute: bool = False) -> int:
+def attention_bwd_flops(lengths, m: int, d: int, recompute: bool = False, full_history: bool = False) -> int:
     """Backward over the allowed pairs: dV = P^T dO, dP = dO V^T, dQ = dS K, dK = dS^T Q
     (2 d flops each per pair, twice the forward); with ``recompute`` also S = Q K^T again
     (2.5 times the forward)."""
     per_pair = 8 * d + (2 * d if recompute else 0)
-    return per_pair * attention_pairs(lengths, m)
+    return per_pair * attention_pairs(lengths, m, full_history)
 
 
 def attention_bwd_hbm_floor_bytes(rows: int, d: int, H: int, elem: int = 2) -> int:

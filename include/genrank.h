@@ -134,6 +134,7 @@ typedef struct {
  * flags (0 = the default above and the causal history mask):
  *   GENRANK_ATTN_FULL_HISTORY: history queries see every history key (the fully visible
  *     mask over the historical positions, [GR-zh] section 1.3.1); candidates unchanged.
+ *     Requires slopes_pos, slopes_time >= 0 (else GENRANK_E_ARG).
  *   GENRANK_ATTN_TIME_BUCKET: the time term is -slopes_time[h]*bucket(|tau_i - tau_j|),
  *     bucket(g) = #{k : time_bounds[k] <= g} ([GR-zh] section 1.4.2, -m_t bucket(t_i - t_j);
  *     the request-gap bucketing of the time embedding).  time_bounds: DEVICE int64

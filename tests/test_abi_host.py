@@ -132,6 +132,38 @@ def test_entry_points_reject_bad_arguments(lib):
     assert lib.genrank_debug_mask(ctypes.byref(bt), FAKE, 2, 10, FAKE, None) == -1  # user >= B
 
 
+def test_attention_variant_checks(lib):
+    """Unknown flag bits, too many or missing bucket edges, and negative slopes under the
+    fully visible mask are refused by every entry that takes ALiBi slopes."""
+    bt = _batch()
+    sp = np.array([0.5, 0.25, 0.125, 0.0625], np.float32)
+    st = np.array([0.1, 0.05, 0.02, 0.01], np.float32)
+    neg = np.array([0.5, -0.25, 0.125, 0.0625], np.float32)
+
+    def alibi(flags, n=0, edges=FAKE, pos=sp):
+        return B.Alibi(pos.ctypes.data, st.ctypes.data, flags, n, edges)
+
+    cases = [(alibi(4), -1),                                       # unknown bit
+             (alibi(B.ATTN_TIME_BUCKET, 1025), -2),                # more than 1024 edges
+             (alibi(B.ATTN_TIME_BUCKET, 3, None), -1),             # edges missing
+             (alibi(B.ATTN_FULL_HISTORY, pos=neg), -1)]            # negative slope, full mask
+    for a, want in cases:
+        assert lib.genrank_attn_fwd(ctypes.byref(bt), FAKE, FAKE, FAKE, a, FAKE, FAKE, FAKE, 768, FAKE, 256,
+                                    None, None) == want
+        assert lib.genrank_attn_bwd(ctypes.byref(bt), FAKE, FAKE, FAKE, a, FAKE, FAKE, FAKE, 768, FAKE, FAKE,
+                                    256, FAKE, FAKE, FAKE, FAKE, 768, 0, FAKE, 1 << 40, None) == want
+        assert lib.genrank_attn_fwd_cached(ctypes.byref(bt), FAKE, FAKE, FAKE, a, FAKE, FAKE, FAKE, 768, FAKE,
+                                           FAKE, 512, FAKE, 256, None, None) == want
+        w = B.LayerWeights(FAKE, FAKE, None, None, None, None, 0, B.BLOCK_ATTN_ONLY, a)
+        assert lib.genrank_layer_fwd(ctypes.byref(bt), ctypes.byref(w), FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE,
+                                     1 << 40, None) == want
+    # the same slopes pass the variant check with the causal mask (and fail later, on the
+    # too-small workspace, not on the slopes)
+    w = B.LayerWeights(FAKE, FAKE, None, None, None, None, 0, B.BLOCK_ATTN_ONLY, alibi(0, pos=neg))
+    assert lib.genrank_layer_fwd(ctypes.byref(bt), ctypes.byref(w), FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, 16,
+                                 None) == -6
+
+
 def _host_structs(cfg, batch, tables):
     keep = {
         "offs": np.ascontiguousarray(batch.hist_offsets, np.int32),

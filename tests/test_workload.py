@@ -65,3 +65,12 @@ def test_attention_bwd_work_model():
     assert W.attention_bwd_flops(lengths, m, d) == 2 * fwd
     assert W.attention_bwd_flops(lengths, m, d, recompute=True) * 2 == 5 * fwd
     assert W.attention_bwd_hbm_floor_bytes(10, 64, 2) == 10 * 64 * 2 * 8 + 10 * 2 * 4 * 3
+
+
+def test_attention_pairs_full_history():
+    """Fully visible history: N^2 history pairs instead of N(N+1)/2; candidates unchanged."""
+    import oracle
+    lengths, m = [5, 0, 3], 2
+    want = sum(int(oracle.attention_mask(n, m, history="full").sum()) for n in lengths)
+    assert W.attention_pairs(lengths, m, full_history=True) == want == 25 + 9 + m * (6 + 1 + 4)
+    assert W.attention_fwd_flops(lengths, m, 64, full_history=True) == 4 * 64 * want
