@@ -497,10 +497,19 @@ def bce_loss_bwd(logits, labels):
     return (1.0 / (1.0 + np.exp(-z)) - y) / z.size
 
 
-def model_fwd(x0, layers, block, H, geom, head=None, store=None):
-    """Embedded rows -> stacked blocks -> (optional) head at candidate rows.
-    Returns (x_final, logits or None, caches).  ``store``: as in ``layer_fwd``, also
-    applied to the embedded rows."""
+def _loss_rows(geom, n_rows, loss_rows):
+    """The rows that carry a loss: the candidate rows [T_h, T) by default ([GR-zh] section
+    1.3.1, loss at candidate positions only), else the given row indices (the section's
+    ablation that also takes the loss at some history positions)."""
+    if loss_rows is None:
+        return np.arange(int(geom["hist_offsets"][-1]), n_rows)
+    return np.asarray(loss_rows, np.int64)
+
+
+def model_fwd(x0, layers, block, H, geom, head=None, store=None, loss_rows=None):
+    """Embedded rows -> stacked blocks -> (optional) head at the loss rows (candidate rows
+    unless ``loss_rows`` lists others).  Returns (x_final, logits or None, caches).
+    ``store``: as in ``layer_fwd``, also applied to the embedded rows."""
     x = (store or _identity)(np.asarray(x0, np.float64))
     caches = []
     for lw in layers:
@@ -508,17 +517,17 @@ def model_fwd(x0, layers, block, H, geom, head=None, store=None):
         caches.append(c)
     logits = None
     if head is not None:
-        T_h = int(geom["hist_offsets"][-1])
-        logits = head_fwd(x[T_h:], head["g_final"], head["w_head"], head["b_head"])
+        rows = _loss_rows(geom, x.shape[0], loss_rows)
+        logits = head_fwd(x[rows], head["g_final"], head["w_head"], head["b_head"])
     return x, logits, caches
 
 
-def model_bwd(dlogits, x_final, layers, block, H, geom, caches, head):
+def model_bwd(dlogits, x_final, layers, block, H, geom, caches, head, loss_rows=None):
     """Backward through the head and the blocks.  Returns (dx0, per-layer grads, head grads)."""
-    T_h = int(geom["hist_offsets"][-1])
+    rows = _loss_rows(geom, np.asarray(x_final).shape[0], loss_rows)
     dx = np.zeros_like(np.asarray(x_final, np.float64))
-    dxc, hgrads = head_bwd(dlogits, x_final[T_h:], head["g_final"], head["w_head"])
-    dx[T_h:] = dxc
+    dxc, hgrads = head_bwd(dlogits, x_final[rows], head["g_final"], head["w_head"])
+    np.add.at(dx, rows, dxc)
     lgrads = [None] * len(layers)
     for li in range(len(layers) - 1, -1, -1):
         dx, lgrads[li] = layer_bwd(dx, layers[li], block, H, geom, caches[li])

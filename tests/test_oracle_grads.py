@@ -159,3 +159,45 @@ def test_model_backward_matches_torch_autograd():
             assert np.allclose(tv.grad.numpy(), lgrads[li][k], atol=1e-12), k
     for k in ("w_head", "b_head", "g_final"):
         assert np.allclose(th[k].grad.numpy(), hgrads[k], atol=1e-12), k
+
+
+def test_history_position_loss_finite_differences():
+    """The ablation of [GR-zh] section 1.3.1 that also takes the loss at some history
+    positions: BCE over the candidate rows plus two history rows, every parameter group
+    against central differences.  Dropping the history rows' head gradient, or scattering
+    it to the wrong rows, fails this."""
+    cfg, batch, tables, weights = tiny_case(seed=4, N=7, m=3, block="prenorm", layers=2, d=16)
+    idx = oracle_indices(cfg, batch, tables)
+    tabs = {k: getattr(tables, k).f32().astype(np.float64).copy()
+            for k in ("item", "action", "pos", "ri", "rt")}
+    layers = [{k: np.asarray(v, np.float64).copy() for k, v in lw.items()} for lw in oracle_layers(weights)]
+    head = {k: np.asarray(v, np.float64).copy() for k, v in oracle_head(weights).items()}
+    geom = oracle_geom(cfg, batch, idx)
+    T_h = batch.total_hist
+    rows = np.concatenate([np.arange(T_h, T_h + cfg.m), [1, 5]])
+    labels = (np.random.default_rng(3).random((rows.size, 4)) < 0.3).astype(np.float64)
+
+    def loss():
+        x = oracle.embed_sum(tabs, batch.hist_items, batch.cand_items, idx)
+        _, logits, _ = oracle.model_fwd(x, layers, "prenorm", cfg.H, geom, head, loss_rows=rows)
+        return oracle.bce_loss(logits, labels)
+
+    x0 = oracle.embed_sum(tabs, batch.hist_items, batch.cand_items, idx)
+    xf, logits, caches = oracle.model_fwd(x0, layers, "prenorm", cfg.H, geom, head, loss_rows=rows)
+    assert logits.shape == (rows.size, 4)
+    dl = oracle.bce_loss_bwd(logits, labels)
+    dx0, lgrads, hgrads = oracle.model_bwd(dl, xf, layers, "prenorm", cfg.H, geom, caches, head,
+                                           loss_rows=rows)
+    tgrads = oracle.embed_bwd(dx0, {k: v.shape for k, v in tabs.items()}, batch.hist_items,
+                              batch.cand_items, idx)
+    rng = np.random.default_rng(1)
+    checks = [(tabs[k], tgrads[k]) for k in ("item", "action", "pos", "ri", "rt")]
+    for li, lw in enumerate(layers):
+        checks += [(lw[k], lgrads[li][k]) for k in lw if k in lgrads[li]]
+    checks += [(head[k], hgrads[k]) for k in ("w_head", "b_head", "g_final")]
+    for arr, grad in checks:
+        for i, g in _fd(loss, arr, samples=min(6, arr.size), rng=rng).items():
+            assert abs(grad.reshape(-1)[i] - g) < 1e-7 * max(1.0, abs(g)) + 1e-10, (i, g)
+    # the default is the candidate rows
+    _, lc, _ = oracle.model_fwd(x0, layers, "prenorm", cfg.H, geom, head)
+    assert np.array_equal(lc, logits[:cfg.m])
