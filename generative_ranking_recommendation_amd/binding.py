@@ -108,6 +108,11 @@ _SIGS = {
     "genrank_head_bwd": (c_int32, [POINTER(Batch), c_void_p, c_void_p, c_void_p, c_int32, c_void_p,
                                    c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
                                    c_void_p]),
+    "genrank_head_fwd_rows": (c_int32, [c_int32, c_int32, c_void_p, c_int64, c_void_p, c_void_p, c_void_p,
+                                        c_void_p, c_int32, c_void_p, c_void_p]),
+    "genrank_head_bwd_rows": (c_int32, [c_int32, c_int32, c_int64, c_void_p, c_int64, c_void_p, c_void_p,
+                                        c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                        c_void_p, c_size_t, c_void_p]),
     "genrank_bce_loss": (c_int32, [c_int64, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
     "genrank_embed_bwd": (c_int32, [POINTER(Batch), POINTER(Inputs), POINTER(Tables), c_void_p,
                                     c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
@@ -339,6 +344,19 @@ def genrank_head_bwd(batch, x, g_final, w_head, n_tasks, dlogits, dx, dg_final, 
                      ws, ws_bytes, stream=None):
     _check("genrank_head_bwd", lib().genrank_head_bwd(
         ctypes.byref(batch), _p(x), _p(g_final), _p(w_head), n_tasks, _p(dlogits), _p(dx),
+        _p(dg_final), _p(dw_head), _p(db_head), _p(ws), ws_bytes, _stream(stream)))
+
+
+def genrank_head_fwd_rows(dtype, d, x, n_rows, rows, g_final, w_head, b_head, n_tasks, logits, stream=None):
+    _check("genrank_head_fwd_rows", lib().genrank_head_fwd_rows(
+        dtype, d, _p(x), n_rows, _p(rows), _p(g_final), _p(w_head), _p(b_head), n_tasks, _p(logits),
+        _stream(stream)))
+
+
+def genrank_head_bwd_rows(dtype, d, n_x_rows, x, n_rows, rows, g_final, w_head, n_tasks, dlogits, dx,
+                          dg_final, dw_head, db_head, ws, ws_bytes, stream=None):
+    _check("genrank_head_bwd_rows", lib().genrank_head_bwd_rows(
+        dtype, d, n_x_rows, _p(x), n_rows, _p(rows), _p(g_final), _p(w_head), n_tasks, _p(dlogits), _p(dx),
         _p(dg_final), _p(dw_head), _p(db_head), _p(ws), ws_bytes, _stream(stream)))
 
 

@@ -602,8 +602,19 @@ genrank_status genrank_head_fwd(const genrank_batch* b, const void* x, const flo
   GR_TRY(check_batch(b));
   if (!x || !g_final || !w_head || !b_head || !logits) return GENRANK_E_ARG;
   if (n_tasks < 1 || n_tasks > 8) return GENRANK_E_SHAPE;
-  return launch_head_fwd(b->dtype, x, b->total_hist, static_cast<int64_t>(b->B) * b->m, b->d,
+  return launch_head_fwd(b->dtype, x, b->total_hist, static_cast<int64_t>(b->B) * b->m, nullptr, b->d,
                          g_final, w_head, b_head, n_tasks, logits, S(stream));
+}
+
+genrank_status genrank_head_fwd_rows(int32_t dtype, int32_t d, const void* x, int64_t n_rows,
+                                     const int32_t* rows, const float* g_final, const float* w_head,
+                                     const float* b_head, int32_t n_tasks, float* logits,
+                                     genrank_stream_t stream) {
+  if (dtype != GENRANK_BF16 && dtype != GENRANK_F32) return GENRANK_E_DTYPE;
+  if (!x || !g_final || !w_head || !b_head || !logits || (n_rows > 0 && !rows)) return GENRANK_E_ARG;
+  if (n_rows < 0 || d < 1) return GENRANK_E_SHAPE;
+  if (n_tasks < 1 || n_tasks > 8) return GENRANK_E_SHAPE;
+  return launch_head_fwd(dtype, x, 0, n_rows, rows, d, g_final, w_head, b_head, n_tasks, logits, S(stream));
 }
 
 genrank_status genrank_head_bwd(const genrank_batch* b, const void* x, const float* g_final,
@@ -618,8 +629,27 @@ genrank_status genrank_head_bwd(const genrank_batch* b, const void* x, const flo
   if (!ws || ws_bytes < head_bwd_workspace(b->d, n_tasks)) return GENRANK_E_WORKSPACE;
   const hipStream_t s = S(stream);
   GR_TRY(launch_fill_zero(b->dtype, dx, b->total_hist * b->d, s));
-  return launch_head_bwd(b->dtype, x, b->total_hist, static_cast<int64_t>(b->B) * b->m, b->d,
+  return launch_head_bwd(b->dtype, x, b->total_hist, static_cast<int64_t>(b->B) * b->m, nullptr, b->d,
                          g_final, w_head, n_tasks, dlogits, dx, dg_final, dw_head, db_head, ws, s);
+}
+
+genrank_status genrank_head_bwd_rows(int32_t dtype, int32_t d, int64_t n_x_rows, const void* x,
+                                     int64_t n_rows, const int32_t* rows, const float* g_final,
+                                     const float* w_head, int32_t n_tasks, const float* dlogits, void* dx,
+                                     float* dg_final, float* dw_head, float* db_head, void* ws,
+                                     size_t ws_bytes, genrank_stream_t stream) {
+  if (dtype != GENRANK_BF16 && dtype != GENRANK_F32) return GENRANK_E_DTYPE;
+  if (!x || !g_final || !w_head || !dlogits || !dx || !dg_final || !dw_head || !db_head ||
+      (n_rows > 0 && !rows))
+    return GENRANK_E_ARG;
+  if (n_rows < 0 || n_x_rows < 0 || d < 1) return GENRANK_E_SHAPE;
+  if (n_tasks < 1 || n_tasks > 4) return GENRANK_E_SHAPE;
+  if (d > 1024 || d % 4) return GENRANK_E_SHAPE;
+  if (!ws || ws_bytes < head_bwd_workspace(d, n_tasks)) return GENRANK_E_WORKSPACE;
+  const hipStream_t s = S(stream);
+  GR_TRY(launch_fill_zero(dtype, dx, n_x_rows * d, s));
+  return launch_head_bwd(dtype, x, 0, n_rows, rows, d, g_final, w_head, n_tasks, dlogits, dx, dg_final, dw_head,
+                         db_head, ws, s);
 }
 
 genrank_status genrank_bce_loss(int64_t n, int32_t n_tasks, const float* logits,

@@ -123,12 +123,13 @@ genrank_status launch_rmsnorm_bwd(int dtype, const void* x, const float* g, cons
                                   hipStream_t stream);
 genrank_status launch_fill_f32(float* p, int64_t n, float v, hipStream_t stream);
 genrank_status launch_fill_zero(int dtype, void* p, int64_t n, hipStream_t stream);
-genrank_status launch_head_fwd(int dtype, const void* x, int64_t row0, int64_t rows, int d,
-                               const float* g, const float* w, const float* bias, int nt,
+// the head at rows row0 .. row0 + rows - 1 of x, or at rows idx[0 .. rows) when idx is given
+genrank_status launch_head_fwd(int dtype, const void* x, int64_t row0, int64_t rows, const int32_t* idx,
+                               int d, const float* g, const float* w, const float* bias, int nt,
                                float* logits, hipStream_t stream);
 size_t head_bwd_workspace(int d, int nt);  // per-block partial rows of dg, dw, db
-genrank_status launch_head_bwd(int dtype, const void* x, int64_t row0, int64_t rows, int d,
-                               const float* g, const float* w, int nt, const float* dlogits,
+genrank_status launch_head_bwd(int dtype, const void* x, int64_t row0, int64_t rows, const int32_t* idx,
+                               int d, const float* g, const float* w, int nt, const float* dlogits,
                                void* dx, float* dg, float* dw, float* db, void* ws, hipStream_t stream);
 genrank_status launch_bce(int64_t n, int nt, const float* logits, const float* labels,
                           float* loss, float* dlogits, hipStream_t stream);

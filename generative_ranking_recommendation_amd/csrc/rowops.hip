@@ -189,17 +189,19 @@ __global__ void fill_u16_kernel(uint16_t* p, int64_t n) {
     p[i] = 0;
 }
 
-// logits[c, t] = rmsnorm(x_c) g . w[t] + b[t]
+// logits[c, t] = rmsnorm(x_c) g . w[t] + b[t] for row c = row0 + r, or idx[r] when a row
+// list is given
 template <typename T>
 __global__ void __launch_bounds__(RW) head_fwd_kernel(const T* __restrict__ x, int64_t row0, int64_t rows,
-                                                      int d, const float* __restrict__ g,
+                                                      const int32_t* __restrict__ idx, int d,
+                                                      const float* __restrict__ g,
                                                       const float* __restrict__ w,
                                                       const float* __restrict__ b, int nt,
                                                       float* __restrict__ logits) {
   const int64_t r = static_cast<int64_t>(blockIdx.x) * (RW / 64) + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (r >= rows) return;
-  const T* xr = x + (row0 + r) * d;
+  const T* xr = x + (idx ? static_cast<int64_t>(idx[r]) : row0 + r) * d;
   float ss = 0.f;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int c = lane; c < d; c += 64) {
@@ -229,7 +231,8 @@ constexpr int HEAD_BLOCKS = 64;
 
 template <typename T>
 __global__ void __launch_bounds__(RW) head_bwd_kernel(const T* __restrict__ x, int64_t row0, int64_t rows,
-                                                      int d, const float* __restrict__ g,
+                                                      const int32_t* __restrict__ idx, int d,
+                                                      const float* __restrict__ g,
                                                       const float* __restrict__ w, int nt,
                                                       const float* __restrict__ dl, T* __restrict__ dx,
                                                       float* __restrict__ part) {
@@ -247,7 +250,8 @@ __global__ void __launch_bounds__(RW) head_bwd_kernel(const T* __restrict__ x, i
       for (int t = 0; t < 4; ++t) pw[t][q][e] = 0.f;
     }
   for (int64_t r = static_cast<int64_t>(blockIdx.x) * (RW / 64) + wave; r < rows; r += nw) {
-    const T* xr = x + (row0 + r) * d;
+    const int64_t xrow = idx ? static_cast<int64_t>(idx[r]) : row0 + r;
+    const T* xr = x + xrow * d;
     float dlr[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) dlr[t] = (t < nt) ? dl[r * nt + t] : 0.f;
@@ -293,7 +297,7 @@ __global__ void __launch_bounds__(RW) head_bwd_kernel(const T* __restrict__ x, i
 #pragma unroll
         for (int t = 0; t < 4; ++t) pw[t][q][e] += dlr[t] * z;
       }
-      st4(dx + (row0 + r) * d + c, o);
+      st4(dx + xrow * d + c, o);
     }
 #pragma unroll
     for (int t = 0; t < 4; ++t) pb[t] += dlr[t];
@@ -403,17 +407,17 @@ genrank_status launch_fill_zero(int dtype, void* p, int64_t n, hipStream_t strea
   return GENRANK_OK;
 }
 
-genrank_status launch_head_fwd(int dtype, const void* x, int64_t row0, int64_t rows, int d,
-                               const float* g, const float* w, const float* bias, int nt,
+genrank_status launch_head_fwd(int dtype, const void* x, int64_t row0, int64_t rows, const int32_t* idx,
+                               int d, const float* g, const float* w, const float* bias, int nt,
                                float* logits, hipStream_t stream) {
   if (rows <= 0) return GENRANK_OK;
   const unsigned grid = static_cast<unsigned>((rows + 3) / 4);
   if (dtype == GENRANK_BF16)
     hipLaunchKernelGGL(head_fwd_kernel<bf16_t>, dim3(grid), dim3(RW), 0, stream,
-                       static_cast<const bf16_t*>(x), row0, rows, d, g, w, bias, nt, logits);
+                       static_cast<const bf16_t*>(x), row0, rows, idx, d, g, w, bias, nt, logits);
   else
     hipLaunchKernelGGL(head_fwd_kernel<float>, dim3(grid), dim3(RW), 0, stream,
-                       static_cast<const float*>(x), row0, rows, d, g, w, bias, nt, logits);
+                       static_cast<const float*>(x), row0, rows, idx, d, g, w, bias, nt, logits);
   GR_CHECK_LAUNCH();
   return GENRANK_OK;
 }
@@ -422,8 +426,8 @@ size_t head_bwd_workspace(int d, int nt) {
   return static_cast<size_t>(HEAD_BLOCKS) * (static_cast<size_t>(d) * (1 + nt) + nt) * sizeof(float);
 }
 
-genrank_status launch_head_bwd(int dtype, const void* x, int64_t row0, int64_t rows, int d,
-                               const float* g, const float* w, int nt, const float* dlogits,
+genrank_status launch_head_bwd(int dtype, const void* x, int64_t row0, int64_t rows, const int32_t* idx,
+                               int d, const float* g, const float* w, int nt, const float* dlogits,
                                void* dx, float* dg, float* dw, float* db, void* ws, hipStream_t stream) {
   if (d > 256 * MAXQ || d % 4 || nt > 4) return GENRANK_E_SHAPE;
   if (rows <= 0) {
@@ -436,11 +440,11 @@ genrank_status launch_head_bwd(int dtype, const void* x, int64_t row0, int64_t r
   const unsigned grid = static_cast<unsigned>(std::min<int64_t>(HEAD_BLOCKS, (rows + 3) / 4));
   if (dtype == GENRANK_BF16)
     hipLaunchKernelGGL(head_bwd_kernel<bf16_t>, dim3(grid), dim3(RW), 0, stream,
-                       static_cast<const bf16_t*>(x), row0, rows, d, g, w, nt, dlogits,
+                       static_cast<const bf16_t*>(x), row0, rows, idx, d, g, w, nt, dlogits,
                        static_cast<bf16_t*>(dx), part);
   else
     hipLaunchKernelGGL(head_bwd_kernel<float>, dim3(grid), dim3(RW), 0, stream,
-                       static_cast<const float*>(x), row0, rows, d, g, w, nt, dlogits,
+                       static_cast<const float*>(x), row0, rows, idx, d, g, w, nt, dlogits,
                        static_cast<float*>(dx), part);
   hipLaunchKernelGGL(column_sum_kernel, dim3((width + 15) / 16), dim3(256), 0, stream, part,
                      static_cast<int>(grid), width, dg, d, dw, nt * d, db);

@@ -140,24 +140,43 @@ class GenRank:
         return x, logits
 
     # ---------------------------------------------------------------- training
-    def train_step(self, inp, labels, stream=None):
+    def train_step(self, inp, labels, stream=None, hist_rows=None, hist_labels=None):
         """Forward with saved activations, BCE at candidates, full backward.  Returns
-        (loss tensor [1], logits, grads dict of f32 tensors)."""
+        (loss tensor [1], logits, grads dict of f32 tensors).
+
+        ``hist_rows`` (device int32, distinct history row indices in [0, T_h)) and
+        ``hist_labels`` ([len(hist_rows), n_tasks] f32): also take the loss at those history
+        positions (the history-position loss ablation); the logits then cover the candidate
+        rows followed by the listed history rows, and the BCE is the mean over all of them."""
         x_final, logits = self.forward(inp, save=True, stream=stream)
         bt = self.batch(inp)
         dev, d = self.device, self.d
         n = inp.B * inp.m
         nt = self.head.n_tasks
+        nwh = B.genrank_workspace_size(B.OP_HEAD_BWD, bt)
+        rows = None
+        if hist_rows is not None and hist_rows.numel() > 0:
+            rows = torch.cat([torch.arange(inp.total_hist, inp.rows, dtype=torch.int32, device=dev),
+                              hist_rows.to(torch.int32)])
+            n = int(rows.numel())
+            labels = torch.cat([labels, hist_labels])
+            logits = torch.empty((n, nt), dtype=torch.float32, device=dev)
+            B.genrank_head_fwd_rows(self.code, d, x_final, n, rows, self.head.g_final, self.head.w_head,
+                                    self.head.b_head, nt, logits, stream)
         loss = torch.empty(1, dtype=torch.float32, device=dev)
         dlogits = torch.empty((n, nt), dtype=torch.float32, device=dev)
         B.genrank_bce_loss(n, nt, logits, labels, loss, dlogits, stream)
         f32 = lambda *s: torch.empty(s, dtype=torch.float32, device=dev)
         grads = {"g_final": f32(d), "w_head": f32(nt, d), "b_head": f32(nt)}
         dx = self.act(inp.rows)
-        nwh = B.genrank_workspace_size(B.OP_HEAD_BWD, bt)
-        B.genrank_head_bwd(bt, x_final, self.head.g_final, self.head.w_head, nt, dlogits, dx,
-                           grads["g_final"], grads["w_head"], grads["b_head"],
-                           self._buf(("head_bwd",), nwh), nwh, stream)
+        if rows is None:
+            B.genrank_head_bwd(bt, x_final, self.head.g_final, self.head.w_head, nt, dlogits, dx,
+                               grads["g_final"], grads["w_head"], grads["b_head"],
+                               self._buf(("head_bwd",), nwh), nwh, stream)
+        else:
+            B.genrank_head_bwd_rows(self.code, d, inp.rows, x_final, n, rows, self.head.g_final,
+                                    self.head.w_head, nt, dlogits, dx, grads["g_final"], grads["w_head"],
+                                    grads["b_head"], self._buf(("head_bwd",), nwh), nwh, stream)
         grads["layers"] = [None] * len(self.layers)
         for i in range(len(self.layers) - 1, -1, -1):
             lay = self.layers[i]
@@ -171,7 +190,7 @@ class GenRank:
             nf = B.genrank_workspace_size(B.OP_LAYER_FWD, bt, lay.struct)
             B.genrank_layer_bwd(bt, lay.struct, inp.hist_offsets, inp.hist_ts, inp.req_ts,
                                 self._xs[i], self._ws[("fwd", i)], dx, dx, gstruct,
-                                1 if i == len(self.layers) - 1 else 0, wsb, nb, stream)
+                                1 if (i == len(self.layers) - 1 and rows is None) else 0, wsb, nb, stream)
             del nf
             grads["layers"][i] = lg
         # table gradients: the item table's sparse (distinct ids ascending, their rows, the

@@ -329,6 +329,31 @@ GENRANK_API genrank_status genrank_head_bwd(const genrank_batch* batch, const vo
                                 void* dx, float* dg_final, float* dw_head, float* db_head,
                                 void* ws, size_t ws_bytes, genrank_stream_t stream);
 
+/* The head of genrank_head_fwd at a list of rows, for a loss taken at candidate and some
+ * history positions (the ablation of [GR-zh] section 1.3.1; the default training loss is
+ * at candidate positions only).  x: [n_x_rows, d] in dtype (GENRANK_BF16 or GENRANK_F32),
+ * row-major; rows: DEVICE int32 [n_rows], each in [0, n_x_rows) (not checked on the
+ * device: an index outside reads outside x); logits: [n_rows, n_tasks] f32, row r for
+ * x row rows[r].  Errors: GENRANK_E_DTYPE, GENRANK_E_ARG (null pointer), GENRANK_E_SHAPE
+ * (n_rows < 0, d < 1, n_tasks outside 1..8). */
+GENRANK_API genrank_status genrank_head_fwd_rows(int32_t dtype, int32_t d, const void* x, int64_t n_rows,
+                                     const int32_t* rows, const float* g_final, const float* w_head,
+                                     const float* b_head, int32_t n_tasks, float* logits,
+                                     genrank_stream_t stream);
+
+/* Backward of genrank_head_fwd_rows.  dx: [n_x_rows, d] in dtype, overwritten: each listed
+ * row gets the head's gradient, every other row zero.  The rows must be distinct (a
+ * repeated row gets one of its gradients, not their sum).  dg_final, dw_head, db_head: as
+ * genrank_head_bwd (f32, overwritten, fixed summation order).  ws: at least
+ * genrank_workspace_size(GENRANK_OP_HEAD_BWD) of a batch with the same d.  Errors as
+ * genrank_head_fwd_rows, plus n_tasks > 4 or d > 1024 or d % 4 != 0 -> GENRANK_E_SHAPE and
+ * GENRANK_E_WORKSPACE. */
+GENRANK_API genrank_status genrank_head_bwd_rows(int32_t dtype, int32_t d, int64_t n_x_rows, const void* x,
+                                     int64_t n_rows, const int32_t* rows, const float* g_final,
+                                     const float* w_head, int32_t n_tasks, const float* dlogits, void* dx,
+                                     float* dg_final, float* dw_head, float* db_head, void* ws,
+                                     size_t ws_bytes, genrank_stream_t stream);
+
 /* Mean sigmoid binary cross-entropy over n rows x n_tasks logits and its gradient:
  * loss[0] = mean(softplus(z) - y z); dlogits = (sigmoid(z) - y) / (n * n_tasks).
  * logits, labels, dlogits: [n, n_tasks] f32; loss: [1] f32 (device). */

@@ -128,6 +128,14 @@ def test_entry_points_reject_bad_arguments(lib):
     assert lib.genrank_layer_fwd(ctypes.byref(bt), ctypes.byref(wf), FAKE, FAKE, FAKE, FAKE, FAKE,
                                  0, FAKE, 1 << 40, None) == -2
     assert lib.genrank_head_fwd(ctypes.byref(bt), FAKE, FAKE, FAKE, FAKE, 9, FAKE, None) == -2
+    # head at a row list: dtype, missing row list, task count, workspace
+    assert lib.genrank_head_fwd_rows(7, 256, FAKE, 4, FAKE, FAKE, FAKE, FAKE, 4, FAKE, None) == -3
+    assert lib.genrank_head_fwd_rows(B.BF16, 256, FAKE, 4, None, FAKE, FAKE, FAKE, 4, FAKE, None) == -1
+    assert lib.genrank_head_fwd_rows(B.BF16, 256, FAKE, 4, FAKE, FAKE, FAKE, FAKE, 9, FAKE, None) == -2
+    assert lib.genrank_head_bwd_rows(B.BF16, 256, 10, FAKE, 4, FAKE, FAKE, FAKE, 4, FAKE, FAKE, FAKE, FAKE,
+                                     FAKE, FAKE, 16, None) == -6
+    assert lib.genrank_head_bwd_rows(B.BF16, 256, 10, FAKE, 4, FAKE, FAKE, FAKE, 5, FAKE, FAKE, FAKE, FAKE,
+                                     FAKE, FAKE, 1 << 30, None) == -2
     assert lib.genrank_bce_loss(0, 4, FAKE, FAKE, FAKE, FAKE, None) == -1
     assert lib.genrank_debug_mask(ctypes.byref(bt), FAKE, 2, 10, FAKE, None) == -1  # user >= B
 

@@ -295,3 +295,65 @@ def test_variant_score_equals_forward(var):
     Th = inp.total_hist
     assert torch.equal(x_c, x_full[Th:]), "candidate rows differ"
     assert torch.equal(logits_c, logits_full), "logits differ"
+
+
+def _hist_loss_case(cfg, batch, tables, weights, n_pick, seed):
+    """Candidate rows plus n_pick history rows (distinct, drawn with a seed) carry the loss."""
+    rng = np.random.default_rng(seed)
+    picks = np.sort(rng.choice(batch.total_hist, size=n_pick, replace=False)).astype(np.int64)
+    labels = synth.make_labels(cfg, B=batch.B)
+    hist_labels = (rng.random((n_pick, labels.shape[1])) < 0.2).astype(np.float32)
+    rows = np.concatenate([np.arange(batch.total_hist, batch.total_rows), picks])
+    all_labels = np.concatenate([labels, hist_labels]).astype(np.float64)
+    idx = oracle_indices(cfg, batch, tables)
+    x0 = oracle.embed_sum(oracle_tables(tables), batch.hist_items, batch.cand_items, idx)
+    geom = _geom(cfg, batch, idx, "causal", None)
+    layers, head = oracle_layers(weights), oracle_head(weights)
+    xf, logits, caches = oracle.model_fwd(x0, layers, cfg.block, cfg.H, geom, head, loss_rows=rows)
+    wl = oracle.bce_loss(logits, all_labels)
+    _, lg, hg = oracle.model_bwd(oracle.bce_loss_bwd(logits, all_labels), xf, layers, cfg.block, cfg.H, geom,
+                                 caches, head, loss_rows=rows)
+    sp, st = gpu_slopes(cfg)
+    model = GenRank.from_host(cfg, tables, weights, sp, st, DEV)
+    inp = DeviceInputs(batch, DEV)
+    gl, glog, grads = model.train_step(inp, to_device(labels, DEV, np.float32),
+                                       hist_rows=torch.as_tensor(picks.astype(np.int32)).to(DEV),
+                                       hist_labels=to_device(hist_labels, DEV, np.float32))
+    torch.cuda.synchronize()
+    return (wl, logits, lg, hg), (float(gl.item()), to_numpy(glog), grads)
+
+
+def test_history_position_loss_f32():
+    """The loss at the candidates and at 5 history positions ([GR-zh] section 1.3.1
+    ablation): loss, logits and every block and head gradient against the oracle."""
+    say("variants: history-position loss f32")
+    cfg = synth.make_config("tiny_fp32", block="prenorm", layers=2)
+    batch = custom_batch(cfg, [16, 9, 0], seed=1)
+    (wl, wlog, lg, hg), (gl, glog, grads) = _hist_loss_case(cfg, batch, synth.make_tables(cfg),
+                                                            synth.make_weights(cfg), 5, 7)
+    assert glog.shape == wlog.shape
+    assert abs(gl - wl) <= 1e-5
+    assert np.abs(glog - wlog).max() <= 1e-5 * max(1.0, np.abs(wlog).max())
+    for li in range(cfg.layers):
+        for k, v in lg[li].items():
+            got = to_numpy(grads["layers"][li][k])
+            assert np.abs(got - v).max() <= 1e-5 * max(np.abs(v).max(), 1e-3), f"layer{li}.{k}"
+    for k in ("w_head", "b_head", "g_final"):
+        got = to_numpy(grads[k])
+        assert np.abs(got - hg[k]).max() <= 1e-5 * max(np.abs(hg[k]).max(), 1e-3), k
+
+
+def test_history_position_loss_bf16():
+    """train2_bf16 shapes on 4 users, 40 history positions in the loss."""
+    say("variants: history-position loss bf16")
+    cfg = synth.make_config("train2_bf16")
+    batch = synth.make_batch(cfg, B=4)
+    (wl, wlog, lg, hg), (gl, glog, grads) = _hist_loss_case(cfg, batch, synth.make_tables(cfg),
+                                                            synth.make_weights(cfg), 40, 8)
+    unit_close([gl], [wl], "loss")
+    unit_close(glog, wlog, "logits")
+    for li in range(cfg.layers):
+        for k, v in lg[li].items():
+            bf16_close(to_numpy(grads["layers"][li][k]), v, f"layer{li}.{k}")
+    for k in ("w_head", "b_head", "g_final"):
+        bf16_close(to_numpy(grads[k]), hg[k], k)
