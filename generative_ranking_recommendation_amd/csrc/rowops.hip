@@ -35,6 +35,59 @@ __global__ void __launch_bounds__(RW) rmsnorm_kernel(const T* __restrict__ x, co
   for (int c = lane; c < d; c += 64) yr[c] = from_f32<T>(to_f32(xr[c]) * inv * g[c]);
 }
 
+// The same normalisation with x read once through 16-byte loads: a group of LPR lanes owns
+// one row, each lane Q 16-byte chunks of it (chunk q of lane l at elements
+// (q LPR + l) VEC ..), kept in registers between the sum of squares and the store; a wave
+// takes 64 / LPR rows.  Each row's result depends only on its own elements.
+template <typename T, int LPR, int Q>
+__global__ void __launch_bounds__(RW) rmsnorm_vec_kernel(const T* __restrict__ x, const float* __restrict__ g,
+                                                         T* __restrict__ y, int64_t rows, int d) {
+  constexpr int VEC = 16 / static_cast<int>(sizeof(T));
+  constexpr int RPW = 64 / LPR;
+  const int lane = threadIdx.x & 63;
+  const int li = lane % LPR;
+  const int64_t r = (static_cast<int64_t>(blockIdx.x) * (RW / 64) + (threadIdx.x >> 6)) * RPW + lane / LPR;
+  const int64_t rc = r < rows ? r : rows - 1;  // every lane takes part in the shuffles
+  float v[Q][VEC];
+  float ss = 0.f;
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    const uint4 u = *reinterpret_cast<const uint4*>(x + rc * d + (q * LPR + li) * VEC);
+    if constexpr (VEC == 8) {
+      unpack8(u, v[q]);
+    } else {
+      v[q][0] = __uint_as_float(u.x); v[q][1] = __uint_as_float(u.y);
+      v[q][2] = __uint_as_float(u.z); v[q][3] = __uint_as_float(u.w);
+    }
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) ss += v[q][e] * v[q][e];
+  }
+#pragma unroll
+  for (int o = LPR / 2; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+  const float inv = rsqrtf(ss / d + RMS_EPS);
+  if (r >= rows) return;
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    const int c = (q * LPR + li) * VEC;
+    float o[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; e += 4) {
+      const float4 g4 = *reinterpret_cast<const float4*>(g + c + e);
+      o[e] = v[q][e] * inv * g4.x;
+      o[e + 1] = v[q][e + 1] * inv * g4.y;
+      o[e + 2] = v[q][e + 2] * inv * g4.z;
+      o[e + 3] = v[q][e + 3] * inv * g4.w;
+    }
+    uint4 u;
+    if constexpr (VEC == 8) {
+      u = pack8(o);
+    } else {
+      u = make_uint4(__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]), __float_as_uint(o[3]));
+    }
+    *reinterpret_cast<uint4*>(y + r * d + c) = u;
+  }
+}
+
 // 4 consecutive elements as f32 (8-byte bf16 / 16-byte f32 accesses)
 __device__ __forceinline__ void ld4(const bf16_t* p, float* f) {
   const uint2 v = *reinterpret_cast<const uint2*>(p);
@@ -354,9 +407,45 @@ unsigned blocks_for(int64_t n, int per_block) {
 
 }  // namespace
 
+template <typename T>
+static bool launch_rmsnorm_vec(const T* x, const float* g, T* y, int64_t rows, int d, hipStream_t stream) {
+  constexpr int VEC = 16 / static_cast<int>(sizeof(T));
+  if (d % VEC != 0 || ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(y) |
+                        reinterpret_cast<uintptr_t>(g)) & 15u))
+    return false;
+  const int chunks = d / VEC;
+  auto go = [&](auto kernel, int lpr) {
+    const int64_t per_block = (RW / 64) * (64 / lpr);
+    hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>((rows + per_block - 1) / per_block)), dim3(RW), 0,
+                       stream, x, g, y, rows, d);
+    return true;
+  };
+  switch (chunks) {
+    case 2: return go(rmsnorm_vec_kernel<T, 2, 1>, 2);
+    case 4: return go(rmsnorm_vec_kernel<T, 4, 1>, 4);
+    case 8: return go(rmsnorm_vec_kernel<T, 8, 1>, 8);
+    case 16: return go(rmsnorm_vec_kernel<T, 16, 1>, 16);
+    case 32: return go(rmsnorm_vec_kernel<T, 32, 1>, 32);
+    case 64: return go(rmsnorm_vec_kernel<T, 64, 1>, 64);
+    case 128: return go(rmsnorm_vec_kernel<T, 64, 2>, 64);
+    case 192: return go(rmsnorm_vec_kernel<T, 64, 3>, 64);
+    case 256: return go(rmsnorm_vec_kernel<T, 64, 4>, 64);
+    default: return false;
+  }
+}
+
 genrank_status launch_rmsnorm(int dtype, const void* x, const float* g, void* y, int64_t rows,
                               int d, hipStream_t stream) {
   if (rows <= 0) return GENRANK_OK;
+  const bool vec = dtype == GENRANK_BF16
+                       ? launch_rmsnorm_vec(static_cast<const bf16_t*>(x), g, static_cast<bf16_t*>(y), rows, d,
+                                            stream)
+                       : launch_rmsnorm_vec(static_cast<const float*>(x), g, static_cast<float*>(y), rows, d,
+                                            stream);
+  if (vec) {
+    GR_CHECK_LAUNCH();
+    return GENRANK_OK;
+  }
   const unsigned grid = static_cast<unsigned>((rows + 3) / 4);
   if (dtype == GENRANK_BF16)
     hipLaunchKernelGGL(rmsnorm_kernel<bf16_t>, dim3(grid), dim3(RW), 0, stream,
