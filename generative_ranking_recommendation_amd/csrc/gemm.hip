@@ -34,10 +34,13 @@ struct GemmArgs {
   int M, N, K;
 };
 
-__device__ __forceinline__ float silu_f(float x) { return x / (1.0f + __expf(-x)); }
+// sigmoid through the hardware reciprocal (about 1 ulp) rather than a full-precision
+// division; exp(-a) = inf for very negative a gives 1 / inf = 0, the right limit
+__device__ __forceinline__ float sigmoid_f(float a) { return __builtin_amdgcn_rcpf(1.0f + __expf(-a)); }
+__device__ __forceinline__ float silu_f(float x) { return x * sigmoid_f(x); }
 // d silu(a) / da = s (1 + a (1 - s)), s = sigmoid(a)
 __device__ __forceinline__ float dsilu_f(float a) {
-  const float sg = 1.0f / (1.0f + __expf(-a));
+  const float sg = sigmoid_f(a);
   return sg * (1.0f + a * (1.0f - sg));
 }
 

@@ -275,6 +275,67 @@ __global__ void __launch_bounds__(RW) head_fwd_kernel(const T* __restrict__ x, i
   }
 }
 
+// The head with rows read once through 16-byte loads, laid out as rmsnorm_vec_kernel: a
+// group of LPR lanes per row, Q 16-byte chunks per lane; the sum of squares and the nt
+// dot products are reduced within the group.
+template <typename T, int LPR, int Q>
+__global__ void __launch_bounds__(RW) head_fwd_vec_kernel(const T* __restrict__ x, int64_t row0, int64_t rows,
+                                                          const int32_t* __restrict__ idx, int d,
+                                                          const float* __restrict__ g,
+                                                          const float* __restrict__ w,
+                                                          const float* __restrict__ b, int nt,
+                                                          float* __restrict__ logits) {
+  constexpr int VEC = 16 / static_cast<int>(sizeof(T));
+  constexpr int RPW = 64 / LPR;
+  const int lane = threadIdx.x & 63;
+  const int li = lane % LPR;
+  const int64_t r = (static_cast<int64_t>(blockIdx.x) * (RW / 64) + (threadIdx.x >> 6)) * RPW + lane / LPR;
+  const int64_t rc = r < rows ? r : rows - 1;  // every lane takes part in the shuffles
+  const T* xr = x + (idx ? static_cast<int64_t>(idx[rc]) : row0 + rc) * d;
+  float ss = 0.f;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    const int c = (q * LPR + li) * VEC;
+    const uint4 u = *reinterpret_cast<const uint4*>(xr + c);
+    float v[VEC];
+    if constexpr (VEC == 8) {
+      unpack8(u, v);
+    } else {
+      v[0] = __uint_as_float(u.x); v[1] = __uint_as_float(u.y);
+      v[2] = __uint_as_float(u.z); v[3] = __uint_as_float(u.w);
+    }
+#pragma unroll
+    for (int e = 0; e < VEC; e += 4) {
+      const float4 g4 = *reinterpret_cast<const float4*>(g + c + e);
+      const float vg[4] = {v[e] * g4.x, v[e + 1] * g4.y, v[e + 2] * g4.z, v[e + 3] * g4.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) ss += v[e + k] * v[e + k];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        if (t >= nt) break;
+        const float4 w4 = *reinterpret_cast<const float4*>(w + t * d + c + e);
+        acc[t] += vg[0] * w4.x + vg[1] * w4.y + vg[2] * w4.z + vg[3] * w4.w;
+      }
+    }
+  }
+#pragma unroll
+  for (int o = LPR / 2; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    if (t >= nt) break;
+#pragma unroll
+    for (int o = LPR / 2; o > 0; o >>= 1) acc[t] += __shfl_xor(acc[t], o);
+  }
+  const float inv = rsqrtf(ss / d + RMS_EPS);
+  if (r >= rows || li != 0) return;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    if (t >= nt) break;
+    logits[r * nt + t] = acc[t] * inv + b[t];
+  }
+}
+
 // z = rmsnorm(x) g; dz = dlogits . w; dx by the RMSNorm backward with dz as the output
 // gradient; dw[t] = sum dlogits[t] z; db[t] = sum dlogits[t]; dg = sum dz x r.  One wave per
 // row (grid stride), lane l owning columns 4 l + 256 q; the block's waves add their
@@ -496,10 +557,44 @@ genrank_status launch_fill_zero(int dtype, void* p, int64_t n, hipStream_t strea
   return GENRANK_OK;
 }
 
+template <typename T>
+static bool launch_head_fwd_vec(const T* x, int64_t row0, int64_t rows, const int32_t* idx, int d,
+                                const float* g, const float* w, const float* bias, int nt, float* logits,
+                                hipStream_t stream) {
+  constexpr int VEC = 16 / static_cast<int>(sizeof(T));
+  if (d % VEC != 0 || ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(g) |
+                        reinterpret_cast<uintptr_t>(w)) & 15u))
+    return false;
+  auto go = [&](auto kernel, int lpr) {
+    const int64_t per_block = (RW / 64) * (64 / lpr);
+    hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>((rows + per_block - 1) / per_block)), dim3(RW), 0,
+                       stream, x, row0, rows, idx, d, g, w, bias, nt, logits);
+    return true;
+  };
+  switch (d / VEC) {
+    case 4: return go(head_fwd_vec_kernel<T, 4, 1>, 4);
+    case 8: return go(head_fwd_vec_kernel<T, 8, 1>, 8);
+    case 16: return go(head_fwd_vec_kernel<T, 16, 1>, 16);
+    case 32: return go(head_fwd_vec_kernel<T, 32, 1>, 32);
+    case 64: return go(head_fwd_vec_kernel<T, 64, 1>, 64);
+    case 128: return go(head_fwd_vec_kernel<T, 64, 2>, 64);
+    default: return false;
+  }
+}
+
 genrank_status launch_head_fwd(int dtype, const void* x, int64_t row0, int64_t rows, const int32_t* idx,
                                int d, const float* g, const float* w, const float* bias, int nt,
                                float* logits, hipStream_t stream) {
   if (rows <= 0) return GENRANK_OK;
+  const bool vec = dtype == GENRANK_BF16
+                       ? launch_head_fwd_vec(static_cast<const bf16_t*>(x), row0, rows, idx, d, g, w, bias, nt,
+                                             logits, stream)
+                       : launch_head_fwd_vec(static_cast<const float*>(x), row0, rows, idx, d, g, w, bias, nt,
+                                             logits, stream);
+  if (vec) {
+    GR_CHECK_LAUNCH();
+    return GENRANK_OK;
+  }
   const unsigned grid = static_cast<unsigned>((rows + 3) / 4);
   if (dtype == GENRANK_BF16)
     hipLaunchKernelGGL(head_fwd_kernel<bf16_t>, dim3(grid), dim3(RW), 0, stream,
