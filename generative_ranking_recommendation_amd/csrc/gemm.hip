@@ -54,6 +54,35 @@ constexpr int CP = GBN + 8;                           // staged C row pitch (bf1
 constexpr int SMEM_OPS = 2 * 2 * GBM * GBK;           // [stage][A|W] operand tiles
 constexpr int SMEM = SMEM_OPS > GBM * CP ? SMEM_OPS : GBM * CP;
 
+// ---- element-wise epilogue math on C[m][n .. n+3] (in f32, before the bf16 store)
+template <int EPI>
+__device__ __forceinline__ void epi_math(const GemmArgs& g, int m, int n, float (&v)[4]) {
+  if constexpr (EPI == GEMM_EPI_RESID) {
+    if (m < g.M) {
+      const uint2 r = *reinterpret_cast<const uint2*>(g.R + static_cast<int64_t>(m) * g.ldr + n);
+      v[0] += __uint_as_float(r.x << 16); v[1] += __uint_as_float(r.x & 0xFFFF0000u);
+      v[2] += __uint_as_float(r.y << 16); v[3] += __uint_as_float(r.y & 0xFFFF0000u);
+    }
+  }
+  if constexpr (EPI == GEMM_EPI_DSILU) {
+    if (m < g.M) {
+      const uint2 r = *reinterpret_cast<const uint2*>(g.R + static_cast<int64_t>(m) * g.ldr + n);
+      v[0] *= dsilu_f(__uint_as_float(r.x << 16)); v[1] *= dsilu_f(__uint_as_float(r.x & 0xFFFF0000u));
+      v[2] *= dsilu_f(__uint_as_float(r.y << 16)); v[3] *= dsilu_f(__uint_as_float(r.y & 0xFFFF0000u));
+    }
+  }
+  if constexpr (EPI == GEMM_EPI_SILU) {
+    if (g.Cpre && m < g.M) {
+      uint2 p;
+      p.x = pack_bf16x2(v[0], v[1]);
+      p.y = pack_bf16x2(v[2], v[3]);
+      *reinterpret_cast<uint2*>(g.Cpre + static_cast<int64_t>(m) * g.ldpre + n) = p;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = silu_f(v[i]);
+  }
+}
+
 // ---- epilogue shared by the MFMA kernels: lane holds C[m][n .. n+3] for each (nb, mb).
 // The 128 x 128 tile (after the epilogue math, in the output dtype) is staged through LDS,
 // rows 0-63 at sC_lo and rows 64-127 at sC_hi (pitch CP), so that every global store is a
@@ -86,30 +115,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, const f32x4_t (&acc)
       const int nl = wn * 64 + nb * 16 + g4 * 4;
       const int n = n0 + nl;
       float v[4] = {acc[nb][mb][0], acc[nb][mb][1], acc[nb][mb][2], acc[nb][mb][3]};
-      if constexpr (EPI == GEMM_EPI_RESID) {
-        if (m < g.M) {
-          const uint2 r = *reinterpret_cast<const uint2*>(g.R + static_cast<int64_t>(m) * g.ldr + n);
-          v[0] += __uint_as_float(r.x << 16); v[1] += __uint_as_float(r.x & 0xFFFF0000u);
-          v[2] += __uint_as_float(r.y << 16); v[3] += __uint_as_float(r.y & 0xFFFF0000u);
-        }
-      }
-      if constexpr (EPI == GEMM_EPI_DSILU) {
-        if (m < g.M) {
-          const uint2 r = *reinterpret_cast<const uint2*>(g.R + static_cast<int64_t>(m) * g.ldr + n);
-          v[0] *= dsilu_f(__uint_as_float(r.x << 16)); v[1] *= dsilu_f(__uint_as_float(r.x & 0xFFFF0000u));
-          v[2] *= dsilu_f(__uint_as_float(r.y << 16)); v[3] *= dsilu_f(__uint_as_float(r.y & 0xFFFF0000u));
-        }
-      }
-      if constexpr (EPI == GEMM_EPI_SILU) {
-        if (g.Cpre && m < g.M) {
-          uint2 p;
-          p.x = pack_bf16x2(v[0], v[1]);
-          p.y = pack_bf16x2(v[2], v[3]);
-          *reinterpret_cast<uint2*>(g.Cpre + static_cast<int64_t>(m) * g.ldpre + n) = p;
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = silu_f(v[i]);
-      }
+      epi_math<EPI>(g, m, n, v);
       uint2 o;
       o.x = pack_bf16x2(v[0], v[1]);
       o.y = pack_bf16x2(v[2], v[3]);
@@ -311,6 +317,126 @@ __global__ void __launch_bounds__(GTHREADS) gemm_nt_bf16_dma_kernel(GemmArgs g) 
   lds_barrier();  // every wave is done with the stage buffers before C goes into st0 / st1
 
   epilogue<EPI>(g, acc, st0, st1, m0, n0, wm, wn, l16, g4, tid);
+}
+
+// ------------------------------------------------------------------ 256 x 256 tiles
+// For the MFMA-bound shapes (K >= 512): the same direct-load ring with 256 x 256 tiles and
+// 8 waves in a 2 (M) x 4 (N) grid, each wave 128 x 64 (32 MFMAs per K tile).  Per K tile a
+// wave reads 12 KB of operands from LDS for 32 MFMAs, against 8 KB for 16 with 64 x 64
+// waves, so LDS traffic no longer matches the MFMA time.  One workgroup per CU (four
+// 33 KB stage buffers); the C tile is staged through all four buffers, 64 rows each.
+constexpr int BBM = 256, BBN = 256, BTHREADS = 512;
+constexpr int BCP = BBN + 8;  // staged C row pitch (bf16)
+constexpr int BSTAGE_ELEMS = (2 * BBM * GBK > 64 * BCP) ? 2 * BBM * GBK : 64 * BCP;
+
+template <int EPI>
+__global__ void __launch_bounds__(BTHREADS) gemm_nt_bf16_big_kernel(GemmArgs g) {
+  __shared__ __attribute__((aligned(16))) bf16_t st0[BSTAGE_ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16_t st1[BSTAGE_ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16_t st2[BSTAGE_ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16_t st3[BSTAGE_ELEMS];
+
+  const int nN = g.N / BBN;
+  const int nM = (g.M + BBM - 1) / BBM;
+  const int L = xcd_local_id(blockIdx.x, nN * nM);
+  const int mblk = L / nN;
+  const int m0 = mblk * BBM;
+  const int n0 = (L - mblk * nN) * BBN;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 1, wn = wave >> 1;
+  const int l16 = lane & 15, g4 = lane >> 4;
+
+  // direct loads as in gemm_nt_bf16_dma_kernel: wave w fills rows 32 w .. 32 w + 31 of the
+  // A tile and of the W tile (256 rows each), 16 rows (1 KB) per load
+  const int lr = lane >> 2, ls = lane & 3;
+  const int r0 = wave * 32 + lr, r1 = r0 + 16;
+  const int c0 = ls ^ ((r0 >> 1) & 3), c1 = ls ^ ((r1 >> 1) & 3);
+  const bf16_t* gA0 = g.A + static_cast<int64_t>(min(m0 + r0, g.M - 1)) * g.lda + c0 * 8;
+  const bf16_t* gA1 = g.A + static_cast<int64_t>(min(m0 + r1, g.M - 1)) * g.lda + c1 * 8;
+  const bf16_t* gW0 = g.W + static_cast<int64_t>(n0 + r0) * g.ldw + c0 * 8;
+  const bf16_t* gW1 = g.W + static_cast<int64_t>(n0 + r1) * g.ldw + c1 * 8;
+  const int dA0 = wave * 32 * GBK, dA1 = dA0 + 16 * GBK;
+  auto load = [&](int kt, bf16_t* stg) {
+    const int k0 = kt * GBK;
+    __builtin_amdgcn_global_load_lds((glb_void_t*)(gA0 + k0), (lds_void_t*)(stg + dA0), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((glb_void_t*)(gA1 + k0), (lds_void_t*)(stg + dA1), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((glb_void_t*)(gW0 + k0), (lds_void_t*)(stg + BBM * GBK + dA0), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((glb_void_t*)(gW1 + k0), (lds_void_t*)(stg + BBM * GBK + dA1), 16, 0, 0);
+  };
+
+  f32x4_t acc[4][8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](const bf16_t* stg) {
+    bf16x8_t fw[4], fa[8];
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+      fw[nb] = as_bf16x8(*reinterpret_cast<const uint4*>(stg + BBM * GBK + swz(wn * 64 + nb * 16 + l16, g4)));
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb)
+      fa[mb] = as_bf16x8(*reinterpret_cast<const uint4*>(stg + swz(wm * 128 + mb * 16 + l16, g4)));
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int mb = 0; mb < 8; ++mb)
+        acc[nb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fw[nb], fa[mb], acc[nb][mb], 0, 0, 0);
+  };
+
+  const int nk = g.K / GBK;  // a multiple of 4
+  load(0, st0);
+  load(1, st1);
+  load(2, st2);
+  int kt = 0;
+  for (; kt + 4 < nk; kt += 4) {
+    wait_vmcnt<8>(); lds_barrier(); load(kt + 3, st3); compute(st0);
+    wait_vmcnt<8>(); lds_barrier(); load(kt + 4, st0); compute(st1);
+    wait_vmcnt<8>(); lds_barrier(); load(kt + 5, st1); compute(st2);
+    wait_vmcnt<8>(); lds_barrier(); load(kt + 6, st2); compute(st3);
+  }
+  wait_vmcnt<8>(); lds_barrier(); load(kt + 3, st3); compute(st0);
+  wait_vmcnt<8>(); lds_barrier(); compute(st1);
+  wait_vmcnt<4>(); lds_barrier(); compute(st2);
+  wait_vmcnt<0>(); lds_barrier(); compute(st3);
+  lds_barrier();  // every wave is done with the stage buffers before C goes into them
+
+  // epilogue: rows 64 q .. 64 q + 63 of the C tile in buffer q; a wave's rows
+  // wm * 128 + mb * 16 + l16 fall in buffers 2 wm (mb < 4) and 2 wm + 1
+  bf16_t* cb_lo = wm ? st2 : st0;
+  bf16_t* cb_hi = wm ? st3 : st1;
+#pragma unroll
+  for (int mb = 0; mb < 8; ++mb) {
+    const int ml = wm * 128 + mb * 16 + l16;
+    const int m = m0 + ml;
+    bf16_t* cb = mb < 4 ? cb_lo : cb_hi;
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const int nl = wn * 64 + nb * 16 + g4 * 4;
+      float v[4] = {acc[nb][mb][0], acc[nb][mb][1], acc[nb][mb][2], acc[nb][mb][3]};
+      epi_math<EPI>(g, m, n0 + nl, v);
+      uint2 o;
+      o.x = pack_bf16x2(v[0], v[1]);
+      o.y = pack_bf16x2(v[2], v[3]);
+      *reinterpret_cast<uint2*>(cb + (ml & 63) * BCP + nl) = o;
+    }
+  }
+  __syncthreads();
+  // 256 rows x 512 B: 32 threads per row, 16 rows per pass
+  bf16_t* C = static_cast<bf16_t*>(g.C);
+#pragma unroll
+  for (int pass = 0; pass < BBM / 16; ++pass) {
+    const int ml = pass * 16 + (tid >> 5);
+    const int m = m0 + ml;
+    if (m >= g.M) continue;
+    const int nl = (tid & 31) * 8;
+    const bf16_t* cb = pass < 4 ? st0 : (pass < 8 ? st1 : (pass < 12 ? st2 : st3));
+    *reinterpret_cast<uint4*>(C + static_cast<int64_t>(m) * g.ldc + n0 + nl) =
+        *reinterpret_cast<const uint4*>(cb + (ml & 63) * BCP + nl);
+  }
 }
 
 // ------------------------------------------------------------------ general GEMM
@@ -551,6 +677,28 @@ genrank_status launch_gemm_nt(int dtype, const void* A, int64_t lda, const void*
     GemmArgs g{static_cast<const bf16_t*>(A), lda, static_cast<const bf16_t*>(W), ldw, C, ldc,
                static_cast<const bf16_t*>(R), ldr, static_cast<bf16_t*>(Cpre), ldpre, M, N, K};
     const int grid = (N / GBN) * ((M + GBM - 1) / GBM);
+    if (K % (4 * GBK) == 0 && K >= 512 && N % BBN == 0 && M >= 4 * BBM &&
+        static_cast<int64_t>(BBN) * ldw * 2 < (int64_t(1) << 32)) {
+      const int bgrid = (N / BBN) * ((M + BBM - 1) / BBM);
+      switch (epi) {
+        case GEMM_EPI_STORE:
+          hipLaunchKernelGGL(gemm_nt_bf16_big_kernel<GEMM_EPI_STORE>, dim3(bgrid), dim3(BTHREADS), 0, stream, g);
+          break;
+        case GEMM_EPI_RESID:
+          hipLaunchKernelGGL(gemm_nt_bf16_big_kernel<GEMM_EPI_RESID>, dim3(bgrid), dim3(BTHREADS), 0, stream, g);
+          break;
+        case GEMM_EPI_SILU:
+          hipLaunchKernelGGL(gemm_nt_bf16_big_kernel<GEMM_EPI_SILU>, dim3(bgrid), dim3(BTHREADS), 0, stream, g);
+          break;
+        case GEMM_EPI_DSILU:
+          hipLaunchKernelGGL(gemm_nt_bf16_big_kernel<GEMM_EPI_DSILU>, dim3(bgrid), dim3(BTHREADS), 0, stream, g);
+          break;
+        default:
+          return GENRANK_E_ARG;
+      }
+      GR_CHECK_LAUNCH();
+      return GENRANK_OK;
+    }
     if (K % (4 * GBK) == 0) {
       switch (epi) {
         case GEMM_EPI_STORE:

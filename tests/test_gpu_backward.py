@@ -172,3 +172,14 @@ def test_train_step_bf16_subset():
     cfg = synth.make_config("train2_bf16")
     batch = synth.make_batch(cfg, B=4)
     _compare_train(cfg, batch, tables_for("train2_bf16"), synth.make_weights(cfg), None)
+
+
+def test_train_step_bf16_d512():
+    """The 4-layer stack's widths (d = 512, 8 heads, FFN 2048) in two blocks on 3 users (1,352
+    rows): the backward's projections with K >= 512 run on the 256 x 256-tile kernel,
+    the SiLU-derivative epilogue included."""
+    say("bwd: train step bf16 d=512")
+    cfg = synth.make_config("stack4_bf16", layers=2, m=64, n_item=5000)  # ids drawn below n_item
+    batch = custom_batch(cfg, [480, 480, 200], seed=12)
+    assert int(max(batch.hist_items.max(), batch.cand_items.max())) < cfg.n_item
+    _compare_train(cfg, batch, synth.make_tables(cfg), synth.make_weights(cfg), None)

@@ -31,6 +31,7 @@ def _bound(a64, w64, want, K):
     (1, 128, 128), (127, 256, 256), (129, 768, 256), (1000, 256, 512), (4099, 128, 2048),
     (300, 512, 96), (64, 128, 32),     # K not a multiple of 128: the register-staged kernel
     (30011, 768, 256), (66000, 256, 512),  # many tiles, ragged M
+    (3001, 512, 512), (2049, 1536, 512), (1500, 256, 2048),  # 256 x 256 tiles (K >= 512)
 ])
 def test_linear_bf16_store(M, N, K):
     say(f"linear: bf16 M={M} N={N} K={K}")
@@ -47,7 +48,7 @@ def test_linear_bf16_store(M, N, K):
     assert np.all(got[:M, N:] == 7.0) and np.all(got[M:] == 7.0)
 
 
-@pytest.mark.parametrize("M,N,K", [(515, 256, 256), (130, 128, 512)])
+@pytest.mark.parametrize("M,N,K", [(515, 256, 256), (130, 128, 512), (2000, 512, 512)])
 def test_linear_bf16_residual_in_place(M, N, K):
     say(f"linear: bf16 residual M={M} N={N} K={K}")
     a, w, a64, w64 = _operands(M, N, K, seed=3 * M + K)
@@ -61,7 +62,7 @@ def test_linear_bf16_residual_in_place(M, N, K):
     assert np.all(err <= _bound(a64, w64, want, K) + 2.0 ** -8 * np.abs(r.f32())), float(err.max())
 
 
-@pytest.mark.parametrize("M,N,K", [(333, 1024, 256), (64, 128, 96)])
+@pytest.mark.parametrize("M,N,K", [(333, 1024, 256), (64, 128, 96), (1300, 2048, 512)])
 def test_linear_bf16_silu_with_pre(M, N, K):
     say(f"linear: bf16 silu M={M} N={N} K={K}")
     a, w, a64, w64 = _operands(M, N, K, seed=5 * M + N)
