@@ -113,3 +113,41 @@ def test_layer_bf16_full_size_sampled():
     rows = np.concatenate([oracle.user_rows(batch.hist_offsets, cfg.m, u) for u in users])
     sub_rows = np.concatenate([oracle.user_rows(sub.hist_offsets, cfg.m, i) for i in range(len(users))])
     bf16_close(gy[rows], wy[sub_rows], "y (sampled users)")
+
+
+def test_stack_bf16_full_size_sampled():
+    """The full 4-layer stack batch (512 users, 480 history actions and 256 candidates each:
+    376,832 rows, d = 512) in the launches the benchmark runs (the 256 x 256-tile
+    projections included); 3 users' logits and final hidden states checked against the
+    oracle on those users alone (users are independent).  Logit bars as for the small
+    stack batch: rms within 1.25x of the bf16-storage-only error, max within
+    max(2e-2, 1.5x the storage-only max)."""
+    say("layer: bf16 stack4 full batch, sampled users")
+    cfg = synth.make_config("stack4_bf16")
+    batch = synth.make_batch(cfg)
+    tables, weights = tables_for("stack4_bf16"), synth.make_weights(cfg)
+    sp, st = gpu_slopes(cfg)
+    model = GenRank.from_host(cfg, tables, weights, sp, st, DEV)
+    inp = DeviceInputs(batch, DEV)
+    y, logits = model.forward(inp)
+    users = [0, 257, 511]
+    rows = np.concatenate([oracle.user_rows(batch.hist_offsets, cfg.m, u) for u in users])
+    gy = to_numpy(y[torch.as_tensor(rows, device=DEV)])
+    gl = logits.view(batch.B, cfg.m, -1)[torch.as_tensor(users, device=DEV)].reshape(-1, logits.shape[1])
+    gl = gl.cpu().numpy().astype(np.float64)
+    finite = bool(torch.isfinite(logits).all()) and bool(torch.isfinite(y).all())
+    del y, logits, model
+    torch.cuda.synchronize()
+    assert finite
+    sub = batch.subset(users)
+    c = cfg.replace(B=len(users))
+    wy, wl = _oracle_forward(c, sub, tables, weights)
+    _, sl = _oracle_forward(c, sub, tables, weights, store=oracle.round_bf16)
+    rms = lambda e: float(np.sqrt(np.mean(np.square(e))))
+    e_gpu, e_store = gl - wl, sl - wl
+    say(f"  logits: gpu rms {rms(e_gpu):.4f} max {np.abs(e_gpu).max():.4f}; "
+        f"bf16 storage alone rms {rms(e_store):.4f} max {np.abs(e_store).max():.4f}")
+    assert rms(e_gpu) <= 1.25 * rms(e_store), (rms(e_gpu), rms(e_store))
+    unit_close(gl, wl, "logits", tol=max(2e-2, 1.5 * float(np.abs(e_store).max())))
+    sub_rows = np.concatenate([oracle.user_rows(sub.hist_offsets, cfg.m, i) for i in range(len(users))])
+    bf16_close(gy, wy[sub_rows], "final hidden state (sampled users)")
