@@ -47,6 +47,7 @@ struct LayerFwdWs {
   char* z2;   // [T, d]   rmsnorm(x1) g2         (PRENORM)
   char* a;    // [T, f]   FFN pre-activation     (PRENORM)
   char* hdn;  // [T, f]   silu(a)                (PRENORM)
+  char* wg;   // [max(3d, f), d] a weight with the RMSNorm gain folded in (PRENORM, fused path)
   size_t bytes;
 };
 
@@ -70,8 +71,20 @@ LayerFwdWs layer_fwd_layout(const genrank_batch* b, int block, int ffn, char* ba
   w.z2 = pre ? take(T * d * es) : nullptr;
   w.a = pre ? take(T * static_cast<size_t>(ffn) * es) : nullptr;
   w.hdn = pre ? take(T * static_cast<size_t>(ffn) * es) : nullptr;
+  w.wg = pre ? take(std::max(3 * d, static_cast<size_t>(ffn)) * d * es) : nullptr;
   w.bytes = off;
   return w;
+}
+
+// The pre-norm block's RMSNorm goes into the GEMMs that read its output (the norm's scale
+// applied to the GEMM rows, its gain folded into the weight) when every such GEMM fits the
+// fused kernel.  The choice depends on the widths only, so the full forward, the history
+// key/value projection and the candidate-only forward take the same arithmetic for a row.
+// A forward that saves activations for the backward keeps the normalised rows.
+bool rms_fused(const genrank_batch* b, const genrank_layer_weights* w) {
+  const int d = b->d;
+  return w->block == GENRANK_BLOCK_PRENORM && b->dtype == GENRANK_BF16 && gemm_rms_ok(3 * d, d) &&
+         gemm_rms_ok(2 * d, d) && gemm_rms_ok(w->ffn_dim, d);
 }
 
 struct LayerBwdWs {
@@ -187,8 +200,10 @@ genrank_status check_cached_attn(const genrank_batch* b, const void* q, const vo
   return GENRANK_OK;
 }
 size_t layer_kv_bytes(const genrank_batch* b, const genrank_layer_weights* w) {
-  return w->block == GENRANK_BLOCK_PRENORM ? align_up(static_cast<size_t>(b->total_hist) * b->d * dtype_size(b->dtype))
-                                           : 0;
+  const size_t es = dtype_size(b->dtype), d = b->d;
+  return w->block == GENRANK_BLOCK_PRENORM
+             ? align_up(static_cast<size_t>(b->total_hist) * d * es) + align_up(2 * d * d * es)
+             : 0;
 }
 size_t layer_fwd_cached_bytes(const genrank_batch* b, const genrank_layer_weights* w) {
   const genrank_batch c = cand_rows_batch(b);
@@ -384,13 +399,19 @@ genrank_status genrank_layer_fwd(const genrank_batch* b, const genrank_layer_wei
   if (T == 0) return GENRANK_OK;
   GR_TRY(check_attn_args(b, offsets, ts, req, w->alibi, L.qkv, L.qkv + d * es, L.qkv + 2 * d * es,
                          3 * d, L.o, d));
-  const void* zin = x_in;
-  if (pre) {
-    GR_TRY(launch_rmsnorm(dt, x_in, w->g1, L.z, T, d, s));
-    zin = L.z;
+  const bool fuse = pre && rms_fused(b, w) && !(flags & GENRANK_FWD_SAVE);
+  if (fuse) {
+    GR_TRY(launch_scale_cols(w->wqkv, d, w->g1, L.wg, d, 3 * d, d, s));
+    GR_TRY(launch_gemm_nt_rms(x_in, d, L.wg, d, L.qkv, 3 * d, T, 3 * d, d, GEMM_EPI_STORE, s));
+  } else {
+    const void* zin = x_in;
+    if (pre) {
+      GR_TRY(launch_rmsnorm(dt, x_in, w->g1, L.z, T, d, s));
+      zin = L.z;
+    }
+    GR_TRY(launch_gemm_nt(dt, zin, d, w->wqkv, d, L.qkv, 3 * d, T, 3 * d, d, GEMM_EPI_STORE,
+                          nullptr, 0, nullptr, 0, s));
   }
-  GR_TRY(launch_gemm_nt(dt, zin, d, w->wqkv, d, L.qkv, 3 * d, T, 3 * d, d, GEMM_EPI_STORE,
-                        nullptr, 0, nullptr, 0, s));
   GR_TRY(launch_attn_fwd(b, offsets, ts, req, w->alibi, L.qkv, L.qkv + d * es, L.qkv + 2 * d * es,
                          3 * d, L.o, d, L.lse, s));
   if (!pre) {
@@ -399,9 +420,14 @@ genrank_status genrank_layer_fwd(const genrank_batch* b, const genrank_layer_wei
   }
   GR_TRY(launch_gemm_nt(dt, L.o, d, w->wo, d, L.x1, d, T, d, d, GEMM_EPI_RESID, x_in, d, nullptr,
                         0, s));
-  GR_TRY(launch_rmsnorm(dt, L.x1, w->g2, L.z2, T, d, s));
-  GR_TRY(launch_gemm_nt(dt, L.z2, d, w->w1, d, L.hdn, ffn, T, ffn, d, GEMM_EPI_SILU, nullptr, 0,
-                        (flags & GENRANK_FWD_SAVE) ? L.a : nullptr, ffn, s));
+  if (fuse) {
+    GR_TRY(launch_scale_cols(w->w1, d, w->g2, L.wg, d, ffn, d, s));
+    GR_TRY(launch_gemm_nt_rms(L.x1, d, L.wg, d, L.hdn, ffn, T, ffn, d, GEMM_EPI_SILU, s));
+  } else {
+    GR_TRY(launch_rmsnorm(dt, L.x1, w->g2, L.z2, T, d, s));
+    GR_TRY(launch_gemm_nt(dt, L.z2, d, w->w1, d, L.hdn, ffn, T, ffn, d, GEMM_EPI_SILU, nullptr, 0,
+                          (flags & GENRANK_FWD_SAVE) ? L.a : nullptr, ffn, s));
+  }
   return launch_gemm_nt(dt, L.hdn, ffn, w->w2, ffn, y_out, d, T, d, ffn, GEMM_EPI_RESID, L.x1, d,
                         nullptr, 0, s);
 }
@@ -439,13 +465,18 @@ genrank_status genrank_layer_kv(const genrank_batch* b, const genrank_layer_weig
   const hipStream_t s = S(stream);
   const int dt = b->dtype;
   const int d = b->d;
+  // rows [d, 3d) of wqkv: the key and value projections
+  const char* wkv = static_cast<const char*>(w->wqkv) + static_cast<size_t>(d) * d * dtype_size(dt);
+  if (rms_fused(b, w)) {
+    char* wg = static_cast<char*>(ws) + align_up(static_cast<size_t>(Th) * d * dtype_size(dt));
+    GR_TRY(launch_scale_cols(wkv, d, w->g1, wg, d, 2 * d, d, s));
+    return launch_gemm_nt_rms(x_hist, d, wg, d, kv, ld_kv, static_cast<int>(Th), 2 * d, d, GEMM_EPI_STORE, s);
+  }
   const void* z = x_hist;
   if (w->block == GENRANK_BLOCK_PRENORM) {
     GR_TRY(launch_rmsnorm(dt, x_hist, w->g1, ws, Th, d, s));
     z = ws;
   }
-  // rows [d, 3d) of wqkv: the key and value projections
-  const char* wkv = static_cast<const char*>(w->wqkv) + static_cast<size_t>(d) * d * dtype_size(dt);
   return launch_gemm_nt(dt, z, d, wkv, d, kv, ld_kv, static_cast<int>(Th), 2 * d, d, GEMM_EPI_STORE, nullptr, 0,
                         nullptr, 0, s);
 }
@@ -472,20 +503,32 @@ genrank_status genrank_layer_fwd_cached(const genrank_batch* b, const genrank_la
                            kh ? kh + d * es : L.qkv, ld_kv, L.o, d));
   if (Tc == 0) return GENRANK_OK;
   const hipStream_t s = S(stream);
-  const void* zin = x_cand;
-  if (pre) {
-    GR_TRY(launch_rmsnorm(dt, x_cand, w->g1, L.z, Tc, d, s));
-    zin = L.z;
+  const bool fuse = pre && rms_fused(b, w);
+  if (fuse) {
+    GR_TRY(launch_scale_cols(w->wqkv, d, w->g1, L.wg, d, 3 * d, d, s));
+    GR_TRY(launch_gemm_nt_rms(x_cand, d, L.wg, d, L.qkv, 3 * d, Tc, 3 * d, d, GEMM_EPI_STORE, s));
+  } else {
+    const void* zin = x_cand;
+    if (pre) {
+      GR_TRY(launch_rmsnorm(dt, x_cand, w->g1, L.z, Tc, d, s));
+      zin = L.z;
+    }
+    GR_TRY(launch_gemm_nt(dt, zin, d, w->wqkv, d, L.qkv, 3 * d, Tc, 3 * d, d, GEMM_EPI_STORE, nullptr, 0, nullptr,
+                          0, s));
   }
-  GR_TRY(launch_gemm_nt(dt, zin, d, w->wqkv, d, L.qkv, 3 * d, Tc, 3 * d, d, GEMM_EPI_STORE, nullptr, 0, nullptr,
-                        0, s));
   GR_TRY(launch_attn_fwd_cached(b, offsets, ts, req, w->alibi, L.qkv, L.qkv + d * es, L.qkv + 2 * d * es, 3 * d,
                                 kh ? kh : L.qkv, kh ? kh + d * es : L.qkv, ld_kv, L.o, d, L.lse, s));
   if (!pre)
     return launch_gemm_nt(dt, L.o, d, w->wo, d, y_cand, d, Tc, d, d, GEMM_EPI_STORE, nullptr, 0, nullptr, 0, s);
   GR_TRY(launch_gemm_nt(dt, L.o, d, w->wo, d, L.x1, d, Tc, d, d, GEMM_EPI_RESID, x_cand, d, nullptr, 0, s));
-  GR_TRY(launch_rmsnorm(dt, L.x1, w->g2, L.z2, Tc, d, s));
-  GR_TRY(launch_gemm_nt(dt, L.z2, d, w->w1, d, L.hdn, ffn, Tc, ffn, d, GEMM_EPI_SILU, nullptr, 0, nullptr, ffn, s));
+  if (fuse) {
+    GR_TRY(launch_scale_cols(w->w1, d, w->g2, L.wg, d, ffn, d, s));
+    GR_TRY(launch_gemm_nt_rms(L.x1, d, L.wg, d, L.hdn, ffn, Tc, ffn, d, GEMM_EPI_SILU, s));
+  } else {
+    GR_TRY(launch_rmsnorm(dt, L.x1, w->g2, L.z2, Tc, d, s));
+    GR_TRY(launch_gemm_nt(dt, L.z2, d, w->w1, d, L.hdn, ffn, Tc, ffn, d, GEMM_EPI_SILU, nullptr, 0, nullptr, ffn,
+                          s));
+  }
   return launch_gemm_nt(dt, L.hdn, ffn, w->w2, ffn, y_cand, d, Tc, d, ffn, GEMM_EPI_RESID, L.x1, d, nullptr, 0, s);
 }
 

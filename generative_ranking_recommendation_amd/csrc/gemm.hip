@@ -329,12 +329,18 @@ constexpr int BBM = 256, BBN = 256, BTHREADS = 512;
 constexpr int BCP = BBN + 8;  // staged C row pitch (bf16)
 constexpr int BSTAGE_ELEMS = (2 * BBM * GBK > 64 * BCP) ? 2 * BBM * GBK : 64 * BCP;
 
-template <int EPI>
+// RMS: the A rows are raw inputs x and W is the weight with the RMSNorm gain folded into its
+// columns (W g); the kernel forms each row's r = 1 / sqrt(mean(x^2) + eps) from the A tiles
+// it already holds in LDS (thread t sums the squares of half of row t / 2 of every K tile,
+// in K order, and a lane pair adds its halves) and scales the row by r before the
+// epilogue: rmsnorm(x) g . W^T = r (x . (W g)^T).  A row's r depends only on that row.
+template <int EPI, bool RMS>
 __global__ void __launch_bounds__(BTHREADS) gemm_nt_bf16_big_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) bf16_t st0[BSTAGE_ELEMS];
   __shared__ __attribute__((aligned(16))) bf16_t st1[BSTAGE_ELEMS];
   __shared__ __attribute__((aligned(16))) bf16_t st2[BSTAGE_ELEMS];
   __shared__ __attribute__((aligned(16))) bf16_t st3[BSTAGE_ELEMS];
+  __shared__ float sR[RMS ? BBM : 1];
 
   const int nN = g.N / BBN;
   const int nM = (g.M + BBM - 1) / BBM;
@@ -372,7 +378,18 @@ __global__ void __launch_bounds__(BTHREADS) gemm_nt_bf16_big_kernel(GemmArgs g) 
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int rr = tid >> 1, rc = (tid & 1) * 2;  // RMS: this thread's row and first chunk
+  float ss = 0.f;
   auto compute = [&](const bf16_t* stg) {
+    if constexpr (RMS) {
+      float f[8];
+      unpack8(*reinterpret_cast<const uint4*>(stg + swz(rr, rc)), f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss += f[e] * f[e];
+      unpack8(*reinterpret_cast<const uint4*>(stg + swz(rr, rc + 1)), f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss += f[e] * f[e];
+    }
     bf16x8_t fw[4], fa[8];
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb)
@@ -402,7 +419,13 @@ __global__ void __launch_bounds__(BTHREADS) gemm_nt_bf16_big_kernel(GemmArgs g) 
   wait_vmcnt<8>(); lds_barrier(); compute(st1);
   wait_vmcnt<4>(); lds_barrier(); compute(st2);
   wait_vmcnt<0>(); lds_barrier(); compute(st3);
-  lds_barrier();  // every wave is done with the stage buffers before C goes into them
+  if constexpr (RMS) {
+    ss += __shfl_xor(ss, 1);
+    if ((tid & 1) == 0) sR[rr] = rsqrtf(ss / static_cast<float>(g.K) + RMS_EPS);
+    lds_sync();  // sR written; every wave is done with the stage buffers
+  } else {
+    lds_barrier();  // every wave is done with the stage buffers before C goes into them
+  }
 
   // epilogue: rows 64 q .. 64 q + 63 of the C tile in buffer q; a wave's rows
   // wm * 128 + mb * 16 + l16 fall in buffers 2 wm (mb < 4) and 2 wm + 1
@@ -417,6 +440,11 @@ __global__ void __launch_bounds__(BTHREADS) gemm_nt_bf16_big_kernel(GemmArgs g) 
     for (int nb = 0; nb < 4; ++nb) {
       const int nl = wn * 64 + nb * 16 + g4 * 4;
       float v[4] = {acc[nb][mb][0], acc[nb][mb][1], acc[nb][mb][2], acc[nb][mb][3]};
+      if constexpr (RMS) {
+        const float r = sR[ml];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] *= r;
+      }
       epi_math<EPI>(g, m, n0 + nl, v);
       uint2 o;
       o.x = pack_bf16x2(v[0], v[1]);
@@ -436,6 +464,24 @@ __global__ void __launch_bounds__(BTHREADS) gemm_nt_bf16_big_kernel(GemmArgs g) 
     const bf16_t* cb = pass < 4 ? st0 : (pass < 8 ? st1 : (pass < 12 ? st2 : st3));
     *reinterpret_cast<uint4*>(C + static_cast<int64_t>(m) * g.ldc + n0 + nl) =
         *reinterpret_cast<const uint4*>(cb + (ml & 63) * BCP + nl);
+  }
+}
+
+// W'[n, k] = bf16(W[n, k] g[k]): the RMSNorm gain folded into a weight's input columns
+__global__ void scale_cols_bf16_kernel(const bf16_t* __restrict__ W, int64_t ldw, const float* __restrict__ gain,
+                                       bf16_t* __restrict__ out, int64_t ldo, int N, int K) {
+  const int kc = K / 8;
+  for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < static_cast<int64_t>(N) * kc;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int64_t n = i / kc;
+    const int k = static_cast<int>(i - n * kc) * 8;
+    float f[8];
+    unpack8(*reinterpret_cast<const uint4*>(W + n * ldw + k), f);
+    const float4 g0 = *reinterpret_cast<const float4*>(gain + k);
+    const float4 g1 = *reinterpret_cast<const float4*>(gain + k + 4);
+    f[0] *= g0.x; f[1] *= g0.y; f[2] *= g0.z; f[3] *= g0.w;
+    f[4] *= g1.x; f[5] *= g1.y; f[6] *= g1.z; f[7] *= g1.w;
+    *reinterpret_cast<uint4*>(out + n * ldo + k) = pack8(f);
   }
 }
 
@@ -682,16 +728,16 @@ genrank_status launch_gemm_nt(int dtype, const void* A, int64_t lda, const void*
       const int bgrid = (N / BBN) * ((M + BBM - 1) / BBM);
       switch (epi) {
         case GEMM_EPI_STORE:
-          hipLaunchKernelGGL(gemm_nt_bf16_big_kernel<GEMM_EPI_STORE>, dim3(bgrid), dim3(BTHREADS), 0, stream, g);
+          hipLaunchKernelGGL((gemm_nt_bf16_big_kernel<GEMM_EPI_STORE, false>), dim3(bgrid), dim3(BTHREADS), 0, stream, g);
           break;
         case GEMM_EPI_RESID:
-          hipLaunchKernelGGL(gemm_nt_bf16_big_kernel<GEMM_EPI_RESID>, dim3(bgrid), dim3(BTHREADS), 0, stream, g);
+          hipLaunchKernelGGL((gemm_nt_bf16_big_kernel<GEMM_EPI_RESID, false>), dim3(bgrid), dim3(BTHREADS), 0, stream, g);
           break;
         case GEMM_EPI_SILU:
-          hipLaunchKernelGGL(gemm_nt_bf16_big_kernel<GEMM_EPI_SILU>, dim3(bgrid), dim3(BTHREADS), 0, stream, g);
+          hipLaunchKernelGGL((gemm_nt_bf16_big_kernel<GEMM_EPI_SILU, false>), dim3(bgrid), dim3(BTHREADS), 0, stream, g);
           break;
         case GEMM_EPI_DSILU:
-          hipLaunchKernelGGL(gemm_nt_bf16_big_kernel<GEMM_EPI_DSILU>, dim3(bgrid), dim3(BTHREADS), 0, stream, g);
+          hipLaunchKernelGGL((gemm_nt_bf16_big_kernel<GEMM_EPI_DSILU, false>), dim3(bgrid), dim3(BTHREADS), 0, stream, g);
           break;
         default:
           return GENRANK_E_ARG;
@@ -741,6 +787,38 @@ genrank_status launch_gemm_nt(int dtype, const void* A, int64_t lda, const void*
   // C = A W^T : B[k, n] = W[n, k]
   return launch_gemm_general(dtype, dtype, A, lda, 1, W, 1, ldw, C, ldc, M, N, K, epi, false, R,
                              ldr, Cpre, ldpre, stream);
+}
+
+bool gemm_rms_ok(int N, int K) { return N > 0 && N % BBN == 0 && K >= 512 && K % (4 * GBK) == 0; }
+
+genrank_status launch_gemm_nt_rms(const void* A, int64_t lda, const void* Wg, int64_t ldw, void* C, int64_t ldc,
+                                  int M, int N, int K, int epi, hipStream_t stream) {
+  if (M <= 0) return GENRANK_OK;
+  if (!gemm_rms_ok(N, K) || lda % 8 || ldw % 8 || ldc % 8 || static_cast<int64_t>(BBN) * ldw * 2 >= (int64_t(1) << 32))
+    return GENRANK_E_SHAPE;
+  GemmArgs g{static_cast<const bf16_t*>(A), lda, static_cast<const bf16_t*>(Wg), ldw, C, ldc, nullptr, 0, nullptr, 0,
+             M, N, K};
+  const int bgrid = (N / BBN) * ((M + BBM - 1) / BBM);
+  if (epi == GEMM_EPI_STORE)
+    hipLaunchKernelGGL((gemm_nt_bf16_big_kernel<GEMM_EPI_STORE, true>), dim3(bgrid), dim3(BTHREADS), 0, stream, g);
+  else if (epi == GEMM_EPI_SILU)
+    hipLaunchKernelGGL((gemm_nt_bf16_big_kernel<GEMM_EPI_SILU, true>), dim3(bgrid), dim3(BTHREADS), 0, stream, g);
+  else
+    return GENRANK_E_ARG;
+  GR_CHECK_LAUNCH();
+  return GENRANK_OK;
+}
+
+genrank_status launch_scale_cols(const void* W, int64_t ldw, const float* gain, void* out, int64_t ldo, int N, int K,
+                                 hipStream_t stream) {
+  if (N <= 0) return GENRANK_OK;
+  if (K % 8 || ldw % 8 || ldo % 8) return GENRANK_E_SHAPE;
+  const int64_t n = static_cast<int64_t>(N) * (K / 8);
+  const unsigned grid = static_cast<unsigned>(std::min<int64_t>((n + 255) / 256, 2048));
+  hipLaunchKernelGGL(scale_cols_bf16_kernel, dim3(grid), dim3(256), 0, stream, static_cast<const bf16_t*>(W), ldw, gain,
+                     static_cast<bf16_t*>(out), ldo, N, K);
+  GR_CHECK_LAUNCH();
+  return GENRANK_OK;
 }
 
 genrank_status launch_gemm_general(int in_dtype, int out_dtype, const void* A, int64_t sam,

@@ -95,6 +95,14 @@ inline genrank_status check_alibi_variant(const genrank_alibi& a, int H) {
 genrank_status launch_gemm_nt(int dtype, const void* A, int64_t lda, const void* W, int64_t ldw,
                               void* C, int64_t ldc, int M, int N, int K, int epi, const void* R,
                               int64_t ldr, void* Cpre, int64_t ldpre, hipStream_t stream);
+// The bf16 GEMM with the RMSNorm of A's rows fused (A raw, Wg = W with the gain folded into
+// its columns, see launch_scale_cols); epi STORE or SILU; requires gemm_rms_ok(N, K)
+bool gemm_rms_ok(int N, int K);
+genrank_status launch_gemm_nt_rms(const void* A, int64_t lda, const void* Wg, int64_t ldw, void* C, int64_t ldc,
+                                  int M, int N, int K, int epi, hipStream_t stream);
+// out[n, k] = bf16(W[n, k] gain[k]) (bf16 W and out)
+genrank_status launch_scale_cols(const void* W, int64_t ldw, const float* gain, void* out, int64_t ldo, int N, int K,
+                                 hipStream_t stream);
 // General strided GEMM: C[m, n] (+)= sum_k A[m*sam + k*sak] B[k*sbk + n*sbn]
 genrank_status launch_gemm_general(int in_dtype, int out_dtype, const void* A, int64_t sam,
                                    int64_t sak, const void* Bm, int64_t sbk, int64_t sbn, void* C,

@@ -255,7 +255,13 @@ GENRANK_API genrank_status genrank_attn_bwd(const genrank_batch* batch, const in
  * x_in, y_out: [T, d] in batch.dtype; y_out may equal x_in (inference only: the backward
  * needs the block input).  ws: genrank_workspace_size(GENRANK_OP_LAYER_FWD) bytes.
  * flags: GENRANK_FWD_SAVE makes the workspace keep every activation genrank_layer_bwd
- * needs (keep it untouched until then); without it the FFN pre-activation is not stored. */
+ * needs (keep it untouched until then); without it the FFN pre-activation is not stored.
+ * Without GENRANK_FWD_SAVE, a bf16 pre-norm block with d >= 512, d % 256 == 0 and
+ * ffn_dim % 256 == 0 fuses each RMSNorm into the GEMM that reads it: rows are scaled by
+ * their 1/rms after the product with the gain-scaled weight, so the normalised rows are
+ * never stored and the result differs from the saving forward by bf16 rounding only.
+ * genrank_layer_kv and genrank_layer_fwd_cached take the same path under the same
+ * conditions (their rows equal this forward's bit for bit). */
 #define GENRANK_FWD_SAVE 1
 GENRANK_API genrank_status genrank_layer_fwd(const genrank_batch* batch, const genrank_layer_weights* w,
                                  const int32_t* hist_offsets, const int64_t* hist_ts,
