@@ -13,11 +13,12 @@ backward, table gradients) and the roofline is the attention backward's.
 With --workload hstu_interleaved it instead measures the HSTU-style comparison on the same
 users: the interleaved item/action sequence (2N + m slots) with a learned relative bias
 materialised in memory, against the action-oriented attention with in-register ALiBi.
-Forward workloads: a breakdown pass brackets every launch with HIP events (on the stream it
-runs on) to find the dominant kernel.  The timed pass then runs exactly --steps steps between
-device synchronisations with one event pair around that kernel alone (events between
-launches add gaps); its wall clock gives the step time and its events the roofline.  Prints
-ONE JSON line on stdout; progress goes to stderr.
+Forward workloads: each kernel is timed in a pass of its own with one HIP event pair around
+it (on the stream it runs on; events between every launch would add gaps), which also picks
+the dominant kernel.  The timed pass then runs exactly --steps steps between device
+synchronisations with one event pair around the dominant kernel alone; its wall clock gives
+the step time and its events the roofline.  Prints ONE JSON line on stdout; progress goes to
+stderr.
 """
 from __future__ import annotations
 
@@ -449,14 +450,15 @@ def bench_serve(args, cfg):
     torch.cuda.synchronize()
     if not torch.equal(y_full[T_h:], y):
         log("WARNING: cached scoring differs from the full forward")
-    # breakdown pass (events between all launches), then the timed pass with one event pair
-    # around the cached attention
-    events = [mk(len(names) + 1) for _ in range(args.steps)]
-    for k in range(args.steps):
-        step(events[k])
-    torch.cuda.synchronize()
-    per = {n: float(np.mean([events[k][i].elapsed_time(events[k][i + 1]) for k in range(args.steps)]))
-           for i, n in enumerate(names)}
+    # per-kernel passes (one event pair around one launch), then the timed pass with one
+    # event pair around the cached attention
+    per = {}
+    for i, n in enumerate(names):
+        events = [mk(2) for _ in range(args.steps)]
+        for k in range(args.steps):
+            step(events[k], only=i)
+        torch.cuda.synchronize()
+        per[n] = float(np.mean([events[k][0].elapsed_time(events[k][1]) for k in range(args.steps)]))
     events = [mk(2) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -611,15 +613,16 @@ def main():
         torch.cuda.synchronize()
         log(f"calibration copy of {args.calibrate_copy_mb} MiB done")
 
-    # breakdown pass: events between all launches; they add gaps between the launches, so
-    # this pass gives the per-kernel figures but not the step time
-    events = [mk(len(units) + 1) for _ in range(args.steps)]
-    for k in range(args.steps):
-        step(events[k])
-    torch.cuda.synchronize()
-    per = {n: float(np.mean([events[k][i].elapsed_time(events[k][i + 1]) for k in range(args.steps)]))
-           for i, n in enumerate(names)}
-    log("breakdown (ms): " + ", ".join(f"{k}={v:.4f}" for k, v in per.items()))
+    # per-kernel passes: --steps steps with one event pair around one launch (events
+    # between every launch would add gaps and inflate each kernel's figure)
+    per = {}
+    for n in names:
+        events = [mk(2) for _ in range(args.steps)]
+        for k in range(args.steps):
+            step(events[k], only=n)
+        torch.cuda.synchronize()
+        per[n] = float(np.mean([events[k][0].elapsed_time(events[k][1]) for k in range(args.steps)]))
+    log("per kernel (ms): " + ", ".join(f"{k}={v:.4f}" for k, v in per.items()))
 
     # algorithmic work per launch
     lengths = inp.lengths
@@ -702,8 +705,8 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernels": kernels,
-        "kernel_timing": "dominant kernel: event pair in the timed pass; the others: a separate pass with "
-                         "events between all launches (which adds gaps, so those figures run high)",
+        "kernel_timing": "each kernel: its own pass of --steps steps with one event pair around it; the "
+                         "dominant kernel: the event pair in the timed pass",
     }
     if attn_flops is not None:
         peak_f = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
