@@ -109,7 +109,7 @@ __device__ __forceinline__ void st4(float* p, const float* f) {
 // partial in registers, the block adds its waves' partials in order through LDS and
 // writes one partial row, and column_sum_kernel adds the blocks' rows in order.
 constexpr int MAXQ = 4;           // 4-column groups per lane: d <= 64 * 4 * MAXQ = 1024
-constexpr int PART_BLOCKS = 512;  // rmsnorm backward blocks (partial rows)
+constexpr int PART_BLOCKS = 1024;  // rmsnorm backward blocks (partial rows)
 
 // dx = r g dy - r^3 x sum(g dy x) / d  (+ add);  dg = sum over rows of dy x r.
 // Lane l owns columns 4 l + 256 q; a wave takes two rows per step.
@@ -273,6 +273,126 @@ __global__ void __launch_bounds__(RW) head_fwd_kernel(const T* __restrict__ x, i
     const float s = wave_sum(acc[t]);
     if (lane == 0) logits[r * nt + t] = s * inv + b[t];
   }
+}
+
+// RMSNorm backward with rows read through 16-byte loads (lane groups as rmsnorm_vec_kernel,
+// two rows per group in flight): dx = r g dy - r^3 x sum(g dy x) / d (+ add), and the
+// block's partial row of dg = sum over rows of dy x r.  The groups of a wave add their dg
+// partials by xor-shuffles, the block's waves in order through LDS: a fixed order.
+template <typename T, int LPR, int Q>
+__global__ void __launch_bounds__(RW) rmsnorm_bwd_vec_kernel(const T* __restrict__ x, const float* __restrict__ g,
+                                                             const T* dy, const T* add, T* dx,
+                                                             float* __restrict__ part, int64_t rows, int d) {
+  constexpr int VEC = 16 / static_cast<int>(sizeof(T));
+  constexpr int RPW = 64 / LPR;
+  constexpr int UR = 2;
+  __shared__ float sp[RW / 64][64 * Q * VEC];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int li = lane % LPR;
+  const int64_t ngroups = static_cast<int64_t>(gridDim.x) * (RW / 64) * RPW;
+  const int64_t gid = (static_cast<int64_t>(blockIdx.x) * (RW / 64) + wave) * RPW + lane / LPR;
+  auto load = [](const T* p, float* f) {
+    const uint4 u = *reinterpret_cast<const uint4*>(p);
+    if constexpr (VEC == 8) {
+      unpack8(u, f);
+    } else {
+      f[0] = __uint_as_float(u.x); f[1] = __uint_as_float(u.y);
+      f[2] = __uint_as_float(u.z); f[3] = __uint_as_float(u.w);
+    }
+  };
+  float pg[Q][VEC];
+#pragma unroll
+  for (int q = 0; q < Q; ++q)
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) pg[q][e] = 0.f;
+  for (int64_t r0 = gid; r0 < rows; r0 += UR * ngroups) {
+    float xv[UR][Q][VEC], gv[UR][Q][VEC], ss[UR], dot[UR];
+#pragma unroll
+    for (int k = 0; k < UR; ++k) {
+      const int64_t r = min(r0 + k * ngroups, rows - 1);  // every lane takes part in the shuffles
+#pragma unroll
+      for (int q = 0; q < Q; ++q) {
+        const int c = (q * LPR + li) * VEC;
+        load(x + r * d + c, xv[k][q]);
+        load(dy + r * d + c, gv[k][q]);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < UR; ++k) {
+      ss[k] = 0.f;
+      dot[k] = 0.f;
+#pragma unroll
+      for (int q = 0; q < Q; ++q) {
+        const int c = (q * LPR + li) * VEC;
+#pragma unroll
+        for (int e = 0; e < VEC; e += 4) {
+          const float4 g4 = *reinterpret_cast<const float4*>(g + c + e);
+          const float gg[4] = {g4.x, g4.y, g4.z, g4.w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            ss[k] += xv[k][q][e + i] * xv[k][q][e + i];
+            dot[k] += gg[i] * gv[k][q][e + i] * xv[k][q][e + i];
+          }
+        }
+      }
+#pragma unroll
+      for (int o = LPR / 2; o > 0; o >>= 1) {
+        ss[k] += __shfl_xor(ss[k], o);
+        dot[k] += __shfl_xor(dot[k], o);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < UR; ++k) {
+      const int64_t r = r0 + k * ngroups;
+      if (r >= rows) continue;
+      const float rr = rsqrtf(ss[k] / d + RMS_EPS);
+      const float c3 = rr * rr * rr * dot[k] / d;
+#pragma unroll
+      for (int q = 0; q < Q; ++q) {
+        const int c = (q * LPR + li) * VEC;
+        float ad[VEC], o[VEC];
+        if (add) {
+          load(add + r * d + c, ad);
+        } else {
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) ad[e] = 0.f;
+        }
+#pragma unroll
+        for (int e = 0; e < VEC; e += 4) {
+          const float4 g4 = *reinterpret_cast<const float4*>(g + c + e);
+          const float gg[4] = {g4.x, g4.y, g4.z, g4.w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            o[e + i] = rr * gg[i] * gv[k][q][e + i] - c3 * xv[k][q][e + i] + ad[e + i];
+            pg[q][e + i] += gv[k][q][e + i] * xv[k][q][e + i] * rr;
+          }
+        }
+        uint4 u;
+        if constexpr (VEC == 8) {
+          u = pack8(o);
+        } else {
+          u = make_uint4(__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]), __float_as_uint(o[3]));
+        }
+        *reinterpret_cast<uint4*>(dx + r * d + c) = u;
+      }
+    }
+  }
+  // the wave's groups hold the same columns: add them, then the waves in order
+#pragma unroll
+  for (int q = 0; q < Q; ++q)
+#pragma unroll
+    for (int e = 0; e < VEC; ++e)
+#pragma unroll
+      for (int o = LPR; o < 64; o <<= 1) pg[q][e] += __shfl_xor(pg[q][e], o);
+  if (lane < LPR) {
+#pragma unroll
+    for (int q = 0; q < Q; ++q)
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) sp[wave][(q * LPR + li) * VEC + e] = pg[q][e];
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < d; c += RW)
+    part[static_cast<int64_t>(blockIdx.x) * d + c] = ((sp[0][c] + sp[1][c]) + sp[2][c]) + sp[3][c];
 }
 
 // The head with rows read once through 16-byte loads, laid out as rmsnorm_vec_kernel: a
@@ -446,10 +566,23 @@ __global__ void __launch_bounds__(1024) bce_kernel(int64_t n, const float* __res
   __shared__ float red[16];
   const float inv_n = 1.f / static_cast<float>(n);
   float s = 0.f;
-  for (int64_t i = threadIdx.x; i < n; i += blockDim.x) {
-    const float zi = z[i], yi = y[i];
-    s += fmaxf(zi, 0.f) + log1pf(__expf(-fabsf(zi))) - yi * zi;
-    dz[i] = (1.f / (1.f + __expf(-zi)) - yi) * inv_n;
+  constexpr int U = 4;  // four elements' loads in flight per thread
+  for (int64_t base = threadIdx.x; base < n; base += U * static_cast<int64_t>(blockDim.x)) {
+    float zv[U], yv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = base + u * static_cast<int64_t>(blockDim.x);
+      zv[u] = i < n ? z[i] : 0.f;
+      yv[u] = i < n ? y[i] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = base + u * static_cast<int64_t>(blockDim.x);
+      if (i >= n) break;
+      const float zi = zv[u], yi = yv[u];
+      s += fmaxf(zi, 0.f) + log1pf(__expf(-fabsf(zi))) - yi * zi;
+      dz[i] = (1.f / (1.f + __expf(-zi)) - yi) * inv_n;
+    }
   }
   s = wave_sum(s);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
@@ -520,12 +653,50 @@ genrank_status launch_rmsnorm(int dtype, const void* x, const float* g, void* y,
 
 size_t rmsnorm_bwd_workspace(int d) { return static_cast<size_t>(PART_BLOCKS) * d * sizeof(float); }
 
+template <typename T>
+static int launch_rmsnorm_bwd_vec(const T* x, const float* g, const T* dy, const T* add, T* dx, float* part,
+                                  int64_t rows, int d, hipStream_t stream) {
+  constexpr int VEC = 16 / static_cast<int>(sizeof(T));
+  if (d % VEC != 0 || ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(dy) |
+                        reinterpret_cast<uintptr_t>(add) | reinterpret_cast<uintptr_t>(dx) |
+                        reinterpret_cast<uintptr_t>(g)) & 15u))
+    return 0;
+  auto go = [&](auto kernel, int lpr) {
+    const int64_t per_block = (RW / 64) * (64 / lpr) * 2;
+    const int grid = static_cast<int>(std::min<int64_t>(PART_BLOCKS, (rows + per_block - 1) / per_block));
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(RW), 0, stream, x, g, dy, add, dx, part, rows, d);
+    return grid;
+  };
+  switch (d / VEC) {
+    case 4: return go(rmsnorm_bwd_vec_kernel<T, 4, 1>, 4);
+    case 8: return go(rmsnorm_bwd_vec_kernel<T, 8, 1>, 8);
+    case 16: return go(rmsnorm_bwd_vec_kernel<T, 16, 1>, 16);
+    case 32: return go(rmsnorm_bwd_vec_kernel<T, 32, 1>, 32);
+    case 64: return go(rmsnorm_bwd_vec_kernel<T, 64, 1>, 64);
+    case 128: return go(rmsnorm_bwd_vec_kernel<T, 64, 2>, 64);
+    default: return 0;
+  }
+}
+
 genrank_status launch_rmsnorm_bwd(int dtype, const void* x, const float* g, const void* dy,
                                   const void* add, void* dx, float* dg, int64_t rows, int d, void* ws,
                                   hipStream_t stream) {
   if (d > 256 * MAXQ || d % 4) return GENRANK_E_SHAPE;
   float* part = static_cast<float*>(ws);
   if (rows <= 0) return launch_fill_f32(dg, d, 0.f, stream);
+  const int vgrid = dtype == GENRANK_BF16
+                        ? launch_rmsnorm_bwd_vec(static_cast<const bf16_t*>(x), g, static_cast<const bf16_t*>(dy),
+                                                 static_cast<const bf16_t*>(add), static_cast<bf16_t*>(dx), part,
+                                                 rows, d, stream)
+                        : launch_rmsnorm_bwd_vec(static_cast<const float*>(x), g, static_cast<const float*>(dy),
+                                                 static_cast<const float*>(add), static_cast<float*>(dx), part,
+                                                 rows, d, stream);
+  if (vgrid > 0) {
+    hipLaunchKernelGGL(column_sum_kernel, dim3((d + 15) / 16), dim3(256), 0, stream, part, vgrid, d, dg, d,
+                       nullptr, 0, nullptr);
+    GR_CHECK_LAUNCH();
+    return GENRANK_OK;
+  }
   const unsigned grid = static_cast<unsigned>(std::min<int64_t>(PART_BLOCKS, (rows + 7) / 8));
   if (dtype == GENRANK_BF16)
     hipLaunchKernelGGL(rmsnorm_bwd_kernel<bf16_t>, dim3(grid), dim3(RW), 0, stream,
