@@ -181,3 +181,17 @@ def test_attn_invariants_on_gpu():
     assert np.array_equal(gp[T_h:].reshape(batch.B, m, d), got[T_h:].reshape(batch.B, m, d)[:, perm])
     # history rows do not depend on the candidates
     assert np.array_equal(gp[:T_h], got[:T_h])
+
+
+def test_attn_bf16_long_histories():
+    """Histories far beyond the workloads' 480 (3000 and 2049 actions: six bias chunks of 512
+    keys, 24 query tiles), with 65 candidates, against the oracle."""
+    say("attn: bf16 long histories [3000, 2049] m=65")
+    cfg = synth.make_config("infer_1layer_bf16", m=65)
+    batch = custom_batch(cfg, [3000, 2049], seed=21)
+    st, q64 = random_qkv(batch.total_rows, cfg.d, "bf16", seed=22)
+    got, glse = _run_gpu(cfg, batch, st)
+    want, wlse, _ = _run_oracle(cfg, batch, q64)
+    assert np.isfinite(got).all()
+    assert np.abs(got - want).max() <= 2e-2
+    assert np.abs(glse - wlse).max() <= 2e-2

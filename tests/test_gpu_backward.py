@@ -225,3 +225,15 @@ def test_train_step_bf16_full_size():
     n = int(tg["n_items"].item())
     assert np.array_equal(tg["item_ids"][:n].cpu().numpy(), used), "item ids"
     bf16_close(to_numpy(tg["item_rows"][:n]), wtg["item"][used], "item")
+
+
+@pytest.mark.parametrize("cand_only", [0, 1])
+def test_attn_bwd_bf16_long_histories(cand_only):
+    """The attention backward on 3000- and 2049-action histories with 65 candidates."""
+    say(f"bwd: attention bf16 long histories cand_only={cand_only}")
+    cfg = synth.make_config("train2_bf16", m=65)
+    batch = custom_batch(cfg, [3000, 2049], seed=23)
+    got, want = _attn_case(cfg, batch, 47, cand_only)
+    d = cfg.d
+    for i, name in enumerate(("dq", "dk", "dv")):
+        bf16_close(got[:, i * d:(i + 1) * d], want[:, i * d:(i + 1) * d], name)
