@@ -731,6 +731,14 @@ def main():
         kernels["attn_fwd"]["tflops"] = round(tf, 2)
         kernels["attn_fwd"]["flops"] = int(attn_flops)
         out["attn_mfma_util_pct"] = round(100 * tf / peak_f, 2)
+    if decomposed:
+        # sum-of-kernels roofline: each kernel at its own bound (bytes at 8 TB/s or flops at
+        # the dense peak), against the measured step
+        floor_us = sum((amount / (PEAK_HBM_GBS * 1e9) if unit == "GB/s" else
+                        amount / ((PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS) * 1e12)) * 1e6
+                       for _, (bound, amount, unit) in work.items())
+        out["step_roofline_us"] = round(floor_us, 2)
+        out["step_roofline_frac"] = round(floor_us / (ms * 1e3), 4)
     out["gather_gbps"] = kernels["embed_sum"]["achieved"]
     # the same launch against its logical bytes (five table rows read and one row written
     # per token): repeated rows that hit in cache count every time

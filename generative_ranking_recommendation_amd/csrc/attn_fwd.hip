@@ -35,7 +35,7 @@ namespace genrank {
 
 namespace {
 
-constexpr int GROUP = 16;       // (user, head) pairs per XCD scheduling group
+constexpr int GROUP = 32;       // (user, head) pairs per XCD scheduling group
 constexpr int QW = 16;          // queries per wave (16-column MFMA blocks)
 constexpr int QB = QW / 16;     // column blocks per wave
 constexpr int NW = 8;           // waves per workgroup
