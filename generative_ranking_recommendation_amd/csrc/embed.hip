@@ -285,15 +285,27 @@ __device__ __forceinline__ void add_vec(const uint4& v, float* acc) {
   }
 }
 
-template <typename T>
+// SACT: the action table (n_action + 1 rows, at most SACT_MAX bytes) is staged in dynamic
+// LDS: every workgroup reads its few rows for every token, so they are copied once per
+// workgroup rather than fetched from the same L2 lines by every row.
+constexpr int SACT_MAX = 32768;
+
+template <typename T, bool SACT>
 __global__ void __launch_bounds__(EMB_THREADS) embed_sum_rows_kernel(EmbedArgs a) {
   __shared__ RowIdx sidx[EMB_ROWS];
   __shared__ int64_t sbounds[MAX_BOUNDS];
   __shared__ int red_c[EMB_THREADS / 64];
   __shared__ int64_t red_m[EMB_THREADS / 64];
+  extern __shared__ __attribute__((aligned(16))) uint4 s_act[];
   int64_t row0;
   const int rows = derive_chunk(a, sidx, sbounds, red_c, red_m, &row0);
   if (rows == 0) return;
+  if constexpr (SACT) {
+    const int n16 = static_cast<int>(a.bytes_action / 16);
+    const uint4* src = static_cast<const uint4*>(a.t_action);
+    for (int i = threadIdx.x; i < n16; i += EMB_THREADS) s_act[i] = src[i];
+    __syncthreads();
+  }
   constexpr int V = Vec<T>::N;
   constexpr int UR = 4;
   const int cpr = a.d / V;
@@ -317,7 +329,12 @@ __global__ void __launch_bounds__(EMB_THREADS) embed_sum_rows_kernel(EmbedArgs a
     for (int u = 0; u < UR; ++u) {
       const RowIdx ix = sidx[min(r + u * rpp, rows - 1)];
       v[u][0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_item, ix.item * rowb + colb, 0, 0));
-      v[u][1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_act, ix.act * rowb + colb, 0, 0));
+      if constexpr (SACT) {
+        v[u][1] = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(s_act) +
+                                                  min(ix.act, a.n_action) * rowb + colb);
+      } else {
+        v[u][1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_act, ix.act * rowb + colb, 0, 0));
+      }
       v[u][2] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_pos, ix.pe * rowb + colb, 0, 0));
       v[u][3] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_ri, ix.ri_slot * rowb + colb, 0, 0));
       v[u][4] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_rt, ix.rt * rowb + colb, 0, 0));
@@ -660,6 +677,23 @@ dim3 grid_of(const EmbedArgs& a) {
   return dim3(static_cast<unsigned>(a.hist_chunks + a.cand_chunks), static_cast<unsigned>(a.B));
 }
 
+// the row kernel, with the action table in LDS when it is small enough
+void launch_rows(const EmbedArgs& a, int dtype, hipStream_t stream) {
+  const bool sact = a.bytes_action % 16 == 0 && a.bytes_action <= static_cast<uint32_t>(SACT_MAX);
+  const size_t lds = sact ? a.bytes_action : 0;
+  if (dtype == GENRANK_BF16) {
+    if (sact)
+      hipLaunchKernelGGL((embed_sum_rows_kernel<bf16_t, true>), grid_of(a), dim3(EMB_THREADS), lds, stream, a);
+    else
+      hipLaunchKernelGGL((embed_sum_rows_kernel<bf16_t, false>), grid_of(a), dim3(EMB_THREADS), 0, stream, a);
+  } else {
+    if (sact)
+      hipLaunchKernelGGL((embed_sum_rows_kernel<float, true>), grid_of(a), dim3(EMB_THREADS), lds, stream, a);
+    else
+      hipLaunchKernelGGL((embed_sum_rows_kernel<float, false>), grid_of(a), dim3(EMB_THREADS), 0, stream, a);
+  }
+}
+
 }  // namespace
 
 genrank_status check_embed_args(const genrank_batch* b, const genrank_inputs* in,
@@ -692,10 +726,8 @@ genrank_status launch_embed_sum(const genrank_batch* b, const genrank_inputs* in
   const int64_t rb = static_cast<int64_t>(b->d) * es;
   const bool rows_ok = b->d * es % 16 == 0 && cpr <= EMB_THREADS && EMB_THREADS % cpr == 0 &&
                        t->n_item * rb < 0xFFFFFFFFll && EMB_ROWS * rb < 0xFFFFFFFFll;
-  if (rows_ok && b->dtype == GENRANK_BF16)
-    hipLaunchKernelGGL(embed_sum_rows_kernel<bf16_t>, grid_of(a), dim3(EMB_THREADS), 0, stream, a);
-  else if (rows_ok)
-    hipLaunchKernelGGL(embed_sum_rows_kernel<float>, grid_of(a), dim3(EMB_THREADS), 0, stream, a);
+  if (rows_ok)
+    launch_rows(a, b->dtype, stream);
   else if (b->dtype == GENRANK_BF16)
     hipLaunchKernelGGL(embed_sum_kernel<bf16_t>, grid_of(a), dim3(EMB_THREADS), 0, stream, a);
   else
@@ -717,10 +749,8 @@ genrank_status launch_embed_sum_cand(const genrank_batch* b, const genrank_input
   const int64_t rb = static_cast<int64_t>(b->d) * es;
   const bool rows_ok = b->d * es % 16 == 0 && cpr <= EMB_THREADS && EMB_THREADS % cpr == 0 &&
                        t->n_item * rb < 0xFFFFFFFFll && EMB_ROWS * rb < 0xFFFFFFFFll;
-  if (rows_ok && b->dtype == GENRANK_BF16)
-    hipLaunchKernelGGL(embed_sum_rows_kernel<bf16_t>, grid_of(a), dim3(EMB_THREADS), 0, stream, a);
-  else if (rows_ok)
-    hipLaunchKernelGGL(embed_sum_rows_kernel<float>, grid_of(a), dim3(EMB_THREADS), 0, stream, a);
+  if (rows_ok)
+    launch_rows(a, b->dtype, stream);
   else if (b->dtype == GENRANK_BF16)
     hipLaunchKernelGGL(embed_sum_kernel<bf16_t>, grid_of(a), dim3(EMB_THREADS), 0, stream, a);
   else
