@@ -64,6 +64,7 @@ struct AttnArgs {
   float sp2[GENRANK_MAX_HEADS];  // slopes * log2(e)
   float st2[GENRANK_MAX_HEADS];
   float scale2;                  // log2(e) / sqrt(dh)
+  float rscale2;                 // 1 / scale2
   int B, m, H, hist_tiles, cand_tiles;
   int64_t T_h;
   const bf16_t* rab;       // learned-bias variant: per-user [L, P] bf16 matrices
@@ -614,6 +615,707 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
   }
 }
 
+// ------------------------------------------------------------------ bf16 ring kernel
+// The ALiBi kernel (and its variants).  Same workgroup shape, schedule and math as
+// attn_fwd_bf16_kernel above; what differs is how K and V reach LDS and how much vector
+// work a tile costs:
+//  - K and V tiles go from global memory straight into LDS (one 16-byte direct load per
+//    lane and tile for each), through a ring of NS stage buffers with NS - 1 tiles in
+//    flight.  No registers hold staged data and each workgroup waits for memory about
+//    once, not once per tile.  Both tiles are stored row-major with an XOR swizzle of
+//    their 16-byte chunks (chosen through which chunk each lane fetches).
+//  - The O^T = V^T P^T row operand comes from the row-major V tile through the gfx950
+//    transposing LDS read (ds_read_b64_tr_b16): within each 16-lane group, output lane j
+//    element e is element j % 4 of what lane 4 e + j / 4 addressed.  Two such reads give
+//    one lane 8 keys of one head dimension.
+//  - With the plain separable bias the key term w_j seeds the score accumulator, so the
+//    MFMA leaves q.k + w_j / c (c = log2(e) / sqrt(dh)) and the softmax scales once, inside
+//    the exponent's FMA.
+//  - The running maximum is raised only when some score exceeds it by more than 2^8 (a
+//    wave-uniform branch); until then probabilities up to 2^8 are accumulated against the
+//    stale maximum, which changes nothing in exact arithmetic and stays far inside fp32
+//    and bf16 range.
+//  - Row sums come from the bf16 probabilities with v_dot2 against ones (the same values
+//    the P V product uses).
+constexpr int NS = 4;               // stage buffers in the K/V ring
+constexpr int STAGE = 2 * AK * DH;  // bf16 per stage buffer: the K tile, then the V tile
+constexpr float RESCALE_LOG2 = 8.f; // headroom of the stale running maximum (log2 units)
+static_assert(QB == 1 && NW * 8 == AK, "one 16-query block per wave; 8 tile rows per wave");
+
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+
+template <int VAR>
+__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8))) attn_fwd_ring_kernel(AttnArgs a) {
+  constexpr bool FULL = (VAR & VAR_FULL) != 0;
+  constexpr bool TBK = (VAR & VAR_TBUCKET) != 0;
+  constexpr bool SEP = VAR == 0;  // bias term of the key only: it seeds the accumulator
+  __shared__ __attribute__((aligned(16))) bf16_t sg0[STAGE];
+  __shared__ __attribute__((aligned(16))) bf16_t sg1[STAGE];
+  __shared__ __attribute__((aligned(16))) bf16_t sg2[STAGE];
+  __shared__ __attribute__((aligned(16))) bf16_t sg3[STAGE];
+  __shared__ __attribute__((aligned(16))) float sW[WCHUNK];
+  __shared__ __attribute__((aligned(16))) int32_t sT[TBK ? WCHUNK : 4];
+  __shared__ int32_t sTB[TBK ? ATTN_MAX_TIME_BOUNDS : 1];
+  __shared__ uint32_t sLUT[TBK ? BK_CELLS : 1];
+
+  // flat grid over (user, head, tile), walked per XCD as in attn_fwd_bf16_kernel
+  const int TY = a.cand_tiles + a.hist_tiles;
+  const int x8 = blockIdx.x & 7;
+  const int kx = blockIdx.x >> 3;
+  const int grp = kx / (TY * GROUP);
+  const int rem = kx - grp * (TY * GROUP);
+  const int y = rem / GROUP;
+  const int bh = (grp * GROUP + (rem - y * GROUP)) * 8 + x8;
+  if (bh >= a.B * a.H) return;
+  const int u = bh / a.H;
+  const int h = bh - u * a.H;
+  const int64_t off = a.offsets[u];
+  const int N = a.offsets[u + 1] - a.offsets[u];
+
+  bool is_cand;
+  int q0, nq, n_tiles;
+  int64_t qrow0;
+  if (y < a.cand_tiles) {
+    is_cand = true;
+    q0 = y * AQ;
+    if (q0 >= a.m) return;
+    nq = min(AQ, a.m - q0);
+    qrow0 = a.crow0 + static_cast<int64_t>(u) * a.m + q0;
+    n_tiles = (N + AK - 1) / AK;
+  } else {
+    is_cand = false;
+    const int t = a.hist_tiles - 1 - (y - a.cand_tiles);  // largest tiles first
+    q0 = t * AQ;
+    if (q0 >= N) return;
+    nq = min(AQ, N - q0);
+    qrow0 = off + q0;
+    n_tiles = FULL ? (N + AK - 1) / AK : (q0 + nq + AK - 1) / AK;
+  }
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, g4 = lane >> 4;
+  const float sp2 = a.sp2[h], st2 = a.st2[h];
+  // Score units.  Separable bias: raw = q.k + w_j / c, log2 units = raw * c.  Otherwise the
+  // scores are formed in log2 units (SC = 1).
+  const float SC = SEP ? a.scale2 : 1.f;
+  const float spr = SEP ? sp2 * a.rscale2 : sp2;
+  const float str = SEP ? st2 * a.rscale2 : st2;
+  const int p_ref = is_cand ? N : q0;
+
+  // ---- register loads, all unconditional from valid addresses (a load behind a branch
+  // makes the compiler wait for it at the join, before the ring below is issued)
+  const int64_t ts_ref = is_cand ? a.req[u] : a.ts[off + q0];
+  const int kt_first = n_tiles - 1;
+  int wbase = n_tiles > 0 ? (kt_first * AK / WCHUNK) * WCHUNK : 0;
+  static_assert(WCHUNK == NT, "one bias key per thread in the first chunk");
+  const int wkey = wbase + tid;
+  const bool wkey_in = wkey < N;
+  int64_t ts_key = *(wkey_in ? a.ts + off + wkey : a.req + u);
+
+  const int q_local = wave * QW + l16;
+  const bool q_valid = q_local < nq;
+  const int64_t qrow = qrow0 + q_local;
+  const int q_slot = is_cand ? (N + q0 + q_local) : (q0 + q_local);
+  const int k_lim = (is_cand || FULL) ? (N - 1) : min(q_slot, N - 1);
+  const int kmax_blk = (is_cand || FULL) ? (N - 1) : min(q0 + wave * QW + 15, N - 1);
+  const int64_t rowoff = (qrow0 + min(q_local, nq - 1)) * a.ld_qkv + h * DH;
+  bf16x8_t qf[2];
+  qf[0] = as_bf16x8(*reinterpret_cast<const uint4*>(a.q + rowoff + g4 * 8));
+  qf[1] = as_bf16x8(*reinterpret_cast<const uint4*>(a.q + rowoff + g4 * 8 + 32));
+  // a candidate's own key and value (the softmax seed; history tiles read and drop them)
+  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+  typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+  u32x4_t kself[2];
+  u32x2_t vself[4];
+  kself[0] = *reinterpret_cast<const u32x4_t*>(a.k + rowoff + g4 * 8);
+  kself[1] = *reinterpret_cast<const u32x4_t*>(a.k + rowoff + g4 * 8 + 32);
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) vself[nb] = *reinterpret_cast<const u32x2_t*>(a.v + rowoff + nb * 16 + g4 * 4);
+  // a history query's own time (fully visible and bucketed variants)
+  int64_t tq_raw = 0;
+  if constexpr (FULL || TBK) tq_raw = *(N > 0 ? a.ts + off + min(q_slot, N - 1) : a.req + u);
+
+  // ---- the K/V ring.  Wave w loads rows 8 w .. 8 w + 7 of each tile: lane l takes row
+  // 8 w + l / 8 and fills LDS chunk l % 8 of it, which holds the row's global chunk
+  // (l % 8) ^ (row & 7) for K and (l % 8) ^ 2 (row & 3) for V.  Rows past the history end
+  // re-read its last row (finite values; the mask gives those keys probability 0).
+  // The prologue always issues NS - 1 tiles, so the compiler's waits for the register
+  // loads above see one fixed count of loads behind them and leave the ring in flight;
+  // tiles past the last read row 0 (with no history at all: the query row) into stage
+  // buffers nothing reads.  Row offsets fit 32 bits (checked on the host).
+  const int lr = wave * 8 + (lane >> 3);
+  const int lc = lane & 7;
+  const uint32_t row_bytes = static_cast<uint32_t>(a.ld_h) * 2u;
+  const char* gk = reinterpret_cast<const char*>(N > 0 ? a.kh + off * a.ld_h + h * DH + ((lc ^ (lr & 7)) * 8) : a.q + rowoff);
+  const char* gv = reinterpret_cast<const char*>(N > 0 ? a.vh + off * a.ld_h + h * DH + ((lc ^ (2 * (lr & 3))) * 8) : a.q + rowoff);
+  auto issue = [&](int it, bf16_t* stg) {
+    const int r = max(min((kt_first - it) * AK + lr, N - 1), 0);
+    const uint32_t ro = static_cast<uint32_t>(r) * row_bytes;
+    __builtin_amdgcn_global_load_lds((glb_void_t*)(gk + ro), (lds_void_t*)(stg + wave * 8 * DH), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((glb_void_t*)(gv + ro), (lds_void_t*)(stg + AK * DH + wave * 8 * DH), 16, 0, 0);
+  };
+  issue(0, sg0);
+  issue(1, sg1);
+  issue(2, sg2);
+  static_assert(NS == 4, "the prologue fills NS - 1 stages");
+  // Direct loads and register loads in flight together leave the compiler unable to
+  // order them, so its first wait for a register load waits for everything.  This empty
+  // asm (which reads and redefines registers the loads above wrote) makes that one wait
+  // come after the whole ring has been issued; the query fragments are covered too (see
+  // attn_fwd_bf16_kernel).
+  asm volatile("" : "+v"(ts_key), "+v"(tq_raw), "+v"(qf[0]), "+v"(qf[1]), "+v"(kself[0]), "+v"(kself[1]),
+               "+v"(vself[0]), "+v"(vself[1]), "+v"(vself[2]), "+v"(vself[3])::"memory");
+  const int32_t tq = (FULL || TBK) && !is_cand && N > 0 ? static_cast<int32_t>(tq_raw - ts_ref) : 0;
+  if constexpr (TBK)
+    for (int k = tid; k < a.tb_p2; k += NT) {
+      const int64_t b = k < a.n_tb ? a.tb[k] : INT64_MAX;
+      sTB[k] = b > INT32_MAX ? INT32_MAX : (b < INT32_MIN ? INT32_MIN : static_cast<int32_t>(b));
+    }
+
+  // ---- bias terms of the first chunk, in the score units above
+  sW[tid] = wkey_in ? (TBK ? spr * static_cast<float>(wkey - p_ref)
+                           : spr * static_cast<float>(wkey - p_ref) + str * static_cast<float>(static_cast<int32_t>(ts_key - ts_ref)))
+                    : 0.f;
+  if constexpr (TBK) sT[tid] = wkey_in ? static_cast<int32_t>(ts_key - ts_ref) : 0;
+  auto load_w = [&](int wb) {
+    for (int j = tid; j < WCHUNK; j += NT) {
+      const int key = wb + j;
+      float w = 0.f;
+      int32_t tk = 0;
+      if (key < N) {
+        tk = static_cast<int32_t>(a.ts[off + key] - ts_ref);
+        w = TBK ? spr * static_cast<float>(key - p_ref) : spr * static_cast<float>(key - p_ref) + str * static_cast<float>(tk);
+      }
+      sW[j] = w;
+      if constexpr (TBK) sT[j] = tk;
+    }
+  };
+
+  // ---- softmax state in score units; a candidate starts from its own key (bias 0)
+  f32x4_t accO[4];
+  float m_run, lsum;
+  if (is_cand) {
+    float dot = 0.f, kf[8], qv[8];
+#pragma unroll
+    for (int hlf = 0; hlf < 2; ++hlf) {
+      unpack8(__builtin_bit_cast(uint4, kself[hlf]), kf);
+      unpack8(__builtin_bit_cast(uint4, qf[hlf]), qv);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dot += qv[e] * kf[e];
+    }
+    dot = xor32_sum(xor16_sum(dot));
+    m_run = SEP ? dot : dot * a.scale2;  // (bucketed time: its gap-0 term follows below)
+    lsum = (g4 == 0) ? 1.f : 0.f;
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const u32x2_t vv = vself[nb];
+      accO[nb] = f32x4_t{__uint_as_float(vv.x << 16), __uint_as_float(vv.x & 0xFFFF0000u),
+                         __uint_as_float(vv.y << 16), __uint_as_float(vv.y & 0xFFFF0000u)};
+    }
+  } else {
+    m_run = -1e30f;
+    lsum = 0.f;
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) accO[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  lds_sync();  // sW, sT, sTB written
+  if constexpr (TBK) {
+    if (is_cand) m_run -= st2 * static_cast<float>(bucket_search(sTB, a.tb_p2, 0));
+    bucket_table_build(sLUT, sTB, a.tb_p2, tid, NT);
+    lds_sync();
+  }
+  // the row term of the bias in log2 units, added back into the log-sum-exp
+  float w_i = 0.f;
+  if constexpr (FULL) {
+    w_i = (!is_cand && q_valid) ? (TBK ? sp2 * static_cast<float>(q_slot - p_ref)
+                                       : sp2 * static_cast<float>(q_slot - p_ref) + st2 * static_cast<float>(tq))
+                                : 0.f;
+  } else {
+    w_i = (!is_cand && q_valid) ? sW[q_slot - wbase] * SC : 0.f;
+  }
+  const float w_i_u = w_i / SC;  // the same in score units (FULL only)
+
+  // LDS offsets (bf16 elements) of this lane's fragments inside a stage buffer
+  const int k_off0 = l16 * DH + (((0 + g4) ^ (l16 & 7)) * 8);
+  const int k_off1 = l16 * DH + (((4 + g4) ^ (l16 & 7)) * 8);
+  int v_off[4];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb)
+    v_off[nb] = AK * DH + (4 * g4 + (l16 >> 2)) * DH + (((2 * nb + ((l16 & 3) >> 1)) ^ (2 * (l16 >> 2))) * 8) + (l16 & 1) * 4;
+  const float th = RESCALE_LOG2 / SC;
+  const bool wave_on = wave * QW < nq;
+
+  auto compute = [&](auto masked_tag, const bf16_t* stg, int it) __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    const int base = (kt_first - it) * AK;
+    f32x4_t s[4];
+    float4 wv[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      wv[kb] = reinterpret_cast<const float4*>(sW)[((base - wbase) >> 2) + kb * 4 + g4];
+      s[kb] = SEP ? f32x4_t{wv[kb].x, wv[kb].y, wv[kb].z, wv[kb].w} : f32x4_t{0.f, 0.f, 0.f, 0.f};
+      if (!MASKED || base + kb * 16 <= kmax_blk) {
+        const bf16x8_t k0 = as_bf16x8(*reinterpret_cast<const uint4*>(stg + kb * 16 * DH + k_off0));
+        const bf16x8_t k1 = as_bf16x8(*reinterpret_cast<const uint4*>(stg + kb * 16 * DH + k_off1));
+        s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[0], s[kb], 0, 0, 0);
+        s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[1], s[kb], 0, 0, 0);
+      }
+    }
+    if constexpr (!SEP) {
+      // fully visible: -|w_j - w_i|; bucketed time: - s' bucket(|t_i - t_j|)
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const float wk[4] = {wv[kb].x, wv[kb].y, wv[kb].z, wv[kb].w};
+        int4 t4 = make_int4(0, 0, 0, 0);
+        if constexpr (TBK) t4 = reinterpret_cast<const int4*>(sT)[((base - wbase) >> 2) + kb * 4 + g4];
+        const int32_t tk[4] = {t4.x, t4.y, t4.z, t4.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float x = s[kb][i] * a.scale2 + (FULL ? -fabsf(wk[i] - w_i_u) : wk[i]);
+          if constexpr (TBK) x -= st2 * static_cast<float>(bucket_lookup(sLUT, sTB, a.tb_p2, abs(tq - tk[i])));
+          s[kb][i] = x;
+        }
+      }
+    }
+    if constexpr (MASKED) {
+      const int lim = k_lim - base - g4 * 4;  // local key kb*16 + i must be <= lim
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (kb * 16 + i > lim) s[kb][i] = -INFINITY;
+    }
+    float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), s[0][2]), fmaxf(fmaxf(s[0][3], s[1][0]), s[1][1]));
+    mx = fmaxf(fmaxf(mx, s[1][2]), fmaxf(fmaxf(s[1][3], s[2][0]), s[2][1]));
+    mx = fmaxf(fmaxf(mx, s[2][2]), fmaxf(fmaxf(s[2][3], s[3][0]), s[3][1]));
+    mx = fmaxf(fmaxf(mx, s[3][2]), s[3][3]);
+    mx = xor32_max(xor16_max(mx));
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + th) != 0) {  // rare: raise the maximum
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * SC);
+      m_run = m_new;
+      lsum *= alpha;
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) accO[nb] = accO[nb] * alpha;
+    }
+    const float mb = -m_run * SC;
+    bf16x8_t pf[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      uint4 pk;
+      uint32_t* pw = reinterpret_cast<uint32_t*>(&pk);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x4_t& sb = s[2 * ks + (j >> 1)];
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sb[(j & 1) * 2], SC, mb));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sb[(j & 1) * 2 + 1], SC, mb));
+        pw[j] = pack_bf16x2(p0, p1);
+        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw[j]),
+                                                __builtin_bit_cast(bf16x2_t, 0x3F803F80u), lsum, false);
+      }
+      pf[ks] = as_bf16x8(pk);
+    }
+    // O^T += V^T P^T; the V^T fragment: two transposing reads of 4 keys each
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      if (MASKED && base + ks * 32 > kmax_blk) continue;
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_v4i16_t*)(stg + v_off[nb] + (ks * 32) * DH));
+        const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_v4i16_t*)(stg + v_off[nb] + (ks * 32 + 16) * DH));
+        const v4i16_t both[2] = {lo, hi};
+        accO[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, both), pf[ks], accO[nb], 0, 0, 0);
+      }
+    }
+  };
+
+  // Tile it (key tile kt_first - it, newest first) sits in stage buffer it % NS.  A step
+  // reloads the bias chunk when the tile leaves it (histories longer than WCHUNK keys),
+  // waits for its own tile (the newer tiles may stay in flight: two loads each), meets the
+  // other waves, refills the buffer the previous step read with tile it + NS - 1, and
+  // computes.  Masks are needed only in the first two tiles (the ragged history end and
+  // the causal diagonal); every later tile lies wholly below every query's limit.
+  auto step = [&](auto masked_tag, auto stage_tag, int it) __attribute__((always_inline)) {
+    constexpr int S = decltype(stage_tag)::value;
+    bf16_t* const cur = S == 0 ? sg0 : S == 1 ? sg1 : S == 2 ? sg2 : sg3;
+    bf16_t* const nxt = S == 0 ? sg3 : S == 1 ? sg0 : S == 2 ? sg1 : sg2;  // stage (it - 1) % NS
+    if ((kt_first - it) * AK < wbase) {
+      lds_sync();
+      wbase -= WCHUNK;
+      load_w(wbase);
+      lds_sync();
+    }
+    const int left = kt_first - it;  // tiles after this one
+    if (left >= 2) wait_vmcnt<4>(); else if (left == 1) wait_vmcnt<2>(); else wait_vmcnt<0>();
+    lds_barrier();
+    if (it + NS - 1 < n_tiles) issue(it + NS - 1, nxt);
+    if (wave_on) compute(masked_tag, cur, it);
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  if (n_tiles > 0) step(std::true_type{}, I0{}, 0);
+  if (n_tiles > 1) step(std::true_type{}, I1{}, 1);
+  for (int it = 2; it < n_tiles; it += NS) {
+    step(std::false_type{}, I2{}, it);
+    if (it + 1 < n_tiles) step(std::false_type{}, I3{}, it + 1);
+    if (it + 2 < n_tiles) step(std::false_type{}, I0{}, it + 2);
+    if (it + 3 < n_tiles) step(std::false_type{}, I1{}, it + 3);
+  }
+  wait_vmcnt<0>();  // no direct load may still be writing LDS when the workgroup ends
+
+  // ---- epilogue
+  const float ltot = xor32_sum(xor16_sum(lsum));
+  if (!q_valid) return;
+  const float inv = 1.f / ltot;
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    uint2 o;
+    o.x = pack_bf16x2(accO[nb][0] * inv, accO[nb][1] * inv);
+    o.y = pack_bf16x2(accO[nb][2] * inv, accO[nb][3] * inv);
+    *reinterpret_cast<uint2*>(a.o + qrow * a.ld_o + h * DH + nb * 16 + g4 * 4) = o;
+  }
+  if (a.lse && g4 == 0) a.lse[qrow * a.H + h] = LN2 * (m_run * SC + log2f(ltot) - (FULL ? 0.f : w_i));
+}
+
+// ------------------------------------------------------------------ bf16 pair kernel
+// One workgroup per (user, head) pair, for batches whose longest history fits in LDS
+// (PAIR_MAXK keys).  The pair's whole K and V history goes into LDS once (direct loads,
+// 64-key tiles with the ring kernel's swizzles and transposing V reads), together with
+// every key's bias term.  The 16 waves then work through the pair's 16-query units
+// (candidate blocks first, then history blocks newest first) with no further barrier:
+// each wave runs its units' key tiles from LDS on its own.  Against the tile kernels this
+// loads every K/V byte of a pair once instead of once per query tile, and pays one
+// workgroup prologue per pair instead of one per query tile.
+// The bias reference point of the whole pair is the candidates' shared (p, tau) = (N,
+// request time), so candidate rows carry no row term.  A candidate's own key is merged
+// into its softmax state after the history keys (same result as seeding with it).
+constexpr int PAIR_WAVES = 16;
+constexpr int PAIR_NT = 64 * PAIR_WAVES;
+constexpr int PAIR_MAXT = 9;                 // key tiles held in LDS
+constexpr int PAIR_MAXK = PAIR_MAXT * AK;    // longest history this kernel takes
+static_assert(PAIR_MAXK <= PAIR_NT, "one bias key per thread");
+
+template <int VAR>
+__global__ void __launch_bounds__(PAIR_NT) attn_fwd_pair_kernel(AttnArgs a) {
+  constexpr bool FULL = (VAR & VAR_FULL) != 0;
+  constexpr bool TBK = (VAR & VAR_TBUCKET) != 0;
+  constexpr bool SEP = VAR == 0;
+  __shared__ __attribute__((aligned(16))) bf16_t sKV[PAIR_MAXT * STAGE];
+  __shared__ __attribute__((aligned(16))) float sW[PAIR_MAXK];
+  __shared__ __attribute__((aligned(16))) int32_t sT[TBK ? PAIR_MAXK : 4];
+  __shared__ int32_t sTB[TBK ? ATTN_MAX_TIME_BOUNDS : 1];
+  __shared__ uint32_t sLUT[TBK ? BK_CELLS : 1];
+  __shared__ int sCnt[PAIR_MAXT + 1];
+  __shared__ int sWave[PAIR_WAVES];
+  __shared__ int sUser;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  // Which pair: workgroups run in launch order, so the pairs go heaviest first (users
+  // ordered by key-tile count, descending, ties by index) and the light ones fill the end
+  // of the launch.  Every workgroup derives the same order from the offsets.  With more
+  // users than threads the order is the plain one.
+  const int ur = blockIdx.x / a.H;
+  const int h = blockIdx.x - ur * a.H;
+  int u = ur;
+  if (a.B <= PAIR_NT) {
+    if (tid <= PAIR_MAXT) sCnt[tid] = 0;
+    int ntl = -1;
+    if (tid < a.B) ntl = (min(a.offsets[tid + 1] - a.offsets[tid], PAIR_MAXK) + AK - 1) / AK;
+    lds_sync();
+    if (ntl >= 0) atomicAdd(&sCnt[ntl], 1);
+    lds_sync();
+    int bk = PAIR_MAXT, before = 0;  // the tile-count class holding rank ur
+    while (bk > 0 && before + sCnt[bk] <= ur) before += sCnt[bk--];
+    const bool mine = ntl == bk;
+    const uint64_t bal = __builtin_amdgcn_ballot_w64(mine);
+    const int below = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(bal >> 32), __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(bal), 0));
+    if (lane == 0) sWave[wave] = __builtin_popcountll(bal);
+    lds_sync();
+    int rank = below;
+    for (int w = 0; w < wave; ++w) rank += sWave[w];
+    if (mine && rank == ur - before) sUser = tid;
+    lds_sync();
+    u = sUser;
+  }
+  const int64_t off = a.offsets[u];
+  // (a history longer than the batch's declared maximum is cut, so that LDS is never
+  // overrun; the declared maximum is the caller's promise)
+  const int N = min(a.offsets[u + 1] - a.offsets[u], PAIR_MAXK);
+  const int n_tiles = (N + AK - 1) / AK;
+  const int l16 = lane & 15, g4 = lane >> 4;
+  const float sp2 = a.sp2[h], st2 = a.st2[h];
+  const float SC = SEP ? a.scale2 : 1.f;
+  const float spr = SEP ? sp2 * a.rscale2 : sp2;
+  const float str = SEP ? st2 * a.rscale2 : st2;
+  const int64_t ts_ref = a.req[u];
+
+  // ---- the pair's K/V tiles: waves 0-7 load K, waves 8-15 V, rows 8 (w % 8) .. + 7 of
+  // every tile (lane l: row 8 (w % 8) + l / 8, LDS chunk l % 8 <- global chunk
+  // (l % 8) ^ (row & 7) for K, (l % 8) ^ 2 (row & 3) for V; rows past the history end
+  // re-read its last row).
+  {
+    const bool ldk = wave < 8;
+    const int lr = (wave & 7) * 8 + (lane >> 3);
+    const int lc = lane & 7;
+    const uint32_t row_bytes = static_cast<uint32_t>(a.ld_h) * 2u;
+    const char* g = reinterpret_cast<const char*>((ldk ? a.kh : a.vh) + off * a.ld_h + h * DH +
+                                                  ((lc ^ (ldk ? (lr & 7) : 2 * (lr & 3))) * 8));
+    bf16_t* dst = sKV + (ldk ? 0 : AK * DH) + (wave & 7) * 8 * DH;
+    for (int t = 0; t < n_tiles; ++t) {
+      const uint32_t ro = static_cast<uint32_t>(min(t * AK + lr, N - 1)) * row_bytes;
+      __builtin_amdgcn_global_load_lds((glb_void_t*)(g + ro), (lds_void_t*)(dst + t * STAGE), 16, 0, 0);
+    }
+  }
+
+  // ---- every key's bias term relative to the candidates (0 past the history end)
+  if (tid < n_tiles * AK) {
+    float w = 0.f;
+    int32_t tk = 0;
+    if (tid < N) {
+      tk = static_cast<int32_t>(a.ts[off + tid] - ts_ref);
+      w = TBK ? spr * static_cast<float>(tid - N) : spr * static_cast<float>(tid - N) + str * static_cast<float>(tk);
+    }
+    sW[tid] = w;
+    if constexpr (TBK) sT[tid] = tk;
+  }
+  if constexpr (TBK)
+    for (int k = tid; k < a.tb_p2; k += PAIR_NT) {
+      const int64_t b = k < a.n_tb ? a.tb[k] : INT64_MAX;
+      sTB[k] = b > INT32_MAX ? INT32_MAX : (b < INT32_MIN ? INT32_MIN : static_cast<int32_t>(b));
+    }
+  wait_vmcnt<0>();
+  lds_sync();
+  float tbk_self = 0.f;  // bucketed time term of a candidate's own key (gap 0)
+  if constexpr (TBK) {
+    tbk_self = st2 * static_cast<float>(bucket_search(sTB, a.tb_p2, 0));
+    bucket_table_build(sLUT, sTB, a.tb_p2, tid, PAIR_NT);
+    lds_sync();
+  }
+
+  const float th = RESCALE_LOG2 / SC;
+  // LDS offsets (bf16 elements) of this lane's fragments inside a tile
+  const int k_off0 = l16 * DH + (((0 + g4) ^ (l16 & 7)) * 8);
+  const int k_off1 = l16 * DH + (((4 + g4) ^ (l16 & 7)) * 8);
+  int v_off[4];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb)
+    v_off[nb] = AK * DH + (4 * g4 + (l16 >> 2)) * DH + (((2 * nb + ((l16 & 3) >> 1)) ^ (2 * (l16 >> 2))) * 8) + (l16 & 1) * 4;
+
+  // ---- units: 16-query blocks, candidates first (each sees every key), then history
+  // blocks newest first; wave w takes units w, w + 16, ...
+  const int nb_c = (a.m + QW - 1) / QW;
+  const int nb_h = a.hist_tiles > 0 ? (N + QW - 1) / QW : 0;
+  const int n_units = nb_c + nb_h;
+  auto q_row = [&](int k) -> int64_t {  // the global row of this lane's query in unit k
+    if (k < nb_c) return a.crow0 + static_cast<int64_t>(u) * a.m + min(k * QW + l16, a.m - 1);
+    const int b = nb_h - 1 - (k - nb_c);
+    return off + min(b * QW + l16, N - 1);
+  };
+  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+  typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+  u32x4_t qn[2] = {};
+  if (wave < n_units) {
+    const int64_t ro = q_row(wave) * a.ld_qkv + h * DH + g4 * 8;
+    qn[0] = *reinterpret_cast<const u32x4_t*>(a.q + ro);
+    qn[1] = *reinterpret_cast<const u32x4_t*>(a.q + ro + 32);
+  }
+
+  for (int k = wave; k < n_units; k += PAIR_WAVES) {
+    const bool is_cand = k < nb_c;
+    const int b = is_cand ? k : nb_h - 1 - (k - nb_c);
+    const int qf0 = b * QW;                               // first query of the unit
+    const int nq = min(QW, (is_cand ? a.m : N) - qf0);
+    const bool q_valid = l16 < nq;
+    const int q_slot = is_cand ? N + qf0 + l16 : qf0 + l16;
+    const int64_t qrow = q_row(k);
+    const int k_lim = (is_cand || FULL) ? (N - 1) : min(q_slot, N - 1);
+    const int kmax_blk = (is_cand || FULL) ? (N - 1) : min(qf0 + QW - 1, N - 1);
+    const int n_t = (is_cand || FULL) ? n_tiles : (qf0 + nq - 1) / AK + 1;
+    bf16x8_t qf[2] = {__builtin_bit_cast(bf16x8_t, qn[0]), __builtin_bit_cast(bf16x8_t, qn[1])};
+    // the next unit's query fragments
+    if (k + PAIR_WAVES < n_units) {
+      const int64_t ro = q_row(k + PAIR_WAVES) * a.ld_qkv + h * DH + g4 * 8;
+      qn[0] = *reinterpret_cast<const u32x4_t*>(a.q + ro);
+      qn[1] = *reinterpret_cast<const u32x4_t*>(a.q + ro + 32);
+    }
+    // a candidate's own key and value (merged after the history keys)
+    u32x4_t kself[2] = {};
+    u32x2_t vself[4] = {};
+    if (is_cand) {
+      const int64_t ro = qrow * a.ld_qkv + h * DH;
+      kself[0] = *reinterpret_cast<const u32x4_t*>(a.k + ro + g4 * 8);
+      kself[1] = *reinterpret_cast<const u32x4_t*>(a.k + ro + g4 * 8 + 32);
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) vself[nb] = *reinterpret_cast<const u32x2_t*>(a.v + ro + nb * 16 + g4 * 4);
+    }
+    // the row term (log2 units) and, for the variants, the query's own terms
+    const float w_i = (!is_cand && q_valid) ? sW[min(q_slot, N - 1)] * SC : 0.f;
+    const float w_i_u = w_i / SC;
+    const int32_t tq = (TBK && !is_cand && N > 0) ? sT[min(q_slot, N - 1)] : 0;
+
+    f32x4_t accO[4];
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) accO[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float m_run = -1e30f, lsum = 0.f;
+
+    // S^T of key tile kt (with the separable bias: seeded with the key terms)
+    auto scores = [&](auto masked_tag, int kt, f32x4_t(&s)[4]) __attribute__((always_inline)) {
+      constexpr bool MASKED = decltype(masked_tag)::value;
+      const bf16_t* stg = sKV + kt * STAGE;
+      const int base = kt * AK;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        if constexpr (SEP) {
+          const float4 w = reinterpret_cast<const float4*>(sW)[(base >> 2) + kb * 4 + g4];
+          s[kb] = f32x4_t{w.x, w.y, w.z, w.w};
+        } else {
+          s[kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+        if (!MASKED || base + kb * 16 <= kmax_blk) {
+          const bf16x8_t k0 = as_bf16x8(*reinterpret_cast<const uint4*>(stg + kb * 16 * DH + k_off0));
+          const bf16x8_t k1 = as_bf16x8(*reinterpret_cast<const uint4*>(stg + kb * 16 * DH + k_off1));
+          s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[0], s[kb], 0, 0, 0);
+          s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[1], s[kb], 0, 0, 0);
+        }
+      }
+    };
+    // bias (variants), mask, online softmax and O^T += V^T P^T for key tile kt
+    auto tile = [&](auto masked_tag, int kt, f32x4_t(&s)[4]) __attribute__((always_inline)) {
+      constexpr bool MASKED = decltype(masked_tag)::value;
+      const bf16_t* stg = sKV + kt * STAGE;
+      const int base = kt * AK;
+      if constexpr (!SEP) {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          const float4 wq = reinterpret_cast<const float4*>(sW)[(base >> 2) + kb * 4 + g4];
+          const float wk[4] = {wq.x, wq.y, wq.z, wq.w};
+          int4 t4 = make_int4(0, 0, 0, 0);
+          if constexpr (TBK) t4 = reinterpret_cast<const int4*>(sT)[(base >> 2) + kb * 4 + g4];
+          const int32_t tk[4] = {t4.x, t4.y, t4.z, t4.w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float x = s[kb][i] * a.scale2 + (FULL ? -fabsf(wk[i] - w_i_u) : wk[i]);
+            if constexpr (TBK) x -= st2 * static_cast<float>(bucket_lookup(sLUT, sTB, a.tb_p2, abs(tq - tk[i])));
+            s[kb][i] = x;
+          }
+        }
+      }
+      if constexpr (MASKED) {
+        const int lim = k_lim - base - g4 * 4;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (kb * 16 + i > lim) s[kb][i] = -INFINITY;
+      }
+      float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), s[0][2]), fmaxf(fmaxf(s[0][3], s[1][0]), s[1][1]));
+      mx = fmaxf(fmaxf(mx, s[1][2]), fmaxf(fmaxf(s[1][3], s[2][0]), s[2][1]));
+      mx = fmaxf(fmaxf(mx, s[2][2]), fmaxf(fmaxf(s[2][3], s[3][0]), s[3][1]));
+      mx = fmaxf(fmaxf(mx, s[3][2]), s[3][3]);
+      mx = xor32_max(xor16_max(mx));
+      if (__builtin_amdgcn_ballot_w64(mx > m_run + th) != 0) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * SC);
+        m_run = m_new;
+        lsum *= alpha;
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) accO[nb] = accO[nb] * alpha;
+      }
+      const float mb = -m_run * SC;
+      bf16x8_t pf[2];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        uint4 pk;
+        uint32_t* pw = reinterpret_cast<uint32_t*>(&pk);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const f32x4_t& sb = s[2 * ks + (j >> 1)];
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sb[(j & 1) * 2], SC, mb));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sb[(j & 1) * 2 + 1], SC, mb));
+          pw[j] = pack_bf16x2(p0, p1);
+          lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw[j]),
+                                                  __builtin_bit_cast(bf16x2_t, 0x3F803F80u), lsum, false);
+        }
+        pf[ks] = as_bf16x8(pk);
+      }
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        if (MASKED && base + ks * 32 > kmax_blk) continue;
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+          const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(stg + v_off[nb] + (ks * 32) * DH));
+          const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(stg + v_off[nb] + (ks * 32 + 16) * DH));
+          const v4i16_t both[2] = {lo, hi};
+          accO[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, both), pf[ks], accO[nb], 0, 0, 0);
+        }
+      }
+    };
+    // Key tiles newest first; only the first can cross a query's limit.  The scores of
+    // the next tile are issued before the softmax of this one, so the matrix cores work
+    // on them while the vector units run the exponentials.
+    if (n_t > 0) {
+      f32x4_t sc[4], sn[4];
+      scores(std::true_type{}, n_t - 1, sc);
+      if (n_t > 1) scores(std::false_type{}, n_t - 2, sn);
+      tile(std::true_type{}, n_t - 1, sc);
+      for (int kt = n_t - 2; kt >= 0; --kt) {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) sc[kb] = sn[kb];
+        if (kt > 0) scores(std::false_type{}, kt - 1, sn);
+        tile(std::false_type{}, kt, sc);
+      }
+    }
+
+    if (is_cand) {  // the candidate's own key: bias 0 (it is the reference point)
+      float dot = 0.f, kf[8], qv[8];
+#pragma unroll
+      for (int hlf = 0; hlf < 2; ++hlf) {
+        unpack8(__builtin_bit_cast(uint4, kself[hlf]), kf);
+        unpack8(__builtin_bit_cast(uint4, qf[hlf]), qv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dot += qv[e] * kf[e];
+      }
+      dot = xor32_sum(xor16_sum(dot));
+      const float m_self = SEP ? dot : dot * a.scale2 - tbk_self;
+      const float m_new = fmaxf(m_run, m_self);
+      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * SC);
+      const float p_self = __builtin_amdgcn_exp2f((m_self - m_new) * SC);
+      m_run = m_new;
+      lsum = lsum * alpha + (g4 == 0 ? p_self : 0.f);
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        const u32x2_t vv = vself[nb];
+        const float v4[4] = {__uint_as_float(vv.x << 16), __uint_as_float(vv.x & 0xFFFF0000u),
+                             __uint_as_float(vv.y << 16), __uint_as_float(vv.y & 0xFFFF0000u)};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) accO[nb][i] = accO[nb][i] * alpha + p_self * v4[i];
+      }
+    }
+    const float ltot = xor32_sum(xor16_sum(lsum));
+    if (q_valid) {
+      const float inv = 1.f / ltot;
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        uint2 o;
+        o.x = pack_bf16x2(accO[nb][0] * inv, accO[nb][1] * inv);
+        o.y = pack_bf16x2(accO[nb][2] * inv, accO[nb][3] * inv);
+        *reinterpret_cast<uint2*>(a.o + qrow * a.ld_o + h * DH + nb * 16 + g4 * 4) = o;
+      }
+      if (a.lse && g4 == 0) a.lse[qrow * a.H + h] = LN2 * (m_run * SC + log2f(ltot) - (FULL ? 0.f : w_i));
+    }
+  }
+}
+
 // ------------------------------------------------------------------ f32 kernel
 // One wave per (row, head); lane d owns output dimension d (dh <= 64).  The bias is the
 // literal -sp|p_i - p_j| - st|tau_i - tau_j| and the mask the literal predicate.
@@ -773,14 +1475,26 @@ void set_variant(AttnArgs& a, const genrank_alibi& alibi) {
   a.n_tb = (alibi.flags & GENRANK_ATTN_TIME_BUCKET) ? alibi.n_time_bounds : 0;
   a.tb_p2 = bucket_p2(a.n_tb);
 }
-void launch_bf16_variant(int flags, dim3 grid, hipStream_t stream, const AttnArgs& a) {
+// Batches whose longest history fits in LDS take the pair kernel (one workgroup per
+// (user, head)); longer histories the ring kernel over the tile grid.
+void launch_bf16_variant(int flags, int max_hist, dim3 grid, hipStream_t stream, const AttnArgs& a) {
   const int var = ((flags & GENRANK_ATTN_FULL_HISTORY) ? VAR_FULL : 0) |
                   ((flags & GENRANK_ATTN_TIME_BUCKET) ? VAR_TBUCKET : 0);
+  if (max_hist <= PAIR_MAXK) {
+    const dim3 pg(static_cast<unsigned>(a.B * a.H));
+    switch (var) {
+      case 0: hipLaunchKernelGGL((attn_fwd_pair_kernel<0>), pg, dim3(PAIR_NT), 0, stream, a); break;
+      case 1: hipLaunchKernelGGL((attn_fwd_pair_kernel<1>), pg, dim3(PAIR_NT), 0, stream, a); break;
+      case 2: hipLaunchKernelGGL((attn_fwd_pair_kernel<2>), pg, dim3(PAIR_NT), 0, stream, a); break;
+      default: hipLaunchKernelGGL((attn_fwd_pair_kernel<3>), pg, dim3(PAIR_NT), 0, stream, a); break;
+    }
+    return;
+  }
   switch (var) {
-    case 0: hipLaunchKernelGGL((attn_fwd_bf16_kernel<false, 0>), grid, dim3(NT), 0, stream, a); break;
-    case 1: hipLaunchKernelGGL((attn_fwd_bf16_kernel<false, 1>), grid, dim3(NT), 0, stream, a); break;
-    case 2: hipLaunchKernelGGL((attn_fwd_bf16_kernel<false, 2>), grid, dim3(NT), 0, stream, a); break;
-    default: hipLaunchKernelGGL((attn_fwd_bf16_kernel<false, 3>), grid, dim3(NT), 0, stream, a); break;
+    case 0: hipLaunchKernelGGL((attn_fwd_ring_kernel<0>), grid, dim3(NT), 0, stream, a); break;
+    case 1: hipLaunchKernelGGL((attn_fwd_ring_kernel<1>), grid, dim3(NT), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((attn_fwd_ring_kernel<2>), grid, dim3(NT), 0, stream, a); break;
+    default: hipLaunchKernelGGL((attn_fwd_ring_kernel<3>), grid, dim3(NT), 0, stream, a); break;
   }
 }
 
@@ -805,6 +1519,7 @@ genrank_status launch_attn_fwd(const genrank_batch* b, const int32_t* offsets, c
       a.st2[h] = alibi.slopes_time[h] * LOG2E;
     }
     a.scale2 = LOG2E / sqrtf(static_cast<float>(b->dh));
+    a.rscale2 = sqrtf(static_cast<float>(b->dh)) / LOG2E;
     a.B = b->B; a.m = b->m; a.H = b->H;
     a.hist_tiles = (b->max_hist + AQ - 1) / AQ;
     a.cand_tiles = (b->m + AQ - 1) / AQ;
@@ -815,7 +1530,7 @@ genrank_status launch_attn_fwd(const genrank_batch* b, const int32_t* offsets, c
     const int64_t G = pairs * (a.hist_tiles + a.cand_tiles);
     if (G > INT32_MAX) return GENRANK_E_SHAPE;
     set_variant(a, alibi);
-    launch_bf16_variant(alibi.flags, dim3(static_cast<unsigned>(G)), stream, a);
+    launch_bf16_variant(alibi.flags, b->max_hist, dim3(static_cast<unsigned>(G)), stream, a);
   } else {
     AttnF32Args a{};
     a.offsets = offsets; a.ts = ts; a.req = req;
@@ -862,6 +1577,7 @@ genrank_status launch_attn_fwd_cached(const genrank_batch* b, const int32_t* off
     a.st2[h] = alibi.slopes_time[h] * LOG2E;
   }
   a.scale2 = LOG2E / sqrtf(static_cast<float>(b->dh));
+  a.rscale2 = sqrtf(static_cast<float>(b->dh)) / LOG2E;
   a.B = b->B; a.m = b->m; a.H = b->H;
   a.hist_tiles = 0;  // candidate tiles only: history queries were answered earlier
   a.cand_tiles = (b->m + AQ - 1) / AQ;
@@ -872,8 +1588,8 @@ genrank_status launch_attn_fwd_cached(const genrank_batch* b, const int32_t* off
   const int64_t G = pairs * a.cand_tiles;
   if (G > INT32_MAX) return GENRANK_E_SHAPE;
   set_variant(a, alibi);
-  // no history query is answered here: only the time variant matters
-  launch_bf16_variant(alibi.flags & GENRANK_ATTN_TIME_BUCKET, dim3(static_cast<unsigned>(G)), stream, a);
+  // the same instance as the full forward's candidate tiles, so that both give the same bits
+  launch_bf16_variant(alibi.flags, b->max_hist, dim3(static_cast<unsigned>(G)), stream, a);
   GR_CHECK_LAUNCH();
   return GENRANK_OK;
 }
