@@ -644,6 +644,47 @@ static_assert(QB == 1 && NW * 8 == AK, "one 16-query block per wave; 8 tile rows
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// The ring and pair kernels give candidate rows the same bits (cached scoring runs the ring
+// kernel, the full forward the pair kernel), so the steps whose rounding could differ are
+// written once, here, with explicit FMAs.
+// Bias term of a key in score units: position part, plus the time part unless bucketed.
+__device__ __forceinline__ float key_term(bool tbk, float spr, float str, int dp, int32_t dt) {
+  return tbk ? spr * static_cast<float>(dp) : __builtin_fmaf(spr, static_cast<float>(dp), str * static_cast<float>(dt));
+}
+// Scaled score plus bias (the non-separable variants, log2 units).
+__device__ __forceinline__ float biased(float s, float scale2, float bias) { return __builtin_fmaf(s, scale2, bias); }
+// Merge a candidate's own key (score m_self in score units, value row vself) into its
+// softmax state after the history keys.
+__device__ __forceinline__ void merge_self(const u32x4_t (&kself)[2], const u32x2_t (&vself)[4], const bf16x8_t (&qf)[2],
+                                           bool sep, float scale2, float self_bias, float SC, int g4, float& m_run,
+                                           float& lsum, f32x4_t (&accO)[4]) {
+  float dot = 0.f, kf[8], qv[8];
+#pragma unroll
+  for (int hlf = 0; hlf < 2; ++hlf) {
+    unpack8(__builtin_bit_cast(uint4, kself[hlf]), kf);
+    unpack8(__builtin_bit_cast(uint4, qf[hlf]), qv);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dot = __builtin_fmaf(qv[e], kf[e], dot);
+  }
+  dot = xor32_sum(xor16_sum(dot));
+  const float m_self = sep ? dot : __builtin_fmaf(dot, scale2, -self_bias);
+  const float m_new = fmaxf(m_run, m_self);
+  const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * SC);
+  const float p_self = __builtin_amdgcn_exp2f((m_self - m_new) * SC);
+  m_run = m_new;
+  lsum = __builtin_fmaf(lsum, alpha, g4 == 0 ? p_self : 0.f);
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    const u32x2_t vv = vself[nb];
+    const float v4[4] = {__uint_as_float(vv.x << 16), __uint_as_float(vv.x & 0xFFFF0000u),
+                         __uint_as_float(vv.y << 16), __uint_as_float(vv.y & 0xFFFF0000u)};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) accO[nb][i] = __builtin_fmaf(accO[nb][i], alpha, p_self * v4[i]);
+  }
+}
 
 template <int VAR>
 __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8))) attn_fwd_ring_kernel(AttnArgs a) {
@@ -725,9 +766,8 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
   bf16x8_t qf[2];
   qf[0] = as_bf16x8(*reinterpret_cast<const uint4*>(a.q + rowoff + g4 * 8));
   qf[1] = as_bf16x8(*reinterpret_cast<const uint4*>(a.q + rowoff + g4 * 8 + 32));
-  // a candidate's own key and value (the softmax seed; history tiles read and drop them)
-  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-  typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+  // a candidate's own key and value (merged after the history keys; history tiles read
+  // and drop them)
   u32x4_t kself[2];
   u32x2_t vself[4];
   kself[0] = *reinterpret_cast<const u32x4_t*>(a.k + rowoff + g4 * 8);
@@ -776,9 +816,7 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
     }
 
   // ---- bias terms of the first chunk, in the score units above
-  sW[tid] = wkey_in ? (TBK ? spr * static_cast<float>(wkey - p_ref)
-                           : spr * static_cast<float>(wkey - p_ref) + str * static_cast<float>(static_cast<int32_t>(ts_key - ts_ref)))
-                    : 0.f;
+  sW[tid] = wkey_in ? key_term(TBK, spr, str, wkey - p_ref, static_cast<int32_t>(ts_key - ts_ref)) : 0.f;
   if constexpr (TBK) sT[tid] = wkey_in ? static_cast<int32_t>(ts_key - ts_ref) : 0;
   auto load_w = [&](int wb) {
     for (int j = tid; j < WCHUNK; j += NT) {
@@ -787,43 +825,22 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
       int32_t tk = 0;
       if (key < N) {
         tk = static_cast<int32_t>(a.ts[off + key] - ts_ref);
-        w = TBK ? spr * static_cast<float>(key - p_ref) : spr * static_cast<float>(key - p_ref) + str * static_cast<float>(tk);
+        w = key_term(TBK, spr, str, key - p_ref, tk);
       }
       sW[j] = w;
       if constexpr (TBK) sT[j] = tk;
     }
   };
 
-  // ---- softmax state in score units; a candidate starts from its own key (bias 0)
+  // ---- softmax state in score units
   f32x4_t accO[4];
-  float m_run, lsum;
-  if (is_cand) {
-    float dot = 0.f, kf[8], qv[8];
+  float m_run = -1e30f, lsum = 0.f;
 #pragma unroll
-    for (int hlf = 0; hlf < 2; ++hlf) {
-      unpack8(__builtin_bit_cast(uint4, kself[hlf]), kf);
-      unpack8(__builtin_bit_cast(uint4, qf[hlf]), qv);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) dot += qv[e] * kf[e];
-    }
-    dot = xor32_sum(xor16_sum(dot));
-    m_run = SEP ? dot : dot * a.scale2;  // (bucketed time: its gap-0 term follows below)
-    lsum = (g4 == 0) ? 1.f : 0.f;
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      const u32x2_t vv = vself[nb];
-      accO[nb] = f32x4_t{__uint_as_float(vv.x << 16), __uint_as_float(vv.x & 0xFFFF0000u),
-                         __uint_as_float(vv.y << 16), __uint_as_float(vv.y & 0xFFFF0000u)};
-    }
-  } else {
-    m_run = -1e30f;
-    lsum = 0.f;
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb) accO[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  }
+  for (int nb = 0; nb < 4; ++nb) accO[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   lds_sync();  // sW, sT, sTB written
+  float tbk_self = 0.f;  // bucketed time term of a candidate's own key (gap 0)
   if constexpr (TBK) {
-    if (is_cand) m_run -= st2 * static_cast<float>(bucket_search(sTB, a.tb_p2, 0));
+    tbk_self = st2 * static_cast<float>(bucket_search(sTB, a.tb_p2, 0));
     bucket_table_build(sLUT, sTB, a.tb_p2, tid, NT);
     lds_sync();
   }
@@ -874,7 +891,7 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
         const int32_t tk[4] = {t4.x, t4.y, t4.z, t4.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          float x = s[kb][i] * a.scale2 + (FULL ? -fabsf(wk[i] - w_i_u) : wk[i]);
+          float x = biased(s[kb][i], a.scale2, FULL ? -fabsf(wk[i] - w_i_u) : wk[i]);
           if constexpr (TBK) x -= st2 * static_cast<float>(bucket_lookup(sLUT, sTB, a.tb_p2, abs(tq - tk[i])));
           s[kb][i] = x;
         }
@@ -969,6 +986,7 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
     if (it + 3 < n_tiles) step(std::false_type{}, I1{}, it + 3);
   }
   wait_vmcnt<0>();  // no direct load may still be writing LDS when the workgroup ends
+  if (is_cand) merge_self(kself, vself, qf, SEP, a.scale2, tbk_self, SC, g4, m_run, lsum, accO);
 
   // ---- epilogue
   const float ltot = xor32_sum(xor16_sum(lsum));
@@ -1083,7 +1101,7 @@ __global__ void __launch_bounds__(PAIR_NT) attn_fwd_pair_kernel(AttnArgs a) {
     int32_t tk = 0;
     if (tid < N) {
       tk = static_cast<int32_t>(a.ts[off + tid] - ts_ref);
-      w = TBK ? spr * static_cast<float>(tid - N) : spr * static_cast<float>(tid - N) + str * static_cast<float>(tk);
+      w = key_term(TBK, spr, str, tid - N, tk);
     }
     sW[tid] = w;
     if constexpr (TBK) sT[tid] = tk;
@@ -1121,8 +1139,6 @@ __global__ void __launch_bounds__(PAIR_NT) attn_fwd_pair_kernel(AttnArgs a) {
     const int b = nb_h - 1 - (k - nb_c);
     return off + min(b * QW + l16, N - 1);
   };
-  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-  typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
   u32x4_t qn[2] = {};
   if (wave < n_units) {
     const int64_t ro = q_row(wave) * a.ld_qkv + h * DH + g4 * 8;
@@ -1204,7 +1220,7 @@ __global__ void __launch_bounds__(PAIR_NT) attn_fwd_pair_kernel(AttnArgs a) {
           const int32_t tk[4] = {t4.x, t4.y, t4.z, t4.w};
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            float x = s[kb][i] * a.scale2 + (FULL ? -fabsf(wk[i] - w_i_u) : wk[i]);
+            float x = biased(s[kb][i], a.scale2, FULL ? -fabsf(wk[i] - w_i_u) : wk[i]);
             if constexpr (TBK) x -= st2 * static_cast<float>(bucket_lookup(sLUT, sTB, a.tb_p2, abs(tq - tk[i])));
             s[kb][i] = x;
           }
@@ -1260,47 +1276,19 @@ __global__ void __launch_bounds__(PAIR_NT) attn_fwd_pair_kernel(AttnArgs a) {
         }
       }
     };
-    // Key tiles newest first; only the first can cross a query's limit.  The scores of
-    // the next tile are issued before the softmax of this one, so the matrix cores work
-    // on them while the vector units run the exponentials.
+    // key tiles newest first; only the first can cross a query's limit
     if (n_t > 0) {
-      f32x4_t sc[4], sn[4];
+      f32x4_t sc[4];
       scores(std::true_type{}, n_t - 1, sc);
-      if (n_t > 1) scores(std::false_type{}, n_t - 2, sn);
       tile(std::true_type{}, n_t - 1, sc);
       for (int kt = n_t - 2; kt >= 0; --kt) {
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) sc[kb] = sn[kb];
-        if (kt > 0) scores(std::false_type{}, kt - 1, sn);
+        scores(std::false_type{}, kt, sc);
         tile(std::false_type{}, kt, sc);
       }
     }
 
-    if (is_cand) {  // the candidate's own key: bias 0 (it is the reference point)
-      float dot = 0.f, kf[8], qv[8];
-#pragma unroll
-      for (int hlf = 0; hlf < 2; ++hlf) {
-        unpack8(__builtin_bit_cast(uint4, kself[hlf]), kf);
-        unpack8(__builtin_bit_cast(uint4, qf[hlf]), qv);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) dot += qv[e] * kf[e];
-      }
-      dot = xor32_sum(xor16_sum(dot));
-      const float m_self = SEP ? dot : dot * a.scale2 - tbk_self;
-      const float m_new = fmaxf(m_run, m_self);
-      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * SC);
-      const float p_self = __builtin_amdgcn_exp2f((m_self - m_new) * SC);
-      m_run = m_new;
-      lsum = lsum * alpha + (g4 == 0 ? p_self : 0.f);
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        const u32x2_t vv = vself[nb];
-        const float v4[4] = {__uint_as_float(vv.x << 16), __uint_as_float(vv.x & 0xFFFF0000u),
-                             __uint_as_float(vv.y << 16), __uint_as_float(vv.y & 0xFFFF0000u)};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) accO[nb][i] = accO[nb][i] * alpha + p_self * v4[i];
-      }
-    }
+    // the candidate's own key: bias 0 (it is the reference point)
+    if (is_cand) merge_self(kself, vself, qf, SEP, a.scale2, tbk_self, SC, g4, m_run, lsum, accO);
     const float ltot = xor32_sum(xor16_sum(lsum));
     if (q_valid) {
       const float inv = 1.f / ltot;
@@ -1588,8 +1576,9 @@ genrank_status launch_attn_fwd_cached(const genrank_batch* b, const int32_t* off
   const int64_t G = pairs * a.cand_tiles;
   if (G > INT32_MAX) return GENRANK_E_SHAPE;
   set_variant(a, alibi);
-  // the same instance as the full forward's candidate tiles, so that both give the same bits
-  launch_bf16_variant(alibi.flags, b->max_hist, dim3(static_cast<unsigned>(G)), stream, a);
+  // the ring kernel (candidate tiles stream the history); the variant instance matches the
+  // full forward's, and candidate rows get the same bits from both kernels
+  launch_bf16_variant(alibi.flags, INT32_MAX, dim3(static_cast<unsigned>(G)), stream, a);
   GR_CHECK_LAUNCH();
   return GENRANK_OK;
 }
