@@ -1032,7 +1032,8 @@ __global__ void __launch_bounds__(PAIR_NT) attn_fwd_pair_kernel(AttnArgs a) {
   __shared__ uint32_t sLUT[TBK ? BK_CELLS : 1];
   __shared__ int sCnt[PAIR_MAXT + 1];
   __shared__ int sWave[PAIR_WAVES];
-  __shared__ int sUser;
+  __shared__ int sUser, sLen;
+  __shared__ int64_t sOff, sReq;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1041,14 +1042,22 @@ __global__ void __launch_bounds__(PAIR_NT) attn_fwd_pair_kernel(AttnArgs a) {
   // Which pair: workgroups run in launch order, so the pairs go heaviest first (users
   // ordered by key-tile count, descending, ties by index) and the light ones fill the end
   // of the launch.  Every workgroup derives the same order from the offsets.  With more
-  // users than threads the order is the plain one.
+  // users than threads the order is the plain one.  The thread that finds the pair
+  // passes on its user's offset, length and request time (no second round trip).
   const int ur = blockIdx.x / a.H;
   const int h = blockIdx.x - ur * a.H;
-  int u = ur;
+  int u = ur, len;
+  int64_t off, ts_ref;
   if (a.B <= PAIR_NT) {
     if (tid <= PAIR_MAXT) sCnt[tid] = 0;
-    int ntl = -1;
-    if (tid < a.B) ntl = (min(a.offsets[tid + 1] - a.offsets[tid], PAIR_MAXK) + AK - 1) / AK;
+    int ntl = -1, o0 = 0, o1 = 0;
+    int64_t rq = 0;
+    if (tid < a.B) {
+      o0 = a.offsets[tid];
+      o1 = a.offsets[tid + 1];
+      rq = a.req[tid];
+      ntl = (min(o1 - o0, PAIR_MAXK) + AK - 1) / AK;
+    }
     lds_sync();
     if (ntl >= 0) atomicAdd(&sCnt[ntl], 1);
     lds_sync();
@@ -1061,21 +1070,31 @@ __global__ void __launch_bounds__(PAIR_NT) attn_fwd_pair_kernel(AttnArgs a) {
     lds_sync();
     int rank = below;
     for (int w = 0; w < wave; ++w) rank += sWave[w];
-    if (mine && rank == ur - before) sUser = tid;
+    if (mine && rank == ur - before) {
+      sUser = tid;
+      sOff = o0;
+      sLen = o1 - o0;
+      sReq = rq;
+    }
     lds_sync();
     u = sUser;
+    off = sOff;
+    len = sLen;
+    ts_ref = sReq;
+  } else {
+    off = a.offsets[u];
+    len = a.offsets[u + 1] - a.offsets[u];
+    ts_ref = a.req[u];
   }
-  const int64_t off = a.offsets[u];
   // (a history longer than the batch's declared maximum is cut, so that LDS is never
   // overrun; the declared maximum is the caller's promise)
-  const int N = min(a.offsets[u + 1] - a.offsets[u], PAIR_MAXK);
+  const int N = min(len, PAIR_MAXK);
   const int n_tiles = (N + AK - 1) / AK;
   const int l16 = lane & 15, g4 = lane >> 4;
   const float sp2 = a.sp2[h], st2 = a.st2[h];
   const float SC = SEP ? a.scale2 : 1.f;
   const float spr = SEP ? sp2 * a.rscale2 : sp2;
   const float str = SEP ? st2 * a.rscale2 : st2;
-  const int64_t ts_ref = a.req[u];
 
   // ---- the pair's K/V tiles: waves 0-7 load K, waves 8-15 V, rows 8 (w % 8) .. + 7 of
   // every tile (lane l: row 8 (w % 8) + l / 8, LDS chunk l % 8 <- global chunk
