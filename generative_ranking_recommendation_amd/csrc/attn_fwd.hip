@@ -11,19 +11,17 @@
 // only added back into the saved log-sum-exp.  The bias therefore costs one FMA per score
 // and no T x T array exists anywhere.
 //
-// bf16 kernel (dh = 64).  One workgroup = 4 waves x 16 query rows of one (user, head):
-// either a 64-row history tile (keys: history tiles up to and including the diagonal) or
-// a 64-row candidate tile (keys: every history tile, plus each candidate's own key, which
-// seeds the online softmax so the m x m candidate block is never formed).
-//   S^T = K Q^T with v_mfma_f32_16x16x32_bf16: K rows from LDS are the row operand, the
-//         wave's 16 queries (registers) the column operand.  Each lane then holds 16
-//         scores of ONE query, so row max / row sum need only two cross-lane steps.
-//   O^T = V^T P^T: P^T goes from the score registers straight into the column operand;
-//         V is stored transposed in LDS with its keys permuted to match that register
-//         order, so each lane's row-operand fragment is one 16-byte LDS read.
-// K/V tiles are double-buffered in LDS and the next tile is fetched into registers while
-// the current one is multiplied.  Workgroups of one (user, head) run next to each other on
-// one XCD, so their K/V reuse hits that XCD's L2.
+// bf16 kernels (dh = 64), all with S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (each lane
+// holds 16 scores of ONE query, so row max / row sum need only two cross-lane steps) and
+// O^T = V^T P^T with P^T taken straight from the score registers; a candidate never
+// forms the m x m candidate block (its own key is handled on its own):
+//   attn_fwd_pair_kernel   one workgroup per (user, head), the user's K/V resident in LDS
+//                          (histories up to PAIR_MAXK keys: the full forward);
+//   attn_fwd_ring_kernel   one workgroup per 128-query tile, K/V streamed through an LDS
+//                          ring (longer histories; candidates-only scoring);
+//   attn_fwd_rab_kernel    the tile grid with a learned bias read from memory instead of
+//                          ALiBi (the HSTU-style comparison).
+// f32 kernel: one wave per (row, head), the literal definition (reference-precision path).
 #include <math.h>
 
 #include <type_traits>
@@ -108,30 +106,25 @@ __device__ __forceinline__ float xor32_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// RAB = false: ALiBi bias computed from positions and times (the action-oriented path).
-// RAB = true: the HSTU-style comparison, where each user's history is the interleaved
-// item/action sequence (2 N slots, rows 2 off .. 2 off + 2N) and the bias is a learned
+// The HSTU-style comparison kernel: each user's history is the interleaved item/action
+// sequence (2 N slots, rows 2 off .. 2 off + 2N of q / k / v) and the bias is a learned
 // matrix read from memory (user u's [L, P] bf16 block, L = 2N + m, row pitch P = L rounded
-// up to 8); everything else is the same kernel.
-template <bool RAB, int VAR = 0>
-__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8))) attn_fwd_bf16_kernel(AttnArgs a) {
-  constexpr bool FULL = (VAR & VAR_FULL) != 0;
-  constexpr bool TBK = (VAR & VAR_TBUCKET) != 0;
-  static_assert(!RAB || VAR == 0, "the learned bias takes no ALiBi variant");
+// up to 8).  One workgroup = 8 waves x 16 query rows of one (user, head): a 128-row history
+// tile (keys up to and including the diagonal) or a 128-row candidate tile (every history
+// key, plus each candidate's own key, which seeds the online softmax).
+//   S^T = K Q^T with v_mfma_f32_16x16x32_bf16: K rows from LDS are the row operand, the
+//         wave's 16 queries (registers) the column operand, so each lane holds 16 scores
+//         of ONE query.
+//   O^T = V^T P^T: P^T goes from the score registers straight into the column operand; V
+//         is stored transposed in LDS with its keys permuted to match that register order.
+// K/V tiles are double-buffered in LDS and the next tile is fetched into registers while
+// the current one is multiplied; the lane's 16 bias values of a tile are loaded one tile
+// ahead.  The pairs' tiles run next to each other on one XCD (the flat-grid order of the
+// ring kernel).
+__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8))) attn_fwd_rab_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) bf16_t sK[2][AK * KLD];
   __shared__ __attribute__((aligned(16))) bf16_t sVt[2][DH * VLD];
-  __shared__ __attribute__((aligned(16))) float sW[WCHUNK];
-  // bucketed time term: the chunk's key times relative to tau_ref, and the bucket edges
-  __shared__ __attribute__((aligned(16))) int32_t sT[TBK ? WCHUNK : 4];
-  __shared__ int32_t sTB[TBK ? ATTN_MAX_TIME_BOUNDS : 1];
-  __shared__ uint32_t sLUT[TBK ? BK_CELLS : 1];  // bucket table over the gap
 
-  // Flat grid over (user, head, tile).  Workgroup w runs on XCD w % 8 as that XCD's
-  // (w / 8)-th workgroup.  Each XCD owns the (user, head) pairs bh = x mod 8 and walks them
-  // in groups of GROUP pairs; inside a group it runs tile 0 of every pair, then tile 1, ...
-  // (candidate tiles first, then history tiles largest first).  A pair's tiles thus run
-  // at about the same time on one XCD and re-read its K/V from that L2, while the
-  // largest-first order inside each group keeps the XCDs' finishing times close.
   const int TY = a.cand_tiles + a.hist_tiles;
   const int x8 = blockIdx.x & 7;
   const int kx = blockIdx.x >> 3;
@@ -142,9 +135,8 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
   if (bh >= a.B * a.H) return;
   const int u = bh / a.H;
   const int h = bh - u * a.H;
-  constexpr int HS = RAB ? 2 : 1;  // history slots per history action
-  const int64_t off = HS * static_cast<int64_t>(a.offsets[u]);
-  const int N = HS * (a.offsets[u + 1] - a.offsets[u]);
+  const int64_t off = 2 * static_cast<int64_t>(a.offsets[u]);
+  const int N = 2 * (a.offsets[u + 1] - a.offsets[u]);  // interleaved history slots
 
   bool is_cand;
   int q0, nq, n_tiles;
@@ -163,91 +155,44 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
     if (q0 >= N) return;
     nq = min(AQ, N - q0);
     qrow0 = off + q0;
-    // keys up to the tile's last query, or every history key
-    n_tiles = FULL ? (N + AK - 1) / AK : (q0 + nq + AK - 1) / AK;
+    n_tiles = (q0 + nq + AK - 1) / AK;
   }
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g4 = lane >> 4;
-  const float sp2 = a.sp2[h], st2 = a.st2[h];
-  // bias reference point: the candidates' shared (p, tau), or the tile's first query
-  const int p_ref = is_cand ? N : q0;
-  const int64_t ts_ref = RAB ? 0 : (is_cand ? a.req[u] : a.ts[off + q0]);
-
-  // ---- per-key bias terms w_j = sp (p_j - p_ref) + st (tau_j - tau_ref) for keys
-  // [wbase, wbase + WCHUNK); keys past the history end get 0 (they are masked).  The time
-  // difference is below 2^24 s, so it converts exactly through int32.
-  // With the bucketed time term w_j holds the position term only and sT the key's time.
-  auto load_w = [&](int wbase) {
-    for (int j = tid; j < WCHUNK; j += NT) {
-      const int key = wbase + j;
-      float w = 0.f;
-      int32_t tk = 0;
-      if (key < N) {
-        tk = static_cast<int32_t>(a.ts[off + key] - ts_ref);
-        w = TBK ? sp2 * static_cast<float>(key - p_ref)
-                : sp2 * static_cast<float>(key - p_ref) + st2 * static_cast<float>(tk);
-      }
-      sW[j] = w;
-      if constexpr (TBK) sT[j] = tk;
-    }
-  };
-  // key tiles run newest first; the first one lies in this bias chunk
   const int kt_first = n_tiles - 1;
-  int wbase = n_tiles > 0 ? (kt_first * AK / WCHUNK) * WCHUNK : 0;
 
-  // ---- Prologue.  Every load below depends only on the user's offsets; they are all
-  // issued before the first wait, so the workgroup pays about one memory round trip
-  // before its first tile instead of one per kind of data.
-  static_assert(WCHUNK == NT, "one bias key per thread in the first chunk");
-  const int wkey = wbase + tid;
-  const bool wkey_in = wkey < N;
-  const int64_t ts_key = (!RAB && wkey_in) ? a.ts[off + wkey] : ts_ref;
-
-  // this lane's queries: column block c of the wave's QW rows
-  int q_local[QB], q_slot[QB], k_lim[QB], kmax_blk[QB];
-  bool q_valid[QB];
-  int64_t qrow[QB], qrow_ld[QB];
-  bf16x8_t qf[QB][2];
-  uint4 kself[QB][2];
-  uint2 vself[QB][4];
+  // this lane's query
+  const int q_local = wave * QW + l16;
+  const bool q_valid = q_local < nq;
+  const int64_t qrow = qrow0 + q_local;
+  const int q_slot = is_cand ? (N + q0 + q_local) : (q0 + q_local);
+  // keys with a slot above k_lim are masked (a candidate's own key is the seed below)
+  const int k_lim = is_cand ? (N - 1) : min(q_slot, N - 1);
+  const int kmax_blk = is_cand ? (N - 1) : min(q0 + wave * QW + 15, N - 1);
+  const int64_t rowoff = (qrow0 + min(q_local, nq - 1)) * a.ld_qkv + h * DH;
+  bf16x8_t qf[2];
+  qf[0] = as_bf16x8(*reinterpret_cast<const uint4*>(a.q + rowoff + g4 * 8));
+  qf[1] = as_bf16x8(*reinterpret_cast<const uint4*>(a.q + rowoff + g4 * 8 + 32));
+  uint4 kself[2] = {};
+  uint2 vself[4] = {};
+  if (is_cand) {
+    kself[0] = *reinterpret_cast<const uint4*>(a.k + rowoff + g4 * 8);
+    kself[1] = *reinterpret_cast<const uint4*>(a.k + rowoff + g4 * 8 + 32);
 #pragma unroll
-  for (int c = 0; c < QB; ++c) {
-    q_local[c] = wave * QW + c * 16 + l16;
-    q_valid[c] = q_local[c] < nq;
-    qrow[c] = qrow0 + q_local[c];
-    q_slot[c] = is_cand ? (N + q0 + q_local[c]) : (q0 + q_local[c]);
-    // lanes past the tile's last query read that query's row (never stored)
-    qrow_ld[c] = qrow0 + min(q_local[c], nq - 1);
-    // keys with a slot above k_lim are masked: history queries see keys up to
-    // themselves (all history keys with the fully visible mask), candidates every
-    // history key (their own key is the seed below)
-    k_lim[c] = (is_cand || FULL) ? (N - 1) : min(q_slot[c], N - 1);
-    // largest key any query of this 16-column block may see (uniform per wave)
-    kmax_blk[c] = (is_cand || FULL) ? (N - 1) : min(q0 + wave * QW + c * 16 + 15, N - 1);
-    const int64_t rowoff = qrow_ld[c] * a.ld_qkv + h * DH;
-    qf[c][0] = as_bf16x8(*reinterpret_cast<const uint4*>(a.q + rowoff + g4 * 8));
-    qf[c][1] = as_bf16x8(*reinterpret_cast<const uint4*>(a.q + rowoff + g4 * 8 + 32));
-    if (is_cand) {  // the candidate's own key and value (the softmax seed below)
-      kself[c][0] = *reinterpret_cast<const uint4*>(a.k + rowoff + g4 * 8);
-      kself[c][1] = *reinterpret_cast<const uint4*>(a.k + rowoff + g4 * 8 + 32);
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
-        vself[c][nb] = *reinterpret_cast<const uint2*>(a.v + rowoff + nb * 16 + g4 * 4);
-    }
+    for (int nb = 0; nb < 4; ++nb) vself[nb] = *reinterpret_cast<const uint2*>(a.v + rowoff + nb * 16 + g4 * 4);
   }
 
   // ---- K/V tile staging: waves 0-3 move K, waves 4-7 move V, two 16-byte loads per lane
-  // per tile.  K: rows krow and krow+32, columns kcol..kcol+7 (8 lanes per 128-byte row:
-  // conflict-free 16-byte LDS writes).  V: the key pair 2pr, 2pr+1, columns 8ch..8ch+7,
-  // into sVt transposed; each 32-bit write holds the two keys' values of one column
-  // (adjacent in the permuted key order).  Loads are buffer loads over the user's history
-  // rows: descriptor in scalar registers, loop-invariant lane offsets, scalar tile offset;
-  // rows past the history end read as zero (the mask gives those keys probability 0).
-  // Two tiles are in flight: the loads for tile kt-2 are issued while tile kt is
-  // multiplied, and tile kt-1 (issued one step earlier) is written to LDS after it.
+  // per tile.  K: rows krow and krow+32, columns kcol..kcol+7 (conflict-free 16-byte LDS
+  // writes).  V: the key pair 2pr, 2pr+1, columns 8ch..8ch+7, into sVt transposed; each
+  // 32-bit write holds the two keys' values of one column.  Buffer loads over the user's
+  // history rows; rows past the history end read as zero (the mask gives those keys
+  // probability 0), and a tile index below 0 gets an offset at the record count (zeros, no
+  // memory access; such a stage is never written to LDS).  Every fetch is issued, so the
+  // wait before a stash covers only that stage's own two loads.
   const bool stage_k = wave < NW / 2;
   const int st = tid & (NT / 2 - 1);
   const int pr = st & 31;
@@ -265,11 +210,6 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
   const uint32_t vo1 = vo0 + (stage_k ? 32u : 1u) * row_bytes;
   struct Stage { uint4 r0, r1; };
   Stage S0, S1;
-  // A tile index below 0 gets an offset at the descriptor's record count: the hardware
-  // returns zeros without touching memory, and such a stage is never written to LDS.  The
-  // whole offset goes in the vector operand, which the range check covers.
-  // Issuing every fetch keeps the count of loads in flight the same on all paths, so the
-  // wait before a stash covers only that stage's own two loads.
   auto fetch = [&](int kt, Stage& S) {
     const uint32_t so = kt >= 0 ? static_cast<uint32_t>(kt * AK) * row_bytes : hist_bytes;
     S.r0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsKV, vo0 + so, 0, 0));
@@ -296,290 +236,158 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
   fetch(kt_first, S0);
   fetch(kt_first - 1, S1);
 
-  // ---- learned bias (RAB): the lane's 16 bias values of a key tile are four 8-byte
-  // pieces of its query's row, loaded one tile ahead.  A buffer descriptor over the user's
-  // matrix: rows past it and tile indices below 0 read zeros without a memory access.
+  // ---- the learned bias: the lane's 16 bias values of a key tile are four 8-byte pieces
+  // of its query's row, loaded one tile ahead.  A buffer descriptor over the user's matrix:
+  // rows past it and tile indices below 0 read zeros without a memory access.
   struct RabRegs { uint2 v[4]; };
   RabRegs R0, R1;
-  static_assert(!RAB || QB == 1, "one query per lane");
-  const uint32_t rab_P = RAB ? static_cast<uint32_t>((N + a.m + 7) & ~7) : 0u;
-  const uint32_t rab_bytes = RAB ? static_cast<uint32_t>(N + a.m) * rab_P * 2u : 0u;
-  const uint32_t rab_row = static_cast<uint32_t>(q_slot[0]) * rab_P * 2u + g4 * 8u;
+  const uint32_t rab_P = static_cast<uint32_t>((N + a.m + 7) & ~7);
+  const uint32_t rab_bytes = static_cast<uint32_t>(N + a.m) * rab_P * 2u;
+  const uint32_t rab_row = static_cast<uint32_t>(q_slot) * rab_P * 2u + g4 * 8u;
   const __amdgpu_buffer_rsrc_t rsR = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<bf16_t*>(RAB ? a.rab + a.rab_off[u] : a.q), static_cast<short>(0), rab_bytes, BUF_DWORD3);
-  float rab_self[QB];
-  if constexpr (RAB) {
-    const uint32_t P = rab_P;
-#pragma unroll
-    for (int c = 0; c < QB; ++c) {
-      const uint16_t b = __builtin_amdgcn_raw_buffer_load_b16(
-          rsR, static_cast<uint32_t>(q_slot[c]) * static_cast<uint32_t>(P + 1) * 2u, 0, 0);
-      rab_self[c] = __uint_as_float(static_cast<uint32_t>(b) << 16);
-    }
-  }
+      const_cast<bf16_t*>(a.rab + a.rab_off[u]), static_cast<short>(0), rab_bytes, BUF_DWORD3);
+  const uint16_t rab_self_b = __builtin_amdgcn_raw_buffer_load_b16(
+      rsR, static_cast<uint32_t>(q_slot) * (rab_P + 1u) * 2u, 0, 0);  // the bias of (i, i)
   auto rab_load = [&](int kt, RabRegs& R) {
-    if constexpr (RAB) {
-      const uint32_t so = kt >= 0 ? static_cast<uint32_t>(kt * AK) * 2u : rab_bytes;
+    const uint32_t so = kt >= 0 ? static_cast<uint32_t>(kt * AK) * 2u : rab_bytes;
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-        R.v[kb] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rsR, rab_row + kb * 32u + so, 0, 0));
-    }
+    for (int kb = 0; kb < 4; ++kb)
+      R.v[kb] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rsR, rab_row + kb * 32u + so, 0, 0));
   };
   rab_load(kt_first, R0);
 
-  // ---- bias terms of the first chunk (the loads above stay in flight)
-  if constexpr (!RAB) {
-    const int32_t tk = static_cast<int32_t>(ts_key - ts_ref);
-    sW[tid] = wkey_in ? (TBK ? sp2 * static_cast<float>(wkey - p_ref)
-                             : sp2 * static_cast<float>(wkey - p_ref) + st2 * static_cast<float>(tk))
-                      : 0.f;
-    if constexpr (TBK) sT[tid] = wkey_in ? tk : 0;
-  }
-  // bucket edges in LDS, padded to a power of two with the largest int32
-  if constexpr (TBK)
-    for (int k = tid; k < a.tb_p2; k += NT) {
-      const int64_t b = k < a.n_tb ? a.tb[k] : INT64_MAX;
-      sTB[k] = b > INT32_MAX ? INT32_MAX : (b < INT32_MIN ? INT32_MIN : static_cast<int32_t>(b));
+  // ---- softmax state (log2 units); a candidate starts from its own key
+  f32x4_t accO[4];
+  float m2, lsum;
+  if (is_cand) {
+    float dot = 0.f, kf[8], qv[8];
+#pragma unroll
+    for (int hlf = 0; hlf < 2; ++hlf) {
+      unpack8(kself[hlf], kf);
+      unpack8(__builtin_bit_cast(uint4, qf[hlf]), qv);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dot += qv[e] * kf[e];
     }
-
-  // ---- softmax state; a candidate starts from its own key: bias 0 (it shares p_ref and
-  // tau_ref), so its score is the plain scaled dot product
-  f32x4_t accO[QB][4];
-  float m2[QB], lsum[QB];
+    dot = xor32_sum(xor16_sum(dot));
+    m2 = dot * a.scale2 + __uint_as_float(static_cast<uint32_t>(rab_self_b) << 16) * LOG2E;
+    lsum = (g4 == 0) ? 1.f : 0.f;
 #pragma unroll
-  for (int c = 0; c < QB; ++c) {
-    if (is_cand) {
-      float dot = 0.f;
-      float kf[8], qv[8];
-#pragma unroll
-      for (int hlf = 0; hlf < 2; ++hlf) {
-        unpack8(kself[c][hlf], kf);
-        unpack8(__builtin_bit_cast(uint4, qf[c][hlf]), qv);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) dot += qv[e] * kf[e];
-      }
-      dot = xor32_sum(xor16_sum(dot));
-      m2[c] = dot * a.scale2;
-      if constexpr (RAB) m2[c] += rab_self[c] * LOG2E;  // the learned bias of (i, i)
-      // the bucketed time term of the candidate's own key (gap 0), read from global
-      // memory: the LDS copy of the edges is not complete yet
-      if constexpr (TBK) m2[c] -= st2 * static_cast<float>(bucket_search_global(a.tb, a.n_tb, 0));
-      lsum[c] = (g4 == 0) ? 1.f : 0.f;
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        const uint2 vv = vself[c][nb];
-        accO[c][nb] = f32x4_t{__uint_as_float(vv.x << 16), __uint_as_float(vv.x & 0xFFFF0000u),
-                              __uint_as_float(vv.y << 16), __uint_as_float(vv.y & 0xFFFF0000u)};
-      }
-    } else {
-      m2[c] = -1e30f;
-      lsum[c] = 0.f;
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) accO[c][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int nb = 0; nb < 4; ++nb) {
+      const uint2 vv = vself[nb];
+      accO[nb] = f32x4_t{__uint_as_float(vv.x << 16), __uint_as_float(vv.x & 0xFFFF0000u),
+                         __uint_as_float(vv.y << 16), __uint_as_float(vv.y & 0xFFFF0000u)};
     }
+  } else {
+    m2 = -1e30f;
+    lsum = 0.f;
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) accO[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 
   stash(0, S0);
   // The query fragments come straight from a global load.  Without this the compiler's
   // wait-count analysis cannot prove at the loop head that the load has landed and makes
-  // every iteration wait for that iteration's K/V prefetch before its first MFMA.  An
-  // empty asm that reads and redefines the registers makes it wait here, once.
-#pragma unroll
-  for (int c = 0; c < QB; ++c) asm volatile("" : "+v"(qf[c][0]), "+v"(qf[c][1]));
+  // every iteration wait for that iteration's K/V prefetch before its first MFMA.  An empty
+  // asm that reads and redefines the registers makes it wait here, once.
+  asm volatile("" : "+v"(qf[0]), "+v"(qf[1]));
   __syncthreads();
-  if constexpr (TBK) {
-    bucket_table_build(sLUT, sTB, a.tb_p2, threadIdx.x, NT);
-    __syncthreads();
-  }
-  // a history query's own bias term w_i (its key lies in the first tile's bias chunk);
-  // the row term of the bias, added back into the log-sum-exp at the end
-  // (With the fully visible mask the query's slot may lie in an earlier chunk: its term is
-  // computed from the definition.)  With the bucketed time term: the query's time tq.
-  float w_i[QB];
-  int32_t tq[QB];
-#pragma unroll
-  for (int c = 0; c < QB; ++c) {
-    tq[c] = 0;
-    if constexpr (FULL || TBK) {
-      const int sl = min(q_slot[c], N - 1);
-      if (!is_cand && N > 0) tq[c] = static_cast<int32_t>(a.ts[off + sl] - ts_ref);
-    }
-    if constexpr (FULL) {
-      w_i[c] = (!is_cand && q_valid[c]) ? (TBK ? sp2 * static_cast<float>(q_slot[c] - p_ref)
-                                               : sp2 * static_cast<float>(q_slot[c] - p_ref) +
-                                                     st2 * static_cast<float>(tq[c]))
-                                        : 0.f;
-    } else {
-      w_i[c] = (!RAB && !is_cand && q_valid[c]) ? sW[q_slot[c] - wbase] : 0.f;
-    }
-  }
 
-  // One key tile, newest first: the recency bias puts each row's maximum in the first
-  // tiles, so the rescaling of O is rarely needed later.  Tiles that reach past some
-  // query's limit (the causal diagonal, the ragged end of the history) take the masked
-  // instantiation; the steady-state loop carries no mask code.
-  // Waves whose 16 queries all lie past the tile's end only stage and synchronise.  They
-  // run their own copy of the loop (same barriers in the same order), so no accumulator
-  // of the working waves crosses a branch inside the loop.
+  // One key tile, newest first.  Tiles that reach past some query's limit (the causal
+  // diagonal, the ragged end of the history) take the masked instantiation.  Waves whose
+  // 16 queries all lie past the tile's end only stage and synchronise, in their own copy
+  // of the loop (same barriers in the same order).
   const bool wave_on = wave * QW < nq;
-  auto tile = [&](auto active_tag, auto masked_tag, int it, Stage& ld, const Stage& nxt,
-                  const RabRegs& rc, RabRegs& rn) {
+  auto tile = [&](auto active_tag, auto masked_tag, int it, Stage& ld, const Stage& nxt, const RabRegs& rc,
+                  RabRegs& rn) {
     constexpr bool ACTIVE = decltype(active_tag)::value;
     constexpr bool MASKED = decltype(masked_tag)::value;
     const int kt = kt_first - it;
     const int buf = it & 1;
     const int base = kt * AK;
-    if constexpr (!RAB) {
-      if (base < wbase) {  // histories longer than WCHUNK keys: previous bias chunk
-        __syncthreads();
-        wbase -= WCHUNK;
-        load_w(wbase);
-        __syncthreads();
-      }
-    }
     fetch(kt - 2, ld);
     rab_load(kt - 1, rn);
     if constexpr (ACTIVE) {
-
-    // S^T = K Q^T for both column blocks (each K fragment feeds two MFMAs).  In masked
-    // tiles a key block entirely above a column block's last query is skipped.
-    f32x4_t s[QB][4];
+      f32x4_t s[4];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      bool need[QB], any = false;
+      for (int kb = 0; kb < 4; ++kb) {
+        s[kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        if (!MASKED || base + kb * 16 <= kmax_blk) {
 #pragma unroll
-      for (int c = 0; c < QB; ++c) {
-        need[c] = !MASKED || base + kb * 16 <= kmax_blk[c];
-        any = any || need[c];
-        s[c][kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      }
-      if (any) {
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const bf16x8_t kf = as_bf16x8(*reinterpret_cast<const uint4*>(
-              &sK[buf][(kb * 16 + l16) * KLD + ks * 32 + g4 * 8]));
-#pragma unroll
-          for (int c = 0; c < QB; ++c)
-            if (need[c]) s[c][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[c][ks], s[c][kb], 0, 0, 0);
-        }
-      }
-    }
-    // scale + separable bias (log2 units), mask, row max
-    float mx[QB];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      float4 w;
-      if constexpr (RAB) {  // the learned bias, natural-log units -> log2 units
-        const uint2 r = rc.v[kb];
-        w = make_float4(__uint_as_float(r.x << 16) * LOG2E, __uint_as_float(r.x & 0xFFFF0000u) * LOG2E,
-                        __uint_as_float(r.y << 16) * LOG2E, __uint_as_float(r.y & 0xFFFF0000u) * LOG2E);
-      } else {
-        w = reinterpret_cast<const float4*>(sW)[((base - wbase) >> 2) + kb * 4 + g4];
-      }
-      if constexpr (!FULL && !TBK) {
-#pragma unroll
-        for (int c = 0; c < QB; ++c) {
-          s[c][kb][0] = s[c][kb][0] * a.scale2 + w.x;
-          s[c][kb][1] = s[c][kb][1] * a.scale2 + w.y;
-          s[c][kb][2] = s[c][kb][2] * a.scale2 + w.z;
-          s[c][kb][3] = s[c][kb][3] * a.scale2 + w.w;
-        }
-      } else {
-        // fully visible: -|w_j - w_i| (positions and times are sorted, so both terms of
-        // a pair have the same sign); bucketed time: - s' bucket(|t_i - t_j|)
-        const float wv[4] = {w.x, w.y, w.z, w.w};
-        int4 t4 = make_int4(0, 0, 0, 0);
-        if constexpr (TBK) t4 = reinterpret_cast<const int4*>(sT)[((base - wbase) >> 2) + kb * 4 + g4];
-        const int32_t tkv[4] = {t4.x, t4.y, t4.z, t4.w};
-#pragma unroll
-        for (int c = 0; c < QB; ++c)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float x = s[c][kb][i] * a.scale2 + (FULL ? -fabsf(wv[i] - w_i[c]) : wv[i]);
-            if constexpr (TBK)
-              x -= st2 * static_cast<float>(bucket_lookup(sLUT, sTB, a.tb_p2, abs(tq[c] - tkv[i])));
-            s[c][kb][i] = x;
+          for (int ks = 0; ks < 2; ++ks) {
+            const bf16x8_t kf = as_bf16x8(*reinterpret_cast<const uint4*>(
+                &sK[buf][(kb * 16 + l16) * KLD + ks * 32 + g4 * 8]));
+            s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], s[kb], 0, 0, 0);
           }
+        }
       }
-    }
+      // scale + the learned bias (natural-log units -> log2 units), mask, row max
 #pragma unroll
-    for (int c = 0; c < QB; ++c) {
+      for (int kb = 0; kb < 4; ++kb) {
+        const uint2 r = rc.v[kb];
+        s[kb][0] = s[kb][0] * a.scale2 + __uint_as_float(r.x << 16) * LOG2E;
+        s[kb][1] = s[kb][1] * a.scale2 + __uint_as_float(r.x & 0xFFFF0000u) * LOG2E;
+        s[kb][2] = s[kb][2] * a.scale2 + __uint_as_float(r.y << 16) * LOG2E;
+        s[kb][3] = s[kb][3] * a.scale2 + __uint_as_float(r.y & 0xFFFF0000u) * LOG2E;
+      }
       if constexpr (MASKED) {
-        const int lim = k_lim[c] - base - g4 * 4;  // local key kb*16 + i must be <= lim
+        const int lim = k_lim - base - g4 * 4;  // local key kb*16 + i must be <= lim
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            if (kb * 16 + i > lim) s[c][kb][i] = -INFINITY;
+            if (kb * 16 + i > lim) s[kb][i] = -INFINITY;
       }
-      float m = fmaxf(fmaxf(fmaxf(s[c][0][0], s[c][0][1]), s[c][0][2]), fmaxf(fmaxf(s[c][0][3], s[c][1][0]), s[c][1][1]));
-      m = fmaxf(fmaxf(m, s[c][1][2]), fmaxf(fmaxf(s[c][1][3], s[c][2][0]), s[c][2][1]));
-      m = fmaxf(fmaxf(m, s[c][2][2]), fmaxf(fmaxf(s[c][2][3], s[c][3][0]), s[c][3][1]));
-      m = fmaxf(fmaxf(m, s[c][3][2]), s[c][3][3]);
-      mx[c] = xor32_max(xor16_max(m));
-    }
-    // online softmax: raise the running maximum and rescale O and l by 2^(m_old - m_new)
+      float m = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), s[0][2]), fmaxf(fmaxf(s[0][3], s[1][0]), s[1][1]));
+      m = fmaxf(fmaxf(m, s[1][2]), fmaxf(fmaxf(s[1][3], s[2][0]), s[2][1]));
+      m = fmaxf(fmaxf(m, s[2][2]), fmaxf(fmaxf(s[2][3], s[3][0]), s[3][1]));
+      m = fmaxf(fmaxf(m, s[3][2]), s[3][3]);
+      const float mx = xor32_max(xor16_max(m));
+      // online softmax: raise the running maximum and rescale O and l by 2^(m_old - m_new)
+      const float m_new = fmaxf(m2, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m2 - m_new);
+      m2 = m_new;
+      lsum *= alpha;
 #pragma unroll
-    for (int c = 0; c < QB; ++c) {
-      const float m_new = fmaxf(m2[c], mx[c]);
-      const float alpha = __builtin_amdgcn_exp2f(m2[c] - m_new);
-      m2[c] = m_new;
-      lsum[c] *= alpha;
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) accO[c][nb] = accO[c][nb] * alpha;
-    }
-    bf16x8_t pf[QB][2];
-#pragma unroll
-    for (int c = 0; c < QB; ++c) {
+      for (int nb = 0; nb < 4; ++nb) accO[nb] = accO[nb] * alpha;
       float psum = 0.f;
+      bf16x8_t pf[2];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float p = __builtin_amdgcn_exp2f(s[c][kb][i] - m2[c]);
-          s[c][kb][i] = p;
+          const float p = __builtin_amdgcn_exp2f(s[kb][i] - m2);
+          s[kb][i] = p;
           psum += p;
         }
-      lsum[c] += psum;
+      lsum += psum;
       // P^T as the column operand: keys {4g..4g+3} of blocks 2ks and 2ks+1
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         uint4 pk;
-        pk.x = pack_bf16x2(s[c][2 * ks][0], s[c][2 * ks][1]);
-        pk.y = pack_bf16x2(s[c][2 * ks][2], s[c][2 * ks][3]);
-        pk.z = pack_bf16x2(s[c][2 * ks + 1][0], s[c][2 * ks + 1][1]);
-        pk.w = pack_bf16x2(s[c][2 * ks + 1][2], s[c][2 * ks + 1][3]);
-        pf[c][ks] = as_bf16x8(pk);
+        pk.x = pack_bf16x2(s[2 * ks][0], s[2 * ks][1]);
+        pk.y = pack_bf16x2(s[2 * ks][2], s[2 * ks][3]);
+        pk.z = pack_bf16x2(s[2 * ks + 1][0], s[2 * ks + 1][1]);
+        pk.w = pack_bf16x2(s[2 * ks + 1][2], s[2 * ks + 1][3]);
+        pf[ks] = as_bf16x8(pk);
       }
-    }
-    // O^T += V^T P^T (each V fragment feeds both column blocks)
+      // O^T += V^T P^T
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      bool need[QB], any = false;
+      for (int ks = 0; ks < 2; ++ks) {
+        if (MASKED && base + ks * 32 > kmax_blk) continue;
 #pragma unroll
-      for (int c = 0; c < QB; ++c) {
-        need[c] = !MASKED || base + ks * 32 <= kmax_blk[c];
-        any = any || need[c];
+        for (int nb = 0; nb < 4; ++nb) {
+          const bf16x8_t vf = as_bf16x8(*reinterpret_cast<const uint4*>(
+              &sVt[buf][(nb * 16 + l16) * VLD + ks * 32 + g4 * 8]));
+          accO[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[ks], accO[nb], 0, 0, 0);
+        }
       }
-      if (!any) continue;
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        const bf16x8_t vf = as_bf16x8(*reinterpret_cast<const uint4*>(
-            &sVt[buf][(nb * 16 + l16) * VLD + ks * 32 + g4 * 8]));
-#pragma unroll
-        for (int c = 0; c < QB; ++c)
-          if (need[c]) accO[c][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[c][ks], accO[c][nb], 0, 0, 0);
-      }
-    }
-
     }  // ACTIVE
-
     if (kt > 0) stash(buf ^ 1, nxt);
     __syncthreads();
   };
 
   // a tile needs the mask when its last key lies past some query's limit
-  const int klim_min = (is_cand || FULL) ? (N - 1) : q0;
+  const int klim_min = is_cand ? (N - 1) : q0;
   auto loop = [&](auto active_tag) {
     auto step = [&](int it, Stage& ld, const Stage& nxt, const RabRegs& rc, RabRegs& rn) {
       if ((kt_first - it) * AK + AK - 1 > klim_min)
@@ -599,26 +407,25 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
     loop(std::false_type{});
 
   // ---- epilogue
+  const float ltot = xor32_sum(xor16_sum(lsum));
+  if (!q_valid) return;
+  const float inv = 1.f / ltot;
 #pragma unroll
-  for (int c = 0; c < QB; ++c) {
-    const float ltot = xor32_sum(xor16_sum(lsum[c]));
-    if (!q_valid[c]) continue;
-    const float inv = 1.f / ltot;
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      uint2 o;
-      o.x = pack_bf16x2(accO[c][nb][0] * inv, accO[c][nb][1] * inv);
-      o.y = pack_bf16x2(accO[c][nb][2] * inv, accO[c][nb][3] * inv);
-      *reinterpret_cast<uint2*>(a.o + qrow[c] * a.ld_o + h * DH + nb * 16 + g4 * 4) = o;
-    }
-    if (a.lse && g4 == 0) a.lse[qrow[c] * a.H + h] = LN2 * (m2[c] + log2f(ltot) - (FULL ? 0.f : w_i[c]));
+  for (int nb = 0; nb < 4; ++nb) {
+    uint2 o;
+    o.x = pack_bf16x2(accO[nb][0] * inv, accO[nb][1] * inv);
+    o.y = pack_bf16x2(accO[nb][2] * inv, accO[nb][3] * inv);
+    *reinterpret_cast<uint2*>(a.o + qrow * a.ld_o + h * DH + nb * 16 + g4 * 4) = o;
   }
+  if (a.lse && g4 == 0) a.lse[qrow * a.H + h] = LN2 * (m2 + log2f(ltot));
 }
 
 // ------------------------------------------------------------------ bf16 ring kernel
-// The ALiBi kernel (and its variants).  Same workgroup shape, schedule and math as
-// attn_fwd_bf16_kernel above; what differs is how K and V reach LDS and how much vector
-// work a tile costs:
+// ALiBi (and its variants) over the tile grid of attn_fwd_rab_kernel above: one workgroup
+// = 8 waves x 16 query rows of one (user, head), a history tile (keys up to the diagonal)
+// or a candidate tile (every history key, then the candidate's own key); same XCD order.
+// What differs from that kernel is how K and V reach LDS and how much vector work a tile
+// costs:
 //  - K and V tiles go from global memory straight into LDS (one 16-byte direct load per
 //    lane and tile for each), through a ring of NS stage buffers with NS - 1 tiles in
 //    flight.  No registers hold staged data and each workgroup waits for memory about
@@ -700,7 +507,7 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
   __shared__ int32_t sTB[TBK ? ATTN_MAX_TIME_BOUNDS : 1];
   __shared__ uint32_t sLUT[TBK ? BK_CELLS : 1];
 
-  // flat grid over (user, head, tile), walked per XCD as in attn_fwd_bf16_kernel
+  // flat grid over (user, head, tile), walked per XCD as in attn_fwd_rab_kernel
   const int TY = a.cand_tiles + a.hist_tiles;
   const int x8 = blockIdx.x & 7;
   const int kx = blockIdx.x >> 3;
@@ -805,7 +612,7 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
   // order them, so its first wait for a register load waits for everything.  This empty
   // asm (which reads and redefines registers the loads above wrote) makes that one wait
   // come after the whole ring has been issued; the query fragments are covered too (see
-  // attn_fwd_bf16_kernel).
+  // attn_fwd_rab_kernel).
   asm volatile("" : "+v"(ts_key), "+v"(tq_raw), "+v"(qf[0]), "+v"(qf[1]), "+v"(kself[0]), "+v"(kself[1]),
                "+v"(vself[0]), "+v"(vself[1]), "+v"(vself[2]), "+v"(vself[3])::"memory");
   const int32_t tq = (FULL || TBK) && !is_cand && N > 0 ? static_cast<int32_t>(tq_raw - ts_ref) : 0;
@@ -1471,7 +1278,7 @@ genrank_status launch_hstu_attn_fwd(const genrank_batch* b, const int32_t* offse
   const int64_t pairs = (static_cast<int64_t>(b->B) * b->H + 8 * GROUP - 1) / (8 * GROUP) * (8 * GROUP);
   const int64_t G = pairs * (a.hist_tiles + a.cand_tiles);
   if (G > INT32_MAX) return GENRANK_E_SHAPE;
-  hipLaunchKernelGGL(attn_fwd_bf16_kernel<true>, dim3(static_cast<unsigned>(G)), dim3(NT), 0, stream, a);
+  hipLaunchKernelGGL(attn_fwd_rab_kernel, dim3(static_cast<unsigned>(G)), dim3(NT), 0, stream, a);
   GR_CHECK_LAUNCH();
   return GENRANK_OK;
 }
