@@ -195,3 +195,36 @@ def test_attn_bf16_long_histories():
     assert np.isfinite(got).all()
     assert np.abs(got - want).max() <= 2e-2
     assert np.abs(glse - wlse).max() <= 2e-2
+
+
+@pytest.mark.parametrize("lengths,m", [
+    ([576, 575, 64, 1, 0], 9),    # the longest history the LDS-resident kernel takes (9 key tiles)
+    ([577, 5, 576], 9),           # one key more: the batch goes to the streaming kernel
+])
+def test_attn_bf16_resident_limit(lengths, m):
+    """Both sides of the history length up to which a user's whole K/V sits in LDS."""
+    say(f"attn: bf16 resident limit lengths={lengths} m={m}")
+    cfg = synth.make_config("infer_1layer_bf16", m=m)
+    batch = custom_batch(cfg, lengths, seed=31)
+    st, q64 = random_qkv(batch.total_rows, cfg.d, "bf16", seed=32)
+    got, glse = _run_gpu(cfg, batch, st)
+    want, wlse, _ = _run_oracle(cfg, batch, q64)
+    assert np.isfinite(got).all()
+    assert np.abs(got - want).max() <= 2e-2
+    assert np.abs(glse - wlse).max() <= 2e-2
+
+
+def test_attn_bf16_more_users_than_threads():
+    """1,100 users (more than the 1,024 threads that order the users heaviest first, so the
+    launch takes them in plain order), short jagged histories; sampled users checked."""
+    say("attn: bf16 1100 users")
+    cfg = synth.make_config("infer_1layer_bf16", m=3)
+    lengths = [(7 * u) % 41 for u in range(1100)]
+    batch = custom_batch(cfg, lengths, seed=33)
+    st, q64 = random_qkv(batch.total_rows, cfg.d, "bf16", seed=34)
+    got, glse = _run_gpu(cfg, batch, st)
+    users = [0, 1, 40, 517, 1023, 1024, 1099]
+    want, wlse, rows = _run_oracle(cfg, batch, q64, users=users)
+    assert np.isfinite(got).all()
+    assert np.abs(got[rows] - want[rows]).max() <= 2e-2
+    assert np.abs(glse[rows] - wlse[rows]).max() <= 2e-2
