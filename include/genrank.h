@@ -223,7 +223,12 @@ GENRANK_API genrank_status genrank_embed_sum(const genrank_batch* batch, const g
  * req_ts; the bias is computed in registers and no T x T array is formed.
  * q, k, v: [T, ld_qkv] rows, head h at columns [h*dh, (h+1)*dh) of each (they may be
  * three views into one [T, 3d] buffer).  o: [T, ld_o], head h at h*dh.
- * lse: [T, H] f32 or NULL.  bf16 requires dh == 64; f32 requires dh <= 64. */
+ * lse: [T, H] f32 or NULL.  bf16 requires dh == 64; f32 requires dh <= 64.
+ * bf16 kernels: when batch.max_hist <= 576, one workgroup per (user, head) holds that
+ * user's whole K/V history in LDS (users taken longest history first); otherwise a tiled
+ * kernel streams K/V per 128-query tile.  batch.max_hist selects between them and must
+ * not be below any user's history length (a longer history would be cut to 576 keys:
+ * wrong results for that user, no out-of-bounds access). */
 GENRANK_API genrank_status genrank_attn_fwd(const genrank_batch* batch, const int32_t* hist_offsets,
                                 const int64_t* hist_ts, const int64_t* req_ts,
                                 genrank_alibi alibi, const void* q, const void* k,
