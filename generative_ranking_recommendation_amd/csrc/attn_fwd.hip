@@ -587,7 +587,9 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
 
   // ---- the K/V ring.  Wave w loads rows 8 w .. 8 w + 7 of each tile: lane l takes row
   // 8 w + l / 8 and fills LDS chunk l % 8 of it, which holds the row's global chunk
-  // (l % 8) ^ (row & 7) for K and (l % 8) ^ 2 (row & 3) for V.  Rows past the history end
+  // (l % 8) ^ ((row >> 1) & 7) for K and (l % 8) ^ 2 ((row >> 1) & 3) for V (LDS has
+  // 64 banks: the 16 rows of a K fragment read, and the 8 rows that two 16-lane groups of
+  // a transposing V read cover, then fall on distinct banks).  Rows past the history end
   // re-read its last row (finite values; the mask gives those keys probability 0).
   // The prologue always issues NS - 1 tiles, so the compiler's waits for the register
   // loads above see one fixed count of loads behind them and leave the ring in flight;
@@ -596,8 +598,8 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
   const int lr = wave * 8 + (lane >> 3);
   const int lc = lane & 7;
   const uint32_t row_bytes = static_cast<uint32_t>(a.ld_h) * 2u;
-  const char* gk = reinterpret_cast<const char*>(N > 0 ? a.kh + off * a.ld_h + h * DH + ((lc ^ (lr & 7)) * 8) : a.q + rowoff);
-  const char* gv = reinterpret_cast<const char*>(N > 0 ? a.vh + off * a.ld_h + h * DH + ((lc ^ (2 * (lr & 3))) * 8) : a.q + rowoff);
+  const char* gk = reinterpret_cast<const char*>(N > 0 ? a.kh + off * a.ld_h + h * DH + ((lc ^ ((lr >> 1) & 7)) * 8) : a.q + rowoff);
+  const char* gv = reinterpret_cast<const char*>(N > 0 ? a.vh + off * a.ld_h + h * DH + ((lc ^ (2 * ((lr >> 1) & 3))) * 8) : a.q + rowoff);
   auto issue = [&](int it, bf16_t* stg) {
     const int r = max(min((kt_first - it) * AK + lr, N - 1), 0);
     const uint32_t ro = static_cast<uint32_t>(r) * row_bytes;
@@ -663,12 +665,13 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
   const float w_i_u = w_i / SC;  // the same in score units (FULL only)
 
   // LDS offsets (bf16 elements) of this lane's fragments inside a stage buffer
-  const int k_off0 = l16 * DH + (((0 + g4) ^ (l16 & 7)) * 8);
-  const int k_off1 = l16 * DH + (((4 + g4) ^ (l16 & 7)) * 8);
+  const int k_off0 = l16 * DH + (((0 + g4) ^ ((l16 >> 1) & 7)) * 8);
+  const int k_off1 = l16 * DH + (((4 + g4) ^ ((l16 >> 1) & 7)) * 8);
   int v_off[4];
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb)
-    v_off[nb] = AK * DH + (4 * g4 + (l16 >> 2)) * DH + (((2 * nb + ((l16 & 3) >> 1)) ^ (2 * (l16 >> 2))) * 8) + (l16 & 1) * 4;
+    v_off[nb] = AK * DH + (4 * g4 + (l16 >> 2)) * DH +
+                (((2 * nb + ((l16 & 3) >> 1)) ^ (2 * (((4 * g4 + (l16 >> 2)) >> 1) & 3))) * 8) + (l16 & 1) * 4;
   const float th = RESCALE_LOG2 / SC;
   const bool wave_on = wave * QW < nq;
 
@@ -905,7 +908,8 @@ __global__ void __launch_bounds__(PAIR_NT) attn_fwd_pair_kernel(AttnArgs a) {
 
   // ---- the pair's K/V tiles: waves 0-7 load K, waves 8-15 V, rows 8 (w % 8) .. + 7 of
   // every tile (lane l: row 8 (w % 8) + l / 8, LDS chunk l % 8 <- global chunk
-  // (l % 8) ^ (row & 7) for K, (l % 8) ^ 2 (row & 3) for V; rows past the history end
+  // (l % 8) ^ ((row >> 1) & 7) for K, (l % 8) ^ 2 ((row >> 1) & 3) for V, as in the ring
+  // kernel; rows past the history end
   // re-read its last row).
   {
     const bool ldk = wave < 8;
@@ -913,7 +917,7 @@ __global__ void __launch_bounds__(PAIR_NT) attn_fwd_pair_kernel(AttnArgs a) {
     const int lc = lane & 7;
     const uint32_t row_bytes = static_cast<uint32_t>(a.ld_h) * 2u;
     const char* g = reinterpret_cast<const char*>((ldk ? a.kh : a.vh) + off * a.ld_h + h * DH +
-                                                  ((lc ^ (ldk ? (lr & 7) : 2 * (lr & 3))) * 8));
+                                                  ((lc ^ (ldk ? ((lr >> 1) & 7) : 2 * ((lr >> 1) & 3))) * 8));
     bf16_t* dst = sKV + (ldk ? 0 : AK * DH) + (wave & 7) * 8 * DH;
     for (int t = 0; t < n_tiles; ++t) {
       const uint32_t ro = static_cast<uint32_t>(min(t * AK + lr, N - 1)) * row_bytes;
@@ -948,12 +952,13 @@ __global__ void __launch_bounds__(PAIR_NT) attn_fwd_pair_kernel(AttnArgs a) {
 
   const float th = RESCALE_LOG2 / SC;
   // LDS offsets (bf16 elements) of this lane's fragments inside a tile
-  const int k_off0 = l16 * DH + (((0 + g4) ^ (l16 & 7)) * 8);
-  const int k_off1 = l16 * DH + (((4 + g4) ^ (l16 & 7)) * 8);
+  const int k_off0 = l16 * DH + (((0 + g4) ^ ((l16 >> 1) & 7)) * 8);
+  const int k_off1 = l16 * DH + (((4 + g4) ^ ((l16 >> 1) & 7)) * 8);
   int v_off[4];
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb)
-    v_off[nb] = AK * DH + (4 * g4 + (l16 >> 2)) * DH + (((2 * nb + ((l16 & 3) >> 1)) ^ (2 * (l16 >> 2))) * 8) + (l16 & 1) * 4;
+    v_off[nb] = AK * DH + (4 * g4 + (l16 >> 2)) * DH +
+                (((2 * nb + ((l16 & 3) >> 1)) ^ (2 * (((4 * g4 + (l16 >> 2)) >> 1) & 3))) * 8) + (l16 & 1) * 4;
 
   // ---- units: 16-query blocks, candidates first (each sees every key), then history
   // blocks newest first; wave w takes units w, w + 16, ...
