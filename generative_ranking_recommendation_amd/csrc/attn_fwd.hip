@@ -801,7 +801,8 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
   // ---- epilogue
   const float ltot = xor32_sum(xor16_sum(lsum));
   if (!q_valid) return;
-  const float inv = 1.f / ltot;
+  // (a row's sum is at least 1: the hardware reciprocal and log2 need no range fix-up)
+  const float inv = __builtin_amdgcn_rcpf(ltot);
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) {
     uint2 o;
@@ -809,7 +810,8 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
     o.y = pack_bf16x2(accO[nb][2] * inv, accO[nb][3] * inv);
     *reinterpret_cast<uint2*>(a.o + qrow * a.ld_o + h * DH + nb * 16 + g4 * 4) = o;
   }
-  if (a.lse && g4 == 0) a.lse[qrow * a.H + h] = LN2 * (m_run * SC + log2f(ltot) - (FULL ? 0.f : w_i));
+  if (a.lse && g4 == 0)
+    a.lse[qrow * a.H + h] = LN2 * (m_run * SC + __builtin_amdgcn_logf(ltot) - (FULL ? 0.f : w_i));
 }
 
 // ------------------------------------------------------------------ bf16 pair kernel
@@ -925,9 +927,10 @@ __global__ void __launch_bounds__(PAIR_NT) attn_fwd_pair_kernel(AttnArgs a) {
     }
   }
 
-  // ---- every key's bias term relative to the candidates (0 past the history end)
+  // ---- every key's bias term relative to the candidates; -inf past the history end, so
+  // that those keys' scores come out -inf (probability 0) without a mask
   if (tid < n_tiles * AK) {
-    float w = 0.f;
+    float w = -INFINITY;
     int32_t tk = 0;
     if (tid < N) {
       tk = static_cast<int32_t>(a.ts[off + tid] - ts_ref);
@@ -1107,11 +1110,17 @@ __global__ void __launch_bounds__(PAIR_NT) attn_fwd_pair_kernel(AttnArgs a) {
         }
       }
     };
-    // key tiles newest first; only the first can cross a query's limit
+    // Key tiles newest first; only the first can cross a query's limit.  A candidate's
+    // limit is the history end, which the -inf bias terms already enforce.
     if (n_t > 0) {
       f32x4_t sc[4];
-      scores(std::true_type{}, n_t - 1, sc);
-      tile(std::true_type{}, n_t - 1, sc);
+      if (is_cand) {
+        scores(std::false_type{}, n_t - 1, sc);
+        tile(std::false_type{}, n_t - 1, sc);
+      } else {
+        scores(std::true_type{}, n_t - 1, sc);
+        tile(std::true_type{}, n_t - 1, sc);
+      }
       for (int kt = n_t - 2; kt >= 0; --kt) {
         scores(std::false_type{}, kt, sc);
         tile(std::false_type{}, kt, sc);
@@ -1122,7 +1131,7 @@ __global__ void __launch_bounds__(PAIR_NT) attn_fwd_pair_kernel(AttnArgs a) {
     if (is_cand) merge_self(kself, vself, qf, SEP, a.scale2, tbk_self, SC, g4, m_run, lsum, accO);
     const float ltot = xor32_sum(xor16_sum(lsum));
     if (q_valid) {
-      const float inv = 1.f / ltot;
+      const float inv = __builtin_amdgcn_rcpf(ltot);  // (as in the ring kernel)
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) {
         uint2 o;
@@ -1130,7 +1139,8 @@ __global__ void __launch_bounds__(PAIR_NT) attn_fwd_pair_kernel(AttnArgs a) {
         o.y = pack_bf16x2(accO[nb][2] * inv, accO[nb][3] * inv);
         *reinterpret_cast<uint2*>(a.o + qrow * a.ld_o + h * DH + nb * 16 + g4 * 4) = o;
       }
-      if (a.lse && g4 == 0) a.lse[qrow * a.H + h] = LN2 * (m_run * SC + log2f(ltot) - (FULL ? 0.f : w_i));
+      if (a.lse && g4 == 0)
+        a.lse[qrow * a.H + h] = LN2 * (m_run * SC + __builtin_amdgcn_logf(ltot) - (FULL ? 0.f : w_i));
     }
   }
 }
