@@ -40,7 +40,7 @@ constexpr int NW = 8;           // waves per workgroup
 constexpr int NT = 64 * NW;     // threads per workgroup
 constexpr int AQ = NW * QW;     // queries per workgroup
 constexpr int AK = 64;          // keys per tile
-constexpr int DH = 64;          // head dim of the bf16 kernel
+constexpr int DH = 64;          // head dim of the bf16 kernels
 constexpr int KLD = DH + 8;     // sK row pitch (bf16)
 constexpr int VLD = AK + 8;     // sVt row pitch (bf16)
 constexpr int WCHUNK = 512;     // keys whose bias terms sit in LDS at a time
@@ -78,7 +78,7 @@ struct AttnArgs {
   int n_tb, tb_p2;
 };
 
-// variant bits of the bf16 kernel: the fully visible history mask, the bucketed time term
+// variant bits of the ALiBi kernels: the fully visible history mask, the bucketed time term
 constexpr int VAR_FULL = 1, VAR_TBUCKET = 2;
 
 // slot of key j (0..63 in a tile) in the permuted key axis of sVt
@@ -820,9 +820,10 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
 // 64-key tiles with the ring kernel's swizzles and transposing V reads), together with
 // every key's bias term.  The 16 waves then work through the pair's 16-query units
 // (candidate blocks first, then history blocks newest first) with no further barrier:
-// each wave runs its units' key tiles from LDS on its own.  Against the tile kernels this
+// each wave runs its units' key tiles from LDS on its own.  Against the tile grid this
 // loads every K/V byte of a pair once instead of once per query tile, and pays one
-// workgroup prologue per pair instead of one per query tile.
+// workgroup prologue per pair instead of one per query tile.  Workgroups take the users
+// heaviest first (see below), so the light pairs fill the end of the launch.
 // The bias reference point of the whole pair is the candidates' shared (p, tau) = (N,
 // request time), so candidate rows carry no row term.  A candidate's own key is merged
 // into its softmax state after the history keys (same result as seeding with it).
