@@ -17,11 +17,12 @@ import numpy as np
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgenrank.so")
 
 F32, BF16 = 0, 1
+RESID_ACT, RESID_F32 = 0, 1
 BLOCK_ATTN_ONLY, BLOCK_PRENORM = 0, 1
 (OP_EMBED_SUM, OP_ATTN_FWD, OP_ATTN_BWD, OP_LAYER_FWD, OP_LAYER_BWD, OP_EMBED_BWD, OP_HEAD_BWD, OP_LAYER_KV,
  OP_LAYER_FWD_CACHED) = range(9)
 FWD_SAVE = 1
-EPI_NONE, EPI_RESIDUAL, EPI_SILU = 0, 1, 2
+EPI_NONE, EPI_RESIDUAL, EPI_SILU, EPI_RESIDUAL_F32 = 0, 1, 2, 3
 STATUS = {0: "OK", -1: "E_ARG", -2: "E_SHAPE", -3: "E_DTYPE", -4: "E_UNSORTED",
           -5: "E_RANGE", -6: "E_WORKSPACE", -7: "E_HIP"}
 
@@ -35,7 +36,7 @@ class GenrankError(RuntimeError):
 class Batch(Structure):
     _fields_ = [("B", c_int32), ("m", c_int32), ("d", c_int32), ("H", c_int32), ("dh", c_int32),
                 ("max_hist", c_int32), ("total_hist", c_int64), ("dtype", c_int32),
-                ("reserved", c_int32)]
+                ("resid", c_int32)]
 
 
 class Inputs(Structure):
@@ -110,7 +111,7 @@ _SIGS = {
                                    c_void_p]),
     "genrank_head_fwd_rows": (c_int32, [c_int32, c_int32, c_void_p, c_int64, c_void_p, c_void_p, c_void_p,
                                         c_void_p, c_int32, c_void_p, c_void_p]),
-    "genrank_head_bwd_rows": (c_int32, [c_int32, c_int32, c_int64, c_void_p, c_int64, c_void_p, c_void_p,
+    "genrank_head_bwd_rows": (c_int32, [c_int32, c_int32, c_int32, c_int64, c_void_p, c_int64, c_void_p, c_void_p,
                                         c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                         c_void_p, c_size_t, c_void_p]),
     "genrank_bce_loss": (c_int32, [c_int64, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
@@ -175,9 +176,9 @@ def _check(name, status):
         raise GenrankError(name, status)
 
 
-def make_batch(B, m, d, H, max_hist, total_hist, dtype) -> Batch:
+def make_batch(B, m, d, H, max_hist, total_hist, dtype, resid=RESID_ACT) -> Batch:
     return Batch(B=B, m=m, d=d, H=H, dh=d // H, max_hist=max_hist, total_hist=total_hist,
-                 dtype=dtype, reserved=0)
+                 dtype=dtype, resid=resid)
 
 
 def make_inputs(hist_offsets, hist_items, hist_actions, hist_ts, cand_items, req_ts) -> Inputs:
@@ -353,10 +354,10 @@ def genrank_head_fwd_rows(dtype, d, x, n_rows, rows, g_final, w_head, b_head, n_
         _stream(stream)))
 
 
-def genrank_head_bwd_rows(dtype, d, n_x_rows, x, n_rows, rows, g_final, w_head, n_tasks, dlogits, dx,
+def genrank_head_bwd_rows(x_dtype, dtype, d, n_x_rows, x, n_rows, rows, g_final, w_head, n_tasks, dlogits, dx,
                           dg_final, dw_head, db_head, ws, ws_bytes, stream=None):
     _check("genrank_head_bwd_rows", lib().genrank_head_bwd_rows(
-        dtype, d, n_x_rows, _p(x), n_rows, _p(rows), _p(g_final), _p(w_head), n_tasks, _p(dlogits), _p(dx),
+        x_dtype, dtype, d, n_x_rows, _p(x), n_rows, _p(rows), _p(g_final), _p(w_head), n_tasks, _p(dlogits), _p(dx),
         _p(dg_final), _p(dw_head), _p(db_head), _p(ws), ws_bytes, _stream(stream)))
 
 

@@ -19,6 +19,7 @@ genrank_status check_batch(const genrank_batch* b) {
   if (b->H > GENRANK_MAX_HEADS) return GENRANK_E_SHAPE;
   if (static_cast<int64_t>(b->H) * b->dh != b->d) return GENRANK_E_SHAPE;
   if (b->dtype != GENRANK_F32 && b->dtype != GENRANK_BF16) return GENRANK_E_DTYPE;
+  if (b->resid != GENRANK_RESID_ACT && b->resid != GENRANK_RESID_F32) return GENRANK_E_DTYPE;
   if (b->total_hist > static_cast<int64_t>(b->max_hist) * b->B) return GENRANK_E_SHAPE;
   const int64_t T = b->total_hist + static_cast<int64_t>(b->B) * b->m;
   if (T >= (int64_t(1) << 31)) return GENRANK_E_SHAPE;
@@ -26,6 +27,8 @@ genrank_status check_batch(const genrank_batch* b) {
 }
 
 size_t dtype_size(int dtype) { return dtype == GENRANK_BF16 ? 2 : 4; }
+
+int resid_dtype(const genrank_batch* b) { return b->resid == GENRANK_RESID_F32 ? GENRANK_F32 : b->dtype; }
 
 namespace {
 
@@ -43,7 +46,7 @@ struct LayerFwdWs {
   char* qkv;  // [T, 3d]
   char* o;    // [T, d]   attention output
   float* lse; // [T, H]
-  char* x1;   // [T, d]   x + attention branch   (PRENORM)
+  char* x1;   // [T, d]   x + attention branch   (PRENORM; in the residual stream's type)
   char* z2;   // [T, d]   rmsnorm(x1) g2         (PRENORM)
   char* a;    // [T, f]   FFN pre-activation     (PRENORM)
   char* hdn;  // [T, f]   silu(a)                (PRENORM)
@@ -67,7 +70,7 @@ LayerFwdWs layer_fwd_layout(const genrank_batch* b, int block, int ffn, char* ba
   w.qkv = take(T * 3 * d * es);
   w.o = take(T * d * es);
   w.lse = reinterpret_cast<float*>(take(T * b->H * sizeof(float)));
-  w.x1 = pre ? take(T * d * es) : nullptr;
+  w.x1 = pre ? take(T * d * dtype_size(resid_dtype(b))) : nullptr;
   w.z2 = pre ? take(T * d * es) : nullptr;
   w.a = pre ? take(T * static_cast<size_t>(ffn) * es) : nullptr;
   w.hdn = pre ? take(T * static_cast<size_t>(ffn) * es) : nullptr;
@@ -83,7 +86,8 @@ LayerFwdWs layer_fwd_layout(const genrank_batch* b, int block, int ffn, char* ba
 // A forward that saves activations for the backward keeps the normalised rows.
 bool rms_fused(const genrank_batch* b, const genrank_layer_weights* w) {
   const int d = b->d;
-  return w->block == GENRANK_BLOCK_PRENORM && b->dtype == GENRANK_BF16 && gemm_rms_ok(3 * d, d) &&
+  return w->block == GENRANK_BLOCK_PRENORM && b->dtype == GENRANK_BF16 && b->resid == GENRANK_RESID_ACT &&
+         gemm_rms_ok(3 * d, d) &&
          gemm_rms_ok(2 * d, d) && gemm_rms_ok(w->ffn_dim, d);
 }
 
@@ -146,6 +150,7 @@ genrank_status check_layer_weights(const genrank_batch* b, const genrank_layer_w
     return GENRANK_E_ARG;
   }
   if (b->d % 64 != 0 && b->dtype == GENRANK_BF16) return GENRANK_E_SHAPE;
+  if (resid_dtype(b) != b->dtype && w->block != GENRANK_BLOCK_PRENORM) return GENRANK_E_DTYPE;
   return check_alibi_variant(w->alibi, b->H);
 }
 
@@ -400,13 +405,16 @@ genrank_status genrank_layer_fwd(const genrank_batch* b, const genrank_layer_wei
   GR_TRY(check_attn_args(b, offsets, ts, req, w->alibi, L.qkv, L.qkv + d * es, L.qkv + 2 * d * es,
                          3 * d, L.o, d));
   const bool fuse = pre && rms_fused(b, w) && !(flags & GENRANK_FWD_SAVE);
+  const int rt = resid_dtype(b);
+  // the residual sums: bf16 (EPI_RESID) or f32 (EPI_RESID_F32) rows
+  const int epi_res = rt == dt ? GEMM_EPI_RESID : GEMM_EPI_RESID_F32;
   if (fuse) {
     GR_TRY(launch_scale_cols(w->wqkv, d, w->g1, L.wg, d, 3 * d, d, s));
     GR_TRY(launch_gemm_nt_rms(x_in, d, L.wg, d, L.qkv, 3 * d, T, 3 * d, d, GEMM_EPI_STORE, s));
   } else {
     const void* zin = x_in;
     if (pre) {
-      GR_TRY(launch_rmsnorm(dt, x_in, w->g1, L.z, T, d, s));
+      GR_TRY(launch_rmsnorm(rt, dt, x_in, w->g1, L.z, T, d, s));
       zin = L.z;
     }
     GR_TRY(launch_gemm_nt(dt, zin, d, w->wqkv, d, L.qkv, 3 * d, T, 3 * d, d, GEMM_EPI_STORE,
@@ -418,18 +426,16 @@ genrank_status genrank_layer_fwd(const genrank_batch* b, const genrank_layer_wei
     return launch_gemm_nt(dt, L.o, d, w->wo, d, y_out, d, T, d, d, GEMM_EPI_STORE, nullptr, 0,
                           nullptr, 0, s);
   }
-  GR_TRY(launch_gemm_nt(dt, L.o, d, w->wo, d, L.x1, d, T, d, d, GEMM_EPI_RESID, x_in, d, nullptr,
-                        0, s));
+  GR_TRY(launch_gemm_nt(dt, L.o, d, w->wo, d, L.x1, d, T, d, d, epi_res, x_in, d, nullptr, 0, s));
   if (fuse) {
     GR_TRY(launch_scale_cols(w->w1, d, w->g2, L.wg, d, ffn, d, s));
     GR_TRY(launch_gemm_nt_rms(L.x1, d, L.wg, d, L.hdn, ffn, T, ffn, d, GEMM_EPI_SILU, s));
   } else {
-    GR_TRY(launch_rmsnorm(dt, L.x1, w->g2, L.z2, T, d, s));
+    GR_TRY(launch_rmsnorm(rt, dt, L.x1, w->g2, L.z2, T, d, s));
     GR_TRY(launch_gemm_nt(dt, L.z2, d, w->w1, d, L.hdn, ffn, T, ffn, d, GEMM_EPI_SILU, nullptr, 0,
                           (flags & GENRANK_FWD_SAVE) ? L.a : nullptr, ffn, s));
   }
-  return launch_gemm_nt(dt, L.hdn, ffn, w->w2, ffn, y_out, d, T, d, ffn, GEMM_EPI_RESID, L.x1, d,
-                        nullptr, 0, s);
+  return launch_gemm_nt(dt, L.hdn, ffn, w->w2, ffn, y_out, d, T, d, ffn, epi_res, L.x1, d, nullptr, 0, s);
 }
 
 genrank_status genrank_embed_sum_cand(const genrank_batch* b, const genrank_inputs* in, const genrank_tables* t,
@@ -474,7 +480,7 @@ genrank_status genrank_layer_kv(const genrank_batch* b, const genrank_layer_weig
   }
   const void* z = x_hist;
   if (w->block == GENRANK_BLOCK_PRENORM) {
-    GR_TRY(launch_rmsnorm(dt, x_hist, w->g1, ws, Th, d, s));
+    GR_TRY(launch_rmsnorm(resid_dtype(b), dt, x_hist, w->g1, ws, Th, d, s));
     z = ws;
   }
   return launch_gemm_nt(dt, z, d, wkv, d, kv, ld_kv, static_cast<int>(Th), 2 * d, d, GEMM_EPI_STORE, nullptr, 0,
@@ -504,13 +510,15 @@ genrank_status genrank_layer_fwd_cached(const genrank_batch* b, const genrank_la
   if (Tc == 0) return GENRANK_OK;
   const hipStream_t s = S(stream);
   const bool fuse = pre && rms_fused(b, w);
+  const int rt = resid_dtype(b);
+  const int epi_res = rt == dt ? GEMM_EPI_RESID : GEMM_EPI_RESID_F32;
   if (fuse) {
     GR_TRY(launch_scale_cols(w->wqkv, d, w->g1, L.wg, d, 3 * d, d, s));
     GR_TRY(launch_gemm_nt_rms(x_cand, d, L.wg, d, L.qkv, 3 * d, Tc, 3 * d, d, GEMM_EPI_STORE, s));
   } else {
     const void* zin = x_cand;
     if (pre) {
-      GR_TRY(launch_rmsnorm(dt, x_cand, w->g1, L.z, Tc, d, s));
+      GR_TRY(launch_rmsnorm(rt, dt, x_cand, w->g1, L.z, Tc, d, s));
       zin = L.z;
     }
     GR_TRY(launch_gemm_nt(dt, zin, d, w->wqkv, d, L.qkv, 3 * d, Tc, 3 * d, d, GEMM_EPI_STORE, nullptr, 0, nullptr,
@@ -520,16 +528,16 @@ genrank_status genrank_layer_fwd_cached(const genrank_batch* b, const genrank_la
                                 kh ? kh : L.qkv, kh ? kh + d * es : L.qkv, ld_kv, L.o, d, L.lse, s));
   if (!pre)
     return launch_gemm_nt(dt, L.o, d, w->wo, d, y_cand, d, Tc, d, d, GEMM_EPI_STORE, nullptr, 0, nullptr, 0, s);
-  GR_TRY(launch_gemm_nt(dt, L.o, d, w->wo, d, L.x1, d, Tc, d, d, GEMM_EPI_RESID, x_cand, d, nullptr, 0, s));
+  GR_TRY(launch_gemm_nt(dt, L.o, d, w->wo, d, L.x1, d, Tc, d, d, epi_res, x_cand, d, nullptr, 0, s));
   if (fuse) {
     GR_TRY(launch_scale_cols(w->w1, d, w->g2, L.wg, d, ffn, d, s));
     GR_TRY(launch_gemm_nt_rms(L.x1, d, L.wg, d, L.hdn, ffn, Tc, ffn, d, GEMM_EPI_SILU, s));
   } else {
-    GR_TRY(launch_rmsnorm(dt, L.x1, w->g2, L.z2, Tc, d, s));
+    GR_TRY(launch_rmsnorm(rt, dt, L.x1, w->g2, L.z2, Tc, d, s));
     GR_TRY(launch_gemm_nt(dt, L.z2, d, w->w1, d, L.hdn, ffn, Tc, ffn, d, GEMM_EPI_SILU, nullptr, 0, nullptr, ffn,
                           s));
   }
-  return launch_gemm_nt(dt, L.hdn, ffn, w->w2, ffn, y_cand, d, Tc, d, ffn, GEMM_EPI_RESID, L.x1, d, nullptr, 0, s);
+  return launch_gemm_nt(dt, L.hdn, ffn, w->w2, ffn, y_cand, d, Tc, d, ffn, epi_res, L.x1, d, nullptr, 0, s);
 }
 
 genrank_status genrank_layer_bwd(const genrank_batch* b, const genrank_layer_weights* w,
@@ -562,7 +570,7 @@ genrank_status genrank_layer_bwd(const genrank_batch* b, const genrank_layer_wei
     GR_TRY(launch_gemm_nn(dt, dy, d, w->w2, ffn, L.dh, ffn, T, ffn, d, L.wt, s, GEMM_EPI_DSILU, F.a, ffn));
     GR_TRY(launch_gemm_tn(dt, L.dh, ffn, F.z2, d, g.w1, d, ffn, d, Tl, L.tn, L.tn_bytes, s));
     GR_TRY(launch_gemm_nn(dt, L.dh, ffn, w->w1, d, L.dz2, d, T, d, ffn, L.wt, s));
-    GR_TRY(launch_rmsnorm_bwd(dt, F.x1, w->g2, L.dz2, dy, L.dx1, g.g2, T, d, L.rms, s));
+    GR_TRY(launch_rmsnorm_bwd(resid_dtype(b), dt, F.x1, w->g2, L.dz2, dy, L.dx1, g.g2, T, d, L.rms, s));
     att_grad = L.dx1;
   }
   // attention branch: out = Wo o
@@ -575,7 +583,7 @@ genrank_status genrank_layer_bwd(const genrank_batch* b, const genrank_layer_wei
   GR_TRY(launch_gemm_tn(dt, L.dqkv, 3 * d, zin, d, g.wqkv, d, 3 * d, d, Tl, L.tn, L.tn_bytes, s));
   if (!pre) return launch_gemm_nn(dt, L.dqkv, 3 * d, w->wqkv, d, dx, d, T, d, 3 * d, L.wt, s);
   GR_TRY(launch_gemm_nn(dt, L.dqkv, 3 * d, w->wqkv, d, L.dz, d, T, d, 3 * d, L.wt, s));
-  return launch_rmsnorm_bwd(dt, x_in, w->g1, L.dz, L.dx1, dx, g.g1, T, d, L.rms, s);
+  return launch_rmsnorm_bwd(resid_dtype(b), dt, x_in, w->g1, L.dz, L.dx1, dx, g.g1, T, d, L.rms, s);
 }
 
 genrank_status genrank_linear(int32_t dtype, const void* x, int64_t ldx, const void* w,
@@ -596,6 +604,12 @@ genrank_status genrank_linear(int32_t dtype, const void* x, int64_t ldx, const v
     case GENRANK_EPI_SILU:
       if (pre && ldpre < N) return GENRANK_E_SHAPE;
       epi = GEMM_EPI_SILU;
+      break;
+    case GENRANK_EPI_RESIDUAL_F32:
+      if (!residual || ldr < N) return GENRANK_E_ARG;
+      if (ldy % 4 || ldr % 4) return GENRANK_E_SHAPE;
+      if ((reinterpret_cast<uintptr_t>(y) | reinterpret_cast<uintptr_t>(residual)) % 16) return GENRANK_E_ARG;
+      epi = GEMM_EPI_RESID_F32;
       break;
     default: return GENRANK_E_ARG;
   }
@@ -645,7 +659,7 @@ genrank_status genrank_head_fwd(const genrank_batch* b, const void* x, const flo
   GR_TRY(check_batch(b));
   if (!x || !g_final || !w_head || !b_head || !logits) return GENRANK_E_ARG;
   if (n_tasks < 1 || n_tasks > 8) return GENRANK_E_SHAPE;
-  return launch_head_fwd(b->dtype, x, b->total_hist, static_cast<int64_t>(b->B) * b->m, nullptr, b->d,
+  return launch_head_fwd(resid_dtype(b), x, b->total_hist, static_cast<int64_t>(b->B) * b->m, nullptr, b->d,
                          g_final, w_head, b_head, n_tasks, logits, S(stream));
 }
 
@@ -672,16 +686,17 @@ genrank_status genrank_head_bwd(const genrank_batch* b, const void* x, const flo
   if (!ws || ws_bytes < head_bwd_workspace(b->d, n_tasks)) return GENRANK_E_WORKSPACE;
   const hipStream_t s = S(stream);
   GR_TRY(launch_fill_zero(b->dtype, dx, b->total_hist * b->d, s));
-  return launch_head_bwd(b->dtype, x, b->total_hist, static_cast<int64_t>(b->B) * b->m, nullptr, b->d,
+  return launch_head_bwd(resid_dtype(b), b->dtype, x, b->total_hist, static_cast<int64_t>(b->B) * b->m, nullptr, b->d,
                          g_final, w_head, n_tasks, dlogits, dx, dg_final, dw_head, db_head, ws, s);
 }
 
-genrank_status genrank_head_bwd_rows(int32_t dtype, int32_t d, int64_t n_x_rows, const void* x,
+genrank_status genrank_head_bwd_rows(int32_t x_dtype, int32_t dtype, int32_t d, int64_t n_x_rows, const void* x,
                                      int64_t n_rows, const int32_t* rows, const float* g_final,
                                      const float* w_head, int32_t n_tasks, const float* dlogits, void* dx,
                                      float* dg_final, float* dw_head, float* db_head, void* ws,
                                      size_t ws_bytes, genrank_stream_t stream) {
   if (dtype != GENRANK_BF16 && dtype != GENRANK_F32) return GENRANK_E_DTYPE;
+  if (x_dtype != dtype && x_dtype != GENRANK_F32) return GENRANK_E_DTYPE;
   if (!x || !g_final || !w_head || !dlogits || !dx || !dg_final || !dw_head || !db_head ||
       (n_rows > 0 && !rows))
     return GENRANK_E_ARG;
@@ -691,7 +706,7 @@ genrank_status genrank_head_bwd_rows(int32_t dtype, int32_t d, int64_t n_x_rows,
   if (!ws || ws_bytes < head_bwd_workspace(d, n_tasks)) return GENRANK_E_WORKSPACE;
   const hipStream_t s = S(stream);
   GR_TRY(launch_fill_zero(dtype, dx, n_x_rows * d, s));
-  return launch_head_bwd(dtype, x, 0, n_rows, rows, d, g_final, w_head, n_tasks, dlogits, dx, dg_final, dw_head,
+  return launch_head_bwd(x_dtype, dtype, x, 0, n_rows, rows, d, g_final, w_head, n_tasks, dlogits, dx, dg_final, dw_head,
                          db_head, ws, s);
 }
 

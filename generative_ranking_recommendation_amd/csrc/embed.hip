@@ -209,7 +209,7 @@ __device__ int derive_chunk(const EmbedArgs& a, RowIdx* sidx, int64_t* sbounds, 
   return rows;
 }
 
-template <typename T>
+template <typename T, typename TO>
 __global__ void __launch_bounds__(EMB_THREADS) embed_sum_kernel(EmbedArgs a) {
   __shared__ RowIdx sidx[EMB_ROWS];
   __shared__ int64_t sbounds[MAX_BOUNDS];
@@ -226,7 +226,7 @@ __global__ void __launch_bounds__(EMB_THREADS) embed_sum_kernel(EmbedArgs a) {
   const T* tp = static_cast<const T*>(a.t_pos);
   const T* tr = static_cast<const T*>(a.t_ri);
   const T* tt = static_cast<const T*>(a.t_rt);
-  T* out = static_cast<T*>(a.out);
+  TO* out = static_cast<TO*>(a.out);
   const int64_t d = a.d;
   constexpr int U = 2;  // items per thread in flight
   for (int base = threadIdx.x; base < total; base += EMB_THREADS * U) {
@@ -260,7 +260,12 @@ __global__ void __launch_bounds__(EMB_THREADS) embed_sum_kernel(EmbedArgs a) {
       if (idx < total) {
         const int r = idx / cpr;
         const int col = (idx - r * cpr) * V;
-        store_vec(out + (row0 + r) * d + col, acc[uu]);
+        if constexpr (sizeof(TO) == sizeof(T)) {
+          store_vec(out + (row0 + r) * d + col, acc[uu]);
+        } else {  // bf16 tables, f32 rows: two 4-column stores
+          store_vec(out + (row0 + r) * d + col, acc[uu]);
+          store_vec(out + (row0 + r) * d + col + 4, acc[uu] + 4);
+        }
       }
     }
   }
@@ -290,7 +295,8 @@ __device__ __forceinline__ void add_vec(const uint4& v, float* acc) {
 // workgroup rather than fetched from the same L2 lines by every row.
 constexpr int SACT_MAX = 32768;
 
-template <typename T, bool SACT>
+// TO: the element type of the output rows (the tables' type, or f32 rows from bf16 tables).
+template <typename T, typename TO, bool SACT>
 __global__ void __launch_bounds__(EMB_THREADS) embed_sum_rows_kernel(EmbedArgs a) {
   __shared__ RowIdx sidx[EMB_ROWS];
   __shared__ int64_t sbounds[MAX_BOUNDS];
@@ -321,8 +327,10 @@ __global__ void __launch_bounds__(EMB_THREADS) embed_sum_rows_kernel(EmbedArgs a
   const __amdgpu_buffer_rsrc_t rs_pos = rsrc(a.t_pos, a.bytes_pos);
   const __amdgpu_buffer_rsrc_t rs_ri = rsrc(a.t_ri, a.bytes_ri);
   const __amdgpu_buffer_rsrc_t rs_rt = rsrc(a.t_rt, a.bytes_rt);
-  const uint32_t out_bytes = static_cast<uint32_t>(rows) * rowb;
-  const __amdgpu_buffer_rsrc_t rs_out = rsrc(static_cast<T*>(a.out) + row0 * a.d, out_bytes);
+  constexpr uint32_t OW = sizeof(TO) / sizeof(T);  // 16-byte output pieces per column chunk
+  const uint32_t orowb = rowb * OW, ocolb = colb * OW;
+  const uint32_t out_bytes = static_cast<uint32_t>(rows) * orowb;
+  const __amdgpu_buffer_rsrc_t rs_out = rsrc(static_cast<TO*>(a.out) + row0 * a.d, out_bytes);
   for (int r = rp; r < rows; r += rpp * UR) {
     uint4 v[UR][5];
 #pragma unroll
@@ -347,16 +355,18 @@ __global__ void __launch_bounds__(EMB_THREADS) embed_sum_rows_kernel(EmbedArgs a
 #pragma unroll
       for (int t = 0; t < 5; ++t) add_vec<T>(v[u][t], acc);
       const int rr = r + u * rpp;
-      const uint32_t ob = rr < rows ? static_cast<uint32_t>(rr) * rowb + colb : out_bytes;
-      uint4 o;
-      if constexpr (sizeof(T) == 2) {
-        o = pack8(acc);
+      const uint32_t ob = rr < rows ? static_cast<uint32_t>(rr) * orowb + ocolb : out_bytes;
+      typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+      if constexpr (sizeof(TO) == 2) {
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, pack8(acc)), rs_out, ob, 0, 0);
       } else {
-        o = make_uint4(__float_as_uint(acc[0]), __float_as_uint(acc[1]), __float_as_uint(acc[2]),
-                       __float_as_uint(acc[3]));
+#pragma unroll
+        for (int q = 0; q < V / 4; ++q) {
+          const uint4 o = make_uint4(__float_as_uint(acc[4 * q]), __float_as_uint(acc[4 * q + 1]),
+                                     __float_as_uint(acc[4 * q + 2]), __float_as_uint(acc[4 * q + 3]));
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), rs_out, ob + 16u * q, 0, 0);
+        }
       }
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, o),
-                                             rs_out, ob, 0, 0);
     }
   }
 }
@@ -677,21 +687,46 @@ dim3 grid_of(const EmbedArgs& a) {
   return dim3(static_cast<unsigned>(a.hist_chunks + a.cand_chunks), static_cast<unsigned>(a.B));
 }
 
-// the row kernel, with the action table in LDS when it is small enough
-void launch_rows(const EmbedArgs& a, int dtype, hipStream_t stream) {
+// the row kernel, with the action table in LDS when it is small enough; f32_out: f32 rows
+// from bf16 tables (the f32 residual stream)
+void launch_rows(const EmbedArgs& a, int dtype, bool f32_out, hipStream_t stream) {
   const bool sact = a.bytes_action % 16 == 0 && a.bytes_action <= static_cast<uint32_t>(SACT_MAX);
   const size_t lds = sact ? a.bytes_action : 0;
-  if (dtype == GENRANK_BF16) {
+  if (dtype == GENRANK_BF16 && f32_out) {
     if (sact)
-      hipLaunchKernelGGL((embed_sum_rows_kernel<bf16_t, true>), grid_of(a), dim3(EMB_THREADS), lds, stream, a);
+      hipLaunchKernelGGL((embed_sum_rows_kernel<bf16_t, float, true>), grid_of(a), dim3(EMB_THREADS), lds, stream, a);
     else
-      hipLaunchKernelGGL((embed_sum_rows_kernel<bf16_t, false>), grid_of(a), dim3(EMB_THREADS), 0, stream, a);
+      hipLaunchKernelGGL((embed_sum_rows_kernel<bf16_t, float, false>), grid_of(a), dim3(EMB_THREADS), 0, stream, a);
+  } else if (dtype == GENRANK_BF16) {
+    if (sact)
+      hipLaunchKernelGGL((embed_sum_rows_kernel<bf16_t, bf16_t, true>), grid_of(a), dim3(EMB_THREADS), lds, stream, a);
+    else
+      hipLaunchKernelGGL((embed_sum_rows_kernel<bf16_t, bf16_t, false>), grid_of(a), dim3(EMB_THREADS), 0, stream, a);
   } else {
     if (sact)
-      hipLaunchKernelGGL((embed_sum_rows_kernel<float, true>), grid_of(a), dim3(EMB_THREADS), lds, stream, a);
+      hipLaunchKernelGGL((embed_sum_rows_kernel<float, float, true>), grid_of(a), dim3(EMB_THREADS), lds, stream, a);
     else
-      hipLaunchKernelGGL((embed_sum_rows_kernel<float, false>), grid_of(a), dim3(EMB_THREADS), 0, stream, a);
+      hipLaunchKernelGGL((embed_sum_rows_kernel<float, float, false>), grid_of(a), dim3(EMB_THREADS), 0, stream, a);
   }
+}
+// either gather kernel for the batch's dtype and residual-stream type
+void launch_gather(const genrank_batch* b, const genrank_tables* t, const EmbedArgs& a, hipStream_t stream) {
+  const int es = b->dtype == GENRANK_BF16 ? 2 : 4;
+  const bool f32_out = b->dtype == GENRANK_BF16 && b->resid == GENRANK_RESID_F32;
+  const int cpr = b->d * es / 16;
+  // the row kernel needs whole 16-byte columns that divide the workgroup, and every table
+  // and the chunk's output addressable with 32-bit offsets
+  const int64_t rb = static_cast<int64_t>(b->d) * es;
+  const bool rows_ok = b->d * es % 16 == 0 && cpr <= EMB_THREADS && EMB_THREADS % cpr == 0 &&
+                       t->n_item * rb < 0xFFFFFFFFll && EMB_ROWS * rb * 2 < 0xFFFFFFFFll;
+  if (rows_ok)
+    launch_rows(a, b->dtype, f32_out, stream);
+  else if (f32_out)
+    hipLaunchKernelGGL((embed_sum_kernel<bf16_t, float>), grid_of(a), dim3(EMB_THREADS), 0, stream, a);
+  else if (b->dtype == GENRANK_BF16)
+    hipLaunchKernelGGL((embed_sum_kernel<bf16_t, bf16_t>), grid_of(a), dim3(EMB_THREADS), 0, stream, a);
+  else
+    hipLaunchKernelGGL((embed_sum_kernel<float, float>), grid_of(a), dim3(EMB_THREADS), 0, stream, a);
 }
 
 }  // namespace
@@ -719,19 +754,7 @@ genrank_status launch_embed_sum(const genrank_batch* b, const genrank_inputs* in
                                 const genrank_tables* t, void* out, hipStream_t stream) {
   EmbedArgs a = make_args(b, in, t);
   a.out = out;
-  const int es = b->dtype == GENRANK_BF16 ? 2 : 4;
-  const int cpr = b->d * es / 16;
-  // the row kernel needs whole 16-byte columns that divide the workgroup, and every table
-  // and the chunk's output addressable with 32-bit offsets
-  const int64_t rb = static_cast<int64_t>(b->d) * es;
-  const bool rows_ok = b->d * es % 16 == 0 && cpr <= EMB_THREADS && EMB_THREADS % cpr == 0 &&
-                       t->n_item * rb < 0xFFFFFFFFll && EMB_ROWS * rb < 0xFFFFFFFFll;
-  if (rows_ok)
-    launch_rows(a, b->dtype, stream);
-  else if (b->dtype == GENRANK_BF16)
-    hipLaunchKernelGGL(embed_sum_kernel<bf16_t>, grid_of(a), dim3(EMB_THREADS), 0, stream, a);
-  else
-    hipLaunchKernelGGL(embed_sum_kernel<float>, grid_of(a), dim3(EMB_THREADS), 0, stream, a);
+  launch_gather(b, t, a, stream);
   GR_CHECK_LAUNCH();
   return GENRANK_OK;
 }
@@ -744,17 +767,7 @@ genrank_status launch_embed_sum_cand(const genrank_batch* b, const genrank_input
   a.T_h = 0;
   a.out = out;
   if (a.cand_chunks == 0) return GENRANK_OK;
-  const int es = b->dtype == GENRANK_BF16 ? 2 : 4;
-  const int cpr = b->d * es / 16;
-  const int64_t rb = static_cast<int64_t>(b->d) * es;
-  const bool rows_ok = b->d * es % 16 == 0 && cpr <= EMB_THREADS && EMB_THREADS % cpr == 0 &&
-                       t->n_item * rb < 0xFFFFFFFFll && EMB_ROWS * rb < 0xFFFFFFFFll;
-  if (rows_ok)
-    launch_rows(a, b->dtype, stream);
-  else if (b->dtype == GENRANK_BF16)
-    hipLaunchKernelGGL(embed_sum_kernel<bf16_t>, grid_of(a), dim3(EMB_THREADS), 0, stream, a);
-  else
-    hipLaunchKernelGGL(embed_sum_kernel<float>, grid_of(a), dim3(EMB_THREADS), 0, stream, a);
+  launch_gather(b, t, a, stream);
   GR_CHECK_LAUNCH();
   return GENRANK_OK;
 }

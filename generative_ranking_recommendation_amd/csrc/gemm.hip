@@ -29,7 +29,7 @@ struct GemmArgs {
   const bf16_t* A; int64_t lda;
   const bf16_t* W; int64_t ldw;
   void* C; int64_t ldc;
-  const bf16_t* R; int64_t ldr;   // residual (EPI_RESID), may alias C
+  const void* R; int64_t ldr;     // residual (EPI_RESID: bf16; EPI_RESID_F32: f32), may alias C
   bf16_t* Cpre; int64_t ldpre;    // pre-activation copy (EPI_SILU, optional)
   int M, N, K;
 };
@@ -59,14 +59,14 @@ template <int EPI>
 __device__ __forceinline__ void epi_math(const GemmArgs& g, int m, int n, float (&v)[4]) {
   if constexpr (EPI == GEMM_EPI_RESID) {
     if (m < g.M) {
-      const uint2 r = *reinterpret_cast<const uint2*>(g.R + static_cast<int64_t>(m) * g.ldr + n);
+      const uint2 r = *reinterpret_cast<const uint2*>(static_cast<const bf16_t*>(g.R) + static_cast<int64_t>(m) * g.ldr + n);
       v[0] += __uint_as_float(r.x << 16); v[1] += __uint_as_float(r.x & 0xFFFF0000u);
       v[2] += __uint_as_float(r.y << 16); v[3] += __uint_as_float(r.y & 0xFFFF0000u);
     }
   }
   if constexpr (EPI == GEMM_EPI_DSILU) {
     if (m < g.M) {
-      const uint2 r = *reinterpret_cast<const uint2*>(g.R + static_cast<int64_t>(m) * g.ldr + n);
+      const uint2 r = *reinterpret_cast<const uint2*>(static_cast<const bf16_t*>(g.R) + static_cast<int64_t>(m) * g.ldr + n);
       v[0] *= dsilu_f(__uint_as_float(r.x << 16)); v[1] *= dsilu_f(__uint_as_float(r.x & 0xFFFF0000u));
       v[2] *= dsilu_f(__uint_as_float(r.y << 16)); v[3] *= dsilu_f(__uint_as_float(r.y & 0xFFFF0000u));
     }
@@ -83,6 +83,20 @@ __device__ __forceinline__ void epi_math(const GemmArgs& g, int m, int n, float 
   }
 }
 
+// f32 output rows straight from the MFMA layout (a lane's 4 consecutive columns of one row are
+// one 16-byte store; four lanes cover 64 contiguous bytes of a row): EPI_F32 stores the
+// accumulator, EPI_RESID_F32 adds the f32 residual first (read by the same lane before its store,
+// so R may alias C).
+template <int EPI>
+__device__ __forceinline__ void store_f32(const GemmArgs& g, int m, int n, const float (&v)[4]) {
+  float4 o = make_float4(v[0], v[1], v[2], v[3]);
+  if constexpr (EPI == GEMM_EPI_RESID_F32) {
+    const float4 r = *reinterpret_cast<const float4*>(static_cast<const float*>(g.R) + static_cast<int64_t>(m) * g.ldr + n);
+    o.x += r.x; o.y += r.y; o.z += r.z; o.w += r.w;
+  }
+  *reinterpret_cast<float4*>(static_cast<float*>(g.C) + static_cast<int64_t>(m) * g.ldc + n) = o;
+}
+
 // ---- epilogue shared by the MFMA kernels: lane holds C[m][n .. n+3] for each (nb, mb).
 // The 128 x 128 tile (after the epilogue math, in the output dtype) is staged through LDS,
 // rows 0-63 at sC_lo and rows 64-127 at sC_hi (pitch CP), so that every global store is a
@@ -91,16 +105,15 @@ template <int EPI>
 __device__ __forceinline__ void epilogue(const GemmArgs& g, const f32x4_t (&acc)[4][4], bf16_t* sC_lo,
                                          bf16_t* sC_hi, int m0, int n0, int wm, int wn, int l16, int g4,
                                          int tid) {
-  if constexpr (EPI == GEMM_EPI_F32) {
+  if constexpr (EPI == GEMM_EPI_F32 || EPI == GEMM_EPI_RESID_F32) {
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
       const int m = m0 + wm * 64 + mb * 16 + l16;
       if (m >= g.M) continue;
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) {
-        const int n = n0 + wn * 64 + nb * 16 + g4 * 4;
-        float* c = static_cast<float*>(g.C) + static_cast<int64_t>(m) * g.ldc + n;
-        *reinterpret_cast<float4*>(c) = make_float4(acc[nb][mb][0], acc[nb][mb][1], acc[nb][mb][2], acc[nb][mb][3]);
+        const float v[4] = {acc[nb][mb][0], acc[nb][mb][1], acc[nb][mb][2], acc[nb][mb][3]};
+        store_f32<EPI>(g, m, n0 + wn * 64 + nb * 16 + g4 * 4, v);
       }
     }
     return;
@@ -427,6 +440,24 @@ __global__ void __launch_bounds__(BTHREADS) gemm_nt_bf16_big_kernel(GemmArgs g) 
     lds_barrier();  // every wave is done with the stage buffers before C goes into them
   }
 
+  if constexpr (EPI == GEMM_EPI_RESID_F32) {  // f32 rows straight from the registers
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) {
+      const int ml = wm * 128 + mb * 16 + l16;
+      if (m0 + ml >= g.M) continue;
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        float v[4] = {acc[nb][mb][0], acc[nb][mb][1], acc[nb][mb][2], acc[nb][mb][3]};
+        if constexpr (RMS) {
+          const float r = sR[ml];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[i] *= r;
+        }
+        store_f32<EPI>(g, m0 + ml, n0 + wn * 64 + nb * 16 + g4 * 4, v);
+      }
+    }
+    return;
+  }
   // epilogue: rows 64 q .. 64 q + 63 of the C tile in buffer q; a wave's rows
   // wm * 128 + mb * 16 + l16 fall in buffers 2 wm (mb < 4) and 2 wm + 1
   bf16_t* cb_lo = wm ? st2 : st0;
@@ -718,10 +749,10 @@ genrank_status launch_gemm_nt(int dtype, const void* A, int64_t lda, const void*
                               int64_t ldr, void* Cpre, int64_t ldpre, hipStream_t stream) {
   if (M <= 0) return GENRANK_OK;
   if (dtype == GENRANK_BF16 && N % GBN == 0 && K % GBK == 0 && lda % 8 == 0 && ldw % 8 == 0 &&
-      ldc % 8 == 0 && ((epi != GEMM_EPI_RESID && epi != GEMM_EPI_DSILU) || ldr % 4 == 0) && (!Cpre || ldpre % 4 == 0) &&
+      ldc % 8 == 0 && (epi == GEMM_EPI_STORE || epi == GEMM_EPI_SILU || ldr % 4 == 0) && (!Cpre || ldpre % 4 == 0) &&
       static_cast<int64_t>(GBN) * ldw * 2 < (int64_t(1) << 32)) {
     GemmArgs g{static_cast<const bf16_t*>(A), lda, static_cast<const bf16_t*>(W), ldw, C, ldc,
-               static_cast<const bf16_t*>(R), ldr, static_cast<bf16_t*>(Cpre), ldpre, M, N, K};
+               R, ldr, static_cast<bf16_t*>(Cpre), ldpre, M, N, K};
     const int grid = (N / GBN) * ((M + GBM - 1) / GBM);
     if (K % (4 * GBK) == 0 && K >= 512 && N % BBN == 0 && M >= 4 * BBM &&
         static_cast<int64_t>(BBN) * ldw * 2 < (int64_t(1) << 32)) {
@@ -738,6 +769,9 @@ genrank_status launch_gemm_nt(int dtype, const void* A, int64_t lda, const void*
           break;
         case GEMM_EPI_DSILU:
           hipLaunchKernelGGL((gemm_nt_bf16_big_kernel<GEMM_EPI_DSILU, false>), dim3(bgrid), dim3(BTHREADS), 0, stream, g);
+          break;
+        case GEMM_EPI_RESID_F32:
+          hipLaunchKernelGGL((gemm_nt_bf16_big_kernel<GEMM_EPI_RESID_F32, false>), dim3(bgrid), dim3(BTHREADS), 0, stream, g);
           break;
         default:
           return GENRANK_E_ARG;
@@ -759,6 +793,9 @@ genrank_status launch_gemm_nt(int dtype, const void* A, int64_t lda, const void*
         case GEMM_EPI_DSILU:
           hipLaunchKernelGGL(gemm_nt_bf16_dma_kernel<GEMM_EPI_DSILU>, dim3(grid), dim3(GTHREADS), 0, stream, g);
           break;
+        case GEMM_EPI_RESID_F32:
+          hipLaunchKernelGGL(gemm_nt_bf16_dma_kernel<GEMM_EPI_RESID_F32>, dim3(grid), dim3(GTHREADS), 0, stream, g);
+          break;
         default:
           return GENRANK_E_ARG;
       }
@@ -778,6 +815,9 @@ genrank_status launch_gemm_nt(int dtype, const void* A, int64_t lda, const void*
       case GEMM_EPI_DSILU:
         hipLaunchKernelGGL(gemm_nt_bf16_kernel<GEMM_EPI_DSILU>, dim3(grid), dim3(GTHREADS), 0, stream, g);
         break;
+      case GEMM_EPI_RESID_F32:
+        hipLaunchKernelGGL(gemm_nt_bf16_kernel<GEMM_EPI_RESID_F32>, dim3(grid), dim3(GTHREADS), 0, stream, g);
+        break;
       default:
         return GENRANK_E_ARG;
     }
@@ -785,6 +825,9 @@ genrank_status launch_gemm_nt(int dtype, const void* A, int64_t lda, const void*
     return GENRANK_OK;
   }
   // C = A W^T : B[k, n] = W[n, k]
+  if (epi == GEMM_EPI_RESID_F32)  // f32 output and residual
+    return launch_gemm_general(dtype, GENRANK_F32, A, lda, 1, W, 1, ldw, C, ldc, M, N, K, GEMM_EPI_RESID, false, R,
+                               ldr, Cpre, ldpre, stream);
   return launch_gemm_general(dtype, dtype, A, lda, 1, W, 1, ldw, C, ldc, M, N, K, epi, false, R,
                              ldr, Cpre, ldpre, stream);
 }

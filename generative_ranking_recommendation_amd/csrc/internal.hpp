@@ -10,12 +10,16 @@ namespace genrank {
 
 // epilogues: STORE C = acc; RESID C = acc + R; SILU C = silu(acc) (Cpre = acc);
 // F32 C = acc in f32; DSILU C = acc * silu'(R) (R the pre-activation: the SiLU backward)
-enum { GEMM_EPI_STORE = 0, GEMM_EPI_RESID = 1, GEMM_EPI_SILU = 2, GEMM_EPI_F32 = 3, GEMM_EPI_DSILU = 4 };
+// RESID_F32 C = acc + R with R and C f32 (the f32 residual stream)
+enum { GEMM_EPI_STORE = 0, GEMM_EPI_RESID = 1, GEMM_EPI_SILU = 2, GEMM_EPI_F32 = 3, GEMM_EPI_DSILU = 4,
+       GEMM_EPI_RESID_F32 = 5 };
 
 constexpr float RMS_EPS = 1e-6f;
 
 genrank_status check_batch(const genrank_batch* b);
 size_t dtype_size(int dtype);
+// the element type of the batch's residual stream (genrank_batch.resid)
+int resid_dtype(const genrank_batch* b);
 
 // embedding
 genrank_status check_embed_args(const genrank_batch* b, const genrank_inputs* in,
@@ -123,10 +127,12 @@ genrank_status launch_gemm_nn(int dtype, const void* A, int64_t lda, const void*
                               int epi = GEMM_EPI_STORE, const void* R = nullptr, int64_t ldr = 0);
 
 // row-wise ops
-genrank_status launch_rmsnorm(int dtype, const void* x, const float* g, void* y, int64_t rows,
+// y = rmsnorm(x) g with x in in_dtype and y in out_dtype (bf16 -> bf16, f32 -> bf16, f32 -> f32)
+genrank_status launch_rmsnorm(int in_dtype, int out_dtype, const void* x, const float* g, void* y, int64_t rows,
                               int d, hipStream_t stream);
 size_t rmsnorm_bwd_workspace(int d);  // per-block partial rows of dg
-genrank_status launch_rmsnorm_bwd(int dtype, const void* x, const float* g, const void* dy,
+// x in x_dtype (the residual stream), dy, add, dx in dtype
+genrank_status launch_rmsnorm_bwd(int x_dtype, int dtype, const void* x, const float* g, const void* dy,
                                   const void* add, void* dx, float* dg, int64_t rows, int d, void* ws,
                                   hipStream_t stream);
 genrank_status launch_fill_f32(float* p, int64_t n, float v, hipStream_t stream);
@@ -136,9 +142,11 @@ genrank_status launch_head_fwd(int dtype, const void* x, int64_t row0, int64_t r
                                int d, const float* g, const float* w, const float* bias, int nt,
                                float* logits, hipStream_t stream);
 size_t head_bwd_workspace(int d, int nt);  // per-block partial rows of dg, dw, db
-genrank_status launch_head_bwd(int dtype, const void* x, int64_t row0, int64_t rows, const int32_t* idx,
-                               int d, const float* g, const float* w, int nt, const float* dlogits,
-                               void* dx, float* dg, float* dw, float* db, void* ws, hipStream_t stream);
+// x in x_dtype (the residual stream), dx in dtype
+genrank_status launch_head_bwd(int x_dtype, int dtype, const void* x, int64_t row0, int64_t rows,
+                               const int32_t* idx, int d, const float* g, const float* w, int nt,
+                               const float* dlogits, void* dx, float* dg, float* dw, float* db, void* ws,
+                               hipStream_t stream);
 genrank_status launch_bce(int64_t n, int nt, const float* logits, const float* labels,
                           float* loss, float* dlogits, hipStream_t stream);
 

@@ -17,13 +17,13 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-template <typename T>
-__global__ void __launch_bounds__(RW) rmsnorm_kernel(const T* __restrict__ x, const float* __restrict__ g,
-                                                     T* __restrict__ y, int64_t rows, int d) {
+template <typename TI, typename TO>
+__global__ void __launch_bounds__(RW) rmsnorm_kernel(const TI* __restrict__ x, const float* __restrict__ g,
+                                                     TO* __restrict__ y, int64_t rows, int d) {
   const int64_t r = static_cast<int64_t>(blockIdx.x) * (RW / 64) + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (r >= rows) return;
-  const T* xr = x + r * d;
+  const TI* xr = x + r * d;
   float ss = 0.f;
   for (int c = lane; c < d; c += 64) {
     const float v = to_f32(xr[c]);
@@ -31,18 +31,19 @@ __global__ void __launch_bounds__(RW) rmsnorm_kernel(const T* __restrict__ x, co
   }
   ss = wave_sum(ss);
   const float inv = rsqrtf(ss / d + RMS_EPS);
-  T* yr = y + r * d;
-  for (int c = lane; c < d; c += 64) yr[c] = from_f32<T>(to_f32(xr[c]) * inv * g[c]);
+  TO* yr = y + r * d;
+  for (int c = lane; c < d; c += 64) yr[c] = from_f32<TO>(to_f32(xr[c]) * inv * g[c]);
 }
 
 // The same normalisation with x read once through 16-byte loads: a group of LPR lanes owns
 // one row, each lane Q 16-byte chunks of it (chunk q of lane l at elements
 // (q LPR + l) VEC ..), kept in registers between the sum of squares and the store; a wave
-// takes 64 / LPR rows.  Each row's result depends only on its own elements.
-template <typename T, int LPR, int Q>
-__global__ void __launch_bounds__(RW) rmsnorm_vec_kernel(const T* __restrict__ x, const float* __restrict__ g,
-                                                         T* __restrict__ y, int64_t rows, int d) {
-  constexpr int VEC = 16 / static_cast<int>(sizeof(T));
+// takes 64 / LPR rows.  Each row's result depends only on its own elements.  TO may be
+// narrower than TI (f32 rows normalised into bf16 operands): then each store is 8 bytes.
+template <typename TI, typename TO, int LPR, int Q>
+__global__ void __launch_bounds__(RW) rmsnorm_vec_kernel(const TI* __restrict__ x, const float* __restrict__ g,
+                                                         TO* __restrict__ y, int64_t rows, int d) {
+  constexpr int VEC = 16 / static_cast<int>(sizeof(TI));
   constexpr int RPW = 64 / LPR;
   const int lane = threadIdx.x & 63;
   const int li = lane % LPR;
@@ -78,13 +79,14 @@ __global__ void __launch_bounds__(RW) rmsnorm_vec_kernel(const T* __restrict__ x
       o[e + 2] = v[q][e + 2] * inv * g4.z;
       o[e + 3] = v[q][e + 3] * inv * g4.w;
     }
-    uint4 u;
     if constexpr (VEC == 8) {
-      u = pack8(o);
+      *reinterpret_cast<uint4*>(y + r * d + c) = pack8(o);
+    } else if constexpr (sizeof(TO) == 2) {
+      *reinterpret_cast<uint2*>(y + r * d + c) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
     } else {
-      u = make_uint4(__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]), __float_as_uint(o[3]));
+      *reinterpret_cast<uint4*>(y + r * d + c) =
+          make_uint4(__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]), __float_as_uint(o[3]));
     }
-    *reinterpret_cast<uint4*>(y + r * d + c) = u;
   }
 }
 
@@ -113,8 +115,8 @@ constexpr int PART_BLOCKS = 1024;  // rmsnorm backward blocks (partial rows)
 
 // dx = r g dy - r^3 x sum(g dy x) / d  (+ add);  dg = sum over rows of dy x r.
 // Lane l owns columns 4 l + 256 q; a wave takes two rows per step.
-template <typename T>
-__global__ void __launch_bounds__(RW) rmsnorm_bwd_kernel(const T* __restrict__ x, const float* __restrict__ g,
+template <typename TX, typename T>
+__global__ void __launch_bounds__(RW) rmsnorm_bwd_kernel(const TX* __restrict__ x, const float* __restrict__ g,
                                                          const T* dy, const T* add, T* dx,
                                                          float* __restrict__ part, int64_t rows, int d) {
   __shared__ float sp[RW / 64][64 * 4 * MAXQ];
@@ -278,9 +280,10 @@ __global__ void __launch_bounds__(RW) head_fwd_kernel(const T* __restrict__ x, i
 // RMSNorm backward with rows read through 16-byte loads (lane groups as rmsnorm_vec_kernel,
 // two rows per group in flight): dx = r g dy - r^3 x sum(g dy x) / d (+ add), and the
 // block's partial row of dg = sum over rows of dy x r.  The groups of a wave add their dg
-// partials by xor-shuffles, the block's waves in order through LDS: a fixed order.
-template <typename T, int LPR, int Q>
-__global__ void __launch_bounds__(RW) rmsnorm_bwd_vec_kernel(const T* __restrict__ x, const float* __restrict__ g,
+// partials by xor-shuffles, the block's waves in order through LDS: a fixed order.  x may be
+// wider than the gradients (f32 residual rows, bf16 gradients): it is then read in two pieces.
+template <typename TX, typename T, int LPR, int Q>
+__global__ void __launch_bounds__(RW) rmsnorm_bwd_vec_kernel(const TX* __restrict__ x, const float* __restrict__ g,
                                                              const T* dy, const T* add, T* dx,
                                                              float* __restrict__ part, int64_t rows, int d) {
   constexpr int VEC = 16 / static_cast<int>(sizeof(T));
@@ -313,7 +316,14 @@ __global__ void __launch_bounds__(RW) rmsnorm_bwd_vec_kernel(const T* __restrict
 #pragma unroll
       for (int q = 0; q < Q; ++q) {
         const int c = (q * LPR + li) * VEC;
-        load(x + r * d + c, xv[k][q]);
+        if constexpr (sizeof(TX) == sizeof(T)) {
+          load(x + r * d + c, xv[k][q]);
+        } else {  // VEC = 8 f32 values: two 16-byte loads
+          const float4 a0 = *reinterpret_cast<const float4*>(x + r * d + c);
+          const float4 a1 = *reinterpret_cast<const float4*>(x + r * d + c + 4);
+          xv[k][q][0] = a0.x; xv[k][q][1] = a0.y; xv[k][q][2] = a0.z; xv[k][q][3] = a0.w;
+          xv[k][q][4] = a1.x; xv[k][q][5] = a1.y; xv[k][q][6] = a1.z; xv[k][q][7] = a1.w;
+        }
         load(dy + r * d + c, gv[k][q]);
       }
     }
@@ -463,8 +473,8 @@ __global__ void __launch_bounds__(RW) head_fwd_vec_kernel(const T* __restrict__ 
 // [dg (d) | dw (nt d) | db (nt)], summed over blocks by column_sum_kernel.
 constexpr int HEAD_BLOCKS = 64;
 
-template <typename T>
-__global__ void __launch_bounds__(RW) head_bwd_kernel(const T* __restrict__ x, int64_t row0, int64_t rows,
+template <typename TX, typename T>
+__global__ void __launch_bounds__(RW) head_bwd_kernel(const TX* __restrict__ x, int64_t row0, int64_t rows,
                                                       const int32_t* __restrict__ idx, int d,
                                                       const float* __restrict__ g,
                                                       const float* __restrict__ w, int nt,
@@ -485,7 +495,7 @@ __global__ void __launch_bounds__(RW) head_bwd_kernel(const T* __restrict__ x, i
     }
   for (int64_t r = static_cast<int64_t>(blockIdx.x) * (RW / 64) + wave; r < rows; r += nw) {
     const int64_t xrow = idx ? static_cast<int64_t>(idx[r]) : row0 + r;
-    const T* xr = x + xrow * d;
+    const TX* xr = x + xrow * d;
     float dlr[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) dlr[t] = (t < nt) ? dl[r * nt + t] : 0.f;
@@ -601,9 +611,9 @@ unsigned blocks_for(int64_t n, int per_block) {
 
 }  // namespace
 
-template <typename T>
-static bool launch_rmsnorm_vec(const T* x, const float* g, T* y, int64_t rows, int d, hipStream_t stream) {
-  constexpr int VEC = 16 / static_cast<int>(sizeof(T));
+template <typename TI, typename TO>
+static bool launch_rmsnorm_vec(const TI* x, const float* g, TO* y, int64_t rows, int d, hipStream_t stream) {
+  constexpr int VEC = 16 / static_cast<int>(sizeof(TI));
   if (d % VEC != 0 || ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(y) |
                         reinterpret_cast<uintptr_t>(g)) & 15u))
     return false;
@@ -615,46 +625,45 @@ static bool launch_rmsnorm_vec(const T* x, const float* g, T* y, int64_t rows, i
     return true;
   };
   switch (chunks) {
-    case 2: return go(rmsnorm_vec_kernel<T, 2, 1>, 2);
-    case 4: return go(rmsnorm_vec_kernel<T, 4, 1>, 4);
-    case 8: return go(rmsnorm_vec_kernel<T, 8, 1>, 8);
-    case 16: return go(rmsnorm_vec_kernel<T, 16, 1>, 16);
-    case 32: return go(rmsnorm_vec_kernel<T, 32, 1>, 32);
-    case 64: return go(rmsnorm_vec_kernel<T, 64, 1>, 64);
-    case 128: return go(rmsnorm_vec_kernel<T, 64, 2>, 64);
-    case 192: return go(rmsnorm_vec_kernel<T, 64, 3>, 64);
-    case 256: return go(rmsnorm_vec_kernel<T, 64, 4>, 64);
+    case 2: return go(rmsnorm_vec_kernel<TI, TO, 2, 1>, 2);
+    case 4: return go(rmsnorm_vec_kernel<TI, TO, 4, 1>, 4);
+    case 8: return go(rmsnorm_vec_kernel<TI, TO, 8, 1>, 8);
+    case 16: return go(rmsnorm_vec_kernel<TI, TO, 16, 1>, 16);
+    case 32: return go(rmsnorm_vec_kernel<TI, TO, 32, 1>, 32);
+    case 64: return go(rmsnorm_vec_kernel<TI, TO, 64, 1>, 64);
+    case 128: return go(rmsnorm_vec_kernel<TI, TO, 64, 2>, 64);
+    case 192: return go(rmsnorm_vec_kernel<TI, TO, 64, 3>, 64);
+    case 256: return go(rmsnorm_vec_kernel<TI, TO, 64, 4>, 64);
     default: return false;
   }
 }
 
-genrank_status launch_rmsnorm(int dtype, const void* x, const float* g, void* y, int64_t rows,
+template <typename TI, typename TO>
+static void launch_rmsnorm_typed(const void* x, const float* g, void* y, int64_t rows, int d, hipStream_t stream) {
+  if (launch_rmsnorm_vec(static_cast<const TI*>(x), g, static_cast<TO*>(y), rows, d, stream)) return;
+  hipLaunchKernelGGL((rmsnorm_kernel<TI, TO>), dim3(static_cast<unsigned>((rows + 3) / 4)), dim3(RW), 0, stream,
+                     static_cast<const TI*>(x), g, static_cast<TO*>(y), rows, d);
+}
+
+genrank_status launch_rmsnorm(int in_dtype, int out_dtype, const void* x, const float* g, void* y, int64_t rows,
                               int d, hipStream_t stream) {
   if (rows <= 0) return GENRANK_OK;
-  const bool vec = dtype == GENRANK_BF16
-                       ? launch_rmsnorm_vec(static_cast<const bf16_t*>(x), g, static_cast<bf16_t*>(y), rows, d,
-                                            stream)
-                       : launch_rmsnorm_vec(static_cast<const float*>(x), g, static_cast<float*>(y), rows, d,
-                                            stream);
-  if (vec) {
-    GR_CHECK_LAUNCH();
-    return GENRANK_OK;
-  }
-  const unsigned grid = static_cast<unsigned>((rows + 3) / 4);
-  if (dtype == GENRANK_BF16)
-    hipLaunchKernelGGL(rmsnorm_kernel<bf16_t>, dim3(grid), dim3(RW), 0, stream,
-                       static_cast<const bf16_t*>(x), g, static_cast<bf16_t*>(y), rows, d);
+  if (in_dtype == GENRANK_BF16 && out_dtype == GENRANK_BF16)
+    launch_rmsnorm_typed<bf16_t, bf16_t>(x, g, y, rows, d, stream);
+  else if (in_dtype == GENRANK_F32 && out_dtype == GENRANK_BF16)
+    launch_rmsnorm_typed<float, bf16_t>(x, g, y, rows, d, stream);
+  else if (in_dtype == GENRANK_F32 && out_dtype == GENRANK_F32)
+    launch_rmsnorm_typed<float, float>(x, g, y, rows, d, stream);
   else
-    hipLaunchKernelGGL(rmsnorm_kernel<float>, dim3(grid), dim3(RW), 0, stream,
-                       static_cast<const float*>(x), g, static_cast<float*>(y), rows, d);
+    return GENRANK_E_DTYPE;
   GR_CHECK_LAUNCH();
   return GENRANK_OK;
 }
 
 size_t rmsnorm_bwd_workspace(int d) { return static_cast<size_t>(PART_BLOCKS) * d * sizeof(float); }
 
-template <typename T>
-static int launch_rmsnorm_bwd_vec(const T* x, const float* g, const T* dy, const T* add, T* dx, float* part,
+template <typename TX, typename T>
+static int launch_rmsnorm_bwd_vec(const TX* x, const float* g, const T* dy, const T* add, T* dx, float* part,
                                   int64_t rows, int d, hipStream_t stream) {
   constexpr int VEC = 16 / static_cast<int>(sizeof(T));
   if (d % VEC != 0 || ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(dy) |
@@ -668,46 +677,45 @@ static int launch_rmsnorm_bwd_vec(const T* x, const float* g, const T* dy, const
     return grid;
   };
   switch (d / VEC) {
-    case 4: return go(rmsnorm_bwd_vec_kernel<T, 4, 1>, 4);
-    case 8: return go(rmsnorm_bwd_vec_kernel<T, 8, 1>, 8);
-    case 16: return go(rmsnorm_bwd_vec_kernel<T, 16, 1>, 16);
-    case 32: return go(rmsnorm_bwd_vec_kernel<T, 32, 1>, 32);
-    case 64: return go(rmsnorm_bwd_vec_kernel<T, 64, 1>, 64);
-    case 128: return go(rmsnorm_bwd_vec_kernel<T, 64, 2>, 64);
+    case 4: return go(rmsnorm_bwd_vec_kernel<TX, T, 4, 1>, 4);
+    case 8: return go(rmsnorm_bwd_vec_kernel<TX, T, 8, 1>, 8);
+    case 16: return go(rmsnorm_bwd_vec_kernel<TX, T, 16, 1>, 16);
+    case 32: return go(rmsnorm_bwd_vec_kernel<TX, T, 32, 1>, 32);
+    case 64: return go(rmsnorm_bwd_vec_kernel<TX, T, 64, 1>, 64);
+    case 128: return go(rmsnorm_bwd_vec_kernel<TX, T, 64, 2>, 64);
     default: return 0;
   }
 }
 
-genrank_status launch_rmsnorm_bwd(int dtype, const void* x, const float* g, const void* dy,
+template <typename TX, typename T>
+static int launch_rmsnorm_bwd_typed(const void* x, const float* g, const void* dy, const void* add, void* dx,
+                                    float* part, int64_t rows, int d, hipStream_t stream) {
+  const int vgrid = launch_rmsnorm_bwd_vec(static_cast<const TX*>(x), g, static_cast<const T*>(dy),
+                                           static_cast<const T*>(add), static_cast<T*>(dx), part, rows, d, stream);
+  if (vgrid > 0) return vgrid;
+  const unsigned grid = static_cast<unsigned>(std::min<int64_t>(PART_BLOCKS, (rows + 7) / 8));
+  hipLaunchKernelGGL((rmsnorm_bwd_kernel<TX, T>), dim3(grid), dim3(RW), 0, stream, static_cast<const TX*>(x), g,
+                     static_cast<const T*>(dy), static_cast<const T*>(add), static_cast<T*>(dx), part, rows, d);
+  return static_cast<int>(grid);
+}
+
+genrank_status launch_rmsnorm_bwd(int x_dtype, int dtype, const void* x, const float* g, const void* dy,
                                   const void* add, void* dx, float* dg, int64_t rows, int d, void* ws,
                                   hipStream_t stream) {
   if (d > 256 * MAXQ || d % 4) return GENRANK_E_SHAPE;
   float* part = static_cast<float*>(ws);
   if (rows <= 0) return launch_fill_f32(dg, d, 0.f, stream);
-  const int vgrid = dtype == GENRANK_BF16
-                        ? launch_rmsnorm_bwd_vec(static_cast<const bf16_t*>(x), g, static_cast<const bf16_t*>(dy),
-                                                 static_cast<const bf16_t*>(add), static_cast<bf16_t*>(dx), part,
-                                                 rows, d, stream)
-                        : launch_rmsnorm_bwd_vec(static_cast<const float*>(x), g, static_cast<const float*>(dy),
-                                                 static_cast<const float*>(add), static_cast<float*>(dx), part,
-                                                 rows, d, stream);
-  if (vgrid > 0) {
-    hipLaunchKernelGGL(column_sum_kernel, dim3((d + 15) / 16), dim3(256), 0, stream, part, vgrid, d, dg, d,
-                       nullptr, 0, nullptr);
-    GR_CHECK_LAUNCH();
-    return GENRANK_OK;
-  }
-  const unsigned grid = static_cast<unsigned>(std::min<int64_t>(PART_BLOCKS, (rows + 7) / 8));
-  if (dtype == GENRANK_BF16)
-    hipLaunchKernelGGL(rmsnorm_bwd_kernel<bf16_t>, dim3(grid), dim3(RW), 0, stream,
-                       static_cast<const bf16_t*>(x), g, static_cast<const bf16_t*>(dy),
-                       static_cast<const bf16_t*>(add), static_cast<bf16_t*>(dx), part, rows, d);
+  int grid;
+  if (x_dtype == GENRANK_BF16 && dtype == GENRANK_BF16)
+    grid = launch_rmsnorm_bwd_typed<bf16_t, bf16_t>(x, g, dy, add, dx, part, rows, d, stream);
+  else if (x_dtype == GENRANK_F32 && dtype == GENRANK_BF16)
+    grid = launch_rmsnorm_bwd_typed<float, bf16_t>(x, g, dy, add, dx, part, rows, d, stream);
+  else if (x_dtype == GENRANK_F32 && dtype == GENRANK_F32)
+    grid = launch_rmsnorm_bwd_typed<float, float>(x, g, dy, add, dx, part, rows, d, stream);
   else
-    hipLaunchKernelGGL(rmsnorm_bwd_kernel<float>, dim3(grid), dim3(RW), 0, stream,
-                       static_cast<const float*>(x), g, static_cast<const float*>(dy),
-                       static_cast<const float*>(add), static_cast<float*>(dx), part, rows, d);
-  hipLaunchKernelGGL(column_sum_kernel, dim3((d + 15) / 16), dim3(256), 0, stream, part,
-                     static_cast<int>(grid), d, dg, d, nullptr, 0, nullptr);
+    return GENRANK_E_DTYPE;
+  hipLaunchKernelGGL(column_sum_kernel, dim3((d + 15) / 16), dim3(256), 0, stream, part, grid, d, dg, d,
+                     nullptr, 0, nullptr);
   GR_CHECK_LAUNCH();
   return GENRANK_OK;
 }
@@ -781,9 +789,10 @@ size_t head_bwd_workspace(int d, int nt) {
   return static_cast<size_t>(HEAD_BLOCKS) * (static_cast<size_t>(d) * (1 + nt) + nt) * sizeof(float);
 }
 
-genrank_status launch_head_bwd(int dtype, const void* x, int64_t row0, int64_t rows, const int32_t* idx,
-                               int d, const float* g, const float* w, int nt, const float* dlogits,
-                               void* dx, float* dg, float* dw, float* db, void* ws, hipStream_t stream) {
+genrank_status launch_head_bwd(int x_dtype, int dtype, const void* x, int64_t row0, int64_t rows,
+                               const int32_t* idx, int d, const float* g, const float* w, int nt,
+                               const float* dlogits, void* dx, float* dg, float* dw, float* db, void* ws,
+                               hipStream_t stream) {
   if (d > 256 * MAXQ || d % 4 || nt > 4) return GENRANK_E_SHAPE;
   if (rows <= 0) {
     genrank_status st = launch_fill_f32(dg, d, 0.f, stream);
@@ -793,14 +802,20 @@ genrank_status launch_head_bwd(int dtype, const void* x, int64_t row0, int64_t r
   float* part = static_cast<float*>(ws);
   const int width = d * (1 + nt) + nt;
   const unsigned grid = static_cast<unsigned>(std::min<int64_t>(HEAD_BLOCKS, (rows + 3) / 4));
-  if (dtype == GENRANK_BF16)
-    hipLaunchKernelGGL(head_bwd_kernel<bf16_t>, dim3(grid), dim3(RW), 0, stream,
+  if (x_dtype == GENRANK_BF16 && dtype == GENRANK_BF16)
+    hipLaunchKernelGGL((head_bwd_kernel<bf16_t, bf16_t>), dim3(grid), dim3(RW), 0, stream,
                        static_cast<const bf16_t*>(x), row0, rows, idx, d, g, w, nt, dlogits,
                        static_cast<bf16_t*>(dx), part);
-  else
-    hipLaunchKernelGGL(head_bwd_kernel<float>, dim3(grid), dim3(RW), 0, stream,
+  else if (x_dtype == GENRANK_F32 && dtype == GENRANK_BF16)
+    hipLaunchKernelGGL((head_bwd_kernel<float, bf16_t>), dim3(grid), dim3(RW), 0, stream,
+                       static_cast<const float*>(x), row0, rows, idx, d, g, w, nt, dlogits,
+                       static_cast<bf16_t*>(dx), part);
+  else if (x_dtype == GENRANK_F32 && dtype == GENRANK_F32)
+    hipLaunchKernelGGL((head_bwd_kernel<float, float>), dim3(grid), dim3(RW), 0, stream,
                        static_cast<const float*>(x), row0, rows, idx, d, g, w, nt, dlogits,
                        static_cast<float*>(dx), part);
+  else
+    return GENRANK_E_DTYPE;
   hipLaunchKernelGGL(column_sum_kernel, dim3((width + 15) / 16), dim3(256), 0, stream, part,
                      static_cast<int>(grid), width, dg, d, dw, nt * d, db);
   GR_CHECK_LAUNCH();

@@ -17,7 +17,10 @@ from .device import DTYPE_CODE, TORCH_DTYPE, DeviceHead, DeviceLayer, DeviceTabl
 
 class GenRank:
     def __init__(self, tables: DeviceTables, layers: list, H: int, head: DeviceHead = None,
-                 device="cuda"):
+                 device="cuda", resid=None):
+        """resid: B.RESID_ACT or B.RESID_F32, the residual stream's element type; by default
+        f32 for a bf16 stack of pre-norm blocks (its residual sums are kept in f32, the
+        projections' operands in bf16), the activation dtype otherwise."""
         self.tables = tables
         self.layers = layers
         self.head = head
@@ -25,22 +28,27 @@ class GenRank:
         self.d = tables.d
         self.dtype = tables.dtype
         self.code = DTYPE_CODE[self.dtype]
+        prenorm = bool(layers) and all(lay.block == B.BLOCK_PRENORM for lay in layers)
+        if resid is None:
+            resid = B.RESID_F32 if (self.dtype == "bf16" and prenorm) else B.RESID_ACT
+        self.resid = resid
+        self.resid_code = B.F32 if resid == B.RESID_F32 else self.code
         self.device = device
         self._ws = {}
 
     @classmethod
     def from_host(cls, cfg, tables, weights, slopes_pos, slopes_time, device="cuda", attn_flags=0,
-                  time_bounds=None):
+                  time_bounds=None, resid=None):
         block = B.BLOCK_PRENORM if cfg.block == "prenorm" else B.BLOCK_ATTN_ONLY
         dt = DeviceTables(tables, device)
         layers = [DeviceLayer(lw, slopes_pos, slopes_time, block, device, attn_flags, time_bounds)
                   for lw in weights.layers]
         head = DeviceHead(weights, device) if cfg.block == "prenorm" else None
-        return cls(dt, layers, cfg.H, head, device)
+        return cls(dt, layers, cfg.H, head, device, resid)
 
     # ---------------------------------------------------------------- helpers
     def batch(self, inp) -> B.Batch:
-        return B.make_batch(inp.B, inp.m, self.d, self.H, inp.max_hist, inp.total_hist, self.code)
+        return B.make_batch(inp.B, inp.m, self.d, self.H, inp.max_hist, inp.total_hist, self.code, self.resid)
 
     def _buf(self, key, nbytes):
         t = self._ws.get(key)
@@ -50,7 +58,13 @@ class GenRank:
         return t
 
     def act(self, rows, cols=None):
+        """rows in the activation dtype (projection operands, gradients)"""
         return torch.empty((rows, cols or self.d), dtype=TORCH_DTYPE[self.dtype], device=self.device)
+
+    def resid_rows(self, rows):
+        """residual-stream rows (embedding output, block inputs and outputs)"""
+        dt = torch.float32 if self.resid == B.RESID_F32 else TORCH_DTYPE[self.dtype]
+        return torch.empty((rows, self.d), dtype=dt, device=self.device)
 
     # ---------------------------------------------------------------- forward
     def embed(self, inp, x_out, stream=None):
@@ -70,14 +84,14 @@ class GenRank:
         {"x": [T, d], "y": [T, d], "logits": [B*m, n_tasks]} tensors."""
         T = inp.rows
         bufs = bufs or {}
-        x = bufs.get("x") if bufs.get("x") is not None else self.act(T)
+        x = bufs.get("x") if bufs.get("x") is not None else self.resid_rows(T)
         self.embed(inp, x, stream)
         xs = [x]
         for i in range(len(self.layers)):
             if self.layers[i].block == B.BLOCK_ATTN_ONLY:
-                y = bufs.get("y") if bufs.get("y") is not None else self.act(T)
+                y = bufs.get("y") if bufs.get("y") is not None else self.resid_rows(T)
             else:
-                y = x if not save else self.act(T)
+                y = x if not save else self.resid_rows(T)
             self.layer(i, inp, x, y, save, stream)
             x = y
             xs.append(x)
@@ -100,8 +114,8 @@ class GenRank:
         projection (its history outputs are never read)."""
         T_h = inp.total_hist
         d = self.d
-        bh = B.make_batch(inp.B, 0, d, self.H, inp.max_hist, T_h, self.code)
-        x = self.act(T_h)
+        bh = B.make_batch(inp.B, 0, d, self.H, inp.max_hist, T_h, self.code, self.resid)
+        x = self.resid_rows(T_h)
         B.genrank_embed_sum(bh, inp.struct, self.tables.struct, x, stream)
         caches = []
         for i, lay in enumerate(self.layers):
@@ -110,7 +124,7 @@ class GenRank:
             B.genrank_layer_kv(bh, lay.struct, x, kv, 2 * d, self._buf(("kv", i), nb), nb, stream)
             caches.append(kv)
             if i + 1 < len(self.layers):
-                y = self.act(T_h)
+                y = self.resid_rows(T_h)
                 nf = B.genrank_workspace_size(B.OP_LAYER_FWD, bh, lay.struct)
                 B.genrank_layer_fwd(bh, lay.struct, inp.hist_offsets, inp.hist_ts, inp.req_ts, x, y, 0,
                                     self._buf(("prefill", i), nf), nf, stream)
@@ -123,17 +137,17 @@ class GenRank:
         bt = self.batch(inp)
         Tc = inp.B * inp.m
         d = self.d
-        x = self.act(Tc)
+        x = self.resid_rows(Tc)
         B.genrank_embed_sum_cand(bt, inp.struct, self.tables.struct, x, stream)
         for i, lay in enumerate(self.layers):
-            y = self.act(Tc) if lay.block == B.BLOCK_ATTN_ONLY else x
+            y = self.resid_rows(Tc) if lay.block == B.BLOCK_ATTN_ONLY else x
             nb = B.genrank_workspace_size(B.OP_LAYER_FWD_CACHED, bt, lay.struct)
             B.genrank_layer_fwd_cached(bt, lay.struct, inp.hist_offsets, inp.hist_ts, inp.req_ts, caches[i],
                                        2 * d, x, y, self._buf(("cached", i), nb), nb, stream)
             x = y
         logits = None
         if self.head is not None:
-            bc = B.make_batch(inp.B, inp.m, d, self.H, 0, 0, self.code)  # candidate rows only
+            bc = B.make_batch(inp.B, inp.m, d, self.H, 0, 0, self.code, self.resid)  # candidate rows only
             logits = torch.empty((Tc, self.head.n_tasks), dtype=torch.float32, device=self.device)
             B.genrank_head_fwd(bc, x, self.head.g_final, self.head.w_head, self.head.b_head, self.head.n_tasks,
                                logits, stream)
@@ -161,7 +175,7 @@ class GenRank:
             n = int(rows.numel())
             labels = torch.cat([labels, hist_labels])
             logits = torch.empty((n, nt), dtype=torch.float32, device=dev)
-            B.genrank_head_fwd_rows(self.code, d, x_final, n, rows, self.head.g_final, self.head.w_head,
+            B.genrank_head_fwd_rows(self.resid_code, d, x_final, n, rows, self.head.g_final, self.head.w_head,
                                     self.head.b_head, nt, logits, stream)
         loss = torch.empty(1, dtype=torch.float32, device=dev)
         dlogits = torch.empty((n, nt), dtype=torch.float32, device=dev)
@@ -174,7 +188,7 @@ class GenRank:
                                grads["g_final"], grads["w_head"], grads["b_head"],
                                self._buf(("head_bwd",), nwh), nwh, stream)
         else:
-            B.genrank_head_bwd_rows(self.code, d, inp.rows, x_final, n, rows, self.head.g_final,
+            B.genrank_head_bwd_rows(self.resid_code, self.code, d, inp.rows, x_final, n, rows, self.head.g_final,
                                     self.head.w_head, nt, dlogits, dx, grads["g_final"], grads["w_head"],
                                     grads["b_head"], self._buf(("head_bwd",), nwh), nwh, stream)
         grads["layers"] = [None] * len(self.layers)

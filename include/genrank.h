@@ -85,7 +85,23 @@ typedef enum {
 } genrank_op;
 
 /* Batch geometry.  total_hist and max_hist are host copies of hist_offsets[B] and
- * max_u N_u so that no device-to-host copy is needed; they must match the device data. */
+ * max_u N_u so that no device-to-host copy is needed; they must match the device data.
+ *
+ * resid chooses the element type of the residual stream: the rows genrank_embed_sum /
+ * genrank_embed_sum_cand write, the block inputs and outputs of genrank_layer_fwd,
+ * genrank_layer_kv and genrank_layer_fwd_cached, the block input genrank_layer_bwd reads,
+ * and the rows genrank_head_fwd / genrank_head_bwd read.
+ *   GENRANK_RESID_ACT (0): the residual stream is in `dtype`;
+ *   GENRANK_RESID_F32 (1): it is f32 while the projections' operands (normalised rows, Q/K/V,
+ *     attention output, FFN hidden) stay in `dtype`.  This is mixed precision in the sense
+ *     of "一、 GenRank [2025]" section 1.3 (training setup): bf16 products with f32
+ *     accumulation, and each residual sum kept in f32 instead of being rounded to bf16 after
+ *     every block.  Pre-norm blocks only (an attention-only block's input is its QKV
+ *     operand): genrank_layer_* return GENRANK_E_DTYPE for it.
+ * Gradients of the residual stream (dy, dx of genrank_layer_bwd, genrank_head_bwd's dx and
+ * genrank_embed_bwd's dx) are in `dtype` either way. */
+#define GENRANK_RESID_ACT 0
+#define GENRANK_RESID_F32 1
 typedef struct {
   int32_t B;          /* users, >= 1 */
   int32_t m;          /* candidates per user, >= 0 */
@@ -95,7 +111,7 @@ typedef struct {
   int32_t max_hist;   /* max_u N_u */
   int64_t total_hist; /* T_h = sum_u N_u */
   int32_t dtype;      /* genrank_dtype of activations and embedding tables */
-  int32_t reserved;
+  int32_t resid;      /* GENRANK_RESID_ACT or GENRANK_RESID_F32 (see above) */
 } genrank_batch;
 
 /* Per-user chronological histories and the candidates of one request
@@ -207,8 +223,9 @@ GENRANK_API genrank_status genrank_validate_host(const genrank_batch* batch, con
  *   prefix is the whole history plus its request), slot min(ri-1, n_ri-1);
  *   gap = t - (largest earlier distinct timestamp), bucket #{k: rt_bounds[k] <= gap},
  *   0 when there is no earlier request.
- * The five rows are summed in f32 and stored once in batch.dtype.
- * x_out: [T, d] in batch.dtype.  d must be a multiple of 8 (bf16) / 4 (f32). */
+ * The five rows are summed in f32 and stored once in the residual stream's type.
+ * x_out: [T, d] in batch.dtype, or f32 with batch.resid == GENRANK_RESID_F32.  d must be a
+ * multiple of 8 (bf16) / 4 (f32). */
 GENRANK_API genrank_status genrank_embed_sum(const genrank_batch* batch, const genrank_inputs* in,
                                  const genrank_tables* tables, void* x_out,
                                  genrank_stream_t stream);
@@ -257,12 +274,14 @@ GENRANK_API genrank_status genrank_attn_bwd(const genrank_batch* batch, const in
 /* One block forward (see genrank_layer_weights for the two block forms): the dense
  * projections (QKV, output, FFN) as bf16 MFMA GEMMs with fused residual / SiLU
  * epilogues, RMSNorm, and genrank_attn_fwd between them.
- * x_in, y_out: [T, d] in batch.dtype; y_out may equal x_in (inference only: the backward
- * needs the block input).  ws: genrank_workspace_size(GENRANK_OP_LAYER_FWD) bytes.
+ * x_in, y_out: [T, d] residual-stream rows (batch.dtype, or f32 with GENRANK_RESID_F32: the
+ * residual sums are then formed and stored in f32 and only the projections' operands are
+ * rounded to batch.dtype); y_out may equal x_in (inference only: the backward needs the block
+ * input).  ws: genrank_workspace_size(GENRANK_OP_LAYER_FWD) bytes.
  * flags: GENRANK_FWD_SAVE makes the workspace keep every activation genrank_layer_bwd
  * needs (keep it untouched until then); without it the FFN pre-activation is not stored.
- * Without GENRANK_FWD_SAVE, a bf16 pre-norm block with d >= 512, d % 256 == 0 and
- * ffn_dim % 256 == 0 fuses each RMSNorm into the GEMM that reads it: rows are scaled by
+ * Without GENRANK_FWD_SAVE, a bf16 pre-norm block with a bf16 residual stream, d >= 512,
+ * d % 256 == 0 and ffn_dim % 256 == 0 fuses each RMSNorm into the GEMM that reads it: rows are scaled by
  * their 1/rms after the product with the gain-scaled weight, so the normalised rows are
  * never stored and the result differs from the saving forward by bf16 rounding only.
  * genrank_layer_kv and genrank_layer_fwd_cached take the same path under the same
@@ -274,8 +293,9 @@ GENRANK_API genrank_status genrank_layer_fwd(const genrank_batch* batch, const g
                                  int32_t flags, void* ws, size_t ws_bytes,
                                  genrank_stream_t stream);
 
-/* Backward of one block.  x_in is the block's forward input, ws the workspace the
- * forward filled; dy: [T, d] gradient of the block output; dx: [T, d] (may equal dy).
+/* Backward of one block.  x_in is the block's forward input (residual-stream rows), ws the
+ * workspace the forward filled; dy: [T, d] gradient of the block output in batch.dtype; dx:
+ * [T, d] in batch.dtype (may equal dy).
  * ws_bwd: genrank_workspace_size(GENRANK_OP_LAYER_BWD) bytes.  Gradients are f32. */
 GENRANK_API genrank_status genrank_layer_bwd(const genrank_batch* batch, const genrank_layer_weights* w,
                                  const int32_t* hist_offsets, const int64_t* hist_ts,
@@ -289,12 +309,16 @@ GENRANK_API genrank_status genrank_layer_bwd(const genrank_batch* batch, const g
  *   GENRANK_EPI_NONE:     y = acc
  *   GENRANK_EPI_RESIDUAL: y = acc + residual   (residual [M, ldr], may equal y)
  *   GENRANK_EPI_SILU:     y = silu(acc), and pre = acc when pre is not NULL.
+ *   GENRANK_EPI_RESIDUAL_F32: y = acc + residual with y and residual f32 (an f32 residual
+ *                         stream, see genrank_batch.resid; ldy and ldr multiples of 4, y and
+ *                         residual 16-byte aligned on the MFMA path).
  * bf16 runs on MFMA when N % 128 == 0, K % 32 == 0 and the leading dimensions are
  * multiples of 8 (K % 128 == 0 takes the kernel that streams operands straight into LDS);
  * other shapes and f32 use a plain tiled kernel.  Rows of y past M are not written. */
 #define GENRANK_EPI_NONE 0
 #define GENRANK_EPI_RESIDUAL 1
 #define GENRANK_EPI_SILU 2
+#define GENRANK_EPI_RESIDUAL_F32 3
 GENRANK_API genrank_status genrank_linear(int32_t dtype, const void* x, int64_t ldx, const void* w,
                                           int64_t ldw, void* y, int64_t ldy, int64_t M, int32_t N,
                                           int32_t K, int32_t epilogue, const void* residual,
@@ -323,14 +347,15 @@ GENRANK_API genrank_status genrank_linear_bwd(int32_t dtype, const void* x, int6
 
 /* Per-candidate action logits ([GR-zh] section 1.2: predictions for a set of predefined
  * tasks): logits[c, t] = (rmsnorm(x[T_h + c]) * g_final) . w_head[t] + b_head[t].
- * x: [T, d] in batch.dtype; g_final [d], w_head [n_tasks, d], b_head [n_tasks] f32;
+ * x: [T, d] residual-stream rows (batch.dtype, or f32 with GENRANK_RESID_F32); g_final [d],
+ * w_head [n_tasks, d], b_head [n_tasks] f32;
  * logits: [B*m, n_tasks] f32.  n_tasks in 1..8. */
 GENRANK_API genrank_status genrank_head_fwd(const genrank_batch* batch, const void* x, const float* g_final,
                                 const float* w_head, const float* b_head, int32_t n_tasks,
                                 float* logits, genrank_stream_t stream);
 
-/* Backward of genrank_head_fwd.  dx: [T, d] in batch.dtype; history rows are set to
- * zero (the loss is taken at candidate positions only, [GR-zh] section 1.3.1).
+/* Backward of genrank_head_fwd.  x as genrank_head_fwd; dx: [T, d] in batch.dtype; history rows
+ * are set to zero (the loss is taken at candidate positions only, [GR-zh] section 1.3.1).
  * dg_final [d], dw_head [n_tasks, d], db_head [n_tasks]: f32, overwritten; they are sums over
  * the candidate rows formed in a fixed order (per-block partials in ws, then summed), so
  * the result does not depend on scheduling.  ws: genrank_workspace_size(GENRANK_OP_HEAD_BWD)
@@ -352,14 +377,16 @@ GENRANK_API genrank_status genrank_head_fwd_rows(int32_t dtype, int32_t d, const
                                      const float* b_head, int32_t n_tasks, float* logits,
                                      genrank_stream_t stream);
 
-/* Backward of genrank_head_fwd_rows.  dx: [n_x_rows, d] in dtype, overwritten: each listed
+/* Backward of genrank_head_fwd_rows.  x: [n_x_rows, d] in x_dtype (dtype, or GENRANK_F32 for an
+ * f32 residual stream); dx: [n_x_rows, d] in dtype, overwritten: each listed
  * row gets the head's gradient, every other row zero.  The rows must be distinct (a
  * repeated row gets one of its gradients, not their sum).  dg_final, dw_head, db_head: as
  * genrank_head_bwd (f32, overwritten, fixed summation order).  ws: at least
  * genrank_workspace_size(GENRANK_OP_HEAD_BWD) of a batch with the same d.  Errors as
  * genrank_head_fwd_rows, plus n_tasks > 4 or d > 1024 or d % 4 != 0 -> GENRANK_E_SHAPE and
  * GENRANK_E_WORKSPACE. */
-GENRANK_API genrank_status genrank_head_bwd_rows(int32_t dtype, int32_t d, int64_t n_x_rows, const void* x,
+GENRANK_API genrank_status genrank_head_bwd_rows(int32_t x_dtype, int32_t dtype, int32_t d, int64_t n_x_rows,
+                                     const void* x,
                                      int64_t n_rows, const int32_t* rows, const float* g_final,
                                      const float* w_head, int32_t n_tasks, const float* dlogits, void* dx,
                                      float* dg_final, float* dw_head, float* db_head, void* ws,
@@ -382,6 +409,7 @@ GENRANK_API genrank_status genrank_bce_loss(int64_t n, int32_t n_tasks, const fl
  *     zero where no row maps.
  * The rows are grouped by slot with a radix sort and each group is summed in ascending row
  * order (no atomics): the result does not depend on scheduling.  5 T must be below 2^31.
+ * dx is in batch.dtype whatever batch.resid says.
  * ws: genrank_workspace_size(GENRANK_OP_EMBED_BWD) bytes. */
 GENRANK_API genrank_status genrank_embed_bwd(const genrank_batch* batch, const genrank_inputs* in,
                                              const genrank_tables* tables, const void* dx,
@@ -400,7 +428,8 @@ GENRANK_API genrank_status genrank_embed_bwd(const genrank_batch* batch, const g
  * values in [d, 2d), head h at h * dh in each; rows in the batch's history order.
  * bf16 with dh == 64 for the attention. */
 
-/* genrank_embed_sum for the candidate rows only: x_cand [B*m, d], row u*m + k. */
+/* genrank_embed_sum for the candidate rows only: x_cand [B*m, d] (residual-stream type), row
+ * u*m + k. */
 GENRANK_API genrank_status genrank_embed_sum_cand(const genrank_batch* batch, const genrank_inputs* in,
                                                   const genrank_tables* tables, void* x_cand,
                                                   genrank_stream_t stream);
@@ -417,14 +446,14 @@ GENRANK_API genrank_status genrank_attn_fwd_cached(const genrank_batch* batch, c
                                                    float* lse, genrank_stream_t stream);
 
 /* A block's history keys and values: kv [T_h, ld_kv] (see above) from the block's input on
- * the history rows, x_hist [T_h, d] (the top block needs nothing else of the history: its
+ * the history rows, x_hist [T_h, d] residual-stream rows (the top block needs nothing else of the history: its
  * history outputs are never read).  ws: genrank_workspace_size(GENRANK_OP_LAYER_KV). */
 GENRANK_API genrank_status genrank_layer_kv(const genrank_batch* batch, const genrank_layer_weights* w,
                                             const void* x_hist, void* kv, int64_t ld_kv, void* ws,
                                             size_t ws_bytes, genrank_stream_t stream);
 
-/* genrank_layer_fwd on the candidate rows only: x_cand, y_cand [B*m, d] (equal only for
- * GENRANK_BLOCK_PRENORM), history keys and values from kv_hist ([T_h, ld_kv]).
+/* genrank_layer_fwd on the candidate rows only: x_cand, y_cand [B*m, d] residual-stream rows
+ * (equal only for GENRANK_BLOCK_PRENORM), history keys and values from kv_hist ([T_h, ld_kv]).
  * ws: genrank_workspace_size(GENRANK_OP_LAYER_FWD_CACHED). */
 GENRANK_API genrank_status genrank_layer_fwd_cached(const genrank_batch* batch, const genrank_layer_weights* w,
                                                     const int32_t* hist_offsets, const int64_t* hist_ts,

@@ -392,38 +392,50 @@ def _identity(t):
     return t
 
 
+def _stored(store, name):
+    """The storage model of one named tensor: ``store`` is None (exact), one callable for
+    every tensor, or a dict from tensor name to callable (names missing from it are exact)."""
+    if store is None:
+        return _identity
+    if callable(store):
+        return store
+    return store.get(name, _identity)
+
+
 def layer_fwd(x, lw, block, H, geom, store=None):
     """One block.  ``lw``: dict with wqkv [3d, d], wo [d, d], and for the pre-norm block
     w1 [f d, d], w2 [d, f d], g1, g2.  ``geom``: dict with hist_offsets, m, pos, tau,
     slopes_pos, slopes_time.  Returns (y, cache).
 
     ``store`` (default: none) is applied to every intermediate tensor that an
-    implementation holds in memory between two operations: the normalised input, Q/K/V,
-    the attention output, the residual sum, the FFN hidden activation and the output.
-    With ``store=round_bf16`` this is the same computation with those tensors kept in
-    bf16, which measures the error that bf16 storage alone brings."""
-    S = store or _identity
+    implementation holds in memory between two operations: the normalised input "z",
+    "qkv", the attention output "o", the residual sum "x1", the FFN hidden activation "hdn"
+    (and "z2", its normalised input) and the output "y".  With ``store=round_bf16`` this is
+    the same computation with those tensors kept in bf16, which measures the error that bf16
+    storage alone brings; a dict {name: callable} models tensors kept in different types
+    (say the residual sums in f32 and the rest in bf16)."""
+    S = lambda name, t: _stored(store, name)(t)
     x = np.asarray(x, np.float64)
     d = x.shape[1]
     wqkv = np.asarray(lw["wqkv"], np.float64)
     wo = np.asarray(lw["wo"], np.float64)
     cache = {"x": x}
-    z = S(rmsnorm(x, lw["g1"])) if block == "prenorm" else x
-    qkv = S(z @ wqkv.T)
+    z = S("z", rmsnorm(x, lw["g1"])) if block == "prenorm" else x
+    qkv = S("qkv", z @ wqkv.T)
     q, k, v = (_split_heads(qkv[:, i * d:(i + 1) * d], H) for i in range(3))
     o, _ = attn_fwd(q, k, v, geom["hist_offsets"], geom["m"], geom["pos"], geom["tau"],
                     geom["slopes_pos"], geom["slopes_time"], history=geom.get("history", "causal"),
                     time_bounds=geom.get("time_bounds"))
-    o2 = S(o.reshape(o.shape[0], d))
+    o2 = S("o", o.reshape(o.shape[0], d))
     attn_out = o2 @ wo.T
     cache.update(z=z, q=q, k=k, v=v, o=o2)
     if block == "attn_only":
-        return S(attn_out), cache
-    x1 = S(x + attn_out)
-    z2 = S(rmsnorm(x1, lw["g2"]))
+        return S("y", attn_out), cache
+    x1 = S("x1", x + attn_out)
+    z2 = S("z2", rmsnorm(x1, lw["g2"]))
     a = z2 @ np.asarray(lw["w1"], np.float64).T
-    hdn = S(silu(a))
-    y = S(x1 + hdn @ np.asarray(lw["w2"], np.float64).T)
+    hdn = S("hdn", silu(a))
+    y = S("y", x1 + hdn @ np.asarray(lw["w2"], np.float64).T)
     cache.update(x1=x1, z2=z2, a=a, hdn=hdn)
     return y, cache
 
@@ -509,8 +521,8 @@ def _loss_rows(geom, n_rows, loss_rows):
 def model_fwd(x0, layers, block, H, geom, head=None, store=None, loss_rows=None):
     """Embedded rows -> stacked blocks -> (optional) head at the loss rows (candidate rows
     unless ``loss_rows`` lists others).  Returns (x_final, logits or None, caches).
-    ``store``: as in ``layer_fwd``, also applied to the embedded rows."""
-    x = (store or _identity)(np.asarray(x0, np.float64))
+    ``store``: as in ``layer_fwd``, also applied to the embedded rows ("x0")."""
+    x = _stored(store, "x0")(np.asarray(x0, np.float64))
     caches = []
     for lw in layers:
         x, c = layer_fwd(x, lw, block, H, geom, store)

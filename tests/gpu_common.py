@@ -80,6 +80,17 @@ def unit_close(got, want, name="", tol=2e-2):
     assert e <= tol, (name, e)
 
 
+def f32_resid_store(store_ops=None):
+    """The storage model of a bf16 stack with an f32 residual stream: the projections'
+    operands (normalised rows, Q/K/V, attention output, FFN hidden) rounded to bf16, the
+    residual rows (embedding sums, mid-block sums, block outputs) to f32."""
+    rb = store_ops or oracle.round_bf16
+    f32 = lambda t: np.asarray(t, np.float64).astype(np.float32).astype(np.float64)
+    d = {k: rb for k in ("z", "qkv", "o", "z2", "hdn")}
+    d.update({k: f32 for k in ("x0", "x1", "y")})
+    return d
+
+
 def random_qkv(T, d, dtype, seed, std=1.0):
     """Seeded Q, K, V [T, 3d] in storage form plus their float64 values."""
     st = synth.inputs.normal_array((T, 3 * d), std=std, seed=seed, dtype=dtype)

@@ -132,10 +132,25 @@ def test_entry_points_reject_bad_arguments(lib):
     assert lib.genrank_head_fwd_rows(7, 256, FAKE, 4, FAKE, FAKE, FAKE, FAKE, 4, FAKE, None) == -3
     assert lib.genrank_head_fwd_rows(B.BF16, 256, FAKE, 4, None, FAKE, FAKE, FAKE, 4, FAKE, None) == -1
     assert lib.genrank_head_fwd_rows(B.BF16, 256, FAKE, 4, FAKE, FAKE, FAKE, FAKE, 9, FAKE, None) == -2
-    assert lib.genrank_head_bwd_rows(B.BF16, 256, 10, FAKE, 4, FAKE, FAKE, FAKE, 4, FAKE, FAKE, FAKE, FAKE,
-                                     FAKE, FAKE, 16, None) == -6
-    assert lib.genrank_head_bwd_rows(B.BF16, 256, 10, FAKE, 4, FAKE, FAKE, FAKE, 5, FAKE, FAKE, FAKE, FAKE,
-                                     FAKE, FAKE, 1 << 30, None) == -2
+    assert lib.genrank_head_bwd_rows(B.BF16, B.BF16, 256, 10, FAKE, 4, FAKE, FAKE, FAKE, 4, FAKE, FAKE, FAKE,
+                                     FAKE, FAKE, FAKE, 16, None) == -6
+    assert lib.genrank_head_bwd_rows(B.BF16, B.BF16, 256, 10, FAKE, 4, FAKE, FAKE, FAKE, 5, FAKE, FAKE, FAKE,
+                                     FAKE, FAKE, FAKE, 1 << 30, None) == -2
+    # rows of an f32 residual stream with bf16 gradients are accepted; bf16 rows with f32
+    # gradients are not
+    assert lib.genrank_head_bwd_rows(B.F32, B.BF16, 256, 10, FAKE, 4, FAKE, FAKE, FAKE, 4, FAKE, FAKE, FAKE,
+                                     FAKE, FAKE, FAKE, 16, None) == -6
+    assert lib.genrank_head_bwd_rows(B.BF16, B.F32, 256, 10, FAKE, 4, FAKE, FAKE, FAKE, 4, FAKE, FAKE, FAKE,
+                                     FAKE, FAKE, FAKE, 1 << 30, None) == -3
+    # the residual-stream field: unknown values, and an f32 stream under an attention-only block
+    bad = _batch()
+    bad.resid = 2
+    n = ctypes.c_size_t(0)
+    assert lib.genrank_workspace_size(B.OP_ATTN_BWD, ctypes.byref(bad), None, ctypes.byref(n)) == -3
+    rf = _batch()
+    rf.resid = B.RESID_F32
+    assert lib.genrank_layer_fwd(ctypes.byref(rf), ctypes.byref(w), FAKE, FAKE, FAKE, FAKE, FAKE + 64,
+                                 0, FAKE, 1 << 40, None) == -3
     assert lib.genrank_bce_loss(0, 4, FAKE, FAKE, FAKE, FAKE, None) == -1
     assert lib.genrank_debug_mask(ctypes.byref(bt), FAKE, 2, 10, FAKE, None) == -1  # user >= B
 

@@ -15,8 +15,8 @@ import torch
 import oracle
 import synth
 from common import oracle_geom, oracle_head, oracle_indices, oracle_layers, oracle_slopes, oracle_tables
-from gpu_common import (DEV, DeviceInputs, GenRank, batch_struct, bf16_close, custom_batch, gpu_slopes,
-                        random_qkv, say, tables_for, to_numpy, unit_close)
+from gpu_common import (DEV, DeviceInputs, GenRank, batch_struct, bf16_close, custom_batch, f32_resid_store,
+                        gpu_slopes, random_qkv, say, tables_for, to_numpy, unit_close)
 from generative_ranking_recommendation_amd import binding as B
 from generative_ranking_recommendation_amd.device import stored_to_device, to_device
 
@@ -191,10 +191,10 @@ def test_train_step_bf16_full_size():
     batch: every block, head and table gradient (the weight gradients are sums over all
     users, so the whole batch is compared, not a sample), the loss, and the 16,384 logits.
 
-    Over this many unit-scale logits, bf16 storage rounding alone (the oracle with every
-    intermediate tensor rounded to bf16) brings the largest error near the 2e-2 bar, as
-    on the 4-layer stack.  So the logits are held to the stack's bars: rms within 1.25x of
-    the storage-only error and max within max(2e-2, 1.5x the storage-only max)."""
+    The logits are held to 2e-2 absolute (the stack's residual stream is f32, its
+    projections' operands bf16); the kernels' rms error must also stay within 1.25x of the
+    same computation's storage-only error (bf16 operands, f32 residual rows, exact
+    arithmetic otherwise)."""
     say("bwd: train step bf16 full train2 batch")
     cfg = synth.make_config("train2_bf16")
     batch = synth.make_batch(cfg)
@@ -205,14 +205,14 @@ def test_train_step_bf16_full_size():
     idx = oracle_indices(cfg, batch, tables)
     x0 = oracle.embed_sum(oracle_tables(tables), batch.hist_items, batch.cand_items, idx)
     _, slog, _ = oracle.model_fwd(x0, oracle_layers(weights), cfg.block, cfg.H, oracle_geom(cfg, batch, idx),
-                                  oracle_head(weights), store=oracle.round_bf16)
+                                  oracle_head(weights), store=f32_resid_store())
     glog = to_numpy(glog)
     rms = lambda e: float(np.sqrt(np.mean(np.square(e))))
     e_gpu, e_store = glog - wlog, slog - wlog
     say(f"  logits: gpu rms {rms(e_gpu):.4f} max {np.abs(e_gpu).max():.4f}; "
-        f"bf16 storage alone rms {rms(e_store):.4f} max {np.abs(e_store).max():.4f}")
+        f"storage alone rms {rms(e_store):.4f} max {np.abs(e_store).max():.4f}")
     assert rms(e_gpu) <= 1.25 * rms(e_store), (rms(e_gpu), rms(e_store))
-    unit_close(glog, wlog, "logits", tol=max(2e-2, 1.5 * float(np.abs(e_store).max())))
+    unit_close(glog, wlog, "logits", tol=2e-2)
     unit_close([float(gl.item())], [wl], "loss")
     for k in ("w_head", "b_head", "g_final"):
         bf16_close(to_numpy(grads[k]), whg[k], k)

@@ -99,6 +99,36 @@ def test_embed_sum_bf16_infer_subset():
     assert rel_err(got, want) <= 2e-2
 
 
+@pytest.mark.parametrize("name,B_", [("stack4_bf16", 5), ("infer_1layer_bf16", 9)])
+def test_embed_sum_bf16_tables_f32_rows(name, B_):
+    """bf16 tables summed into f32 rows (the f32 residual stream of the pre-norm stacks):
+    no bf16 rounding of the sum, so each element is within the f32 summation bound of five
+    terms (4 roundings of at most 2^-24 of the partial sums) of the float64 sum; candidates'
+    rows and their whole-history request index included."""
+    say(f"embed: bf16 tables, f32 rows, {name} ({B_} users)")
+    cfg = synth.make_config(name)
+    batch = synth.make_batch(cfg, B=B_)
+    tables = tables_for(name)
+    inp = DeviceInputs(batch, DEV)
+    tab = DeviceTables(tables, DEV)
+    bt = B.make_batch(inp.B, inp.m, cfg.d, cfg.H, inp.max_hist, inp.total_hist, B.BF16, B.RESID_F32)
+    x = torch.full((inp.rows, cfg.d), float("nan"), dtype=torch.float32, device=DEV)
+    B.genrank_embed_sum(bt, inp.struct, tab.struct, x)
+    xc = torch.full((inp.B * inp.m, cfg.d), float("nan"), dtype=torch.float32, device=DEV)
+    B.genrank_embed_sum_cand(bt, inp.struct, tab.struct, xc)
+    torch.cuda.synchronize()
+    got = x.cpu().numpy().astype(np.float64)
+    idx = oracle_indices(cfg, batch, tables)
+    want = oracle.embed_sum(oracle_tables(tables), batch.hist_items, batch.cand_items, idx)
+    t = oracle_tables(tables)
+    items = np.concatenate([batch.hist_items, batch.cand_items]).astype(np.int64)
+    mag = sum(np.abs(np.asarray(t[k][ids], np.float64)) for k, ids in
+              (("item", items), ("action", idx["act"]), ("pos", idx["pe"]), ("ri", idx["ri_slot"]), ("rt", idx["rt"])))
+    assert np.all(np.abs(got - want) <= 4 * 2.0 ** -24 * mag + 1e-12)
+    # the candidate-only gather writes the same bits as the candidate rows of the full one
+    assert np.array_equal(xc.cpu().numpy(), x[inp.total_hist:].cpu().numpy())
+
+
 def test_embed_sum_full_size_sampled():
     """Full infer_1layer_bf16 batch (256 users), as the benchmark runs it; rows of 6 users
     checked against the oracle (users are independent)."""

@@ -1,7 +1,8 @@
 """GPU parity of the block forward (embed -> QKV -> attention -> output projection [-> FFN])
 and the action head, through the same GenRank model wrapper the benchmark drives.
 
-Bars: f32 <= 1e-5 absolute; bf16 logits (unit-scale) <= 2e-2 absolute; bf16 hidden states
+Bars: f32 <= 1e-5 absolute; bf16 logits (unit-scale) <= 2e-2 absolute (the pre-norm stacks keep
+their residual stream in f32, the projections' operands in bf16); bf16 hidden states
 (scale ~1e-3 with N(0, 0.02) weights) by ``bf16_close``: norm-wise <= 1e-2 and max error
 <= 2e-2 of the tensor's largest magnitude."""
 import numpy as np
@@ -11,8 +12,8 @@ import torch
 import oracle
 import synth
 from common import oracle_geom, oracle_head, oracle_indices, oracle_layers, oracle_tables
-from gpu_common import (DEV, DeviceInputs, GenRank, bf16_close, custom_batch, gpu_slopes, say, tables_for,
-                        to_numpy, unit_close)
+from gpu_common import (DEV, DeviceInputs, GenRank, bf16_close, custom_batch, f32_resid_store, gpu_slopes, say,
+                        tables_for, to_numpy, unit_close)
 
 pytestmark = pytest.mark.gpu
 
@@ -72,14 +73,10 @@ def test_layer_bf16_infer_subset():
 
 def test_stack_bf16_small_batch():
     """stack4_bf16 shapes (4 pre-norm layers, d = 512, 8 heads, FFN 4x, head of 4 logits)
-    on 3 users with jagged lengths.
-
-    Four bf16 blocks put the logits' error at the 2e-2 bar by storage alone: the oracle
-    with every intermediate tensor rounded to bf16 (and exact arithmetic otherwise) is
-    off by 0.0057 rms and 0.0176 at most over these 480 logits, and which elements round
-    which way decides the maximum.  So the kernels are held to (a) an rms error within
-    1.25x of that storage-only error, and (b) a maximum within max(2e-2, 1.5x the
-    storage-only maximum)."""
+    on 3 users with jagged lengths, with the stack's f32 residual stream: logits within
+    2e-2 of the exact oracle.  The error of the same computation with the stack's storage
+    (bf16 operands, f32 residual rows) and exact arithmetic otherwise is printed beside it,
+    and the kernels' rms error must stay within 1.25x of it."""
     say("layer: bf16 stack4 small batch")
     cfg = synth.make_config("stack4_bf16", m=40)
     batch = custom_batch(cfg, [480, 123, 7], seed=4)
@@ -87,14 +84,14 @@ def test_stack_bf16_small_batch():
     weights = synth.make_weights(cfg)
     gy, gl = _gpu_forward(cfg, batch, tables, weights)
     wy, wl = _oracle_forward(cfg, batch, tables, weights)
-    _, sl = _oracle_forward(cfg, batch, tables, weights, store=oracle.round_bf16)
+    _, sl = _oracle_forward(cfg, batch, tables, weights, store=f32_resid_store())
     assert np.std(wl) > 0.3  # the logits are unit-scale
     rms = lambda e: float(np.sqrt(np.mean(np.square(e))))
     e_gpu, e_store = gl - wl, sl - wl
     say(f"  logits: gpu rms {rms(e_gpu):.4f} max {np.abs(e_gpu).max():.4f}; "
-        f"bf16 storage alone rms {rms(e_store):.4f} max {np.abs(e_store).max():.4f}")
+        f"storage alone rms {rms(e_store):.4f} max {np.abs(e_store).max():.4f}")
     assert rms(e_gpu) <= 1.25 * rms(e_store), (rms(e_gpu), rms(e_store))
-    unit_close(gl, wl, "logits", tol=max(2e-2, 1.5 * float(np.abs(e_store).max())))
+    unit_close(gl, wl, "logits", tol=2e-2)
     bf16_close(gy, wy, "final hidden state")
 
 
@@ -120,8 +117,7 @@ def test_stack_bf16_full_size_sampled():
     376,832 rows, d = 512) in the launches the benchmark runs (the 256 x 256-tile
     projections included); 3 users' logits and final hidden states checked against the
     oracle on those users alone (users are independent).  Logit bars as for the small
-    stack batch: rms within 1.25x of the bf16-storage-only error, max within
-    max(2e-2, 1.5x the storage-only max)."""
+    stack batch: max error 2e-2, rms within 1.25x of the storage-only error."""
     say("layer: bf16 stack4 full batch, sampled users")
     cfg = synth.make_config("stack4_bf16")
     batch = synth.make_batch(cfg)
@@ -142,12 +138,12 @@ def test_stack_bf16_full_size_sampled():
     sub = batch.subset(users)
     c = cfg.replace(B=len(users))
     wy, wl = _oracle_forward(c, sub, tables, weights)
-    _, sl = _oracle_forward(c, sub, tables, weights, store=oracle.round_bf16)
+    _, sl = _oracle_forward(c, sub, tables, weights, store=f32_resid_store())
     rms = lambda e: float(np.sqrt(np.mean(np.square(e))))
     e_gpu, e_store = gl - wl, sl - wl
     say(f"  logits: gpu rms {rms(e_gpu):.4f} max {np.abs(e_gpu).max():.4f}; "
-        f"bf16 storage alone rms {rms(e_store):.4f} max {np.abs(e_store).max():.4f}")
+        f"storage alone rms {rms(e_store):.4f} max {np.abs(e_store).max():.4f}")
     assert rms(e_gpu) <= 1.25 * rms(e_store), (rms(e_gpu), rms(e_store))
-    unit_close(gl, wl, "logits", tol=max(2e-2, 1.5 * float(np.abs(e_store).max())))
+    unit_close(gl, wl, "logits", tol=2e-2)
     sub_rows = np.concatenate([oracle.user_rows(sub.hist_offsets, cfg.m, i) for i in range(len(users))])
     bf16_close(gy, wy[sub_rows], "final hidden state (sampled users)")

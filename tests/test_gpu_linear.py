@@ -62,6 +62,33 @@ def test_linear_bf16_residual_in_place(M, N, K):
     assert np.all(err <= _bound(a64, w64, want, K) + 2.0 ** -8 * np.abs(r.f32())), float(err.max())
 
 
+@pytest.mark.parametrize("M,N,K", [
+    (515, 256, 256),     # 128 x 128 tiles, operands streamed into LDS
+    (130, 128, 96),      # the register-staged kernel
+    (2000, 512, 512),    # 256 x 256 tiles
+    (37, 64, 64),        # N not a multiple of 128: the plain tiled kernel
+])
+def test_linear_bf16_residual_f32_in_place(M, N, K):
+    """The f32 residual stream's epilogue: y = x w^T + y with y f32 (no bf16 rounding of
+    the sum): within the f32 accumulation bound of the exact product plus the residual, and
+    the pad columns and rows past M untouched."""
+    say(f"linear: bf16 operands, f32 residual M={M} N={N} K={K}")
+    a, w, a64, w64 = _operands(M, N, K, seed=7 * M + K)
+    r = np.random.default_rng(M).standard_normal((M + 2, N + 8)).astype(np.float32)
+    x, wt = stored_to_device(a, DEV), stored_to_device(w, DEV)
+    y = torch.from_numpy(r).to(DEV)
+    B.genrank_linear(B.BF16, x, K, wt, K, y, N + 8, M, N, K, B.EPI_RESIDUAL_F32, y, N + 8)
+    torch.cuda.synchronize()
+    got = y.cpu().numpy().astype(np.float64)
+    want = a64 @ w64.T + r[:M, :N].astype(np.float64)
+    mag = np.abs(a64) @ np.abs(w64).T
+    bound = K * 2.0 ** -23 * mag + 2.0 ** -23 * np.abs(want) + 1e-6
+    err = np.abs(got[:M, :N] - want)
+    assert np.all(err <= bound), float((err - bound).max())
+    assert np.array_equal(got[:M, N:], r[:M, N:].astype(np.float64))
+    assert np.array_equal(got[M:], r[M:].astype(np.float64))
+
+
 @pytest.mark.parametrize("M,N,K", [(333, 1024, 256), (64, 128, 96), (1300, 2048, 512)])
 def test_linear_bf16_silu_with_pre(M, N, K):
     say(f"linear: bf16 silu M={M} N={N} K={K}")

@@ -67,3 +67,31 @@ def test_store_hook():
     # and the result moves by about bf16's resolution, not more
     rel = np.abs(ys - y).max() / np.abs(y).max()
     assert 0 < rel < 2.0 ** -4
+
+
+def test_store_hook_by_name():
+    """A dict storage model rounds only the named tensors: with the residual sums ("x0",
+    "x1", "y") kept exact and every other stored tensor rounded to bf16, the residual
+    tensors are untouched by rounding (the block output of the last layer is the exact sum
+    of its stored inputs) while the operands are bf16."""
+    cfg = synth.make_config("tiny_fp32", block="prenorm", layers=2)
+    batch, tables, weights = synth.make_batch(cfg), synth.make_tables(cfg), synth.make_weights(cfg)
+    idx = oracle_indices(cfg, batch, tables)
+    x0 = oracle.embed_sum(oracle_tables(tables), batch.hist_items, batch.cand_items, idx)
+    geom = oracle_geom(cfg, batch, idx)
+    layers, head = oracle_layers(weights), oracle_head(weights)
+    ops = {k: oracle.round_bf16 for k in ("z", "qkv", "o", "z2", "hdn")}
+    y, _, caches = oracle.model_fwd(x0, layers, cfg.block, cfg.H, geom, head, store=ops)
+    for c in caches:
+        for name in ("z", "o", "z2", "hdn"):
+            assert not np.any(c[name].astype(np.float32).view(np.uint32) & 0xFFFF), name
+    # x0 is passed through unrounded
+    assert np.array_equal(caches[0]["x"], x0)
+    # y = x1 + hdn W2^T exactly (no rounding of the sum)
+    last = caches[-1]
+    want = last["x1"] + last["hdn"] @ np.asarray(layers[-1]["w2"], np.float64).T
+    assert np.array_equal(y, want)
+    # the name "y" alone rounds only the block outputs
+    y2, _, c2 = oracle.model_fwd(x0, layers, cfg.block, cfg.H, geom, head, store={"y": oracle.round_bf16})
+    assert not np.any(y2.astype(np.float32).view(np.uint32) & 0xFFFF)
+    assert np.array_equal(c2[0]["x"], x0)
