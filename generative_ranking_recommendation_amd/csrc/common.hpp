@@ -82,8 +82,11 @@ __device__ __forceinline__ int xcd_local_id(int w, int G) {
 
 // The attention mask on one user's sequence slots: 0..N-1 history, N.. candidates.
 // History queries see history keys at or before them (every history key with the fully
-// visible history variant); a candidate sees all history and itself.  Every attention
-// kernel's masked tiles and genrank_debug_mask use this.
+// visible history variant); a candidate sees all history and itself.  The f32 kernels and
+// genrank_debug_mask evaluate this predicate per pair.  The bf16 kernels enforce the same
+// rule without it: a history query's key limit (its own slot, or the history's end), keys
+// past the history's end given probability 0, and a candidate's own key merged on its own;
+// their mask is checked bit for bit by reading it out of their outputs.
 __device__ __forceinline__ bool attn_allowed(int i, int j, int N, bool full_history = false) {
   return (i < N) ? (full_history ? j < N : j <= i) : (j < N || j == i);
 }

@@ -470,7 +470,7 @@ GENRANK_API genrank_status genrank_debug_indices(const genrank_batch* batch, con
                                      const genrank_tables* tables, int32_t* out,
                                      genrank_stream_t stream);
 
-/* The attention mask of user `user` as the attention kernels evaluate it, on sequence
+/* The attention mask of user `user` as the f32 attention kernels evaluate it, on sequence
  * slots (0..N_u-1 history, N_u..N_u+m-1 candidates): out[i*L_cap + j] = 1 if i and j are
  * below L = N_u + m and slot i may attend slot j, else 0.  out: [L_cap * L_cap] uint8;
  * L_cap >= 1 (pass max_hist + m to see every user whole). */
