@@ -29,6 +29,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -37,7 +39,9 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3
 KERNEL_SOURCES = {"embed_sum": "embed.hip", "attn_fwd": "attn_fwd.hip", "qkv_gemm": "gemm.hip",
-                  "out_gemm": "gemm.hip"}
+                  "out_gemm": "gemm.hip", "embed": "embed.hip", "norm": "rowops.hip", "qkv": "gemm.hip",
+                  "attn": "attn_fwd.hip", "attn_cand": "attn_fwd.hip", "wo": "gemm.hip", "ffn_up": "gemm.hip",
+                  "ffn_down": "gemm.hip", "kv": "gemm.hip", "head": "rowops.hip"}
 
 
 # --attn-variant -> genrank_alibi.flags (1 = fully visible history, 2 = bucketed time term)
@@ -72,7 +76,12 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="infer_1layer_bf16")
+    p.add_argument("--workload", default="stack4_bf16",
+                   help="stack4_bf16 (the 4-layer pre-norm stack, default), infer_1layer_bf16, train2_bf16, "
+                        "hstu_interleaved")
+    p.add_argument("--no-prune", action="store_true",
+                   help="pre-norm stacks: form every row of the top block (by default the top block forms "
+                        "the history rows' keys and values only, which is all the logits read)")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="CPU-oracle baseline budget (0 disables the leg)")
     p.add_argument("--kv-cache", action="store_true",
@@ -517,6 +526,267 @@ def bench_serve(args, cfg):
     print(json.dumps(out), flush=True)
 
 
+def stack_units(model, inp, bufs, prune=True):
+    """The pre-norm stack's forward as a chain of C-ABI calls, one per kernel-sized unit:
+    embed -> per block [norm, QKV, attention, output projection + residual, norm, FFN up +
+    SiLU, FFN down + residual] -> head at the candidate rows.  With ``prune`` the top block
+    forms only what the logits read: the history rows' keys and values, then the candidate
+    rows' block (their queries attend the history K/V and themselves); its history outputs
+    are never formed.  Returns [(name, kind, fn, (bound, amount, unit))]."""
+    from generative_ranking_recommendation_amd import binding as B
+    from generative_ranking_recommendation_amd import workload as W
+    x, z, qkv, o, lse, x1, hdn, kv, logits = (bufs[k] for k in ("x", "z", "qkv", "o", "lse", "x1", "hdn", "kv",
+                                                                 "logits"))
+    bt = model.batch(inp)
+    bc = B.make_batch(inp.B, inp.m, model.d, model.H, 0, 0, model.code, model.resid)  # candidate rows only
+    T, T_h, d, H, m = inp.rows, inp.total_hist, model.d, model.H, inp.m
+    Tc = inp.B * m
+    rc, ac = model.resid_code, model.code
+    es, rs = (2 if ac == B.BF16 else 4), (4 if rc == B.F32 else 2)
+    stream = torch_stream()
+    ptr = lambda t, rows=0, cols=0, ld=None: t.data_ptr() + (rows * (ld or t.shape[-1]) + cols) * t.element_size()
+    gemm = lambda M, N, K, out_es=es, res_es=0: ("mfma", W.gemm_flops(M, N, K), "TFLOP/s")
+    norm = lambda rows: ("hbm", rows * d * (rs + es) + d * 4, "GB/s")
+    units = []
+    uniq = int(np.unique(np.concatenate([inp.host.hist_items, inp.host.cand_items])).size)
+    tabs = model.tables
+    small_rows = int(tabs.action.shape[0] + tabs.pos.shape[0] + tabs.ri.shape[0] + tabs.rt.shape[0])
+    idx_bytes = T_h * (4 + 4 + 8) + Tc * 4 + (inp.B + 1) * 4 + inp.B * 8
+    gbytes = T * d * rs + uniq * d * es + small_rows * d * es + idx_bytes
+    units.append(("embed", "embed", lambda: B.genrank_embed_sum(bt, inp.struct, tabs.struct, x, stream),
+                  ("hbm", gbytes, "GB/s")))
+    L = len(model.layers)
+    lengths = inp.lengths
+    attn_flops = W.attention_fwd_flops(lengths, m, d)
+    attn_bytes = T * 3 * d * es + T * d * es + T * H * 4
+    cand_attn_flops = 4 * d * int(m * (np.asarray(lengths, np.int64) + 1).sum())
+    cand_attn_bytes = T_h * 2 * d * es + Tc * 3 * d * es + Tc * d * es + Tc * H * 4
+
+    def attn_work(flops, nbytes):
+        if nbytes / (PEAK_HBM_GBS * 1e9) >= flops / (PEAK_BF16_TFLOPS * 1e12):
+            return ("hbm", nbytes, "GB/s")
+        return ("mfma", flops, "TFLOP/s")
+
+    for i, lay in enumerate(model.layers):
+        F = lay.ffn_dim
+        sl = lay.slopes
+        top = prune and i == L - 1
+        pre = f"L{i}."
+        if not top:
+            q = qkv.data_ptr()
+            units += [
+                (pre + "norm1", "norm", lambda lay=lay: B.genrank_rmsnorm(rc, ac, x, lay.g1, z, T, d, stream), norm(T)),
+                (pre + "qkv", "qkv", lambda lay=lay: B.genrank_linear(ac, z, d, lay.wqkv, d, qkv, 3 * d, T, 3 * d, d,
+                                                                      stream=stream), gemm(T, 3 * d, d)),
+                (pre + "attn", "attn", lambda sl=sl, q=q: B.genrank_attn_fwd(bt, inp.hist_offsets, inp.hist_ts,
+                                                                              inp.req_ts, sl, q, q + d * es,
+                                                                              q + 2 * d * es, 3 * d, o, d, lse,
+                                                                              stream), attn_work(attn_flops, attn_bytes)),
+                (pre + "wo", "wo", lambda lay=lay: B.genrank_linear(ac, o, d, lay.wo, d, x1, d, T, d, d,
+                                                                    epilogue=B.EPI_RESIDUAL_F32 if rc == B.F32
+                                                                    else B.EPI_RESIDUAL, residual=x, ldr=d,
+                                                                    stream=stream), gemm(T, d, d)),
+                (pre + "norm2", "norm", lambda lay=lay: B.genrank_rmsnorm(rc, ac, x1, lay.g2, z, T, d, stream), norm(T)),
+                (pre + "ffn_up", "ffn_up", lambda lay=lay, F=F: B.genrank_linear(ac, z, d, lay.w1, d, hdn, F, T, F, d,
+                                                                                 epilogue=B.EPI_SILU, stream=stream),
+                 gemm(T, F, d)),
+                (pre + "ffn_down", "ffn_down", lambda lay=lay, F=F: B.genrank_linear(
+                    ac, hdn, F, lay.w2, F, x, d, T, d, F, epilogue=B.EPI_RESIDUAL_F32 if rc == B.F32 else B.EPI_RESIDUAL,
+                    residual=x1, ldr=d, stream=stream), gemm(T, d, F)),
+            ]
+            continue
+        # top block: history keys and values, then the candidate rows alone
+        xc, zc, oc, lc, x1c, hc = (ptr(x, T_h), z.data_ptr(), o.data_ptr(), lse.data_ptr(), x1.data_ptr(),
+                                   hdn.data_ptr())
+        q = qkv.data_ptr()
+        wkv = lay.wqkv.data_ptr() + d * d * es
+        kvp = kv.data_ptr()
+        units += [
+            (pre + "norm1_hist", "norm", lambda lay=lay: B.genrank_rmsnorm(rc, ac, x, lay.g1, z, T_h, d, stream),
+             norm(T_h)),
+            (pre + "kv_hist", "kv", lambda: B.genrank_linear(ac, z, d, wkv, d, kv, 2 * d, T_h, 2 * d, d, stream=stream),
+             gemm(T_h, 2 * d, d)),
+            (pre + "norm1", "norm", lambda lay=lay, xc=xc: B.genrank_rmsnorm(rc, ac, xc, lay.g1, zc, Tc, d, stream),
+             norm(Tc)),
+            (pre + "qkv", "qkv", lambda lay=lay: B.genrank_linear(ac, zc, d, lay.wqkv, d, q, 3 * d, Tc, 3 * d, d,
+                                                                  stream=stream), gemm(Tc, 3 * d, d)),
+            (pre + "attn", "attn_cand", lambda sl=sl: B.genrank_attn_fwd_cached(
+                bt, inp.hist_offsets, inp.hist_ts, inp.req_ts, sl, q, q + d * es, q + 2 * d * es, 3 * d, kvp,
+                kvp + d * es, 2 * d, oc, d, lc, stream), attn_work(cand_attn_flops, cand_attn_bytes)),
+            (pre + "wo", "wo", lambda lay=lay, xc=xc: B.genrank_linear(
+                ac, oc, d, lay.wo, d, x1c, d, Tc, d, d, epilogue=B.EPI_RESIDUAL_F32 if rc == B.F32 else B.EPI_RESIDUAL,
+                residual=xc, ldr=d, stream=stream), gemm(Tc, d, d)),
+            (pre + "norm2", "norm", lambda lay=lay: B.genrank_rmsnorm(rc, ac, x1c, lay.g2, zc, Tc, d, stream), norm(Tc)),
+            (pre + "ffn_up", "ffn_up", lambda lay=lay, F=F: B.genrank_linear(ac, zc, d, lay.w1, d, hc, F, Tc, F, d,
+                                                                             epilogue=B.EPI_SILU, stream=stream),
+             gemm(Tc, F, d)),
+            (pre + "ffn_down", "ffn_down", lambda lay=lay, F=F, xc=xc: B.genrank_linear(
+                ac, hc, F, lay.w2, F, xc, d, Tc, d, F, epilogue=B.EPI_RESIDUAL_F32 if rc == B.F32 else B.EPI_RESIDUAL,
+                residual=x1c, ldr=d, stream=stream), gemm(Tc, d, F)),
+        ]
+    head = model.head
+    xh = ptr(x, T_h) if prune else x
+    hb = bc if prune else bt
+    units.append(("head", "head", lambda: B.genrank_head_fwd(hb, xh, head.g_final, head.w_head, head.b_head,
+                                                             head.n_tasks, logits, stream),
+                  ("hbm", Tc * d * rs + Tc * head.n_tasks * 4, "GB/s")))
+    return units
+
+
+def torch_stream():
+    import torch
+    return torch.cuda.current_stream()
+
+
+def bench_stack(args, cfg):
+    """The full pre-norm stack forward (embed -> L blocks -> action head), each kernel-sized
+    unit a C-ABI call of its own on one stream; candidates scored per second."""
+    import torch
+
+    import synth
+    from generative_ranking_recommendation_amd import binding as B
+    from generative_ranking_recommendation_amd import workload as W
+    from generative_ranking_recommendation_amd.device import DeviceInputs
+    from generative_ranking_recommendation_amd.model import GenRank
+    from generative_ranking_recommendation_amd.slopes import alibi_slopes
+
+    log(f"workload {cfg.name}: generating inputs")
+    batch, tables, weights = synth.make_batch(cfg), synth.make_tables(cfg), synth.make_weights(cfg)
+    sp, st = alibi_slopes(cfg.H, cfg.time_ratio)
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    vflags, vedges = variant_args(args, cfg)
+    model = GenRank.from_host(cfg, tables, weights, sp, st, dev, attn_flags=vflags, time_bounds=vedges)
+    inp = DeviceInputs(batch, dev)
+    T, T_h, d, H, m = inp.rows, inp.total_hist, cfg.d, cfg.H, cfg.m
+    Tc = inp.B * m
+    F = model.layers[0].ffn_dim
+    bf = torch.bfloat16
+    bufs = {"x": model.resid_rows(T), "z": torch.empty((T, d), dtype=bf, device=dev),
+            "qkv": torch.empty((T, 3 * d), dtype=bf, device=dev), "o": torch.empty((T, d), dtype=bf, device=dev),
+            "lse": torch.empty((T, H), dtype=torch.float32, device=dev), "x1": model.resid_rows(T),
+            "hdn": torch.empty((T, F), dtype=bf, device=dev),
+            "kv": torch.empty((T_h, 2 * d), dtype=bf, device=dev),
+            "logits": torch.empty((Tc, model.head.n_tasks), dtype=torch.float32, device=dev)}
+    log(f"T={T} rows (history {T_h}, candidates {Tc}); uploading done")
+    prune = not args.no_prune
+    units = stack_units(model, inp, bufs, prune=prune)
+    stream = torch.cuda.current_stream()
+    names = [u[0] for u in units]
+
+    def step(ev=None, only=None):
+        for n, _, fn, _ in units:
+            if n == only:
+                ev[0].record(stream)
+            fn()
+            if n == only:
+                ev[1].record(stream)
+
+    mk = lambda k: [torch.cuda.Event(enable_timing=True) for _ in range(k)]
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    # the decomposed (and pruned) step must give the logits of the model's own forward
+    got = bufs["logits"].clone()
+    _, ref = model.forward(inp)
+    torch.cuda.synchronize()
+    same = bool(torch.equal(got, ref))
+    if not same:
+        log(f"WARNING: the decomposed step's logits differ from the forward's (max "
+            f"{(got - ref).abs().max().item():.3g})")
+    # the unpruned forward (every block over every row, one genrank_layer_fwd per block)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    n_ref = max(3, args.steps // 4)
+    for _ in range(n_ref):
+        model.forward(inp)
+    torch.cuda.synchronize()
+    ms_unpruned = (time.perf_counter() - t0) * 1e3 / n_ref
+    # per-unit passes: --steps steps with one event pair around one unit
+    per = {}
+    for n in names:
+        events = [mk(2) for _ in range(args.steps)]
+        for k in range(args.steps):
+            step(events[k], only=n)
+        torch.cuda.synchronize()
+        per[n] = float(np.mean([events[k][0].elapsed_time(events[k][1]) for k in range(args.steps)]))
+    traffic = load_traffic(cfg.name) if args.item_dist is None else {}
+
+    def rate(work, t_ms, kind=None):
+        bound, amount, unit = work
+        if unit == "GB/s":
+            achieved, peak = amount / (t_ms * 1e-3) / 1e9, PEAK_HBM_GBS
+        else:
+            achieved, peak = amount / (t_ms * 1e-3) / 1e12, PEAK_BF16_TFLOPS
+        return {"time_us": round(t_ms * 1e3, 2), "bound": bound, "achieved": round(achieved, 2), "peak": peak,
+                "unit": unit, "frac": round(achieved / peak, 4), "algorithmic": int(amount),
+                "traffic": traffic.get(kind)}
+    # by kind: total time per step and the launches
+    kinds = {}
+    for n, kind, _, work in units:
+        k = kinds.setdefault(kind, {"launches": [], "time_us": 0.0})
+        k["launches"].append(n)
+        k["time_us"] += per[n] * 1e3
+    dominant_kind = max(kinds, key=lambda k: kinds[k]["time_us"])
+    dom = kinds[dominant_kind]["launches"][0]
+    dom_work = next(w for n, _, _, w in units if n == dom)
+    # timed pass: exactly --steps steps between two device synchronisations, one event pair
+    # around the dominant kind's first launch
+    events = [mk(2) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(events[k], only=dom)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    t_dom = float(np.mean([events[k][0].elapsed_time(events[k][1]) for k in range(args.steps)]))
+    log(f"{ms:.4f} ms/step (unpruned forward {ms_unpruned:.4f} ms); {dom} {t_dom * 1e3:.1f} us in the timed pass")
+    kd = rate(dom_work, t_dom, dominant_kind)
+    roofline = {"kernel": f"{dominant_kind} ({dom})", "bound": kd["bound"], "achieved": kd["achieved"],
+                "peak": kd["peak"], "unit": kd["unit"], "frac": kd["frac"], "traffic": kd["traffic"]}
+    units_out = {n: rate(w, per[n], kind) for n, kind, _, w in units}
+    kinds_out = {k: {"time_us_per_step": round(v["time_us"], 1), "launches": len(v["launches"]),
+                     "share": round(v["time_us"] / (ms * 1e3), 4)} for k, v in kinds.items()}
+    floor_us = sum((w[1] / (PEAK_HBM_GBS * 1e9) if w[2] == "GB/s" else w[1] / (PEAK_BF16_TFLOPS * 1e12)) * 1e6
+                   for _, _, _, w in units)
+    a0 = units_out["L0.attn"]
+    attn_flops = W.attention_fwd_flops(inp.lengths, m, d)
+    attn_tf = attn_flops / (a0["time_us"] * 1e-6) / 1e12
+    cpu = None
+    if args.cpu_seconds > 0:
+        log("CPU oracle baseline ...")
+        cpu = cpu_baseline(cfg, batch, tables, weights, args.cpu_seconds, (vflags, vedges))
+        log(f"CPU oracle: {cpu['value']:.1f} candidates/s on {cpu['cores']} threads")
+    out = {
+        "metric": METRIC,
+        "value": round(Tc / (ms * 1e-3), 1),
+        "unit": "candidates/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype,
+        "data": "synthetic (seeded; Zipf(1.1) item ids, jagged histories, runs of 1-4 actions per request)",
+        "config": {"workload": cfg.name, "users": inp.B, "candidates_per_user": m,
+                   "history": f"U[{cfg.hist_min},{cfg.hist_max}]", "rows": T, "d": d, "heads": H,
+                   "layers": cfg.layers, "ffn": F, "block": cfg.block, "attn_variant": args.attn_variant,
+                   "residual_stream": "f32" if model.resid == B.RESID_F32 else cfg.dtype,
+                   "top_block": "history rows: keys and values only; candidate rows: the whole block"
+                   if prune else "every row", "item_dist": cfg.item_dist},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "ms_per_step_unpruned": round(ms_unpruned, 4),
+        "logits_equal_forward": same,
+        "kinds": kinds_out,
+        "kernels": units_out,
+        "kernel_timing": "each unit: its own pass of --steps steps with one event pair around it; the "
+                         "dominant unit: the event pair in the timed pass",
+        "attn_mfma_util_pct": round(100 * attn_tf / PEAK_BF16_TFLOPS, 2),
+        "attn_tflops": round(attn_tf, 2),
+        "step_roofline_us": round(floor_us, 1),
+        "step_roofline_frac": round(floor_us / (ms * 1e3), 4),
+        "gather_gbps": units_out["embed"]["achieved"],
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.workload == "hstu_interleaved":
@@ -547,6 +817,9 @@ def main():
         return
     if args.kv_cache:
         bench_serve(args, cfg)
+        return
+    if cfg.block == "prenorm":
+        bench_stack(args, cfg)
         return
     log(f"workload {cfg.name}: generating inputs")
     batch = synth.make_batch(cfg)

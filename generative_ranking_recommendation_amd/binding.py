@@ -104,6 +104,7 @@ _SIGS = {
                                    c_size_t, c_void_p]),
     "genrank_layer_fwd_cached": (c_int32, [POINTER(Batch), POINTER(LayerWeights), c_void_p, c_void_p, c_void_p,
                                            c_void_p, c_int64, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "genrank_rmsnorm": (c_int32, [c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_int64, c_int32, c_void_p]),
     "genrank_head_fwd": (c_int32, [POINTER(Batch), c_void_p, c_void_p, c_void_p, c_void_p, c_int32,
                                    c_void_p, c_void_p]),
     "genrank_head_bwd": (c_int32, [POINTER(Batch), c_void_p, c_void_p, c_void_p, c_int32, c_void_p,
@@ -346,6 +347,11 @@ def genrank_head_bwd(batch, x, g_final, w_head, n_tasks, dlogits, dx, dg_final, 
     _check("genrank_head_bwd", lib().genrank_head_bwd(
         ctypes.byref(batch), _p(x), _p(g_final), _p(w_head), n_tasks, _p(dlogits), _p(dx),
         _p(dg_final), _p(dw_head), _p(db_head), _p(ws), ws_bytes, _stream(stream)))
+
+
+def genrank_rmsnorm(x_dtype, y_dtype, x, g, y, rows, d, stream=None):
+    _check("genrank_rmsnorm", lib().genrank_rmsnorm(x_dtype, y_dtype, _p(x), _p(g), _p(y), rows, d,
+                                                    _stream(stream)))
 
 
 def genrank_head_fwd_rows(dtype, d, x, n_rows, rows, g_final, w_head, b_head, n_tasks, logits, stream=None):

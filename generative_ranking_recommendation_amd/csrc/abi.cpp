@@ -653,6 +653,16 @@ genrank_status genrank_linear_bwd(int32_t dtype, const void* x, int64_t ldx, con
   return GENRANK_OK;
 }
 
+genrank_status genrank_rmsnorm(int32_t x_dtype, int32_t y_dtype, const void* x, const float* g, void* y,
+                               int64_t rows, int32_t d, genrank_stream_t stream) {
+  if (!x || !g || !y) return GENRANK_E_ARG;
+  if (rows < 0 || d < 1) return GENRANK_E_SHAPE;
+  const bool ok = (x_dtype == GENRANK_BF16 && y_dtype == GENRANK_BF16) ||
+                  (x_dtype == GENRANK_F32 && (y_dtype == GENRANK_BF16 || y_dtype == GENRANK_F32));
+  if (!ok) return GENRANK_E_DTYPE;
+  return launch_rmsnorm(x_dtype, y_dtype, x, g, y, rows, d, S(stream));
+}
+
 genrank_status genrank_head_fwd(const genrank_batch* b, const void* x, const float* g_final,
                                 const float* w_head, const float* b_head, int32_t n_tasks,
                                 float* logits, genrank_stream_t stream) {

@@ -282,11 +282,12 @@ __device__ __forceinline__ bf16x8_t pack_blocks(const f32x4_t& lo, const f32x4_t
 template <int VAR>
 __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(BwdMArgs a) {
   constexpr bool FULL = (VAR & BVAR_FULL) != 0, TBK = (VAR & BVAR_TBUCKET) != 0;
+  constexpr bool CAN_FAR = !TBK;  // the bucketed variants' key terms hold the position part only
   __shared__ __attribute__((aligned(16))) bf16_t sK[2][TB * PLD];
   __shared__ __attribute__((aligned(16))) bf16_t sKt[2][DHB * PLD];
   __shared__ __attribute__((aligned(16))) bf16_t sV[2][TB * PLD];
   __shared__ __attribute__((aligned(16))) float sW[BWCH];
-  __shared__ __attribute__((aligned(16))) int32_t sT[TBK ? BWCH : 4];
+  __shared__ __attribute__((aligned(16))) int32_t sT[BWCH];  // key times relative to the reference
   __shared__ int32_t sTB[TBK ? ATTN_MAX_TIME_BOUNDS : 1];
   __shared__ uint32_t sLUT[TBK ? BK_CELLS : 1];  // bucket table over the gap
 
@@ -337,7 +338,7 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(BwdMArgs a) {
       sW[j] = key < N ? (TBK ? sp2 * static_cast<float>(key - p_ref)
                              : sp2 * static_cast<float>(key - p_ref) + st2 * static_cast<float>(tk))
                       : 0.f;
-      if constexpr (TBK) sT[j] = tk;
+      sT[j] = tk;
     }
   };
   if constexpr (TBK)
@@ -371,7 +372,10 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(BwdMArgs a) {
     w_i = TBK ? sp2 * static_cast<float>(q_slot - p_ref)
               : sp2 * static_cast<float>(q_slot - p_ref) + st2 * static_cast<float>(tq);
   }
-  const float c_i = w_i + lse2;
+  // a wave whose queries lie far from the tile's reference point forms each bias exactly from
+  // the pair's own position and time differences (its row term is then 0)
+  const bool far = CAN_FAR && __builtin_amdgcn_ballot_w64(q_valid && fabsf(w_i) > BIAS_FAR_LOG2) != 0;
+  const float c_i = far ? lse2 : w_i + lse2;
 
   f32x4_t accQ[4];
 #pragma unroll
@@ -485,15 +489,16 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(BwdMArgs a) {
     for (int kb = 0; kb < 4; ++kb) {
       const float4 w = reinterpret_cast<const float4*>(sW)[((base - wbase) >> 2) + kb * 4 + g4];
       const float wv[4] = {w.x, w.y, w.z, w.w};
-      int32_t tkv[4] = {0, 0, 0, 0};
-      if constexpr (TBK) {
-        const int4 t4 = reinterpret_cast<const int4*>(sT)[((base - wbase) >> 2) + kb * 4 + g4];
-        tkv[0] = t4.x; tkv[1] = t4.y; tkv[2] = t4.z; tkv[3] = t4.w;
-      }
+      const int4 t4 = reinterpret_cast<const int4*>(sT)[((base - wbase) >> 2) + kb * 4 + g4];
+      const int32_t tkv[4] = {t4.x, t4.y, t4.z, t4.w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         float arg;
-        if constexpr (!FULL && !TBK) {
+        if (CAN_FAR && far) {  // the exact bias of the pair, log2 units
+          const float b = sp2 * static_cast<float>(base + kb * 16 + g4 * 4 + i - q_slot) +
+                          st2 * static_cast<float>(tkv[i] - tq);
+          arg = s[kb][i] * a.scale2 + (FULL ? -fabsf(b) : b) - c_i;
+        } else if constexpr (!FULL && !TBK) {
           arg = s[kb][i] * a.scale2 + wv[i] - c_i;
         } else {
           // fully visible: -|w_j - w_i|; bucketed time: - s' bucket(|t_i - t_j|)
@@ -533,6 +538,7 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(BwdMArgs a) {
 template <int VAR>
 __global__ void __launch_bounds__(256) attn_bwd_dkv_kernel(BwdMArgs a) {
   constexpr bool FULL = (VAR & BVAR_FULL) != 0, TBK = (VAR & BVAR_TBUCKET) != 0;
+  constexpr bool CAN_FAR = !TBK;  // the bucketed variants' key terms hold the position part only
   __shared__ __attribute__((aligned(16))) bf16_t sQ[2][TB * PLD];
   __shared__ __attribute__((aligned(16))) bf16_t sQt[2][DHB * PLD];
   __shared__ __attribute__((aligned(16))) bf16_t sO[2][TB * PLD];
@@ -545,7 +551,11 @@ __global__ void __launch_bounds__(256) attn_bwd_dkv_kernel(BwdMArgs a) {
   // sTB the bucket edges
   constexpr bool SPLIT_L = FULL && !TBK;
   __shared__ __attribute__((aligned(16))) float sL[SPLIT_L ? 2 : 1][SPLIT_L ? TB : 4];
-  __shared__ __attribute__((aligned(16))) int32_t sTq[TBK ? 2 : 1][TBK ? TB : 4];
+  __shared__ __attribute__((aligned(16))) int32_t sTq[2][TB];
+  // a query tile far from its reference point (a query's row term above BIAS_FAR_LOG2): its
+  // pairs' biases are formed exactly from their position and time differences, and sC holds
+  // the queries' lse alone
+  __shared__ int sFar[2];
   __shared__ int32_t sTB[TBK ? ATTN_MAX_TIME_BOUNDS : 1];
   __shared__ uint32_t sLUT[TBK ? BK_CELLS : 1];  // bucket table over the gap
 
@@ -603,6 +613,7 @@ __global__ void __launch_bounds__(256) attn_bwd_dkv_kernel(BwdMArgs a) {
   uint4 rqa, rqb, roa, rob;
   float rc = 0.f, rd = 0.f, rl = 0.f;
   int32_t rt = 0;
+  bool rfar = false;
   auto fetch = [&](const QT& t) {
     const int64_t ra = t.row0 + min(2 * pr, t.nq - 1), rb = t.row0 + min(2 * pr + 1, t.nq - 1);
     rqa = *reinterpret_cast<const uint4*>(a.q + ra * a.ld_qkv + h * DHB + ch * 8);
@@ -619,7 +630,8 @@ __global__ void __launch_bounds__(256) attn_bwd_dkv_kernel(BwdMArgs a) {
         w_i = TBK ? sp2 * static_cast<float>(ql) : sp2 * static_cast<float>(ql) + st2 * static_cast<float>(tq);
       }
       const float lse2 = a.lse[r * a.H + h] * LOG2E_B;
-      rc = FULL ? (TBK ? lse2 : w_i) : w_i + lse2;
+      rfar = CAN_FAR && __builtin_amdgcn_ballot_w64(fabsf(w_i) > BIAS_FAR_LOG2) != 0;  // wave 0 alone
+      rc = rfar ? lse2 : (FULL ? (TBK ? lse2 : w_i) : w_i + lse2);
       rl = lse2;
       rt = tq;
       rd = a.delta[r * a.H + h];
@@ -632,7 +644,8 @@ __global__ void __launch_bounds__(256) attn_bwd_dkv_kernel(BwdMArgs a) {
       sC[buf][tid] = rc;
       sD[buf][tid] = rd;
       if constexpr (SPLIT_L) sL[buf][tid] = rl;
-      if constexpr (TBK) sTq[buf][tid] = rt;
+      sTq[buf][tid] = rt;
+      if (tid == 0) sFar[buf] = rfar ? 1 : 0;
     }
   };
   if constexpr (TBK)
@@ -668,6 +681,7 @@ __global__ void __launch_bounds__(256) attn_bwd_dkv_kernel(BwdMArgs a) {
     const int32_t tk = static_cast<int32_t>(ts_j - ts_ref);
     const float w_j = TBK ? sp2 * static_cast<float>(j - p_ref)
                           : sp2 * static_cast<float>(j - p_ref) + st2 * static_cast<float>(tk);
+    const bool far = CAN_FAR && __builtin_amdgcn_readfirstlane(sFar[buf]) != 0;
     f32x4_t s[4], dp[4];
 #pragma unroll
     for (int qb = 0; qb < 4; ++qb) {
@@ -689,22 +703,22 @@ __global__ void __launch_bounds__(256) attn_bwd_dkv_kernel(BwdMArgs a) {
       const float cv[4] = {c4.x, c4.y, c4.z, c4.w};
       const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
       float lv[4] = {0.f, 0.f, 0.f, 0.f};
-      int32_t tv[4] = {0, 0, 0, 0};
       if constexpr (SPLIT_L) {
         const float4 l4 = reinterpret_cast<const float4*>(sL[buf])[qb * 4 + g4];
         lv[0] = l4.x; lv[1] = l4.y; lv[2] = l4.z; lv[3] = l4.w;
       }
-      if constexpr (TBK) {
-        const int4 t4 = reinterpret_cast<const int4*>(sTq[buf])[qb * 4 + g4];
-        tv[0] = t4.x; tv[1] = t4.y; tv[2] = t4.z; tv[3] = t4.w;
-      }
+      const int4 t4 = reinterpret_cast<const int4*>(sTq[buf])[qb * 4 + g4];
+      const int32_t tv[4] = {t4.x, t4.y, t4.z, t4.w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int ql = qb * 16 + g4 * 4 + i;
         const int slot = t.cand ? N + t.q0 + ql : t.q0 + ql;
         const bool ok = key_valid && ql < t.nq && (t.cand || FULL || j <= slot);
         float arg;
-        if constexpr (!FULL && !TBK) {
+        if (CAN_FAR && far) {  // the exact bias of the pair, log2 units (sC holds the lse)
+          const float b = sp2 * static_cast<float>(j - slot) + st2 * static_cast<float>(tk - tv[i]);
+          arg = s[qb][i] * a.scale2 + (FULL ? -fabsf(b) : b) - cv[i];
+        } else if constexpr (!FULL && !TBK) {
           arg = s[qb][i] * a.scale2 + w_j - cv[i];
         } else {
           // fully visible: -|w_j - w_i|; bucketed time: - s' bucket(|t_i - t_j|)

@@ -498,12 +498,13 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
   constexpr bool FULL = (VAR & VAR_FULL) != 0;
   constexpr bool TBK = (VAR & VAR_TBUCKET) != 0;
   constexpr bool SEP = VAR == 0;  // bias term of the key only: it seeds the accumulator
+  constexpr bool CAN_FAR = !TBK;  // the bucketed variants' key terms hold the position part only
   __shared__ __attribute__((aligned(16))) bf16_t sg0[STAGE];
   __shared__ __attribute__((aligned(16))) bf16_t sg1[STAGE];
   __shared__ __attribute__((aligned(16))) bf16_t sg2[STAGE];
   __shared__ __attribute__((aligned(16))) bf16_t sg3[STAGE];
   __shared__ __attribute__((aligned(16))) float sW[WCHUNK];
-  __shared__ __attribute__((aligned(16))) int32_t sT[TBK ? WCHUNK : 4];
+  __shared__ __attribute__((aligned(16))) int32_t sT[WCHUNK];  // key times relative to the reference
   __shared__ int32_t sTB[TBK ? ATTN_MAX_TIME_BOUNDS : 1];
   __shared__ uint32_t sLUT[TBK ? BK_CELLS : 1];
 
@@ -581,9 +582,8 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
   kself[1] = *reinterpret_cast<const u32x4_t*>(a.k + rowoff + g4 * 8 + 32);
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) vself[nb] = *reinterpret_cast<const u32x2_t*>(a.v + rowoff + nb * 16 + g4 * 4);
-  // a history query's own time (fully visible and bucketed variants)
-  int64_t tq_raw = 0;
-  if constexpr (FULL || TBK) tq_raw = *(N > 0 ? a.ts + off + min(q_slot, N - 1) : a.req + u);
+  // a history query's own time
+  int64_t tq_raw = *(N > 0 ? a.ts + off + min(q_slot, N - 1) : a.req + u);
 
   // ---- the K/V ring.  Wave w loads rows 8 w .. 8 w + 7 of each tile: lane l takes row
   // 8 w + l / 8 and fills LDS chunk l % 8 of it, which holds the row's global chunk
@@ -617,7 +617,7 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
   // attn_fwd_rab_kernel).
   asm volatile("" : "+v"(ts_key), "+v"(tq_raw), "+v"(qf[0]), "+v"(qf[1]), "+v"(kself[0]), "+v"(kself[1]),
                "+v"(vself[0]), "+v"(vself[1]), "+v"(vself[2]), "+v"(vself[3])::"memory");
-  const int32_t tq = (FULL || TBK) && !is_cand && N > 0 ? static_cast<int32_t>(tq_raw - ts_ref) : 0;
+  const int32_t tq = !is_cand && N > 0 ? static_cast<int32_t>(tq_raw - ts_ref) : 0;
   if constexpr (TBK)
     for (int k = tid; k < a.tb_p2; k += NT) {
       const int64_t b = k < a.n_tb ? a.tb[k] : INT64_MAX;
@@ -626,7 +626,7 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
 
   // ---- bias terms of the first chunk, in the score units above
   sW[tid] = wkey_in ? key_term(TBK, spr, str, wkey - p_ref, static_cast<int32_t>(ts_key - ts_ref)) : 0.f;
-  if constexpr (TBK) sT[tid] = wkey_in ? static_cast<int32_t>(ts_key - ts_ref) : 0;
+  sT[tid] = wkey_in ? static_cast<int32_t>(ts_key - ts_ref) : 0;
   auto load_w = [&](int wb) {
     for (int j = tid; j < WCHUNK; j += NT) {
       const int key = wb + j;
@@ -637,7 +637,7 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
         w = key_term(TBK, spr, str, key - p_ref, tk);
       }
       sW[j] = w;
-      if constexpr (TBK) sT[j] = tk;
+      sT[j] = tk;
     }
   };
 
@@ -663,6 +663,14 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
     w_i = (!is_cand && q_valid) ? sW[q_slot - wbase] * SC : 0.f;
   }
   const float w_i_u = w_i / SC;  // the same in score units (FULL only)
+  // a wave whose queries lie far from the tile's reference point forms each bias exactly
+  // from the pair's own position and time differences (its row term is then 0)
+  const bool far = CAN_FAR && __builtin_amdgcn_ballot_w64(fabsf(w_i) > BIAS_FAR_LOG2) != 0;
+  if (far) w_i = 0.f;
+  // the exact bias of key slot j for this lane's query, in score units (far waves)
+  auto exact_bias = [&](int j, int32_t tk) __attribute__((always_inline)) {
+    return key_term(false, spr, str, j - q_slot, tk - tq);
+  };
 
   // LDS offsets (bf16 elements) of this lane's fragments inside a stage buffer
   const int k_off0 = l16 * DH + (((0 + g4) ^ ((l16 >> 1) & 7)) * 8);
@@ -675,15 +683,24 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
   const float th = RESCALE_LOG2 / SC;
   const bool wave_on = wave * QW < nq;
 
-  auto compute = [&](auto masked_tag, const bf16_t* stg, int it) __attribute__((always_inline)) {
+  auto compute = [&](auto masked_tag, auto far_tag, const bf16_t* stg, int it) __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(masked_tag)::value;
+    constexpr bool FAR = decltype(far_tag)::value;
     const int base = (kt_first - it) * AK;
     f32x4_t s[4];
     float4 wv[4];
+    int4 tv[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       wv[kb] = reinterpret_cast<const float4*>(sW)[((base - wbase) >> 2) + kb * 4 + g4];
-      s[kb] = SEP ? f32x4_t{wv[kb].x, wv[kb].y, wv[kb].z, wv[kb].w} : f32x4_t{0.f, 0.f, 0.f, 0.f};
+      tv[kb] = (TBK || FAR) ? reinterpret_cast<const int4*>(sT)[((base - wbase) >> 2) + kb * 4 + g4]
+                            : make_int4(0, 0, 0, 0);
+      const int j0 = base + kb * 16 + g4 * 4;
+      if constexpr (SEP && FAR)
+        s[kb] = f32x4_t{exact_bias(j0, tv[kb].x), exact_bias(j0 + 1, tv[kb].y), exact_bias(j0 + 2, tv[kb].z),
+                        exact_bias(j0 + 3, tv[kb].w)};
+      else
+        s[kb] = SEP ? f32x4_t{wv[kb].x, wv[kb].y, wv[kb].z, wv[kb].w} : f32x4_t{0.f, 0.f, 0.f, 0.f};
       if (!MASKED || base + kb * 16 <= kmax_blk) {
         const bf16x8_t k0 = as_bf16x8(*reinterpret_cast<const uint4*>(stg + kb * 16 * DH + k_off0));
         const bf16x8_t k1 = as_bf16x8(*reinterpret_cast<const uint4*>(stg + kb * 16 * DH + k_off1));
@@ -696,12 +713,11 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
         const float wk[4] = {wv[kb].x, wv[kb].y, wv[kb].z, wv[kb].w};
-        int4 t4 = make_int4(0, 0, 0, 0);
-        if constexpr (TBK) t4 = reinterpret_cast<const int4*>(sT)[((base - wbase) >> 2) + kb * 4 + g4];
-        const int32_t tk[4] = {t4.x, t4.y, t4.z, t4.w};
+        const int32_t tk[4] = {tv[kb].x, tv[kb].y, tv[kb].z, tv[kb].w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          float x = biased(s[kb][i], a.scale2, FULL ? -fabsf(wk[i] - w_i_u) : wk[i]);
+          const float fb = FAR ? -fabsf(exact_bias(base + kb * 16 + g4 * 4 + i, tk[i])) : -fabsf(wk[i] - w_i_u);
+          float x = biased(s[kb][i], a.scale2, FULL ? fb : wk[i]);
           if constexpr (TBK) x -= st2 * static_cast<float>(bucket_lookup(sLUT, sTB, a.tb_p2, abs(tq - tk[i])));
           s[kb][i] = x;
         }
@@ -767,7 +783,7 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
   // other waves, refills the buffer the previous step read with tile it + NS - 1, and
   // computes.  Masks are needed only in the first two tiles (the ragged history end and
   // the causal diagonal); every later tile lies wholly below every query's limit.
-  auto step = [&](auto masked_tag, auto stage_tag, int it) __attribute__((always_inline)) {
+  auto step = [&](auto masked_tag, auto far_tag, auto stage_tag, int it) __attribute__((always_inline)) {
     constexpr int S = decltype(stage_tag)::value;
     bf16_t* const cur = S == 0 ? sg0 : S == 1 ? sg1 : S == 2 ? sg2 : sg3;
     bf16_t* const nxt = S == 0 ? sg3 : S == 1 ? sg0 : S == 2 ? sg1 : sg2;  // stage (it - 1) % NS
@@ -781,19 +797,31 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
     if (left >= 2) wait_vmcnt<4>(); else if (left == 1) wait_vmcnt<2>(); else wait_vmcnt<0>();
     lds_barrier();
     if (it + NS - 1 < n_tiles) issue(it + NS - 1, nxt);
-    if (wave_on) compute(masked_tag, cur, it);
+    if (wave_on) compute(masked_tag, far_tag, cur, it);
   };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
   using I3 = std::integral_constant<int, 3>;
-  if (n_tiles > 0) step(std::true_type{}, I0{}, 0);
-  if (n_tiles > 1) step(std::true_type{}, I1{}, 1);
-  for (int it = 2; it < n_tiles; it += NS) {
-    step(std::false_type{}, I2{}, it);
-    if (it + 1 < n_tiles) step(std::false_type{}, I3{}, it + 1);
-    if (it + 2 < n_tiles) step(std::false_type{}, I0{}, it + 2);
-    if (it + 3 < n_tiles) step(std::false_type{}, I1{}, it + 3);
+  // (a far wave runs its own copy of the loop, with the same waits and barriers in the same
+  // order as the other waves)
+  auto loop = [&](auto far_tag) __attribute__((always_inline)) {
+    if (n_tiles > 0) step(std::true_type{}, far_tag, I0{}, 0);
+    if (n_tiles > 1) step(std::true_type{}, far_tag, I1{}, 1);
+    for (int it = 2; it < n_tiles; it += NS) {
+      step(std::false_type{}, far_tag, I2{}, it);
+      if (it + 1 < n_tiles) step(std::false_type{}, far_tag, I3{}, it + 1);
+      if (it + 2 < n_tiles) step(std::false_type{}, far_tag, I0{}, it + 2);
+      if (it + 3 < n_tiles) step(std::false_type{}, far_tag, I1{}, it + 3);
+    }
+  };
+  if constexpr (CAN_FAR) {
+    if (far)
+      loop(std::true_type{});
+    else
+      loop(std::false_type{});
+  } else {
+    loop(std::false_type{});
   }
   wait_vmcnt<0>();  // no direct load may still be writing LDS when the workgroup ends
   if (is_cand) merge_self(kself, vself, qf, SEP, a.scale2, tbk_self, SC, g4, m_run, lsum, accO);
@@ -838,9 +866,10 @@ __global__ void __launch_bounds__(PAIR_NT) attn_fwd_pair_kernel(AttnArgs a) {
   constexpr bool FULL = (VAR & VAR_FULL) != 0;
   constexpr bool TBK = (VAR & VAR_TBUCKET) != 0;
   constexpr bool SEP = VAR == 0;
+  constexpr bool CAN_FAR = !TBK;  // the bucketed variants' key terms hold the position part only
   __shared__ __attribute__((aligned(16))) bf16_t sKV[PAIR_MAXT * STAGE];
   __shared__ __attribute__((aligned(16))) float sW[PAIR_MAXK];
-  __shared__ __attribute__((aligned(16))) int32_t sT[TBK ? PAIR_MAXK : 4];
+  __shared__ __attribute__((aligned(16))) int32_t sT[PAIR_MAXK];  // key times relative to the request
   __shared__ int32_t sTB[TBK ? ATTN_MAX_TIME_BOUNDS : 1];
   __shared__ uint32_t sLUT[TBK ? BK_CELLS : 1];
   __shared__ int sCnt[PAIR_MAXT + 1];
@@ -938,7 +967,7 @@ __global__ void __launch_bounds__(PAIR_NT) attn_fwd_pair_kernel(AttnArgs a) {
       w = key_term(TBK, spr, str, tid - N, tk);
     }
     sW[tid] = w;
-    if constexpr (TBK) sT[tid] = tk;
+    sT[tid] = tk;
   }
   if constexpr (TBK)
     for (int k = tid; k < a.tb_p2; k += PAIR_NT) {
@@ -1009,24 +1038,39 @@ __global__ void __launch_bounds__(PAIR_NT) attn_fwd_pair_kernel(AttnArgs a) {
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) vself[nb] = *reinterpret_cast<const u32x2_t*>(a.v + ro + nb * 16 + g4 * 4);
     }
-    // the row term (log2 units) and, for the variants, the query's own terms
-    const float w_i = (!is_cand && q_valid) ? sW[min(q_slot, N - 1)] * SC : 0.f;
-    const float w_i_u = w_i / SC;
-    const int32_t tq = (TBK && !is_cand && N > 0) ? sT[min(q_slot, N - 1)] : 0;
+    // the row term (log2 units) and the query's own time
+    const float w_i_ref = (!is_cand && q_valid) ? sW[min(q_slot, N - 1)] * SC : 0.f;
+    const float w_i_u = w_i_ref / SC;
+    const int32_t tq = (!is_cand && N > 0) ? sT[min(q_slot, N - 1)] : 0;
+    // a history block far from the candidates' reference point forms each bias exactly
+    // from the pair's own position and time differences (the row term is then 0)
+    const bool far = CAN_FAR && __builtin_amdgcn_ballot_w64(fabsf(w_i_ref) > BIAS_FAR_LOG2) != 0;
+    const float w_i = far ? 0.f : w_i_ref;
 
     f32x4_t accO[4];
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) accO[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     float m_run = -1e30f, lsum = 0.f;
 
+    // the exact bias of key slot j for this lane's query, in score units (far blocks): from
+    // the integer position and time differences, each product rounded once
+    auto exact_bias = [&](int j, int32_t tk) __attribute__((always_inline)) {
+      return key_term(false, spr, str, j - q_slot, tk - tq);
+    };
     // S^T of key tile kt (with the separable bias: seeded with the key terms)
-    auto scores = [&](auto masked_tag, int kt, f32x4_t(&s)[4]) __attribute__((always_inline)) {
+    auto scores = [&](auto masked_tag, auto far_tag, int kt, f32x4_t(&s)[4]) __attribute__((always_inline)) {
       constexpr bool MASKED = decltype(masked_tag)::value;
+      constexpr bool FAR = decltype(far_tag)::value;
       const bf16_t* stg = sKV + kt * STAGE;
       const int base = kt * AK;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        if constexpr (SEP) {
+        if constexpr (SEP && FAR) {
+          const int4 t4 = reinterpret_cast<const int4*>(sT)[(base >> 2) + kb * 4 + g4];
+          const int j0 = base + kb * 16 + g4 * 4;
+          s[kb] = f32x4_t{exact_bias(j0, t4.x), exact_bias(j0 + 1, t4.y), exact_bias(j0 + 2, t4.z),
+                          exact_bias(j0 + 3, t4.w)};
+        } else if constexpr (SEP) {
           const float4 w = reinterpret_cast<const float4*>(sW)[(base >> 2) + kb * 4 + g4];
           s[kb] = f32x4_t{w.x, w.y, w.z, w.w};
         } else {
@@ -1041,8 +1085,9 @@ __global__ void __launch_bounds__(PAIR_NT) attn_fwd_pair_kernel(AttnArgs a) {
       }
     };
     // bias (variants), mask, online softmax and O^T += V^T P^T for key tile kt
-    auto tile = [&](auto masked_tag, int kt, f32x4_t(&s)[4]) __attribute__((always_inline)) {
+    auto tile = [&](auto masked_tag, auto far_tag, int kt, f32x4_t(&s)[4]) __attribute__((always_inline)) {
       constexpr bool MASKED = decltype(masked_tag)::value;
+      constexpr bool FAR = decltype(far_tag)::value;
       const bf16_t* stg = sKV + kt * STAGE;
       const int base = kt * AK;
       if constexpr (!SEP) {
@@ -1051,11 +1096,13 @@ __global__ void __launch_bounds__(PAIR_NT) attn_fwd_pair_kernel(AttnArgs a) {
           const float4 wq = reinterpret_cast<const float4*>(sW)[(base >> 2) + kb * 4 + g4];
           const float wk[4] = {wq.x, wq.y, wq.z, wq.w};
           int4 t4 = make_int4(0, 0, 0, 0);
-          if constexpr (TBK) t4 = reinterpret_cast<const int4*>(sT)[(base >> 2) + kb * 4 + g4];
+          if constexpr (TBK || FAR) t4 = reinterpret_cast<const int4*>(sT)[(base >> 2) + kb * 4 + g4];
           const int32_t tk[4] = {t4.x, t4.y, t4.z, t4.w};
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            float x = biased(s[kb][i], a.scale2, FULL ? -fabsf(wk[i] - w_i_u) : wk[i]);
+            // fully visible: -|w_j - w_i|, or the exact -|bias| of the pair in far blocks
+            const float fb = FAR ? -fabsf(exact_bias(base + kb * 16 + g4 * 4 + i, tk[i])) : -fabsf(wk[i] - w_i_u);
+            float x = biased(s[kb][i], a.scale2, FULL ? fb : wk[i]);
             if constexpr (TBK) x -= st2 * static_cast<float>(bucket_lookup(sLUT, sTB, a.tb_p2, abs(tq - tk[i])));
             s[kb][i] = x;
           }
@@ -1112,19 +1159,30 @@ __global__ void __launch_bounds__(PAIR_NT) attn_fwd_pair_kernel(AttnArgs a) {
       }
     };
     // Key tiles newest first; only the first can cross a query's limit.  A candidate's
-    // limit is the history end, which the -inf bias terms already enforce.
-    if (n_t > 0) {
+    // limit is the history end, which the -inf bias terms already enforce (candidate
+    // blocks are never far: their reference point is their own).
+    auto run_tiles = [&](auto far_tag) __attribute__((always_inline)) {
       f32x4_t sc[4];
       if (is_cand) {
-        scores(std::false_type{}, n_t - 1, sc);
-        tile(std::false_type{}, n_t - 1, sc);
+        scores(std::false_type{}, far_tag, n_t - 1, sc);
+        tile(std::false_type{}, far_tag, n_t - 1, sc);
       } else {
-        scores(std::true_type{}, n_t - 1, sc);
-        tile(std::true_type{}, n_t - 1, sc);
+        scores(std::true_type{}, far_tag, n_t - 1, sc);
+        tile(std::true_type{}, far_tag, n_t - 1, sc);
       }
       for (int kt = n_t - 2; kt >= 0; --kt) {
-        scores(std::false_type{}, kt, sc);
-        tile(std::false_type{}, kt, sc);
+        scores(std::false_type{}, far_tag, kt, sc);
+        tile(std::false_type{}, far_tag, kt, sc);
+      }
+    };
+    if (n_t > 0) {
+      if constexpr (CAN_FAR) {
+        if (far)
+          run_tiles(std::true_type{});
+        else
+          run_tiles(std::false_type{});
+      } else {
+        run_tiles(std::false_type{});
       }
     }
 

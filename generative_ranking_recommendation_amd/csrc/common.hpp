@@ -91,6 +91,16 @@ __device__ __forceinline__ bool attn_allowed(int i, int j, int N, bool full_hist
   return (i < N) ? (full_history ? j < N : j <= i) : (j < N || j == i);
 }
 
+// Bias terms of large magnitude.  The bf16 attention kernels form a pair's ALiBi bias as
+// w_j - w_i, the key's and the query's terms relative to one reference point per query block
+// (w = s p + s' tau), or seed the scores with w_j alone.  In f32 that is exact to about
+// 2^-24 |w|: harmless while |w| stays small, but a history that spans millions of seconds
+// puts w_i and w_j both near s' 2^23 while their difference is a few units, and the rounding
+// then swamps it.  A query block whose row terms exceed this bound (log2 units) forms every
+// bias exactly instead, from the integer position and time differences of the pair; below
+// it the error of the separable form is at most 2^-24 * 2^12 = 2^-12 in the exponent.
+constexpr float BIAS_FAR_LOG2 = 4096.f;
+
 // #{k : b[k] <= g} for b sorted ascending in p2 entries (a power of two >= the edge count,
 // at least 1), the entries past the real edges being INT32_MAX (g < INT32_MAX): a branchless
 // binary search over the first p2 - 1 entries, then one compare with the entry it stops at

@@ -345,6 +345,15 @@ GENRANK_API genrank_status genrank_linear_bwd(int32_t dtype, const void* x, int6
                                               int32_t N, int32_t K, void* ws, size_t ws_bytes,
                                               genrank_stream_t stream);
 
+/* The pre-norm block's RMSNorm on its own (the pages are silent on the block's internals;
+ * reading: pre-RMSNorm blocks, eps 1e-6): y[r] = x[r] / sqrt(mean(x[r]^2) + 1e-6) * g, per
+ * row.  x: [rows, d] in x_dtype (the residual stream); y: [rows, d] in y_dtype (the next
+ * projection's operand); g: [d] f32.  Supported (x_dtype, y_dtype): (BF16, BF16), (F32, BF16),
+ * (F32, F32) (else GENRANK_E_DTYPE).  This is the normalisation genrank_layer_fwd runs
+ * without GENRANK_FWD_SAVE on an f32 residual stream (and with it on any stream). */
+GENRANK_API genrank_status genrank_rmsnorm(int32_t x_dtype, int32_t y_dtype, const void* x, const float* g, void* y,
+                                           int64_t rows, int32_t d, genrank_stream_t stream);
+
 /* Per-candidate action logits ([GR-zh] section 1.2: predictions for a set of predefined
  * tasks): logits[c, t] = (rmsnorm(x[T_h + c]) * g_final) . w_head[t] + b_head[t].
  * x: [T, d] residual-stream rows (batch.dtype, or f32 with GENRANK_RESID_F32); g_final [d],

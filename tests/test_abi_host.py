@@ -152,6 +152,12 @@ def test_entry_points_reject_bad_arguments(lib):
     assert lib.genrank_layer_fwd(ctypes.byref(rf), ctypes.byref(w), FAKE, FAKE, FAKE, FAKE, FAKE + 64,
                                  0, FAKE, 1 << 40, None) == -3
     assert lib.genrank_bce_loss(0, 4, FAKE, FAKE, FAKE, FAKE, None) == -1
+    # RMSNorm: dtype pairs, null pointers, shapes
+    assert lib.genrank_rmsnorm(B.BF16, B.F32, FAKE, FAKE, FAKE, 4, 256, None) == -3
+    assert lib.genrank_rmsnorm(B.F32, 7, FAKE, FAKE, FAKE, 4, 256, None) == -3
+    assert lib.genrank_rmsnorm(B.F32, B.BF16, None, FAKE, FAKE, 4, 256, None) == -1
+    assert lib.genrank_rmsnorm(B.F32, B.BF16, FAKE, FAKE, FAKE, -1, 256, None) == -2
+    assert lib.genrank_rmsnorm(B.F32, B.BF16, FAKE, FAKE, FAKE, 0, 256, None) == 0  # nothing to do
     assert lib.genrank_debug_mask(ctypes.byref(bt), FAKE, 2, 10, FAKE, None) == -1  # user >= B
 
 

@@ -161,3 +161,25 @@ def test_linear_bwd_one_output_and_f32():
         bound_w = M * 2.0 ** -23 * (np.abs(dy64).T @ np.abs(x64)) + 1e-6
         assert np.all(np.abs(to_numpy(dx) - want_x) <= bound_x), name
         assert np.all(np.abs(to_numpy(dw) - want_w) <= bound_w), name
+
+
+@pytest.mark.parametrize("x_dtype,y_dtype,rows,d", [("f32", "bf16", 3001, 512), ("bf16", "bf16", 1000, 256),
+                                                   ("f32", "f32", 77, 512), ("f32", "bf16", 5, 96)])
+def test_rmsnorm(x_dtype, y_dtype, rows, d):
+    """genrank_rmsnorm against the oracle's RMSNorm of the same stored rows: one rounding of the
+    output to y_dtype (2^-8 relative for bf16) plus the f32 evaluation (a few 2^-24)."""
+    import oracle
+    say(f"rmsnorm: {x_dtype} -> {y_dtype} rows={rows} d={d}")
+    xs = synth.inputs.normal_array((rows, d), std=0.7, seed=rows + d, dtype=x_dtype)
+    g = (1.0 + 0.1 * np.random.default_rng(d).standard_normal(d)).astype(np.float32)
+    x = stored_to_device(xs, DEV)
+    gd = torch.from_numpy(g).to(DEV)
+    ty = torch.bfloat16 if y_dtype == "bf16" else torch.float32
+    y = torch.full((rows, d), float("nan"), dtype=ty, device=DEV)
+    code = {"f32": B.F32, "bf16": B.BF16}
+    B.genrank_rmsnorm(code[x_dtype], code[y_dtype], x, gd, y, rows, d)
+    torch.cuda.synchronize()
+    want = oracle.rmsnorm(xs.f32().astype(np.float64), g)
+    rel = 2.0 ** -8 if y_dtype == "bf16" else 0.0
+    bound = rel * np.abs(want) + 64 * 2.0 ** -24 * np.abs(want) + 1e-7
+    assert np.all(np.abs(to_numpy(y) - want) <= bound)
