@@ -83,6 +83,10 @@ _SIGS = {
                                    c_void_p, c_void_p, c_int64, c_void_p, c_void_p, c_int64,
                                    c_void_p, c_void_p, c_void_p, c_void_p, c_int64, c_int32,
                                    c_void_p, c_size_t, c_void_p]),
+    "genrank_attn_bwd_noalloc": (c_int32, [POINTER(Batch), c_void_p, c_void_p, c_void_p, Alibi, c_void_p,
+                                           c_void_p, c_void_p, c_int64, c_void_p, c_void_p, c_int64,
+                                           c_void_p, c_void_p, c_void_p, c_void_p, c_int64, c_int32,
+                                           c_void_p]),
     "genrank_layer_fwd": (c_int32, [POINTER(Batch), POINTER(LayerWeights), c_void_p, c_void_p,
                                     c_void_p, c_void_p, c_void_p, c_int32, c_void_p, c_size_t,
                                     c_void_p]),
@@ -273,6 +277,14 @@ def genrank_attn_bwd(batch, hist_offsets, hist_ts, req_ts, slopes: HostSlopes, q
         ctypes.byref(batch), _p(hist_offsets), _p(hist_ts), _p(req_ts), slopes.struct, _p(q), _p(k),
         _p(v), ld_qkv, _p(o), _p(dout), ld_o, _p(lse), _p(dq), _p(dk), _p(dv), ld_dqkv,
         int(cand_only), _p(ws), ws_bytes, _stream(stream)))
+
+
+def genrank_attn_bwd_noalloc(batch, hist_offsets, hist_ts, req_ts, slopes: HostSlopes, q, k, v, ld_qkv, o,
+                             dout, ld_o, lse, dq, dk, dv, ld_dqkv, cand_only, stream=None):
+    _check("genrank_attn_bwd_noalloc", lib().genrank_attn_bwd_noalloc(
+        ctypes.byref(batch), _p(hist_offsets), _p(hist_ts), _p(req_ts), slopes.struct, _p(q), _p(k),
+        _p(v), ld_qkv, _p(o), _p(dout), ld_o, _p(lse), _p(dq), _p(dk), _p(dv), ld_dqkv,
+        int(cand_only), _stream(stream)))
 
 
 def genrank_layer_fwd(batch, weights: LayerWeights, hist_offsets, hist_ts, req_ts, x_in, y_out,

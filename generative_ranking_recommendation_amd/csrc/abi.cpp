@@ -384,6 +384,28 @@ genrank_status genrank_attn_bwd(const genrank_batch* b, const int32_t* offsets,
                          dv, ld_dqkv, cand_only, ws, S(stream));
 }
 
+genrank_status genrank_attn_bwd_noalloc(const genrank_batch* b, const int32_t* offsets, const int64_t* ts,
+                                        const int64_t* req, genrank_alibi alibi, const void* q, const void* k,
+                                        const void* v, int64_t ld_qkv, const void* o, const void* dout,
+                                        int64_t ld_o, const float* lse, void* dq, void* dk, void* dv,
+                                        int64_t ld_dqkv, int32_t cand_only, genrank_stream_t stream) {
+  GR_TRY(check_attn_args(b, offsets, ts, req, alibi, q, k, v, ld_qkv, o, ld_o));
+  if (!dout || !lse || !dq || !dk || !dv) return GENRANK_E_ARG;
+  if (ld_dqkv < b->d) return GENRANK_E_SHAPE;
+  if (b->dh > 64) return GENRANK_E_SHAPE;
+  if (b->dtype == GENRANK_BF16) {
+    if (ld_o % 8 || ld_dqkv % 4) return GENRANK_E_SHAPE;
+    if (reinterpret_cast<uintptr_t>(dout) % 16 || reinterpret_cast<uintptr_t>(o) % 16 ||
+        (reinterpret_cast<uintptr_t>(dq) | reinterpret_cast<uintptr_t>(dk) | reinterpret_cast<uintptr_t>(dv)) % 8)
+      return GENRANK_E_ARG;
+  }
+  if (attn_bwd_workspace(b) > attn_bwd_scratch_bytes()) return GENRANK_E_WORKSPACE;
+  void* ws = nullptr;
+  GR_TRY(attn_bwd_scratch(&ws));
+  return launch_attn_bwd(b, offsets, ts, req, alibi, q, k, v, ld_qkv, o, dout, ld_o, lse, dq, dk,
+                         dv, ld_dqkv, cand_only, ws, S(stream));
+}
+
 genrank_status genrank_layer_fwd(const genrank_batch* b, const genrank_layer_weights* w,
                                  const int32_t* offsets, const int64_t* ts, const int64_t* req,
                                  const void* x_in, void* y_out, int32_t flags, void* ws,

@@ -13,6 +13,8 @@
 // With cand_only set, history query rows carry dO = 0 and are skipped.
 #include <math.h>
 
+#include <mutex>
+
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -770,6 +772,34 @@ __global__ void __launch_bounds__(256) attn_bwd_dkv_kernel(BwdMArgs a) {
 }
 
 }  // namespace
+
+// ---- the allocation-free entry point's scratch: the per-row D of the backward, in a
+// file-scope device array (one copy per GPU, held until the process ends).  In host code
+// `scratch` names a host-side stand-in, not device memory: every use goes through the
+// per-device address hipGetSymbolAddress returns.
+constexpr size_t ATTN_BWD_SCRATCH_BYTES = size_t(16) << 20;
+static __device__ __align__(256) float scratch[ATTN_BWD_SCRATCH_BYTES / sizeof(float)];
+
+namespace {
+constexpr int SCRATCH_MAX_DEVICES = 64;
+std::once_flag scratch_once[SCRATCH_MAX_DEVICES];
+void* scratch_ptr[SCRATCH_MAX_DEVICES];
+hipError_t scratch_err[SCRATCH_MAX_DEVICES];
+}  // namespace
+
+size_t attn_bwd_scratch_bytes() { return ATTN_BWD_SCRATCH_BYTES; }
+
+// The current device's copy of the scratch array, looked up once per device.
+genrank_status attn_bwd_scratch(void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= SCRATCH_MAX_DEVICES) return GENRANK_E_HIP;
+  std::call_once(scratch_once[dev], [dev] {
+    scratch_err[dev] = hipGetSymbolAddress(&scratch_ptr[dev], HIP_SYMBOL(scratch));
+  });
+  if (scratch_err[dev] != hipSuccess || !scratch_ptr[dev]) return GENRANK_E_HIP;
+  *ptr = scratch_ptr[dev];
+  return GENRANK_OK;
+}
 
 size_t attn_bwd_workspace(const genrank_batch* b) {
   const int64_t T = b->total_hist + static_cast<int64_t>(b->B) * b->m;

@@ -61,6 +61,10 @@ genrank_status launch_attn_fwd(const genrank_batch* b, const int32_t* offsets, c
 genrank_status launch_debug_mask(const int32_t* offsets, int m, int user, int L_cap, uint8_t* out,
                                  hipStream_t stream);
 size_t attn_bwd_workspace(const genrank_batch* b);
+// the allocation-free backward: the size of its library-owned scratch array, and the current
+// device's copy of it (looked up on the first call on each device)
+size_t attn_bwd_scratch_bytes();
+genrank_status attn_bwd_scratch(void** ptr);
 genrank_status launch_attn_bwd(const genrank_batch* b, const int32_t* offsets, const int64_t* ts,
                                const int64_t* req, genrank_alibi alibi, const void* q,
                                const void* k, const void* v, int64_t ld_qkv, const void* o,

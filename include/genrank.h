@@ -271,6 +271,24 @@ GENRANK_API genrank_status genrank_attn_bwd(const genrank_batch* batch, const in
                                 void* dk, void* dv, int64_t ld_dqkv, int32_t cand_only_dout,
                                 void* ws, size_t ws_bytes, genrank_stream_t stream);
 
+/* genrank_attn_bwd without the workspace argument, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving or training loops, harnesses that
+ * forbid allocation.  Same arguments (minus ws, ws_bytes), results and errors as
+ * genrank_attn_bwd.  Its scratch (the per-row D = rowsum(dout * o), T * H f32) is a
+ * library-owned 16 MiB device array, one copy per GPU, found on the first call on each
+ * device and held until the process ends; this call allocates nothing.  Limit: a batch with
+ * T * H * 4 + 256 > 16 MiB (T * H > 4,194,240) returns GENRANK_E_WORKSPACE.  Every call on a
+ * GPU shares that GPU's array: calls that overlap on one GPU (different streams, or threads)
+ * race and must be serialised by the caller.  The current device must be the one `stream`
+ * and the pointers belong to.  GENRANK_E_HIP if the array cannot be located. */
+GENRANK_API genrank_status genrank_attn_bwd_noalloc(const genrank_batch* batch, const int32_t* hist_offsets,
+                                                    const int64_t* hist_ts, const int64_t* req_ts,
+                                                    genrank_alibi alibi, const void* q, const void* k,
+                                                    const void* v, int64_t ld_qkv, const void* o,
+                                                    const void* dout, int64_t ld_o, const float* lse, void* dq,
+                                                    void* dk, void* dv, int64_t ld_dqkv, int32_t cand_only,
+                                                    genrank_stream_t stream);
+
 /* One block forward (see genrank_layer_weights for the two block forms): the dense
  * projections (QKV, output, FFN) as bf16 MFMA GEMMs with fused residual / SiLU
  * epilogues, RMSNorm, and genrank_attn_fwd between them.

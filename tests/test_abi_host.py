@@ -152,6 +152,13 @@ def test_entry_points_reject_bad_arguments(lib):
     assert lib.genrank_layer_fwd(ctypes.byref(rf), ctypes.byref(w), FAKE, FAKE, FAKE, FAKE, FAKE + 64,
                                  0, FAKE, 1 << 40, None) == -3
     assert lib.genrank_bce_loss(0, 4, FAKE, FAKE, FAKE, FAKE, None) == -1
+    # the allocation-free attention backward: a batch whose per-row scratch (T * H f32) exceeds its
+    # 16 MiB array is refused before anything is enqueued
+    big = B.make_batch(1, 0, 256, 4, 1_100_000, 1_100_000, B.F32)
+    assert lib.genrank_attn_bwd_noalloc(ctypes.byref(big), FAKE, FAKE, FAKE, sl.struct, FAKE, FAKE, FAKE, 768, FAKE,
+                                        FAKE, 256, FAKE, FAKE, FAKE, FAKE, 768, 0, None) == -6
+    assert lib.genrank_attn_bwd_noalloc(ctypes.byref(big), FAKE, FAKE, FAKE, sl.struct, FAKE, FAKE, FAKE, 768, FAKE,
+                                        None, 256, FAKE, FAKE, FAKE, FAKE, 768, 0, None) == -1
     # RMSNorm: dtype pairs, null pointers, shapes
     assert lib.genrank_rmsnorm(B.BF16, B.F32, FAKE, FAKE, FAKE, 4, 256, None) == -3
     assert lib.genrank_rmsnorm(B.F32, 7, FAKE, FAKE, FAKE, 4, 256, None) == -3
