@@ -45,10 +45,11 @@ __device__ __forceinline__ float dsilu_f(float a) {
 }
 
 // LDS operand tile: [128 rows][32 bf16] = 64 B per row, four 16-byte chunks.  Chunk c of
-// row r is stored at chunk c ^ ((r >> 1) & 3): the 16-byte reads of 16 consecutive rows at
-// one chunk (an MFMA operand fragment) and the 16-byte writes of the staging pattern both
-// hit distinct banks.
-__device__ __forceinline__ int swz(int r, int c) { return r * GBK + ((c ^ ((r >> 1) & 3)) << 3); }
+// row r is stored at chunk c ^ ((r >> 2) & 3): the 16-byte reads of 16 consecutive rows at
+// one chunk (an MFMA operand fragment) fall on 16 distinct 16-byte slots of the 64-bank LDS
+// (4 rows of 64 B span its 256 bytes; the XOR spreads the 4 row groups over the 4 chunks),
+// and so do the 16-byte writes of the staging pattern.
+__device__ __forceinline__ int swz(int r, int c) { return r * GBK + ((c ^ ((r >> 2) & 3)) << 3); }
 
 constexpr int CP = GBN + 8;                           // staged C row pitch (bf16)
 constexpr int SMEM_OPS = 2 * 2 * GBM * GBK;           // [stage][A|W] operand tiles
@@ -271,10 +272,10 @@ __global__ void __launch_bounds__(GTHREADS) gemm_nt_bf16_dma_kernel(GemmArgs g) 
 
   // direct loads: wave w fills rows 32 w .. 32 w + 31 of the A tile and of the W tile, 16
   // rows (1 KB) per load; lane -> row r = r0 + lane / 4, LDS chunk lane % 4, which holds
-  // global chunk (lane % 4) ^ ((r >> 1) & 3).  A rows past M re-read row M - 1 (never stored).
+  // global chunk (lane % 4) ^ ((r >> 2) & 3).  A rows past M re-read row M - 1 (never stored).
   const int lr = lane >> 2, ls = lane & 3;
   const int r0 = wave * 32 + lr, r1 = r0 + 16;
-  const int c0 = ls ^ ((r0 >> 1) & 3), c1 = ls ^ ((r1 >> 1) & 3);
+  const int c0 = ls ^ ((r0 >> 2) & 3), c1 = ls ^ ((r1 >> 2) & 3);
   const bf16_t* gA0 = g.A + static_cast<int64_t>(min(m0 + r0, g.M - 1)) * g.lda + c0 * 8;
   const bf16_t* gA1 = g.A + static_cast<int64_t>(min(m0 + r1, g.M - 1)) * g.lda + c1 * 8;
   const bf16_t* gW0 = g.W + static_cast<int64_t>(n0 + r0) * g.ldw + c0 * 8;
@@ -372,7 +373,7 @@ __global__ void __launch_bounds__(BTHREADS) gemm_nt_bf16_big_kernel(GemmArgs g) 
   // A tile and of the W tile (256 rows each), 16 rows (1 KB) per load
   const int lr = lane >> 2, ls = lane & 3;
   const int r0 = wave * 32 + lr, r1 = r0 + 16;
-  const int c0 = ls ^ ((r0 >> 1) & 3), c1 = ls ^ ((r1 >> 1) & 3);
+  const int c0 = ls ^ ((r0 >> 2) & 3), c1 = ls ^ ((r1 >> 2) & 3);
   const bf16_t* gA0 = g.A + static_cast<int64_t>(min(m0 + r0, g.M - 1)) * g.lda + c0 * 8;
   const bf16_t* gA1 = g.A + static_cast<int64_t>(min(m0 + r1, g.M - 1)) * g.lda + c1 * 8;
   const bf16_t* gW0 = g.W + static_cast<int64_t>(n0 + r0) * g.ldw + c0 * 8;
