@@ -466,30 +466,44 @@ __device__ __forceinline__ float biased(float s, float scale2, float bias) { ret
 // Merge a candidate's own key (score m_self in score units, value row vself) into its
 // softmax state after the history keys.
 __device__ __forceinline__ void merge_self(const u32x4_t (&kself)[2], const u32x2_t (&vself)[4], const bf16x8_t (&qf)[2],
-                                           bool sep, float scale2, float self_bias, float SC, int g4, float& m_run,
-                                           float& lsum, f32x4_t (&accO)[4]) {
-  float dot = 0.f, kf[8], qv[8];
+                                           bool sep, float scale2, float self_bias, float SC, float th, int g4,
+                                           float& m_run, float& lsum, f32x4_t (&accO)[4]) {
+  // q . k over this lane's 16 dimensions, two products per step (exact bf16 products)
+  float dot = 0.f;
 #pragma unroll
   for (int hlf = 0; hlf < 2; ++hlf) {
-    unpack8(__builtin_bit_cast(uint4, kself[hlf]), kf);
-    unpack8(__builtin_bit_cast(uint4, qf[hlf]), qv);
+    const uint4 kw = __builtin_bit_cast(uint4, kself[hlf]);
+    const uint4 qw = __builtin_bit_cast(uint4, qf[hlf]);
+    const uint32_t kk[4] = {kw.x, kw.y, kw.z, kw.w}, qq[4] = {qw.x, qw.y, qw.z, qw.w};
 #pragma unroll
-    for (int e = 0; e < 8; ++e) dot = __builtin_fmaf(qv[e], kf[e], dot);
+    for (int e = 0; e < 4; ++e)
+      dot = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qq[e]), __builtin_bit_cast(bf16x2_t, kk[e]), dot,
+                                            false);
   }
   dot = xor32_sum(xor16_sum(dot));
   const float m_self = sep ? dot : __builtin_fmaf(dot, scale2, -self_bias);
-  const float m_new = fmaxf(m_run, m_self);
-  const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * SC);
-  const float p_self = __builtin_amdgcn_exp2f((m_self - m_new) * SC);
-  m_run = m_new;
-  lsum = __builtin_fmaf(lsum, alpha, g4 == 0 ? p_self : 0.f);
+  // as for the key tiles, the running maximum moves only when the own-key score exceeds
+  // it by more than th; decided per query (lane), so that a candidate's result does not
+  // depend on the other candidates of its block (the branch is skipped when no lane needs
+  // it)
+  if (m_self > m_run + th) {
+    const float alpha = __builtin_amdgcn_exp2f((m_run - m_self) * SC);
+    m_run = m_self;
+    lsum *= alpha;
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) accO[nb] = accO[nb] * alpha;
+  }
+  const float p_self = __builtin_amdgcn_exp2f((m_self - m_run) * SC);
+  lsum += g4 == 0 ? p_self : 0.f;
+  uint32_t hi = 0xFFFF0000u;  // kept in a scalar register
+  asm volatile("" : "+s"(hi));
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) {
     const u32x2_t vv = vself[nb];
-    const float v4[4] = {__uint_as_float(vv.x << 16), __uint_as_float(vv.x & 0xFFFF0000u),
-                         __uint_as_float(vv.y << 16), __uint_as_float(vv.y & 0xFFFF0000u)};
+    const float v4[4] = {__uint_as_float(vv.x << 16), __uint_as_float(vv.x & hi), __uint_as_float(vv.y << 16),
+                         __uint_as_float(vv.y & hi)};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) accO[nb][i] = __builtin_fmaf(accO[nb][i], alpha, p_self * v4[i]);
+    for (int i = 0; i < 4; ++i) accO[nb][i] = __builtin_fmaf(p_self, v4[i], accO[nb][i]);
   }
 }
 
@@ -824,7 +838,7 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
     loop(std::false_type{});
   }
   wait_vmcnt<0>();  // no direct load may still be writing LDS when the workgroup ends
-  if (is_cand) merge_self(kself, vself, qf, SEP, a.scale2, tbk_self, SC, g4, m_run, lsum, accO);
+  if (is_cand) merge_self(kself, vself, qf, SEP, a.scale2, tbk_self, SC, th, g4, m_run, lsum, accO);
 
   // ---- epilogue
   const float ltot = xor32_sum(xor16_sum(lsum));
@@ -846,20 +860,29 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
 // One workgroup per (user, head) pair, for batches whose longest history fits in LDS
 // (PAIR_MAXK keys).  The pair's whole K and V history goes into LDS once (direct loads,
 // 64-key tiles with the ring kernel's swizzles and transposing V reads), together with
-// every key's bias term.  The 16 waves then work through the pair's 16-query units
-// (candidate blocks first, then history blocks newest first) with no further barrier:
+// every key's bias term.  The 8 waves then work through the pair's 32-query units
+// (candidate units first, then history units newest first) with no further barrier:
 // each wave runs its units' key tiles from LDS on its own.  Against the tile grid this
 // loads every K/V byte of a pair once instead of once per query tile, and pays one
 // workgroup prologue per pair instead of one per query tile.  Workgroups take the users
 // heaviest first (see below), so the light pairs fill the end of the launch.
+// A unit is two 16-query blocks, A and B, that share every K and V fragment read (half
+// the LDS traffic per query of one block per wave).  Per key tile the wave issues both
+// blocks' score products, runs A's softmax while B's products finish, then B's softmax
+// while A's PV product runs, so one wave keeps the matrix cores and the vector ALUs busy
+// at once, and two waves per SIMD (256 registers each) fill the rest.  Each block's
+// arithmetic is that of one 16-query wave of the ring kernel: the same bias terms, the
+// same lazy-rescaling decisions over its 16 queries, the same row-sum order, so candidate
+// rows come out of both kernels bit for bit alike.
 // The bias reference point of the whole pair is the candidates' shared (p, tau) = (N,
 // request time), so candidate rows carry no row term.  A candidate's own key is merged
 // into its softmax state after the history keys (same result as seeding with it).
-constexpr int PAIR_WAVES = 16;
+constexpr int PAIR_WAVES = 8;
 constexpr int PAIR_NT = 64 * PAIR_WAVES;
 constexpr int PAIR_MAXT = 9;                 // key tiles held in LDS
 constexpr int PAIR_MAXK = PAIR_MAXT * AK;    // longest history this kernel takes
-static_assert(PAIR_MAXK <= PAIR_NT, "one bias key per thread");
+constexpr int PQ = 2 * QW;                   // queries per unit (two 16-query blocks)
+static_assert(PAIR_WAVES * 8 == AK, "each wave loads 8 rows of every K and V tile");
 
 template <int VAR>
 __global__ void __launch_bounds__(PAIR_NT) attn_fwd_pair_kernel(AttnArgs a) {
@@ -938,36 +961,69 @@ __global__ void __launch_bounds__(PAIR_NT) attn_fwd_pair_kernel(AttnArgs a) {
   const float spr = SEP ? sp2 * a.rscale2 : sp2;
   const float str = SEP ? st2 * a.rscale2 : st2;
 
-  // ---- the pair's K/V tiles: waves 0-7 load K, waves 8-15 V, rows 8 (w % 8) .. + 7 of
-  // every tile (lane l: row 8 (w % 8) + l / 8, LDS chunk l % 8 <- global chunk
-  // (l % 8) ^ ((row >> 1) & 7) for K, (l % 8) ^ 2 ((row >> 1) & 3) for V, as in the ring
-  // kernel; rows past the history end
-  // re-read its last row).
+  // ---- units: 32-query blocks, candidates first (each sees every key), then history
+  // blocks newest first; wave w takes units w, w + 8, ...
+  const int nu_c = (a.m + PQ - 1) / PQ;
+  const int nu_h = a.hist_tiles > 0 ? (N + PQ - 1) / PQ : 0;
+  const int n_units = nu_c + nu_h;
+  // unit k's first row in q / k / v / o (wave-uniform) and its number of queries; a
+  // lane's rows are that row plus a small offset, so addresses are a scalar base plus a
+  // 32-bit lane offset (row strides fit 32 bits: checked on the host)
+  auto unit_row0 = [&](int k) -> int64_t {
+    return k < nu_c ? a.crow0 + static_cast<int64_t>(u) * a.m + k * PQ : off + (nu_h - 1 - (k - nu_c)) * PQ;
+  };
+  auto unit_nq = [&](int k) -> int { return min(PQ, k < nu_c ? a.m - k * PQ : N - (nu_h - 1 - (k - nu_c)) * PQ); };
+  const uint32_t ldq = static_cast<uint32_t>(a.ld_qkv);
+  u32x4_t qn[2][2] = {};
+  auto fetch_q = [&](int k) __attribute__((always_inline)) {
+    const char* qb = reinterpret_cast<const char*>(a.q + unit_row0(k) * a.ld_qkv + h * DH);
+    const int nq = unit_nq(k);
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {  // rows past the unit's last query re-read it
+      const uint32_t lo = (static_cast<uint32_t>(min(hb * QW + l16, nq - 1)) * ldq + g4 * 8) * 2u;
+      qn[hb][0] = *reinterpret_cast<const u32x4_t*>(qb + lo);
+      qn[hb][1] = *reinterpret_cast<const u32x4_t*>(qb + lo + 64);
+    }
+  };
+  // the first unit's query fragments travel with the K/V tiles
+  if (wave < n_units) fetch_q(wave);
+
+  // ---- the pair's K/V tiles.  A tile's K half is row-major (key, dim) as the ring
+  // kernel keeps it: wave w loads rows 8 w .. 8 w + 7 straight into LDS (lane l: row
+  // 8 w + l / 8, LDS chunk l % 8 <- global chunk (l % 8) ^ ((row >> 1) & 7)).  Its V half
+  // is V^T (dim, key), with the keys of each 32-key half in the order the P^T fragments
+  // hold them (vt_slot) and the same 16-byte chunk swizzle by (dim >> 1) & 7, so that a
+  // PV operand (one dim, the 8 keys a lane group multiplies) is one 16-byte read.  V
+  // rows come through registers and are written transposed, once per pair.  Rows past the
+  // history end re-read its last row.
+  uint4 vrow[PAIR_MAXT];
+  const int lr = wave * 8 + (lane >> 3);
+  const int lc = lane & 7;
   {
-    const bool ldk = wave < 8;
-    const int lr = (wave & 7) * 8 + (lane >> 3);
-    const int lc = lane & 7;
     const uint32_t row_bytes = static_cast<uint32_t>(a.ld_h) * 2u;
-    const char* g = reinterpret_cast<const char*>((ldk ? a.kh : a.vh) + off * a.ld_h + h * DH +
-                                                  ((lc ^ (ldk ? ((lr >> 1) & 7) : 2 * ((lr >> 1) & 3))) * 8));
-    bf16_t* dst = sKV + (ldk ? 0 : AK * DH) + (wave & 7) * 8 * DH;
-    for (int t = 0; t < n_tiles; ++t) {
-      const uint32_t ro = static_cast<uint32_t>(min(t * AK + lr, N - 1)) * row_bytes;
-      __builtin_amdgcn_global_load_lds((glb_void_t*)(g + ro), (lds_void_t*)(dst + t * STAGE), 16, 0, 0);
+    const char* gk = reinterpret_cast<const char*>(a.kh + off * a.ld_h + h * DH + ((lc ^ ((lr >> 1) & 7)) * 8));
+    const char* gv = reinterpret_cast<const char*>(a.vh + off * a.ld_h + h * DH + lc * 8);
+#pragma unroll
+    for (int t = 0; t < PAIR_MAXT; ++t) {
+      if (t < n_tiles) {
+        const uint32_t ro = static_cast<uint32_t>(min(t * AK + lr, N - 1)) * row_bytes;
+        __builtin_amdgcn_global_load_lds((glb_void_t*)(gk + ro), (lds_void_t*)(sKV + t * STAGE + wave * 8 * DH), 16, 0, 0);
+        vrow[t] = *reinterpret_cast<const uint4*>(gv + ro);
+      }
     }
   }
 
   // ---- every key's bias term relative to the candidates; -inf past the history end, so
   // that those keys' scores come out -inf (probability 0) without a mask
-  if (tid < n_tiles * AK) {
+  for (int j = tid; j < n_tiles * AK; j += PAIR_NT) {
     float w = -INFINITY;
     int32_t tk = 0;
-    if (tid < N) {
-      tk = static_cast<int32_t>(a.ts[off + tid] - ts_ref);
-      w = key_term(TBK, spr, str, tid - N, tk);
+    if (j < N) {
+      tk = static_cast<int32_t>(a.ts[off + j] - ts_ref);
+      w = key_term(TBK, spr, str, j - N, tk);
     }
-    sW[tid] = w;
-    sT[tid] = tk;
+    sW[j] = w;
+    sT[j] = tk;
   }
   if constexpr (TBK)
     for (int k = tid; k < a.tb_p2; k += PAIR_NT) {
@@ -975,6 +1031,22 @@ __global__ void __launch_bounds__(PAIR_NT) attn_fwd_pair_kernel(AttnArgs a) {
       sTB[k] = b > INT32_MAX ? INT32_MAX : (b < INT32_MIN ? INT32_MIN : static_cast<int32_t>(b));
     }
   wait_vmcnt<0>();
+  {
+    const int slot = vt_slot(lr);
+#pragma unroll
+    for (int t = 0; t < PAIR_MAXT; ++t) {
+      if (t < n_tiles) {
+        const uint32_t w4[4] = {vrow[t].x, vrow[t].y, vrow[t].z, vrow[t].w};
+        bf16_t* vt = sKV + t * STAGE + AK * DH;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int d = lc * 8 + e;
+          vt[d * AK + (((slot >> 3) ^ ((d >> 1) & 7)) << 3) + (slot & 7)] =
+              static_cast<bf16_t>((e & 1) ? (w4[e >> 1] >> 16) : (w4[e >> 1] & 0xFFFFu));
+        }
+      }
+    }
+  }
   lds_sync();
   float tbk_self = 0.f;  // bucketed time term of a candidate's own key (gap 0)
   if constexpr (TBK) {
@@ -987,109 +1059,132 @@ __global__ void __launch_bounds__(PAIR_NT) attn_fwd_pair_kernel(AttnArgs a) {
   // LDS offsets (bf16 elements) of this lane's fragments inside a tile
   const int k_off0 = l16 * DH + (((0 + g4) ^ ((l16 >> 1) & 7)) * 8);
   const int k_off1 = l16 * DH + (((4 + g4) ^ ((l16 >> 1) & 7)) * 8);
-  int v_off[4];
-#pragma unroll
-  for (int nb = 0; nb < 4; ++nb)
-    v_off[nb] = AK * DH + (4 * g4 + (l16 >> 2)) * DH +
-                (((2 * nb + ((l16 & 3) >> 1)) ^ (2 * (((4 * g4 + (l16 >> 2)) >> 1) & 3))) * 8) + (l16 & 1) * 4;
-
-  // ---- units: 16-query blocks, candidates first (each sees every key), then history
-  // blocks newest first; wave w takes units w, w + 16, ...
-  const int nb_c = (a.m + QW - 1) / QW;
-  const int nb_h = a.hist_tiles > 0 ? (N + QW - 1) / QW : 0;
-  const int n_units = nb_c + nb_h;
-  auto q_row = [&](int k) -> int64_t {  // the global row of this lane's query in unit k
-    if (k < nb_c) return a.crow0 + static_cast<int64_t>(u) * a.m + min(k * QW + l16, a.m - 1);
-    const int b = nb_h - 1 - (k - nb_c);
-    return off + min(b * QW + l16, N - 1);
+  // V^T: dim nb * 16 + l16, the 8 keys of lane group g4 in 32-key half ks
+  const int vt_off0 = AK * DH + l16 * AK + (((0 + g4) ^ ((l16 >> 1) & 7)) * 8);
+  const int vt_off1 = AK * DH + l16 * AK + (((4 + g4) ^ ((l16 >> 1) & 7)) * 8);
+  // a tile's start as a wave-uniform value: every fragment read is then one address
+  // register plus a constant offset
+  auto tile_at = [&](int kt) __attribute__((always_inline)) {
+    return sKV + __builtin_amdgcn_readfirstlane(kt * STAGE);
   };
-  u32x4_t qn[2] = {};
-  if (wave < n_units) {
-    const int64_t ro = q_row(wave) * a.ld_qkv + h * DH + g4 * 8;
-    qn[0] = *reinterpret_cast<const u32x4_t*>(a.q + ro);
-    qn[1] = *reinterpret_cast<const u32x4_t*>(a.q + ro + 32);
-  }
 
   for (int k = wave; k < n_units; k += PAIR_WAVES) {
-    const bool is_cand = k < nb_c;
-    const int b = is_cand ? k : nb_h - 1 - (k - nb_c);
-    const int qf0 = b * QW;                               // first query of the unit
-    const int nq = min(QW, (is_cand ? a.m : N) - qf0);
-    const bool q_valid = l16 < nq;
-    const int q_slot = is_cand ? N + qf0 + l16 : qf0 + l16;
-    const int64_t qrow = q_row(k);
-    const int k_lim = (is_cand || FULL) ? (N - 1) : min(q_slot, N - 1);
-    const int kmax_blk = (is_cand || FULL) ? (N - 1) : min(qf0 + QW - 1, N - 1);
+    const bool is_cand = k < nu_c;
+    const int b = is_cand ? k : nu_h - 1 - (k - nu_c);
+    const int qf0 = b * PQ;                               // first query of the unit
+    const int nq = min(PQ, (is_cand ? a.m : N) - qf0);
     const int n_t = (is_cand || FULL) ? n_tiles : (qf0 + nq - 1) / AK + 1;
-    bf16x8_t qf[2] = {__builtin_bit_cast(bf16x8_t, qn[0]), __builtin_bit_cast(bf16x8_t, qn[1])};
+    // causal history units: the 16-key block of the first (newest) tile that holds block
+    // A's diagonal; block B's is the next one (query blocks are 16-aligned, the unit's
+    // 32 queries lie in one tile)
+    const int kd0 = (qf0 - (n_t - 1) * AK) >> 4;
+    const int64_t row0 = unit_row0(k);
+    bf16x8_t qf[2][2];
+    bool q_valid[2];
+    int q_slot[2];
+    int32_t tq[2];
+    float w_i_ref[2];
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      qf[hb][0] = __builtin_bit_cast(bf16x8_t, qn[hb][0]);
+      qf[hb][1] = __builtin_bit_cast(bf16x8_t, qn[hb][1]);
+      q_valid[hb] = hb * QW + l16 < nq;
+      q_slot[hb] = (is_cand ? N : 0) + qf0 + hb * QW + l16;
+      // the row term (log2 units) and the query's own time
+      w_i_ref[hb] = (!is_cand && q_valid[hb]) ? sW[min(q_slot[hb], N - 1)] * SC : 0.f;
+      tq[hb] = (!is_cand && N > 0) ? sT[min(q_slot[hb], N - 1)] : 0;
+    }
     // the next unit's query fragments
-    if (k + PAIR_WAVES < n_units) {
-      const int64_t ro = q_row(k + PAIR_WAVES) * a.ld_qkv + h * DH + g4 * 8;
-      qn[0] = *reinterpret_cast<const u32x4_t*>(a.q + ro);
-      qn[1] = *reinterpret_cast<const u32x4_t*>(a.q + ro + 32);
-    }
+    if (k + PAIR_WAVES < n_units) fetch_q(k + PAIR_WAVES);
     // a candidate's own key and value (merged after the history keys)
-    u32x4_t kself[2] = {};
-    u32x2_t vself[4] = {};
+    u32x4_t kself[2][2] = {};
+    u32x2_t vself[2][4] = {};
     if (is_cand) {
-      const int64_t ro = qrow * a.ld_qkv + h * DH;
-      kself[0] = *reinterpret_cast<const u32x4_t*>(a.k + ro + g4 * 8);
-      kself[1] = *reinterpret_cast<const u32x4_t*>(a.k + ro + g4 * 8 + 32);
+      const char* kb0 = reinterpret_cast<const char*>(a.k + row0 * a.ld_qkv + h * DH);
+      const char* vb0 = reinterpret_cast<const char*>(a.v + row0 * a.ld_qkv + h * DH);
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) vself[nb] = *reinterpret_cast<const u32x2_t*>(a.v + ro + nb * 16 + g4 * 4);
+      for (int hb = 0; hb < 2; ++hb) {
+        const uint32_t lo = static_cast<uint32_t>(min(hb * QW + l16, nq - 1)) * ldq * 2u;
+        kself[hb][0] = *reinterpret_cast<const u32x4_t*>(kb0 + lo + g4 * 16);
+        kself[hb][1] = *reinterpret_cast<const u32x4_t*>(kb0 + lo + g4 * 16 + 64);
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) vself[hb][nb] = *reinterpret_cast<const u32x2_t*>(vb0 + lo + nb * 32 + g4 * 8);
+      }
     }
-    // the row term (log2 units) and the query's own time
-    const float w_i_ref = (!is_cand && q_valid) ? sW[min(q_slot, N - 1)] * SC : 0.f;
-    const float w_i_u = w_i_ref / SC;
-    const int32_t tq = (!is_cand && N > 0) ? sT[min(q_slot, N - 1)] : 0;
-    // a history block far from the candidates' reference point forms each bias exactly
-    // from the pair's own position and time differences (the row term is then 0)
-    const bool far = CAN_FAR && __builtin_amdgcn_ballot_w64(fabsf(w_i_ref) > BIAS_FAR_LOG2) != 0;
-    const float w_i = far ? 0.f : w_i_ref;
+    // a history unit far from the candidates' reference point forms each bias exactly
+    // from the pair's own position and time differences (the row terms are then 0)
+    const bool far = CAN_FAR && __builtin_amdgcn_ballot_w64(fabsf(w_i_ref[0]) > BIAS_FAR_LOG2 ||
+                                                            fabsf(w_i_ref[1]) > BIAS_FAR_LOG2) != 0;
+    const float w_i[2] = {far ? 0.f : w_i_ref[0], far ? 0.f : w_i_ref[1]};
+    const float w_i_u[2] = {w_i_ref[0] / SC, w_i_ref[1] / SC};
 
-    f32x4_t accO[4];
+    f32x4_t accO[2][4];
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) accO[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float m_run = -1e30f, lsum = 0.f;
+    for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) accO[hb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float m_run[2] = {-1e30f, -1e30f}, lsum[2] = {0.f, 0.f};
+    f32x4_t s[2][4];
+    uint32_t ones = 0x3F803F80u;  // two bf16 ones, kept in a scalar register
+    asm volatile("" : "+s"(ones));
 
-    // the exact bias of key slot j for this lane's query, in score units (far blocks): from
-    // the integer position and time differences, each product rounded once
-    auto exact_bias = [&](int j, int32_t tk) __attribute__((always_inline)) {
-      return key_term(false, spr, str, j - q_slot, tk - tq);
+    // the exact bias of key slot j for this lane's query of block hb, in score units (far
+    // units): from the integer position and time differences, each product rounded once
+    auto exact_bias = [&](int hb, int j, int32_t tk) __attribute__((always_inline)) {
+      return key_term(false, spr, str, j - q_slot[hb], tk - tq[hb]);
     };
-    // S^T of key tile kt (with the separable bias: seeded with the key terms)
-    auto scores = [&](auto masked_tag, auto far_tag, int kt, f32x4_t(&s)[4]) __attribute__((always_inline)) {
+    // S^T of key tile kt for both blocks (with the separable bias: seeded with the key
+    // terms); each K fragment read feeds both blocks
+    auto scores = [&](auto masked_tag, auto far_tag, int kt) __attribute__((always_inline)) {
       constexpr bool MASKED = decltype(masked_tag)::value;
       constexpr bool FAR = decltype(far_tag)::value;
-      const bf16_t* stg = sKV + kt * STAGE;
+      const bf16_t* stg = tile_at(kt);
       const int base = kt * AK;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
         if constexpr (SEP && FAR) {
           const int4 t4 = reinterpret_cast<const int4*>(sT)[(base >> 2) + kb * 4 + g4];
           const int j0 = base + kb * 16 + g4 * 4;
-          s[kb] = f32x4_t{exact_bias(j0, t4.x), exact_bias(j0 + 1, t4.y), exact_bias(j0 + 2, t4.z),
-                          exact_bias(j0 + 3, t4.w)};
+#pragma unroll
+          for (int hb = 0; hb < 2; ++hb)
+            s[hb][kb] = f32x4_t{exact_bias(hb, j0, t4.x), exact_bias(hb, j0 + 1, t4.y),
+                                exact_bias(hb, j0 + 2, t4.z), exact_bias(hb, j0 + 3, t4.w)};
         } else if constexpr (SEP) {
           const float4 w = reinterpret_cast<const float4*>(sW)[(base >> 2) + kb * 4 + g4];
-          s[kb] = f32x4_t{w.x, w.y, w.z, w.w};
+          s[0][kb] = f32x4_t{w.x, w.y, w.z, w.w};
+          s[1][kb] = s[0][kb];
         } else {
-          s[kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          s[0][kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          s[1][kb] = s[0][kb];
         }
-        if (!MASKED || base + kb * 16 <= kmax_blk) {
-          const bf16x8_t k0 = as_bf16x8(*reinterpret_cast<const uint4*>(stg + kb * 16 * DH + k_off0));
-          const bf16x8_t k1 = as_bf16x8(*reinterpret_cast<const uint4*>(stg + kb * 16 * DH + k_off1));
-          s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[0], s[kb], 0, 0, 0);
-          s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[1], s[kb], 0, 0, 0);
+        if (MASKED && kb > kd0) {  // block A lies wholly above its diagonal here
+          s[0][kb] = f32x4_t{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+          if (kb > kd0 + 1) {
+            s[1][kb] = s[0][kb];
+            continue;
+          }
+        }
+        const bf16x8_t k0 = as_bf16x8(*reinterpret_cast<const uint4*>(stg + kb * 16 * DH + k_off0));
+        const bf16x8_t k1 = as_bf16x8(*reinterpret_cast<const uint4*>(stg + kb * 16 * DH + k_off1));
+        if (!MASKED || kb <= kd0) {
+          s[0][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[0][0], s[0][kb], 0, 0, 0);
+          s[1][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[1][0], s[1][kb], 0, 0, 0);
+          s[0][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[0][1], s[0][kb], 0, 0, 0);
+          s[1][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[1][1], s[1][kb], 0, 0, 0);
+        } else {
+          s[1][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[1][0], s[1][kb], 0, 0, 0);
+          s[1][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[1][1], s[1][kb], 0, 0, 0);
         }
       }
     };
-    // bias (variants), mask, online softmax and O^T += V^T P^T for key tile kt
-    auto tile = [&](auto masked_tag, auto far_tag, int kt, f32x4_t(&s)[4]) __attribute__((always_inline)) {
+    // block hb on key tile kt: bias (variants), mask, online softmax; P^T as two bf16
+    // fragments
+    auto softmax = [&](auto masked_tag, auto far_tag, int kt, auto hb_tag, bf16x8_t(&pf)[2]) __attribute__((always_inline)) {
       constexpr bool MASKED = decltype(masked_tag)::value;
       constexpr bool FAR = decltype(far_tag)::value;
-      const bf16_t* stg = sKV + kt * STAGE;
+      constexpr int hb = decltype(hb_tag)::value;
       const int base = kt * AK;
+      f32x4_t(&sc)[4] = s[hb];
       if constexpr (!SEP) {
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
@@ -1100,80 +1195,102 @@ __global__ void __launch_bounds__(PAIR_NT) attn_fwd_pair_kernel(AttnArgs a) {
           const int32_t tk[4] = {t4.x, t4.y, t4.z, t4.w};
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            // fully visible: -|w_j - w_i|, or the exact -|bias| of the pair in far blocks
-            const float fb = FAR ? -fabsf(exact_bias(base + kb * 16 + g4 * 4 + i, tk[i])) : -fabsf(wk[i] - w_i_u);
-            float x = biased(s[kb][i], a.scale2, FULL ? fb : wk[i]);
-            if constexpr (TBK) x -= st2 * static_cast<float>(bucket_lookup(sLUT, sTB, a.tb_p2, abs(tq - tk[i])));
-            s[kb][i] = x;
+            // fully visible: -|w_j - w_i|, or the exact -|bias| of the pair in far units (keys
+            // past the history end, whose key terms are -inf, stay -inf)
+            const float fb = FAR ? (wk[i] == -INFINITY ? -INFINITY : -fabsf(exact_bias(hb, base + kb * 16 + g4 * 4 + i, tk[i])))
+                                 : -fabsf(wk[i] - w_i_u[hb]);
+            float x = biased(sc[kb][i], a.scale2, FULL ? fb : wk[i]);
+            if constexpr (TBK) x -= st2 * static_cast<float>(bucket_lookup(sLUT, sTB, a.tb_p2, abs(tq[hb] - tk[i])));
+            sc[kb][i] = x;
           }
         }
       }
-      if constexpr (MASKED) {
-        const int lim = k_lim - base - g4 * 4;
+      if constexpr (MASKED) {  // the diagonal block: key g4 * 4 + i against query l16
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
+          if (kb == kd0 + hb) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (kb * 16 + i > lim) s[kb][i] = -INFINITY;
+            for (int i = 0; i < 4; ++i)
+              if (g4 * 4 + i > l16) sc[kb][i] = -INFINITY;
+          }
       }
-      float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), s[0][2]), fmaxf(fmaxf(s[0][3], s[1][0]), s[1][1]));
-      mx = fmaxf(fmaxf(mx, s[1][2]), fmaxf(fmaxf(s[1][3], s[2][0]), s[2][1]));
-      mx = fmaxf(fmaxf(mx, s[2][2]), fmaxf(fmaxf(s[2][3], s[3][0]), s[3][1]));
-      mx = fmaxf(fmaxf(mx, s[3][2]), s[3][3]);
+      float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), sc[0][2]), fmaxf(fmaxf(sc[0][3], sc[1][0]), sc[1][1]));
+      mx = fmaxf(fmaxf(mx, sc[1][2]), fmaxf(fmaxf(sc[1][3], sc[2][0]), sc[2][1]));
+      mx = fmaxf(fmaxf(mx, sc[2][2]), fmaxf(fmaxf(sc[2][3], sc[3][0]), sc[3][1]));
+      mx = fmaxf(fmaxf(mx, sc[3][2]), sc[3][3]);
       mx = xor32_max(xor16_max(mx));
-      if (__builtin_amdgcn_ballot_w64(mx > m_run + th) != 0) {
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * SC);
-        m_run = m_new;
-        lsum *= alpha;
+      if (__builtin_amdgcn_ballot_w64(mx > m_run[hb] + th) != 0) {
+        const float m_new = fmaxf(m_run[hb], mx);
+        const float alpha = __builtin_amdgcn_exp2f((m_run[hb] - m_new) * SC);
+        m_run[hb] = m_new;
+        lsum[hb] *= alpha;
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) accO[nb] = accO[nb] * alpha;
+        for (int nb = 0; nb < 4; ++nb) accO[hb][nb] = accO[hb][nb] * alpha;
       }
-      const float mb = -m_run * SC;
-      bf16x8_t pf[2];
+      const float mb = -m_run[hb] * SC;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         uint4 pk;
         uint32_t* pw = reinterpret_cast<uint32_t*>(&pk);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const f32x4_t& sb = s[2 * ks + (j >> 1)];
+          const f32x4_t& sb = sc[2 * ks + (j >> 1)];
           const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sb[(j & 1) * 2], SC, mb));
           const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sb[(j & 1) * 2 + 1], SC, mb));
           pw[j] = pack_bf16x2(p0, p1);
-          lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw[j]),
-                                                  __builtin_bit_cast(bf16x2_t, 0x3F803F80u), lsum, false);
+          lsum[hb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, ones),
+                                                      __builtin_bit_cast(bf16x2_t, pw[j]), lsum[hb], false);
         }
         pf[ks] = as_bf16x8(pk);
       }
+    };
+    // V^T fragments of key tile kt (shared by both blocks)
+    bf16x8_t vf[2][4];
+    auto read_v = [&](auto masked_tag, int kt) __attribute__((always_inline)) {
+      constexpr bool MASKED = decltype(masked_tag)::value;
+      const bf16_t* stg = tile_at(kt);
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        if (MASKED && base + ks * 32 > kmax_blk) continue;
+        if (MASKED && 2 * ks > kd0 + 1) continue;  // past both blocks' diagonals
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-          const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(stg + v_off[nb] + (ks * 32) * DH));
-          const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(stg + v_off[nb] + (ks * 32 + 16) * DH));
-          const v4i16_t both[2] = {lo, hi};
-          accO[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, both), pf[ks], accO[nb], 0, 0, 0);
-        }
+        for (int nb = 0; nb < 4; ++nb)
+          vf[ks][nb] = as_bf16x8(*reinterpret_cast<const uint4*>(stg + (ks ? vt_off1 : vt_off0) + nb * 16 * AK));
       }
     };
-    // Key tiles newest first; only the first can cross a query's limit.  A candidate's
-    // limit is the history end, which the -inf bias terms already enforce (candidate
-    // blocks are never far: their reference point is their own).
+    // O^T += V^T P^T for block hb
+    auto pv = [&](auto masked_tag, int kt, auto hb_tag, const bf16x8_t(&pf)[2]) __attribute__((always_inline)) {
+      constexpr bool MASKED = decltype(masked_tag)::value;
+      constexpr int hb = decltype(hb_tag)::value;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        if (MASKED && 2 * ks > kd0 + hb) continue;  // past this block's diagonal
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+          accO[hb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[ks][nb], pf[ks], accO[hb][nb], 0, 0, 0);
+      }
+    };
+    // one key tile: both blocks' scores, A's softmax, A's PV while B's softmax runs, B's PV
+    auto tile = [&](auto masked_tag, auto far_tag, int kt) __attribute__((always_inline)) {
+      using HA = std::integral_constant<int, 0>;
+      using HB = std::integral_constant<int, 1>;
+      bf16x8_t pa[2], pb[2];
+      scores(masked_tag, far_tag, kt);
+      softmax(masked_tag, far_tag, kt, HA{}, pa);
+      read_v(masked_tag, kt);
+      pv(masked_tag, kt, HA{}, pa);
+      softmax(masked_tag, far_tag, kt, HB{}, pb);
+      pv(masked_tag, kt, HB{}, pb);
+    };
+    // Key tiles newest first; only the first can cross a causal query's limit.  A
+    // candidate's limit is the history end, which the -inf bias terms already enforce, and
+    // so is every key's limit under the fully visible history (candidate units are never
+    // far: their reference point is their own).
     auto run_tiles = [&](auto far_tag) __attribute__((always_inline)) {
-      f32x4_t sc[4];
-      if (is_cand) {
-        scores(std::false_type{}, far_tag, n_t - 1, sc);
-        tile(std::false_type{}, far_tag, n_t - 1, sc);
-      } else {
-        scores(std::true_type{}, far_tag, n_t - 1, sc);
-        tile(std::true_type{}, far_tag, n_t - 1, sc);
-      }
-      for (int kt = n_t - 2; kt >= 0; --kt) {
-        scores(std::false_type{}, far_tag, kt, sc);
-        tile(std::false_type{}, far_tag, kt, sc);
-      }
+      if (is_cand || FULL)
+        tile(std::false_type{}, far_tag, n_t - 1);
+      else
+        tile(std::true_type{}, far_tag, n_t - 1);
+      for (int kt = n_t - 2; kt >= 0; --kt) tile(std::false_type{}, far_tag, kt);
     };
     if (n_t > 0) {
       if constexpr (CAN_FAR) {
@@ -1186,20 +1303,30 @@ __global__ void __launch_bounds__(PAIR_NT) attn_fwd_pair_kernel(AttnArgs a) {
       }
     }
 
-    // the candidate's own key: bias 0 (it is the reference point)
-    if (is_cand) merge_self(kself, vself, qf, SEP, a.scale2, tbk_self, SC, g4, m_run, lsum, accO);
-    const float ltot = xor32_sum(xor16_sum(lsum));
-    if (q_valid) {
-      const float inv = __builtin_amdgcn_rcpf(ltot);  // (as in the ring kernel)
+    // Every load of this unit has landed by now (the next unit's query fragments too):
+    // waiting for them here, ahead of the stores, leaves the stores in flight into the
+    // next unit instead of a wait for everything at its start.
+    wait_vmcnt<0>();
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        uint2 o;
-        o.x = pack_bf16x2(accO[nb][0] * inv, accO[nb][1] * inv);
-        o.y = pack_bf16x2(accO[nb][2] * inv, accO[nb][3] * inv);
-        *reinterpret_cast<uint2*>(a.o + qrow * a.ld_o + h * DH + nb * 16 + g4 * 4) = o;
+    for (int hb = 0; hb < 2; ++hb) {
+      // the candidate's own key: bias 0 (it is the reference point)
+      if (is_cand)
+        merge_self(kself[hb], vself[hb], qf[hb], SEP, a.scale2, tbk_self, SC, th, g4, m_run[hb], lsum[hb], accO[hb]);
+      const float ltot = xor32_sum(xor16_sum(lsum[hb]));
+      if (q_valid[hb]) {
+        const float inv = __builtin_amdgcn_rcpf(ltot);  // (as in the ring kernel)
+        char* ob = reinterpret_cast<char*>(a.o + row0 * a.ld_o + h * DH);
+        const uint32_t lo = (static_cast<uint32_t>(hb * QW + l16) * static_cast<uint32_t>(a.ld_o) + g4 * 4) * 2u;
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+          uint2 o;
+          o.x = pack_bf16x2(accO[hb][nb][0] * inv, accO[hb][nb][1] * inv);
+          o.y = pack_bf16x2(accO[hb][nb][2] * inv, accO[hb][nb][3] * inv);
+          *reinterpret_cast<uint2*>(ob + lo + nb * 32) = o;
+        }
+        if (a.lse && g4 == 0)
+          a.lse[(row0 + hb * QW + l16) * a.H + h] = LN2 * (m_run[hb] * SC + __builtin_amdgcn_logf(ltot) - (FULL ? 0.f : w_i[hb]));
       }
-      if (a.lse && g4 == 0)
-        a.lse[qrow * a.H + h] = LN2 * (m_run * SC + __builtin_amdgcn_logf(ltot) - (FULL ? 0.f : w_i));
     }
   }
 }

@@ -168,6 +168,13 @@ typedef struct {
 /* Weights of one block.  GENRANK_BLOCK_ATTN_ONLY: y = Wo . attn(Wqkv . x).
  * GENRANK_BLOCK_PRENORM: x1 = x + Wo . attn(Wqkv . rmsnorm(x)*g1);
  *                         y = x1 + W2 . silu(W1 . rmsnorm(x1)*g2).
+ * The pages fix the attention ([GR-zh] section 1.4.2, [FR-en] section 7.2) but not what
+ * surrounds it in a block.  This library takes the plain pre-norm reading: RMSNorm
+ * (eps 1e-6, learned gain) before the attention and before the FFN, bias-free projections,
+ * residual adds, a non-gated SiLU FFN of ffn_dim, and (genrank_head_fwd) a final RMSNorm
+ * and a 4-logit head with bias.  The attention-only block is the single-layer form of the
+ * pages' inference description: QKV, attention, output projection, no norm or residual.
+ * genrank_layer_fwd, genrank_layer_bwd and genrank_linear compute exactly these.
  * Matrices are in batch.dtype; gains are f32. */
 typedef struct {
   const void* wqkv;  /* [3d, d]: rows [0,d) -> Q, [d,2d) -> K, [2d,3d) -> V; head h at h*dh */

@@ -215,7 +215,7 @@ def test_attn_bf16_resident_limit(lengths, m):
 
 
 def test_attn_bf16_more_users_than_threads():
-    """1,100 users (more than the 1,024 threads that order the users heaviest first, so the
+    """1,100 users (more than the 512 threads that order the users heaviest first, so the
     launch takes them in plain order), short jagged histories; sampled users checked."""
     say("attn: bf16 1100 users")
     cfg = synth.make_config("infer_1layer_bf16", m=3)
