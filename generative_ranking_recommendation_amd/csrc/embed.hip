@@ -271,11 +271,19 @@ __global__ void __launch_bounds__(EMB_THREADS) embed_sum_kernel(EmbedArgs a) {
   }
 }
 
-// Gather phase with a fixed 16-byte column per thread: thread t handles column chunk
-// t % cpr of rows t / cpr, t / cpr + rpp, ... (rpp = threads / cpr), four rows in flight
-// (twenty 16-byte loads).  Table reads and output writes are buffer accesses with 32-bit
-// byte offsets (every table is below 4 GB); rows past the chunk write nothing.
+// Gather phase with a fixed column per thread: thread t handles column piece t % cpr of
+// rows t / cpr, t / cpr + rpp, ... (cpr = d / 8 threads per row, rpp = threads / cpr),
+// four rows in flight.  A piece is 16 bytes of each table row (8 bf16 or 4 f32 columns),
+// except for f32 rows summed from bf16 tables: there thread c of a row takes the 4-column
+// groups c and c + cpr (two 8-byte reads per table), so that each of its two 16-byte
+// output stores lands next to its neighbours' (a wave's store covers one contiguous span).
+// Table reads and output writes are buffer accesses with 32-bit byte offsets (every table
+// is below 4 GB); rows past the chunk write nothing.  NT: outputs far larger than the
+// last-level cache go out as streaming (non-temporal) stores, so that they leave no dirty
+// lines behind for the next kernels to evict; smaller ones stay cached for the next kernel.
 constexpr int BUF_DWORD3 = 0x00020000;  // raw buffer descriptor word 3 (gfx9 family)
+constexpr int CPOL_NT = 2;              // buffer cache policy: non-temporal
+constexpr int64_t STREAM_OUT_BYTES = int64_t(128) << 20;  // outputs above this use NT stores
 
 template <typename T>
 __device__ __forceinline__ void add_vec(const uint4& v, float* acc) {
@@ -296,8 +304,9 @@ __device__ __forceinline__ void add_vec(const uint4& v, float* acc) {
 constexpr int SACT_MAX = 32768;
 
 // TO: the element type of the output rows (the tables' type, or f32 rows from bf16 tables).
-template <typename T, typename TO, bool SACT>
+template <typename T, typename TO, bool SACT, bool NT>
 __global__ void __launch_bounds__(EMB_THREADS) embed_sum_rows_kernel(EmbedArgs a) {
+  constexpr int CPOL = NT ? CPOL_NT : 0;
   __shared__ RowIdx sidx[EMB_ROWS];
   __shared__ int64_t sbounds[MAX_BOUNDS];
   __shared__ int red_c[EMB_THREADS / 64];
@@ -312,13 +321,17 @@ __global__ void __launch_bounds__(EMB_THREADS) embed_sum_rows_kernel(EmbedArgs a
     for (int i = threadIdx.x; i < n16; i += EMB_THREADS) s_act[i] = src[i];
     __syncthreads();
   }
+  constexpr bool SPLIT = sizeof(TO) > sizeof(T);  // bf16 tables, f32 rows
   constexpr int V = Vec<T>::N;
   constexpr int UR = 4;
   const int cpr = a.d / V;
   const int rpp = EMB_THREADS / cpr;
   const int rp = threadIdx.x / cpr;
-  const uint32_t colb = static_cast<uint32_t>((threadIdx.x - rp * cpr) * V * sizeof(T));
+  const int c = threadIdx.x - rp * cpr;
   const uint32_t rowb = static_cast<uint32_t>(a.d * sizeof(T));
+  // byte offsets of this thread's piece(s) in a table row and in an output row
+  const uint32_t colb = SPLIT ? 8u * c : static_cast<uint32_t>(c * V * sizeof(T));
+  const uint32_t colb2 = 8u * (c + cpr);  // SPLIT: the second 4-column group
   auto rsrc = [](const void* p, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), static_cast<short>(0), bytes, BUF_DWORD3);
   };
@@ -327,25 +340,44 @@ __global__ void __launch_bounds__(EMB_THREADS) embed_sum_rows_kernel(EmbedArgs a
   const __amdgpu_buffer_rsrc_t rs_pos = rsrc(a.t_pos, a.bytes_pos);
   const __amdgpu_buffer_rsrc_t rs_ri = rsrc(a.t_ri, a.bytes_ri);
   const __amdgpu_buffer_rsrc_t rs_rt = rsrc(a.t_rt, a.bytes_rt);
-  constexpr uint32_t OW = sizeof(TO) / sizeof(T);  // 16-byte output pieces per column chunk
-  const uint32_t orowb = rowb * OW, ocolb = colb * OW;
+  constexpr uint32_t OW = sizeof(TO) / sizeof(T);  // output bytes per table byte
+  const uint32_t orowb = rowb * OW;
   const uint32_t out_bytes = static_cast<uint32_t>(rows) * orowb;
   const __amdgpu_buffer_rsrc_t rs_out = rsrc(static_cast<TO*>(a.out) + row0 * a.d, out_bytes);
+  typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+  // one table piece at byte offset `o` of a row: 16 bytes, or (SPLIT) two 8-byte groups
+  auto load = [&](const __amdgpu_buffer_rsrc_t& rs, uint32_t rowoff) -> uint4 {
+    if constexpr (SPLIT) {
+      const uint2 lo = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, rowoff + colb, 0, 0));
+      const uint2 hi = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, rowoff + colb2, 0, 0));
+      return make_uint4(lo.x, lo.y, hi.x, hi.y);
+    } else {
+      return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, rowoff + colb, 0, 0));
+    }
+  };
+  auto load_act = [&](int act) -> uint4 {
+    const char* base = reinterpret_cast<const char*>(s_act) + min(act, a.n_action) * rowb;
+    if constexpr (SPLIT) {
+      const uint2 lo = *reinterpret_cast<const uint2*>(base + colb);
+      const uint2 hi = *reinterpret_cast<const uint2*>(base + colb2);
+      return make_uint4(lo.x, lo.y, hi.x, hi.y);
+    } else {
+      return *reinterpret_cast<const uint4*>(base + colb);
+    }
+  };
   for (int r = rp; r < rows; r += rpp * UR) {
     uint4 v[UR][5];
 #pragma unroll
     for (int u = 0; u < UR; ++u) {
       const RowIdx ix = sidx[min(r + u * rpp, rows - 1)];
-      v[u][0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_item, ix.item * rowb + colb, 0, 0));
-      if constexpr (SACT) {
-        v[u][1] = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(s_act) +
-                                                  min(ix.act, a.n_action) * rowb + colb);
-      } else {
-        v[u][1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_act, ix.act * rowb + colb, 0, 0));
-      }
-      v[u][2] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_pos, ix.pe * rowb + colb, 0, 0));
-      v[u][3] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_ri, ix.ri_slot * rowb + colb, 0, 0));
-      v[u][4] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_rt, ix.rt * rowb + colb, 0, 0));
+      v[u][0] = load(rs_item, ix.item * rowb);
+      if constexpr (SACT)
+        v[u][1] = load_act(ix.act);
+      else
+        v[u][1] = load(rs_act, ix.act * rowb);
+      v[u][2] = load(rs_pos, ix.pe * rowb);
+      v[u][3] = load(rs_ri, ix.ri_slot * rowb);
+      v[u][4] = load(rs_rt, ix.rt * rowb);
     }
 #pragma unroll
     for (int u = 0; u < UR; ++u) {
@@ -355,17 +387,25 @@ __global__ void __launch_bounds__(EMB_THREADS) embed_sum_rows_kernel(EmbedArgs a
 #pragma unroll
       for (int t = 0; t < 5; ++t) add_vec<T>(v[u][t], acc);
       const int rr = r + u * rpp;
-      const uint32_t ob = rr < rows ? static_cast<uint32_t>(rr) * orowb + ocolb : out_bytes;
-      typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+      const bool ok = rr < rows;
+      const uint32_t ro = static_cast<uint32_t>(rr) * orowb;
       if constexpr (sizeof(TO) == 2) {
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, pack8(acc)), rs_out, ob, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, pack8(acc)), rs_out,
+                                               ok ? ro + colb : out_bytes, 0, CPOL);
+      } else if constexpr (SPLIT) {  // groups c and c + cpr: 16 bytes each at 16 c and 16 (c + cpr)
+        const uint4 o0 = make_uint4(__float_as_uint(acc[0]), __float_as_uint(acc[1]), __float_as_uint(acc[2]),
+                                    __float_as_uint(acc[3]));
+        const uint4 o1 = make_uint4(__float_as_uint(acc[4]), __float_as_uint(acc[5]), __float_as_uint(acc[6]),
+                                    __float_as_uint(acc[7]));
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o0), rs_out, ok ? ro + 2u * colb : out_bytes,
+                                               0, CPOL);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o1), rs_out, ok ? ro + 2u * colb2 : out_bytes,
+                                               0, CPOL);
       } else {
-#pragma unroll
-        for (int q = 0; q < V / 4; ++q) {
-          const uint4 o = make_uint4(__float_as_uint(acc[4 * q]), __float_as_uint(acc[4 * q + 1]),
-                                     __float_as_uint(acc[4 * q + 2]), __float_as_uint(acc[4 * q + 3]));
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), rs_out, ob + 16u * q, 0, 0);
-        }
+        const uint4 o = make_uint4(__float_as_uint(acc[0]), __float_as_uint(acc[1]), __float_as_uint(acc[2]),
+                                   __float_as_uint(acc[3]));
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), rs_out, ok ? ro + colb : out_bytes, 0,
+                                               CPOL);
       }
     }
   }
@@ -688,26 +728,28 @@ dim3 grid_of(const EmbedArgs& a) {
 }
 
 // the row kernel, with the action table in LDS when it is small enough; f32_out: f32 rows
-// from bf16 tables (the f32 residual stream)
-void launch_rows(const EmbedArgs& a, int dtype, bool f32_out, hipStream_t stream) {
-  const bool sact = a.bytes_action % 16 == 0 && a.bytes_action <= static_cast<uint32_t>(SACT_MAX);
+// from bf16 tables (the f32 residual stream); out_bytes: the size of the output rows
+template <typename T, typename TO>
+void launch_rows_t(const EmbedArgs& a, bool sact, bool nt, hipStream_t stream) {
   const size_t lds = sact ? a.bytes_action : 0;
-  if (dtype == GENRANK_BF16 && f32_out) {
-    if (sact)
-      hipLaunchKernelGGL((embed_sum_rows_kernel<bf16_t, float, true>), grid_of(a), dim3(EMB_THREADS), lds, stream, a);
-    else
-      hipLaunchKernelGGL((embed_sum_rows_kernel<bf16_t, float, false>), grid_of(a), dim3(EMB_THREADS), 0, stream, a);
-  } else if (dtype == GENRANK_BF16) {
-    if (sact)
-      hipLaunchKernelGGL((embed_sum_rows_kernel<bf16_t, bf16_t, true>), grid_of(a), dim3(EMB_THREADS), lds, stream, a);
-    else
-      hipLaunchKernelGGL((embed_sum_rows_kernel<bf16_t, bf16_t, false>), grid_of(a), dim3(EMB_THREADS), 0, stream, a);
-  } else {
-    if (sact)
-      hipLaunchKernelGGL((embed_sum_rows_kernel<float, float, true>), grid_of(a), dim3(EMB_THREADS), lds, stream, a);
-    else
-      hipLaunchKernelGGL((embed_sum_rows_kernel<float, float, false>), grid_of(a), dim3(EMB_THREADS), 0, stream, a);
-  }
+  if (sact && nt)
+    hipLaunchKernelGGL((embed_sum_rows_kernel<T, TO, true, true>), grid_of(a), dim3(EMB_THREADS), lds, stream, a);
+  else if (sact)
+    hipLaunchKernelGGL((embed_sum_rows_kernel<T, TO, true, false>), grid_of(a), dim3(EMB_THREADS), lds, stream, a);
+  else if (nt)
+    hipLaunchKernelGGL((embed_sum_rows_kernel<T, TO, false, true>), grid_of(a), dim3(EMB_THREADS), 0, stream, a);
+  else
+    hipLaunchKernelGGL((embed_sum_rows_kernel<T, TO, false, false>), grid_of(a), dim3(EMB_THREADS), 0, stream, a);
+}
+void launch_rows(const EmbedArgs& a, int dtype, bool f32_out, int64_t out_bytes, hipStream_t stream) {
+  const bool sact = a.bytes_action % 16 == 0 && a.bytes_action <= static_cast<uint32_t>(SACT_MAX);
+  const bool nt = out_bytes > STREAM_OUT_BYTES;
+  if (dtype == GENRANK_BF16 && f32_out)
+    launch_rows_t<bf16_t, float>(a, sact, nt, stream);
+  else if (dtype == GENRANK_BF16)
+    launch_rows_t<bf16_t, bf16_t>(a, sact, nt, stream);
+  else
+    launch_rows_t<float, float>(a, sact, nt, stream);
 }
 // either gather kernel for the batch's dtype and residual-stream type
 void launch_gather(const genrank_batch* b, const genrank_tables* t, const EmbedArgs& a, hipStream_t stream) {
@@ -719,8 +761,9 @@ void launch_gather(const genrank_batch* b, const genrank_tables* t, const EmbedA
   const int64_t rb = static_cast<int64_t>(b->d) * es;
   const bool rows_ok = b->d * es % 16 == 0 && cpr <= EMB_THREADS && EMB_THREADS % cpr == 0 &&
                        t->n_item * rb < 0xFFFFFFFFll && EMB_ROWS * rb * 2 < 0xFFFFFFFFll;
+  const int64_t out_bytes = (a.T_h + static_cast<int64_t>(a.B) * a.m) * b->d * (f32_out ? 4 : es);
   if (rows_ok)
-    launch_rows(a, b->dtype, f32_out, stream);
+    launch_rows(a, b->dtype, f32_out, out_bytes, stream);
   else if (f32_out)
     hipLaunchKernelGGL((embed_sum_kernel<bf16_t, float>), grid_of(a), dim3(EMB_THREADS), 0, stream, a);
   else if (b->dtype == GENRANK_BF16)
