@@ -279,11 +279,11 @@ __global__ void __launch_bounds__(EMB_THREADS) embed_sum_kernel(EmbedArgs a) {
 // output stores lands next to its neighbours' (a wave's store covers one contiguous span).
 // Table reads and output writes are buffer accesses with 32-bit byte offsets (every table
 // is below 4 GB); rows past the chunk write nothing.  NT: outputs far larger than the
-// last-level cache go out as streaming (non-temporal) stores, so that they leave no dirty
+// last-level cache (256 MiB) go out as streaming (non-temporal) stores, so that they leave no dirty
 // lines behind for the next kernels to evict; smaller ones stay cached for the next kernel.
 constexpr int BUF_DWORD3 = 0x00020000;  // raw buffer descriptor word 3 (gfx9 family)
 constexpr int CPOL_NT = 2;              // buffer cache policy: non-temporal
-constexpr int64_t STREAM_OUT_BYTES = int64_t(128) << 20;  // outputs above this use NT stores
+constexpr int64_t STREAM_OUT_BYTES = int64_t(256) << 20;  // outputs above this use NT stores
 
 template <typename T>
 __device__ __forceinline__ void add_vec(const uint4& v, float* acc) {

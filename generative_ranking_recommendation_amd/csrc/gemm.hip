@@ -32,7 +32,21 @@ struct GemmArgs {
   const void* R; int64_t ldr;     // residual (EPI_RESID: bf16; EPI_RESID_F32: f32), may alias C
   bf16_t* Cpre; int64_t ldpre;    // pre-activation copy (EPI_SILU, optional)
   int M, N, K;
+  int nt;                          // outputs far beyond the last-level cache: streaming stores
 };
+
+// Outputs larger than the last-level cache (256 MiB) are written with non-temporal stores:
+// the next kernel finds them in memory either way, and they leave no dirty cache lines
+// behind for later kernels to evict.
+constexpr int64_t STREAM_OUT_BYTES = int64_t(256) << 20;
+
+// one 16-byte piece of an output row (wave-uniform choice of the store kind)
+__device__ __forceinline__ void store16(void* p, const uint4& v, bool nt) {
+  if (nt)
+    __builtin_nontemporal_store(__builtin_bit_cast(f32x4_t, v), reinterpret_cast<f32x4_t*>(p));
+  else
+    *reinterpret_cast<uint4*>(p) = v;
+}
 
 // sigmoid through the hardware reciprocal (about 1 ulp) rather than a full-precision
 // division; exp(-a) = inf for very negative a gives 1 / inf = 0, the right limit
@@ -146,7 +160,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, const f32x4_t (&acc)
     if (m >= g.M) continue;
     const int nl = (tid & 15) * 8;
     const bf16_t* src = (ml < 64 ? sC_lo : sC_hi) + (ml & 63) * CP + nl;
-    *reinterpret_cast<uint4*>(C + static_cast<int64_t>(m) * g.ldc + n0 + nl) = *reinterpret_cast<const uint4*>(src);
+    store16(C + static_cast<int64_t>(m) * g.ldc + n0 + nl, *reinterpret_cast<const uint4*>(src), g.nt);
   }
 }
 
@@ -441,21 +455,54 @@ __global__ void __launch_bounds__(BTHREADS) gemm_nt_bf16_big_kernel(GemmArgs g) 
     lds_barrier();  // every wave is done with the stage buffers before C goes into them
   }
 
-  if constexpr (EPI == GEMM_EPI_RESID_F32) {  // f32 rows straight from the registers
+  if constexpr (EPI == GEMM_EPI_RESID_F32) {
+    // f32 rows through LDS, one half of the tile (128 rows, the waves with wm = half) at a
+    // time: those waves write their 128 x 64 blocks (stage buffer q holds rows 32 q ..
+    // 32 q + 31 of the half, pitch FCP floats), then every wave adds the residual to whole
+    // rows and stores them, lane l on columns 4 l .. 4 l + 3, so that each access of a wave
+    // is one contiguous 1 KB span.  A residual element is read by the lane that stores its
+    // sum, so R may alias C.
+    static_assert(!RMS, "the RMSNorm-folded kernel has no f32 residual epilogue");
+    constexpr int FCP = BBN + 4;
+    static_assert(32 * FCP * 4 <= BSTAGE_ELEMS * 2, "32 f32 rows per stage buffer");
+    auto fb = [&](int q) -> float* {
+      return reinterpret_cast<float*>(q == 0 ? st0 : (q == 1 ? st1 : (q == 2 ? st2 : st3)));
+    };
+    const float* Rp = static_cast<const float*>(g.R);
+    float* Cp = static_cast<float*>(g.C);
 #pragma unroll
-    for (int mb = 0; mb < 8; ++mb) {
-      const int ml = wm * 128 + mb * 16 + l16;
-      if (m0 + ml >= g.M) continue;
+    for (int half = 0; half < 2; ++half) {
+      // the residual rows this wave adds (rows wave, wave + 8, ... of the half): the first
+      // eight in flight before the tile half goes through LDS, each later one issued as an
+      // earlier one is consumed (rows past M re-read row M - 1)
+      auto rrow = [&](int i) {
+        const int m = min(m0 + half * 128 + wave + 8 * i, g.M - 1);
+        return *reinterpret_cast<const f32x4_t*>(Rp + static_cast<int64_t>(m) * g.ldr + n0 + lane * 4);
+      };
+      f32x4_t rv[8];
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        float v[4] = {acc[nb][mb][0], acc[nb][mb][1], acc[nb][mb][2], acc[nb][mb][3]};
-        if constexpr (RMS) {
-          const float r = sR[ml];
+      for (int i = 0; i < 8; ++i) rv[i] = rrow(i);
+      if (wm == half) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) v[i] *= r;
+        for (int mb = 0; mb < 8; ++mb) {
+          float* rowp = fb(mb >> 1) + ((mb & 1) * 16 + l16) * FCP + wn * 64 + g4 * 4;
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb) *reinterpret_cast<f32x4_t*>(rowp + nb * 16) = acc[nb][mb];
         }
-        store_f32<EPI>(g, m0 + ml, n0 + wn * 64 + nb * 16 + g4 * 4, v);
       }
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int rr = wave + 8 * i;
+        const int m = m0 + half * 128 + rr;
+        const f32x4_t r = rv[i & 7];
+        if (i < 8) rv[i] = rrow(i + 8);
+        if (m < g.M) {
+          const f32x4_t v = *reinterpret_cast<const f32x4_t*>(fb(rr >> 5) + (rr & 31) * FCP + lane * 4) + r;
+          store16(Cp + static_cast<int64_t>(m) * g.ldc + n0 + lane * 4, __builtin_bit_cast(uint4, v), g.nt);
+        }
+      }
+      __syncthreads();
     }
     return;
   }
@@ -494,8 +541,8 @@ __global__ void __launch_bounds__(BTHREADS) gemm_nt_bf16_big_kernel(GemmArgs g) 
     if (m >= g.M) continue;
     const int nl = (tid & 31) * 8;
     const bf16_t* cb = pass < 4 ? st0 : (pass < 8 ? st1 : (pass < 12 ? st2 : st3));
-    *reinterpret_cast<uint4*>(C + static_cast<int64_t>(m) * g.ldc + n0 + nl) =
-        *reinterpret_cast<const uint4*>(cb + (ml & 63) * BCP + nl);
+    store16(C + static_cast<int64_t>(m) * g.ldc + n0 + nl, *reinterpret_cast<const uint4*>(cb + (ml & 63) * BCP + nl),
+            g.nt);
   }
 }
 
@@ -754,6 +801,7 @@ genrank_status launch_gemm_nt(int dtype, const void* A, int64_t lda, const void*
       static_cast<int64_t>(GBN) * ldw * 2 < (int64_t(1) << 32)) {
     GemmArgs g{static_cast<const bf16_t*>(A), lda, static_cast<const bf16_t*>(W), ldw, C, ldc,
                R, ldr, static_cast<bf16_t*>(Cpre), ldpre, M, N, K};
+    g.nt = static_cast<int64_t>(M) * N * (epi == GEMM_EPI_RESID_F32 ? 4 : 2) > STREAM_OUT_BYTES;
     const int grid = (N / GBN) * ((M + GBM - 1) / GBM);
     if (K % (4 * GBK) == 0 && K >= 512 && N % BBN == 0 && M >= 4 * BBM &&
         static_cast<int64_t>(BBN) * ldw * 2 < (int64_t(1) << 32)) {
@@ -842,6 +890,7 @@ genrank_status launch_gemm_nt_rms(const void* A, int64_t lda, const void* Wg, in
     return GENRANK_E_SHAPE;
   GemmArgs g{static_cast<const bf16_t*>(A), lda, static_cast<const bf16_t*>(Wg), ldw, C, ldc, nullptr, 0, nullptr, 0,
              M, N, K};
+  g.nt = static_cast<int64_t>(M) * N * 2 > STREAM_OUT_BYTES;
   const int bgrid = (N / BBN) * ((M + BBM - 1) / BBM);
   if (epi == GEMM_EPI_STORE)
     hipLaunchKernelGGL((gemm_nt_bf16_big_kernel<GEMM_EPI_STORE, true>), dim3(bgrid), dim3(BTHREADS), 0, stream, g);
