@@ -94,6 +94,14 @@ def parse():
                         "control run, where nearly every item row is read once")
     p.add_argument("--calibrate-copy-mb", type=int, default=0,
                    help="also run one plain device copy of this many MiB (counter calibration)")
+    p.add_argument("--units-once", metavar="ORDER_JSON", default=None,
+                   help="pre-norm stacks, for counter runs: after the warm-up steps run every unit of "
+                        "the step once, in order, write the units' names and kinds to ORDER_JSON, make the "
+                        "calibration copy (--calibrate-copy-mb) and stop")
+    p.add_argument("--write-traffic", nargs=3, metavar=("ORDER_JSON", "FETCH_DIR", "WRITE_DIR"), default=None,
+                   help="host only: read the rocprofv3 FETCH_SIZE and WRITE_SIZE counter runs of a "
+                        "--units-once run and store the per-launch HBM bytes of each unit kind in "
+                        "profiles/traffic.json")
     return p.parse_args()
 
 
@@ -686,6 +694,24 @@ def bench_stack(args, cfg):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    if args.units_once:
+        # one launch per unit, in step order, each alone on the device; then the copy (its
+        # buffers filled beforehand, so that no other kernel runs between the units and it)
+        if args.calibrate_copy_mb > 0:
+            src = torch.ones(args.calibrate_copy_mb * (1 << 20) // 4, dtype=torch.float32, device=dev)
+            dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for n, _, fn, _ in units:
+            fn()
+            torch.cuda.synchronize()
+        with open(args.units_once, "w") as f:
+            json.dump({"workload": cfg.name, "units": [[n, kind] for n, kind, _, _ in units],
+                       "copy_mib": args.calibrate_copy_mb}, f)
+        if args.calibrate_copy_mb > 0:
+            dst.copy_(src)
+            torch.cuda.synchronize()
+        log(f"units once: {len(units)} launches; order in {args.units_once}")
+        return
     # the decomposed (and pruned) step must give the logits of the model's own forward
     got = bufs["logits"].clone()
     _, ref = model.forward(inp)
@@ -787,8 +813,68 @@ def bench_stack(args, cfg):
     print(json.dumps(out), flush=True)
 
 
+def write_traffic(order_json, fetch_dir, write_dir):
+    """profiles/traffic.json from two rocprofv3 counter runs (FETCH_SIZE, WRITE_SIZE) of
+    `bench.py --units-once ... --calibrate-copy-mb N`: the dispatches that precede the
+    calibration copy are the step's units in order; each counter is scaled by what it reads
+    for the copy (N MiB each way), and each kind keeps the bytes of its first launch."""
+    import csv
+    import glob
+
+    def short(kernel):  # "void genrank::(anonymous namespace)::k<...>(args)" -> "k<...>"
+        return kernel.replace("genrank::(anonymous namespace)::", "").rsplit("(", 1)[0].replace("void ", "")
+    with open(order_json) as f:
+        order = json.load(f)
+    units = order["units"]
+
+    def dispatches(d):
+        rows = {}
+        for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(path) as f:
+                for r in csv.DictReader(f):
+                    rows.setdefault(int(r["Dispatch_Id"]), [r["Kernel_Name"], 0.0])[1] += float(r["Counter_Value"])
+        return [rows[k] for k in sorted(rows)]
+    out = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        ds = dispatches(d)
+        ci = max(i for i, (name, _) in enumerate(ds) if "copyBuffer" in name or "copy" in name.lower())
+        copy_kib = ds[ci][1]
+        unit_ds = ds[ci - len(units):ci]
+        out[counter] = (copy_kib, unit_ds)
+    fetch_copy, fetch_units = out["FETCH_SIZE"]
+    write_copy, write_units = out["WRITE_SIZE"]
+    mib = order.get("copy_mib")
+    moved_kib = float(mib) * 1024 if mib else None
+    fs = moved_kib / fetch_copy if moved_kib else 1.0
+    wscale = moved_kib / write_copy if moved_kib else 1.0
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    data = json.load(open(path)) if os.path.exists(path) else {}
+    rec = {}
+    for (n, kind), (kn, fk), (_, wk) in zip(units, fetch_units, write_units):
+        src = KERNEL_SOURCES.get(kind)
+        if kind in rec or not src:
+            continue
+        rec[kind] = {"unit": n, "kernel": short(kn), "source_sha": source_sha(src),
+                     "fetch_bytes": int(fk * 1024 * fs), "write_bytes": int(wk * 1024 * wscale),
+                     "fetch_kib_raw": int(fk), "write_kib_raw": int(wk)}
+    rec["calibration"] = {"fetch_scale": fs, "write_scale": wscale,
+                          "copy": f"torch device copy of {mib} MiB ({fetch_copy:.0f} KiB FETCH_SIZE, "
+                                  f"{write_copy:.0f} KiB WRITE_SIZE)"}
+    data[order["workload"]] = rec
+    with open(path, "w") as f:
+        json.dump(data, f, indent=1)
+    for (n, kind), (kn, _) in zip(units, fetch_units):
+        print(f"{n:16s} {kind:10s} {short(kn)}")
+    for kind, r in rec.items():
+        if kind != "calibration":
+            print(f"{kind:10s} {r['unit']:14s} read {r['fetch_bytes'] / 1e6:9.1f} MB  write {r['write_bytes'] / 1e6:9.1f} MB")
+
+
 def main():
     args = parse()
+    if args.write_traffic:
+        write_traffic(*args.write_traffic)
+        return
     if args.workload == "hstu_interleaved":
         bench_hstu(args)
         return
