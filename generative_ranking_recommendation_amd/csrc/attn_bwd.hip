@@ -230,12 +230,6 @@ struct BwdMArgs {
 };
 constexpr int BVAR_FULL = 1, BVAR_TBUCKET = 2;  // the ALiBi variants, as template bits
 
-// slot of row j (0..63 of a tile) in the permuted axis: the 8 values a lane packs from two
-// 16-row MFMA result blocks land in 8 consecutive slots
-__device__ __forceinline__ int perm_slot(int j) {
-  const int ks = j >> 5, r = j & 31, hi = r >> 4, rr = r & 15;
-  return ks * 32 + (rr >> 2) * 8 + hi * 4 + (rr & 3);
-}
 __device__ __forceinline__ float bxor16_sum(float x) {
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
@@ -255,21 +249,26 @@ __device__ __forceinline__ float dot16(const uint4& a0, const uint4& a1, const u
   return s;
 }
 // row-pair staging: a thread moves rows 2pr, 2pr+1, columns 8ch..8ch+7 of a 64 x 64 tile
-// into a row-major copy and a transposed copy with permuted rows
-__device__ __forceinline__ void stash_pair(bf16_t* rows, bf16_t* tr, int pr, int ch, const uint4& ra,
-                                           const uint4& rb) {
+// into its row-major LDS copy
+__device__ __forceinline__ void stash_rows(bf16_t* rows, int pr, int ch, const uint4& ra, const uint4& rb) {
   *reinterpret_cast<uint4*>(rows + (2 * pr) * PLD + ch * 8) = ra;
   *reinterpret_cast<uint4*>(rows + (2 * pr + 1) * PLD + ch * 8) = rb;
-  uint32_t* col = reinterpret_cast<uint32_t*>(tr + ch * 8 * PLD + perm_slot(2 * pr));
-  constexpr int P = PLD / 2;
-  col[0 * P] = __builtin_amdgcn_perm(rb.x, ra.x, 0x05040100u);
-  col[1 * P] = __builtin_amdgcn_perm(rb.x, ra.x, 0x07060302u);
-  col[2 * P] = __builtin_amdgcn_perm(rb.y, ra.y, 0x05040100u);
-  col[3 * P] = __builtin_amdgcn_perm(rb.y, ra.y, 0x07060302u);
-  col[4 * P] = __builtin_amdgcn_perm(rb.z, ra.z, 0x05040100u);
-  col[5 * P] = __builtin_amdgcn_perm(rb.z, ra.z, 0x07060302u);
-  col[6 * P] = __builtin_amdgcn_perm(rb.w, ra.w, 0x05040100u);
-  col[7 * P] = __builtin_amdgcn_perm(rb.w, ra.w, 0x07060302u);
+}
+typedef short bv4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bv4i16_t lds_bv4i16_t;
+// The transposed operand X^T (columns nb*16 .. nb*16+15 of a row-major 64 x 64 LDS tile as
+// rows, 32 of its rows as the k axis) of a product whose other operand packs two 16-row
+// result blocks (pack_blocks): lane (l16, g4) gets column nb*16 + l16 at rows
+// 32 ks + 4 g4 + e and 32 ks + 16 + 4 g4 + e (e = 0..3), the order of those packed values.
+// gfx950's transposing read gives within each 16-lane group lane j, element e, the element
+// j % 4 of what lane 4 e + j / 4 addressed: lane 4 e + r addresses row 4 g4 + e, columns
+// nb*16 + 4 r .. + 3.
+__device__ __forceinline__ bf16x8_t tr_operand(const bf16_t* tile, int nb, int ks, int l16, int g4) {
+  const bf16_t* p = tile + (ks * 32 + 4 * g4 + (l16 >> 2)) * PLD + nb * 16 + (l16 & 3) * 4;
+  const bv4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_bv4i16_t*)p);
+  const bv4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_bv4i16_t*)(p + 16 * PLD));
+  const bv4i16_t both[2] = {lo, hi};
+  return __builtin_bit_cast(bf16x8_t, both);
 }
 // pack the 8 values a lane holds for two 16-row result blocks into an MFMA operand
 __device__ __forceinline__ bf16x8_t pack_blocks(const f32x4_t& lo, const f32x4_t& hi) {
@@ -286,7 +285,6 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(BwdMArgs a) {
   constexpr bool FULL = (VAR & BVAR_FULL) != 0, TBK = (VAR & BVAR_TBUCKET) != 0;
   constexpr bool CAN_FAR = !TBK;  // the bucketed variants' key terms hold the position part only
   __shared__ __attribute__((aligned(16))) bf16_t sK[2][TB * PLD];
-  __shared__ __attribute__((aligned(16))) bf16_t sKt[2][DHB * PLD];
   __shared__ __attribute__((aligned(16))) bf16_t sV[2][TB * PLD];
   __shared__ __attribute__((aligned(16))) float sW[BWCH];
   __shared__ __attribute__((aligned(16))) int32_t sT[BWCH];  // key times relative to the reference
@@ -444,7 +442,7 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(BwdMArgs a) {
     rvb = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsV, voB + so, 0, 0));
   };
   auto stash = [&](int buf) {
-    stash_pair(sK[buf], sKt[buf], pr, ch, rka, rkb);
+    stash_rows(sK[buf], pr, ch, rka, rkb);
     *reinterpret_cast<uint4*>(&sV[buf][(2 * pr) * PLD + ch * 8]) = rva;
     *reinterpret_cast<uint4*>(&sV[buf][(2 * pr + 1) * PLD + ch * 8]) = rvb;
   };
@@ -518,7 +516,7 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(BwdMArgs a) {
       const bf16x8_t dsf = pack_blocks(s[2 * ks], s[2 * ks + 1]);
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) {
-        const bf16x8_t ktf = as_bf16x8(*reinterpret_cast<const uint4*>(&sKt[buf][(nb * 16 + l16) * PLD + ks * 32 + g4 * 8]));
+        const bf16x8_t ktf = tr_operand(sK[buf], nb, ks, l16, g4);
         accQ[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ktf, dsf, accQ[nb], 0, 0, 0);
       }
     }
@@ -542,9 +540,7 @@ __global__ void __launch_bounds__(256) attn_bwd_dkv_kernel(BwdMArgs a) {
   constexpr bool FULL = (VAR & BVAR_FULL) != 0, TBK = (VAR & BVAR_TBUCKET) != 0;
   constexpr bool CAN_FAR = !TBK;  // the bucketed variants' key terms hold the position part only
   __shared__ __attribute__((aligned(16))) bf16_t sQ[2][TB * PLD];
-  __shared__ __attribute__((aligned(16))) bf16_t sQt[2][DHB * PLD];
   __shared__ __attribute__((aligned(16))) bf16_t sO[2][TB * PLD];
-  __shared__ __attribute__((aligned(16))) bf16_t sOt[2][DHB * PLD];
   __shared__ __attribute__((aligned(16))) float sC[2][TB];
   __shared__ __attribute__((aligned(16))) float sD[2][TB];
   // variants: with the fully visible history sC holds w_i alone and sL the query's lse (with
@@ -640,8 +636,8 @@ __global__ void __launch_bounds__(256) attn_bwd_dkv_kernel(BwdMArgs a) {
     }
   };
   auto stash = [&](int buf) {
-    stash_pair(sQ[buf], sQt[buf], pr, ch, rqa, rqb);
-    stash_pair(sO[buf], sOt[buf], pr, ch, roa, rob);
+    stash_rows(sQ[buf], pr, ch, rqa, rqb);
+    stash_rows(sO[buf], pr, ch, roa, rob);
     if (tid < TB) {
       sC[buf][tid] = rc;
       sD[buf][tid] = rd;
@@ -746,8 +742,8 @@ __global__ void __launch_bounds__(256) attn_bwd_dkv_kernel(BwdMArgs a) {
       const bf16x8_t dsf = pack_blocks(dp[2 * ks], dp[2 * ks + 1]);
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) {
-        const bf16x8_t otf = as_bf16x8(*reinterpret_cast<const uint4*>(&sOt[buf][(nb * 16 + l16) * PLD + ks * 32 + g4 * 8]));
-        const bf16x8_t qtf = as_bf16x8(*reinterpret_cast<const uint4*>(&sQt[buf][(nb * 16 + l16) * PLD + ks * 32 + g4 * 8]));
+        const bf16x8_t otf = tr_operand(sO[buf], nb, ks, l16, g4);
+        const bf16x8_t qtf = tr_operand(sQ[buf], nb, ks, l16, g4);
         accV[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(otf, pf, accV[nb], 0, 0, 0);
         accK[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qtf, dsf, accK[nb], 0, 0, 0);
       }
