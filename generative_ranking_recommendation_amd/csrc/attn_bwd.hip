@@ -248,11 +248,13 @@ __device__ __forceinline__ float dot16(const uint4& a0, const uint4& a1, const u
   for (int e = 0; e < 8; ++e) s += fa[e] * fb[e];
   return s;
 }
-// row-pair staging: a thread moves rows 2pr, 2pr+1, columns 8ch..8ch+7 of a 64 x 64 tile
-// into its row-major LDS copy
+// tile staging: a thread moves rows pr and pr + 32, columns 8ch..8ch+7 of a 64 x 64 tile
+// into its row-major LDS copy (pr = tid / 8, ch = tid % 8: eight lanes cover a row's 128
+// bytes, so global loads read whole rows, and the two rows a 16-lane group writes together
+// are neighbours, which meet on at most one 16-byte bank group at this pitch)
 __device__ __forceinline__ void stash_rows(bf16_t* rows, int pr, int ch, const uint4& ra, const uint4& rb) {
-  *reinterpret_cast<uint4*>(rows + (2 * pr) * PLD + ch * 8) = ra;
-  *reinterpret_cast<uint4*>(rows + (2 * pr + 1) * PLD + ch * 8) = rb;
+  *reinterpret_cast<uint4*>(rows + pr * PLD + ch * 8) = ra;
+  *reinterpret_cast<uint4*>(rows + (pr + 32) * PLD + ch * 8) = rb;
 }
 typedef short bv4i16_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bv4i16_t lds_bv4i16_t;
@@ -421,18 +423,18 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(BwdMArgs a) {
     }
   }
 
-  // K/V staging (rows 2pr, 2pr+1, columns 8ch..8ch+7), one tile ahead, buffer loads over the
+  // K/V staging (rows pr, pr + 32, columns 8ch..8ch+7), one tile ahead, buffer loads over the
   // user's history rows (rows past it read as zero; the whole offset sits in the vector
   // operand, which the range check covers)
-  const int pr = tid & 31, ch = tid >> 5;
+  const int pr = tid >> 3, ch = tid & 7;
   const uint32_t row_bytes = static_cast<uint32_t>(a.ld_qkv) * 2u;
   const uint32_t hist_bytes = static_cast<uint32_t>(N) * row_bytes;
   const __amdgpu_buffer_rsrc_t rsK = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<bf16_t*>(a.k + off * a.ld_qkv), static_cast<short>(0), hist_bytes, BUF_DWORD3_B);
   const __amdgpu_buffer_rsrc_t rsV = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<bf16_t*>(a.v + off * a.ld_qkv), static_cast<short>(0), hist_bytes, BUF_DWORD3_B);
-  const uint32_t voA = static_cast<uint32_t>(2 * pr) * row_bytes + (h * DHB + ch * 8) * 2u;
-  const uint32_t voB = voA + row_bytes;
+  const uint32_t voA = static_cast<uint32_t>(pr) * row_bytes + (h * DHB + ch * 8) * 2u;
+  const uint32_t voB = voA + 32u * row_bytes;
   uint4 rka, rkb, rva, rvb;
   auto fetch = [&](int kt) {
     const uint32_t so = static_cast<uint32_t>(kt * TB) * row_bytes;
@@ -443,8 +445,7 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(BwdMArgs a) {
   };
   auto stash = [&](int buf) {
     stash_rows(sK[buf], pr, ch, rka, rkb);
-    *reinterpret_cast<uint4*>(&sV[buf][(2 * pr) * PLD + ch * 8]) = rva;
-    *reinterpret_cast<uint4*>(&sV[buf][(2 * pr + 1) * PLD + ch * 8]) = rvb;
+    stash_rows(sV[buf], pr, ch, rva, rvb);
   };
   if (n_tiles > 0) {
     load_w(wbase);
@@ -605,15 +606,15 @@ __global__ void __launch_bounds__(256) attn_bwd_dkv_kernel(BwdMArgs a) {
     return t;
   };
 
-  // staging of a query tile: Q and dO rows 2pr, 2pr+1 (clamped to the tile), columns
+  // staging of a query tile: Q and dO rows pr, pr + 32 (clamped to the tile), columns
   // 8ch..8ch+7; threads 0..63 also compute c_i and D_i of query tid
-  const int pr = tid & 31, ch = tid >> 5;
+  const int pr = tid >> 3, ch = tid & 7;
   uint4 rqa, rqb, roa, rob;
   float rc = 0.f, rd = 0.f, rl = 0.f;
   int32_t rt = 0;
   bool rfar = false;
   auto fetch = [&](const QT& t) {
-    const int64_t ra = t.row0 + min(2 * pr, t.nq - 1), rb = t.row0 + min(2 * pr + 1, t.nq - 1);
+    const int64_t ra = t.row0 + min(pr, t.nq - 1), rb = t.row0 + min(pr + 32, t.nq - 1);
     rqa = *reinterpret_cast<const uint4*>(a.q + ra * a.ld_qkv + h * DHB + ch * 8);
     rqb = *reinterpret_cast<const uint4*>(a.q + rb * a.ld_qkv + h * DHB + ch * 8);
     roa = *reinterpret_cast<const uint4*>(a.dout + ra * a.ld_o + h * DHB + ch * 8);
