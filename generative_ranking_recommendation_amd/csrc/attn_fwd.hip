@@ -76,6 +76,7 @@ struct AttnArgs {
   // bucketed time term: edges (int64, device), their count, and the power of two >= count + 1
   const int64_t* tb;
   int n_tb, tb_p2;
+  int nt_o;  // o far larger than the last-level cache: streaming stores (pair kernel)
 };
 
 // variant bits of the ALiBi kernels: the fully visible history mask, the bucketed time term
@@ -1313,16 +1314,37 @@ __global__ void __launch_bounds__(PAIR_NT) attn_fwd_pair_kernel(AttnArgs a) {
       if (is_cand)
         merge_self(kself[hb], vself[hb], qf[hb], SEP, a.scale2, tbk_self, SC, th, g4, m_run[hb], lsum[hb], accO[hb]);
       const float ltot = xor32_sum(xor16_sum(lsum[hb]));
-      if (q_valid[hb]) {
-        const float inv = __builtin_amdgcn_rcpf(ltot);  // (as in the ring kernel)
-        char* ob = reinterpret_cast<char*>(a.o + row0 * a.ld_o + h * DH);
-        const uint32_t lo = (static_cast<uint32_t>(hb * QW + l16) * static_cast<uint32_t>(a.ld_o) + g4 * 4) * 2u;
+      const float inv = __builtin_amdgcn_rcpf(ltot);  // (as in the ring kernel)
+      // Lane groups g4 and g4 ^ 1 (same query) trade halves: lane group g4 then holds the 8
+      // consecutive dimensions 8 (g4 / 2) + 16 (g4 % 2) .. + 7 of blocks nb = 0, 1, and the
+      // same + 32 of nb = 2, 3, so a row leaves in two 16-byte stores per lane, each wave store
+      // covering 64 contiguous bytes of a row.  (The lane-swap puts odd 16-lane rows of its
+      // first operand in the even rows of its second.)
+      uint4 ow[2];
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-          uint2 o;
-          o.x = pack_bf16x2(accO[hb][nb][0] * inv, accO[hb][nb][1] * inv);
-          o.y = pack_bf16x2(accO[hb][nb][2] * inv, accO[hb][nb][3] * inv);
-          *reinterpret_cast<uint2*>(ob + lo + nb * 32) = o;
+      for (int pp = 0; pp < 2; ++pp) {
+        float xs[4], ys[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(accO[hb][2 * pp][i] * inv),
+                                                          __float_as_uint(accO[hb][2 * pp + 1][i] * inv), false, false);
+          xs[i] = __uint_as_float(r[0]);
+          ys[i] = __uint_as_float(r[1]);
+        }
+        ow[pp] = make_uint4(pack_bf16x2(xs[0], xs[1]), pack_bf16x2(xs[2], xs[3]), pack_bf16x2(ys[0], ys[1]),
+                            pack_bf16x2(ys[2], ys[3]));
+      }
+      if (q_valid[hb]) {
+        char* ob = reinterpret_cast<char*>(a.o + row0 * a.ld_o + h * DH);
+        const uint32_t dbase = 8 * (g4 >> 1) + 16 * (g4 & 1);
+        const uint32_t lo = (static_cast<uint32_t>(hb * QW + l16) * static_cast<uint32_t>(a.ld_o) + dbase) * 2u;
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp) {
+          char* dst = ob + lo + pp * 64;
+          if (a.nt_o)
+            __builtin_nontemporal_store(__builtin_bit_cast(f32x4_t, ow[pp]), reinterpret_cast<f32x4_t*>(dst));
+          else
+            *reinterpret_cast<uint4*>(dst) = ow[pp];
         }
         if (a.lse && g4 == 0)
           a.lse[(row0 + hb * QW + l16) * a.H + h] = LN2 * (m_run[hb] * SC + __builtin_amdgcn_logf(ltot) - (FULL ? 0.f : w_i[hb]));
@@ -1528,6 +1550,7 @@ genrank_status launch_attn_fwd(const genrank_batch* b, const int32_t* offsets, c
     a.ld_qkv = ld_qkv;
     a.o = static_cast<bf16_t*>(o);
     a.ld_o = ld_o;
+    a.nt_o = T * b->d * 2 > (int64_t(256) << 20);  // streaming stores for o beyond the last-level cache
     a.lse = lse;
     for (int h = 0; h < b->H; ++h) {
       a.sp2[h] = alibi.slopes_pos[h] * LOG2E;
