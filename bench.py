@@ -38,6 +38,7 @@ METRIC = "candidates scored/sec (GenRank fwd, bf16) + attn MFMA util % and gathe
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3
+N_XCD, N_SIMD = 8, 256 * 4     # MI355X: 8 XCDs, 256 CUs of 4 SIMDs
 KERNEL_SOURCES = {"embed_sum": "embed.hip", "attn_fwd": "attn_fwd.hip", "qkv_gemm": "gemm.hip",
                   "out_gemm": "gemm.hip", "embed": "embed.hip", "norm": "rowops.hip", "qkv": "gemm.hip",
                   "attn": "attn_fwd.hip", "attn_cand": "attn_fwd.hip", "wo": "gemm.hip", "ffn_up": "gemm.hip",
@@ -98,10 +99,11 @@ def parse():
                    help="pre-norm stacks, for counter runs: after the warm-up steps run every unit of "
                         "the step once, in order, write the units' names and kinds to ORDER_JSON, make the "
                         "calibration copy (--calibrate-copy-mb) and stop")
-    p.add_argument("--write-traffic", nargs=3, metavar=("ORDER_JSON", "FETCH_DIR", "WRITE_DIR"), default=None,
-                   help="host only: read the rocprofv3 FETCH_SIZE and WRITE_SIZE counter runs of a "
-                        "--units-once run and store the per-launch HBM bytes of each unit kind in "
-                        "profiles/traffic.json")
+    p.add_argument("--write-traffic", nargs="+", metavar="ARG", default=None,
+                   help="host only: ORDER_JSON FETCH_DIR WRITE_DIR [MFMA_DIR]: read the rocprofv3 "
+                        "FETCH_SIZE and WRITE_SIZE counter runs of a --units-once run (and optionally its "
+                        "SQ_VALU_MFMA_BUSY_CYCLES + GRBM_GUI_ACTIVE run) and store each unit kind's "
+                        "per-launch HBM bytes (and MFMA busy share) in profiles/traffic.json")
     return p.parse_args()
 
 
@@ -111,9 +113,10 @@ def source_sha(fn):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def load_traffic(workload):
+def load_traffic(workload, field=None):
     """Counter-measured HBM bytes per launch, from committed rocprofv3 summaries; a kernel
-    whose source changed since the counters were taken gets None."""
+    whose source changed since the counters were taken gets None.  field: another value of
+    the same records instead (e.g. the MFMA busy share)."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return {}
@@ -123,7 +126,10 @@ def load_traffic(workload):
     for name, rec in data.get(workload, {}).items():
         src = KERNEL_SOURCES.get(name)
         if src and rec.get("source_sha") == source_sha(src):
-            out[name] = rec["fetch_bytes"] + rec["write_bytes"]
+            if field is None:
+                out[name] = rec["fetch_bytes"] + rec["write_bytes"]
+            elif field in rec:
+                out[name] = rec[field]
     return out
 
 
@@ -447,7 +453,6 @@ def bench_serve(args, cfg):
     xc = torch.empty((Tc, d), dtype=torch.bfloat16, device=dev)
     qkv = torch.empty((Tc, 3 * d), dtype=torch.bfloat16, device=dev)
     o = torch.empty((Tc, d), dtype=torch.bfloat16, device=dev)
-    lse = torch.empty((Tc, H), dtype=torch.float32, device=dev)
     y = torch.empty((Tc, d), dtype=torch.bfloat16, device=dev)
     qp, kp = qkv.data_ptr(), kv.data_ptr()
     names = ["embed_cand", "qkv_gemm", "attn_cached", "out_gemm"]
@@ -455,7 +460,7 @@ def bench_serve(args, cfg):
         lambda: B.genrank_embed_sum_cand(bt, inp.struct, model.tables.struct, xc, stream),
         lambda: B.genrank_linear(B.BF16, xc, d, lay.wqkv, d, qkv, 3 * d, Tc, 3 * d, d, stream=stream),
         lambda: B.genrank_attn_fwd_cached(bt, inp.hist_offsets, inp.hist_ts, inp.req_ts, lay.slopes, qp,
-                                          qp + 2 * d, qp + 4 * d, 3 * d, kp, kp + 2 * d, 2 * d, o, d, lse,
+                                          qp + 2 * d, qp + 4 * d, 3 * d, kp, kp + 2 * d, 2 * d, o, d, None,
                                           stream),
         lambda: B.genrank_linear(B.BF16, o, d, lay.wo, d, y, d, Tc, d, d, stream=stream),
     ]
@@ -502,7 +507,7 @@ def bench_serve(args, cfg):
     lengths = inp.lengths
     cand_pairs = int(m * (np.asarray(lengths, np.int64) + 1).sum())
     flops = 4 * d * cand_pairs
-    nbytes = T_h * 2 * d * 2 + Tc * 3 * d * 2 + Tc * d * 2 + Tc * H * 4
+    nbytes = T_h * 2 * d * 2 + Tc * 3 * d * 2 + Tc * d * 2
     t_us = per["attn_cached"] * 1e3
     achieved = nbytes / (t_us * 1e-6) / 1e9
     roofline = {"kernel": "attn_cached", "bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS,
@@ -543,8 +548,7 @@ def stack_units(model, inp, bufs, prune=True):
     are never formed.  Returns [(name, kind, fn, (bound, amount, unit))]."""
     from generative_ranking_recommendation_amd import binding as B
     from generative_ranking_recommendation_amd import workload as W
-    x, z, qkv, o, lse, x1, hdn, kv, logits = (bufs[k] for k in ("x", "z", "qkv", "o", "lse", "x1", "hdn", "kv",
-                                                                 "logits"))
+    x, z, qkv, o, x1, hdn, kv, logits = (bufs[k] for k in ("x", "z", "qkv", "o", "x1", "hdn", "kv", "logits"))
     bt = model.batch(inp)
     bc = B.make_batch(inp.B, inp.m, model.d, model.H, 0, 0, model.code, model.resid)  # candidate rows only
     T, T_h, d, H, m = inp.rows, inp.total_hist, model.d, model.H, inp.m
@@ -566,9 +570,10 @@ def stack_units(model, inp, bufs, prune=True):
     L = len(model.layers)
     lengths = inp.lengths
     attn_flops = W.attention_fwd_flops(lengths, m, d)
-    attn_bytes = T * 3 * d * es + T * d * es + T * H * 4
+    # a forward that serves no backward stores no softmax statistics
+    attn_bytes = T * 3 * d * es + T * d * es
     cand_attn_flops = 4 * d * int(m * (np.asarray(lengths, np.int64) + 1).sum())
-    cand_attn_bytes = T_h * 2 * d * es + Tc * 3 * d * es + Tc * d * es + Tc * H * 4
+    cand_attn_bytes = T_h * 2 * d * es + Tc * 3 * d * es + Tc * d * es
 
     def attn_work(flops, nbytes):
         if nbytes / (PEAK_HBM_GBS * 1e9) >= flops / (PEAK_BF16_TFLOPS * 1e12):
@@ -588,7 +593,7 @@ def stack_units(model, inp, bufs, prune=True):
                                                                       stream=stream), gemm(T, 3 * d, d)),
                 (pre + "attn", "attn", lambda sl=sl, q=q: B.genrank_attn_fwd(bt, inp.hist_offsets, inp.hist_ts,
                                                                               inp.req_ts, sl, q, q + d * es,
-                                                                              q + 2 * d * es, 3 * d, o, d, lse,
+                                                                              q + 2 * d * es, 3 * d, o, d, None,
                                                                               stream), attn_work(attn_flops, attn_bytes)),
                 (pre + "wo", "wo", lambda lay=lay: B.genrank_linear(ac, o, d, lay.wo, d, x1, d, T, d, d,
                                                                     epilogue=B.EPI_RESIDUAL_F32 if rc == B.F32
@@ -604,8 +609,7 @@ def stack_units(model, inp, bufs, prune=True):
             ]
             continue
         # top block: history keys and values, then the candidate rows alone
-        xc, zc, oc, lc, x1c, hc = (ptr(x, T_h), z.data_ptr(), o.data_ptr(), lse.data_ptr(), x1.data_ptr(),
-                                   hdn.data_ptr())
+        xc, zc, oc, x1c, hc = ptr(x, T_h), z.data_ptr(), o.data_ptr(), x1.data_ptr(), hdn.data_ptr()
         q = qkv.data_ptr()
         wkv = lay.wqkv.data_ptr() + d * d * es
         kvp = kv.data_ptr()
@@ -620,7 +624,7 @@ def stack_units(model, inp, bufs, prune=True):
                                                                   stream=stream), gemm(Tc, 3 * d, d)),
             (pre + "attn", "attn_cand", lambda sl=sl: B.genrank_attn_fwd_cached(
                 bt, inp.hist_offsets, inp.hist_ts, inp.req_ts, sl, q, q + d * es, q + 2 * d * es, 3 * d, kvp,
-                kvp + d * es, 2 * d, oc, d, lc, stream), attn_work(cand_attn_flops, cand_attn_bytes)),
+                kvp + d * es, 2 * d, oc, d, None, stream), attn_work(cand_attn_flops, cand_attn_bytes)),
             (pre + "wo", "wo", lambda lay=lay, xc=xc: B.genrank_linear(
                 ac, oc, d, lay.wo, d, x1c, d, Tc, d, d, epilogue=B.EPI_RESIDUAL_F32 if rc == B.F32 else B.EPI_RESIDUAL,
                 residual=xc, ldr=d, stream=stream), gemm(Tc, d, d)),
@@ -672,7 +676,7 @@ def bench_stack(args, cfg):
     bf = torch.bfloat16
     bufs = {"x": model.resid_rows(T), "z": torch.empty((T, d), dtype=bf, device=dev),
             "qkv": torch.empty((T, 3 * d), dtype=bf, device=dev), "o": torch.empty((T, d), dtype=bf, device=dev),
-            "lse": torch.empty((T, H), dtype=torch.float32, device=dev), "x1": model.resid_rows(T),
+            "x1": model.resid_rows(T),
             "hdn": torch.empty((T, F), dtype=bf, device=dev),
             "kv": torch.empty((T_h, 2 * d), dtype=bf, device=dev),
             "logits": torch.empty((Tc, model.head.n_tasks), dtype=torch.float32, device=dev)}
@@ -805,6 +809,9 @@ def bench_stack(args, cfg):
         "kernel_timing": "each unit: its own pass of --steps steps with one event pair around it; the "
                          "dominant unit: the event pair in the timed pass",
         "attn_mfma_util_pct": round(100 * attn_tf / PEAK_BF16_TFLOPS, 2),
+        # the same from rocprofv3 counters of layer 0's attention launch: MFMA busy cycles
+        # over (SIMDs x the launch's cycles), None while the source differs from the profile's
+        "attn_mfma_busy_pct_counters": load_traffic(cfg.name, "mfma_busy_pct").get("attn"),
         "attn_tflops": round(attn_tf, 2),
         "step_roofline_us": round(floor_us, 1),
         "step_roofline_frac": round(floor_us / (ms * 1e3), 4),
@@ -813,7 +820,7 @@ def bench_stack(args, cfg):
     print(json.dumps(out), flush=True)
 
 
-def write_traffic(order_json, fetch_dir, write_dir):
+def write_traffic(order_json, fetch_dir, write_dir, mfma_dir=None):
     """profiles/traffic.json from two rocprofv3 counter runs (FETCH_SIZE, WRITE_SIZE) of
     `bench.py --units-once ... --calibrate-copy-mb N`: the dispatches that precede the
     calibration copy are the step's units in order; each counter is scaled by what it reads
@@ -827,12 +834,13 @@ def write_traffic(order_json, fetch_dir, write_dir):
         order = json.load(f)
     units = order["units"]
 
-    def dispatches(d):
+    def dispatches(d, counter=None):
         rows = {}
         for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
             with open(path) as f:
                 for r in csv.DictReader(f):
-                    rows.setdefault(int(r["Dispatch_Id"]), [r["Kernel_Name"], 0.0])[1] += float(r["Counter_Value"])
+                    if counter is None or r["Counter_Name"] == counter:
+                        rows.setdefault(int(r["Dispatch_Id"]), [r["Kernel_Name"], 0.0])[1] += float(r["Counter_Value"])
         return [rows[k] for k in sorted(rows)]
     out = {}
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
@@ -857,6 +865,19 @@ def write_traffic(order_json, fetch_dir, write_dir):
         rec[kind] = {"unit": n, "kernel": short(kn), "source_sha": source_sha(src),
                      "fetch_bytes": int(fk * 1024 * fs), "write_bytes": int(wk * 1024 * wscale),
                      "fetch_kib_raw": int(fk), "write_kib_raw": int(wk)}
+    if mfma_dir:
+        # MFMA busy share of a launch: SQ_VALU_MFMA_BUSY_CYCLES is summed over the SIMDs (16
+        # cycles per 16 x 16 x 32 bf16 MFMA); GRBM_GUI_ACTIVE over the XCDs, each counting the
+        # launch's cycles once
+        busy, gui = dispatches(mfma_dir, "SQ_VALU_MFMA_BUSY_CYCLES"), dispatches(mfma_dir, "GRBM_GUI_ACTIVE")
+        ci = max(i for i, (name, _) in enumerate(busy) if "copy" in name.lower())
+        busy_u, gui_u = busy[ci - len(units):ci], gui[ci - len(units):ci]
+        for (n, kind), (_, b), (_, g) in zip(units, busy_u, gui_u):
+            if kind in rec and rec[kind]["unit"] == n and g > 0:
+                cycles = g / N_XCD
+                rec[kind]["mfma_busy_cycles"] = int(b)
+                rec[kind]["gui_active_cycles"] = int(g)
+                rec[kind]["mfma_busy_pct"] = round(100.0 * b / (N_SIMD * cycles), 2)
     rec["calibration"] = {"fetch_scale": fs, "write_scale": wscale,
                           "copy": f"torch device copy of {mib} MiB ({fetch_copy:.0f} KiB FETCH_SIZE, "
                                   f"{write_copy:.0f} KiB WRITE_SIZE)"}
@@ -935,14 +956,13 @@ def main():
         lay = model.layers[0]
         qkv = torch.empty((T, 3 * d), dtype=tdt, device=dev)
         o = torch.empty((T, d), dtype=tdt, device=dev)
-        lse = torch.empty((T, H), dtype=torch.float32, device=dev)
         y = torch.empty((T, d), dtype=tdt, device=dev)
         qp = qkv.data_ptr()
         units = [
             ("embed_sum", lambda: B.genrank_embed_sum(bt, inp.struct, model.tables.struct, x, stream)),
             ("qkv_gemm", lambda: B.genrank_linear(code, x, d, lay.wqkv, d, qkv, 3 * d, T, 3 * d, d, stream=stream)),
             ("attn_fwd", lambda: B.genrank_attn_fwd(bt, inp.hist_offsets, inp.hist_ts, inp.req_ts, lay.slopes, qp,
-                                                    qp + d * es, qp + 2 * d * es, 3 * d, o, d, lse, stream)),
+                                                    qp + d * es, qp + 2 * d * es, 3 * d, o, d, None, stream)),
             ("out_gemm", lambda: B.genrank_linear(code, o, d, lay.wo, d, y, d, T, d, d, stream=stream)),
         ]
     else:
@@ -1009,9 +1029,10 @@ def main():
     attn_flops = None
     if decomposed:
         # attention: algorithmic flops over allowed pairs, and the floor bytes (Q, K, V read
-        # once, O and the log-sum-exp written once); the bound is whichever needs longer at peak
+        # once, O written once; an inference forward stores no log-sum-exp); the bound is
+        # whichever needs longer at peak
         attn_flops = W.attention_fwd_flops(lengths, m, d, full_history=bool(vflags & 1))
-        attn_bytes = T * 3 * d * es + T * d * es + T * H * 4
+        attn_bytes = T * 3 * d * es + T * d * es
         peak_f = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
         if attn_bytes / (PEAK_HBM_GBS * 1e9) >= attn_flops / (peak_f * 1e12):
             work["attn_fwd"] = ("hbm", attn_bytes, "GB/s")

@@ -442,8 +442,9 @@ genrank_status genrank_layer_fwd(const genrank_batch* b, const genrank_layer_wei
     GR_TRY(launch_gemm_nt(dt, zin, d, w->wqkv, d, L.qkv, 3 * d, T, 3 * d, d, GEMM_EPI_STORE,
                           nullptr, 0, nullptr, 0, s));
   }
+  // the softmax statistics only serve the backward
   GR_TRY(launch_attn_fwd(b, offsets, ts, req, w->alibi, L.qkv, L.qkv + d * es, L.qkv + 2 * d * es,
-                         3 * d, L.o, d, L.lse, s));
+                         3 * d, L.o, d, (flags & GENRANK_FWD_SAVE) ? L.lse : nullptr, s));
   if (!pre) {
     return launch_gemm_nt(dt, L.o, d, w->wo, d, y_out, d, T, d, d, GEMM_EPI_STORE, nullptr, 0,
                           nullptr, 0, s);
@@ -547,7 +548,7 @@ genrank_status genrank_layer_fwd_cached(const genrank_batch* b, const genrank_la
                           0, s));
   }
   GR_TRY(launch_attn_fwd_cached(b, offsets, ts, req, w->alibi, L.qkv, L.qkv + d * es, L.qkv + 2 * d * es, 3 * d,
-                                kh ? kh : L.qkv, kh ? kh + d * es : L.qkv, ld_kv, L.o, d, L.lse, s));
+                                kh ? kh : L.qkv, kh ? kh + d * es : L.qkv, ld_kv, L.o, d, nullptr, s));
   if (!pre)
     return launch_gemm_nt(dt, L.o, d, w->wo, d, y_cand, d, Tc, d, d, GEMM_EPI_STORE, nullptr, 0, nullptr, 0, s);
   GR_TRY(launch_gemm_nt(dt, L.o, d, w->wo, d, L.x1, d, Tc, d, d, epi_res, x_cand, d, nullptr, 0, s));

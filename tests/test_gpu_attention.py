@@ -148,6 +148,19 @@ def test_attn_bf16_full_size_sampled():
     assert np.isfinite(got).all()
 
 
+def test_attn_bf16_without_lse_same_output():
+    """lse = NULL (an inference forward) leaves the outputs bit for bit as with the
+    statistics stored, on both bf16 kernels (histories within and beyond 576 keys)."""
+    say("attn: bf16 without lse")
+    cfg = synth.make_config("infer_1layer_bf16", m=40)
+    for lengths in ([480, 17, 300], [700, 64]):
+        batch = custom_batch(cfg, lengths, seed=3)
+        st, _ = random_qkv(batch.total_rows, cfg.d, "bf16", seed=6)
+        with_lse, _ = _run_gpu(cfg, batch, st)
+        without, _ = _run_gpu(cfg, batch, st, lse=False)
+        assert np.array_equal(with_lse, without)
+
+
 def _sub_candidates(batch, m_new, pick):
     cands = batch.cand_items.reshape(batch.B, batch.m)[:, pick].reshape(-1)
     return synth.Batch(B=batch.B, m=m_new, hist_offsets=batch.hist_offsets, hist_items=batch.hist_items,
