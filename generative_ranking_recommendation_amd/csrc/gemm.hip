@@ -13,6 +13,7 @@
 // A second, simple kernel handles f32 data and the transposed products of the backward
 // pass (general strides, LDS-tiled FMA).
 #include <algorithm>
+#include <type_traits>
 
 #include "common.hpp"
 #include "internal.hpp"
@@ -58,12 +59,14 @@ __device__ __forceinline__ float dsilu_f(float a) {
   return sg * (1.0f + a * (1.0f - sg));
 }
 
-// LDS operand tile: [128 rows][32 bf16] = 64 B per row, four 16-byte chunks.  Chunk c of
-// row r is stored at chunk c ^ ((r >> 2) & 3): the 16-byte reads of 16 consecutive rows at
-// one chunk (an MFMA operand fragment) fall on 16 distinct 16-byte slots of the 64-bank LDS
-// (4 rows of 64 B span its 256 bytes; the XOR spreads the 4 row groups over the 4 chunks),
-// and so do the 16-byte writes of the staging pattern.
-__device__ __forceinline__ int swz(int r, int c) { return r * GBK + ((c ^ ((r >> 2) & 3)) << 3); }
+// LDS operand tile: [rows][32 bf16] = 64 B per row, four 16-byte chunks.  Chunk c of row r
+// is stored at slot c ^ swz_row(r), swz_row(r) = (r >> 2) & 3: the 16-byte reads of 16
+// consecutive rows at one chunk (an MFMA operand fragment) fall on 16 distinct 16-byte slots
+// of the 64-bank LDS (4 rows of 64 B span its 256 bytes; the XOR spreads the 4 row groups
+// over the 4 chunks), and so do the 16-byte writes of the staging pattern.  A 16-row block
+// keeps its swizzle under any offset that is a multiple of 16.
+__device__ __forceinline__ int swz_row(int r) { return (r >> 2) & 3; }
+__device__ __forceinline__ int swz(int r, int c) { return r * GBK + ((c ^ swz_row(r)) << 3); }
 
 constexpr int CP = GBN + 8;                           // staged C row pitch (bf16)
 constexpr int SMEM_OPS = 2 * 2 * GBM * GBK;           // [stage][A|W] operand tiles
@@ -286,10 +289,10 @@ __global__ void __launch_bounds__(GTHREADS) gemm_nt_bf16_dma_kernel(GemmArgs g) 
 
   // direct loads: wave w fills rows 32 w .. 32 w + 31 of the A tile and of the W tile, 16
   // rows (1 KB) per load; lane -> row r = r0 + lane / 4, LDS chunk lane % 4, which holds
-  // global chunk (lane % 4) ^ ((r >> 2) & 3).  A rows past M re-read row M - 1 (never stored).
+  // global chunk (lane % 4) ^ swz_row(r).  A rows past M re-read row M - 1 (never stored).
   const int lr = lane >> 2, ls = lane & 3;
   const int r0 = wave * 32 + lr, r1 = r0 + 16;
-  const int c0 = ls ^ ((r0 >> 2) & 3), c1 = ls ^ ((r1 >> 2) & 3);
+  const int c0 = ls ^ swz_row(r0), c1 = ls ^ swz_row(r1);
   const bf16_t* gA0 = g.A + static_cast<int64_t>(min(m0 + r0, g.M - 1)) * g.lda + c0 * 8;
   const bf16_t* gA1 = g.A + static_cast<int64_t>(min(m0 + r1, g.M - 1)) * g.lda + c1 * 8;
   const bf16_t* gW0 = g.W + static_cast<int64_t>(n0 + r0) * g.ldw + c0 * 8;
@@ -387,7 +390,7 @@ __global__ void __launch_bounds__(BTHREADS) gemm_nt_bf16_big_kernel(GemmArgs g) 
   // A tile and of the W tile (256 rows each), 16 rows (1 KB) per load
   const int lr = lane >> 2, ls = lane & 3;
   const int r0 = wave * 32 + lr, r1 = r0 + 16;
-  const int c0 = ls ^ ((r0 >> 2) & 3), c1 = ls ^ ((r1 >> 2) & 3);
+  const int c0 = ls ^ swz_row(r0), c1 = ls ^ swz_row(r1);
   const bf16_t* gA0 = g.A + static_cast<int64_t>(min(m0 + r0, g.M - 1)) * g.lda + c0 * 8;
   const bf16_t* gA1 = g.A + static_cast<int64_t>(min(m0 + r1, g.M - 1)) * g.lda + c1 * 8;
   const bf16_t* gW0 = g.W + static_cast<int64_t>(n0 + r0) * g.ldw + c0 * 8;
@@ -408,45 +411,120 @@ __global__ void __launch_bounds__(BTHREADS) gemm_nt_bf16_big_kernel(GemmArgs g) 
     for (int j = 0; j < 8; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const int rr = tid >> 1, rc = (tid & 1) * 2;  // RMS: this thread's row and first chunk
   float ss = 0.f;
-  auto compute = [&](const bf16_t* stg) {
-    if constexpr (RMS) {
-      float f[8];
-      unpack8(*reinterpret_cast<const uint4*>(stg + swz(rr, rc)), f);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) ss += f[e] * f[e];
-      unpack8(*reinterpret_cast<const uint4*>(stg + swz(rr, rc + 1)), f);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) ss += f[e] * f[e];
-    }
-    bf16x8_t fw[4], fa[8];
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
-      fw[nb] = as_bf16x8(*reinterpret_cast<const uint4*>(stg + BBM * GBK + swz(wn * 64 + nb * 16 + l16, g4)));
-#pragma unroll
-    for (int mb = 0; mb < 8; ++mb)
-      fa[mb] = as_bf16x8(*reinterpret_cast<const uint4*>(stg + swz(wm * 128 + mb * 16 + l16, g4)));
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-      for (int mb = 0; mb < 8; ++mb)
-        acc[nb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fw[nb], fa[mb], acc[nb][mb], 0, 0, 0);
+  // a wave's operand fragments of one K tile: 4 W blocks and 8 A blocks of 16 rows
+  auto read_w = [&](const bf16_t* stg, int nb) {
+    return as_bf16x8(*reinterpret_cast<const uint4*>(stg + BBM * GBK + swz(wn * 64 + nb * 16 + l16, g4)));
+  };
+  auto read_a = [&](const bf16_t* stg, int mb) {
+    return as_bf16x8(*reinterpret_cast<const uint4*>(stg + swz(wm * 128 + mb * 16 + l16, g4)));
   };
 
-  const int nk = g.K / GBK;  // a multiple of 4
-  load(0, st0);
-  load(1, st1);
-  load(2, st2);
-  int kt = 0;
-  for (; kt + 4 < nk; kt += 4) {
+  const int nk = g.K / GBK;  // a multiple of 4, at least 16
+  if constexpr (RMS) {
+    // the row sums of squares need registers the pipelined schedule below does not leave:
+    // stage s is read and multiplied in step s, three stages in flight
+    auto compute = [&](const bf16_t* stg) {
+      float x[8];
+      unpack8(*reinterpret_cast<const uint4*>(stg + swz(rr, rc)), x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
+      unpack8(*reinterpret_cast<const uint4*>(stg + swz(rr, rc + 1)), x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
+      bf16x8_t fw[4], fa[8];
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) fw[nb] = read_w(stg, nb);
+#pragma unroll
+      for (int mb = 0; mb < 8; ++mb) fa[mb] = read_a(stg, mb);
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < 8; ++mb)
+          acc[nb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fw[nb], fa[mb], acc[nb][mb], 0, 0, 0);
+    };
+    load(0, st0);
+    load(1, st1);
+    load(2, st2);
+    int kt = 0;
+    for (; kt + 4 < nk; kt += 4) {
+      wait_vmcnt<8>(); lds_barrier(); load(kt + 3, st3); compute(st0);
+      wait_vmcnt<8>(); lds_barrier(); load(kt + 4, st0); compute(st1);
+      wait_vmcnt<8>(); lds_barrier(); load(kt + 5, st1); compute(st2);
+      wait_vmcnt<8>(); lds_barrier(); load(kt + 6, st2); compute(st3);
+    }
     wait_vmcnt<8>(); lds_barrier(); load(kt + 3, st3); compute(st0);
-    wait_vmcnt<8>(); lds_barrier(); load(kt + 4, st0); compute(st1);
-    wait_vmcnt<8>(); lds_barrier(); load(kt + 5, st1); compute(st2);
-    wait_vmcnt<8>(); lds_barrier(); load(kt + 6, st2); compute(st3);
+    wait_vmcnt<8>(); lds_barrier(); compute(st1);
+    wait_vmcnt<4>(); lds_barrier(); compute(st2);
+    wait_vmcnt<0>(); lds_barrier(); compute(st3);
+  } else {
+    // Stage s of the K loop lives in buffer s % 4.  Step s multiplies the fragments of
+    // stage s, already in registers, and refills those registers with stage s + 1 as they
+    // free up: the W blocks into spare registers first, then A block mb right after the
+    // four MFMAs that read A block mb.  So each wave's LDS reads run under its own MFMAs and
+    // are spread over the step.  At the start of step s every wave has waited for its
+    // loads of stage s + 1 and for its reads of stage s (lds_sync): after the barrier stage
+    // s + 1 is complete in LDS and buffer s % 4 is free for stage s + 4.
+    bf16x8_t fw[4], fa[8];
+    using Yes = std::true_type;
+    using No = std::false_type;
+    auto step = [&](auto vm, auto do_load, auto do_read, bf16_t* ld_buf, int ld_kt, const bf16_t* rd_buf) {
+      constexpr bool LOAD = decltype(do_load)::value, READ = decltype(do_read)::value;
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (READ) {
+        wait_vmcnt<decltype(vm)::value>();
+        if constexpr (LOAD) lds_sync(); else lds_barrier();
+      }
+      if constexpr (LOAD) load(ld_kt, ld_buf);
+      bf16x8_t wnx[4];
+      if constexpr (READ) {
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) wnx[nb] = read_w(rd_buf, nb);
+      }
+#pragma unroll
+      for (int mb = 0; mb < 8; ++mb) {
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+          acc[nb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fw[nb], fa[mb], acc[nb][mb], 0, 0, 0);
+        if constexpr (READ) fa[mb] = read_a(rd_buf, mb);
+      }
+      if constexpr (READ) {
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) fw[nb] = wnx[nb];
+        // 4 W reads, then 8 x (4 MFMAs, 1 A read)
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int mb = 0; mb < 8; ++mb) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+      }
+    };
+    load(0, st0);
+    load(1, st1);
+    load(2, st2);
+    load(3, st3);
+    wait_vmcnt<12>();
+    lds_barrier();
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) fw[nb] = read_w(st0, nb);
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) fa[mb] = read_a(st0, mb);
+    using V8 = std::integral_constant<int, 8>;
+    using V4 = std::integral_constant<int, 4>;
+    using V0 = std::integral_constant<int, 0>;
+    int kt = 0;
+    for (; kt + 4 < nk; kt += 4) {
+      step(V8{}, Yes{}, Yes{}, st0, kt + 4, st1);
+      step(V8{}, Yes{}, Yes{}, st1, kt + 5, st2);
+      step(V8{}, Yes{}, Yes{}, st2, kt + 6, st3);
+      step(V8{}, Yes{}, Yes{}, st3, kt + 7, st0);
+    }
+    step(V8{}, No{}, Yes{}, st0, 0, st1);
+    step(V4{}, No{}, Yes{}, st0, 0, st2);
+    step(V0{}, No{}, Yes{}, st0, 0, st3);
+    step(V0{}, No{}, No{}, st0, 0, st0);
+    __builtin_amdgcn_sched_barrier(0);
   }
-  wait_vmcnt<8>(); lds_barrier(); load(kt + 3, st3); compute(st0);
-  wait_vmcnt<8>(); lds_barrier(); compute(st1);
-  wait_vmcnt<4>(); lds_barrier(); compute(st2);
-  wait_vmcnt<0>(); lds_barrier(); compute(st3);
   if constexpr (RMS) {
     ss += __shfl_xor(ss, 1);
     if ((tid & 1) == 0) sR[rr] = rsqrtf(ss / static_cast<float>(g.K) + RMS_EPS);
@@ -543,6 +621,212 @@ __global__ void __launch_bounds__(BTHREADS) gemm_nt_bf16_big_kernel(GemmArgs g) 
     const bf16_t* cb = pass < 4 ? st0 : (pass < 8 ? st1 : (pass < 12 ? st2 : st3));
     store16(C + static_cast<int64_t>(m) * g.ldc + n0 + nl, *reinterpret_cast<const uint4*>(cb + (ml & 63) * BCP + nl),
             g.nt);
+  }
+}
+
+// ------------------------------------------------------------------ 256 x 128 tiles, two per CU
+// The 256 x 256 kernel's operand path with half the tile width: 4 waves in a 2 (M) x 2 (N)
+// grid, each 128 x 64, and a three-stage ring of 24 KB stages (72 KB of LDS), so that two
+// workgroups share each CU.  With one workgroup per CU every CU runs its K loop, then its
+// epilogue, in step with the others, so the MFMAs idle while the whole chip stores C and
+// HBM idles while it multiplies; with two, one workgroup's epilogue, prologue and barrier
+// waits run under the other's MFMAs.
+constexpr int HBM = 256, HBN = 128, HTHREADS = 256;
+constexpr int HSTAGE = (HBM + HBN) * GBK;  // bf16 per stage: the A tile, then the W tile
+constexpr int HCP = HBN + 8;               // staged bf16 C row pitch
+constexpr int HFCP = HBN + 4;              // staged f32 C row pitch (half a tile at a time)
+static_assert(3 * HSTAGE >= HBM * HCP, "the bf16 C tile fits the stage buffers");
+static_assert(3 * HSTAGE * 2 >= (HBM / 2) * HFCP * 4, "half the f32 C tile fits the stage buffers");
+
+template <int EPI>
+__global__ void __launch_bounds__(HTHREADS, 2) gemm_nt_bf16_half_kernel(GemmArgs g) {
+  __shared__ __attribute__((aligned(16))) bf16_t sm[3 * HSTAGE];
+
+  const int nN = g.N / HBN;
+  const int nM = (g.M + HBM - 1) / HBM;
+  const int L = xcd_local_id(blockIdx.x, nN * nM);
+  const int mblk = L / nN;
+  const int m0 = mblk * HBM;
+  const int n0 = (L - mblk * nN) * HBN;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 1, wn = wave >> 1;
+  const int l16 = lane & 15, g4 = lane >> 4;
+
+  // direct loads: wave w fills A rows 64 w .. 64 w + 63 and W rows 32 w .. 32 w + 31 of a
+  // stage, 16 rows (1 KB) per load; lane (lr, ls) loads chunk ls ^ swz_row(lr) of its row,
+  // which lands in slot ls (the swizzle of swz(); the row's bits from 4 up do not enter)
+  const int lr = lane >> 2, ls = lane & 3;
+  const int ck = (ls ^ swz_row(lr)) * 8;
+  const bf16_t* gA[4];
+  const bf16_t* gW[2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    gA[i] = g.A + static_cast<int64_t>(min(m0 + wave * 64 + i * 16 + lr, g.M - 1)) * g.lda + ck;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) gW[i] = g.W + static_cast<int64_t>(n0 + wave * 32 + i * 16 + lr) * g.ldw + ck;
+  auto load = [&](int kt, bf16_t* stg) {
+    const int k0 = kt * GBK;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_global_load_lds((glb_void_t*)(gA[i] + k0), (lds_void_t*)(stg + (wave * 64 + i * 16) * GBK), 16,
+                                       0, 0);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      __builtin_amdgcn_global_load_lds((glb_void_t*)(gW[i] + k0),
+                                       (lds_void_t*)(stg + HBM * GBK + (wave * 32 + i * 16) * GBK), 16, 0, 0);
+  };
+  auto read_w = [&](const bf16_t* stg, int nb) {
+    return as_bf16x8(*reinterpret_cast<const uint4*>(stg + HBM * GBK + swz(wn * 64 + nb * 16 + l16, g4)));
+  };
+  auto read_a = [&](const bf16_t* stg, int mb) {
+    return as_bf16x8(*reinterpret_cast<const uint4*>(stg + swz(wm * 128 + mb * 16 + l16, g4)));
+  };
+
+  f32x4_t acc[4][8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // Stage s lives in buffer s % 3.  Step s multiplies the fragments of stage s, already in
+  // registers, and refills those registers with stage s + 1 as they free up (the W blocks
+  // into spare registers, A block mb right after its four MFMAs).  At the start of step s
+  // every wave has waited for its loads of stage s + 1 and its reads of stage s (lds_sync),
+  // so after the barrier stage s + 1 is complete and buffer s % 3 is free for stage s + 3.
+  bf16x8_t fw[4], fa[8];
+  auto mma_read = [&](const bf16_t* rd, auto do_read) {
+    constexpr bool READ = decltype(do_read)::value;
+    bf16x8_t wnx[4];
+    if constexpr (READ) {
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) wnx[nb] = read_w(rd, nb);
+    }
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) {
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+        acc[nb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fw[nb], fa[mb], acc[nb][mb], 0, 0, 0);
+      if constexpr (READ) fa[mb] = read_a(rd, mb);
+    }
+    if constexpr (READ) {
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) fw[nb] = wnx[nb];
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int mb = 0; mb < 8; ++mb) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    }
+  };
+  const int nk = g.K / GBK;  // at least 4
+  load(0, sm);
+  load(1, sm + HSTAGE);
+  load(2, sm + 2 * HSTAGE);
+  wait_vmcnt<12>();
+  lds_barrier();
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) fw[nb] = read_w(sm, nb);
+#pragma unroll
+  for (int mb = 0; mb < 8; ++mb) fa[mb] = read_a(sm, mb);
+  int bl = 0;  // buffer of stage s
+  for (int kt = 0; kt + 3 < nk; ++kt) {
+    const int br = bl == 2 ? 0 : bl + 1;
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt<6>();
+    lds_sync();
+    load(kt + 3, sm + bl * HSTAGE);
+    mma_read(sm + br * HSTAGE, std::true_type{});
+    __builtin_amdgcn_sched_barrier(0);
+    bl = br;
+  }
+  // the last three stages: nothing more to load
+  {
+    const int b1 = bl == 2 ? 0 : bl + 1, b2 = b1 == 2 ? 0 : b1 + 1;
+    wait_vmcnt<6>();
+    lds_barrier();
+    mma_read(sm + b1 * HSTAGE, std::true_type{});
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt<0>();
+    lds_barrier();
+    mma_read(sm + b2 * HSTAGE, std::true_type{});
+    __builtin_amdgcn_sched_barrier(0);
+    mma_read(sm, std::false_type{});
+  }
+  lds_sync();  // every wave is done with the stage buffers before C goes into them
+
+  if constexpr (EPI == GEMM_EPI_RESID_F32) {
+    // f32 rows through LDS, half the tile (128 rows, the waves with wm = half) at a time,
+    // then whole rows: lane l of a wave on columns 4 l .. 4 l + 3 of every other row pair,
+    // each access of a half wave one contiguous 512-byte row.  A residual element is read
+    // by the lane that stores its sum, so R may alias C.
+    float* fb = reinterpret_cast<float*>(sm);
+    const float* Rp = static_cast<const float*>(g.R);
+    float* Cp = static_cast<float*>(g.C);
+    const int hr = lane >> 5, hc = (lane & 31) * 4;  // a wave stores two rows per access
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      // rows 2 (wave + 4 i) + hr of the half, i = 0 .. 15; the first eight residual rows in
+      // flight before the tile half goes through LDS (rows past M re-read row M - 1)
+      auto rrow = [&](int i) {
+        const int m = min(m0 + half * 128 + 2 * (wave + 4 * i) + hr, g.M - 1);
+        return *reinterpret_cast<const f32x4_t*>(Rp + static_cast<int64_t>(m) * g.ldr + n0 + hc);
+      };
+      f32x4_t rv[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) rv[i] = rrow(i);
+      if (wm == half) {
+#pragma unroll
+        for (int mb = 0; mb < 8; ++mb) {
+          float* rowp = fb + (mb * 16 + l16) * HFCP + wn * 64 + g4 * 4;
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb) *reinterpret_cast<f32x4_t*>(rowp + nb * 16) = acc[nb][mb];
+        }
+      }
+      lds_sync();
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int rl = 2 * (wave + 4 * i) + hr;
+        const int m = m0 + half * 128 + rl;
+        const f32x4_t r = rv[i & 7];
+        if (i < 8) rv[i] = rrow(i + 8);
+        if (m < g.M) {
+          const f32x4_t v = *reinterpret_cast<const f32x4_t*>(fb + rl * HFCP + hc) + r;
+          store16(Cp + static_cast<int64_t>(m) * g.ldc + n0 + hc, __builtin_bit_cast(uint4, v), g.nt);
+        }
+      }
+      lds_sync();
+    }
+    return;
+  }
+#pragma unroll
+  for (int mb = 0; mb < 8; ++mb) {
+    const int ml = wm * 128 + mb * 16 + l16;
+    const int m = m0 + ml;
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const int nl = wn * 64 + nb * 16 + g4 * 4;
+      float v[4] = {acc[nb][mb][0], acc[nb][mb][1], acc[nb][mb][2], acc[nb][mb][3]};
+      epi_math<EPI>(g, m, n0 + nl, v);
+      uint2 o;
+      o.x = pack_bf16x2(v[0], v[1]);
+      o.y = pack_bf16x2(v[2], v[3]);
+      *reinterpret_cast<uint2*>(sm + ml * HCP + nl) = o;
+    }
+  }
+  lds_sync();
+  // 256 rows x 256 B: 16 threads per row, 16 rows per pass
+  bf16_t* C = static_cast<bf16_t*>(g.C);
+#pragma unroll
+  for (int pass = 0; pass < HBM / 16; ++pass) {
+    const int ml = pass * 16 + (tid >> 4);
+    const int m = m0 + ml;
+    if (m >= g.M) continue;
+    const int nl = (tid & 15) * 8;
+    store16(C + static_cast<int64_t>(m) * g.ldc + n0 + nl, *reinterpret_cast<const uint4*>(sm + ml * HCP + nl), g.nt);
   }
 }
 
@@ -803,6 +1087,35 @@ genrank_status launch_gemm_nt(int dtype, const void* A, int64_t lda, const void*
                R, ldr, static_cast<bf16_t*>(Cpre), ldpre, M, N, K};
     g.nt = static_cast<int64_t>(M) * N * (epi == GEMM_EPI_RESID_F32 ? 4 : 2) > STREAM_OUT_BYTES;
     const int grid = (N / GBN) * ((M + GBM - 1) / GBM);
+    // 256 x 128 tiles two per CU, or 256 x 256 tiles one per CU: measured on the pre-norm
+    // block's projections at d = 512 (K = 512), the former wins for N = 512 and N = 2048 (by
+    // 30-50 us at 377K rows), the latter for N = 1536 (by 40-60 us) and for K = 2048
+    const bool half_tiles = K == 512 && (N <= 512 || N >= 2048);
+    if (half_tiles && N % HBN == 0 && M >= 8 * HBM &&
+        static_cast<int64_t>(HBN) * ldw * 2 < (int64_t(1) << 32)) {
+      const int hgrid = (N / HBN) * ((M + HBM - 1) / HBM);
+      switch (epi) {
+        case GEMM_EPI_STORE:
+          hipLaunchKernelGGL(gemm_nt_bf16_half_kernel<GEMM_EPI_STORE>, dim3(hgrid), dim3(HTHREADS), 0, stream, g);
+          break;
+        case GEMM_EPI_RESID:
+          hipLaunchKernelGGL(gemm_nt_bf16_half_kernel<GEMM_EPI_RESID>, dim3(hgrid), dim3(HTHREADS), 0, stream, g);
+          break;
+        case GEMM_EPI_SILU:
+          hipLaunchKernelGGL(gemm_nt_bf16_half_kernel<GEMM_EPI_SILU>, dim3(hgrid), dim3(HTHREADS), 0, stream, g);
+          break;
+        case GEMM_EPI_DSILU:
+          hipLaunchKernelGGL(gemm_nt_bf16_half_kernel<GEMM_EPI_DSILU>, dim3(hgrid), dim3(HTHREADS), 0, stream, g);
+          break;
+        case GEMM_EPI_RESID_F32:
+          hipLaunchKernelGGL(gemm_nt_bf16_half_kernel<GEMM_EPI_RESID_F32>, dim3(hgrid), dim3(HTHREADS), 0, stream, g);
+          break;
+        default:
+          return GENRANK_E_ARG;
+      }
+      GR_CHECK_LAUNCH();
+      return GENRANK_OK;
+    }
     if (K % (4 * GBK) == 0 && K >= 512 && N % BBN == 0 && M >= 4 * BBM &&
         static_cast<int64_t>(BBN) * ldw * 2 < (int64_t(1) << 32)) {
       const int bgrid = (N / BBN) * ((M + BBM - 1) / BBM);

@@ -31,7 +31,8 @@ def _bound(a64, w64, want, K):
     (1, 128, 128), (127, 256, 256), (129, 768, 256), (1000, 256, 512), (4099, 128, 2048),
     (300, 512, 96), (64, 128, 32),     # K not a multiple of 128: the register-staged kernel
     (30011, 768, 256), (66000, 256, 512),  # many tiles, ragged M
-    (3001, 512, 512), (2049, 1536, 512), (1500, 256, 2048),  # 256 x 256 tiles (K >= 512)
+    (1500, 256, 2048), (2047, 1536, 512), (2049, 1536, 512),  # 256 x 256 tiles (K >= 512)
+    (3001, 512, 512),  # 256 x 128 tiles, two per CU (K = 512, N <= 512 or N >= 2048, M >= 2048)
 ])
 def test_linear_bf16_store(M, N, K):
     say(f"linear: bf16 M={M} N={N} K={K}")
@@ -48,7 +49,7 @@ def test_linear_bf16_store(M, N, K):
     assert np.all(got[:M, N:] == 7.0) and np.all(got[M:] == 7.0)
 
 
-@pytest.mark.parametrize("M,N,K", [(515, 256, 256), (130, 128, 512), (2000, 512, 512)])
+@pytest.mark.parametrize("M,N,K", [(515, 256, 256), (130, 128, 512), (2000, 512, 512), (2100, 384, 512)])
 def test_linear_bf16_residual_in_place(M, N, K):
     say(f"linear: bf16 residual M={M} N={N} K={K}")
     a, w, a64, w64 = _operands(M, N, K, seed=3 * M + K)
@@ -66,6 +67,8 @@ def test_linear_bf16_residual_in_place(M, N, K):
     (515, 256, 256),     # 128 x 128 tiles, operands streamed into LDS
     (130, 128, 96),      # the register-staged kernel
     (2000, 512, 512),    # 256 x 256 tiles
+    (2305, 512, 512),    # 256 x 128 tiles, ragged M
+    (4100, 128, 2048),   # 128 x 128 tiles, long K
     (37, 64, 64),        # N not a multiple of 128: the plain tiled kernel
 ])
 def test_linear_bf16_residual_f32_in_place(M, N, K):
@@ -89,7 +92,8 @@ def test_linear_bf16_residual_f32_in_place(M, N, K):
     assert np.array_equal(got[M:], r[M:].astype(np.float64))
 
 
-@pytest.mark.parametrize("M,N,K", [(333, 1024, 256), (64, 128, 96), (1300, 2048, 512)])
+@pytest.mark.parametrize("M,N,K", [(333, 1024, 256), (64, 128, 96), (1300, 2048, 512), (2600, 1024, 512),
+                                   (2100, 2048, 512)])
 def test_linear_bf16_silu_with_pre(M, N, K):
     say(f"linear: bf16 silu M={M} N={N} K={K}")
     a, w, a64, w64 = _operands(M, N, K, seed=5 * M + N)
