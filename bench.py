@@ -101,7 +101,7 @@ def parse():
     p.add_argument("--calibrate-copy-mb", type=int, default=0,
                    help="also run one plain device copy of this many MiB (counter calibration)")
     p.add_argument("--units-once", metavar="ORDER_JSON", default=None,
-                   help="pre-norm stacks, for counter runs: after the warm-up steps run every unit of "
+                   help="for counter runs: after the warm-up steps run every unit of "
                         "the step once, in order, write the units' names and kinds to ORDER_JSON, make the "
                         "calibration copy (--calibrate-copy-mb) and stop")
     p.add_argument("--write-traffic", nargs="+", metavar="ARG", default=None,
@@ -1070,6 +1070,22 @@ def main():
         torch.cuda.synchronize()
         if not torch.equal(y_ref, y):
             log("WARNING: decomposed step differs from genrank_layer_fwd")
+    if args.units_once:
+        # as for the stacks: every unit once, alone, then the calibration copy
+        if args.calibrate_copy_mb > 0:
+            src = torch.ones(args.calibrate_copy_mb * (1 << 20) // 4, dtype=torch.float32, device=dev)
+            dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _, fn in units:
+            fn()
+            torch.cuda.synchronize()
+        with open(args.units_once, "w") as f:
+            json.dump({"workload": cfg.name, "units": [[n, n] for n in names], "copy_mib": args.calibrate_copy_mb}, f)
+        if args.calibrate_copy_mb > 0:
+            dst.copy_(src)
+            torch.cuda.synchronize()
+        log(f"units once: {len(units)} launches; order in {args.units_once}")
+        return
     if args.calibrate_copy_mb > 0:
         n = args.calibrate_copy_mb * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)
