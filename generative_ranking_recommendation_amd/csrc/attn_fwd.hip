@@ -859,9 +859,9 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
 
 // ------------------------------------------------------------------ bf16 pair kernel
 // One workgroup per (user, head) pair, for batches whose longest history fits in LDS
-// (PAIR_MAXK keys).  The pair's whole K and V history goes into LDS once (direct loads,
-// 64-key tiles with the ring kernel's swizzles and transposing V reads), together with
-// every key's bias term.  The 8 waves then work through the pair's 32-query units
+// (PAIR_MAXK keys).  The pair's whole K and V history goes into LDS once, in 64-key tiles
+// (K by direct loads with the ring kernel's swizzle, V written transposed from registers),
+// together with every key's bias term.  The 8 waves then work through the pair's 32-query units
 // (candidate units first, then history units newest first) with no further barrier:
 // each wave runs its units' key tiles from LDS on its own.  Against the tile grid this
 // loads every K/V byte of a pair once instead of once per query tile, and pays one
