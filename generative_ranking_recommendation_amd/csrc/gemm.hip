@@ -2,16 +2,19 @@
 //
 //   C[M, N] = A[M, K] . W[N, K]^T  (+ epilogue), f32 accumulation.
 //
-// Tile: 128 (M) x 128 (N) x 64 (K) per 256-thread workgroup; 2 x 2 waves of 64 x 64.
-// Each wave issues v_mfma_f32_16x16x32_bf16 with W rows as the MFMA row operand and A
-// rows as the column operand, so each lane ends with 4 consecutive N values of one A row
-// and stores them as one 8-byte write.  Both operands are K-contiguous and staged through
-// LDS with a 16-byte row pad (conflict-free 16-byte reads).  The next K tile is fetched
-// into registers while the current one is multiplied.  Workgroups are renumbered so that
-// the N tiles of one M tile run on the same XCD and share its L2.
-//
-// A second, simple kernel handles f32 data and the transposed products of the backward
-// pass (general strides, LDS-tiled FMA).
+// Every bf16 kernel issues v_mfma_f32_16x16x32_bf16 with W rows as the MFMA row operand and
+// A rows as the column operand, so each lane ends with 4 consecutive N values of one A row.
+// Both operands are K-contiguous and XOR-swizzled in LDS (conflict-free 16-byte fragment
+// reads).  C tiles leave through LDS, so that every global store writes whole 16-byte pieces
+// of long row runs (measured faster than 16-byte stores straight from the registers, whose
+// runs are 64 bytes).  Workgroups are renumbered so that the N tiles of one M tile run on the
+// same XCD and share its L2.  The kernels, by shape (launch_gemm_nt picks):
+//   gemm_nt_bf16_kernel       128 x 128, 4 waves, operands staged through registers
+//   gemm_nt_bf16_dma_kernel   128 x 128, 4 waves, operands loaded straight into LDS
+//   gemm_nt_bf16_big_kernel   256 x 256, 8 waves, one workgroup per CU (K >= 512)
+//   gemm_nt_bf16_half_kernel  256 x 128, 4 waves, two workgroups per CU (K = 512)
+// plus an LDS-tiled FMA kernel for f32 and general strides, and the transposed products of
+// the backward pass.
 #include <algorithm>
 #include <type_traits>
 
