@@ -10,7 +10,7 @@ from __future__ import annotations
 
 import ctypes
 import os
-from ctypes import POINTER, Structure, c_char_p, c_float, c_int32, c_int64, c_size_t, c_uint8, c_void_p
+from ctypes import POINTER, Structure, c_char_p, c_float, c_int32, c_int64, c_size_t, c_uint8, c_uint32, c_void_p
 
 import numpy as np
 
@@ -76,6 +76,7 @@ _SIGS = {
     "genrank_version": (c_int32, []),
     "genrank_workspace_size": (c_int32, [c_int32, POINTER(Batch), POINTER(LayerWeights), POINTER(c_size_t)]),
     "genrank_validate_host": (c_int32, [POINTER(Batch), POINTER(Inputs), POINTER(Tables), POINTER(c_int64)]),
+    "genrank_error_word": (c_int32, [POINTER(c_uint32), c_int32, c_void_p]),
     "genrank_embed_sum": (c_int32, [POINTER(Batch), POINTER(Inputs), POINTER(Tables), c_void_p, c_void_p]),
     "genrank_attn_fwd": (c_int32, [POINTER(Batch), c_void_p, c_void_p, c_void_p, Alibi, c_void_p,
                                    c_void_p, c_void_p, c_int64, c_void_p, c_int64, c_void_p, c_void_p]),
@@ -238,6 +239,17 @@ def genrank_validate_host(batch: Batch, inputs: Inputs, tables: Tables):
     s = lib().genrank_validate_host(ctypes.byref(batch), ctypes.byref(inputs), ctypes.byref(tables),
                                     ctypes.byref(bad))
     return s, bad.value
+
+
+ERR_ID_RANGE, ERR_HIST_LONG = 1, 2
+
+
+def genrank_error_word(clear=True, stream=None) -> int:
+    """The current device's error word (GENRANK_ERR_* bits), read after `stream` finishes;
+    cleared afterwards unless clear is False."""
+    w = c_uint32(0)
+    _check("genrank_error_word", lib().genrank_error_word(ctypes.byref(w), int(bool(clear)), _stream(stream)))
+    return int(w.value)
 
 
 def genrank_embed_sum(batch, inputs, tables, x_out, stream=None):

@@ -254,6 +254,19 @@ genrank_status genrank_workspace_size(int32_t op, const genrank_batch* b,
   }
 }
 
+genrank_status genrank_error_word(uint32_t* word, int32_t clear, genrank_stream_t stream) {
+  if (!word) return GENRANK_E_ARG;
+  uint32_t* dev = device_error_word();
+  if (!dev) return GENRANK_E_HIP;
+  if (hipStreamSynchronize(S(stream)) != hipSuccess) return GENRANK_E_HIP;
+  if (hipMemcpy(word, dev, sizeof(uint32_t), hipMemcpyDeviceToHost) != hipSuccess) return GENRANK_E_HIP;
+  if (clear) {
+    const uint32_t zero = 0;
+    if (hipMemcpy(dev, &zero, sizeof(uint32_t), hipMemcpyHostToDevice) != hipSuccess) return GENRANK_E_HIP;
+  }
+  return GENRANK_OK;
+}
+
 genrank_status genrank_validate_host(const genrank_batch* b, const genrank_inputs* in,
                                      const genrank_tables* t, int64_t* bad_row) {
   if (bad_row) *bad_row = -1;

@@ -77,6 +77,7 @@ struct AttnArgs {
   const int64_t* tb;
   int n_tb, tb_p2;
   int nt_o;  // o far larger than the last-level cache: streaming stores (pair kernel)
+  uint32_t* err;  // the device error word (GENRANK_ERR_*)
 };
 
 // variant bits of the ALiBi kernels: the fully visible history mask, the bucketed time term
@@ -953,7 +954,9 @@ __global__ void __launch_bounds__(PAIR_NT) attn_fwd_pair_kernel(AttnArgs a) {
     ts_ref = a.req[u];
   }
   // (a history longer than the batch's declared maximum is cut, so that LDS is never
-  // overrun; the declared maximum is the caller's promise)
+  // overrun, and flagged in the device error word; the declared maximum is the caller's
+  // promise)
+  if (len > PAIR_MAXK && tid == 0) report_error(a.err, GENRANK_ERR_HIST_LONG);
   const int N = min(len, PAIR_MAXK);
   const int n_tiles = (N + AK - 1) / AK;
   const int l16 = lane & 15, g4 = lane >> 4;
@@ -1551,6 +1554,7 @@ genrank_status launch_attn_fwd(const genrank_batch* b, const int32_t* offsets, c
     a.o = static_cast<bf16_t*>(o);
     a.ld_o = ld_o;
     a.nt_o = T * b->d * 2 > (int64_t(256) << 20);  // streaming stores for o beyond the last-level cache
+    a.err = device_error_word();
     a.lse = lse;
     for (int h = 0; h < b->H; ++h) {
       a.sp2[h] = alibi.slopes_pos[h] * LOG2E;

@@ -186,6 +186,10 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
+// Sets a bit of the device error word (GENRANK_ERR_*); err may be NULL
+__device__ __forceinline__ void report_error(uint32_t* err, uint32_t bit) {
+  if (err) atomicOr(err, bit);
+}
 // lgkmcnt(0) with vmcnt and expcnt left alone: the wave's LDS reads and writes are done
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 // Barrier for ordinary LDS writes and reads (without the vmcnt wait __syncthreads implies)

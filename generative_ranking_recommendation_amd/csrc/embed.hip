@@ -13,6 +13,7 @@
 // rows are then gathered with 16-byte loads (d/8 lanes per bf16 row), summed in f32 and
 // written once.  The small tables stay L2-resident across the grid.
 #include <algorithm>
+#include <mutex>
 
 #include "common.hpp"
 #include "internal.hpp"
@@ -42,6 +43,8 @@ struct EmbedArgs {
   int n_action, n_pos, n_ri, n_bounds;
   int64_t T_h;
   uint32_t bytes_item, bytes_action, bytes_pos, bytes_ri, bytes_rt;  // table sizes (< 4 GB)
+  int64_t n_item;
+  uint32_t* err;        // the device error word (GENRANK_ERR_*)
   void* out;            // gather: [T, d]; debug: int32 [6, T]
   const void* dx;       // backward: [T, d]
   float* g_item; float* g_action; float* g_pos; float* g_ri; float* g_rt;
@@ -125,6 +128,8 @@ __device__ int derive_chunk(const EmbedArgs& a, RowIdx* sidx, int64_t* sbounds, 
   if (is_hist) {
     const int s0 = chunk * EMB_ROWS;  // first sequence slot of the chunk
     if (s0 >= N) return 0;            // uniform across the block
+    // the grid covers batch.max_hist rows per user: a longer history is cut here
+    if (tid == 0 && chunk == a.hist_chunks - 1 && N > s0 + EMB_ROWS) report_error(a.err, GENRANK_ERR_HIST_LONG);
     const int rows = min(EMB_ROWS, N - s0);
     const int64_t r0 = off + s0;
     // the chunk's own rows (wave 0), the bucket bounds and the prefix, all in flight
@@ -136,6 +141,12 @@ __device__ int derive_chunk(const EmbedArgs& a, RowIdx* sidx, int64_t* sbounds, 
       t = a.hist_ts[r];
       item = a.hist_items[r];
       act = a.hist_actions[r];
+      // ids outside their tables: flagged, and the nearest valid row used
+      if (item < 0 || item >= a.n_item || act < 0 || act >= a.n_action) {
+        report_error(a.err, GENRANK_ERR_ID_RANGE);
+        item = static_cast<int>(min<int64_t>(max(item, 0), a.n_item - 1));
+        act = min(max(act, 0), a.n_action - 1);
+      }
     }
     for (int k = tid; k < a.n_bounds; k += EMB_THREADS) sbounds[k] = a.rt_bounds[k];
     const int64_t t_r0 = a.hist_ts[r0];
@@ -184,7 +195,13 @@ __device__ int derive_chunk(const EmbedArgs& a, RowIdx* sidx, int64_t* sbounds, 
   const int rows = min(EMB_ROWS, a.m - c0);
   const int64_t r0 = a.T_h + static_cast<int64_t>(u) * a.m + c0;
   int item = 0;
-  if (tid < rows) item = a.cand_items[static_cast<int64_t>(u) * a.m + c0 + tid];
+  if (tid < rows) {
+    item = a.cand_items[static_cast<int64_t>(u) * a.m + c0 + tid];
+    if (item < 0 || item >= a.n_item) {
+      report_error(a.err, GENRANK_ERR_ID_RANGE);
+      item = static_cast<int>(min<int64_t>(max(item, 0), a.n_item - 1));
+    }
+  }
   for (int k = tid; k < a.n_bounds; k += EMB_THREADS) sbounds[k] = a.rt_bounds[k];
   const int64_t req = a.req_ts[u];
   const int64_t t_last = N > 0 ? a.hist_ts[off + N - 1] : 0;
@@ -688,6 +705,13 @@ __global__ void __launch_bounds__(256) seg_fix_kernel(SegArgs g) {
   }
 }
 
+// ---- the device error word: one per GPU (file-scope device memory, located once per device
+// with hipGetSymbolAddress; `error_words` names a host-side stand-in, never device memory)
+static __device__ __align__(16) uint32_t error_words[4];
+constexpr int ERR_MAX_DEVICES = 64;
+std::once_flag err_once[ERR_MAX_DEVICES];
+uint32_t* err_ptr[ERR_MAX_DEVICES];
+
 EmbedArgs make_args(const genrank_batch* b, const genrank_inputs* in, const genrank_tables* t) {
   EmbedArgs a{};
   a.offsets = in->hist_offsets;
@@ -720,6 +744,8 @@ EmbedArgs make_args(const genrank_batch* b, const genrank_inputs* in, const genr
   a.bytes_pos = clamp32(static_cast<int64_t>(t->n_pos) * rb);
   a.bytes_ri = clamp32(static_cast<int64_t>(t->n_ri) * rb);
   a.bytes_rt = clamp32(static_cast<int64_t>(t->n_rt) * rb);
+  a.n_item = t->n_item;
+  a.err = device_error_word();
   return a;
 }
 
@@ -773,6 +799,16 @@ void launch_gather(const genrank_batch* b, const genrank_tables* t, const EmbedA
 }
 
 }  // namespace
+
+uint32_t* device_error_word() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= ERR_MAX_DEVICES) return nullptr;
+  std::call_once(err_once[dev], [dev] {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(error_words)) == hipSuccess) err_ptr[dev] = static_cast<uint32_t*>(p);
+  });
+  return err_ptr[dev];
+}
 
 genrank_status check_embed_args(const genrank_batch* b, const genrank_inputs* in,
                                 const genrank_tables* t) {

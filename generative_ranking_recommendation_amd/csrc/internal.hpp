@@ -106,6 +106,8 @@ genrank_status launch_gemm_nt(int dtype, const void* A, int64_t lda, const void*
 // The bf16 GEMM with the RMSNorm of A's rows fused (A raw, Wg = W with the gain folded into
 // its columns, see launch_scale_cols); epi STORE or SILU; requires gemm_rms_ok(N, K)
 bool gemm_rms_ok(int N, int K);
+// The current device's error word (GENRANK_ERR_* bits), or NULL if it cannot be located
+uint32_t* device_error_word();
 genrank_status launch_gemm_nt_rms(const void* A, int64_t lda, const void* Wg, int64_t ldw, void* C, int64_t ldc,
                                   int M, int N, int K, int epi, hipStream_t stream);
 // out[n, k] = bf16(W[n, k] gain[k]) (bf16 W and out)

@@ -219,6 +219,23 @@ GENRANK_API genrank_status genrank_workspace_size(int32_t op, const genrank_batc
 GENRANK_API genrank_status genrank_validate_host(const genrank_batch* batch, const genrank_inputs* in,
                                      const genrank_tables* tables, int64_t* bad_row);
 
+/* Device error word: one per GPU, sticky.  Kernels that meet an input genrank_validate_host
+ * would have rejected (a caller that skipped it) neither fault nor stop: they go on as
+ * stated below and set a bit of this word, which stays set until read with clear != 0.
+ *   GENRANK_ERR_ID_RANGE   an item id outside [0, n_item) or an action id outside
+ *                          [0, n_action) reached the embedding kernels (forward, backward,
+ *                          genrank_debug_indices): the nearest valid row is used.
+ *   GENRANK_ERR_HIST_LONG  a history longer than batch.max_hist reached the embedding
+ *                          kernels (rows past max_hist are not written), or a history longer
+ *                          than 576 actions reached the bf16 attention kernel that holds a
+ *                          user's keys in LDS (chosen when batch.max_hist <= 576): keys and
+ *                          queries past the 576th are ignored.
+ * genrank_error_word waits for `stream`, then copies the current device's word to *word
+ * (E_ARG if word is NULL, E_HIP if the word cannot be read). */
+#define GENRANK_ERR_ID_RANGE 1u
+#define GENRANK_ERR_HIST_LONG 2u
+GENRANK_API genrank_status genrank_error_word(uint32_t* word, int32_t clear, genrank_stream_t stream);
+
 /* ------------------------------------------------------------------ hot path */
 
 /* Fused index derivation + five-table gather-sum ([GR-zh] section 1.4.2, the input

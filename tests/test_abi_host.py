@@ -159,6 +159,8 @@ def test_entry_points_reject_bad_arguments(lib):
                                         FAKE, 256, FAKE, FAKE, FAKE, FAKE, 768, 0, None) == -6
     assert lib.genrank_attn_bwd_noalloc(ctypes.byref(big), FAKE, FAKE, FAKE, sl.struct, FAKE, FAKE, FAKE, 768, FAKE,
                                         None, 256, FAKE, FAKE, FAKE, FAKE, 768, 0, None) == -1
+    # the device error word needs somewhere to put it
+    assert lib.genrank_error_word(None, 1, None) == -1
     # RMSNorm: dtype pairs, null pointers, shapes
     assert lib.genrank_rmsnorm(B.BF16, B.F32, FAKE, FAKE, FAKE, 4, 256, None) == -3
     assert lib.genrank_rmsnorm(B.F32, 7, FAKE, FAKE, FAKE, 4, 256, None) == -3
