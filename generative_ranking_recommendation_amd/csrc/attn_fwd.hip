@@ -861,7 +861,7 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
 // ------------------------------------------------------------------ bf16 pair kernel
 // One workgroup per (user, head) pair, for batches whose longest history fits in LDS
 // (PAIR_MAXK keys).  The pair's whole K and V history goes into LDS once, in 64-key tiles
-// (K by direct loads with the ring kernel's swizzle, V written transposed from registers),
+// (direct loads with the ring kernel's swizzles; V^T operands through transposing reads),
 // together with every key's bias term.  The 8 waves then work through the pair's 32-query units
 // (candidate units first, then history units newest first) with no further barrier:
 // each wave runs its units' key tiles from LDS on its own.  Against the tile grid this
@@ -992,27 +992,23 @@ __global__ void __launch_bounds__(PAIR_NT) attn_fwd_pair_kernel(AttnArgs a) {
   // the first unit's query fragments travel with the K/V tiles
   if (wave < n_units) fetch_q(wave);
 
-  // ---- the pair's K/V tiles.  A tile's K half is row-major (key, dim) as the ring
-  // kernel keeps it: wave w loads rows 8 w .. 8 w + 7 straight into LDS (lane l: row
-  // 8 w + l / 8, LDS chunk l % 8 <- global chunk (l % 8) ^ ((row >> 1) & 7)).  Its V half
-  // is V^T (dim, key), with the keys of each 32-key half in the order the P^T fragments
-  // hold them (vt_slot) and the same 16-byte chunk swizzle by (dim >> 1) & 7, so that a
-  // PV operand (one dim, the 8 keys a lane group multiplies) is one 16-byte read.  V
-  // rows come through registers and are written transposed, once per pair.  Rows past the
-  // history end re-read its last row.
-  uint4 vrow[PAIR_MAXT];
+  // ---- the pair's K/V tiles, row-major (key, dim), straight into LDS: wave w loads rows
+  // 8 w .. 8 w + 7 of every K and V tile (lane l: row 8 w + l / 8, LDS chunk l % 8 <- global
+  // chunk (l % 8) ^ ((row >> 1) & 7) for K, (l % 8) ^ 2 ((row >> 1) & 3) for V).  Rows past
+  // the history end re-read its last row.
   const int lr = wave * 8 + (lane >> 3);
   const int lc = lane & 7;
   {
     const uint32_t row_bytes = static_cast<uint32_t>(a.ld_h) * 2u;
     const char* gk = reinterpret_cast<const char*>(a.kh + off * a.ld_h + h * DH + ((lc ^ ((lr >> 1) & 7)) * 8));
-    const char* gv = reinterpret_cast<const char*>(a.vh + off * a.ld_h + h * DH + lc * 8);
+    const char* gv = reinterpret_cast<const char*>(a.vh + off * a.ld_h + h * DH + ((lc ^ (2 * ((lr >> 1) & 3))) * 8));
 #pragma unroll
     for (int t = 0; t < PAIR_MAXT; ++t) {
       if (t < n_tiles) {
         const uint32_t ro = static_cast<uint32_t>(min(t * AK + lr, N - 1)) * row_bytes;
         __builtin_amdgcn_global_load_lds((glb_void_t*)(gk + ro), (lds_void_t*)(sKV + t * STAGE + wave * 8 * DH), 16, 0, 0);
-        vrow[t] = *reinterpret_cast<const uint4*>(gv + ro);
+        __builtin_amdgcn_global_load_lds((glb_void_t*)(gv + ro), (lds_void_t*)(sKV + t * STAGE + AK * DH + wave * 8 * DH),
+                                         16, 0, 0);
       }
     }
   }
@@ -1035,22 +1031,6 @@ __global__ void __launch_bounds__(PAIR_NT) attn_fwd_pair_kernel(AttnArgs a) {
       sTB[k] = b > INT32_MAX ? INT32_MAX : (b < INT32_MIN ? INT32_MIN : static_cast<int32_t>(b));
     }
   wait_vmcnt<0>();
-  {
-    const int slot = vt_slot(lr);
-#pragma unroll
-    for (int t = 0; t < PAIR_MAXT; ++t) {
-      if (t < n_tiles) {
-        const uint32_t w4[4] = {vrow[t].x, vrow[t].y, vrow[t].z, vrow[t].w};
-        bf16_t* vt = sKV + t * STAGE + AK * DH;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int d = lc * 8 + e;
-          vt[d * AK + (((slot >> 3) ^ ((d >> 1) & 7)) << 3) + (slot & 7)] =
-              static_cast<bf16_t>((e & 1) ? (w4[e >> 1] >> 16) : (w4[e >> 1] & 0xFFFFu));
-        }
-      }
-    }
-  }
   lds_sync();
   float tbk_self = 0.f;  // bucketed time term of a candidate's own key (gap 0)
   if constexpr (TBK) {
@@ -1063,9 +1043,17 @@ __global__ void __launch_bounds__(PAIR_NT) attn_fwd_pair_kernel(AttnArgs a) {
   // LDS offsets (bf16 elements) of this lane's fragments inside a tile
   const int k_off0 = l16 * DH + (((0 + g4) ^ ((l16 >> 1) & 7)) * 8);
   const int k_off1 = l16 * DH + (((4 + g4) ^ ((l16 >> 1) & 7)) * 8);
-  // V^T: dim nb * 16 + l16, the 8 keys of lane group g4 in 32-key half ks
-  const int vt_off0 = AK * DH + l16 * AK + (((0 + g4) ^ ((l16 >> 1) & 7)) * 8);
-  const int vt_off1 = AK * DH + l16 * AK + (((4 + g4) ^ ((l16 >> 1) & 7)) * 8);
+  // V^T operand of dim block nb through transposing reads of the row-major V tile: within
+  // each 16-lane group, output lane j element e of ds_read_b64_tr_b16 is element j % 4 of
+  // the 8 bytes lane 4 e + j / 4 addressed.  Lane (l16, g4) addresses key row 4 g4 + l16 / 4
+  // (and + 16, in the 32-key half), dims 16 nb + 4 (l16 % 4) .., through V's swizzle; so
+  // lane group g4 receives dim 16 nb + l16 of keys 4 g4 .. 4 g4 + 3 and 16 + 4 g4 .., the
+  // keys its P^T fragment holds.
+  int v_off[4];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb)
+    v_off[nb] = AK * DH + (4 * g4 + (l16 >> 2)) * DH +
+                (((2 * nb + ((l16 & 3) >> 1)) ^ (2 * (((4 * g4 + (l16 >> 2)) >> 1) & 3))) * 8) + (l16 & 1) * 4;
   // a tile's start as a wave-uniform value: every fragment read is then one address
   // register plus a constant offset
   auto tile_at = [&](int kt) __attribute__((always_inline)) {
@@ -1258,7 +1246,12 @@ __global__ void __launch_bounds__(PAIR_NT) attn_fwd_pair_kernel(AttnArgs a) {
         if (MASKED && 2 * ks > kd0 + 1) continue;  // past both blocks' diagonals
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb)
-          vf[ks][nb] = as_bf16x8(*reinterpret_cast<const uint4*>(stg + (ks ? vt_off1 : vt_off0) + nb * 16 * AK));
+        {
+          const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(stg + v_off[nb] + (ks * 32) * DH));
+          const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(stg + v_off[nb] + (ks * 32 + 16) * DH));
+          const v4i16_t both[2] = {lo, hi};
+          vf[ks][nb] = __builtin_bit_cast(bf16x8_t, both);
+        }
       }
     };
     // O^T += V^T P^T for block hb
