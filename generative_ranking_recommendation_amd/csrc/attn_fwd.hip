@@ -78,6 +78,7 @@ struct AttnArgs {
   int n_tb, tb_p2;
   int nt_o;  // o far larger than the last-level cache: streaming stores (pair kernel)
   uint32_t* err;  // the device error word (GENRANK_ERR_*)
+  int order;      // pair kernel: take the users heaviest first (0: every history has one length)
 };
 
 // variant bits of the ALiBi kernels: the fully visible history mask, the bucketed time term
@@ -909,13 +910,14 @@ __global__ void __launch_bounds__(PAIR_NT) attn_fwd_pair_kernel(AttnArgs a) {
   // Which pair: workgroups run in launch order, so the pairs go heaviest first (users
   // ordered by key-tile count, descending, ties by index) and the light ones fill the end
   // of the launch.  Every workgroup derives the same order from the offsets.  With more
-  // users than threads the order is the plain one.  The thread that finds the pair
+  // users than threads, or when every history has the same length (the host knows it:
+  // total_hist = B max_hist), the order is the plain one.  The thread that finds the pair
   // passes on its user's offset, length and request time (no second round trip).
   const int ur = blockIdx.x / a.H;
   const int h = blockIdx.x - ur * a.H;
   int u = ur, len;
   int64_t off, ts_ref;
-  if (a.B <= PAIR_NT) {
+  if (a.order && a.B <= PAIR_NT) {
     if (tid <= PAIR_MAXT) sCnt[tid] = 0;
     int ntl = -1, o0 = 0, o1 = 0;
     int64_t rq = 0;
@@ -1548,6 +1550,7 @@ genrank_status launch_attn_fwd(const genrank_batch* b, const int32_t* offsets, c
     a.ld_o = ld_o;
     a.nt_o = T * b->d * 2 > (int64_t(256) << 20);  // streaming stores for o beyond the last-level cache
     a.err = device_error_word();
+    a.order = b->total_hist != static_cast<int64_t>(b->B) * b->max_hist;
     a.lse = lse;
     for (int h = 0; h < b->H; ++h) {
       a.sp2[h] = alibi.slopes_pos[h] * LOG2E;

@@ -97,6 +97,7 @@ def test_attn_f32_shapes(lengths, m):
     ([37, 64], 0),
     ([512, 511, 1, 17], 33),
     ([700, 3, 513, 64], 21),      # histories beyond one bias chunk (512 keys)
+    ([200, 200, 200], 24),        # one history length: users in plain order
 ])
 def test_attn_bf16_shapes(lengths, m):
     say(f"attn: bf16 lengths={lengths} m={m}")
