@@ -1511,11 +1511,14 @@ void set_variant(AttnArgs& a, const genrank_alibi& alibi) {
   a.tb_p2 = bucket_p2(a.n_tb);
 }
 // Batches whose longest history fits in LDS take the pair kernel (one workgroup per
-// (user, head)); longer histories the ring kernel over the tile grid.
+// (user, head)); longer histories, and outputs not 16-byte aligned row by row, the ring
+// kernel over the tile grid.
 void launch_bf16_variant(int flags, int max_hist, dim3 grid, hipStream_t stream, const AttnArgs& a) {
   const int var = ((flags & GENRANK_ATTN_FULL_HISTORY) ? VAR_FULL : 0) |
                   ((flags & GENRANK_ATTN_TIME_BUCKET) ? VAR_TBUCKET : 0);
-  if (max_hist <= PAIR_MAXK) {
+  // the pair kernel's epilogue stores 16-byte runs of an output row: o and its rows 16-byte aligned
+  const bool o16 = reinterpret_cast<uintptr_t>(a.o) % 16 == 0 && a.ld_o % 8 == 0;
+  if (max_hist <= PAIR_MAXK && o16) {
     const dim3 pg(static_cast<unsigned>(a.B * a.H));
     switch (var) {
       case 0: hipLaunchKernelGGL((attn_fwd_pair_kernel<0>), pg, dim3(PAIR_NT), 0, stream, a); break;
@@ -1626,8 +1629,12 @@ genrank_status launch_attn_fwd_cached(const genrank_batch* b, const int32_t* off
   const int64_t G = pairs * a.cand_tiles;
   if (G > INT32_MAX) return GENRANK_E_SHAPE;
   set_variant(a, alibi);
-  // the ring kernel (candidate tiles stream the history); the variant instance matches the
-  // full forward's, and candidate rows get the same bits from both kernels
+  a.err = device_error_word();
+  // The ring kernel: each 128-candidate tile streams its user's history.  The pair kernel,
+  // which loads a history once for all of a user's candidates, measured slower here (342
+  // against 329 us at 512 users x 256 candidates x 480 keys, d = 512): with no history
+  // queries to share the load, its one workgroup per CU waits on it.  The variant instance
+  // matches the full forward's, and candidate rows get the same bits from both kernels.
   launch_bf16_variant(alibi.flags, INT32_MAX, dim3(static_cast<unsigned>(G)), stream, a);
   GR_CHECK_LAUNCH();
   return GENRANK_OK;

@@ -265,9 +265,10 @@ GENRANK_API genrank_status genrank_embed_sum(const genrank_batch* batch, const g
  * q, k, v: [T, ld_qkv] rows, head h at columns [h*dh, (h+1)*dh) of each (they may be
  * three views into one [T, 3d] buffer).  o: [T, ld_o], head h at h*dh.
  * lse: [T, H] f32 or NULL.  bf16 requires dh == 64; f32 requires dh <= 64.
- * bf16 kernels: when batch.max_hist <= 576, one workgroup per (user, head) holds that
- * user's whole K/V history in LDS (users taken longest history first); otherwise a tiled
- * kernel streams K/V per 128-query tile.  batch.max_hist selects between them and must
+ * bf16 kernels: when batch.max_hist <= 576 and o is 16-byte aligned with ld_o a multiple
+ * of 8, one workgroup per (user, head) holds that user's whole K/V history in LDS (users
+ * taken longest history first); otherwise a tiled kernel streams K/V per 128-query tile.
+ * Both give the same bits.  batch.max_hist selects between them and must
  * not be below any user's history length (a longer history would be cut to 576 keys:
  * wrong results for that user, no out-of-bounds access). */
 GENRANK_API genrank_status genrank_attn_fwd(const genrank_batch* batch, const int32_t* hist_offsets,
@@ -488,7 +489,9 @@ GENRANK_API genrank_status genrank_embed_sum_cand(const genrank_batch* batch, co
 /* The attention of genrank_attn_fwd for the candidate rows only: q, k, v, o: [B*m] rows
  * (row stride ld_qkv, ld_o; lse [B*m, H] or NULL); the history keys and values come from
  * k_hist, v_hist ([T_h] rows, stride ld_hist).  ld_qkv, ld_hist multiples of 8, ld_o of 4;
- * q, k, v, k_hist, v_hist 16-byte and o 8-byte aligned (else GENRANK_E_SHAPE / E_ARG). */
+ * q, k, v, k_hist, v_hist 16-byte and o 8-byte aligned (else GENRANK_E_SHAPE / E_ARG).
+ * The tiled kernel of genrank_attn_fwd, which reads a user's history once per 128-candidate
+ * tile; candidate rows get the same bits as from genrank_attn_fwd. */
 GENRANK_API genrank_status genrank_attn_fwd_cached(const genrank_batch* batch, const int32_t* hist_offsets,
                                                    const int64_t* hist_ts, const int64_t* req_ts,
                                                    genrank_alibi alibi, const void* q, const void* k,

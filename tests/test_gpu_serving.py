@@ -19,9 +19,19 @@ from generative_ranking_recommendation_amd.device import stored_to_device
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("lengths,m", [([64, 300, 480, 5, 0, 1], 32), ([129, 0, 200], 130)])
-def test_attn_fwd_cached_equals_full(lengths, m):
-    say(f"serving: cached attention {lengths} m={m}")
+# the full forward runs the LDS-resident pair kernel for histories up to 576 keys (the ring
+# kernel beyond), the cached one the ring kernel: the candidate rows must agree bit for bit
+@pytest.mark.parametrize("lengths,m", [
+    ([64, 300, 480, 5, 0, 1], 32),
+    ([129, 0, 200], 130),
+    ([480, 480, 17], 256),           # the stack workload's top block
+    ([600, 30], 200),                # a history past 576 keys: the ring kernel on both sides
+])
+# both outputs have row stride d + pad: pad 8 keeps the full forward's rows 16-byte aligned (the
+# pair kernel's stores); with pad 4 it takes the ring kernel too
+@pytest.mark.parametrize("pad", [8, 4])
+def test_attn_fwd_cached_equals_full(lengths, m, pad):
+    say(f"serving: cached attention {lengths} m={m} output pad {pad}")
     cfg = synth.make_config("train2_bf16", m=m)
     batch = custom_batch(cfg, lengths, seed=5)
     d, H = cfg.d, cfg.H
@@ -32,23 +42,23 @@ def test_attn_fwd_cached_equals_full(lengths, m):
     qkv = stored_to_device(st, DEV)
     es = 2
     sl = B.HostSlopes(*gpu_slopes(cfg))
-    o = torch.empty((T, d), dtype=torch.bfloat16, device=DEV)
+    o = torch.full((T, d + pad), 7.0, dtype=torch.bfloat16, device=DEV)
     lse = torch.empty((T, H), dtype=torch.float32, device=DEV)
     p = qkv.data_ptr()
     B.genrank_attn_fwd(bt, inp.hist_offsets, inp.hist_ts, inp.req_ts, sl, p, p + d * es, p + 2 * d * es, 3 * d,
-                       o, d, lse)
+                       o, d + pad, lse)
     # history K/V as a separate cache [T_h, 2d]; candidate q/k/v rows as their own buffer
     kv = qkv[:Th, d:].contiguous()
     qc = qkv[Th:].contiguous()
-    oc = torch.full((T - Th, d + 4), 7.0, dtype=torch.bfloat16, device=DEV)
+    oc = torch.full((T - Th, d + pad), 7.0, dtype=torch.bfloat16, device=DEV)
     lc = torch.empty((T - Th, H), dtype=torch.float32, device=DEV)
     c, k = qc.data_ptr(), kv.data_ptr()
     B.genrank_attn_fwd_cached(bt, inp.hist_offsets, inp.hist_ts, inp.req_ts, sl, c, c + d * es, c + 2 * d * es,
-                              3 * d, k, k + d * es, 2 * d, oc, d + 4, lc)
+                              3 * d, k, k + d * es, 2 * d, oc, d + pad, lc)
     torch.cuda.synchronize()
-    assert torch.equal(oc[:, :d], o[Th:]), "candidate outputs differ"
+    assert torch.equal(oc[:, :d], o[Th:, :d]), "candidate outputs differ"
     assert torch.equal(lc, lse[Th:]), "candidate log-sum-exp differs"
-    assert bool((oc[:, d:].float() == 7.0).all())
+    assert bool((oc[:, d:].float() == 7.0).all()) and bool((o[:, d:].float() == 7.0).all())
 
 
 def _model(cfg, batch):
@@ -60,6 +70,7 @@ def _model(cfg, batch):
 @pytest.mark.parametrize("name,lengths,m", [
     ("infer_1layer_bf16", [0, 1, 63, 64, 65, 480, 300], 130),
     ("stack4_bf16", [480, 123, 7, 0], 40),
+    ("stack4_bf16", [480, 480, 31], 256),
     ("train2_bf16", [64, 300, 480, 5], 32),
 ])
 def test_score_equals_forward(name, lengths, m):
