@@ -199,12 +199,14 @@ __global__ void __launch_bounds__(64) dkv_kernel(BwdArgs a) {
 //   Q, dO fragments in registers), dS^T = P^T (dP^T - D), dQ^T += K^T dS^T (K^T in LDS with
 //   its keys permuted to match the registers).  Candidate tiles also take the candidate's
 //   own key, which gives the candidate rows their whole dK and dV.
-// dK/dV kernel: one workgroup per 64-key history tile (4 waves x 16 keys, one key per lane):
-//   per query tile that sees the keys (every later history tile unless the loss sits at
-//   the candidates only, then every candidate tile) S = Q K^T and dP = dO V^T (Q, dO rows in
-//   LDS, K, V fragments in registers), dV^T += dO^T P and dK^T += Q^T dS (Q^T, dO^T in LDS
-//   with the queries permuted to match).
+// dK/dV kernel: one workgroup per 128-key history tile (4 waves x 32 keys, two 16-key blocks
+//   per wave that share every Q and dO fragment read): per 64-query tile that sees the keys
+//   (every later history tile unless the loss sits at the candidates only, then every
+//   candidate tile) S = Q K^T and dP = dO V^T (Q, dO rows in LDS, K, V fragments in
+//   registers), dV^T += dO^T P and dK^T += Q^T dS (Q^T, dO^T read transposed out of LDS).
 constexpr int TB = 64;      // rows per tile (queries or keys)
+constexpr int KW = 32;      // keys per wave in the dK/dV kernel (two 16-key blocks)
+constexpr int KT = 4 * KW;  // keys per dK/dV workgroup
 constexpr int DHB = 64;     // head dim
 constexpr int PLD = 72;     // LDS row pitch (bf16)
 constexpr int BWCH = 512;   // keys whose bias terms sit in LDS at a time
@@ -315,7 +317,7 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(BwdMArgs a) {
     n_tiles = (N + TB - 1) / TB;
   } else {
     is_cand = false;
-    q0 = (y - a.cand_tiles) * TB;
+    q0 = (a.hist_tiles - 1 - (y - a.cand_tiles)) * TB;  // the latest (longest) query tiles first
     if (q0 >= N) return;
     nq = min(TB, N - q0);
     qrow0 = off + q0;
@@ -560,10 +562,9 @@ __global__ void __launch_bounds__(256) attn_bwd_dkv_kernel(BwdMArgs a) {
 
   const int u = blockIdx.x / a.H;
   const int h = blockIdx.x - u * a.H;
-  const int kt = blockIdx.y;
   const int64_t off = a.offsets[u];
   const int N = a.offsets[u + 1] - a.offsets[u];
-  const int k0 = kt * TB;
+  const int k0 = blockIdx.y * KT;
   if (k0 >= N) return;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -571,23 +572,32 @@ __global__ void __launch_bounds__(256) attn_bwd_dkv_kernel(BwdMArgs a) {
   const int l16 = lane & 15, g4 = lane >> 4;
   const float sp2 = a.sp2[h], st2 = a.st2[h];
 
-  // this lane's key
-  const int j = k0 + wave * 16 + l16;
-  const bool key_valid = j < N;
-  const int64_t krow = off + min(j, N - 1);
-  const int64_t rk = krow * a.ld_qkv + h * DHB;
-  bf16x8_t kf[2], vf[2];
-  kf[0] = as_bf16x8(*reinterpret_cast<const uint4*>(a.k + rk + g4 * 8));
-  kf[1] = as_bf16x8(*reinterpret_cast<const uint4*>(a.k + rk + g4 * 8 + 32));
-  vf[0] = as_bf16x8(*reinterpret_cast<const uint4*>(a.v + rk + g4 * 8));
-  vf[1] = as_bf16x8(*reinterpret_cast<const uint4*>(a.v + rk + g4 * 8 + 32));
-  const int64_t ts_j = a.ts[krow];
+  // this lane's keys: kw0 + 16 kb + l16 (kb = 0, 1), kw0 the wave's first key; both blocks
+  // share every Q and dO fragment the wave reads
+  const int kw0 = k0 + wave * KW;
+  const bool wave_live = kw0 < N;
+  int j[2];
+  bool key_valid[2];
+  int64_t krow[2], ts_j[2];
+  bf16x8_t kf[2][2], vf[2][2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    j[kb] = kw0 + kb * 16 + l16;
+    key_valid[kb] = j[kb] < N;
+    krow[kb] = off + min(j[kb], N - 1);
+    const int64_t rk = krow[kb] * a.ld_qkv + h * DHB;
+    kf[kb][0] = as_bf16x8(*reinterpret_cast<const uint4*>(a.k + rk + g4 * 8));
+    kf[kb][1] = as_bf16x8(*reinterpret_cast<const uint4*>(a.k + rk + g4 * 8 + 32));
+    vf[kb][0] = as_bf16x8(*reinterpret_cast<const uint4*>(a.v + rk + g4 * 8));
+    vf[kb][1] = as_bf16x8(*reinterpret_cast<const uint4*>(a.v + rk + g4 * 8 + 32));
+    ts_j[kb] = a.ts[krow[kb]];
+  }
 
-  // query tiles that see these keys: history tiles kt .. (unless only candidates carry a
-  // gradient), then every candidate tile
+  // query tiles that see these keys: history tiles from the one holding key k0 (unless only
+  // candidates carry a gradient), then every candidate tile
   const int n_ht = (N + TB - 1) / TB;
   const int n_ct = (a.m + TB - 1) / TB;
-  const int h_first = a.cand_only ? n_ht : (FULL ? 0 : kt);
+  const int h_first = a.cand_only ? n_ht : (FULL ? 0 : k0 / TB);
   const int n_qt = (n_ht - h_first) + n_ct;
   struct QT { bool cand; int q0, nq; int64_t row0; };
   auto qtile = [&](int qi) {
@@ -653,17 +663,20 @@ __global__ void __launch_bounds__(256) attn_bwd_dkv_kernel(BwdMArgs a) {
       sTB[k] = b > INT32_MAX ? INT32_MAX : (b < INT32_MIN ? INT32_MIN : static_cast<int32_t>(b));
     }
 
-  f32x4_t accK[4], accV[4];
+  f32x4_t accK[2][4], accV[2][4];
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
-    accK[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    accV[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  }
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      accK[kb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      accV[kb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
   if (n_qt > 0) {
     fetch(qtile(0));
     stash(0);
   }
-  asm volatile("" : "+v"(kf[0]), "+v"(kf[1]), "+v"(vf[0]), "+v"(vf[1]));
+  asm volatile("" : "+v"(kf[0][0]), "+v"(kf[0][1]), "+v"(vf[0][0]), "+v"(vf[0][1]));
+  asm volatile("" : "+v"(kf[1][0]), "+v"(kf[1][1]), "+v"(vf[1][0]), "+v"(vf[1][1]));
   __syncthreads();
   if constexpr (TBK) {
     bucket_table_build(sLUT, sTB, a.tb_p2, tid, 256);
@@ -674,95 +687,128 @@ __global__ void __launch_bounds__(256) attn_bwd_dkv_kernel(BwdMArgs a) {
     const int buf = qi & 1;
     const QT t = qtile(qi);
     if (qi + 1 < n_qt) fetch(qtile(qi + 1));
-    // this tile's bias reference: its first query, or the candidates' (N, request time)
-    const int p_ref = t.cand ? N : t.q0;
-    const int64_t ts_ref = t.cand ? a.req[u] : a.ts[off + t.q0];
-    const int32_t tk = static_cast<int32_t>(ts_j - ts_ref);
-    const float w_j = TBK ? sp2 * static_cast<float>(j - p_ref)
-                          : sp2 * static_cast<float>(j - p_ref) + st2 * static_cast<float>(tk);
-    const bool far = CAN_FAR && __builtin_amdgcn_readfirstlane(sFar[buf]) != 0;
-    f32x4_t s[4], dp[4];
+    // a wave whose keys no query of this tile sees (past the history, or after the tile's
+    // last query) skips the products; it still stages and meets the barrier
+    const bool live = wave_live && (t.cand || FULL || kw0 <= t.q0 + t.nq - 1);
+    if (live) {
+      // this tile's bias reference: its first query, or the candidates' (N, request time)
+      const int p_ref = t.cand ? N : t.q0;
+      const int64_t ts_ref = t.cand ? a.req[u] : a.ts[off + t.q0];
+      int32_t tk[2];
+      float w_j[2];
 #pragma unroll
-    for (int qb = 0; qb < 4; ++qb) {
-      s[qb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      dp[qb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const bf16x8_t qf = as_bf16x8(*reinterpret_cast<const uint4*>(&sQ[buf][(qb * 16 + l16) * PLD + ks * 32 + g4 * 8]));
-        const bf16x8_t of = as_bf16x8(*reinterpret_cast<const uint4*>(&sO[buf][(qb * 16 + l16) * PLD + ks * 32 + g4 * 8]));
-        s[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf, kf[ks], s[qb], 0, 0, 0);
-        dp[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(of, vf[ks], dp[qb], 0, 0, 0);
+      for (int kb = 0; kb < 2; ++kb) {
+        tk[kb] = static_cast<int32_t>(ts_j[kb] - ts_ref);
+        w_j[kb] = TBK ? sp2 * static_cast<float>(j[kb] - p_ref)
+                      : sp2 * static_cast<float>(j[kb] - p_ref) + st2 * static_cast<float>(tk[kb]);
       }
-    }
-    // P and dS for queries qb*16 + 4*g4 + i of the tile and this lane's key
+      const bool far = CAN_FAR && __builtin_amdgcn_readfirstlane(sFar[buf]) != 0;
+      // two halves of 32 queries each (query blocks 2 hq, 2 hq + 1): the k axis of the dV and
+      // dK products
 #pragma unroll
-    for (int qb = 0; qb < 4; ++qb) {
-      const float4 c4 = reinterpret_cast<const float4*>(sC[buf])[qb * 4 + g4];
-      const float4 d4 = reinterpret_cast<const float4*>(sD[buf])[qb * 4 + g4];
-      const float cv[4] = {c4.x, c4.y, c4.z, c4.w};
-      const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
-      float lv[4] = {0.f, 0.f, 0.f, 0.f};
-      if constexpr (SPLIT_L) {
-        const float4 l4 = reinterpret_cast<const float4*>(sL[buf])[qb * 4 + g4];
-        lv[0] = l4.x; lv[1] = l4.y; lv[2] = l4.z; lv[3] = l4.w;
-      }
-      const int4 t4 = reinterpret_cast<const int4*>(sTq[buf])[qb * 4 + g4];
-      const int32_t tv[4] = {t4.x, t4.y, t4.z, t4.w};
+      for (int hq = 0; hq < 2; ++hq) {
+        f32x4_t s[2][2], dp[2][2];  // [key block][query block of the half]
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int ql = qb * 16 + g4 * 4 + i;
-        const int slot = t.cand ? N + t.q0 + ql : t.q0 + ql;
-        const bool ok = key_valid && ql < t.nq && (t.cand || FULL || j <= slot);
-        float arg;
-        if (CAN_FAR && far) {  // the exact bias of the pair, log2 units (sC holds the lse)
-          const float b = sp2 * static_cast<float>(j - slot) + st2 * static_cast<float>(tk - tv[i]);
-          arg = s[qb][i] * a.scale2 + (FULL ? -fabsf(b) : b) - cv[i];
-        } else if constexpr (!FULL && !TBK) {
-          arg = s[qb][i] * a.scale2 + w_j - cv[i];
-        } else {
-          // fully visible: -|w_j - w_i|; bucketed time: - s' bucket(|t_i - t_j|)
-          if constexpr (SPLIT_L) {
-            arg = s[qb][i] * a.scale2 - fabsf(w_j - cv[i]) - lv[i];
-          } else if constexpr (FULL) {  // and TBK: w_i = s (p_i - p_ref) = s ql on history tiles
-            const float w_i = t.cand ? 0.f : sp2 * static_cast<float>(ql);
-            arg = s[qb][i] * a.scale2 - fabsf(w_j - w_i) - cv[i];
-          } else {
-            arg = s[qb][i] * a.scale2 + w_j - cv[i];
+        for (int qq = 0; qq < 2; ++qq) {
+          const int qb = 2 * hq + qq;
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) {
+            s[kb][qq] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            dp[kb][qq] = f32x4_t{0.f, 0.f, 0.f, 0.f};
           }
-          if constexpr (TBK) arg -= st2 * static_cast<float>(bucket_lookup(sLUT, sTB, a.tb_p2, abs(tv[i] - tk)));
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            const bf16x8_t qf = as_bf16x8(*reinterpret_cast<const uint4*>(&sQ[buf][(qb * 16 + l16) * PLD + ks * 32 + g4 * 8]));
+            const bf16x8_t of = as_bf16x8(*reinterpret_cast<const uint4*>(&sO[buf][(qb * 16 + l16) * PLD + ks * 32 + g4 * 8]));
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+              s[kb][qq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf, kf[kb][ks], s[kb][qq], 0, 0, 0);
+              dp[kb][qq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(of, vf[kb][ks], dp[kb][qq], 0, 0, 0);
+            }
+          }
         }
-        const float p = ok ? __builtin_amdgcn_exp2f(arg) : 0.f;
-        s[qb][i] = p;
-        dp[qb][i] = p * (dp[qb][i] - dv[i]);
-      }
-    }
-    // dV^T += dO^T P,  dK^T += Q^T dS
+        // P and dS for queries qb*16 + 4*g4 + i of the tile and this lane's keys
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const bf16x8_t pf = pack_blocks(s[2 * ks], s[2 * ks + 1]);
-      const bf16x8_t dsf = pack_blocks(dp[2 * ks], dp[2 * ks + 1]);
+        for (int qq = 0; qq < 2; ++qq) {
+          const int qb = 2 * hq + qq;
+          const float4 c4 = reinterpret_cast<const float4*>(sC[buf])[qb * 4 + g4];
+          const float4 d4 = reinterpret_cast<const float4*>(sD[buf])[qb * 4 + g4];
+          const float cv[4] = {c4.x, c4.y, c4.z, c4.w};
+          const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
+          float lv[4] = {0.f, 0.f, 0.f, 0.f};
+          if constexpr (SPLIT_L) {
+            const float4 l4 = reinterpret_cast<const float4*>(sL[buf])[qb * 4 + g4];
+            lv[0] = l4.x; lv[1] = l4.y; lv[2] = l4.z; lv[3] = l4.w;
+          }
+          const int4 t4 = reinterpret_cast<const int4*>(sTq[buf])[qb * 4 + g4];
+          const int32_t tv[4] = {t4.x, t4.y, t4.z, t4.w};
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        const bf16x8_t otf = tr_operand(sO[buf], nb, ks, l16, g4);
-        const bf16x8_t qtf = tr_operand(sQ[buf], nb, ks, l16, g4);
-        accV[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(otf, pf, accV[nb], 0, 0, 0);
-        accK[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qtf, dsf, accK[nb], 0, 0, 0);
+          for (int i = 0; i < 4; ++i) {
+            const int ql = qb * 16 + g4 * 4 + i;
+            const int slot = t.cand ? N + t.q0 + ql : t.q0 + ql;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+              const bool ok = key_valid[kb] && ql < t.nq && (t.cand || FULL || j[kb] <= slot);
+              const float sv = s[kb][qq][i];
+              float arg;
+              if (CAN_FAR && far) {  // the exact bias of the pair, log2 units (sC holds the lse)
+                const float b = sp2 * static_cast<float>(j[kb] - slot) + st2 * static_cast<float>(tk[kb] - tv[i]);
+                arg = sv * a.scale2 + (FULL ? -fabsf(b) : b) - cv[i];
+              } else if constexpr (!FULL && !TBK) {
+                arg = sv * a.scale2 + w_j[kb] - cv[i];
+              } else {
+                // fully visible: -|w_j - w_i|; bucketed time: - s' bucket(|t_i - t_j|)
+                if constexpr (SPLIT_L) {
+                  arg = sv * a.scale2 - fabsf(w_j[kb] - cv[i]) - lv[i];
+                } else if constexpr (FULL) {  // and TBK: w_i = s (p_i - p_ref) = s ql on history tiles
+                  const float w_i = t.cand ? 0.f : sp2 * static_cast<float>(ql);
+                  arg = sv * a.scale2 - fabsf(w_j[kb] - w_i) - cv[i];
+                } else {
+                  arg = sv * a.scale2 + w_j[kb] - cv[i];
+                }
+                if constexpr (TBK) arg -= st2 * static_cast<float>(bucket_lookup(sLUT, sTB, a.tb_p2, abs(tv[i] - tk[kb])));
+              }
+              const float p = ok ? __builtin_amdgcn_exp2f(arg) : 0.f;
+              s[kb][qq][i] = p;
+              dp[kb][qq][i] = p * (dp[kb][qq][i] - dv[i]);
+            }
+          }
+        }
+        // dV^T += dO^T P,  dK^T += Q^T dS over this half's 32 queries
+        bf16x8_t pf[2], dsf[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          pf[kb] = pack_blocks(s[kb][0], s[kb][1]);
+          dsf[kb] = pack_blocks(dp[kb][0], dp[kb][1]);
+        }
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+          const bf16x8_t otf = tr_operand(sO[buf], nb, hq, l16, g4);
+          const bf16x8_t qtf = tr_operand(sQ[buf], nb, hq, l16, g4);
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) {
+            accV[kb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(otf, pf[kb], accV[kb][nb], 0, 0, 0);
+            accK[kb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qtf, dsf[kb], accK[kb][nb], 0, 0, 0);
+          }
+        }
       }
     }
     if (qi + 1 < n_qt) stash(buf ^ 1);
     __syncthreads();
   }
 
-  if (key_valid) {
-    const int64_t dro = krow * a.ld_d + h * DHB;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    if (!key_valid[kb]) continue;
+    const int64_t dro = krow[kb] * a.ld_d + h * DHB;
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
       uint2 o;
-      o.x = pack_bf16x2(accK[nb][0] * a.scale, accK[nb][1] * a.scale);
-      o.y = pack_bf16x2(accK[nb][2] * a.scale, accK[nb][3] * a.scale);
+      o.x = pack_bf16x2(accK[kb][nb][0] * a.scale, accK[kb][nb][1] * a.scale);
+      o.y = pack_bf16x2(accK[kb][nb][2] * a.scale, accK[kb][nb][3] * a.scale);
       *reinterpret_cast<uint2*>(a.dk + dro + nb * 16 + g4 * 4) = o;
-      o.x = pack_bf16x2(accV[nb][0], accV[nb][1]);
-      o.y = pack_bf16x2(accV[nb][2], accV[nb][3]);
+      o.x = pack_bf16x2(accV[kb][nb][0], accV[kb][nb][1]);
+      o.y = pack_bf16x2(accV[kb][nb][2], accV[kb][nb][3]);
       *reinterpret_cast<uint2*>(a.dv + dro + nb * 16 + g4 * 4) = o;
     }
   }
@@ -855,12 +901,13 @@ genrank_status launch_attn_bwd(const genrank_batch* b, const int32_t* offsets, c
       m.n_tb = alibi.n_time_bounds;
       m.tb_p2 = bucket_p2(m.n_tb);
     }
-    const dim3 gq(b->B * b->H, m.cand_tiles + m.hist_tiles), gk(b->B * b->H, m.hist_tiles);
+    const int key_tiles = (b->max_hist + KT - 1) / KT;
+    const dim3 gq(b->B * b->H, m.cand_tiles + m.hist_tiles), gk(b->B * b->H, key_tiles);
     const int var = ((alibi.flags & GENRANK_ATTN_FULL_HISTORY) ? BVAR_FULL : 0) |
                     ((alibi.flags & GENRANK_ATTN_TIME_BUCKET) ? BVAR_TBUCKET : 0);
     auto launch = [&](auto dq_kernel, auto dkv_kernel) {
       if (m.hist_tiles + m.cand_tiles > 0) hipLaunchKernelGGL(dq_kernel, gq, dim3(256), 0, stream, m);
-      if (m.hist_tiles > 0) hipLaunchKernelGGL(dkv_kernel, gk, dim3(256), 0, stream, m);
+      if (key_tiles > 0) hipLaunchKernelGGL(dkv_kernel, gk, dim3(256), 0, stream, m);
     };
     switch (var) {
       case 0: launch(attn_bwd_dq_kernel<0>, attn_bwd_dkv_kernel<0>); break;
