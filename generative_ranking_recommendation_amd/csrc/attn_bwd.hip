@@ -14,6 +14,7 @@
 #include <math.h>
 
 #include <mutex>
+#include <type_traits>
 
 #include "common.hpp"
 #include "internal.hpp"
@@ -92,28 +93,6 @@ __global__ void __launch_bounds__(64) delta_kernel(BwdArgs a) {
   if (lane < a.dh) v = to_f32(o[row * a.ld_o + h * a.dh + lane]) * to_f32(dO[row * a.ld_o + h * a.dh + lane]);
   v = wsum(v);
   if (lane == 0) a.delta[row * a.H + h] = v;
-}
-
-// bf16, dh = 64: D for 32 (row, head) pairs per 256-thread block, 8 lanes per pair, each
-// lane one 16-byte piece of O and of dO
-__global__ void __launch_bounds__(256) delta_bf16_kernel(BwdArgs a, int64_t pairs) {
-  const int64_t p = static_cast<int64_t>(blockIdx.x) * 32 + (threadIdx.x >> 3);
-  const int l8 = threadIdx.x & 7;
-  float v = 0.f;
-  if (p < pairs) {
-    const int64_t row = p / a.H;
-    const int h = static_cast<int>(p - row * a.H);
-    const int64_t off = row * a.ld_o + h * 64 + l8 * 8;
-    float fo[8], fd[8];
-    unpack8(*reinterpret_cast<const uint4*>(static_cast<const bf16_t*>(a.o) + off), fo);
-    unpack8(*reinterpret_cast<const uint4*>(static_cast<const bf16_t*>(a.dout) + off), fd);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v += fo[e] * fd[e];
-  }
-  v += __shfl_xor(v, 1);
-  v += __shfl_xor(v, 2);
-  v += __shfl_xor(v, 4);
-  if (p < pairs && l8 == 0) a.delta[p] = v;
 }
 
 template <typename T>
@@ -198,7 +177,8 @@ __global__ void __launch_bounds__(64) dkv_kernel(BwdArgs a) {
 //   lane as in the forward): per key tile S^T = K Q^T and dP^T = V dO^T (K, V rows in LDS,
 //   Q, dO fragments in registers), dS^T = P^T (dP^T - D), dQ^T += K^T dS^T (K^T in LDS with
 //   its keys permuted to match the registers).  Candidate tiles also take the candidate's
-//   own key, which gives the candidate rows their whole dK and dV.
+//   own key, which gives the candidate rows their whole dK and dV.  Its prologue forms
+//   D_i = dO_i . O_i of its queries and stores it for the dK/dV kernel.
 // dK/dV kernel: one workgroup per 128-key history tile (4 waves x 32 keys, two 16-key blocks
 //   per wave that share every Q and dO fragment read): per 64-query tile that sees the keys
 //   (every later history tile unless the loss sits at the candidates only, then every
@@ -218,9 +198,9 @@ struct BwdMArgs {
   const int64_t* ts;
   const int64_t* req;
   const bf16_t* q; const bf16_t* k; const bf16_t* v; int64_t ld_qkv;
-  const bf16_t* dout; int64_t ld_o;
+  const bf16_t* o; const bf16_t* dout; int64_t ld_o;
   const float* lse;
-  const float* delta;
+  float* delta;  // D per (row, head): written by the dQ kernel, read by the dK/dV kernel
   bf16_t* dq; bf16_t* dk; bf16_t* dv; int64_t ld_d;
   float sp2[GENRANK_MAX_HEADS];
   float st2[GENRANK_MAX_HEADS];
@@ -368,7 +348,12 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(BwdMArgs a) {
   bf16x8_t qf[2] = {as_bf16x8(qa), as_bf16x8(qb)};
   bf16x8_t dof[2] = {as_bf16x8(da), as_bf16x8(db)};
   const float lse2 = a.lse[qrow * a.H + h] * LOG2E_B;
-  const float Di = a.delta[qrow * a.H + h];
+  // D_i = dO_i . O_i over the head's 64 dimensions (16 per lane of the query's lane group);
+  // stored for the dK/dV kernel, which runs after this one
+  const uint4 oa = *reinterpret_cast<const uint4*>(a.o + rdo + g4 * 8);
+  const uint4 ob = *reinterpret_cast<const uint4*>(a.o + rdo + g4 * 8 + 32);
+  const float Di = bxor32_sum(bxor16_sum(dot16(da, db, oa, ob)));
+  if (q_valid && g4 == 0) a.delta[qrow * a.H + h] = Di;
   float w_i = 0.f;
   int32_t tq = 0;  // the query's time relative to ts_ref
   if (!is_cand) {
@@ -487,31 +472,53 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(BwdMArgs a) {
         dp[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, dof[ks], dp[kb], 0, 0, 0);
       }
     }
-    // P^T and dS^T for keys base + kb*16 + 4*g4 + i of this lane's query
+    // P^T and dS^T for keys base + kb*16 + 4*g4 + i of this lane's query.  F: the exact bias
+    // of each pair (rare).  MASK 0: no key limit, 1: the key limit, 2: the key limit on masked
+    // tiles, decided at run time (one instance for both).
+    auto pds = [&](auto FARC, auto MASKC) {
+      constexpr bool F = decltype(FARC)::value;
+      constexpr int MASK = decltype(MASKC)::value;
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      const float4 w = reinterpret_cast<const float4*>(sW)[((base - wbase) >> 2) + kb * 4 + g4];
-      const float wv[4] = {w.x, w.y, w.z, w.w};
-      const int4 t4 = reinterpret_cast<const int4*>(sT)[((base - wbase) >> 2) + kb * 4 + g4];
-      const int32_t tkv[4] = {t4.x, t4.y, t4.z, t4.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float arg;
-        if (CAN_FAR && far) {  // the exact bias of the pair, log2 units
-          const float b = sp2 * static_cast<float>(base + kb * 16 + g4 * 4 + i - q_slot) +
-                          st2 * static_cast<float>(tkv[i] - tq);
-          arg = s[kb][i] * a.scale2 + (FULL ? -fabsf(b) : b) - c_i;
-        } else if constexpr (!FULL && !TBK) {
-          arg = s[kb][i] * a.scale2 + wv[i] - c_i;
-        } else {
-          // fully visible: -|w_j - w_i|; bucketed time: - s' bucket(|t_i - t_j|)
-          arg = s[kb][i] * a.scale2 + (FULL ? -fabsf(wv[i] - w_i) : wv[i] - w_i) - lse2;
-          if constexpr (TBK) arg -= st2 * static_cast<float>(bucket_lookup(sLUT, sTB, a.tb_p2, abs(tq - tkv[i])));
+      for (int kb = 0; kb < 4; ++kb) {
+        const float4 w = reinterpret_cast<const float4*>(sW)[((base - wbase) >> 2) + kb * 4 + g4];
+        const float wv[4] = {w.x, w.y, w.z, w.w};
+        int32_t tkv[4] = {0, 0, 0, 0};
+        if constexpr (F || TBK) {
+          const int4 t4 = reinterpret_cast<const int4*>(sT)[((base - wbase) >> 2) + kb * 4 + g4];
+          tkv[0] = t4.x; tkv[1] = t4.y; tkv[2] = t4.z; tkv[3] = t4.w;
         }
-        float p = __builtin_amdgcn_exp2f(arg);
-        if (masked && base + kb * 16 + g4 * 4 + i > k_lim) p = 0.f;
-        s[kb][i] = p * (dp[kb][i] - Di);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float arg;
+          if constexpr (F) {  // the exact bias of the pair, log2 units
+            const float b = sp2 * static_cast<float>(base + kb * 16 + g4 * 4 + i - q_slot) +
+                            st2 * static_cast<float>(tkv[i] - tq);
+            arg = s[kb][i] * a.scale2 + (FULL ? -fabsf(b) : b) - c_i;
+          } else if constexpr (!FULL && !TBK) {
+            arg = __builtin_fmaf(s[kb][i], a.scale2, wv[i] - c_i);
+          } else {
+            // fully visible: -|w_j - w_i|; bucketed time: - s' bucket(|t_i - t_j|)
+            arg = s[kb][i] * a.scale2 + (FULL ? -fabsf(wv[i] - w_i) : wv[i] - w_i) - lse2;
+            if constexpr (TBK) arg -= st2 * static_cast<float>(bucket_lookup(sLUT, sTB, a.tb_p2, abs(tq - tkv[i])));
+          }
+          float p = __builtin_amdgcn_exp2f(arg);
+          if constexpr (MASK == 1) {
+            if (base + kb * 16 + g4 * 4 + i > k_lim) p = 0.f;
+          } else if constexpr (MASK == 2) {
+            if (masked && base + kb * 16 + g4 * 4 + i > k_lim) p = 0.f;
+          }
+          s[kb][i] = p * (dp[kb][i] - Di);
+        }
       }
+    };
+    using FT = std::integral_constant<bool, true>;
+    using FF = std::integral_constant<bool, false>;
+    if constexpr (CAN_FAR) {
+      if (far) pds(FT{}, std::integral_constant<int, 2>{});
+      else if (masked) pds(FF{}, std::integral_constant<int, 1>{});
+      else pds(FF{}, std::integral_constant<int, 0>{});
+    } else {  // the bucketed variants: one instance
+      pds(FF{}, std::integral_constant<int, 2>{});
     }
     // dQ^T += K^T dS^T
 #pragma unroll
@@ -640,8 +647,10 @@ __global__ void __launch_bounds__(256) attn_bwd_dkv_kernel(BwdMArgs a) {
       }
       const float lse2 = a.lse[r * a.H + h] * LOG2E_B;
       rfar = CAN_FAR && __builtin_amdgcn_ballot_w64(fabsf(w_i) > BIAS_FAR_LOG2) != 0;  // wave 0 alone
-      rc = rfar ? lse2 : (FULL ? (TBK ? lse2 : w_i) : w_i + lse2);
-      rl = lse2;
+      // rows past the tile's last query: +inf row terms, so every exponent of theirs is 0
+      const bool q_in = tid < t.nq;
+      rc = q_in ? (rfar ? lse2 : (FULL ? (TBK ? lse2 : w_i) : w_i + lse2)) : INFINITY;
+      rl = q_in ? lse2 : INFINITY;
       rt = tq;
       rd = a.delta[r * a.H + h];
     }
@@ -694,15 +703,19 @@ __global__ void __launch_bounds__(256) attn_bwd_dkv_kernel(BwdMArgs a) {
       // this tile's bias reference: its first query, or the candidates' (N, request time)
       const int p_ref = t.cand ? N : t.q0;
       const int64_t ts_ref = t.cand ? a.req[u] : a.ts[off + t.q0];
+      // key terms; keys past the history get -inf, so every exponent of theirs is 0
       int32_t tk[2];
-      float w_j[2];
+      float w_j[2], kneg[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         tk[kb] = static_cast<int32_t>(ts_j[kb] - ts_ref);
-        w_j[kb] = TBK ? sp2 * static_cast<float>(j[kb] - p_ref)
-                      : sp2 * static_cast<float>(j[kb] - p_ref) + st2 * static_cast<float>(tk[kb]);
+        kneg[kb] = key_valid[kb] ? 0.f : -INFINITY;
+        w_j[kb] = (TBK ? sp2 * static_cast<float>(j[kb] - p_ref)
+                       : sp2 * static_cast<float>(j[kb] - p_ref) + st2 * static_cast<float>(tk[kb])) + kneg[kb];
       }
       const bool far = CAN_FAR && __builtin_amdgcn_readfirstlane(sFar[buf]) != 0;
+      // a history tile on the diagonal (some key after some query) needs the causal test
+      const bool diag = !t.cand && !FULL && kw0 + KW - 1 > t.q0;
       // two halves of 32 queries each (query blocks 2 hq, 2 hq + 1): the k axis of the dV and
       // dK products
 #pragma unroll
@@ -727,52 +740,74 @@ __global__ void __launch_bounds__(256) attn_bwd_dkv_kernel(BwdMArgs a) {
             }
           }
         }
-        // P and dS for queries qb*16 + 4*g4 + i of the tile and this lane's keys
+        // P and dS for queries qb*16 + 4*g4 + i of the tile and this lane's keys.  F: the
+        // exact bias of each pair (rare).  MASK 0: no causal test, 1: the causal test, 2: the
+        // causal test on diagonal tiles, decided at run time (one instance for both).
+        auto pds = [&](auto FARC, auto MASKC) {
+          constexpr bool F = decltype(FARC)::value;
+          constexpr int MASK = decltype(MASKC)::value;
 #pragma unroll
-        for (int qq = 0; qq < 2; ++qq) {
-          const int qb = 2 * hq + qq;
-          const float4 c4 = reinterpret_cast<const float4*>(sC[buf])[qb * 4 + g4];
-          const float4 d4 = reinterpret_cast<const float4*>(sD[buf])[qb * 4 + g4];
-          const float cv[4] = {c4.x, c4.y, c4.z, c4.w};
-          const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
-          float lv[4] = {0.f, 0.f, 0.f, 0.f};
-          if constexpr (SPLIT_L) {
-            const float4 l4 = reinterpret_cast<const float4*>(sL[buf])[qb * 4 + g4];
-            lv[0] = l4.x; lv[1] = l4.y; lv[2] = l4.z; lv[3] = l4.w;
-          }
-          const int4 t4 = reinterpret_cast<const int4*>(sTq[buf])[qb * 4 + g4];
-          const int32_t tv[4] = {t4.x, t4.y, t4.z, t4.w};
+          for (int qq = 0; qq < 2; ++qq) {
+            const int qb = 2 * hq + qq;
+            const float4 c4 = reinterpret_cast<const float4*>(sC[buf])[qb * 4 + g4];
+            const float4 d4 = reinterpret_cast<const float4*>(sD[buf])[qb * 4 + g4];
+            const float cv[4] = {c4.x, c4.y, c4.z, c4.w};
+            const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
+            float lv[4] = {0.f, 0.f, 0.f, 0.f};
+            if constexpr (SPLIT_L) {
+              const float4 l4 = reinterpret_cast<const float4*>(sL[buf])[qb * 4 + g4];
+              lv[0] = l4.x; lv[1] = l4.y; lv[2] = l4.z; lv[3] = l4.w;
+            }
+            int32_t tv[4] = {0, 0, 0, 0};
+            if constexpr (F || TBK) {
+              const int4 t4 = reinterpret_cast<const int4*>(sTq[buf])[qb * 4 + g4];
+              tv[0] = t4.x; tv[1] = t4.y; tv[2] = t4.z; tv[3] = t4.w;
+            }
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int ql = qb * 16 + g4 * 4 + i;
-            const int slot = t.cand ? N + t.q0 + ql : t.q0 + ql;
+            for (int i = 0; i < 4; ++i) {
+              const int ql = qb * 16 + g4 * 4 + i;
+              const int slot = t.cand ? N + t.q0 + ql : t.q0 + ql;
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-              const bool ok = key_valid[kb] && ql < t.nq && (t.cand || FULL || j[kb] <= slot);
-              const float sv = s[kb][qq][i];
-              float arg;
-              if (CAN_FAR && far) {  // the exact bias of the pair, log2 units (sC holds the lse)
-                const float b = sp2 * static_cast<float>(j[kb] - slot) + st2 * static_cast<float>(tk[kb] - tv[i]);
-                arg = sv * a.scale2 + (FULL ? -fabsf(b) : b) - cv[i];
-              } else if constexpr (!FULL && !TBK) {
-                arg = sv * a.scale2 + w_j[kb] - cv[i];
-              } else {
-                // fully visible: -|w_j - w_i|; bucketed time: - s' bucket(|t_i - t_j|)
-                if constexpr (SPLIT_L) {
-                  arg = sv * a.scale2 - fabsf(w_j[kb] - cv[i]) - lv[i];
-                } else if constexpr (FULL) {  // and TBK: w_i = s (p_i - p_ref) = s ql on history tiles
-                  const float w_i = t.cand ? 0.f : sp2 * static_cast<float>(ql);
-                  arg = sv * a.scale2 - fabsf(w_j[kb] - w_i) - cv[i];
+              for (int kb = 0; kb < 2; ++kb) {
+                const float sv = s[kb][qq][i];
+                float arg;
+                if constexpr (F) {  // log2 units; sC holds the lse
+                  const float b = sp2 * static_cast<float>(j[kb] - slot) + st2 * static_cast<float>(tk[kb] - tv[i]);
+                  arg = sv * a.scale2 + (FULL ? -fabsf(b) : b) - cv[i] + kneg[kb];
+                } else if constexpr (!FULL && !TBK) {
+                  arg = __builtin_fmaf(sv, a.scale2, w_j[kb] - cv[i]);
                 } else {
-                  arg = sv * a.scale2 + w_j[kb] - cv[i];
+                  // fully visible: -|w_j - w_i|; bucketed time: - s' bucket(|t_i - t_j|)
+                  if constexpr (SPLIT_L) {
+                    arg = sv * a.scale2 - fabsf(w_j[kb] - cv[i]) - lv[i];
+                  } else if constexpr (FULL) {  // and TBK: w_i = s (p_i - p_ref) = s ql on history tiles
+                    const float w_i = t.cand ? 0.f : sp2 * static_cast<float>(ql);
+                    arg = sv * a.scale2 - fabsf(w_j[kb] - w_i) - cv[i];
+                  } else {
+                    arg = sv * a.scale2 + w_j[kb] - cv[i];
+                  }
+                  if constexpr (TBK) arg -= st2 * static_cast<float>(bucket_lookup(sLUT, sTB, a.tb_p2, abs(tv[i] - tk[kb])));
                 }
-                if constexpr (TBK) arg -= st2 * static_cast<float>(bucket_lookup(sLUT, sTB, a.tb_p2, abs(tv[i] - tk[kb])));
+                float p = __builtin_amdgcn_exp2f(arg);
+                if constexpr (MASK == 1) {
+                  if (j[kb] > slot) p = 0.f;
+                } else if constexpr (MASK == 2) {
+                  if (diag && j[kb] > slot) p = 0.f;
+                }
+                s[kb][qq][i] = p;
+                dp[kb][qq][i] = p * (dp[kb][qq][i] - dv[i]);
               }
-              const float p = ok ? __builtin_amdgcn_exp2f(arg) : 0.f;
-              s[kb][qq][i] = p;
-              dp[kb][qq][i] = p * (dp[kb][qq][i] - dv[i]);
             }
           }
+        };
+        using FT = std::integral_constant<bool, true>;
+        using FF = std::integral_constant<bool, false>;
+        if constexpr (CAN_FAR) {
+          if (far) pds(FT{}, std::integral_constant<int, 2>{});
+          else if (diag) pds(FF{}, std::integral_constant<int, 1>{});
+          else pds(FF{}, std::integral_constant<int, 0>{});
+        } else {  // the bucketed variants: one instance
+          pds(FF{}, std::integral_constant<int, 2>{});
         }
         // dV^T += dO^T P,  dK^T += Q^T dS over this half's 32 queries
         bf16x8_t pf[2], dsf[2];
@@ -875,14 +910,11 @@ genrank_status launch_attn_bwd(const genrank_batch* b, const int32_t* offsets, c
   a.n_tb = alibi.n_time_bounds;
   dim3 grid(static_cast<unsigned>(T), b->H);
   if (b->dtype == GENRANK_BF16) {  // dh == 64 and the alignments are checked by the caller
-    const int64_t pairs = T * b->H;
-    hipLaunchKernelGGL(delta_bf16_kernel, dim3(static_cast<unsigned>((pairs + 31) / 32)), dim3(256), 0, stream, a,
-                       pairs);
     BwdMArgs m{};
     m.offsets = offsets; m.ts = ts; m.req = req;
     m.q = static_cast<const bf16_t*>(q); m.k = static_cast<const bf16_t*>(k); m.v = static_cast<const bf16_t*>(v);
     m.ld_qkv = ld_qkv;
-    m.dout = static_cast<const bf16_t*>(dout); m.ld_o = ld_o;
+    m.o = static_cast<const bf16_t*>(o); m.dout = static_cast<const bf16_t*>(dout); m.ld_o = ld_o;
     m.lse = lse; m.delta = a.delta;
     m.dq = static_cast<bf16_t*>(dq); m.dk = static_cast<bf16_t*>(dk); m.dv = static_cast<bf16_t*>(dv);
     m.ld_d = ld_dqkv;
