@@ -624,12 +624,13 @@ __global__ void __launch_bounds__(256) attn_bwd_dkv_kernel(BwdMArgs a) {
   };
 
   // staging of a query tile: Q and dO rows pr, pr + 32 (clamped to the tile), columns
-  // 8ch..8ch+7; threads 0..63 also compute c_i and D_i of query tid
+  // 8ch..8ch+7; threads 0..63 also load the time, lse and D of query tid.  What depends on
+  // those loads (the row terms, the far test) is formed at the stash, a tile later, so no
+  // wave waits on its loads at the fetch.
   const int pr = tid >> 3, ch = tid & 7;
   uint4 rqa, rqb, roa, rob;
-  float rc = 0.f, rd = 0.f, rl = 0.f;
-  int32_t rt = 0;
-  bool rfar = false;
+  int64_t rtsq = 0, rts0 = 0;
+  float rlse = 0.f, rd = 0.f;
   auto fetch = [&](const QT& t) {
     const int64_t ra = t.row0 + min(pr, t.nq - 1), rb = t.row0 + min(pr + 32, t.nq - 1);
     rqa = *reinterpret_cast<const uint4*>(a.q + ra * a.ld_qkv + h * DHB + ch * 8);
@@ -639,30 +640,33 @@ __global__ void __launch_bounds__(256) attn_bwd_dkv_kernel(BwdMArgs a) {
     if (tid < TB) {
       const int ql = min(tid, t.nq - 1);
       const int64_t r = t.row0 + ql;
-      float w_i = 0.f;
-      int32_t tq = 0;
       if (!t.cand) {
-        tq = static_cast<int32_t>(a.ts[off + t.q0 + ql] - a.ts[off + t.q0]);
-        w_i = TBK ? sp2 * static_cast<float>(ql) : sp2 * static_cast<float>(ql) + st2 * static_cast<float>(tq);
+        rtsq = a.ts[off + t.q0 + ql];
+        rts0 = a.ts[off + t.q0];
       }
-      const float lse2 = a.lse[r * a.H + h] * LOG2E_B;
-      rfar = CAN_FAR && __builtin_amdgcn_ballot_w64(fabsf(w_i) > BIAS_FAR_LOG2) != 0;  // wave 0 alone
-      // rows past the tile's last query: +inf row terms, so every exponent of theirs is 0
-      const bool q_in = tid < t.nq;
-      rc = q_in ? (rfar ? lse2 : (FULL ? (TBK ? lse2 : w_i) : w_i + lse2)) : INFINITY;
-      rl = q_in ? lse2 : INFINITY;
-      rt = tq;
+      rlse = a.lse[r * a.H + h];
       rd = a.delta[r * a.H + h];
     }
   };
-  auto stash = [&](int buf) {
+  auto stash = [&](const QT& t, int buf) {
     stash_rows(sQ[buf], pr, ch, rqa, rqb);
     stash_rows(sO[buf], pr, ch, roa, rob);
     if (tid < TB) {
-      sC[buf][tid] = rc;
+      const int ql = min(tid, t.nq - 1);
+      float w_i = 0.f;
+      int32_t tq = 0;
+      if (!t.cand) {
+        tq = static_cast<int32_t>(rtsq - rts0);
+        w_i = TBK ? sp2 * static_cast<float>(ql) : sp2 * static_cast<float>(ql) + st2 * static_cast<float>(tq);
+      }
+      const float lse2 = rlse * LOG2E_B;
+      const bool rfar = CAN_FAR && __builtin_amdgcn_ballot_w64(fabsf(w_i) > BIAS_FAR_LOG2) != 0;  // wave 0 alone
+      // rows past the tile's last query: +inf row terms, so every exponent of theirs is 0
+      const bool q_in = tid < t.nq;
+      sC[buf][tid] = q_in ? (rfar ? lse2 : (FULL ? (TBK ? lse2 : w_i) : w_i + lse2)) : INFINITY;
       sD[buf][tid] = rd;
-      if constexpr (SPLIT_L) sL[buf][tid] = rl;
-      sTq[buf][tid] = rt;
+      if constexpr (SPLIT_L) sL[buf][tid] = q_in ? lse2 : INFINITY;
+      sTq[buf][tid] = tq;
       if (tid == 0) sFar[buf] = rfar ? 1 : 0;
     }
   };
@@ -681,8 +685,9 @@ __global__ void __launch_bounds__(256) attn_bwd_dkv_kernel(BwdMArgs a) {
       accV[kb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
   if (n_qt > 0) {
-    fetch(qtile(0));
-    stash(0);
+    const QT t0 = qtile(0);
+    fetch(t0);
+    stash(t0, 0);
   }
   asm volatile("" : "+v"(kf[0][0]), "+v"(kf[0][1]), "+v"(vf[0][0]), "+v"(vf[0][1]));
   asm volatile("" : "+v"(kf[1][0]), "+v"(kf[1][1]), "+v"(vf[1][0]), "+v"(vf[1][1]));
@@ -828,7 +833,7 @@ __global__ void __launch_bounds__(256) attn_bwd_dkv_kernel(BwdMArgs a) {
         }
       }
     }
-    if (qi + 1 < n_qt) stash(buf ^ 1);
+    if (qi + 1 < n_qt) stash(qtile(qi + 1), buf ^ 1);
     __syncthreads();
   }
 
