@@ -42,7 +42,7 @@ N_XCD, N_SIMD = 8, 256 * 4     # MI355X: 8 XCDs, 256 CUs of 4 SIMDs
 KERNEL_SOURCES = {"embed_sum": "embed.hip", "attn_fwd": "attn_fwd.hip", "qkv_gemm": "gemm.hip",
                   "out_gemm": "gemm.hip", "embed": "embed.hip", "norm": "rowops.hip", "qkv": "gemm.hip",
                   "attn": "attn_fwd.hip", "attn_cand": "attn_fwd.hip", "wo": "gemm.hip", "ffn_up": "gemm.hip",
-                  "ffn_down": "gemm.hip", "kv": "gemm.hip", "head": "rowops.hip"}
+                  "ffn_down": "gemm.hip", "kv": "gemm.hip", "head": "rowops.hip", "attn_bwd": "attn_bwd.hip"}
 
 
 # --attn-variant -> genrank_alibi.flags (1 = fully visible history, 2 = bucketed time term)
@@ -314,7 +314,7 @@ def bench_train(args, cfg):
     """One training step (forward with saved activations, BCE at candidate positions, full
     backward with table gradients) per step; candidates trained per second.  The roofline is
     reported for the attention backward, timed alone on the same batch geometry with
-    q, k, v, dO ~ N(0, 1) (two MFMA kernels plus the D pass)."""
+    q, k, v, dO ~ N(0, 1) (two MFMA kernels: dQ, which also forms D, then dK/dV)."""
     import numpy as np
     import torch
 
@@ -376,6 +376,23 @@ def bench_train(args, cfg):
         ev[k + 1].record(stream)
     torch.cuda.synchronize()
     t_us = float(np.mean([ev[k].elapsed_time(ev[k + 1]) for k in range(args.steps)])) * 1e3
+    if args.units_once:
+        # the attention backward once, alone on the device (its dQ and dK/dV dispatches), then
+        # the calibration copy
+        if args.calibrate_copy_mb > 0:
+            src = torch.ones(args.calibrate_copy_mb * (1 << 20) // 4, dtype=torch.float32, device=dev)
+            dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        bwd()
+        torch.cuda.synchronize()
+        with open(args.units_once, "w") as f:
+            json.dump({"workload": cfg.name, "units": [["attn_bwd", "attn_bwd", 2]],
+                       "copy_mib": args.calibrate_copy_mb}, f)
+        if args.calibrate_copy_mb > 0:
+            dst.copy_(src)
+            torch.cuda.synchronize()
+        log(f"units once: the attention backward; order in {args.units_once}")
+        return
     lengths = inp.lengths
     flops = W.attention_bwd_flops(lengths, m, d, full_history=bool(vflags & 1))
     flops_rc = W.attention_bwd_flops(lengths, m, d, recompute=True, full_history=bool(vflags & 1))
@@ -386,8 +403,9 @@ def bench_train(args, cfg):
         bound, achieved, peak, unit = "mfma", flops / (t_us * 1e-6) / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
     tf = flops / (t_us * 1e-6) / 1e12
     log(f"attention backward {t_us:.1f} us, {tf:.1f} TFLOP/s (recompute excluded)")
+    traffic = load_traffic(cfg.name).get("attn_bwd") if args.attn_variant == "causal" else None
     roofline = {"kernel": "attn_bwd", "bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
-                "frac": round(achieved / peak, 4), "traffic": None}
+                "frac": round(achieved / peak, 4), "traffic": traffic}
     cpu = None
     if args.cpu_seconds > 0:
         log("CPU oracle baseline ...")
@@ -902,7 +920,17 @@ def write_traffic(order_json, fetch_dir, write_dir, mfma_dir=None):
         return kernel.replace("genrank::(anonymous namespace)::", "").rsplit("(", 1)[0].replace("void ", "")
     with open(order_json) as f:
         order = json.load(f)
-    units = order["units"]
+    # [name, kind] or [name, kind, dispatches]: a unit of several dispatches sums their counters
+    counts = [u[2] if len(u) > 2 else 1 for u in order["units"]]
+    units = [u[:2] for u in order["units"]]
+    n_disp = sum(counts)
+
+    def group(ds):
+        out, i = [], 0
+        for c in counts:
+            out.append([" + ".join(dict.fromkeys(n for n, _ in ds[i:i + c])), sum(v for _, v in ds[i:i + c])])
+            i += c
+        return out
 
     def dispatches(d, counter=None):
         rows = {}
@@ -917,8 +945,7 @@ def write_traffic(order_json, fetch_dir, write_dir, mfma_dir=None):
         ds = dispatches(d)
         ci = max(i for i, (name, _) in enumerate(ds) if "copyBuffer" in name or "copy" in name.lower())
         copy_kib = ds[ci][1]
-        unit_ds = ds[ci - len(units):ci]
-        out[counter] = (copy_kib, unit_ds)
+        out[counter] = (copy_kib, group(ds[ci - n_disp:ci]))
     fetch_copy, fetch_units = out["FETCH_SIZE"]
     write_copy, write_units = out["WRITE_SIZE"]
     mib = order.get("copy_mib")
@@ -932,7 +959,7 @@ def write_traffic(order_json, fetch_dir, write_dir, mfma_dir=None):
         src = KERNEL_SOURCES.get(kind)
         if kind in rec or not src:
             continue
-        rec[kind] = {"unit": n, "kernel": short(kn), "source_sha": source_sha(src),
+        rec[kind] = {"unit": n, "kernel": " + ".join(short(x) for x in kn.split(" + ")), "source_sha": source_sha(src),
                      "fetch_bytes": int(fk * 1024 * fs), "write_bytes": int(wk * 1024 * wscale),
                      "fetch_kib_raw": int(fk), "write_kib_raw": int(wk)}
     if mfma_dir:
@@ -941,7 +968,7 @@ def write_traffic(order_json, fetch_dir, write_dir, mfma_dir=None):
         # launch's cycles once
         busy, gui = dispatches(mfma_dir, "SQ_VALU_MFMA_BUSY_CYCLES"), dispatches(mfma_dir, "GRBM_GUI_ACTIVE")
         ci = max(i for i, (name, _) in enumerate(busy) if "copy" in name.lower())
-        busy_u, gui_u = busy[ci - len(units):ci], gui[ci - len(units):ci]
+        busy_u, gui_u = group(busy[ci - n_disp:ci]), group(gui[ci - n_disp:ci])
         for (n, kind), (_, b), (_, g) in zip(units, busy_u, gui_u):
             if kind in rec and rec[kind]["unit"] == n and g > 0:
                 cycles = g / N_XCD
@@ -955,7 +982,7 @@ def write_traffic(order_json, fetch_dir, write_dir, mfma_dir=None):
     with open(path, "w") as f:
         json.dump(data, f, indent=1)
     for (n, kind), (kn, _) in zip(units, fetch_units):
-        print(f"{n:16s} {kind:10s} {short(kn)}")
+        print(f"{n:16s} {kind:10s} {' + '.join(short(x) for x in kn.split(' + '))}")
     for kind, r in rec.items():
         if kind != "calibration":
             print(f"{kind:10s} {r['unit']:14s} read {r['fetch_bytes'] / 1e6:9.1f} MB  write {r['write_bytes'] / 1e6:9.1f} MB")
