@@ -908,7 +908,7 @@ def bench_stack(args, cfg):
     print(json.dumps(out), flush=True)
 
 
-def write_traffic(order_json, fetch_dir, write_dir, mfma_dir=None):
+def write_traffic(order_json, fetch_dir, write_dir, mfma_dir=None, out_path=None):
     """profiles/traffic.json from two rocprofv3 counter runs (FETCH_SIZE, WRITE_SIZE) of
     `bench.py --units-once ... --calibrate-copy-mb N`: the dispatches that precede the
     calibration copy are the step's units in order; each counter is scaled by what it reads
@@ -952,7 +952,7 @@ def write_traffic(order_json, fetch_dir, write_dir, mfma_dir=None):
     moved_kib = float(mib) * 1024 if mib else None
     fs = moved_kib / fetch_copy if moved_kib else 1.0
     wscale = moved_kib / write_copy if moved_kib else 1.0
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+    path = out_path or os.path.join(ROOT, "profiles", "traffic.json")
     data = json.load(open(path)) if os.path.exists(path) else {}
     rec = {}
     for (n, kind), (kn, fk), (_, wk) in zip(units, fetch_units, write_units):
