@@ -179,13 +179,16 @@ __global__ void __launch_bounds__(64) dkv_kernel(BwdArgs a) {
 //   its keys permuted to match the registers).  Candidate tiles also take the candidate's
 //   own key, which gives the candidate rows their whole dK and dV.  Its prologue forms
 //   D_i = dO_i . O_i of its queries and stores it for the dK/dV kernel.
-// dK/dV kernel: one workgroup per 128-key history tile (4 waves x 32 keys, two 16-key blocks
-//   per wave that share every Q and dO fragment read): per 64-query tile that sees the keys
+// dK/dV kernel: one workgroup per 64-key history tile (4 waves x KW keys; with KW = 32 two
+//   16-key blocks per wave would share every Q and dO fragment read, but need 250 VGPRs, two
+//   waves per SIMD: 16 keys at 165 VGPRs and three waves per SIMD measured faster): per
+//   64-query tile that sees the keys
 //   (every later history tile unless the loss sits at the candidates only, then every
 //   candidate tile) S = Q K^T and dP = dO V^T (Q, dO rows in LDS, K, V fragments in
 //   registers), dV^T += dO^T P and dK^T += Q^T dS (Q^T, dO^T read transposed out of LDS).
 constexpr int TB = 64;      // rows per tile (queries or keys)
-constexpr int KW = 32;      // keys per wave in the dK/dV kernel (two 16-key blocks)
+constexpr int KW = 16;      // keys per wave in the dK/dV kernel
+constexpr int KB = KW / 16; // its 16-key blocks
 constexpr int KT = 4 * KW;  // keys per dK/dV workgroup
 constexpr int DHB = 64;     // head dim
 constexpr int PLD = 72;     // LDS row pitch (bf16)
@@ -579,16 +582,16 @@ __global__ void __launch_bounds__(256) attn_bwd_dkv_kernel(BwdMArgs a) {
   const int l16 = lane & 15, g4 = lane >> 4;
   const float sp2 = a.sp2[h], st2 = a.st2[h];
 
-  // this lane's keys: kw0 + 16 kb + l16 (kb = 0, 1), kw0 the wave's first key; both blocks
+  // this lane's keys: kw0 + 16 kb + l16 (kb < KB), kw0 the wave's first key; the blocks
   // share every Q and dO fragment the wave reads
   const int kw0 = k0 + wave * KW;
   const bool wave_live = kw0 < N;
-  int j[2];
-  bool key_valid[2];
-  int64_t krow[2], ts_j[2];
-  bf16x8_t kf[2][2], vf[2][2];
+  int j[KB];
+  bool key_valid[KB];
+  int64_t krow[KB], ts_j[KB];
+  bf16x8_t kf[KB][2], vf[KB][2];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
+  for (int kb = 0; kb < KB; ++kb) {
     j[kb] = kw0 + kb * 16 + l16;
     key_valid[kb] = j[kb] < N;
     krow[kb] = off + min(j[kb], N - 1);
@@ -676,9 +679,9 @@ __global__ void __launch_bounds__(256) attn_bwd_dkv_kernel(BwdMArgs a) {
       sTB[k] = b > INT32_MAX ? INT32_MAX : (b < INT32_MIN ? INT32_MIN : static_cast<int32_t>(b));
     }
 
-  f32x4_t accK[2][4], accV[2][4];
+  f32x4_t accK[KB][4], accV[KB][4];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
+  for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
       accK[kb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -689,8 +692,8 @@ __global__ void __launch_bounds__(256) attn_bwd_dkv_kernel(BwdMArgs a) {
     fetch(t0);
     stash(t0, 0);
   }
-  asm volatile("" : "+v"(kf[0][0]), "+v"(kf[0][1]), "+v"(vf[0][0]), "+v"(vf[0][1]));
-  asm volatile("" : "+v"(kf[1][0]), "+v"(kf[1][1]), "+v"(vf[1][0]), "+v"(vf[1][1]));
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) asm volatile("" : "+v"(kf[kb][0]), "+v"(kf[kb][1]), "+v"(vf[kb][0]), "+v"(vf[kb][1]));
   __syncthreads();
   if constexpr (TBK) {
     bucket_table_build(sLUT, sTB, a.tb_p2, tid, 256);
@@ -709,10 +712,10 @@ __global__ void __launch_bounds__(256) attn_bwd_dkv_kernel(BwdMArgs a) {
       const int p_ref = t.cand ? N : t.q0;
       const int64_t ts_ref = t.cand ? a.req[u] : a.ts[off + t.q0];
       // key terms; keys past the history get -inf, so every exponent of theirs is 0
-      int32_t tk[2];
-      float w_j[2], kneg[2];
+      int32_t tk[KB];
+      float w_j[KB], kneg[KB];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < KB; ++kb) {
         tk[kb] = static_cast<int32_t>(ts_j[kb] - ts_ref);
         kneg[kb] = key_valid[kb] ? 0.f : -INFINITY;
         w_j[kb] = (TBK ? sp2 * static_cast<float>(j[kb] - p_ref)
@@ -725,12 +728,12 @@ __global__ void __launch_bounds__(256) attn_bwd_dkv_kernel(BwdMArgs a) {
       // dK products
 #pragma unroll
       for (int hq = 0; hq < 2; ++hq) {
-        f32x4_t s[2][2], dp[2][2];  // [key block][query block of the half]
+        f32x4_t s[KB][2], dp[KB][2];  // [key block][query block of the half]
 #pragma unroll
         for (int qq = 0; qq < 2; ++qq) {
           const int qb = 2 * hq + qq;
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb) {
+          for (int kb = 0; kb < KB; ++kb) {
             s[kb][qq] = f32x4_t{0.f, 0.f, 0.f, 0.f};
             dp[kb][qq] = f32x4_t{0.f, 0.f, 0.f, 0.f};
           }
@@ -739,7 +742,7 @@ __global__ void __launch_bounds__(256) attn_bwd_dkv_kernel(BwdMArgs a) {
             const bf16x8_t qf = as_bf16x8(*reinterpret_cast<const uint4*>(&sQ[buf][(qb * 16 + l16) * PLD + ks * 32 + g4 * 8]));
             const bf16x8_t of = as_bf16x8(*reinterpret_cast<const uint4*>(&sO[buf][(qb * 16 + l16) * PLD + ks * 32 + g4 * 8]));
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
+            for (int kb = 0; kb < KB; ++kb) {
               s[kb][qq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf, kf[kb][ks], s[kb][qq], 0, 0, 0);
               dp[kb][qq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(of, vf[kb][ks], dp[kb][qq], 0, 0, 0);
             }
@@ -773,7 +776,7 @@ __global__ void __launch_bounds__(256) attn_bwd_dkv_kernel(BwdMArgs a) {
               const int ql = qb * 16 + g4 * 4 + i;
               const int slot = t.cand ? N + t.q0 + ql : t.q0 + ql;
 #pragma unroll
-              for (int kb = 0; kb < 2; ++kb) {
+              for (int kb = 0; kb < KB; ++kb) {
                 const float sv = s[kb][qq][i];
                 float arg;
                 if constexpr (F) {  // log2 units; sC holds the lse
@@ -815,9 +818,9 @@ __global__ void __launch_bounds__(256) attn_bwd_dkv_kernel(BwdMArgs a) {
           pds(FF{}, std::integral_constant<int, 2>{});
         }
         // dV^T += dO^T P,  dK^T += Q^T dS over this half's 32 queries
-        bf16x8_t pf[2], dsf[2];
+        bf16x8_t pf[KB], dsf[KB];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < KB; ++kb) {
           pf[kb] = pack_blocks(s[kb][0], s[kb][1]);
           dsf[kb] = pack_blocks(dp[kb][0], dp[kb][1]);
         }
@@ -826,7 +829,7 @@ __global__ void __launch_bounds__(256) attn_bwd_dkv_kernel(BwdMArgs a) {
           const bf16x8_t otf = tr_operand(sO[buf], nb, hq, l16, g4);
           const bf16x8_t qtf = tr_operand(sQ[buf], nb, hq, l16, g4);
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb) {
+          for (int kb = 0; kb < KB; ++kb) {
             accV[kb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(otf, pf[kb], accV[kb][nb], 0, 0, 0);
             accK[kb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qtf, dsf[kb], accK[kb][nb], 0, 0, 0);
           }
@@ -838,7 +841,7 @@ __global__ void __launch_bounds__(256) attn_bwd_dkv_kernel(BwdMArgs a) {
   }
 
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
+  for (int kb = 0; kb < KB; ++kb) {
     if (!key_valid[kb]) continue;
     const int64_t dro = krow[kb] * a.ld_d + h * DHB;
 #pragma unroll
