@@ -179,13 +179,13 @@ __global__ void __launch_bounds__(64) dkv_kernel(BwdArgs a) {
 //   its keys permuted to match the registers).  Candidate tiles also take the candidate's
 //   own key, which gives the candidate rows their whole dK and dV.  Its prologue forms
 //   D_i = dO_i . O_i of its queries and stores it for the dK/dV kernel.
-// dK/dV kernel: one workgroup per 64-key history tile (4 waves x KW keys; with KW = 32 two
-//   16-key blocks per wave would share every Q and dO fragment read, but need 250 VGPRs, two
-//   waves per SIMD: 16 keys at 165 VGPRs and three waves per SIMD measured faster): per
-//   64-query tile that sees the keys
-//   (every later history tile unless the loss sits at the candidates only, then every
-//   candidate tile) S = Q K^T and dP = dO V^T (Q, dO rows in LDS, K, V fragments in
-//   registers), dV^T += dO^T P and dK^T += Q^T dS (Q^T, dO^T read transposed out of LDS).
+// dK/dV kernel: one workgroup per KT = 4 KW history keys (4 waves x KW keys, KW = 16; with
+//   KW = 32 two 16-key blocks per wave would share every Q and dO fragment read, but need
+//   250 VGPRs, two waves per SIMD, and 16 keys at 165 VGPRs and three waves per SIMD
+//   measured faster): per 64-query tile that sees the keys (every later history tile unless
+//   the loss sits at the candidates only, then every candidate tile) S = Q K^T and
+//   dP = dO V^T (Q, dO rows in LDS, K, V fragments in registers), dV^T += dO^T P and
+//   dK^T += Q^T dS (Q^T, dO^T read transposed out of LDS).
 constexpr int TB = 64;      // rows per tile (queries or keys)
 constexpr int KW = 16;      // keys per wave in the dK/dV kernel
 constexpr int KB = KW / 16; // its 16-key blocks
