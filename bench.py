@@ -479,14 +479,15 @@ def bench_serve(args, cfg):
     y = torch.empty((Tc, d), dtype=torch.bfloat16, device=dev)
     qp, kp = qkv.data_ptr(), kv.data_ptr()
     names = ["embed_cand", "qkv_gemm", "attn_cached", "out_gemm"]
-    launches = [
-        lambda: B.genrank_embed_sum_cand(bt, inp.struct, model.tables.struct, xc, stream),
-        lambda: B.genrank_linear(B.BF16, xc, d, lay.wqkv, d, qkv, 3 * d, Tc, 3 * d, d, stream=stream),
+    launches_on = lambda st: [
+        lambda: B.genrank_embed_sum_cand(bt, inp.struct, model.tables.struct, xc, st),
+        lambda: B.genrank_linear(B.BF16, xc, d, lay.wqkv, d, qkv, 3 * d, Tc, 3 * d, d, stream=st),
         lambda: B.genrank_attn_fwd_cached(bt, inp.hist_offsets, inp.hist_ts, inp.req_ts, lay.slopes, qp,
                                           qp + 2 * d, qp + 4 * d, 3 * d, kp, kp + 2 * d, 2 * d, o, d, None,
-                                          stream),
-        lambda: B.genrank_linear(B.BF16, o, d, lay.wo, d, y, d, Tc, d, d, stream=stream),
+                                          st),
+        lambda: B.genrank_linear(B.BF16, o, d, lay.wo, d, y, d, Tc, d, d, stream=st),
     ]
+    launches = launches_on(stream)
 
     def step(ev=None, only=None):
         """Events after every launch (breakdown), or one pair around launch ``only``."""
@@ -524,9 +525,34 @@ def bench_serve(args, cfg):
     for k in range(args.steps):
         step(events[k], only=2)
     torch.cuda.synchronize()
-    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    ms_eager = (time.perf_counter() - t0) * 1e3 / args.steps
     per["attn_cached"] = float(np.mean([events[k][0].elapsed_time(events[k][1]) for k in range(args.steps)]))
-    log(f"{ms:.4f} ms/step; kernels (ms): " + ", ".join(f"{k}={v:.4f}" for k, v in per.items()))
+    log(f"{ms_eager:.4f} ms/step launched one call at a time; kernels (ms): " +
+        ", ".join(f"{k}={v:.4f}" for k, v in per.items()))
+    # the timed step: the four launches captured once in a HIP graph and replayed, so that
+    # the host enqueues one graph per request batch instead of four calls (the same kernels,
+    # arguments and buffers; a replay must reproduce the eager rows bit for bit)
+    y_eager = y.clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        cap = torch.cuda.current_stream()
+        for fn in launches_on(cap):
+            fn()
+    y.zero_()
+    graph.replay()
+    torch.cuda.synchronize()
+    graph_same = bool(torch.equal(y, y_eager))
+    if not graph_same:
+        log("WARNING: the graph replay differs from the eager step")
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    log(f"{ms:.4f} ms/step replayed as one graph (equal to the eager rows: {graph_same})")
     lengths = inp.lengths
     cand_pairs = int(m * (np.asarray(lengths, np.int64) + 1).sum())
     flops = 4 * d * cand_pairs
@@ -555,6 +581,9 @@ def bench_serve(args, cfg):
                    "history": f"U[{cfg.hist_min},{cfg.hist_max}]", "history_rows": T_h, "d": d, "heads": H,
                    "attn_variant": args.attn_variant},
         "prefill_ms": round(prefill_ms, 4),
+        "ms_per_step_eager": round(ms_eager, 5),
+        "step_launch": "HIP graph replay of the step's four launches",
+        "graph_equals_eager": graph_same,
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernels": kernels,

@@ -24,7 +24,12 @@
  *    call returns.  Scratch memory comes from a caller-supplied workspace whose size
  *    genrank_workspace_size() reports.
  *  - Streams.  Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
- *    is asynchronous; nothing synchronises except genrank_validate_host (host only).
+ *    is asynchronous; nothing synchronises except genrank_validate_host (host only) and
+ *    genrank_error_word (it waits for `stream` before reading the word).
+ *  - Graph capture.  The compute entry points only launch kernels on `stream`: none
+ *    allocates, synchronises or clears memory with a memset, so a caller may capture them
+ *    in a HIP graph (stream capture) and replay it; kernel arguments, including the
+ *    host-side ALiBi slopes, are taken at capture.  genrank_error_word cannot be captured.
  *  - Errors.  Host-side argument checks run before anything is enqueued; on error the
  *    call returns a negative genrank_status, enqueues nothing and leaves outputs
  *    untouched.  A failed kernel launch returns GENRANK_E_HIP.  Data-dependent

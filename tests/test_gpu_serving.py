@@ -104,3 +104,38 @@ def test_score_single_layer_against_oracle():
     x0 = oracle.embed_sum(oracle_tables(tables), batch.hist_items, batch.cand_items, idx)
     y, _, _ = oracle.model_fwd(x0, oracle_layers(weights), cfg.block, cfg.H, oracle_geom(cfg, batch, idx))
     bf16_close(to_numpy(x_c), y[batch.total_hist:], "candidate block output")
+
+
+@pytest.mark.parametrize("name,lengths,m", [
+    ("infer_1layer_bf16", [0, 1, 63, 64, 65, 480, 300], 130),
+    ("stack4_bf16", [480, 123, 7, 0], 40),
+])
+def test_score_graph_replay(name, lengths, m):
+    """Cached scoring captured once in a HIP graph (the entry points take the capturing
+    stream; none of them allocates, synchronises or clears memory with a memset): each of
+    several replays, with the program's own eager scoring and synchronisations between them,
+    reproduces the eager rows and logits bit for bit."""
+    say(f"serving: graph replay {name} {lengths} m={m}")
+    cfg = synth.make_config(name, m=m)
+    batch = custom_batch(cfg, lengths, seed=9)
+    model, inp = _model(cfg, batch)
+    caches = model.prefill(inp)
+    x_ref, logits_ref = model.score(inp, caches)  # eager; also sets up every lazily made buffer
+    torch.cuda.synchronize()
+    x_ref = x_ref.clone()
+    logits_ref = None if logits_ref is None else logits_ref.clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        x_g, logits_g = model.score(inp, caches)
+    for r in range(3):
+        x_g.fill_(float("nan"))
+        if logits_g is not None:
+            logits_g.fill_(float("nan"))
+        x_e, _ = model.score(inp, caches)  # eager work between the replays
+        torch.cuda.synchronize()
+        assert torch.equal(x_e, x_ref)
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(x_g, x_ref), f"replay {r}: rows differ"
+        if logits_ref is not None:
+            assert torch.equal(logits_g, logits_ref), f"replay {r}: logits differ"
