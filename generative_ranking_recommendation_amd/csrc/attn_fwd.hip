@@ -100,6 +100,18 @@ __device__ __forceinline__ float xor32_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
+
+// the largest of a lane's 16 scores (as a chain of three-way maxima)
+__device__ __forceinline__ float max16(const f32x4_t (&sc)[4]) {
+  float m = fmaxf(fmaxf(sc[0][0], sc[0][1]), sc[0][2]);
+  m = fmaxf(fmaxf(m, sc[0][3]), sc[1][0]);
+  m = fmaxf(fmaxf(m, sc[1][1]), sc[1][2]);
+  m = fmaxf(fmaxf(m, sc[1][3]), sc[2][0]);
+  m = fmaxf(fmaxf(m, sc[2][1]), sc[2][2]);
+  m = fmaxf(fmaxf(m, sc[2][3]), sc[3][0]);
+  m = fmaxf(fmaxf(m, sc[3][1]), sc[3][2]);
+  return fmaxf(m, sc[3][3]);
+}
 __device__ __forceinline__ float xor16_sum(float x) {
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
@@ -748,12 +760,12 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
         for (int i = 0; i < 4; ++i)
           if (kb * 16 + i > lim) s[kb][i] = -INFINITY;
     }
-    float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), s[0][2]), fmaxf(fmaxf(s[0][3], s[1][0]), s[1][1]));
-    mx = fmaxf(fmaxf(mx, s[1][2]), fmaxf(fmaxf(s[1][3], s[2][0]), s[2][1]));
-    mx = fmaxf(fmaxf(mx, s[2][2]), fmaxf(fmaxf(s[2][3], s[3][0]), s[3][1]));
-    mx = fmaxf(fmaxf(mx, s[3][2]), s[3][3]);
-    mx = xor32_max(xor16_max(mx));
+    float mx = max16(s);
+    // Some query's maximum exceeds its threshold exactly when some lane's share of it does,
+    // so the lane-local maximum decides, and the four lane groups of a query combine their
+    // shares only on the rare raise.
     if (__builtin_amdgcn_ballot_w64(mx > m_run + th) != 0) {  // rare: raise the maximum
+      mx = xor32_max(xor16_max(mx));
       const float m_new = fmaxf(m_run, mx);
       const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * SC);
       m_run = m_new;
@@ -968,7 +980,10 @@ __global__ void __launch_bounds__(PAIR_NT) attn_fwd_pair_kernel(AttnArgs a) {
   const float str = SEP ? st2 * a.rscale2 : st2;
 
   // ---- units: 32-query blocks, candidates first (each sees every key), then history
-  // blocks newest first; wave w takes units w, w + 8, ...
+  // blocks newest first, so in order of non-increasing key-tile count.  Wave w takes one
+  // unit per round, in snake order: w in even rounds, 7 - w in odd ones, which evens out
+  // the waves' key tiles (with 480 history rows and 256 candidates: 16 tiles each, where
+  // w, w + 8, ... gave 12 to 20).
   const int nu_c = (a.m + PQ - 1) / PQ;
   const int nu_h = a.hist_tiles > 0 ? (N + PQ - 1) / PQ : 0;
   const int n_units = nu_c + nu_h;
@@ -991,6 +1006,7 @@ __global__ void __launch_bounds__(PAIR_NT) attn_fwd_pair_kernel(AttnArgs a) {
       qn[hb][1] = *reinterpret_cast<const u32x4_t*>(qb + lo + 64);
     }
   };
+  auto unit_of = [&](int r) -> int { return r * PAIR_WAVES + ((r & 1) ? PAIR_WAVES - 1 - wave : wave); };
   // the first unit's query fragments travel with the K/V tiles
   if (wave < n_units) fetch_q(wave);
 
@@ -1062,7 +1078,7 @@ __global__ void __launch_bounds__(PAIR_NT) attn_fwd_pair_kernel(AttnArgs a) {
     return sKV + __builtin_amdgcn_readfirstlane(kt * STAGE);
   };
 
-  for (int k = wave; k < n_units; k += PAIR_WAVES) {
+  for (int r = 0, k = wave; k < n_units; k = unit_of(++r)) {
     const bool is_cand = k < nu_c;
     const int b = is_cand ? k : nu_h - 1 - (k - nu_c);
     const int qf0 = b * PQ;                               // first query of the unit
@@ -1089,7 +1105,7 @@ __global__ void __launch_bounds__(PAIR_NT) attn_fwd_pair_kernel(AttnArgs a) {
       tq[hb] = (!is_cand && N > 0) ? sT[min(q_slot[hb], N - 1)] : 0;
     }
     // the next unit's query fragments
-    if (k + PAIR_WAVES < n_units) fetch_q(k + PAIR_WAVES);
+    if (unit_of(r + 1) < n_units) fetch_q(unit_of(r + 1));
     // a candidate's own key and value (merged after the history keys)
     u32x4_t kself[2][2] = {};
     u32x2_t vself[2][4] = {};
@@ -1118,6 +1134,8 @@ __global__ void __launch_bounds__(PAIR_NT) attn_fwd_pair_kernel(AttnArgs a) {
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) accO[hb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     float m_run[2] = {-1e30f, -1e30f}, lsum[2] = {0.f, 0.f};
+    // the raise threshold and the exponent's offset follow the maximum (set where it moves)
+    float m_thr[2] = {-1e30f + th, -1e30f + th}, m_bias[2] = {1e30f * SC, 1e30f * SC};
     f32x4_t s[2][4];
     uint32_t ones = 0x3F803F80u;  // two bf16 ones, kept in a scalar register
     asm volatile("" : "+s"(ones));
@@ -1208,20 +1226,21 @@ __global__ void __launch_bounds__(PAIR_NT) attn_fwd_pair_kernel(AttnArgs a) {
               if (g4 * 4 + i > l16) sc[kb][i] = -INFINITY;
           }
       }
-      float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), sc[0][2]), fmaxf(fmaxf(sc[0][3], sc[1][0]), sc[1][1]));
-      mx = fmaxf(fmaxf(mx, sc[1][2]), fmaxf(fmaxf(sc[1][3], sc[2][0]), sc[2][1]));
-      mx = fmaxf(fmaxf(mx, sc[2][2]), fmaxf(fmaxf(sc[2][3], sc[3][0]), sc[3][1]));
-      mx = fmaxf(fmaxf(mx, sc[3][2]), sc[3][3]);
-      mx = xor32_max(xor16_max(mx));
-      if (__builtin_amdgcn_ballot_w64(mx > m_run[hb] + th) != 0) {
+      float mx = max16(sc);
+      // (the lane-local maximum decides, as in the ring kernel; a query's four lane groups
+      // combine their shares only on the rare raise)
+      if (__builtin_amdgcn_ballot_w64(mx > m_thr[hb]) != 0) {
+        mx = xor32_max(xor16_max(mx));
         const float m_new = fmaxf(m_run[hb], mx);
         const float alpha = __builtin_amdgcn_exp2f((m_run[hb] - m_new) * SC);
         m_run[hb] = m_new;
+        m_thr[hb] = m_new + th;
+        m_bias[hb] = -m_new * SC;
         lsum[hb] *= alpha;
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) accO[hb][nb] = accO[hb][nb] * alpha;
       }
-      const float mb = -m_run[hb] * SC;
+      const float mb = m_bias[hb];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         uint4 pk;
