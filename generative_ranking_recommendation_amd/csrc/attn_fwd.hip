@@ -875,7 +875,7 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
 // One workgroup per (user, head) pair, for batches whose longest history fits in LDS
 // (PAIR_MAXK keys).  The pair's whole K and V history goes into LDS once, in 64-key tiles
 // (direct loads with the ring kernel's swizzles; V^T operands through transposing reads),
-// together with every key's bias term.  The 8 waves then work through the pair's 32-query units
+// together with every key's bias term.  The 12 waves then work through the pair's 32-query units
 // (candidate units first, then history units newest first) with no further barrier:
 // each wave runs its units' key tiles from LDS on its own.  Against the tile grid this
 // loads every K/V byte of a pair once instead of once per query tile, and pays one
@@ -883,21 +883,27 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
 // heaviest first (see below), so the light pairs fill the end of the launch.
 // A unit is two 16-query blocks, A and B, that share every K and V fragment read (half
 // the LDS traffic per query of one block per wave).  Per key tile the wave issues both
-// blocks' score products, runs A's softmax while B's products finish, then B's softmax
-// while A's PV product runs, so one wave keeps the matrix cores and the vector ALUs busy
-// at once, and two waves per SIMD (256 registers each) fill the rest.  Each block's
+// blocks' score products, runs A's softmax while B's products finish, then B's, then the
+// PV products of each 32-key half right after that half's V^T fragments are read.  The
+// fragments of one half only are held, the next unit's queries and a candidate's own
+// key and value are fetched after the key tiles, so a wave fits 168 registers and three
+// waves share each SIMD (with two per SIMD at 256 registers: 553 us against 520 us per
+// launch of the four-layer batch; one 16-query block per wave, 16 waves: 535 us, as the
+// K/V fragment reads per query double).  Each block's
 // arithmetic is that of one 16-query wave of the ring kernel: the same bias terms, the
 // same lazy-rescaling decisions over its 16 queries, the same row-sum order, so candidate
 // rows come out of both kernels bit for bit alike.
 // The bias reference point of the whole pair is the candidates' shared (p, tau) = (N,
 // request time), so candidate rows carry no row term.  A candidate's own key is merged
 // into its softmax state after the history keys (same result as seeding with it).
-constexpr int PAIR_WAVES = 8;
+constexpr int PAIR_WAVES = 12;
 constexpr int PAIR_NT = 64 * PAIR_WAVES;
 constexpr int PAIR_MAXT = 9;                 // key tiles held in LDS
 constexpr int PAIR_MAXK = PAIR_MAXT * AK;    // longest history this kernel takes
-constexpr int PQ = 2 * QW;                   // queries per unit (two 16-query blocks)
-static_assert(PAIR_WAVES * 8 == AK, "each wave loads 8 rows of every K and V tile");
+constexpr int PB = 2;                        // 16-query blocks per unit
+constexpr int PQ = PB * QW;                  // queries per unit
+constexpr int PAIR_RG = 2 * AK / 8;          // 8-row groups of a K tile and its V tile
+static_assert(PAIR_WAVES <= PAIR_RG && 2 * PAIR_WAVES >= PAIR_RG, "each wave loads one or two row groups");
 
 template <int VAR>
 __global__ void __launch_bounds__(PAIR_NT) attn_fwd_pair_kernel(AttnArgs a) {
@@ -979,11 +985,10 @@ __global__ void __launch_bounds__(PAIR_NT) attn_fwd_pair_kernel(AttnArgs a) {
   const float spr = SEP ? sp2 * a.rscale2 : sp2;
   const float str = SEP ? st2 * a.rscale2 : st2;
 
-  // ---- units: 32-query blocks, candidates first (each sees every key), then history
+  // ---- units: PQ-query blocks, candidates first (each sees every key), then history
   // blocks newest first, so in order of non-increasing key-tile count.  Wave w takes one
-  // unit per round, in snake order: w in even rounds, 7 - w in odd ones, which evens out
-  // the waves' key tiles (with 480 history rows and 256 candidates: 16 tiles each, where
-  // w, w + 8, ... gave 12 to 20).
+  // unit per round, in snake order: w in even rounds, PAIR_WAVES - 1 - w in odd ones, which
+  // evens out the waves' key tiles.
   const int nu_c = (a.m + PQ - 1) / PQ;
   const int nu_h = a.hist_tiles > 0 ? (N + PQ - 1) / PQ : 0;
   const int n_units = nu_c + nu_h;
@@ -995,12 +1000,12 @@ __global__ void __launch_bounds__(PAIR_NT) attn_fwd_pair_kernel(AttnArgs a) {
   };
   auto unit_nq = [&](int k) -> int { return min(PQ, k < nu_c ? a.m - k * PQ : N - (nu_h - 1 - (k - nu_c)) * PQ); };
   const uint32_t ldq = static_cast<uint32_t>(a.ld_qkv);
-  u32x4_t qn[2][2] = {};
+  u32x4_t qn[PB][2] = {};
   auto fetch_q = [&](int k) __attribute__((always_inline)) {
     const char* qb = reinterpret_cast<const char*>(a.q + unit_row0(k) * a.ld_qkv + h * DH);
     const int nq = unit_nq(k);
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {  // rows past the unit's last query re-read it
+    for (int hb = 0; hb < PB; ++hb) {  // rows past the unit's last query re-read it
       const uint32_t lo = (static_cast<uint32_t>(min(hb * QW + l16, nq - 1)) * ldq + g4 * 8) * 2u;
       qn[hb][0] = *reinterpret_cast<const u32x4_t*>(qb + lo);
       qn[hb][1] = *reinterpret_cast<const u32x4_t*>(qb + lo + 64);
@@ -1010,23 +1015,25 @@ __global__ void __launch_bounds__(PAIR_NT) attn_fwd_pair_kernel(AttnArgs a) {
   // the first unit's query fragments travel with the K/V tiles
   if (wave < n_units) fetch_q(wave);
 
-  // ---- the pair's K/V tiles, row-major (key, dim), straight into LDS: wave w loads rows
-  // 8 w .. 8 w + 7 of every K and V tile (lane l: row 8 w + l / 8, LDS chunk l % 8 <- global
-  // chunk (l % 8) ^ ((row >> 1) & 7) for K, (l % 8) ^ 2 ((row >> 1) & 3) for V).  Rows past
-  // the history end re-read its last row.
-  const int lr = wave * 8 + (lane >> 3);
+  // ---- the pair's K/V tiles, row-major (key, dim), straight into LDS, in 8-row groups:
+  // groups 0-7 are rows 8 g .. 8 g + 7 of every K tile, groups 8-15 the same rows of every V
+  // tile; wave w loads groups w and w + PAIR_WAVES (lane l: row 8 (g % 8) + l / 8, LDS chunk
+  // l % 8 <- global chunk (l % 8) ^ ((row >> 1) & 7) for K, (l % 8) ^ 2 ((row >> 1) & 3) for
+  // V).  Rows past the history end re-read its last row.
   const int lc = lane & 7;
-  {
+  for (int rg = wave; rg < PAIR_RG; rg += PAIR_WAVES) {
+    const int kv_half = rg >> 3;  // 0: K, 1: V (wave-uniform)
+    const int lr = (rg & 7) * 8 + (lane >> 3);
     const uint32_t row_bytes = static_cast<uint32_t>(a.ld_h) * 2u;
-    const char* gk = reinterpret_cast<const char*>(a.kh + off * a.ld_h + h * DH + ((lc ^ ((lr >> 1) & 7)) * 8));
-    const char* gv = reinterpret_cast<const char*>(a.vh + off * a.ld_h + h * DH + ((lc ^ (2 * ((lr >> 1) & 3))) * 8));
+    const char* g = kv_half == 0
+                        ? reinterpret_cast<const char*>(a.kh + off * a.ld_h + h * DH + ((lc ^ ((lr >> 1) & 7)) * 8))
+                        : reinterpret_cast<const char*>(a.vh + off * a.ld_h + h * DH + ((lc ^ (2 * ((lr >> 1) & 3))) * 8));
+    bf16_t* dst = sKV + kv_half * AK * DH + (rg & 7) * 8 * DH;
 #pragma unroll
     for (int t = 0; t < PAIR_MAXT; ++t) {
       if (t < n_tiles) {
         const uint32_t ro = static_cast<uint32_t>(min(t * AK + lr, N - 1)) * row_bytes;
-        __builtin_amdgcn_global_load_lds((glb_void_t*)(gk + ro), (lds_void_t*)(sKV + t * STAGE + wave * 8 * DH), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((glb_void_t*)(gv + ro), (lds_void_t*)(sKV + t * STAGE + AK * DH + wave * 8 * DH),
-                                         16, 0, 0);
+        __builtin_amdgcn_global_load_lds((glb_void_t*)(g + ro), (lds_void_t*)(dst + t * STAGE), 16, 0, 0);
       }
     }
   }
@@ -1084,18 +1091,18 @@ __global__ void __launch_bounds__(PAIR_NT) attn_fwd_pair_kernel(AttnArgs a) {
     const int qf0 = b * PQ;                               // first query of the unit
     const int nq = min(PQ, (is_cand ? a.m : N) - qf0);
     const int n_t = (is_cand || FULL) ? n_tiles : (qf0 + nq - 1) / AK + 1;
-    // causal history units: the 16-key block of the first (newest) tile that holds block
-    // A's diagonal; block B's is the next one (query blocks are 16-aligned, the unit's
-    // 32 queries lie in one tile)
+    // causal history units: the 16-key block of the first (newest) tile that holds the
+    // unit's (first) block's diagonal; a second block's would be the next one (query blocks
+    // are 16-aligned, a unit's queries lie in one tile)
     const int kd0 = (qf0 - (n_t - 1) * AK) >> 4;
     const int64_t row0 = unit_row0(k);
-    bf16x8_t qf[2][2];
-    bool q_valid[2];
-    int q_slot[2];
-    int32_t tq[2];
-    float w_i_ref[2];
+    bf16x8_t qf[PB][2];
+    bool q_valid[PB];
+    int q_slot[PB];
+    int32_t tq[PB];
+    float w_i_ref[PB];
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
+    for (int hb = 0; hb < PB; ++hb) {
       qf[hb][0] = __builtin_bit_cast(bf16x8_t, qn[hb][0]);
       qf[hb][1] = __builtin_bit_cast(bf16x8_t, qn[hb][1]);
       q_valid[hb] = hb * QW + l16 < nq;
@@ -1104,39 +1111,35 @@ __global__ void __launch_bounds__(PAIR_NT) attn_fwd_pair_kernel(AttnArgs a) {
       w_i_ref[hb] = (!is_cand && q_valid[hb]) ? sW[min(q_slot[hb], N - 1)] * SC : 0.f;
       tq[hb] = (!is_cand && N > 0) ? sT[min(q_slot[hb], N - 1)] : 0;
     }
-    // the next unit's query fragments
-    if (unit_of(r + 1) < n_units) fetch_q(unit_of(r + 1));
-    // a candidate's own key and value (merged after the history keys)
-    u32x4_t kself[2][2] = {};
-    u32x2_t vself[2][4] = {};
-    if (is_cand) {
-      const char* kb0 = reinterpret_cast<const char*>(a.k + row0 * a.ld_qkv + h * DH);
-      const char* vb0 = reinterpret_cast<const char*>(a.v + row0 * a.ld_qkv + h * DH);
-#pragma unroll
-      for (int hb = 0; hb < 2; ++hb) {
-        const uint32_t lo = static_cast<uint32_t>(min(hb * QW + l16, nq - 1)) * ldq * 2u;
-        kself[hb][0] = *reinterpret_cast<const u32x4_t*>(kb0 + lo + g4 * 16);
-        kself[hb][1] = *reinterpret_cast<const u32x4_t*>(kb0 + lo + g4 * 16 + 64);
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) vself[hb][nb] = *reinterpret_cast<const u32x2_t*>(vb0 + lo + nb * 32 + g4 * 8);
-      }
-    }
     // a history unit far from the candidates' reference point forms each bias exactly
     // from the pair's own position and time differences (the row terms are then 0)
-    const bool far = CAN_FAR && __builtin_amdgcn_ballot_w64(fabsf(w_i_ref[0]) > BIAS_FAR_LOG2 ||
-                                                            fabsf(w_i_ref[1]) > BIAS_FAR_LOG2) != 0;
-    const float w_i[2] = {far ? 0.f : w_i_ref[0], far ? 0.f : w_i_ref[1]};
-    const float w_i_u[2] = {w_i_ref[0] / SC, w_i_ref[1] / SC};
-
-    f32x4_t accO[2][4];
+    bool far_lane = false;
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb)
+    for (int hb = 0; hb < PB; ++hb) far_lane = far_lane || fabsf(w_i_ref[hb]) > BIAS_FAR_LOG2;
+    const bool far = CAN_FAR && __builtin_amdgcn_ballot_w64(far_lane) != 0;
+    float w_i[PB], w_i_u[PB];
+#pragma unroll
+    for (int hb = 0; hb < PB; ++hb) {
+      w_i[hb] = far ? 0.f : w_i_ref[hb];
+      w_i_u[hb] = w_i_ref[hb] / SC;
+    }
+
+    f32x4_t accO[PB][4];
+#pragma unroll
+    for (int hb = 0; hb < PB; ++hb)
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) accO[hb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float m_run[2] = {-1e30f, -1e30f}, lsum[2] = {0.f, 0.f};
+    float m_run[PB], lsum[PB];
     // the raise threshold and the exponent's offset follow the maximum (set where it moves)
-    float m_thr[2] = {-1e30f + th, -1e30f + th}, m_bias[2] = {1e30f * SC, 1e30f * SC};
-    f32x4_t s[2][4];
+    float m_thr[PB], m_bias[PB];
+#pragma unroll
+    for (int hb = 0; hb < PB; ++hb) {
+      m_run[hb] = -1e30f;
+      lsum[hb] = 0.f;
+      m_thr[hb] = -1e30f + th;
+      m_bias[hb] = 1e30f * SC;
+    }
+    f32x4_t s[PB][4];
     uint32_t ones = 0x3F803F80u;  // two bf16 ones, kept in a scalar register
     asm volatile("" : "+s"(ones));
 
@@ -1158,34 +1161,37 @@ __global__ void __launch_bounds__(PAIR_NT) attn_fwd_pair_kernel(AttnArgs a) {
           const int4 t4 = reinterpret_cast<const int4*>(sT)[(base >> 2) + kb * 4 + g4];
           const int j0 = base + kb * 16 + g4 * 4;
 #pragma unroll
-          for (int hb = 0; hb < 2; ++hb)
+          for (int hb = 0; hb < PB; ++hb)
             s[hb][kb] = f32x4_t{exact_bias(hb, j0, t4.x), exact_bias(hb, j0 + 1, t4.y),
                                 exact_bias(hb, j0 + 2, t4.z), exact_bias(hb, j0 + 3, t4.w)};
         } else if constexpr (SEP) {
           const float4 w = reinterpret_cast<const float4*>(sW)[(base >> 2) + kb * 4 + g4];
           s[0][kb] = f32x4_t{w.x, w.y, w.z, w.w};
-          s[1][kb] = s[0][kb];
+          if constexpr (PB == 2) s[PB - 1][kb] = s[0][kb];
         } else {
           s[0][kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-          s[1][kb] = s[0][kb];
+          if constexpr (PB == 2) s[PB - 1][kb] = s[0][kb];
         }
-        if (MASKED && kb > kd0) {  // block A lies wholly above its diagonal here
+        if (MASKED && kb > kd0) {  // the first block lies wholly above its diagonal here
           s[0][kb] = f32x4_t{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-          if (kb > kd0 + 1) {
-            s[1][kb] = s[0][kb];
+          if (PB == 1 || kb > kd0 + 1) {
+            if constexpr (PB == 2) s[PB - 1][kb] = s[0][kb];
             continue;
           }
         }
         const bf16x8_t k0 = as_bf16x8(*reinterpret_cast<const uint4*>(stg + kb * 16 * DH + k_off0));
         const bf16x8_t k1 = as_bf16x8(*reinterpret_cast<const uint4*>(stg + kb * 16 * DH + k_off1));
-        if (!MASKED || kb <= kd0) {
+        if constexpr (PB == 1) {
           s[0][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[0][0], s[0][kb], 0, 0, 0);
-          s[1][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[1][0], s[1][kb], 0, 0, 0);
           s[0][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[0][1], s[0][kb], 0, 0, 0);
-          s[1][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[1][1], s[1][kb], 0, 0, 0);
+        } else if (!MASKED || kb <= kd0) {
+          s[0][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[0][0], s[0][kb], 0, 0, 0);
+          s[PB - 1][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[PB - 1][0], s[PB - 1][kb], 0, 0, 0);
+          s[0][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[0][1], s[0][kb], 0, 0, 0);
+          s[PB - 1][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[PB - 1][1], s[PB - 1][kb], 0, 0, 0);
         } else {
-          s[1][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[1][0], s[1][kb], 0, 0, 0);
-          s[1][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[1][1], s[1][kb], 0, 0, 0);
+          s[PB - 1][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[PB - 1][0], s[PB - 1][kb], 0, 0, 0);
+          s[PB - 1][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[PB - 1][1], s[PB - 1][kb], 0, 0, 0);
         }
       }
     };
@@ -1257,47 +1263,43 @@ __global__ void __launch_bounds__(PAIR_NT) attn_fwd_pair_kernel(AttnArgs a) {
         pf[ks] = as_bf16x8(pk);
       }
     };
-    // V^T fragments of key tile kt (shared by both blocks)
-    bf16x8_t vf[2][4];
-    auto read_v = [&](auto masked_tag, int kt) __attribute__((always_inline)) {
+    // O^T += V^T P^T for every block, the V^T fragments of each 32-key half read right
+    // before its products (16 registers of fragments held instead of 32)
+    auto pv_direct = [&](auto masked_tag, int kt, const bf16x8_t(&pa)[2], const bf16x8_t(&pb)[2]) __attribute__((always_inline)) {
       constexpr bool MASKED = decltype(masked_tag)::value;
       const bf16_t* stg = tile_at(kt);
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        if (MASKED && 2 * ks > kd0 + 1) continue;  // past both blocks' diagonals
+        if (MASKED && 2 * ks > kd0 + PB - 1) continue;  // past every block's diagonal
+        bf16x8_t vh[4];
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
-        {
+        for (int nb = 0; nb < 4; ++nb) {
           const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(stg + v_off[nb] + (ks * 32) * DH));
           const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(stg + v_off[nb] + (ks * 32 + 16) * DH));
           const v4i16_t both[2] = {lo, hi};
-          vf[ks][nb] = __builtin_bit_cast(bf16x8_t, both);
+          vh[nb] = __builtin_bit_cast(bf16x8_t, both);
+        }
+        if (!(MASKED && 2 * ks > kd0)) {  // (the first block's diagonal)
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb)
+            accO[0][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vh[nb], pa[ks], accO[0][nb], 0, 0, 0);
+        }
+        if constexpr (PB == 2) {
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb)
+            accO[PB - 1][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vh[nb], pb[ks], accO[PB - 1][nb], 0, 0, 0);
         }
       }
     };
-    // O^T += V^T P^T for block hb
-    auto pv = [&](auto masked_tag, int kt, auto hb_tag, const bf16x8_t(&pf)[2]) __attribute__((always_inline)) {
-      constexpr bool MASKED = decltype(masked_tag)::value;
-      constexpr int hb = decltype(hb_tag)::value;
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        if (MASKED && 2 * ks > kd0 + hb) continue;  // past this block's diagonal
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
-          accO[hb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[ks][nb], pf[ks], accO[hb][nb], 0, 0, 0);
-      }
-    };
-    // one key tile: both blocks' scores, A's softmax, A's PV while B's softmax runs, B's PV
+    // one key tile: the blocks' scores, their softmaxes, then the PV products
     auto tile = [&](auto masked_tag, auto far_tag, int kt) __attribute__((always_inline)) {
       using HA = std::integral_constant<int, 0>;
-      using HB = std::integral_constant<int, 1>;
+      using HB = std::integral_constant<int, PB - 1>;
       bf16x8_t pa[2], pb[2];
       scores(masked_tag, far_tag, kt);
       softmax(masked_tag, far_tag, kt, HA{}, pa);
-      read_v(masked_tag, kt);
-      pv(masked_tag, kt, HA{}, pa);
-      softmax(masked_tag, far_tag, kt, HB{}, pb);
-      pv(masked_tag, kt, HB{}, pb);
+      if constexpr (PB == 2) softmax(masked_tag, far_tag, kt, HB{}, pb);
+      pv_direct(masked_tag, kt, pa, pb);
     };
     // Key tiles newest first; only the first can cross a causal query's limit.  A
     // candidate's limit is the history end, which the -inf bias terms already enforce, and
@@ -1321,12 +1323,28 @@ __global__ void __launch_bounds__(PAIR_NT) attn_fwd_pair_kernel(AttnArgs a) {
       }
     }
 
-    // Every load of this unit has landed by now (the next unit's query fragments too):
-    // waiting for them here, ahead of the stores, leaves the stores in flight into the
-    // next unit instead of a wait for everything at its start.
+    // the next unit's query fragments, and a candidate's own key and value (merged after
+    // the history keys), fetched only now so that they hold no registers in the tile loop
+    if (unit_of(r + 1) < n_units) fetch_q(unit_of(r + 1));
+    u32x4_t kself[PB][2] = {};
+    u32x2_t vself[PB][4] = {};
+    if (is_cand) {
+      const char* kb0 = reinterpret_cast<const char*>(a.k + row0 * a.ld_qkv + h * DH);
+      const char* vb0 = reinterpret_cast<const char*>(a.v + row0 * a.ld_qkv + h * DH);
+#pragma unroll
+      for (int hb = 0; hb < PB; ++hb) {
+        const uint32_t lo = static_cast<uint32_t>(min(hb * QW + l16, nq - 1)) * ldq * 2u;
+        kself[hb][0] = *reinterpret_cast<const u32x4_t*>(kb0 + lo + g4 * 16);
+        kself[hb][1] = *reinterpret_cast<const u32x4_t*>(kb0 + lo + g4 * 16 + 64);
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) vself[hb][nb] = *reinterpret_cast<const u32x2_t*>(vb0 + lo + nb * 32 + g4 * 8);
+      }
+    }
+    // Waiting for these loads here, ahead of the stores, leaves the stores in flight into
+    // the next unit instead of a wait for everything at its start.
     wait_vmcnt<0>();
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
+    for (int hb = 0; hb < PB; ++hb) {
       // the candidate's own key: bias 0 (it is the reference point)
       if (is_cand)
         merge_self(kself[hb], vself[hb], qf[hb], SEP, a.scale2, tbk_self, SC, th, g4, m_run[hb], lsum[hb], accO[hb]);
