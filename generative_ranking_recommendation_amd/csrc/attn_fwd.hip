@@ -457,8 +457,9 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
 //    wave-uniform branch); until then probabilities up to 2^8 are accumulated against the
 //    stale maximum, which changes nothing in exact arithmetic and stays far inside fp32
 //    and bf16 range.
-//  - Row sums come from the bf16 probabilities with v_dot2 against ones (the same values
-//    the P V product uses).
+//  - Row sums come from the bf16 probabilities the P V product uses, on the matrix cores:
+//    one more product per 32-key half, ones^T P^T, leaves every lane its query's whole sum
+//    (no vector instruction per probability, no cross-lane sum at the end).
 constexpr int NS = 4;               // stage buffers in the K/V ring
 constexpr int STAGE = 2 * AK * DH;  // bf16 per stage buffer: the K tile, then the V tile
 constexpr float RESCALE_LOG2 = 8.f; // headroom of the stale running maximum (log2 units)
@@ -509,7 +510,7 @@ __device__ __forceinline__ void merge_self(const u32x4_t (&kself)[2], const u32x
     for (int nb = 0; nb < 4; ++nb) accO[nb] = accO[nb] * alpha;
   }
   const float p_self = __builtin_amdgcn_exp2f((m_self - m_run) * SC);
-  lsum += g4 == 0 ? p_self : 0.f;
+  lsum += p_self;  // (every lane holds its query's whole row sum)
   uint32_t hi = 0xFFFF0000u;  // kept in a scalar register
   asm volatile("" : "+s"(hi));
 #pragma unroll
@@ -672,7 +673,11 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
 
   // ---- softmax state in score units
   f32x4_t accO[4];
-  float m_run = -1e30f, lsum = 0.f;
+  // row sums on the matrix cores: ones^T P^T adds a query's probabilities over all 32 keys
+  // of a half tile into every element of its column, so each lane holds its query's sum
+  f32x4_t lacc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const bf16x8_t ones8 = as_bf16x8(make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
+  float m_run = -1e30f;
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) accO[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   lds_sync();  // sW, sT, sTB written
@@ -769,7 +774,7 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
       const float m_new = fmaxf(m_run, mx);
       const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * SC);
       m_run = m_new;
-      lsum *= alpha;
+      lacc = lacc * alpha;
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) accO[nb] = accO[nb] * alpha;
     }
@@ -785,8 +790,6 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
         const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sb[(j & 1) * 2], SC, mb));
         const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sb[(j & 1) * 2 + 1], SC, mb));
         pw[j] = pack_bf16x2(p0, p1);
-        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw[j]),
-                                                __builtin_bit_cast(bf16x2_t, 0x3F803F80u), lsum, false);
       }
       pf[ks] = as_bf16x8(pk);
     }
@@ -803,6 +806,7 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
         const v4i16_t both[2] = {lo, hi};
         accO[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, both), pf[ks], accO[nb], 0, 0, 0);
       }
+      lacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones8, pf[ks], lacc, 0, 0, 0);
     }
   };
 
@@ -853,10 +857,11 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 8)))
     loop(std::false_type{});
   }
   wait_vmcnt<0>();  // no direct load may still be writing LDS when the workgroup ends
+  float lsum = lacc[0];
   if (is_cand) merge_self(kself, vself, qf, SEP, a.scale2, tbk_self, SC, th, g4, m_run, lsum, accO);
 
   // ---- epilogue
-  const float ltot = xor32_sum(xor16_sum(lsum));
+  const float ltot = lsum;
   if (!q_valid) return;
   // (a row's sum is at least 1: the hardware reciprocal and log2 need no range fix-up)
   const float inv = __builtin_amdgcn_rcpf(ltot);
@@ -1129,19 +1134,19 @@ __global__ void __launch_bounds__(PAIR_NT) attn_fwd_pair_kernel(AttnArgs a) {
     for (int hb = 0; hb < PB; ++hb)
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) accO[hb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float m_run[PB], lsum[PB];
+    float m_run[PB];
+    f32x4_t lacc[PB];  // row sums on the matrix cores, as in the ring kernel
     // the raise threshold and the exponent's offset follow the maximum (set where it moves)
     float m_thr[PB], m_bias[PB];
 #pragma unroll
     for (int hb = 0; hb < PB; ++hb) {
       m_run[hb] = -1e30f;
-      lsum[hb] = 0.f;
+      lacc[hb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       m_thr[hb] = -1e30f + th;
       m_bias[hb] = 1e30f * SC;
     }
     f32x4_t s[PB][4];
-    uint32_t ones = 0x3F803F80u;  // two bf16 ones, kept in a scalar register
-    asm volatile("" : "+s"(ones));
+    const bf16x8_t ones8 = as_bf16x8(make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
 
     // the exact bias of key slot j for this lane's query of block hb, in score units (far
     // units): from the integer position and time differences, each product rounded once
@@ -1242,7 +1247,7 @@ __global__ void __launch_bounds__(PAIR_NT) attn_fwd_pair_kernel(AttnArgs a) {
         m_run[hb] = m_new;
         m_thr[hb] = m_new + th;
         m_bias[hb] = -m_new * SC;
-        lsum[hb] *= alpha;
+        lacc[hb] = lacc[hb] * alpha;
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) accO[hb][nb] = accO[hb][nb] * alpha;
       }
@@ -1257,8 +1262,6 @@ __global__ void __launch_bounds__(PAIR_NT) attn_fwd_pair_kernel(AttnArgs a) {
           const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sb[(j & 1) * 2], SC, mb));
           const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sb[(j & 1) * 2 + 1], SC, mb));
           pw[j] = pack_bf16x2(p0, p1);
-          lsum[hb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, ones),
-                                                      __builtin_bit_cast(bf16x2_t, pw[j]), lsum[hb], false);
         }
         pf[ks] = as_bf16x8(pk);
       }
@@ -1283,11 +1286,13 @@ __global__ void __launch_bounds__(PAIR_NT) attn_fwd_pair_kernel(AttnArgs a) {
 #pragma unroll
           for (int nb = 0; nb < 4; ++nb)
             accO[0][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vh[nb], pa[ks], accO[0][nb], 0, 0, 0);
+          lacc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones8, pa[ks], lacc[0], 0, 0, 0);
         }
         if constexpr (PB == 2) {
 #pragma unroll
           for (int nb = 0; nb < 4; ++nb)
             accO[PB - 1][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vh[nb], pb[ks], accO[PB - 1][nb], 0, 0, 0);
+          lacc[PB - 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones8, pb[ks], lacc[PB - 1], 0, 0, 0);
         }
       }
     };
@@ -1346,9 +1351,10 @@ __global__ void __launch_bounds__(PAIR_NT) attn_fwd_pair_kernel(AttnArgs a) {
 #pragma unroll
     for (int hb = 0; hb < PB; ++hb) {
       // the candidate's own key: bias 0 (it is the reference point)
+      float lsum = lacc[hb][0];
       if (is_cand)
-        merge_self(kself[hb], vself[hb], qf[hb], SEP, a.scale2, tbk_self, SC, th, g4, m_run[hb], lsum[hb], accO[hb]);
-      const float ltot = xor32_sum(xor16_sum(lsum[hb]));
+        merge_self(kself[hb], vself[hb], qf[hb], SEP, a.scale2, tbk_self, SC, th, g4, m_run[hb], lsum, accO[hb]);
+      const float ltot = lsum;
       const float inv = __builtin_amdgcn_rcpf(ltot);  // (as in the ring kernel)
       // Lane groups g4 and g4 ^ 1 (same query) trade halves: lane group g4 then holds the 8
       // consecutive dimensions 8 (g4 / 2) + 16 (g4 % 2) .. + 7 of blocks nb = 0, 1, and the
